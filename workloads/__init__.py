@@ -1,0 +1,279 @@
+"""Seeded synthetic inputs for single-query decode attention.
+
+This module only *draws* inputs: query vectors, a KV cache (contiguous
+``[kv_len, num_kv_heads, head_dim]`` or paged
+``[num_pages, page_size, num_kv_heads, head_dim]``), the page table and the
+per-request lengths.  It holds none of the attention arithmetic; both the
+fp64 oracle and the HIP path consume what it returns, so the two see the
+identical bits.
+
+Values are returned as the raw storage codes the library reads:
+``float32`` arrays for fp32, ``uint16`` bit patterns for bfloat16 and
+``uint8`` bit patterns for fp8 e4m3 (OCP "fn" variant).  Rounding from the
+float32 draws to the stored type uses torch's round-to-nearest-even casts
+(a library routine); fp8 values are clamped to +-448 first because torch's
+cast does not saturate.
+
+Recipe (one numpy ``Generator(PCG64(SeedSequence(seed)))``; child streams
+spawned in the fixed order lengths, permutation, q, k, v):
+
+* lengths: fixed, uniform integers, or a clipped rounded log-normal;
+* logical K/V for every (request, token, kv head, dim) ~ N(0, 1) in float32,
+  drawn in logical token order, then scattered into the page pool through
+  a seeded permutation of the pool, so a different permutation reproduces
+  the identical logical cache;
+* optional per-head RMS normalisation of q and k (eps 1e-6, unit weight),
+  standing in for the QK-norm of a Gemma-3 style model;
+* fp8: per-(request, kv head) scale = amax / 448 over that request's K (and
+  separately V) values, codes = e4m3(x / scale) with saturation;
+* unused slots of each request's last page are poisoned with NaN codes when
+  ``poison=True`` so that any read of padding shows up.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "DecodeSpec",
+    "DecodeInputs",
+    "make_inputs",
+    "CONFIGS",
+    "config",
+    "small_variant",
+    "F32",
+    "BF16",
+    "FP8",
+]
+
+F32, BF16, FP8 = "f32", "bf16", "fp8"
+_STORE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
+_POISON = {F32: np.float32(np.nan).view(np.uint32), BF16: 0x7FC0, FP8: 0x7F}
+FP8_MAX = 448.0
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeSpec:
+    """Shape and distribution of one decode workload."""
+
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int  # 0 = contiguous cache (batch must be 1)
+    kv_dtype: str
+    q_dtype: str
+    sm_scale: float
+    window: int = -1
+    # lengths: ("fixed", L) | ("uniform", lo, hi) | ("lognormal", mu, sigma, lo, hi)
+    lengths: tuple = ("fixed", 512)
+    qk_rmsnorm: bool = False
+    seed: int = 1000
+
+    @property
+    def group(self) -> int:
+        return self.num_qo_heads // self.num_kv_heads
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    spec: DecodeSpec
+    q: np.ndarray  # [batch, Hq, d] raw codes
+    k: np.ndarray  # contiguous [L, Hk, d] or paged [num_pages, P, Hk, d] raw codes
+    v: np.ndarray
+    kv_len: np.ndarray  # int32 [batch]
+    page_indptr: Optional[np.ndarray]  # int32 [batch + 1] (paged only)
+    page_indices: Optional[np.ndarray]  # int32 [nnz] (paged only)
+    k_scale: Optional[np.ndarray]  # float32 [batch, Hk] (fp8 only)
+    v_scale: Optional[np.ndarray]
+
+    @property
+    def num_pages(self) -> int:
+        return 0 if self.spec.page_size == 0 else int(self.k.shape[0])
+
+
+def _rng(seed: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(5)]
+
+
+def _draw_lengths(spec: DecodeSpec, rng) -> np.ndarray:
+    kind = spec.lengths[0]
+    if kind == "fixed":
+        out = np.full(spec.batch, int(spec.lengths[1]), dtype=np.int64)
+    elif kind == "uniform":
+        lo, hi = spec.lengths[1], spec.lengths[2]
+        out = rng.integers(lo, hi, size=spec.batch, endpoint=True)
+    elif kind == "lognormal":
+        mu, sigma, lo, hi = spec.lengths[1:5]
+        out = np.clip(np.rint(np.exp(rng.normal(mu, sigma, size=spec.batch))), lo, hi)
+    elif kind == "list":
+        out = np.asarray(spec.lengths[1], dtype=np.int64)
+        assert out.shape == (spec.batch,)
+    else:
+        raise ValueError(f"unknown length law {kind!r}")
+    return out.astype(np.int32)
+
+
+def _to_bf16_codes(x: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _to_fp8_codes(x: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -FP8_MAX, FP8_MAX))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _rms_normalize(x: np.ndarray) -> np.ndarray:
+    """Per-head RMS normalisation over the last axis, eps 1e-6, unit weight."""
+    ms = np.mean(np.square(x, dtype=np.float32), axis=-1, keepdims=True, dtype=np.float32)
+    return (x / np.sqrt(ms + np.float32(1e-6))).astype(np.float32)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == BF16:
+        return _to_bf16_codes(x)
+    raise ValueError(dtype)
+
+
+def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = False,
+                permute_pages: bool = True, perm_seed: Optional[int] = None,
+                lengths: Optional[np.ndarray] = None) -> DecodeInputs:
+    """Draw one seeded workload.
+
+    ``perm_seed`` (paged only) replaces the permutation stream's seed while
+    keeping every value identical; ``permute_pages=False`` lays pages out in
+    logical order (identity page table).  ``lengths`` overrides the length
+    draw (used by edge-case tests).
+    """
+    seed = spec.seed if seed is None else seed
+    r_len, r_perm, r_q, r_k, r_v = _rng(seed)
+    if perm_seed is not None:
+        r_perm = np.random.Generator(np.random.PCG64(np.random.SeedSequence(perm_seed)))
+    B, Hq, Hk, d, P = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size
+    if Hq % Hk:
+        raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
+    kv_len = _draw_lengths(spec, r_len) if lengths is None else np.asarray(lengths, np.int32)
+    if P == 0 and B != 1:
+        raise ValueError("a contiguous cache holds one request")
+
+    q = r_q.standard_normal((B, Hq, d), dtype=np.float32)
+    total = int(kv_len.sum())
+    k_log = r_k.standard_normal((total, Hk, d), dtype=np.float32)
+    v_log = r_v.standard_normal((total, Hk, d), dtype=np.float32)
+    if spec.qk_rmsnorm:
+        q = _rms_normalize(q)
+        k_log = _rms_normalize(k_log)
+
+    q_codes = _store(q, spec.q_dtype)
+    offs = np.concatenate([[0], np.cumsum(kv_len, dtype=np.int64)])
+    k_scale = v_scale = None
+    if spec.kv_dtype == FP8:
+        k_scale = np.ones((B, Hk), np.float32)
+        v_scale = np.ones((B, Hk), np.float32)
+        k_codes = np.empty(k_log.shape, np.uint8)
+        v_codes = np.empty(v_log.shape, np.uint8)
+        for b in range(B):
+            sl = slice(offs[b], offs[b + 1])
+            for src, codes, scale in ((k_log, k_codes, k_scale), (v_log, v_codes, v_scale)):
+                blk = src[sl]  # [L_b, Hk, d]
+                if blk.shape[0] == 0:
+                    continue
+                amax = np.max(np.abs(blk), axis=(0, 2))
+                s = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+                scale[b] = s
+                codes[sl] = _to_fp8_codes(blk / s[None, :, None])
+    else:
+        k_codes = _store(k_log, spec.kv_dtype)
+        v_codes = _store(v_log, spec.kv_dtype)
+    del k_log, v_log
+
+    if P == 0:
+        return DecodeInputs(spec, q_codes, k_codes, v_codes, kv_len, None, None, k_scale, v_scale)
+
+    n_pages = (kv_len.astype(np.int64) + P - 1) // P
+    indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    N = int(indptr[-1])
+    perm = r_perm.permutation(N).astype(np.int32) if permute_pages else np.arange(N, dtype=np.int32)
+    store = _STORE[spec.kv_dtype]
+    pool_shape = (N, P, Hk, d)
+    if poison:
+        fill = _POISON[spec.kv_dtype]
+        if spec.kv_dtype == F32:
+            k_pool = np.full(pool_shape, np.uint32(fill), np.uint32).view(np.float32)
+            v_pool = k_pool.copy()
+        else:
+            k_pool = np.full(pool_shape, fill, store)
+            v_pool = np.full(pool_shape, fill, store)
+    else:
+        k_pool = np.zeros(pool_shape, store)
+        v_pool = np.zeros(pool_shape, store)
+    # scatter logical tokens into their pages
+    for b in range(B):
+        L = int(kv_len[b])
+        if L == 0:
+            continue
+        pages = perm[indptr[b]:indptr[b + 1]]
+        full, rem = divmod(L, P)
+        src_k = k_codes[offs[b]:offs[b + 1]]
+        src_v = v_codes[offs[b]:offs[b + 1]]
+        if full:
+            k_pool[pages[:full]] = src_k[:full * P].reshape(full, P, Hk, d)
+            v_pool[pages[:full]] = src_v[:full * P].reshape(full, P, Hk, d)
+        if rem:
+            k_pool[pages[full], :rem] = src_k[full * P:]
+            v_pool[pages[full], :rem] = src_v[full * P:]
+    return DecodeInputs(spec, q_codes, k_pool, v_pool, kv_len, indptr, perm, k_scale, v_scale)
+
+
+# The five workloads.  Sizes follow the decode shapes the pages discuss: an
+# MHA fp32 toy, a Gemma-3-1B-like single decode (GQA 4, head_dim 256, QK-norm,
+# local window 512), a Llama-2-7B long-context decode, and two batched paged
+# GQA decodes (bf16 and fp8 e4m3 KV).
+CONFIGS = {
+    "c1_mha_f32": DecodeSpec("c1_mha_f32", 1, 8, 8, 64, 0, F32, F32, 1.0 / 8.0,
+                             lengths=("fixed", 512), seed=1000),
+    "c2_gemma3_1b": DecodeSpec("c2_gemma3_1b", 1, 4, 1, 256, 0, BF16, BF16, 1.0 / 16.0,
+                               lengths=("fixed", 8192), qk_rmsnorm=True, seed=1001),
+    "c2_gemma3_1b_w512": DecodeSpec("c2_gemma3_1b_w512", 1, 4, 1, 256, 0, BF16, BF16, 1.0 / 16.0,
+                                    window=512, lengths=("fixed", 8192), qk_rmsnorm=True, seed=1001),
+    "c3_llama2_7b_32k": DecodeSpec("c3_llama2_7b_32k", 1, 32, 32, 128, 0, BF16, BF16,
+                                   1.0 / math.sqrt(128.0), lengths=("fixed", 32768), seed=1002),
+    "c4_paged_bf16_b64": DecodeSpec("c4_paged_bf16_b64", 64, 32, 8, 128, 16, BF16, BF16,
+                                    1.0 / math.sqrt(128.0), lengths=("uniform", 512, 16384), seed=1003),
+    "c5_paged_fp8_b128": DecodeSpec("c5_paged_fp8_b128", 128, 64, 8, 128, 16, FP8, BF16,
+                                    1.0 / math.sqrt(128.0),
+                                    lengths=("lognormal", math.log(4096.0), 0.8, 128, 65536), seed=1004),
+}
+
+
+def config(name: str) -> DecodeSpec:
+    return CONFIGS[name]
+
+
+def small_variant(name: str, *, batch: Optional[int] = None, lengths: Optional[tuple] = None,
+                  window: Optional[int] = None, seed: Optional[int] = None) -> DecodeSpec:
+    """Same heads, head_dim, dtypes and layout as a named workload, smaller sizes."""
+    base = CONFIGS[name]
+    kw = {}
+    if batch is not None:
+        kw["batch"] = batch
+    if lengths is not None:
+        kw["lengths"] = lengths
+    if window is not None:
+        kw["window"] = window
+    if seed is not None:
+        kw["seed"] = seed
+    return dataclasses.replace(base, name=base.name + "_small", **kw)
+
