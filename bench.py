@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode-attention step (split-KV partial softmax + merge)
+on one MI355X.
+
+Default workload: batched paged GQA decode, batch 64, 32 query / 8 KV heads,
+head_dim 128, page size 16, kv_len ~ U[512, 16384], bf16 KV (seeded synthetic
+inputs).  One step = one kvs_decode call over the whole batch, inputs already
+resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+CONFIG_ALIASES = {"c1": "c1_mha_f32", "c2": "c2_gemma3_1b", "c2w": "c2_gemma3_1b_w512",
+                  "c3": "c3_llama2_7b_32k", "c4": "c4_paged_bf16_b64", "c5": "c5_paged_fp8_b128"}
+DEFAULT = "c4_paged_bf16_b64"
+_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def algorithmic_bytes(inp) -> int:
+    """Bytes the method must move once: K and V of every visible (token, KV
+    head), q, o, lse, kv_len, the page-table entries it reads and the fp8
+    scales."""
+    s = inp.spec
+    b_kv, b_q = _BYTES[s.kv_dtype], _BYTES[s.q_dtype]
+    L = inp.kv_len.astype(np.int64)
+    lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
+    vis = int(np.sum(L - lo))
+    kv = 2 * vis * s.num_kv_heads * s.head_dim * b_kv
+    qo = 2 * s.batch * s.num_qo_heads * s.head_dim * b_q + 4 * s.batch * s.num_qo_heads
+    meta = 4 * s.batch
+    if s.page_size:
+        first = lo // s.page_size
+        last = (L + s.page_size - 1) // s.page_size
+        meta += 4 * (s.batch + 1) + 4 * int(np.sum(np.maximum(0, last - first)))
+    if s.kv_dtype == "fp8":
+        meta += 2 * 4 * s.batch * s.num_kv_heads
+    return kv + qo + meta
+
+
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.hip.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def cpu_baseline(inp, budget_s: float = 15.0):
+    """The fp64 oracle as it stands, on a bounded sample of the same workload:
+    whole requests in order until the time budget is spent."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    s = inp.spec
+    sub_bytes = 0
+    done = []
+    t0 = time.perf_counter()
+    for b in range(s.batch):
+        oracle.decode_reference(inp, requests=[b])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    L = inp.kv_len.astype(np.int64)
+    lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
+    vis = int(np.sum((L - lo)[done]))
+    frac_bytes = algorithmic_bytes(inp) * (vis / max(1, int(np.sum(L - lo))))
+    return {"value": round(frac_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {len(done)} of {s.batch} requests ({vis} visible tokens), "
+                      f"{dt:.1f} s, same seeded inputs"}
+
+
+def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
+        with_cpu: bool = True) -> dict:
+    import torch
+
+    import decode_attention_kv_split_amd as kvs
+    from workloads import CONFIGS, make_inputs
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from kvs_testlib import to_torch
+
+    kvs.load_library()
+    spec = CONFIGS[config_name]
+    t_gen = time.perf_counter()
+    inp = make_inputs(spec)
+    t = to_torch(inp)
+    t_gen = time.perf_counter() - t_gen
+    s = spec
+    a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
+                            page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
+                            k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
+                            window=s.window, kv_chunk=kv_chunk, algo=algo)
+    plan = kvs.kvs_decode_plan(a)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    evs = ev.create(2 * steps)
+
+    def step(e0=None, e1=None):
+        a.prof_events[0] = e0
+        a.prof_events[1] = e1
+        st = kvs.kvs_decode(a, ws.data_ptr(), ws.numel(), stream)
+        if st != kvs.KVS_OK:
+            raise kvs.KvsError(st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[2 * i], evs[2 * i + 1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = [ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    ev.destroy(evs)
+
+    nbytes = algorithmic_bytes(inp)
+    ms_per_step = wall * 1e3 / steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    part_avg = float(np.mean(part_ms))
+    achieved = nbytes / (part_avg * 1e-3) / 1e9
+    props = torch.cuda.get_device_properties(0)
+    kernel = ("partial_mfma_kernel" if plan.algo == kvs.KVS_ALGO_MFMA else "partial_valu_kernel")
+    out = {
+        "metric": "decode-attention us/step and achieved HBM GB/s (% of peak), paged GQA batch",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{s.kv_dtype} KV, {s.q_dtype} q, fp32 accumulate",
+        "data": "synthetic (seeded; N(0,1) K/V, shapes of the named workload)",
+        "config": {
+            "workload": config_name,
+            "batch": s.batch, "num_qo_heads": s.num_qo_heads, "num_kv_heads": s.num_kv_heads,
+            "head_dim": s.head_dim, "page_size": s.page_size, "window": s.window, "kv_dtype": s.kv_dtype,
+            "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
+            "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
+            "max_splits": plan.max_splits, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel_us": round(part_avg * 1e3, 2),
+            "algorithmic_bytes": nbytes,
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count, "host": platform.node()},
+        "input_gen_s": round(t_gen, 1),
+    }
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=DEFAULT)
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(each GPU would run its own requests or KV heads independently).", file=sys.stderr)
+        sys.exit(2)
+    name = CONFIG_ALIASES.get(args.config, args.config)
+    res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

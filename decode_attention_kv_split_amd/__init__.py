@@ -1,0 +1,308 @@
+"""Python binding of libkvsplit (split-KV decode attention on MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libkvsplit.so``.  There is no CPU fallback; if the library is
+not built, every call raises.
+
+Low level (same names as the C ABI in ``include/kvsplit.h``):
+    kvs_decode(args, workspace_ptr, workspace_bytes, stream) -> status
+    kvs_decode_plan(args) -> KvsPlanInfo
+    kvs_decode_workspace_bytes(args) -> int
+    kvs_status_string(status) -> str
+    kvs_abi_version() -> int
+High level, on torch tensors already on the GPU:
+    decode(...)              any layout, returns (o, lse)
+    single_decode(q, k, v)   one request, contiguous cache
+    batch_decode_paged(...)  paged cache
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+__all__ = [
+    "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
+    "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
+    "KvsDecodeArgs", "KvsPlanInfo", "KvsError",
+    "library_path", "load_library",
+    "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_status_string", "kvs_abi_version",
+    "decode", "single_decode", "batch_decode_paged",
+]
+
+KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
+KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
+KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA = 0, 1, 2
+_ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "_lib", "libkvsplit.so")
+
+
+class KvsDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("page_indptr", ctypes.c_void_p),
+        ("page_indices", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
+        ("kv_len_host", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("sm_scale", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("kv_chunk", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("prof_events", ctypes.c_void_p * 2),
+    ]
+
+
+class KvsPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("kv_chunk", ctypes.c_int32),
+        ("items_per_kv_head", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("needs_merge", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, what: str = "kvs_decode"):
+        self.status = status
+        super().__init__(f"{what}: {kvs_status_string(status)} (status {status})")
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library():
+    """Load libkvsplit.so; raises if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"libkvsplit.so is not built ({path}); run `python -m decode_attention_kv_split_amd.build`")
+            lib = ctypes.CDLL(path)
+            lib.kvs_decode.restype = ctypes.c_int
+            lib.kvs_decode.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+            lib.kvs_decode_plan.restype = ctypes.c_int
+            lib.kvs_decode_plan.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.POINTER(KvsPlanInfo)]
+            lib.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
+            lib.kvs_decode_workspace_bytes.argtypes = [ctypes.POINTER(KvsDecodeArgs)]
+            lib.kvs_status_string.restype = ctypes.c_char_p
+            lib.kvs_status_string.argtypes = [ctypes.c_int]
+            lib.kvs_abi_version.restype = ctypes.c_int
+            lib.kvs_abi_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------------------------
+# C ABI, same names
+# ----------------------------------------------------------------------------
+
+def kvs_decode(args: KvsDecodeArgs, workspace: int, workspace_bytes: int, stream: int) -> int:
+    return int(load_library().kvs_decode(ctypes.byref(args), ctypes.c_void_p(workspace or None),
+                                         ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def kvs_decode_plan(args: KvsDecodeArgs) -> KvsPlanInfo:
+    info = KvsPlanInfo()
+    st = int(load_library().kvs_decode_plan(ctypes.byref(args), ctypes.byref(info)))
+    if st != KVS_OK:
+        raise KvsError(st, "kvs_decode_plan")
+    return info
+
+
+def kvs_decode_workspace_bytes(args: KvsDecodeArgs) -> int:
+    return int(load_library().kvs_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def kvs_status_string(status: int) -> str:
+    return load_library().kvs_status_string(int(status)).decode()
+
+
+def kvs_abi_version() -> int:
+    return int(load_library().kvs_abi_version())
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _dtype_code(t, what: str) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return KVS_F32
+    if t.dtype == torch.bfloat16:
+        return KVS_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8) and what == "kv":
+        return KVS_FP8_E4M3
+    raise ValueError(f"unsupported {what} dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(t, name: str, device) -> None:
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_ws_cache = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(nbytes: int, device, stream: int):
+    """Per (device, stream) scratch buffer, grown on demand (torch allocation)."""
+    import torch
+
+    if nbytes == 0:
+        return None
+    key = (device.index, stream)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+    return buf
+
+
+def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None,
+              k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
+              algo="auto", out=None, lse=None, num_cus: int = 0) -> Tuple[KvsDecodeArgs, object]:
+    """Build the C argument block from torch tensors.
+
+    q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
+    [num_pages, page_size, Hk, d]; kv_len: int32 [batch] on the device.
+    Returns (args, keepalive)."""
+    import numpy as np
+    import torch
+
+    device = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, num_qo_heads, head_dim]")
+    B, Hq, d = q.shape
+    paged = page_indptr is not None
+    if paged:
+        if k.dim() != 4:
+            raise ValueError("paged k/v must be [num_pages, page_size, num_kv_heads, head_dim]")
+        num_pages, P, Hk, dk = k.shape
+    else:
+        if k.dim() != 3:
+            raise ValueError("contiguous k/v must be [kv_len, num_kv_heads, head_dim]")
+        _, Hk, dk = k.shape
+        P, num_pages = 0, 0
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    if dk != d:
+        raise ValueError("head_dim of q and k differ")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len"), (page_indptr, "page_indptr"),
+                 (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check_dev(t, n, device)
+    if kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("kv_len must be int32 [batch]")
+    if kv_len_host is None:
+        kv_len_host = kv_len.cpu()
+    kvh = np.ascontiguousarray(np.asarray(kv_len_host.cpu() if isinstance(kv_len_host, torch.Tensor)
+                                          else kv_len_host, dtype=np.int32))
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=q.dtype, device=device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=device)
+    _check_dev(out, "out", device)
+    _check_dev(lse, "lse", device)
+    a = KvsDecodeArgs()
+    a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = B, Hq, Hk, d
+    a.q_dtype = _dtype_code(q, "q")
+    a.kv_dtype = _dtype_code(k, "kv")
+    a.page_size, a.num_pages = P, num_pages
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.page_indptr, a.page_indices = _ptr(page_indptr), _ptr(page_indices)
+    a.kv_len = _ptr(kv_len)
+    a.kv_len_host = kvh.ctypes.data
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.sm_scale = float(1.0 / math.sqrt(d) if sm_scale is None else sm_scale)
+    a.window = int(window)
+    a.kv_chunk = int(kv_chunk)
+    a.algo = _ALGOS[algo] if isinstance(algo, str) else int(algo)
+    a.num_cus = int(num_cus)
+    a.o, a.lse = _ptr(out), _ptr(lse)
+    keep = (kvh, out, lse)
+    return a, keep
+
+
+def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
+           v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
+           workspace=None, stream=None):
+    """One decode-attention step on the current (or given) HIP stream.
+    Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
+    import torch
+
+    a, keep = make_args(q, k, v, kv_len, page_indptr=page_indptr, page_indices=page_indices,
+                        kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
+                        window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
+    need = kvs_decode_workspace_bytes(a)
+    if workspace is None:
+        ws = _workspace(need, q.device, s)
+        ws_ptr, ws_bytes = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
+    else:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = kvs_decode(a, ws_ptr, ws_bytes, s)
+    if st != KVS_OK:
+        if st in (KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE):
+            raise ValueError(f"kvs_decode: {kvs_status_string(st)}")
+        raise KvsError(st)
+    return keep[1], keep[2]
+
+
+def single_decode(q, k, v, *, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto",
+                  k_scale=None, v_scale=None):
+    """One request: q [Hq, d], k/v [kv_len, Hk, d].  Returns (o [Hq, d], lse [Hq])."""
+    import torch
+
+    L = k.shape[0]
+    kv_len = torch.tensor([L], dtype=torch.int32, device=q.device)
+    o, lse = decode(q[None], k, v, kv_len, kv_len_host=[L], sm_scale=sm_scale, window=window,
+                    kv_chunk=kv_chunk, algo=algo, k_scale=k_scale, v_scale=v_scale)
+    return o[0], lse[0]
+
+
+def batch_decode_paged(q, k_pages, v_pages, page_indptr, page_indices, kv_len, *, kv_len_host=None,
+                       sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", k_scale=None,
+                       v_scale=None):
+    """Batched decode over a paged cache; q [batch, Hq, d]."""
+    return decode(q, k_pages, v_pages, kv_len, page_indptr=page_indptr, page_indices=page_indices,
+                  kv_len_host=kv_len_host, sm_scale=sm_scale, window=window, kv_chunk=kv_chunk, algo=algo,
+                  k_scale=k_scale, v_scale=v_scale)

@@ -1,0 +1,209 @@
+// C ABI of the split-KV decode-attention library: argument validation on the
+// host, planning, and the two launches (partial softmax per chunk, then the
+// log-sum-exp merge).  No device memory is allocated and nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kvsplit.h"
+#include "kvs_device.h"
+#include "plan.h"
+
+namespace kvs {
+hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStream_t stream);
+hipError_t launch_partial_valu(const Params &p, int head_dim, int kv_dtype, hipStream_t stream);
+hipError_t launch_merge(const Params &p, int head_dim, hipStream_t stream);
+int valu_max_group(int kv_dtype);
+} // namespace kvs
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+// Host-only checks shared by plan and decode.  need_ptrs: device pointers must
+// be non-null.  Resolves the kernel family into *algo.
+kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
+  if (!a) return KVS_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->num_qo_heads < 1 || a->num_kv_heads < 1) return KVS_ERR_INVALID_ARG;
+  if (a->num_qo_heads % a->num_kv_heads) return KVS_ERR_INVALID_ARG;
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) return KVS_ERR_UNSUPPORTED;
+  const int group = a->num_qo_heads / a->num_kv_heads;
+  if (group > 16) return KVS_ERR_UNSUPPORTED;
+  const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
+  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 2) return KVS_ERR_INVALID_ARG;
+  if (!pair_ok) return KVS_ERR_UNSUPPORTED;
+  if (a->page_size < 0) return KVS_ERR_INVALID_ARG;
+  if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
+  if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
+  if (a->page_size > 0 && a->num_pages < 1) return KVS_ERR_INVALID_ARG;
+  if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale)) return KVS_ERR_INVALID_ARG;
+  if (a->window < -1 || a->window == 0) return KVS_ERR_INVALID_ARG;
+  if (a->kv_chunk < 0) return KVS_ERR_INVALID_ARG;
+  if (a->num_cus < 0) return KVS_ERR_INVALID_ARG;
+  if (!a->kv_len_host) return KVS_ERR_INVALID_ARG;
+  for (int b = 0; b < a->batch; ++b) {
+    const int L = a->kv_len_host[b];
+    if (L < 0) return KVS_ERR_INVALID_ARG;
+    if (a->page_size > 0 && (int64_t)L > (int64_t)a->num_pages * a->page_size) return KVS_ERR_INVALID_ARG;
+  }
+  if (need_ptrs) {
+    if (!a->q || !a->k || !a->v || !a->kv_len || !a->o) return KVS_ERR_INVALID_ARG;
+    if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
+    if (a->kv_dtype == KVS_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
+  }
+  // kernel family
+  const bool mfma_ok = a->kv_dtype != KVS_F32 && a->q_dtype == KVS_BF16 &&
+                       (a->page_size == 0 || a->page_size >= 16);
+  const bool valu_ok = group <= kvs::valu_max_group(a->kv_dtype);
+  switch (a->algo) {
+  case KVS_ALGO_AUTO:
+    if (mfma_ok)
+      *algo = KVS_ALGO_MFMA;
+    else if (valu_ok)
+      *algo = KVS_ALGO_VALU;
+    else
+      return KVS_ERR_UNSUPPORTED;
+    break;
+  case KVS_ALGO_MFMA:
+    if (!mfma_ok) return KVS_ERR_UNSUPPORTED;
+    *algo = KVS_ALGO_MFMA;
+    break;
+  case KVS_ALGO_VALU:
+    if (!valu_ok) return KVS_ERR_UNSUPPORTED;
+    *algo = KVS_ALGO_VALU;
+    break;
+  default:
+    return KVS_ERR_INVALID_ARG;
+  }
+  return KVS_OK;
+}
+
+kvs_status resolve_cus(const kvs_decode_args *a, int *cus) {
+  if (a->num_cus > 0) {
+    *cus = a->num_cus;
+    return KVS_OK;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVS_ERR_HIP;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return KVS_ERR_HIP;
+  *cus = n;
+  return KVS_OK;
+}
+
+kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, int *algo, int *cus) {
+  kvs_status st = validate(a, need_ptrs, algo);
+  if (st != KVS_OK) return st;
+  st = resolve_cus(a, cus);
+  if (st != KVS_OK) return st;
+  const int group = a->num_qo_heads / a->num_kv_heads;
+  if (!kvs::make_plan(a->kv_len_host, a->batch, a->window, a->num_kv_heads, group, a->head_dim,
+                      a->kv_chunk, *cus, pl))
+    return KVS_ERR_INVALID_ARG;
+  return KVS_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
+  if (!out) return KVS_ERR_INVALID_ARG;
+  kvs::Plan pl;
+  int algo = 0, cus = 0;
+  const kvs_status st = plan_call(args, false, &pl, &algo, &cus);
+  if (st != KVS_OK) return st;
+  out->kv_chunk = pl.chunk;
+  out->items_per_kv_head = pl.items;
+  out->max_splits = pl.max_splits;
+  out->needs_merge = pl.needs_merge ? 1 : 0;
+  out->algo = algo;
+  out->num_cus = cus;
+  out->workspace_bytes = pl.workspace_bytes;
+  return KVS_OK;
+}
+
+size_t kvs_decode_workspace_bytes(const kvs_decode_args *args) {
+  kvs::Plan pl;
+  int algo = 0, cus = 0;
+  if (plan_call(args, false, &pl, &algo, &cus) != KVS_OK) return 0;
+  return pl.workspace_bytes;
+}
+
+kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  kvs::Plan pl;
+  int algo = 0, cus = 0;
+  kvs_status st = plan_call(a, true, &pl, &algo, &cus);
+  if (st != KVS_OK) return st;
+  if (pl.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.workspace_bytes) return KVS_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return KVS_ERR_WORKSPACE;
+  }
+  kvs::Params p{};
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.page_indptr = a->page_indptr;
+  p.page_indices = a->page_indices;
+  p.kv_len = a->kv_len;
+  p.k_scale = a->kv_dtype == KVS_FP8_E4M3 ? a->k_scale : nullptr;
+  p.v_scale = a->kv_dtype == KVS_FP8_E4M3 ? a->v_scale : nullptr;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.o_part = pl.workspace_bytes ? reinterpret_cast<float *>(workspace) : nullptr;
+  p.lse_part = pl.workspace_bytes
+                   ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.o_part_bytes)
+                   : nullptr;
+  p.batch = a->batch;
+  p.num_qo_heads = a->num_qo_heads;
+  p.num_kv_heads = a->num_kv_heads;
+  p.group = a->num_qo_heads / a->num_kv_heads;
+  p.page_size = a->page_size;
+  p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;
+  p.window = a->window;
+  p.chunk = pl.chunk;
+  p.items = pl.items;
+  p.out_bf16 = a->q_dtype == KVS_BF16 ? 1 : 0;
+  p.score_scale = a->sm_scale * kvs::kLog2e;
+
+  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a->prof_events[0]);
+  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a->prof_events[1]);
+  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return KVS_ERR_HIP;
+  hipError_t e;
+  if (algo == KVS_ALGO_MFMA)
+    e = kvs::launch_partial_mfma(p, a->head_dim, a->kv_dtype == KVS_FP8_E4M3, stream);
+  else
+    e = kvs::launch_partial_valu(p, a->head_dim, a->kv_dtype, stream);
+  if (e != hipSuccess) return KVS_ERR_HIP;
+  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return KVS_ERR_HIP;
+  if (pl.needs_merge) {
+    e = kvs::launch_merge(p, a->head_dim, stream);
+    if (e != hipSuccess) return KVS_ERR_HIP;
+  }
+  return KVS_OK;
+}
+
+const char *kvs_status_string(int s) {
+  switch (s) {
+  case KVS_OK: return "ok";
+  case KVS_ERR_INVALID_ARG: return "invalid argument";
+  case KVS_ERR_UNSUPPORTED: return "unsupported shape or type";
+  case KVS_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+  case KVS_ERR_HIP: return "HIP runtime or launch error";
+  default: return "unknown status";
+  }
+}
+
+int kvs_abi_version(void) { return KVS_ABI_VERSION; }
+
+} // extern "C"

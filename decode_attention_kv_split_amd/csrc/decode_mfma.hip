@@ -1,0 +1,334 @@
+// Split-KV partial softmax for bf16 / fp8-e4m3 KV on gfx950 matrix cores.
+//
+// One workgroup (4 waves) owns one chunk of one (request, KV head); wave w
+// takes the chunk's 16-token tiles w, w+4, w+8, ...  All query heads of the
+// GQA group share every K/V byte the wave loads.
+//
+// Per 16-token tile, with lane = 16 * q4 + c16:
+//   * loads: lane reads token c16 of the tile, dims [q4*D/4, (q4+1)*D/4) of
+//     its K and V rows (contiguous 16-byte loads; the 16 lanes of a quarter
+//     cover 16 rows).  That is already the operand layout of a matrix tile
+//     whose rows are tokens and whose reduction index is the head dimension.
+//   * scores S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_bf16
+//     (fp8 K converted to bf16 first, exactly); lane ends up with tokens
+//     4*q4 + r (r = 0..3) of query head c16.
+//   * online softmax per head c16 in the log2 domain: tile max over the 16
+//     tokens (in-lane over r, then across the four quarters), rescale factor,
+//     weights p = exp2(s - max), running sum.
+//   * V^T: multiplying the V tile by an identity (bf16, 16x16x16) or by a
+//     0/1 selection (fp8, 16x16x32 fp8) puts tokens 4*q4 + r of one head
+//     dimension in lane c16 -- the operand layout the next product needs --
+//     and, for fp8, decodes the codes exactly into fp32.
+//   * O^T[dim][head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane keeps
+//     dims q4*D/4 + 4*w + r (w = 0..D/16-1) of query head c16, so the running
+//     max, sum and rescale of a head never leave its lane.
+// The first product, the online update and the rescaled accumulation follow
+// the tiled online softmax of "Forcing Flash Attention onto TPU", section
+// "Flash Attention in JAX"; chunk results are merged by log-sum-exp (FlashDecoding++
+// explainer, asynchronous-softmax section: partial softmax per tile, then an
+// update with the previous max and sum).
+#include "kvs_device.h"
+
+namespace kvs {
+namespace {
+
+template <int D, bool FP8>
+struct Shape {
+  static constexpr int kBytes = FP8 ? 1 : 2;
+  static constexpr int kLaneDims = D / 4;
+  static constexpr int kLaneVec = kLaneDims * kBytes / 16; // uint4 per lane per row
+  static constexpr int kKSteps = D / 32;                   // 16x16x32 products for S^T
+  static constexpr int kOTiles = D / 16;                   // 16-dim slices of O^T
+  static_assert(kLaneVec >= 1, "row slice must hold at least 16 bytes");
+};
+
+template <int D, bool FP8>
+struct TileRegs {
+  uint4 k[Shape<D, FP8>::kLaneVec];
+  uint4 v[Shape<D, FP8>::kLaneVec];
+};
+
+__device__ __forceinline__ float xor16_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 16, 64));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+// 8 consecutive fp8 codes (two dwords) -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<D, FP8> &t, int j) {
+  if constexpr (FP8) {
+    const uint4 w = t.k[j >> 1];
+    return (j & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+  } else {
+    return __builtin_bit_cast(bf16x8_t, t.k[j]);
+  }
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_tile(TileRegs<D, FP8> &t, const char *kbase, const char *vbase,
+                                          size_t row_off_bytes, bool valid) {
+  using S = Shape<D, FP8>;
+  if (valid) {
+    const uint4 *kp = reinterpret_cast<const uint4 *>(kbase + row_off_bytes);
+    const uint4 *vp = reinterpret_cast<const uint4 *>(vbase + row_off_bytes);
+#pragma unroll
+    for (int i = 0; i < S::kLaneVec; ++i) t.k[i] = kp[i];
+#pragma unroll
+    for (int i = 0; i < S::kLaneVec; ++i) t.v[i] = vp[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::kLaneVec; ++i) {
+      t.k[i] = make_uint4(0, 0, 0, 0);
+      t.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int D, bool FP8, int PF>
+__global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) {
+  using S = Shape<D, FP8>;
+  constexpr int NBUF = PF + 1;
+  constexpr int OSTRIDE = D + 4;
+
+  __shared__ int s_scan[2 * 64];
+  __shared__ int s_item[4];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves * 16 * OSTRIDE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int kvh = blockIdx.y;
+  const int item = blockIdx.x;
+  const int g = p.group;
+  const int Hk = p.num_kv_heads;
+
+  // ---- which (request, split) is this workgroup? ----
+  if (tid == 0) s_item[0] = -1;
+  scan_requests(p, s_scan, [&](int b, int first, int nb) {
+    if (item >= first && item < first + nb) {
+      s_item[0] = b;
+      s_item[1] = item - first;
+      s_item[2] = nb;
+    }
+  });
+  __syncthreads();
+  const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
+  const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
+  const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
+  if (b < 0) return; // kv_len on the device disagrees with the planned launch
+
+  const int L = p.kv_len[b];
+  const int lo = visible_lo(L, p.window);
+  const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
+  const int t_begin = max(lo, a0);
+  const int t_end = min(L, a0 + p.chunk);
+  const int ntiles = t_end > t_begin ? (t_end - a0 + kTile - 1) / kTile : 0;
+  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+  // ---- Q^T operand (query head c16 of this group; zero rows beyond the group) ----
+  bf16x8_t qop[S::kKSteps];
+  {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) +
+                         ((size_t)b * p.num_qo_heads + (size_t)kvh * g + c16) * D + q4 * S::kLaneDims;
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j) {
+      if (c16 < g)
+        qop[j] = __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4 *>(qb)[j]);
+      else
+        qop[j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    }
+  }
+  float cscale = p.score_scale;
+  if (FP8) cscale *= p.k_scale[b * Hk + kvh];
+
+  // identity / selection operands of the V transposition
+  const short one_bf16 = 0x3F80;
+  s16x4_t ident;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
+  long sel[2] = {0, 0};
+  if (FP8) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint64_t s = 0;
+      if (q4 == (c16 >> 2)) s = (uint64_t)0x38 << (8 * (4 * hh + (c16 & 3)));
+      sel[hh] = (long)s;
+    }
+  }
+
+  // ---- addressing ----
+  const size_t row_bytes = (size_t)Hk * D * S::kBytes; // bytes between consecutive tokens
+  const size_t lane_off = (size_t)kvh * D * S::kBytes + (size_t)q4 * S::kLaneDims * S::kBytes;
+  const char *kbase = reinterpret_cast<const char *>(p.k) + lane_off;
+  const char *vbase = reinterpret_cast<const char *>(p.v) + lane_off;
+  const bool paged = p.page_size > 0;
+  const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
+  const int pshift = p.page_shift;
+  const int pmask = p.page_size - 1;
+
+  auto tile_row_base = [&](int i) -> size_t {
+    const int ts = a0 + (wave + i * kWaves) * kTile; // absolute first token of the tile
+    if (!paged) return (size_t)ts;
+    const int pid = pages[ts >> pshift];
+    return (size_t)pid * p.page_size + (ts & pmask);
+  };
+  auto issue = [&](TileRegs<D, FP8> &t, int i) {
+    const int ic = min(i, my_tiles - 1); // clamp: prefetch past the end re-reads the last tile
+    const int ts = a0 + (wave + ic * kWaves) * kTile;
+    const int tok = ts + c16;
+    const bool valid = (i < my_tiles) && tok >= t_begin && tok < t_end;
+    load_tile<D, FP8>(t, kbase, vbase, (tile_row_base(ic) + c16) * row_bytes, valid);
+  };
+
+  // ---- running state ----
+  float m_run = -INFINITY; // log2 domain, per head c16 (same in the 4 quarters)
+  float l_run = 0.0f;      // partial sum over this lane's tokens
+  f32x4_t oacc[S::kOTiles];
+#pragma unroll
+  for (int w = 0; w < S::kOTiles; ++w) oacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const TileRegs<D, FP8> &t, int i) {
+    const int ts = a0 + (wave + i * kWaves) * kTile;
+    // S^T = K . Q^T
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(t, j), qop[j], s, 0, 0, 0);
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = ts + 4 * q4 + r;
+      sv[r] = (tok >= t_begin && tok < t_end) ? s[r] * cscale : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = xor32_max(xor16_max(mx));
+    const float m_new = fmaxf(m_run, mx);
+    float alpha = 1.0f;
+    float pr[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_new != -INFINITY) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new); // m_run = -inf -> 0
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
+    }
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int w = 0; w < S::kOTiles; ++w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[w][r] *= alpha;
+      }
+    }
+    s16x4_t pt;
+    {
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
+      const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
+      pt[0] = (short)(p01 & 0xFFFF);
+      pt[1] = (short)(p01 >> 16);
+      pt[2] = (short)(p23 & 0xFFFF);
+      pt[3] = (short)(p23 >> 16);
+    }
+    // V^T slices and O^T += V^T . P^T
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) {
+      f32x4_t vt;
+      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FP8) {
+        const int u = w >> 1, hh = w & 1;            // 8-byte group u of the lane slice
+        const uint4 wv = t.v[u >> 1];
+        const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
+        const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
+        const long a = (long)(((uint64_t)hi32 << 32) | lo32);
+        vt = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
+      } else {
+        const uint4 wv = t.v[w >> 1];
+        const uint32_t lo32 = (w & 1) ? wv.z : wv.x;
+        const uint32_t hi32 = (w & 1) ? wv.w : wv.y;
+        s16x4_t a;
+        a[0] = (short)(lo32 & 0xFFFF);
+        a[1] = (short)(lo32 >> 16);
+        a[2] = (short)(hi32 & 0xFFFF);
+        a[3] = (short)(hi32 >> 16);
+        vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+      }
+      const uint32_t v01 = pack_bf16x2(vt[0], vt[1]);
+      const uint32_t v23 = pack_bf16x2(vt[2], vt[3]);
+      s16x4_t va;
+      va[0] = (short)(v01 & 0xFFFF);
+      va[1] = (short)(v01 >> 16);
+      va[2] = (short)(v23 & 0xFFFF);
+      va[3] = (short)(v23 >> 16);
+      oacc[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pt, oacc[w], 0, 0, 0);
+    }
+  };
+
+  if (my_tiles > 0) {
+    TileRegs<D, FP8> buf[NBUF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) issue(buf[j], j);
+    for (int it = 0; it < my_tiles; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int i = it + j;
+        if (i < my_tiles) {
+          issue(buf[(j + PF) % NBUF], i + PF);
+          compute(buf[j], i);
+        }
+      }
+    }
+  }
+
+  // ---- per-wave state to LDS ----
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (c16 < g) {
+    if (q4 == 0) {
+      sm_m[wave][c16] = m_run;
+      sm_l[wave][c16] = l_tot;
+    }
+    float *dst = sm_o + (wave * 16 + c16) * OSTRIDE + q4 * S::kLaneDims;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w)
+      *reinterpret_cast<float4 *>(dst + 4 * w) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+  }
+  __syncthreads();
+  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, item, nb);
+}
+
+} // namespace
+
+template <int D, bool FP8>
+static hipError_t launch_mfma_d(const Params &p, hipStream_t stream) {
+  constexpr int PF = FP8 ? 3 : 2;
+  dim3 grid(p.items, p.num_kv_heads);
+  hipLaunchKernelGGL((partial_mfma_kernel<D, FP8, PF>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStream_t stream) {
+  switch (head_dim) {
+  case 64: return fp8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
+  case 128: return fp8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
+  case 256: return fp8 ? launch_mfma_d<256, true>(p, stream) : launch_mfma_d<256, false>(p, stream);
+  default: return hipErrorInvalidValue;
+  }
+}
+
+} // namespace kvs

@@ -1,0 +1,166 @@
+// Device-side pieces shared by the split-KV decode kernels (gfx950).
+//
+// Work decomposition.  The visible keys of request b start at
+// lo_b = max(0, L_b - window) (window > 0) and end at L_b.  Tokens are grouped
+// in tiles of 16 aligned to absolute token positions; the chunks of a request
+// start at A_b = lo_b rounded down to 16 and are kv_chunk tokens long (a
+// multiple of 16), so request b has n_b = max(1, ceil((L_b - A_b) / kv_chunk))
+// splits.  Work items of one KV head are numbered request by request; grid.x
+// runs over them and grid.y over KV heads.  Both kernels derive (request,
+// split) from kv_len on the device, so no work list crosses the PCIe bus.
+//
+// Partial results of split x (numbered within KV head kvh) live in the
+// workspace: o_part[((kvh * I + x) * g + h) * D + d] (fp32, already divided by
+// the chunk's sum and multiplied by the V scale) and lse_part[(kvh * I + x) *
+// g + h] (log2 domain: chunk max + log2(chunk sum), -inf when the chunk saw no
+// key), I = items per KV head.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+constexpr int kTile = 16;        // tokens per tile
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+struct Params {
+  const void *q;
+  const void *k;
+  const void *v;
+  const int *page_indptr;
+  const int *page_indices;
+  const int *kv_len;
+  const float *k_scale;
+  const float *v_scale;
+  void *o;
+  float *lse;
+  float *o_part;
+  float *lse_part;
+  int batch;
+  int num_qo_heads;
+  int num_kv_heads;
+  int group;
+  int page_size;  // 0: contiguous
+  int page_shift; // log2(page_size) when a power of two, else -1
+  int window;
+  int chunk;
+  int items;      // work items per KV head
+  int out_bf16;   // o (and q) stored as bf16
+  float score_scale; // sm_scale * log2(e)
+};
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ int visible_lo(int L, int window) {
+  return window > 0 ? max(0, L - window) : 0;
+}
+
+// Number of splits of a request with L keys.
+__device__ __forceinline__ int num_splits(int L, int window, int chunk) {
+  const int a = visible_lo(L, window) & ~(kTile - 1);
+  const int span = L - a;
+  return span <= 0 ? 1 : (span + chunk - 1) / chunk;
+}
+
+// Exclusive scan of per-request split counts over the whole batch, done by one
+// 256-thread workgroup.  Calls f(b, first_item, n_b) for every request b whose
+// range may interest the caller; returns nothing.  `scratch` holds 2 * 64 ints.
+template <typename F>
+__device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &&f) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int base = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+    const int b = b0 + tid;
+    const int nb = b < p.batch ? num_splits(p.kv_len[b], p.window, p.chunk) : 0;
+    // inclusive wave scan
+    int incl = nb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) scratch[wave] = incl;
+    __syncthreads();
+    int wave_base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = scratch[w];
+      wave_base += (w < wave) ? t : 0;
+      total += t;
+    }
+    if (b < p.batch) f(b, base + wave_base + incl - nb, nb);
+    base += total;
+    __syncthreads();
+  }
+}
+
+// Merge the per-wave softmax states staged in LDS and write either the final
+// output (request with one split) or the split's partial.
+//   sm_m[w][h], sm_l[w][h]: running max (log2 domain) and sum of wave w;
+//   sm_o[w][h][d]: unnormalised accumulator of wave w (fp32).
+template <int D, int OSTRIDE>
+__device__ __forceinline__ void merge_waves_and_store(const Params &p, const float (*sm_m)[16],
+                                                      const float (*sm_l)[16], const float *sm_o,
+                                                      int b, int kvh, int item, int nb) {
+  const int g = p.group;
+  const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + kvh] : 1.0f;
+  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float val = 0.0f, lse2 = -INFINITY;
+    if (M != -INFINITY) {
+      float L = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][h];
+        const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        L += a * sm_l[w][h];
+        acc += a * sm_o[(w * 16 + h) * OSTRIDE + d];
+      }
+      val = acc / L * vscale;
+      lse2 = M + __log2f(L);
+    }
+    const int hq = kvh * g + h;
+    if (nb == 1) {
+      const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
+      if (p.out_bf16)
+        reinterpret_cast<uint16_t *>(p.o)[off] = f32_to_bf16_bits(val);
+      else
+        reinterpret_cast<float *>(p.o)[off] = val;
+      if (d == 0 && p.lse) p.lse[(size_t)b * p.num_qo_heads + hq] = lse2 * kLn2;
+    } else {
+      const size_t slot = (size_t)kvh * p.items + item;
+      p.o_part[(slot * g + h) * D + d] = val;
+      if (d == 0) p.lse_part[slot * g + h] = lse2;
+    }
+  }
+}
+
+} // namespace kvs

@@ -1,0 +1,36 @@
+// Host-side planning of a split-KV decode call: chunk size and launch shape.
+// Pure C++; no HIP calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+struct Plan {
+  int chunk = 0;        // tokens per split (multiple of 16)
+  int items = 0;        // work items per KV head (sum of splits)
+  int max_splits = 0;
+  bool needs_merge = false;
+  size_t o_part_bytes = 0;
+  size_t lse_part_bytes = 0;
+  size_t workspace_bytes = 0;
+};
+
+// Split-count heuristic.  The pages motivate choosing the decode dataflow
+// from input length, batch size and the GPU's resources (FlashDecoding++
+// explainer, section "hardware-aware heuristic dataflow"), and blame idle
+// compute units at small batch (section "problem").  Here: aim for about
+// kItemsPerCu work items per compute unit over all KV heads so every CU has
+// several chunks to stream, but never cut chunks below kMinChunk tokens,
+// where per-chunk fixed costs (partial write + read, workgroup start-up)
+// stop being small against the chunk's K/V bytes.
+constexpr int kItemsPerCu = 8;
+constexpr int kMinChunk = 512;
+constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
+
+// kv_len: host lengths [batch]; returns false if a length is negative.
+bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, int group, int head_dim,
+               int forced_chunk, int num_cus, Plan *out);
+
+} // namespace kvs

@@ -1,0 +1,161 @@
+/*
+ * kvsplit: split-KV single-query decode attention for AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operation (one decode step of one attention layer).  For request b,
+ * query head h and its KV head kh = h / (num_qo_heads / num_kv_heads):
+ *
+ *   visible keys   J = { t : lo <= t < L },  L = kv_len[b],
+ *                  lo = max(0, L - window) if window > 0 else 0
+ *   scores         s_t = sm_scale * <q[b,h,:], K[b,t,kh,:]>      (t in J)
+ *   lse[b,h]       = ln sum_{t in J} exp(s_t)                     (natural log)
+ *   o[b,h,:]       = sum_{t in J} exp(s_t - lse[b,h]) * V[b,t,kh,:]
+ *   J empty        o = 0, lse = -inf
+ *
+ * Sources, by page and section:
+ *   - scaled scores, softmax, weighted sum of V: "Forcing Flash Attention onto
+ *     TPU" (Hacker News translation on socker-news), section "standard causal
+ *     attention", with one query row and no causal mask;
+ *   - one new query against the growing K/V cache, paged KV cache, fp8 KV
+ *     cache: "Beyond the Memory Wall" (tiptinker.com), section "2. FlashInfer";
+ *   - single-request decode with GQA, a scratch buffer and sentinel values for
+ *     optional arguments: the FlashInfer-from-JAX tutorial page (upppp.jp),
+ *     section on the three kernels (single_decode);
+ *   - local (sliding-window) layers: same page, Gemma 3 section;
+ *   - splitting the keys into chunks whose partial softmax results are merged
+ *     afterwards: the FlashDecoding++ explainer (abeam.tech), sections
+ *     "problem" and "asynchronous softmax and unified max value"; the merge
+ *     rescales each chunk by exp(chunk max - global max), the same update as
+ *     the online softmax of the TPU page's "Flash Attention in JAX" section.
+ *
+ * Computation: the visible keys of each (request, KV head) are cut into
+ * chunks of kv_chunk tokens; one workgroup computes the partial softmax of a
+ * chunk (fp32 running max / sum / accumulator) for all query heads of the
+ * group; a second kernel merges the chunks of each request by log-sum-exp.
+ * A request whose keys fit in one chunk is written directly by the first
+ * kernel.
+ *
+ * Threading / streams: every call is asynchronous on the given stream and
+ * never synchronises.  The library keeps no pointer after returning and
+ * allocates no device memory.  Calls that may run concurrently (different
+ * streams) need different workspaces.
+ */
+#ifndef KVSPLIT_H
+#define KVSPLIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVS_ABI_VERSION 1
+
+/* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
+ * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
+typedef enum {
+  KVS_OK = 0,
+  KVS_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
+  KVS_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
+  KVS_ERR_WORKSPACE = -3,   /* workspace null, too small or misaligned */
+  KVS_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+} kvs_status;
+
+/* Element types.  q and o share q_dtype; K and V share kv_dtype.
+ * Supported (q_dtype, kv_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * FP8_E4M3 is the OCP E4M3 ("fn") format: bias 7, max 448, NaN = S.1111.111. */
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_FP8_E4M3 = 2 } kvs_dtype;
+
+/* Kernel family for the per-chunk partial softmax.  AUTO picks MFMA for bf16
+ * and fp8 KV (query group packed into the rows of 16x16 matrix tiles) and
+ * VALU for fp32 KV (one KV row per 4..64 lanes, fp32 FMA). */
+typedef enum { KVS_ALGO_AUTO = 0, KVS_ALGO_VALU = 1, KVS_ALGO_MFMA = 2 } kvs_algo;
+
+typedef struct {
+  /* shape */
+  int32_t batch;        /* >= 1; must be 1 for a contiguous cache */
+  int32_t num_qo_heads; /* >= 1 */
+  int32_t num_kv_heads; /* >= 1, divides num_qo_heads; group = Hq / Hk <= 16 */
+  int32_t head_dim;     /* 64, 128 or 256 */
+  int32_t q_dtype;      /* kvs_dtype of q and o */
+  int32_t kv_dtype;     /* kvs_dtype of K and V */
+  int32_t page_size;    /* 0: contiguous K, V [kv_len, Hk, head_dim];
+                           > 0: paged pools [num_pages, page_size, Hk, head_dim] */
+  int32_t num_pages;    /* paged: number of pages in each pool (for validation of
+                           the host-side lengths only; page ids are not checked) */
+
+  /* device inputs (caller-owned, row-major, dense) */
+  const void *q;               /* [batch, Hq, head_dim], q_dtype */
+  const void *k;               /* cache pool, kv_dtype */
+  const void *v;               /* cache pool, kv_dtype, same layout as k */
+  const int32_t *page_indptr;  /* paged: [batch + 1]; pages of request b are
+                                  page_indices[page_indptr[b] .. page_indptr[b+1]) */
+  const int32_t *page_indices; /* paged: page ids, logical order within a request */
+  const int32_t *kv_len;       /* [batch] tokens in the cache of each request
+                                  (the current token included) */
+  const int32_t *kv_len_host;  /* host copy of kv_len, used to plan the launch;
+                                  must equal kv_len */
+  const float *k_scale;        /* FP8 only: [batch, Hk] dequantisation scale of K */
+  const float *v_scale;        /* FP8 only: [batch, Hk] dequantisation scale of V */
+
+  /* scalars */
+  float sm_scale;     /* > 0 and finite, multiplies <q, k> */
+  int32_t window;     /* -1: no window; W > 0: attend to the last W keys */
+  int32_t kv_chunk;   /* 0: heuristic; > 0: tokens per split, rounded up to 16 */
+  int32_t algo;       /* kvs_algo */
+  int32_t num_cus;    /* 0: ask the current device; > 0: plan for this many CUs */
+
+  /* device outputs (caller-owned) */
+  void *o;    /* [batch, Hq, head_dim], q_dtype, round to nearest even */
+  float *lse; /* [batch, Hq] natural-log LSE of the scaled scores, or NULL */
+
+  /* optional profiling: two hipEvent_t recorded on the stream right before
+   * and right after the partial-softmax kernel; NULL to skip */
+  void *prof_events[2];
+} kvs_decode_args;
+
+/* What a call will launch, computed on the host from kv_len_host. */
+typedef struct {
+  int32_t kv_chunk;          /* tokens per split */
+  int32_t items_per_kv_head; /* sum over requests of splits; grid.x of the partial kernel */
+  int32_t max_splits;        /* largest number of splits of one request */
+  int32_t needs_merge;       /* 1 if some request has more than one split */
+  int32_t algo;              /* resolved kvs_algo (VALU or MFMA) */
+  int32_t num_cus;           /* CU count the plan was made for */
+  size_t workspace_bytes;    /* bytes kvs_decode needs for this plan */
+} kvs_plan_info;
+
+/* Plan a call without launching anything.  Makes no HIP call when
+ * args->num_cus > 0.  Validates the arguments like kvs_decode (except that
+ * device pointers may be NULL) and fills *out. */
+kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out);
+
+/* Workspace bytes kvs_decode needs for these arguments (0 on invalid
+ * arguments).  Same HIP-call rule as kvs_decode_plan. */
+size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
+
+/* Run one decode-attention step asynchronously on `stream`.
+ * workspace: device memory, 256-byte aligned, at least
+ * kvs_decode_workspace_bytes(args) bytes; holds the per-split partial
+ * outputs (fp32) and their log-sum-exp values.  It needs no initialisation.
+ * Preconditions that are not checked (they would need a device sync):
+ * kv_len equals kv_len_host, page_indptr[b+1] - page_indptr[b] >=
+ * ceil(kv_len[b] / page_size), every page id is < num_pages, and all
+ * visible K/V values are finite. */
+kvs_status kvs_decode(const kvs_decode_args *args, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Static description of a status code. */
+const char *kvs_status_string(int status);
+
+/* KVS_ABI_VERSION of the built library. */
+int kvs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSPLIT_H */
