@@ -82,6 +82,27 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+def probe_read_gbs(nbytes: int = 4 << 30, reps: int = 10) -> float:
+    """Achievable streaming-read bandwidth of this GPU (kvs_probe_stream_read)."""
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert kvs.kvs_probe_stream_read(buf.data_ptr(), nbytes, 0, stream) == 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        assert kvs.kvs_probe_stream_read(buf.data_ptr(), nbytes, 0, stream) == 0
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del buf
+    torch.cuda.empty_cache()
+    return nbytes / dt / 1e9
+
+
 def cpu_baseline(inp, budget_s: float = 15.0):
     """The fp64 oracle as it stands, on a bounded sample of the same workload:
     whole requests in order until the time budget is spent."""
@@ -199,6 +220,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "algorithmic_bytes": nbytes,
         },
         "device": {"name": props.name, "cus": props.multi_processor_count, "host": platform.node()},
+        "probe_stream_read_GBs": round(probe_read_gbs(), 1),
         "input_gen_s": round(t_gen, 1),
     }
     if with_cpu:

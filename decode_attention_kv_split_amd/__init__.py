@@ -29,6 +29,7 @@ __all__ = [
     "KvsDecodeArgs", "KvsPlanInfo", "KvsError",
     "library_path", "load_library",
     "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_status_string", "kvs_abi_version",
+    "kvs_probe_stream_read", "kvs_probe_copy",
     "decode", "single_decode", "batch_decode_paged",
 ]
 
@@ -117,6 +118,11 @@ def load_library():
             lib.kvs_status_string.argtypes = [ctypes.c_int]
             lib.kvs_abi_version.restype = ctypes.c_int
             lib.kvs_abi_version.argtypes = []
+            lib.kvs_probe_stream_read.restype = ctypes.c_int
+            lib.kvs_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+            lib.kvs_probe_copy.restype = ctypes.c_int
+            lib.kvs_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
             _lib = lib
     return _lib
 
@@ -148,6 +154,17 @@ def kvs_status_string(status: int) -> str:
 
 def kvs_abi_version() -> int:
     return int(load_library().kvs_abi_version())
+
+
+def kvs_probe_stream_read(buf_ptr: int, nbytes: int, sink_ptr: int, stream: int) -> int:
+    return int(load_library().kvs_probe_stream_read(ctypes.c_void_p(buf_ptr), ctypes.c_size_t(nbytes),
+                                                    ctypes.c_void_p(sink_ptr or None),
+                                                    ctypes.c_void_p(stream or None)))
+
+
+def kvs_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream: int) -> int:
+    return int(load_library().kvs_probe_copy(ctypes.c_void_p(dst_ptr), ctypes.c_void_p(src_ptr),
+                                             ctypes.c_size_t(nbytes), ctypes.c_void_p(stream or None)))
 
 
 # ----------------------------------------------------------------------------

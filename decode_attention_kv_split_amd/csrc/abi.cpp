@@ -36,6 +36,8 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) return KVS_ERR_UNSUPPORTED;
   const int group = a->num_qo_heads / a->num_kv_heads;
   if (group > 16) return KVS_ERR_UNSUPPORTED;
+  // 16 rows of one KV head must be addressable with 32-bit byte offsets
+  if ((int64_t)a->num_kv_heads * a->head_dim * 4 * 16 >= ((int64_t)1 << 31)) return KVS_ERR_UNSUPPORTED;
   const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
@@ -164,6 +166,9 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.lse_part = pl.workspace_bytes
                    ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.o_part_bytes)
                    : nullptr;
+  p.meta = pl.workspace_bytes ? reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + pl.o_part_bytes +
+                                                        pl.lse_part_bytes)
+                              : nullptr;
   p.batch = a->batch;
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;

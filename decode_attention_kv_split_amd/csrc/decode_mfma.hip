@@ -5,10 +5,12 @@
 // GQA group share every K/V byte the wave loads.
 //
 // Per 16-token tile, with lane = 16 * q4 + c16:
-//   * loads: lane reads token c16 of the tile, dims [q4*D/4, (q4+1)*D/4) of
-//     its K and V rows (contiguous 16-byte loads; the 16 lanes of a quarter
-//     cover 16 rows).  That is already the operand layout of a matrix tile
-//     whose rows are tokens and whose reduction index is the head dimension.
+//   * loads: lane reads token c16 of the tile, the 16-byte pieces 4*pc + q4
+//     (pc = 0, 1, ...) of its K and V rows, so the four lanes of a token read
+//     64 contiguous bytes per load instruction.  That is already the operand
+//     layout of a matrix tile whose rows are tokens and whose reduction index
+//     is the head dimension (any fixed order of the head dimension works as
+//     long as Q uses the same order).
 //   * scores S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_bf16
 //     (fp8 K converted to bf16 first, exactly); lane ends up with tokens
 //     4*q4 + r (r = 0..3) of query head c16.
@@ -20,8 +22,8 @@
 //     dimension in lane c16 -- the operand layout the next product needs --
 //     and, for fp8, decodes the codes exactly into fp32.
 //   * O^T[dim][head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane keeps
-//     dims q4*D/4 + 4*w + r (w = 0..D/16-1) of query head c16, so the running
-//     max, sum and rescale of a head never leave its lane.
+//     four consecutive dims per 16-dim slice w (see out_dim) of query head
+//     c16, so the running max, sum and rescale of a head never leave its lane.
 // The first product, the online update and the rescaled accumulation follow
 // the tiled online softmax of "Forcing Flash Attention onto TPU", section
 // "Flash Attention in JAX"; chunk results are merged by log-sum-exp (FlashDecoding++
@@ -39,8 +41,14 @@ struct Shape {
   static constexpr int kLaneVec = kLaneDims * kBytes / 16; // uint4 per lane per row
   static constexpr int kKSteps = D / 32;                   // 16x16x32 products for S^T
   static constexpr int kOTiles = D / 16;                   // 16-dim slices of O^T
+  static constexpr int kEpp = 16 / kBytes;                 // elements per 16-byte piece
   static_assert(kLaneVec >= 1, "row slice must hold at least 16 bytes");
 };
+
+// Word 3 of a raw buffer descriptor on CDNA (gfx9 family): 32-bit data format,
+// no swizzling; with stride 0 the size field is a byte count and lanes whose
+// offset falls outside it read zero.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D, bool FP8>
 struct TileRegs {
@@ -66,6 +74,23 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// First head dimension of the 8 that lane (q4) feeds to the S^T product in
+// k-step j (16x16x32: 8 reduction indices per lane).
+template <int D, bool FP8>
+__device__ __forceinline__ int k_dim(int j, int q4) {
+  if constexpr (FP8)
+    return 16 * (4 * (j >> 1) + q4) + 8 * (j & 1);
+  else
+    return 8 * (4 * j + q4);
+}
+
+// First of the four consecutive head dimensions lane (q4) holds in O^T slice w.
+template <int D, bool FP8>
+__device__ __forceinline__ int out_dim(int w, int q4) {
+  constexpr int per_piece = Shape<D, FP8>::kEpp / 4; // slices per 16-byte piece
+  return (4 * (w / per_piece) + q4) * Shape<D, FP8>::kEpp + 4 * (w % per_piece);
+}
+
 template <int D, bool FP8>
 __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<D, FP8> &t, int j) {
   if constexpr (FP8) {
@@ -73,26 +98,6 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<D, FP8> &t, int j) 
     return (j & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
   } else {
     return __builtin_bit_cast(bf16x8_t, t.k[j]);
-  }
-}
-
-template <int D, bool FP8>
-__device__ __forceinline__ void load_tile(TileRegs<D, FP8> &t, const char *kbase, const char *vbase,
-                                          size_t row_off_bytes, bool valid) {
-  using S = Shape<D, FP8>;
-  if (valid) {
-    const uint4 *kp = reinterpret_cast<const uint4 *>(kbase + row_off_bytes);
-    const uint4 *vp = reinterpret_cast<const uint4 *>(vbase + row_off_bytes);
-#pragma unroll
-    for (int i = 0; i < S::kLaneVec; ++i) t.k[i] = kp[i];
-#pragma unroll
-    for (int i = 0; i < S::kLaneVec; ++i) t.v[i] = vp[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < S::kLaneVec; ++i) {
-      t.k[i] = make_uint4(0, 0, 0, 0);
-      t.v[i] = make_uint4(0, 0, 0, 0);
-    }
   }
 }
 
@@ -125,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
       s_item[0] = b;
       s_item[1] = item - first;
       s_item[2] = nb;
+      s_item[3] = first;
     }
   });
   __syncthreads();
@@ -132,6 +138,10 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
   const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
   if (b < 0) return; // kv_len on the device disagrees with the planned launch
+  if (p.meta && split == 0 && kvh == 0 && tid == 0) {
+    p.meta[2 * b] = s_item[3];
+    p.meta[2 * b + 1] = nb;
+  }
 
   const int L = p.kv_len[b];
   const int lo = visible_lo(L, p.window);
@@ -145,11 +155,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   bf16x8_t qop[S::kKSteps];
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) +
-                         ((size_t)b * p.num_qo_heads + (size_t)kvh * g + c16) * D + q4 * S::kLaneDims;
+                         ((size_t)b * p.num_qo_heads + (size_t)kvh * g + c16) * D;
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j) {
       if (c16 < g)
-        qop[j] = __builtin_bit_cast(bf16x8_t, reinterpret_cast<const uint4 *>(qb)[j]);
+        qop[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + k_dim<D, FP8>(j, q4)));
       else
         qop[j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     }
@@ -174,26 +184,52 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
 
   // ---- addressing ----
   const size_t row_bytes = (size_t)Hk * D * S::kBytes; // bytes between consecutive tokens
-  const size_t lane_off = (size_t)kvh * D * S::kBytes + (size_t)q4 * S::kLaneDims * S::kBytes;
-  const char *kbase = reinterpret_cast<const char *>(p.k) + lane_off;
-  const char *vbase = reinterpret_cast<const char *>(p.v) + lane_off;
+  const size_t lane_off = (size_t)kvh * D * S::kBytes + (size_t)q4 * 16;
   const bool paged = p.page_size > 0;
   const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
   const int pshift = p.page_shift;
   const int pmask = p.page_size - 1;
 
-  auto tile_row_base = [&](int i) -> size_t {
-    const int ts = a0 + (wave + i * kWaves) * kTile; // absolute first token of the tile
-    if (!paged) return (size_t)ts;
-    const int pid = pages[ts >> pshift];
-    return (size_t)pid * p.page_size + (ts & pmask);
-  };
+  // Page ids of this wave's tiles, one per lane (lane i: tile i).  A wave owns
+  // at most 64 tiles because chunks are capped at 64 * kWaves * kTile tokens,
+  // so the main loop reads page ids with v_readlane and never waits on memory
+  // for an address.
+  int vpage = 0;
+  if (paged && my_tiles > 0) {
+    const int ic = min(lane, my_tiles - 1);
+    vpage = pages[(a0 + (wave + ic * kWaves) * kTile) >> pshift];
+  }
+  // K/V tiles are read with raw buffer loads through a per-tile descriptor
+  // built in scalar registers: base = the tile's first row, size = the rows
+  // that hold keys of this chunk.  Rows past the chunk end and whole tiles
+  // past the wave's last tile (prefetch overrun) fall outside the descriptor
+  // and read as zero without touching memory, so the prefetch ring needs no
+  // branches and no per-lane address arithmetic.
+  const int lane_voff = c16 * (int)row_bytes + (int)lane_off; // < 2^31: asserted on the host
+  const char *kpool = reinterpret_cast<const char *>(p.k);
+  const char *vpool = reinterpret_cast<const char *>(p.v);
   auto issue = [&](TileRegs<D, FP8> &t, int i) {
-    const int ic = min(i, my_tiles - 1); // clamp: prefetch past the end re-reads the last tile
-    const int ts = a0 + (wave + ic * kWaves) * kTile;
-    const int tok = ts + c16;
-    const bool valid = (i < my_tiles) && tok >= t_begin && tok < t_end;
-    load_tile<D, FP8>(t, kbase, vbase, (tile_row_base(ic) + c16) * row_bytes, valid);
+    const int ts = a0 + (wave + i * kWaves) * kTile;
+    const int nrows = i < my_tiles ? min(kTile, t_end - ts) : 0;
+    size_t row0;
+    if (paged) {
+      const int pid = __builtin_amdgcn_readlane(vpage, min(i, 63));
+      row0 = (size_t)pid * p.page_size + (ts & pmask);
+    } else {
+      row0 = (size_t)ts;
+    }
+    const size_t base = i < my_tiles ? row0 * row_bytes : 0;
+    const int nbytes = nrows * (int)row_bytes;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
+#pragma unroll
+    for (int k = 0; k < S::kLaneVec; ++k)
+      t.k[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lane_voff + 64 * k, 0, 0));
+#pragma unroll
+    for (int k = 0; k < S::kLaneVec; ++k)
+      t.v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lane_voff + 64 * k, 0, 0));
   };
 
   // ---- running state ----
@@ -203,8 +239,14 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w) oacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const TileRegs<D, FP8> &t, int i) {
+  auto compute = [&](TileRegs<D, FP8> t, int i) {
     const int ts = a0 + (wave + i * kWaves) * kTile;
+    if (ts < t_begin) { // rows before the window / chunk start hold keys of no interest
+      const bool ok = ts + c16 >= t_begin;
+#pragma unroll
+      for (int k = 0; k < S::kLaneVec; ++k)
+        if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+    }
     // S^T = K . Q^T
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -283,14 +325,13 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
     TileRegs<D, FP8> buf[NBUF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) issue(buf[j], j);
-    for (int it = 0; it < my_tiles; it += NBUF) {
+    const int n_iter = (my_tiles + NBUF - 1) / NBUF * NBUF;
+    for (int it = 0; it < n_iter; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
         const int i = it + j;
-        if (i < my_tiles) {
-          issue(buf[(j + PF) % NBUF], i + PF);
-          compute(buf[j], i);
-        }
+        issue(buf[(j + PF) % NBUF], i + PF);
+        if (i < my_tiles) compute(buf[j], i);
       }
     }
   }
@@ -303,10 +344,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
       sm_m[wave][c16] = m_run;
       sm_l[wave][c16] = l_tot;
     }
-    float *dst = sm_o + (wave * 16 + c16) * OSTRIDE + q4 * S::kLaneDims;
+    float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w)
-      *reinterpret_cast<float4 *>(dst + 4 * w) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+      *reinterpret_cast<float4 *>(dst + out_dim<D, FP8>(w, q4)) =
+          make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
   }
   __syncthreads();
   merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, item, nb);

@@ -9,6 +9,10 @@
 // runs over them and grid.y over KV heads.  Both kernels derive (request,
 // split) from kv_len on the device, so no work list crosses the PCIe bus.
 //
+// The workgroup that runs split 0 of KV head 0 of a request records the
+// request's first work item and split count in meta[2b], meta[2b+1]; the merge
+// kernel reads them instead of scanning the batch again.
+//
 // Partial results of split x (numbered within KV head kvh) live in the
 // workspace: o_part[((kvh * I + x) * g + h) * D + d] (fp32, already divided by
 // the chunk's sum and multiplied by the V scale) and lse_part[(kvh * I + x) *
@@ -42,6 +46,7 @@ struct Params {
   float *lse;
   float *o_part;
   float *lse_part;
+  int *meta;       // [batch][2]: first work item and split count of each request
   int batch;
   int num_qo_heads;
   int num_kv_heads;

@@ -26,7 +26,7 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
     chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
     chunk = std::max<int64_t>(chunk, kMinChunk);
   }
-  chunk = std::min<int64_t>(chunk, (int64_t)1 << 30);
+  chunk = std::min<int64_t>(chunk, kMaxChunk);
   pl.chunk = (int)chunk;
   int64_t items = 0;
   int max_splits = 0;
@@ -46,8 +46,9 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
     const size_t slots = (size_t)items * num_kv_heads * group;
     pl.o_part_bytes = align256(slots * head_dim * sizeof(float));
     pl.lse_part_bytes = align256(slots * sizeof(float));
+    pl.meta_bytes = align256((size_t)batch * 2 * sizeof(int));
   }
-  pl.workspace_bytes = pl.o_part_bytes + pl.lse_part_bytes;
+  pl.workspace_bytes = pl.o_part_bytes + pl.lse_part_bytes + pl.meta_bytes;
   *out = pl;
   return true;
 }

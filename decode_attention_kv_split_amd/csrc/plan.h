@@ -14,6 +14,7 @@ struct Plan {
   bool needs_merge = false;
   size_t o_part_bytes = 0;
   size_t lse_part_bytes = 0;
+  size_t meta_bytes = 0;
   size_t workspace_bytes = 0;
 };
 
@@ -22,12 +23,14 @@ struct Plan {
 // explainer, section "hardware-aware heuristic dataflow"), and blame idle
 // compute units at small batch (section "problem").  Here: aim for about
 // kItemsPerCu work items per compute unit over all KV heads so every CU has
-// several chunks to stream, but never cut chunks below kMinChunk tokens,
-// where per-chunk fixed costs (partial write + read, workgroup start-up)
-// stop being small against the chunk's K/V bytes.
+// several chunks to stream; small problems get chunks down to kMinChunk
+// tokens (one tile per wave) so that they still spread over many CUs.
 constexpr int kItemsPerCu = 8;
-constexpr int kMinChunk = 512;
+constexpr int kMinChunk = 64;
 constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
+// Largest chunk: 64 tiles of 16 tokens per wave (a wave keeps the page ids of
+// its tiles in one register, one per lane).
+constexpr int kMaxChunk = 4096;
 
 // kv_len: host lengths [batch]; returns false if a length is negative.
 bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, int group, int head_dim,

@@ -104,7 +104,8 @@ typedef struct {
   /* scalars */
   float sm_scale;     /* > 0 and finite, multiplies <q, k> */
   int32_t window;     /* -1: no window; W > 0: attend to the last W keys */
-  int32_t kv_chunk;   /* 0: heuristic; > 0: tokens per split, rounded up to 16 */
+  int32_t kv_chunk;   /* 0: heuristic; > 0: tokens per split, rounded up to a
+                         multiple of 16 and capped at 4096 */
   int32_t algo;       /* kvs_algo */
   int32_t num_cus;    /* 0: ask the current device; > 0: plan for this many CUs */
 
@@ -153,6 +154,16 @@ const char *kvs_status_string(int status);
 
 /* KVS_ABI_VERSION of the built library. */
 int kvs_abi_version(void);
+
+/* Measurement helpers (not part of the attention computation).
+ * kvs_probe_stream_read streams `bytes` (multiple of 16, 16-byte aligned
+ * buffer) from device memory with 16-byte loads: the achievable read
+ * bandwidth of the GPU.  `sink`: device buffer of >= 1024 uint32, or NULL.
+ * kvs_probe_copy copies `bytes` between two non-overlapping 16-byte aligned
+ * device buffers; its known traffic calibrates hardware byte counters.
+ * Both are asynchronous on `stream` and return 0 or a hipError_t code. */
+int kvs_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+int kvs_probe_copy(void *dst, const void *src, size_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -233,3 +233,19 @@ def test_lse_output_optional_and_stream():
     o_ref, lse_ref = oracle.decode_reference(inp)
     o = keep[1].to(torch.float64).cpu().numpy()
     assert np.max(np.abs(o - o_ref)) <= O_TOL["bf16"]
+
+
+def test_bandwidth_probes():
+    print("case probes", flush=True)
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    n = (64 << 20) + 48
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    s = torch.cuda.current_stream().cuda_stream
+    assert kvs.kvs_probe_copy(dst.data_ptr(), src.data_ptr(), n, s) == 0
+    assert kvs.kvs_probe_stream_read(src.data_ptr(), n, 0, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert kvs.kvs_probe_copy(dst.data_ptr(), src.data_ptr(), 17, s) != 0  # not a multiple of 16
