@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/kvsplit.h"
+#include "kvsplit.h"
 #include "kvs_device.h"
 #include "plan.h"
 

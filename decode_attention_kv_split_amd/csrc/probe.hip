@@ -23,10 +23,13 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4 
   const size_t end = min(n16, start + per_block);
   uint32_t x = 0;
   size_t i = start + threadIdx.x;
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
   for (; i + (kProbeUnroll - 1) * kProbeThreads < end; i += kProbeUnroll * kProbeThreads) {
     uint4 v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = buf[i + u * kProbeThreads];
+    for (int u = 0; u < kProbeUnroll; ++u)  // streaming (non-temporal) loads
+      v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                           reinterpret_cast<const u32x4_t *>(buf) + i + u * kProbeThreads));
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
