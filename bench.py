@@ -103,6 +103,27 @@ def probe_read_gbs(nbytes: int = 4 << 30, reps: int = 10) -> float:
     return nbytes / dt / 1e9
 
 
+def probe_copy(nbytes: int, reps: int) -> dict:
+    """kvs_probe_copy over nbytes (read nbytes + write nbytes per launch)."""
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    kvs.load_library()
+    nbytes = nbytes // 16 * 16
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert kvs.kvs_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream) == 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        assert kvs.kvs_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, stream) == 0
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"probe": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "us": round(dt * 1e6, 2),
+            "GBs": round(2 * nbytes / dt / 1e9, 1)}
+
+
 def cpu_baseline(inp, budget_s: float = 15.0):
     """The fp64 oracle as it stands, on a bounded sample of the same workload:
     whole requests in order until the time budget is spent."""
@@ -234,10 +255,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=DEFAULT)
-    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "mfma_packed", "valu"])
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
+                    help="only run kvs_probe_copy of BYTES bytes (hardware byte-counter calibration)")
     args = ap.parse_args()
+    if args.probe_copy:
+        print(json.dumps(probe_copy(args.probe_copy, args.steps)), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(each GPU would run its own requests or KV heads independently).", file=sys.stderr)

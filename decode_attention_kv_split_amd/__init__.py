@@ -26,6 +26,7 @@ from typing import Optional, Tuple
 __all__ = [
     "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
+    "KVS_ALGO_MFMA_PACKED",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsError",
     "library_path", "load_library",
     "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_status_string", "kvs_abi_version",
@@ -35,8 +36,8 @@ __all__ = [
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
-KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA = 0, 1, 2
-_ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA}
+KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
+_ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 

@@ -27,6 +27,10 @@ FLAGS = [
     "-Wno-unused-result",
     # packed fp32 instructions stay off: ordinary fp32 math only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the softmax rescale and the
+    # bf16 packing read them every tile, and AGPR placement cost ~130 extra
+    # register moves per tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -15,6 +15,7 @@ hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStrea
 hipError_t launch_partial_valu(const Params &p, int head_dim, int kv_dtype, hipStream_t stream);
 hipError_t launch_merge(const Params &p, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
+int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack);
 } // namespace kvs
 
 namespace {
@@ -76,8 +77,9 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
       return KVS_ERR_UNSUPPORTED;
     break;
   case KVS_ALGO_MFMA:
+  case KVS_ALGO_MFMA_PACKED:
     if (!mfma_ok) return KVS_ERR_UNSUPPORTED;
-    *algo = KVS_ALGO_MFMA;
+    *algo = a->algo;
     break;
   case KVS_ALGO_VALU:
     if (!valu_ok) return KVS_ERR_UNSUPPORTED;
@@ -173,6 +175,10 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;
   p.group = a->num_qo_heads / a->num_kv_heads;
+  const bool fp8 = a->kv_dtype == KVS_FP8_E4M3;
+  p.pack = algo == KVS_ALGO_VALU ? 1
+                                 : kvs::mfma_pack(a->head_dim, p.group, a->num_kv_heads, fp8,
+                                                  algo == KVS_ALGO_MFMA_PACKED);
   p.page_size = a->page_size;
   p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;
   p.window = a->window;
@@ -185,8 +191,8 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a->prof_events[1]);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return KVS_ERR_HIP;
   hipError_t e;
-  if (algo == KVS_ALGO_MFMA)
-    e = kvs::launch_partial_mfma(p, a->head_dim, a->kv_dtype == KVS_FP8_E4M3, stream);
+  if (algo != KVS_ALGO_VALU)
+    e = kvs::launch_partial_mfma(p, a->head_dim, fp8, stream);
   else
     e = kvs::launch_partial_valu(p, a->head_dim, a->kv_dtype, stream);
   if (e != hipSuccess) return KVS_ERR_HIP;

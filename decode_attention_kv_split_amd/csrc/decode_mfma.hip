@@ -1,29 +1,34 @@
 // Split-KV partial softmax for bf16 / fp8-e4m3 KV on gfx950 matrix cores.
 //
-// One workgroup (4 waves) owns one chunk of one (request, KV head); wave w
-// takes the chunk's 16-token tiles w, w+4, w+8, ...  All query heads of the
-// GQA group share every K/V byte the wave loads.
+// One workgroup (4 waves) owns one chunk of one (request, KV-head pack); wave
+// w takes the chunk's 16-token tiles w, w+4, w+8, ...  A pack is PACK
+// adjacent KV heads (1 or 2) whose PACK * g query heads fill at most the 16
+// columns of a matrix tile; every query head of the pack shares each K/V byte
+// the wave loads, and the pack's row segments are contiguous in memory
+// (token-major layout), so a wave reads PACK * head_dim * bytes contiguous
+// bytes per token.
 //
-// Per 16-token tile, with lane = 16 * q4 + c16:
-//   * loads: lane reads token c16 of the tile, the 16-byte pieces 4*pc + q4
-//     (pc = 0, 1, ...) of its K and V rows, so the four lanes of a token read
-//     64 contiguous bytes per load instruction.  That is already the operand
-//     layout of a matrix tile whose rows are tokens and whose reduction index
-//     is the head dimension (any fixed order of the head dimension works as
-//     long as Q uses the same order).
-//   * scores S^T[token][head] = K . Q^T with v_mfma_f32_16x16x32_bf16
-//     (fp8 K converted to bf16 first, exactly); lane ends up with tokens
-//     4*q4 + r (r = 0..3) of query head c16.
-//   * online softmax per head c16 in the log2 domain: tile max over the 16
+// Per 16-token tile, with lane = 16 * q4 + c16 and DE = PACK * head_dim:
+//   * staging: K and V rows of the tile go from HBM into the wave's LDS slot
+//     with 16-byte DMA loads in cache-line order (non-temporal); lane
+//     (c16, q4) then reads the 16-byte pieces 4*pc + q4 of row c16, which is
+//     the operand layout of a matrix whose rows are tokens and whose
+//     reduction index runs over the pack's head dimensions.
+//   * scores S^T[token][query head] = K . Q^T with v_mfma_f32_16x16x32_bf16
+//     (fp8 K converted to bf16 first, exactly); Q^T is block diagonal, query
+//     head c16 only sees the dims of its own KV head.  Lane ends up with
+//     tokens 4*q4 + r (r = 0..3) of query head c16.
+//   * online softmax per query head in the log2 domain: tile max over the 16
 //     tokens (in-lane over r, then across the four quarters), rescale factor,
 //     weights p = exp2(s - max), running sum.
 //   * V^T: multiplying the V tile by an identity (bf16, 16x16x16) or by a
 //     0/1 selection (fp8, 16x16x32 fp8) puts tokens 4*q4 + r of one head
 //     dimension in lane c16 -- the operand layout the next product needs --
 //     and, for fp8, decodes the codes exactly into fp32.
-//   * O^T[dim][head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane keeps
-//     four consecutive dims per 16-dim slice w (see out_dim) of query head
-//     c16, so the running max, sum and rescale of a head never leave its lane.
+//   * O^T[dim][query head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane
+//     keeps four consecutive dims per 16-dim slice w (see out_dim) of query
+//     head c16, so the running max, sum and rescale of a head never leave its
+//     lane; dims of the other KV head of the pack are dropped at the end.
 // The first product, the online update and the rescaled accumulation follow
 // the tiled online softmax of "Forcing Flash Attention onto TPU", section
 // "Flash Attention in JAX"; chunk results are merged by log-sum-exp (FlashDecoding++
@@ -34,31 +39,40 @@
 namespace kvs {
 namespace {
 
-template <int D, bool FP8>
+template <int DE, bool FP8>
 struct Shape {
   static constexpr int kBytes = FP8 ? 1 : 2;
-  static constexpr int kLaneDims = D / 4;
-  static constexpr int kLaneVec = kLaneDims * kBytes / 16; // uint4 per lane per row
-  static constexpr int kKSteps = D / 32;                   // 16x16x32 products for S^T
-  static constexpr int kOTiles = D / 16;                   // 16-dim slices of O^T
+  static constexpr int kRowBytes = DE * kBytes;            // one token's K (or V) row of the pack
+  static constexpr int kLaneVec = kRowBytes / 64;          // 16-byte pieces per lane per row
+  static constexpr int kKSteps = DE / 32;                  // 16x16x32 products for S^T
+  static constexpr int kOTiles = DE / 16;                  // 16-dim slices of O^T
   static constexpr int kEpp = 16 / kBytes;                 // elements per 16-byte piece
   static_assert(kLaneVec >= 1, "row slice must hold at least 16 bytes");
-  // LDS staging of a 16-token tile of one KV head
-  static constexpr int kRowBytes = D * kBytes;             // one token's K (or V) row of this head
+  // LDS staging of a 16-token tile
   static constexpr int kPieces = kRowBytes / 16;           // 16-byte pieces per row
   static constexpr int kRowsPerDma = 1024 / kRowBytes;     // rows one 64-lane x 16-byte load covers
   static constexpr int kDma = kTile * kRowBytes / 1024;    // loads per tile (K or V)
   static constexpr int kTileBytes = kTile * kRowBytes;     // K (or V) bytes of a tile
   static constexpr int kRowsPerBankPeriod = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
-  // tiles staged per wave: about 16 KB of K+V in LDS per wave, at least two
-  static constexpr int kNBuf = (16384 / (2 * kTileBytes)) < 2 ? 2 : ((16384 / (2 * kTileBytes)) > 8 ? 8 : (16384 / (2 * kTileBytes)));
+  // tiles staged per wave: about 16 KB of K+V in LDS per wave, two to eight
+  static constexpr int kFit = 16384 / (2 * kTileBytes);
+  static constexpr int kNBuf = kFit < 2 ? 2 : (kFit > 8 ? 8 : kFit);
 };
+
+// Word 3 of a raw buffer descriptor on CDNA (gfx9 family): 32-bit data format,
+// no swizzling; with stride 0 the size field is a byte count and lanes whose
+// offset falls outside it read zero.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the K/V loads: non-temporal.  Every K/V byte is read once
+// per call, and streaming loads measured about 10% more HBM bandwidth than
+// default-policy loads on MI355X (6.7 vs 6.0 TB/s on a plain read).
+constexpr int kKvLoadPolicy = 2;
 
 // XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
 // operand reads at the same logical piece land in distinct LDS banks.
-template <int D, bool FP8>
+template <int DE, bool FP8>
 __device__ __forceinline__ int stage_swizzle(int r) {
-  using S = Shape<D, FP8>;
+  using S = Shape<DE, FP8>;
   return (r / S::kRowsPerBankPeriod) & (S::kPieces - 1);
 }
 
@@ -73,15 +87,6 @@ __device__ __forceinline__ void wait_vmem() {
   __asm__ volatile("" ::: "memory");
 }
 
-// Word 3 of a raw buffer descriptor on CDNA (gfx9 family): 32-bit data format,
-// no swizzling; with stride 0 the size field is a byte count and lanes whose
-// offset falls outside it read zero.
-constexpr int kBufferFlags = 0x00020000;
-// Cache policy of the K/V loads: non-temporal.  Every K/V byte is read once
-// per call, and streaming loads measured about 10% more HBM bandwidth than
-// default-policy loads on MI355X (6.7 vs 6.0 TB/s on a plain read).
-constexpr int kKvLoadPolicy = 2;
-
 // One 16-byte-per-lane DMA load from a buffer into LDS: lane i's bytes land
 // at lds + 16 * i.  (Kept out of the kernel body: the host compilation pass
 // must not see the LDS address-space cast.)
@@ -90,10 +95,10 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
                                            kKvLoadPolicy);
 }
 
-template <int D, bool FP8>
+template <int DE, bool FP8>
 struct TileRegs {
-  uint4 k[Shape<D, FP8>::kLaneVec];
-  uint4 v[Shape<D, FP8>::kLaneVec];
+  uint4 k[Shape<DE, FP8>::kLaneVec];
+  uint4 v[Shape<DE, FP8>::kLaneVec];
 };
 
 __device__ __forceinline__ float xor16_max(float x) {
@@ -114,9 +119,9 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// First head dimension of the 8 that lane (q4) feeds to the S^T product in
-// k-step j (16x16x32: 8 reduction indices per lane).
-template <int D, bool FP8>
+// First of the 8 pack dims that lane (q4) feeds to the S^T product in k-step j
+// (16x16x32: 8 reduction indices per lane).
+template <int DE, bool FP8>
 __device__ __forceinline__ int k_dim(int j, int q4) {
   if constexpr (FP8)
     return 16 * (4 * (j >> 1) + q4) + 8 * (j & 1);
@@ -124,15 +129,15 @@ __device__ __forceinline__ int k_dim(int j, int q4) {
     return 8 * (4 * j + q4);
 }
 
-// First of the four consecutive head dimensions lane (q4) holds in O^T slice w.
-template <int D, bool FP8>
+// First of the four consecutive pack dims lane (q4) holds in O^T slice w.
+template <int DE, bool FP8>
 __device__ __forceinline__ int out_dim(int w, int q4) {
-  constexpr int per_piece = Shape<D, FP8>::kEpp / 4; // slices per 16-byte piece
-  return (4 * (w / per_piece) + q4) * Shape<D, FP8>::kEpp + 4 * (w % per_piece);
+  constexpr int per_piece = Shape<DE, FP8>::kEpp / 4; // slices per 16-byte piece
+  return (4 * (w / per_piece) + q4) * Shape<DE, FP8>::kEpp + 4 * (w % per_piece);
 }
 
-template <int D, bool FP8>
-__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<D, FP8> &t, int j) {
+template <int DE, bool FP8>
+__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, FP8> &t, int j) {
   if constexpr (FP8) {
     const uint4 w = t.k[j >> 1];
     return (j & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
@@ -141,9 +146,10 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<D, FP8> &t, int j) 
   }
 }
 
-template <int D, bool FP8, int NBUF>
+template <int D, int PACK, bool FP8, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) {
-  using S = Shape<D, FP8>;
+  constexpr int DE = D * PACK;
+  using S = Shape<DE, FP8>;
   constexpr int PF = NBUF - 1; // tiles in flight while one is computed
   constexpr int OSTRIDE = D + 4;
   constexpr int kStageBytes = kWaves * NBUF * 2 * S::kTileBytes;
@@ -163,10 +169,12 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int kvh = blockIdx.y;
+  const int kvg = blockIdx.y; // KV-head pack: KV heads kvg*PACK .. kvg*PACK+PACK-1
   const int item = blockIdx.x;
   const int g = p.group;
+  const int gp = g * PACK;    // query heads of the pack (<= 16)
   const int Hk = p.num_kv_heads;
+  const int my_kv = c16 / g;  // KV head (within the pack) of query head c16
 
   // ---- which (request, split) is this workgroup? ----
   if (tid == 0) s_item[0] = -1;
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
   const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
   if (b < 0) return; // kv_len on the device disagrees with the planned launch
-  if (p.meta && split == 0 && kvh == 0 && tid == 0) {
+  if (p.meta && split == 0 && kvg == 0 && tid == 0) {
     p.meta[2 * b] = s_item[3];
     p.meta[2 * b + 1] = nb;
   }
@@ -196,21 +204,22 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   const int ntiles = t_end > t_begin ? (t_end - a0 + kTile - 1) / kTile : 0;
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-  // ---- Q^T operand (query head c16 of this group; zero rows beyond the group) ----
+  // ---- Q^T operand: block diagonal over the pack, zero columns past gp ----
   bf16x8_t qop[S::kKSteps];
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) +
-                         ((size_t)b * p.num_qo_heads + (size_t)kvh * g + c16) * D;
+                         ((size_t)b * p.num_qo_heads + (size_t)kvg * gp + c16) * D;
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j) {
-      if (c16 < g)
-        qop[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + k_dim<D, FP8>(j, q4)));
+      const int kd = k_dim<DE, FP8>(j, q4);
+      if (c16 < gp && kd / D == my_kv)
+        qop[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
       else
         qop[j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     }
   }
   float cscale = p.score_scale;
-  if (FP8) cscale *= p.k_scale[b * Hk + kvh];
+  if (FP8) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
 
   // identity / selection operands of the V transposition
   const short one_bf16 = 0x3F80;
@@ -244,21 +253,21 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
     vpage = pages[(a0 + (wave + ic * kWaves) * kTile) >> pshift];
   }
   // K/V tiles go from HBM straight into this wave's LDS slots with 16-byte
-  // DMA loads in cache-line order (each load covers whole rows of the head),
-  // non-temporal, then the operand registers are read from LDS.  The loads
-  // use a per-tile buffer descriptor built in scalar registers: base = the
-  // tile's first row, size = the rows that hold keys of this chunk.  Rows past
-  // the chunk end and whole tiles past the wave's last tile (prefetch overrun)
-  // fall outside the descriptor and land in LDS as zeros without touching
-  // memory, so the prefetch ring needs no branches.
+  // DMA loads in cache-line order (each load covers whole row segments of the
+  // pack), non-temporal, then the operand registers are read from LDS.  The
+  // loads use a per-tile buffer descriptor built in scalar registers: base =
+  // the tile's first row, size = the rows that hold keys of this chunk.  Rows
+  // past the chunk end and whole tiles past the wave's last tile (prefetch
+  // overrun) fall outside the descriptor and land in LDS as zeros without
+  // touching memory, so the prefetch ring needs no branches.
   const char *kpool = reinterpret_cast<const char *>(p.k);
   const char *vpool = reinterpret_cast<const char *>(p.v);
   int dma_voff[S::kDma]; // lane's byte offset within a tile, per DMA load
 #pragma unroll
   for (int k = 0; k < S::kDma; ++k) {
     const int r = k * S::kRowsPerDma + lane / S::kPieces;
-    const int piece = (lane % S::kPieces) ^ stage_swizzle<D, FP8>(r);
-    dma_voff[k] = r * (int)row_bytes + kvh * S::kRowBytes + piece * 16; // < 2^31: checked on the host
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<DE, FP8>(r);
+    dma_voff[k] = r * (int)row_bytes + kvg * S::kRowBytes + piece * 16; // < 2^31: checked on the host
   }
   char *wave_stage = smem + wave * NBUF * 2 * S::kTileBytes;
   auto issue = [&](int i, int slot) {
@@ -280,18 +289,16 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
     char *kst = wave_stage + slot * 2 * S::kTileBytes;
     char *vst = kst + S::kTileBytes;
 #pragma unroll
-    for (int k = 0; k < S::kDma; ++k)
-      dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
 #pragma unroll
-    for (int k = 0; k < S::kDma; ++k)
-      dma16_to_lds(vr, vst + 1024 * k, dma_voff[k]);
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, vst + 1024 * k, dma_voff[k]);
   };
   // operand registers of a staged tile: lane (c16, q4) takes pieces 4*pc + q4
   // of row c16 (the same pieces the operand layout below expects)
-  auto read_stage = [&](TileRegs<D, FP8> &t, int slot) {
+  auto read_stage = [&](TileRegs<DE, FP8> &t, int slot) {
     const char *kst = wave_stage + slot * 2 * S::kTileBytes;
     const char *vst = kst + S::kTileBytes;
-    const int swz = stage_swizzle<D, FP8>(c16);
+    const int swz = stage_swizzle<DE, FP8>(c16);
 #pragma unroll
     for (int pc = 0; pc < S::kLaneVec; ++pc) {
       const int off = c16 * S::kRowBytes + ((4 * pc + q4) ^ swz) * 16;
@@ -301,13 +308,13 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   };
 
   // ---- running state ----
-  float m_run = -INFINITY; // log2 domain, per head c16 (same in the 4 quarters)
+  float m_run = -INFINITY; // log2 domain, per query head c16 (same in the 4 quarters)
   float l_run = 0.0f;      // partial sum over this lane's tokens
   f32x4_t oacc[S::kOTiles];
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w) oacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](TileRegs<D, FP8> t, int i) {
+  auto compute = [&](TileRegs<DE, FP8> t, int i) {
     const int ts = a0 + (wave + i * kWaves) * kTile;
     if (ts < t_begin) { // rows before the window / chunk start hold keys of no interest
       const bool ok = ts + c16 >= t_begin;
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(t, j), qop[j], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, FP8>(t, j), qop[j], s, 0, 0, 0);
     float sv[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -346,22 +353,14 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
         for (int r = 0; r < 4; ++r) oacc[w][r] *= alpha;
       }
     }
-    s16x4_t pt;
-    {
-      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
-      const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
-      pt[0] = (short)(p01 & 0xFFFF);
-      pt[1] = (short)(p01 >> 16);
-      pt[2] = (short)(p23 & 0xFFFF);
-      pt[3] = (short)(p23 >> 16);
-    }
+    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
     // V^T slices and O^T += V^T . P^T
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) {
       f32x4_t vt;
       const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FP8) {
-        const int u = w >> 1, hh = w & 1;            // 8-byte group u of the lane slice
+        const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
         const uint4 wv = t.v[u >> 1];
         const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
         const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
@@ -369,22 +368,10 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
         vt = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
       } else {
         const uint4 wv = t.v[w >> 1];
-        const uint32_t lo32 = (w & 1) ? wv.z : wv.x;
-        const uint32_t hi32 = (w & 1) ? wv.w : wv.y;
-        s16x4_t a;
-        a[0] = (short)(lo32 & 0xFFFF);
-        a[1] = (short)(lo32 >> 16);
-        a[2] = (short)(hi32 & 0xFFFF);
-        a[3] = (short)(hi32 >> 16);
+        const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
         vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
       }
-      const uint32_t v01 = pack_bf16x2(vt[0], vt[1]);
-      const uint32_t v23 = pack_bf16x2(vt[2], vt[3]);
-      s16x4_t va;
-      va[0] = (short)(v01 & 0xFFFF);
-      va[1] = (short)(v01 >> 16);
-      va[2] = (short)(v23 & 0xFFFF);
-      va[3] = (short)(v23 >> 16);
+      const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[0], vt[1]), pack_bf16x2(vt[2], vt[3])));
       oacc[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pt, oacc[w], 0, 0, 0);
     }
   };
@@ -400,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
         issue(i + PF, (j + PF) % NBUF);
         wait_vmem<PF * 2 * S::kDma>(); // tile i has landed; PF newer tiles may still fly
         if (i < my_tiles) {
-          TileRegs<D, FP8> t;
+          TileRegs<DE, FP8> t;
           read_stage(t, j);
           compute(t, i);
         }
@@ -409,39 +396,59 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   }
   __syncthreads(); // staging area is reused for the per-wave states below
 
-  // ---- per-wave state to LDS ----
+  // ---- per-wave state to LDS (each query head keeps the dims of its KV head) ----
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (c16 < g) {
+  if (c16 < gp) {
     if (q4 == 0) {
       sm_m[wave][c16] = m_run;
       sm_l[wave][c16] = l_tot;
     }
     float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
 #pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w)
-      *reinterpret_cast<float4 *>(dst + out_dim<D, FP8>(w, q4)) =
-          make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+    for (int w = 0; w < S::kOTiles; ++w) {
+      const int od = out_dim<DE, FP8>(w, q4);
+      if (od / D == my_kv)
+        *reinterpret_cast<float4 *>(dst + od % D) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+    }
   }
   __syncthreads();
-  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, item, nb);
+  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, item, nb);
 }
 
 } // namespace
 
-template <int D, bool FP8>
+template <int D, int PACK, bool FP8>
 static hipError_t launch_mfma_d(const Params &p, hipStream_t stream) {
-  constexpr int NB = Shape<D, FP8>::kNBuf;
-  dim3 grid(p.items, p.num_kv_heads);
-  hipLaunchKernelGGL((partial_mfma_kernel<D, FP8, NB>), grid, dim3(kThreads), 0, stream, p);
+  constexpr int NB = Shape<D * PACK, FP8>::kNBuf;
+  dim3 grid(p.items, p.num_kv_heads / PACK);
+  hipLaunchKernelGGL((partial_mfma_kernel<D, PACK, FP8, NB>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+// KV heads per workgroup.  Two heads per pack would make every staged row at
+// least 256 contiguous bytes for fp8 head_dim 128 (128-byte segments stream
+// about 12% slower), but a packed tile then fills the LDS budget of two
+// staging slots per wave, and on MI355X that lost more than the longer rows
+// gained (batch-128 fp8 decode: 311 us unpacked, 407-424 us packed).  So the
+// default is one head per workgroup; KVS_ALGO_MFMA_PACKED asks for packs.
+int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack) {
+  const int seg = head_dim * (fp8 ? 1 : 2);
+  return (allow_pack && seg < 256 && 2 * group <= 16 && num_kv_heads % 2 == 0) ? 2 : 1;
+}
+
 hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStream_t stream) {
+  const bool pack2 = p.pack == 2;
   switch (head_dim) {
-  case 64: return fp8 ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
-  case 128: return fp8 ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
-  case 256: return fp8 ? launch_mfma_d<256, true>(p, stream) : launch_mfma_d<256, false>(p, stream);
+  case 64:
+    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, stream) : launch_mfma_d<64, 1, true>(p, stream);
+    return pack2 ? launch_mfma_d<64, 2, false>(p, stream) : launch_mfma_d<64, 1, false>(p, stream);
+  case 128:
+    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, stream) : launch_mfma_d<128, 1, true>(p, stream);
+    return pack2 ? launch_mfma_d<128, 2, false>(p, stream) : launch_mfma_d<128, 1, false>(p, stream);
+  case 256:
+    if (pack2) return hipErrorInvalidValue;
+    return fp8 ? launch_mfma_d<256, 1, true>(p, stream) : launch_mfma_d<256, 1, false>(p, stream);
   default: return hipErrorInvalidValue;
   }
 }

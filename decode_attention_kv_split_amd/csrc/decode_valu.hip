@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p) 
   const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
   const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
   if (b < 0) return; // kv_len on the device disagrees with the planned launch
-  if (p.meta && split == 0 && kvh == 0 && tid == 0) {
+  if (p.meta && split == 0 && kvh == 0 && tid == 0) { // this kernel runs one KV head per workgroup
     p.meta[2 * b] = s_item[3];
     p.meta[2 * b + 1] = nb;
   }

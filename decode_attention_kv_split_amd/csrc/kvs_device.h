@@ -13,11 +13,12 @@
 // request's first work item and split count in meta[2b], meta[2b+1]; the merge
 // kernel reads them instead of scanning the batch again.
 //
-// Partial results of split x (numbered within KV head kvh) live in the
-// workspace: o_part[((kvh * I + x) * g + h) * D + d] (fp32, already divided by
-// the chunk's sum and multiplied by the V scale) and lse_part[(kvh * I + x) *
-// g + h] (log2 domain: chunk max + log2(chunk sum), -inf when the chunk saw no
-// key), I = items per KV head.
+// A workgroup may serve `pack` adjacent KV heads (its query heads are the
+// gp = g * pack consecutive heads kvg * gp ...).  Partial results of split x
+// of pack kvg live in the workspace: o_part[((kvg * I + x) * gp + h) * D + d]
+// (fp32, already divided by the chunk's sum and multiplied by the V scale)
+// and lse_part[(kvg * I + x) * gp + h] (log2 domain: chunk max + log2(chunk
+// sum), -inf when the chunk saw no key), I = items per KV head.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,6 +52,7 @@ struct Params {
   int num_qo_heads;
   int num_kv_heads;
   int group;
+  int pack;       // KV heads per workgroup (partials and merge run per pack)
   int page_size;  // 0: contiguous
   int page_shift; // log2(page_size) when a power of two, else -1
   int window;
@@ -74,8 +76,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2_ev;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_ev;
+
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, low half
+// first; a single v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  const f32x2_ev x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_ev));
 }
 
 __device__ __forceinline__ int visible_lo(int L, int window) {
@@ -130,12 +138,13 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
 template <int D, int OSTRIDE>
 __device__ __forceinline__ void merge_waves_and_store(const Params &p, const float (*sm_m)[16],
                                                       const float (*sm_l)[16], const float *sm_o,
-                                                      int b, int kvh, int item, int nb) {
+                                                      int b, int kvg, int item, int nb) {
   const int g = p.group;
-  const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + kvh] : 1.0f;
-  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+  const int gp = g * p.pack;
+  for (int idx = threadIdx.x; idx < gp * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
+    const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + kvg * p.pack + h / g] : 1.0f;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -152,7 +161,7 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, const flo
       val = acc / L * vscale;
       lse2 = M + __log2f(L);
     }
-    const int hq = kvh * g + h;
+    const int hq = kvg * gp + h;
     if (nb == 1) {
       const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16)
@@ -161,9 +170,9 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, const flo
         reinterpret_cast<float *>(p.o)[off] = val;
       if (d == 0 && p.lse) p.lse[(size_t)b * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
-      const size_t slot = (size_t)kvh * p.items + item;
-      p.o_part[(slot * g + h) * D + d] = val;
-      if (d == 0) p.lse_part[slot * g + h] = lse2;
+      const size_t slot = (size_t)kvg * p.items + item;
+      p.o_part[(slot * gp + h) * D + d] = val;
+      if (d == 0) p.lse_part[slot * gp + h] = lse2;
     }
   }
 }

@@ -10,7 +10,7 @@
 // explainer's asynchronous-softmax section describes this synchronised update
 // of per-tile partial softmax results with the previous max and sum.
 //
-// Grid: (request, KV head, slice of the head dimension).  Requests with a
+// Grid: (request, KV-head pack, slice of the head dimension).  Requests with a
 // single split were already written by the partial kernel and exit at once.
 // A workgroup first turns the split LSEs of every query head of the group
 // into normalised weights (LDS), then streams the partial outputs as float4,
@@ -40,16 +40,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, int D, 
   __shared__ float s_m[16], s_inv[16], s_lse[16];
   __shared__ float4 s_red[kThreads];
   const int b = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int kvg = blockIdx.y; // KV-head pack
   const int slice = blockIdx.z;
   const int first = p.meta[2 * b];
   const int nb = p.meta[2 * b + 1];
   if (nb <= 1) return;
-  const int g = p.group;
+  const int g = p.group * p.pack; // query heads merged by this workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const size_t slot0 = (size_t)kvh * p.items + first;
+  const size_t slot0 = (size_t)kvg * p.items + first;
   const bool in_lds = g * nb <= kMergeLds;
 
   // ---- weights: one wave per query head ----
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, int D, 
       }
     }
     if (active && cg == 0) {
-      const int hq = kvh * g + h;
+      const int hq = kvg * g + h;
       const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16) {
         const uint32_t lo = pack_bf16x2(acc.x, acc.y), hi = pack_bf16x2(acc.z, acc.w);
@@ -150,8 +150,9 @@ hipError_t launch_merge(const Params &p, int head_dim, hipStream_t stream) {
   // to head_dim / 64 slices while there are fewer than ~256 (request, KV head)
   // pairs
   int slices = 1;
-  while (slices * 64 < head_dim && (int64_t)p.batch * p.num_kv_heads * slices < 256) slices *= 2;
-  dim3 grid(p.batch, p.num_kv_heads, slices);
+  const int packs = p.num_kv_heads / p.pack;
+  while (slices * 64 < head_dim && (int64_t)p.batch * packs * slices < 256) slices *= 2;
+  dim3 grid(p.batch, packs, slices);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, p, head_dim, slices);
   return hipGetLastError();
 }

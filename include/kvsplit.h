@@ -70,9 +70,13 @@ typedef enum {
 typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_FP8_E4M3 = 2 } kvs_dtype;
 
 /* Kernel family for the per-chunk partial softmax.  AUTO picks MFMA for bf16
- * and fp8 KV (query group packed into the rows of 16x16 matrix tiles) and
- * VALU for fp32 KV (one KV row per 4..64 lanes, fp32 FMA). */
-typedef enum { KVS_ALGO_AUTO = 0, KVS_ALGO_VALU = 1, KVS_ALGO_MFMA = 2 } kvs_algo;
+ * and fp8 KV with page_size 0 or >= 16 (query group packed into the columns
+ * of 16x16 matrix tiles) and VALU otherwise (fp32 KV, small pages: one KV
+ * row per 4..64 lanes, fp32 FMA).  MFMA_PACKED is the matrix-core kernel with
+ * two adjacent KV heads per workgroup when 2 * group <= 16, the head count is
+ * even and one head's row is shorter than 256 bytes (fp8 head_dim 128,
+ * head_dim 64); otherwise it is MFMA. */
+typedef enum { KVS_ALGO_AUTO = 0, KVS_ALGO_VALU = 1, KVS_ALGO_MFMA = 2, KVS_ALGO_MFMA_PACKED = 3 } kvs_algo;
 
 typedef struct {
   /* shape */
@@ -124,7 +128,7 @@ typedef struct {
   int32_t items_per_kv_head; /* sum over requests of splits; grid.x of the partial kernel */
   int32_t max_splits;        /* largest number of splits of one request */
   int32_t needs_merge;       /* 1 if some request has more than one split */
-  int32_t algo;              /* resolved kvs_algo (VALU or MFMA) */
+  int32_t algo;              /* resolved kvs_algo (VALU, MFMA or MFMA_PACKED) */
   int32_t num_cus;           /* CU count the plan was made for */
   size_t workspace_bytes;    /* bytes kvs_decode needs for this plan */
 } kvs_plan_info;

@@ -199,3 +199,9 @@ def test_algo_resolution(lib):
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_VALU
     a, keep = _args(kv=kvs.KVS_FP8_E4M3)
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+    a.algo = kvs.KVS_ALGO_MFMA_PACKED
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA_PACKED
+    a, keep = _args(q=kvs.KVS_F32, kv=kvs.KVS_F32, Hq=8, Hk=8, d=64, batch=1, P=0, lens=(512,), num_pages=0,
+                    algo=kvs.KVS_ALGO_MFMA_PACKED)
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_decode_plan(a)

@@ -249,3 +249,19 @@ def test_bandwidth_probes():
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
     assert kvs.kvs_probe_copy(dst.data_ptr(), src.data_ptr(), 17, s) != 0  # not a multiple of 16
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("Hk,g,d", [(3, 4, 128), (3, 8, 64), (6, 8, 128), (2, 16, 64)])
+def test_kv_head_packing_shapes(kv, Hk, g, d):
+    """The packed matrix-core variant: two KV heads per workgroup when the shape
+    allows it, one otherwise (odd KV-head counts, groups of 16); per-head fp8
+    scales differ inside a pack."""
+    print(f"case packing kv={kv} Hk={Hk} g={g} d={d}", flush=True)
+    spec = DecodeSpec("pack", 3, Hk * g, Hk, d, 16, kv, "bf16", 1 / math.sqrt(d),
+                      lengths=("list", [33, 700, 1500]), seed=Hk * 100 + g + d)
+    inp = make_inputs(spec, poison=True)
+    for chunk in (0, 48):
+        o, lse = run_library(inp, algo="mfma_packed", kv_chunk=chunk)
+        o_ref, lse_ref = oracle.decode_reference(inp)
+        compare(o, lse, o_ref, lse_ref, kv)
