@@ -11,9 +11,10 @@
 #include "plan.h"
 
 namespace kvs {
-hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStream_t stream);
-hipError_t launch_partial_valu(const Params &p, int head_dim, int kv_dtype, hipStream_t stream);
-hipError_t launch_merge(const Params &p, int head_dim, hipStream_t stream);
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, hipStream_t stream);
+hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype,
+                               hipStream_t stream);
+hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack);
 } // namespace kvs
@@ -187,18 +188,32 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.out_bf16 = a->q_dtype == KVS_BF16 ? 1 : 0;
   p.score_scale = a->sm_scale * kvs::kLog2e;
 
+  // host-planned work lists, passed inline when they fit
+  kvs::InlineWork w;
+  w.n_items = 0;
+  kvs::InlineMerge ml;
+  ml.n = -1;
+  if (a->batch <= kvs::kInlineRequests && pl.items <= kvs::kInlineItems) {
+    int n_merges = 0; // at most one entry per request, so it fits too
+    kvs::list_work(a->kv_len_host, a->batch, a->window, pl.chunk, w.item, ml.req, ml.first, &n_merges);
+    for (int b = 0; b < a->batch; ++b) w.req_len[b] = a->kv_len_host[b];
+    w.n_items = pl.items;
+    ml.n = n_merges;
+    p.meta = nullptr; // the merge kernel reads its list from the arguments
+  }
+
   hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a->prof_events[0]);
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a->prof_events[1]);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return KVS_ERR_HIP;
   hipError_t e;
   if (algo != KVS_ALGO_VALU)
-    e = kvs::launch_partial_mfma(p, a->head_dim, fp8, stream);
+    e = kvs::launch_partial_mfma(p, w, a->head_dim, fp8, stream);
   else
-    e = kvs::launch_partial_valu(p, a->head_dim, a->kv_dtype, stream);
+    e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, stream);
   if (e != hipSuccess) return KVS_ERR_HIP;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return KVS_ERR_HIP;
   if (pl.needs_merge) {
-    e = kvs::launch_merge(p, a->head_dim, stream);
+    e = kvs::launch_merge(p, ml, a->head_dim, stream);
     if (e != hipSuccess) return KVS_ERR_HIP;
   }
   return KVS_OK;

@@ -147,7 +147,7 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, FP8> &t, int j)
 }
 
 template <int D, int PACK, bool FP8, int NBUF>
-__global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, const InlineWork w) {
   constexpr int DE = D * PACK;
   using S = Shape<DE, FP8>;
   constexpr int PF = NBUF - 1; // tiles in flight while one is computed
@@ -177,26 +177,35 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
   const int my_kv = c16 / g;  // KV head (within the pack) of query head c16
 
   // ---- which (request, split) is this workgroup? ----
-  if (tid == 0) s_item[0] = -1;
-  scan_requests(p, s_scan, [&](int b, int first, int nb) {
-    if (item >= first && item < first + nb) {
-      s_item[0] = b;
-      s_item[1] = item - first;
-      s_item[2] = nb;
-      s_item[3] = first;
+  int b, split, nb, L;
+  if (w.n_items > 0) { // planned on the host
+    const uint32_t e = w.item[item];
+    b = (int)(e >> 16);
+    split = (int)(e & 0xFFFF);
+    L = w.req_len[b];
+    nb = num_splits(L, p.window, p.chunk);
+  } else {
+    if (tid == 0) s_item[0] = -1;
+    scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
+      if (item >= first && item < first + nbb) {
+        s_item[0] = bb;
+        s_item[1] = item - first;
+        s_item[2] = nbb;
+        s_item[3] = first;
+      }
+    });
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_item[0]);
+    split = __builtin_amdgcn_readfirstlane(s_item[1]);
+    nb = __builtin_amdgcn_readfirstlane(s_item[2]);
+    if (b < 0) return; // kv_len on the device disagrees with the planned launch
+    if (p.meta && split == 0 && kvg == 0 && tid == 0) {
+      p.meta[2 * b] = s_item[3];
+      p.meta[2 * b + 1] = nb;
     }
-  });
-  __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
-  const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
-  const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
-  if (b < 0) return; // kv_len on the device disagrees with the planned launch
-  if (p.meta && split == 0 && kvg == 0 && tid == 0) {
-    p.meta[2 * b] = s_item[3];
-    p.meta[2 * b + 1] = nb;
+    L = p.kv_len[b];
   }
 
-  const int L = p.kv_len[b];
   const int lo = visible_lo(L, p.window);
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
   const int t_begin = max(lo, a0);
@@ -337,13 +346,12 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
     }
     mx = xor32_max(xor16_max(mx));
     const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.0f;
-    float pr[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m_new != -INFINITY) {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new); // m_run = -inf -> 0
+    // no visible key so far for this head: keep the state (selects, no branch)
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f; // m_run = -inf -> 0
+    float pr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
-    }
+    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_new) : 0.0f;
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -419,10 +427,10 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p) 
 } // namespace
 
 template <int D, int PACK, bool FP8>
-static hipError_t launch_mfma_d(const Params &p, hipStream_t stream) {
+static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, hipStream_t stream) {
   constexpr int NB = Shape<D * PACK, FP8>::kNBuf;
   dim3 grid(p.items, p.num_kv_heads / PACK);
-  hipLaunchKernelGGL((partial_mfma_kernel<D, PACK, FP8, NB>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((partial_mfma_kernel<D, PACK, FP8, NB>), grid, dim3(kThreads), 0, stream, p, w);
   return hipGetLastError();
 }
 
@@ -437,18 +445,18 @@ int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pa
   return (allow_pack && seg < 256 && 2 * group <= 16 && num_kv_heads % 2 == 0) ? 2 : 1;
 }
 
-hipError_t launch_partial_mfma(const Params &p, int head_dim, bool fp8, hipStream_t stream) {
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, hipStream_t stream) {
   const bool pack2 = p.pack == 2;
   switch (head_dim) {
   case 64:
-    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, stream) : launch_mfma_d<64, 1, true>(p, stream);
-    return pack2 ? launch_mfma_d<64, 2, false>(p, stream) : launch_mfma_d<64, 1, false>(p, stream);
+    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, w, stream) : launch_mfma_d<64, 1, true>(p, w, stream);
+    return pack2 ? launch_mfma_d<64, 2, false>(p, w, stream) : launch_mfma_d<64, 1, false>(p, w, stream);
   case 128:
-    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, stream) : launch_mfma_d<128, 1, true>(p, stream);
-    return pack2 ? launch_mfma_d<128, 2, false>(p, stream) : launch_mfma_d<128, 1, false>(p, stream);
+    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, w, stream) : launch_mfma_d<128, 1, true>(p, w, stream);
+    return pack2 ? launch_mfma_d<128, 2, false>(p, w, stream) : launch_mfma_d<128, 1, false>(p, w, stream);
   case 256:
     if (pack2) return hipErrorInvalidValue;
-    return fp8 ? launch_mfma_d<256, 1, true>(p, stream) : launch_mfma_d<256, 1, false>(p, stream);
+    return fp8 ? launch_mfma_d<256, 1, true>(p, w, stream) : launch_mfma_d<256, 1, false>(p, w, stream);
   default: return hipErrorInvalidValue;
   }
 }

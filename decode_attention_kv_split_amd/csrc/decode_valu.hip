@@ -58,7 +58,7 @@ __device__ __forceinline__ void dequant16(const uint4 w, float *out) {
 }
 
 template <int D, int KVT, int G>
-__global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p) {
+__global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, const InlineWork w) {
   constexpr int BYTES = KvType<KVT>::kBytes;
   constexpr int EPL = 16 / BYTES;        // elements per lane
   constexpr int RL = D * BYTES / 16;     // lanes per row
@@ -84,26 +84,36 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p) 
   const int g = p.group;
   const int Hk = p.num_kv_heads;
 
-  if (tid == 0) s_item[0] = -1;
-  scan_requests(p, s_scan, [&](int b, int first, int nb) {
-    if (item >= first && item < first + nb) {
-      s_item[0] = b;
-      s_item[1] = item - first;
-      s_item[2] = nb;
-      s_item[3] = first;
+  // ---- which (request, split) is this workgroup? ----
+  int b, split, nb, L;
+  if (w.n_items > 0) { // planned on the host
+    const uint32_t e = w.item[item];
+    b = (int)(e >> 16);
+    split = (int)(e & 0xFFFF);
+    L = w.req_len[b];
+    nb = num_splits(L, p.window, p.chunk);
+  } else {
+    if (tid == 0) s_item[0] = -1;
+    scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
+      if (item >= first && item < first + nbb) {
+        s_item[0] = bb;
+        s_item[1] = item - first;
+        s_item[2] = nbb;
+        s_item[3] = first;
+      }
+    });
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_item[0]);
+    split = __builtin_amdgcn_readfirstlane(s_item[1]);
+    nb = __builtin_amdgcn_readfirstlane(s_item[2]);
+    if (b < 0) return; // kv_len on the device disagrees with the planned launch
+    if (p.meta && split == 0 && kvh == 0 && tid == 0) {
+      p.meta[2 * b] = s_item[3];
+      p.meta[2 * b + 1] = nb;
     }
-  });
-  __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(s_item[0]);
-  const int split = __builtin_amdgcn_readfirstlane(s_item[1]);
-  const int nb = __builtin_amdgcn_readfirstlane(s_item[2]);
-  if (b < 0) return; // kv_len on the device disagrees with the planned launch
-  if (p.meta && split == 0 && kvh == 0 && tid == 0) { // this kernel runs one KV head per workgroup
-    p.meta[2 * b] = s_item[3];
-    p.meta[2 * b + 1] = nb;
+    L = p.kv_len[b];
   }
 
-  const int L = p.kv_len[b];
   const int lo = visible_lo(L, p.window);
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk;
   const int t_begin = max(lo, a0);
@@ -223,19 +233,19 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p) 
 }
 
 template <int D, int KVT>
-hipError_t launch_valu_dk(const Params &p, hipStream_t stream) {
+hipError_t launch_valu_dk(const Params &p, const InlineWork &w, hipStream_t stream) {
   dim3 grid(p.items, p.num_kv_heads);
   const int g = p.group;
   if (g == 1)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 1>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 1>), grid, dim3(kThreads), 0, stream, p, w);
   else if (g == 2)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 2>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 2>), grid, dim3(kThreads), 0, stream, p, w);
   else if (g <= 4)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 4>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 4>), grid, dim3(kThreads), 0, stream, p, w);
   else if (g <= 8)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 8>), grid, dim3(kThreads), 0, stream, p, w);
   else if constexpr (KVT != DT_FP8)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 16>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 16>), grid, dim3(kThreads), 0, stream, p, w);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -246,27 +256,27 @@ hipError_t launch_valu_dk(const Params &p, hipStream_t stream) {
 // Largest GQA group the vector kernel takes for a KV type.
 int valu_max_group(int kv_dtype) { return kv_dtype == DT_FP8 ? 8 : 16; }
 
-hipError_t launch_partial_valu(const Params &p, int head_dim, int kv_dtype, hipStream_t stream) {
+hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, hipStream_t stream) {
   switch (kv_dtype) {
   case DT_F32:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_F32>(p, stream);
-    case 128: return launch_valu_dk<128, DT_F32>(p, stream);
-    case 256: return launch_valu_dk<256, DT_F32>(p, stream);
+    case 64: return launch_valu_dk<64, DT_F32>(p, w, stream);
+    case 128: return launch_valu_dk<128, DT_F32>(p, w, stream);
+    case 256: return launch_valu_dk<256, DT_F32>(p, w, stream);
     }
     break;
   case DT_BF16:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_BF16>(p, stream);
-    case 128: return launch_valu_dk<128, DT_BF16>(p, stream);
-    case 256: return launch_valu_dk<256, DT_BF16>(p, stream);
+    case 64: return launch_valu_dk<64, DT_BF16>(p, w, stream);
+    case 128: return launch_valu_dk<128, DT_BF16>(p, w, stream);
+    case 256: return launch_valu_dk<256, DT_BF16>(p, w, stream);
     }
     break;
   case DT_FP8:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_FP8>(p, stream);
-    case 128: return launch_valu_dk<128, DT_FP8>(p, stream);
-    case 256: return launch_valu_dk<256, DT_FP8>(p, stream);
+    case 64: return launch_valu_dk<64, DT_FP8>(p, w, stream);
+    case 128: return launch_valu_dk<128, DT_FP8>(p, w, stream);
+    case 256: return launch_valu_dk<256, DT_FP8>(p, w, stream);
     }
     break;
   }

@@ -62,6 +62,26 @@ struct Params {
   float score_scale; // sm_scale * log2(e)
 };
 
+// Work lists planned on the host from kv_len_host and passed in the kernel
+// arguments when they fit, which saves each workgroup a dependent memory read
+// before its first K/V load; larger batches derive the same lists from kv_len
+// on the device (scan_requests, meta).
+constexpr int kInlineRequests = 256;
+constexpr int kInlineItems = 448;
+constexpr int kInlineMerges = 384;
+
+struct InlineWork {
+  int n_items;                   // items per KV head listed below; 0: not provided
+  int req_len[kInlineRequests];  // kv_len of each request (the host copy)
+  uint32_t item[kInlineItems];   // work item x: (request << 16) | split
+};
+
+struct InlineMerge {
+  int n;                         // requests listed below; -1: not provided
+  uint32_t req[kInlineMerges];   // (request << 16) | number of splits (> 1)
+  uint32_t first[kInlineMerges]; // work item of the request's split 0
+};
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;

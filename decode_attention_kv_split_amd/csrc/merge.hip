@@ -12,148 +12,141 @@
 //
 // Grid: (request, KV-head pack, slice of the head dimension).  Requests with a
 // single split were already written by the partial kernel and exit at once.
-// A workgroup first turns the split LSEs of every query head of the group
-// into normalised weights (LDS), then streams the partial outputs as float4,
-// eight splits in flight per thread, with the splits spread over thread
-// groups whose sums meet in LDS.
+// Each thread owns four consecutive output dims of one query head and a
+// subset of the splits: it issues the LSE and partial loads of up to 16
+// splits at once and folds them with the same running-max rescale, so a
+// request's merge costs about one memory round trip after its metadata; the
+// thread groups that share an output then combine their (max, weight,
+// accumulator) states in LDS.
 #include "kvs_device.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kMergeLds = 8192; // weights kept in LDS (heads x splits)
-constexpr int kBatch = 8;       // partial loads in flight per thread
+constexpr int kBatch = 16; // splits whose loads are in flight together per thread
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+struct MergeState {
+  float m;   // running max of the split LSEs (log2 domain)
+  float w;   // sum of 2^(lse_c - m)
+  float4 acc; // sum of 2^(lse_c - m) * o_c
+};
+
+__device__ __forceinline__ void fold(MergeState &st, float lc, const float4 &o) {
+  // lc = -inf (a split that saw no key) contributes nothing
+  if (lc == -INFINITY) return;
+  if (lc > st.m) {
+    const float r = st.m == -INFINITY ? 0.0f : exp2f(st.m - lc);
+    st.w *= r;
+    st.acc.x *= r;
+    st.acc.y *= r;
+    st.acc.z *= r;
+    st.acc.w *= r;
+    st.m = lc;
+  }
+  const float e = exp2f(lc - st.m);
+  st.w += e;
+  st.acc.x += e * o.x;
+  st.acc.y += e * o.y;
+  st.acc.z += e * o.z;
+  st.acc.w += e * o.w;
 }
 
-__global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, int D, int slices) {
-  __shared__ float s_w[kMergeLds];
-  __shared__ float s_m[16], s_inv[16], s_lse[16];
-  __shared__ float4 s_red[kThreads];
-  const int b = blockIdx.x;
+__device__ __forceinline__ void combine(MergeState &a, const MergeState &b) {
+  if (b.m == -INFINITY) return;
+  const float M = fmaxf(a.m, b.m);
+  const float ra = a.m == -INFINITY ? 0.0f : exp2f(a.m - M);
+  const float rb = exp2f(b.m - M);
+  a.w = a.w * ra + b.w * rb;
+  a.acc.x = a.acc.x * ra + b.acc.x * rb;
+  a.acc.y = a.acc.y * ra + b.acc.y * rb;
+  a.acc.z = a.acc.z * ra + b.acc.z * rb;
+  a.acc.w = a.acc.w * ra + b.acc.w * rb;
+  a.m = M;
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const InlineMerge ml, int D, int slices) {
+  __shared__ MergeState s_st[kThreads];
   const int kvg = blockIdx.y; // KV-head pack
   const int slice = blockIdx.z;
-  const int first = p.meta[2 * b];
-  const int nb = p.meta[2 * b + 1];
+  int b, first, nb;
+  if (ml.n >= 0) { // requests with several splits, listed by the host
+    b = (int)(ml.req[blockIdx.x] >> 16);
+    nb = (int)(ml.req[blockIdx.x] & 0xFFFF);
+    first = (int)ml.first[blockIdx.x];
+  } else {         // one workgroup per request, metadata from the partial kernel
+    b = blockIdx.x;
+    first = p.meta[2 * b];
+    nb = p.meta[2 * b + 1];
+  }
   if (nb <= 1) return;
   const int g = p.group * p.pack; // query heads merged by this workgroup
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const size_t slot0 = (size_t)kvg * p.items + first;
-  const bool in_lds = g * nb <= kMergeLds;
-
-  // ---- weights: one wave per query head ----
-  for (int h = wave; h < g; h += kWaves) {
-    float M = -INFINITY;
-    for (int c = lane; c < nb; c += 64) M = fmaxf(M, p.lse_part[(slot0 + c) * g + h]);
-    M = wave_max(M);
-    float W = 0.0f;
-    for (int c = lane; c < nb; c += 64) {
-      const float lc = p.lse_part[(slot0 + c) * g + h];
-      const float w = (lc == -INFINITY) ? 0.0f : exp2f(lc - M);
-      W += w;
-      if (in_lds) s_w[h * nb + c] = w;
-    }
-    W = wave_sum(W);
-    const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-    if (in_lds)
-      for (int c = lane; c < nb; c += 64) s_w[h * nb + c] *= inv;
-    if (lane == 0) {
-      s_m[h] = M;
-      s_inv[h] = inv;
-      s_lse[h] = (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2;
-    }
-  }
-  __syncthreads();
-
-  auto weight = [&](int h, int c) -> float {
-    if (in_lds) return s_w[h * nb + c];
-    const float lc = p.lse_part[(slot0 + c) * g + h];
-    return (lc == -INFINITY) ? 0.0f : exp2f(lc - s_m[h]) * s_inv[h];
-  };
-
-  // ---- weighted sum of the partial outputs ----
   const int Ds = D / slices;
   const int d0 = slice * Ds;
-  const int F = g * Ds / 4;                     // float4 outputs of this workgroup
-  const int SG = F >= kThreads ? 1 : kThreads / F; // split groups
-  const size_t cstride = (size_t)g * D / 4;      // float4 between consecutive splits
+  const int F = g * Ds / 4;                        // float4 outputs of this workgroup
+  const int SG = F >= kThreads ? 1 : kThreads / F; // thread groups splitting the splits
+  const size_t cstride = (size_t)g * D / 4;        // float4 between consecutive splits
   const float4 *op = reinterpret_cast<const float4 *>(p.o_part) + slot0 * cstride;
+  const float *lp = p.lse_part + slot0 * g;
   for (int f0 = 0; f0 < F; f0 += kThreads) {
     const int t = f0 + (SG > 1 ? tid % F : tid);
     const int cg = SG > 1 ? tid / F : 0;
     const bool active = t < F && cg < SG;
     const int h = t / (Ds / 4);
     const int d = d0 + 4 * (t % (Ds / 4));
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
     if (active) {
       const float4 *src = op + ((size_t)h * D + d) / 4;
       for (int c0 = cg; c0 < nb; c0 += SG * kBatch) {
+        float lc[kBatch];
         float4 v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int c = c0 + u * SG;
+          lc[u] = c < nb ? lp[(size_t)c * g + h] : -INFINITY;
           v[u] = c < nb ? src[c * cstride] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int c = c0 + u * SG;
-          const float w = c < nb ? weight(h, c) : 0.0f;
-          acc.x += w * v[u].x;
-          acc.y += w * v[u].y;
-          acc.z += w * v[u].z;
-          acc.w += w * v[u].w;
-        }
+        for (int u = 0; u < kBatch; ++u) fold(st, lc[u], v[u]);
       }
     }
     if (SG > 1) {
-      s_red[tid] = acc;
+      s_st[tid] = st;
       __syncthreads();
-      if (tid < F) {
-        for (int j = 1; j < SG; ++j) {
-          const float4 o = s_red[tid + j * F];
-          acc.x += o.x;
-          acc.y += o.y;
-          acc.z += o.z;
-          acc.w += o.w;
-        }
-      }
+      if (tid < F)
+        for (int j = 1; j < SG; ++j) combine(st, s_st[tid + j * F]);
     }
     if (active && cg == 0) {
+      const float inv = st.w > 0.0f ? 1.0f / st.w : 0.0f;
+      const float4 o = make_float4(st.acc.x * inv, st.acc.y * inv, st.acc.z * inv, st.acc.w * inv);
       const int hq = kvg * g + h;
       const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16) {
-        const uint32_t lo = pack_bf16x2(acc.x, acc.y), hi = pack_bf16x2(acc.z, acc.w);
-        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
+            make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
       } else {
-        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + off) = acc;
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + off) = o;
       }
-      if (d == 0 && p.lse) p.lse[(size_t)b * p.num_qo_heads + hq] = s_lse[h];
+      if (d == 0 && p.lse)
+        p.lse[(size_t)b * p.num_qo_heads + hq] = st.m == -INFINITY ? -INFINITY : (st.m + __log2f(st.w)) * kLn2;
     }
   }
 }
 
 } // namespace
 
-hipError_t launch_merge(const Params &p, int head_dim, hipStream_t stream) {
+hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream) {
+  const int rows = ml.n >= 0 ? ml.n : p.batch;
+  if (rows == 0) return hipSuccess;
   // enough workgroups to spread a small batch: cut the head dimension into up
-  // to head_dim / 64 slices while there are fewer than ~256 (request, KV head)
+  // to head_dim / 64 slices while there are fewer than ~256 (request, pack)
   // pairs
   int slices = 1;
   const int packs = p.num_kv_heads / p.pack;
-  while (slices * 64 < head_dim && (int64_t)p.batch * packs * slices < 256) slices *= 2;
-  dim3 grid(p.batch, packs, slices);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, p, head_dim, slices);
+  while (slices * 64 < head_dim && (int64_t)rows * packs * slices < 256) slices *= 2;
+  dim3 grid(rows, packs, slices);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, p, ml, head_dim, slices);
   return hipGetLastError();
 }
 

@@ -53,4 +53,22 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
   return true;
 }
 
+void list_work(const int32_t *kv_len, int batch, int window, int chunk, uint32_t *items,
+               uint32_t *merge_req, uint32_t *merge_first, int *n_merges) {
+  int x = 0, m = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int L = kv_len[b];
+    const int lo = window > 0 ? std::max(0, L - window) : 0;
+    const int64_t span = L - (lo & ~15);
+    const int n = span <= 0 ? 1 : (int)((span + chunk - 1) / chunk);
+    if (n > 1 && merge_req) {
+      merge_req[m] = ((uint32_t)b << 16) | (uint32_t)n;
+      merge_first[m] = (uint32_t)x;
+      ++m;
+    }
+    for (int s = 0; s < n; ++s) items[x++] = ((uint32_t)b << 16) | (uint32_t)s;
+  }
+  if (n_merges) *n_merges = m;
+}
+
 } // namespace kvs

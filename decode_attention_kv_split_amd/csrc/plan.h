@@ -32,6 +32,13 @@ constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
 // its tiles in one register, one per lane).
 constexpr int kMaxChunk = 4096;
 
+// Host copies of the device work lists for a plan (see InlineWork /
+// InlineMerge): items[x] = (request << 16) | split for the items of one KV
+// head in device order; merges = (request << 16) | splits and the request's
+// first item, for requests with more than one split.
+void list_work(const int32_t *kv_len, int batch, int window, int chunk, uint32_t *items,
+               uint32_t *merge_req, uint32_t *merge_first, int *n_merges);
+
 // kv_len: host lengths [batch]; returns false if a length is negative.
 bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, int group, int head_dim,
                int forced_chunk, int num_cus, Plan *out);

@@ -265,3 +265,27 @@ def test_kv_head_packing_shapes(kv, Hk, g, d):
         o, lse = run_library(inp, algo="mfma_packed", kv_chunk=chunk)
         o_ref, lse_ref = oracle.decode_reference(inp)
         compare(o, lse, o_ref, lse_ref, kv)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_large_batch_device_planned(kv):
+    """More than 256 requests: the kernels derive the work lists from kv_len on
+    the device instead of taking them from the launch arguments."""
+    print(f"case large batch {kv}", flush=True)
+    spec = DecodeSpec("big", 300, 8, 2, 128, 16, kv, "bf16", 0.1, lengths=("uniform", 0, 700), seed=31)
+    inp = make_inputs(spec, poison=True)
+    for chunk in (0, 64):
+        o, lse = run_library(inp, kv_chunk=chunk)
+        o_ref, lse_ref = oracle.decode_reference(inp)
+        compare(o, lse, o_ref, lse_ref, kv)
+
+
+def test_many_items_device_planned():
+    """More than 448 work items per KV head (small forced chunks)."""
+    print("case many items", flush=True)
+    spec = DecodeSpec("items", 2, 8, 2, 128, 16, "bf16", "bf16", 0.1, lengths=("list", [8192, 300]), seed=32)
+    inp = make_inputs(spec, poison=True)
+    for algo in ("mfma", "valu"):
+        o, lse = run_library(inp, kv_chunk=16, algo=algo)
+        o_ref, lse_ref = oracle.decode_reference(inp)
+        compare(o, lse, o_ref, lse_ref, "bf16")
