@@ -26,10 +26,44 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "decode-attention \u00b5s/step and achieved HBM GB/s (% of peak), paged GQA batch"
 CONFIG_ALIASES = {"c1": "c1_mha_f32", "c2": "c2_gemma3_1b", "c2w": "c2_gemma3_1b_w512",
                   "c3": "c3_llama2_7b_32k", "c4": "c4_paged_bf16_b64", "c5": "c5_paged_fp8_b128"}
 DEFAULT = "c4_paged_bf16_b64"
 _BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+# HBM bytes per launch of the partial kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over the default command of
+# each workload, each scaled by the factor the same counter gives for
+# kvs_probe_copy of 1 GiB (the counter summaries under profiles/ hold the
+# commands and raw figures).  A figure is reported only while the library
+# sources hash to the digest it was measured with; otherwise traffic is null.
+MEASURED_TRAFFIC = {
+}
+
+
+def library_digest() -> str:
+    """SHA-256 over the library's device and host sources and build flags."""
+    import hashlib
+
+    pkg = os.path.join(ROOT, "decode_attention_kv_split_amd")
+    files = [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "kvsplit.h")]
+    csrc = os.path.join(pkg, "csrc")
+    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
+              if f.endswith((".hip", ".h", ".cpp"))]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config_name: str, kernel: str):
+    rec = MEASURED_TRAFFIC.get((config_name, kernel))
+    if rec is None or rec["digest"] != library_digest():
+        return None
+    return rec["bytes"]
 
 
 def algorithmic_bytes(inp) -> int:
@@ -124,9 +158,11 @@ def probe_copy(nbytes: int, reps: int) -> dict:
             "GBs": round(2 * nbytes / dt / 1e9, 1)}
 
 
-def cpu_baseline(inp, budget_s: float = 15.0):
+def cpu_baseline(inp, budget_s: float = 12.0):
     """The fp64 oracle as it stands, on a bounded sample of the same workload:
-    whole requests in order until the time budget is spent."""
+    whole requests in order, wrapping round to the first request, until the
+    time budget is spent; the rate is the algorithmic bytes of the requests
+    done over the time taken."""
     import oracle
 
     try:
@@ -136,26 +172,27 @@ def cpu_baseline(inp, budget_s: float = 15.0):
     except Exception:
         threads = os.cpu_count() or 1
     s = inp.spec
-    sub_bytes = 0
-    done = []
-    t0 = time.perf_counter()
-    for b in range(s.batch):
-        oracle.decode_reference(inp, requests=[b])
-        done.append(b)
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
     L = inp.kv_len.astype(np.int64)
     lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
-    vis = int(np.sum((L - lo)[done]))
-    frac_bytes = algorithmic_bytes(inp) * (vis / max(1, int(np.sum(L - lo))))
+    vis_all = max(1, int(np.sum(L - lo)))
+    vis = 0
+    n_req = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = n_req % s.batch
+        oracle.decode_reference(inp, requests=[b])
+        vis += int(L[b] - lo[b])
+        n_req += 1
+    dt = time.perf_counter() - t0
+    frac_bytes = algorithmic_bytes(inp) * (vis / vis_all)
     return {"value": round(frac_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle on {len(done)} of {s.batch} requests ({vis} visible tokens), "
-                      f"{dt:.1f} s, same seeded inputs"}
+            "sample": f"fp64 numpy oracle, {n_req} requests of the {s.batch}-request batch taken in order "
+                      f"and wrapping ({vis} visible tokens, {n_req / s.batch:.2f} passes), {dt:.1f} s, "
+                      f"same seeded inputs"}
 
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
-        with_cpu: bool = True) -> dict:
+        with_cpu: bool = True, events: bool = True) -> dict:
     import torch
 
     import decode_attention_kv_split_amd as kvs
@@ -178,8 +215,15 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     plan = kvs.kvs_decode_plan(a)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
+    # The partial kernel's own dispatch stamps a pair of events with its start
+    # and end (kvs_decode_args.prof_events).  Stamping costs a few microseconds
+    # per call, so inside the timed region every `every`-th step carries them
+    # (about 20 samples), which keeps the step time close to an unstamped run.
+    every = max(1, steps // 20) if events else 0
+    stamped = [i for i in range(steps) if events and i % every == 0]
     ev = HipEvents()
-    evs = ev.create(2 * steps)
+    evs = ev.create(2 * len(stamped))
+    pair = {i: (evs[2 * j], evs[2 * j + 1]) for j, i in enumerate(stamped)}
 
     def step(e0=None, e1=None):
         a.prof_events[0] = e0
@@ -193,21 +237,21 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[2 * i], evs[2 * i + 1])
+        step(*pair.get(i, (None, None)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = [ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    part_ms = [ev.elapsed_ms(*pair[i]) for i in stamped] or [float("nan")]
     ev.destroy(evs)
-
     nbytes = algorithmic_bytes(inp)
     ms_per_step = wall * 1e3 / steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     part_avg = float(np.mean(part_ms))
+    p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(part_ms, [10, 50, 90]))
     achieved = nbytes / (part_avg * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(0)
     kernel = ("partial_mfma_kernel" if plan.algo == kvs.KVS_ALGO_MFMA else "partial_valu_kernel")
     out = {
-        "metric": "decode-attention us/step and achieved HBM GB/s (% of peak), paged GQA batch",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -236,14 +280,19 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(config_name, kernel),
             "kernel_us": round(part_avg * 1e3, 2),
+            "kernel_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+            "kernel_launches_timed": len(stamped),
             "algorithmic_bytes": nbytes,
         },
         "device": {"name": props.name, "cus": props.multi_processor_count, "host": platform.node()},
+        "library_digest": library_digest()[:16],
         "probe_stream_read_GBs": round(probe_read_gbs(), 1),
         "input_gen_s": round(t_gen, 1),
     }
+    if not events:
+        out["roofline"].update(achieved=None, frac=None, kernel_us=None, kernel_us_p10_p50_p90=None)
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(inp)
     return out
@@ -258,6 +307,9 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "mfma_packed", "valu"])
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-events", action="store_true",
+                    help="no per-launch kernel timing (the event stamps add host time per call, which "
+                         "shows in the step time of launch-bound workloads); roofline timing fields become null")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run kvs_probe_copy of BYTES bytes (hardware byte-counter calibration)")
     args = ap.parse_args()
@@ -269,7 +321,8 @@ def main():
               "(each GPU would run its own requests or KV heads independently).", file=sys.stderr)
         sys.exit(2)
     name = CONFIG_ALIASES.get(args.config, args.config)
-    res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu)
+    res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
+              events=not args.no_events)
     print(json.dumps(res), flush=True)
 
 

@@ -11,9 +11,8 @@
 #include "plan.h"
 
 namespace kvs {
-hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, hipStream_t stream);
-hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype,
-                               hipStream_t stream);
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, const Launch &l);
+hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, const Launch &l);
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack);
@@ -115,6 +114,8 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   if (!kvs::make_plan(a->kv_len_host, a->batch, a->window, a->num_kv_heads, group, a->head_dim,
                       a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
+  // grid.x (items) of kThreads work-items must stay below 2^32 work-items
+  if ((int64_t)pl->items * a->num_kv_heads > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
   return KVS_OK;
 }
 
@@ -202,16 +203,15 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
     p.meta = nullptr; // the merge kernel reads its list from the arguments
   }
 
-  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a->prof_events[0]);
-  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a->prof_events[1]);
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return KVS_ERR_HIP;
+  // the partial kernel's dispatch stamps the profiling events itself
+  const kvs::Launch lp{stream, reinterpret_cast<hipEvent_t>(a->prof_events[0]),
+                       reinterpret_cast<hipEvent_t>(a->prof_events[1])};
   hipError_t e;
   if (algo != KVS_ALGO_VALU)
-    e = kvs::launch_partial_mfma(p, w, a->head_dim, fp8, stream);
+    e = kvs::launch_partial_mfma(p, w, a->head_dim, fp8, lp);
   else
-    e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, stream);
+    e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, lp);
   if (e != hipSuccess) return KVS_ERR_HIP;
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return KVS_ERR_HIP;
   if (pl.needs_merge) {
     e = kvs::launch_merge(p, ml, a->head_dim, stream);
     if (e != hipSuccess) return KVS_ERR_HIP;

@@ -19,8 +19,9 @@
 //     head c16 only sees the dims of its own KV head.  Lane ends up with
 //     tokens 4*q4 + r (r = 0..3) of query head c16.
 //   * online softmax per query head in the log2 domain: tile max over the 16
-//     tokens (in-lane over r, then across the four quarters), rescale factor,
-//     weights p = exp2(s - max), running sum.
+//     tokens (in-lane over r, then across the four quarters); the reference
+//     max moves, with a rescale of the running state, only when the tile max
+//     exceeds it by more than 8; weights p = exp2(s - reference), running sum.
 //   * V^T: multiplying the V tile by an identity (bf16, 16x16x16) or by a
 //     0/1 selection (fp8, 16x16x32 fp8) puts tokens 4*q4 + r of one head
 //     dimension in lane c16 -- the operand layout the next product needs --
@@ -54,8 +55,9 @@ struct Shape {
   static constexpr int kDma = kTile * kRowBytes / 1024;    // loads per tile (K or V)
   static constexpr int kTileBytes = kTile * kRowBytes;     // K (or V) bytes of a tile
   static constexpr int kRowsPerBankPeriod = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
-  // tiles staged per wave: about 16 KB of K+V in LDS per wave, two to eight
-  static constexpr int kFit = 16384 / (2 * kTileBytes);
+  // tiles staged per wave: about 12 KB of K+V in LDS per wave (three
+  // workgroups per CU for fp8 head_dim 128), two to eight
+  static constexpr int kFit = 12288 / (2 * kTileBytes);
   static constexpr int kNBuf = kFit < 2 ? 2 : (kFit > 8 ? 8 : kFit);
 };
 
@@ -67,6 +69,9 @@ constexpr int kBufferFlags = 0x00020000;
 // per call, and streaming loads measured about 10% more HBM bandwidth than
 // default-policy loads on MI355X (6.7 vs 6.0 TB/s on a plain read).
 constexpr int kKvLoadPolicy = 2;
+// Largest rise of a head's running max (log2 units) absorbed without a
+// rescale of its state; weights then stay below 2^8.
+constexpr float kLazy = 8.0f;
 
 // XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
 // operand reads at the same logical piece land in distinct LDS banks.
@@ -85,6 +90,48 @@ __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
   __asm__ volatile("" ::: "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Reads of a staged tile.  Each asm block issues the K and V pieces at one or
+// two lane addresses (V sits VOFF bytes after K) and waits for them
+// (lgkmcnt 0) before it ends, so the registers are complete when the block
+// returns and the slot may be refilled at once.  Written out because the
+// compiler's own wait insertion cannot tell, across the main loop's back edge,
+// which DMA load filled which slot, and would otherwise drain every load in
+// flight there; the explicit vmcnt wait before each read orders DMA and read.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <int VOFF>
+__device__ __forceinline__ void lds_read_kv1(uint4 &k0, uint4 &v0, uint32_t a0) {
+  u32x4_t rk0, rv0;
+  __asm__ volatile("ds_read_b128 %0, %2\n\t"
+                   "ds_read_b128 %1, %2 offset:%3\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk0), "=&v"(rv0)
+                   : "v"(a0), "i"(VOFF)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk0);
+  v0 = __builtin_bit_cast(uint4, rv0);
+}
+template <int VOFF>
+__device__ __forceinline__ void lds_read_kv2(uint4 &k0, uint4 &v0, uint4 &k1, uint4 &v1, uint32_t a0, uint32_t a1) {
+  u32x4_t rk0, rv0, rk1, rv1;
+  __asm__ volatile("ds_read_b128 %0, %4\n\t"
+                   "ds_read_b128 %1, %4 offset:%6\n\t"
+                   "ds_read_b128 %2, %5\n\t"
+                   "ds_read_b128 %3, %5 offset:%6\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk0), "=&v"(rv0), "=&v"(rk1), "=&v"(rv1)
+                   : "v"(a0), "v"(a1), "i"(VOFF)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk0);
+  v0 = __builtin_bit_cast(uint4, rv0);
+  k1 = __builtin_bit_cast(uint4, rk1);
+  v1 = __builtin_bit_cast(uint4, rv1);
 }
 
 // One 16-byte-per-lane DMA load from a buffer into LDS: lane i's bytes land
@@ -150,7 +197,6 @@ template <int D, int PACK, bool FP8, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, const InlineWork w) {
   constexpr int DE = D * PACK;
   using S = Shape<DE, FP8>;
-  constexpr int PF = NBUF - 1; // tiles in flight while one is computed
   constexpr int OSTRIDE = D + 4;
   constexpr int kStageBytes = kWaves * NBUF * 2 * S::kTileBytes;
   constexpr int kEpiBytes = 2 * kWaves * 16 * 4 + kWaves * 16 * OSTRIDE * 4;
@@ -169,8 +215,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int kvg = blockIdx.y; // KV-head pack: KV heads kvg*PACK .. kvg*PACK+PACK-1
+  // Item-major grid: concurrent workgroups read one KV head of many requests'
+  // pages spread over the pool, which streamed faster on MI355X than grids
+  // that run all heads of an item together (on one XCD or spread over XCDs).
   const int item = blockIdx.x;
+  const int kvg = blockIdx.y; // KV heads kvg*PACK .. kvg*PACK+PACK-1
   const int g = p.group;
   const int gp = g * PACK;    // query heads of the pack (<= 16)
   const int Hk = p.num_kv_heads;
@@ -252,14 +301,19 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   const int pshift = p.page_shift;
   const int pmask = p.page_size - 1;
 
-  // Page ids of this wave's tiles, one per lane (lane i: tile i).  A wave owns
-  // at most 64 tiles because chunks are capped at 64 * kWaves * kTile tokens,
-  // so the main loop reads page ids with v_readlane and never waits on memory
-  // for an address.
-  int vpage = 0;
-  if (paged && my_tiles > 0) {
-    const int ic = min(lane, my_tiles - 1);
-    vpage = pages[(a0 + (wave + ic * kWaves) * kTile) >> pshift];
+  // Where each of this wave's tiles starts (byte offset of its first row in
+  // the K or V pool) and how many of its bytes hold keys of this chunk, one
+  // tile per lane (lane i: tile i; a wave owns at most 64 tiles because
+  // chunks are capped at 64 * kWaves * kTile tokens).  The main loop takes
+  // them with v_readlane and never waits on memory for an address.
+  uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
+  if (lane < my_tiles) {
+    const int ts = a0 + (wave + lane * kWaves) * kTile;
+    const size_t row0 = paged ? (size_t)pages[ts >> pshift] * p.page_size + (ts & pmask) : (size_t)ts;
+    const size_t off = row0 * row_bytes;
+    voff_lo = (uint32_t)off;
+    voff_hi = (uint32_t)(off >> 32);
+    vbytes = (uint32_t)(min(kTile, t_end - ts) * (int)row_bytes);
   }
   // K/V tiles go from HBM straight into this wave's LDS slots with 16-byte
   // DMA loads in cache-line order (each load covers whole row segments of the
@@ -280,17 +334,9 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
   char *wave_stage = smem + wave * NBUF * 2 * S::kTileBytes;
   auto issue = [&](int i, int slot) {
-    const int ts = a0 + (wave + i * kWaves) * kTile;
-    const int nrows = i < my_tiles ? min(kTile, t_end - ts) : 0;
-    size_t row0;
-    if (paged) {
-      const int pid = __builtin_amdgcn_readlane(vpage, min(i, 63));
-      row0 = (size_t)pid * p.page_size + (ts & pmask);
-    } else {
-      row0 = (size_t)ts;
-    }
-    const size_t base = i < my_tiles ? row0 * row_bytes : 0;
-    const int nbytes = nrows * (int)row_bytes;
+    const int li = min(i, 63);
+    const size_t base = ((size_t)__builtin_amdgcn_readlane(voff_hi, li) << 32) | __builtin_amdgcn_readlane(voff_lo, li);
+    const int nbytes = i < my_tiles ? (int)__builtin_amdgcn_readlane(vbytes, li) : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr =
@@ -304,15 +350,22 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   };
   // operand registers of a staged tile: lane (c16, q4) takes pieces 4*pc + q4
   // of row c16 (the same pieces the operand layout below expects)
-  auto read_stage = [&](TileRegs<DE, FP8> &t, int slot) {
-    const char *kst = wave_stage + slot * 2 * S::kTileBytes;
-    const char *vst = kst + S::kTileBytes;
+  uint32_t stage_addr[S::kLaneVec]; // LDS address of piece pc of the K tile in slot 0
+  {
+    const uint32_t base = lds_address(wave_stage) + c16 * S::kRowBytes;
     const int swz = stage_swizzle<DE, FP8>(c16);
 #pragma unroll
-    for (int pc = 0; pc < S::kLaneVec; ++pc) {
-      const int off = c16 * S::kRowBytes + ((4 * pc + q4) ^ swz) * 16;
-      t.k[pc] = *reinterpret_cast<const uint4 *>(kst + off);
-      t.v[pc] = *reinterpret_cast<const uint4 *>(vst + off);
+    for (int pc = 0; pc < S::kLaneVec; ++pc) stage_addr[pc] = base + ((4 * pc + q4) ^ swz) * 16;
+  }
+  auto read_stage = [&](TileRegs<DE, FP8> &t, int slot) {
+    const uint32_t so = slot * 2 * S::kTileBytes;
+    if constexpr (S::kLaneVec == 1) {
+      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], stage_addr[0] + so);
+    } else {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2)
+        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], stage_addr[pc] + so,
+                                    stage_addr[pc + 1] + so);
     }
   };
 
@@ -337,70 +390,88 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     for (int j = 0; j < S::kKSteps; ++j)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, FP8>(t, j), qop[j], s, 0, 0, 0);
     float sv[4];
-    float mx = -INFINITY;
+    if (ts >= t_begin && ts + kTile <= t_end) { // every key of the tile is visible (uniform branch)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = ts + 4 * q4 + r;
-      sv[r] = (tok >= t_begin && tok < t_end) ? s[r] * cscale : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
+      for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = ts + 4 * q4 + r;
+        sv[r] = (tok >= t_begin && tok < t_end) ? s[r] * cscale : -INFINITY;
+      }
     }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = xor32_max(xor16_max(mx));
-    const float m_new = fmaxf(m_run, mx);
-    // no visible key so far for this head: keep the state (selects, no branch)
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f; // m_run = -inf -> 0
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_new) : 0.0f;
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    // Lazy rescale: the reference max m_run moves (and the state is rescaled
+    // by 2^(m_run - m_new)) only when a score exceeds it by more than kLazy,
+    // so weights stay below 2^kLazy and after the first tiles the rescale is
+    // almost never needed.  m + log2(l) and acc / l do not depend on which
+    // reference is used.
+    const bool grow = mx > m_run + kLazy; // m_run = -inf: any visible key
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f; // m_run = -inf -> 0
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
 #pragma unroll
       for (int w = 0; w < S::kOTiles; ++w) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) oacc[w][r] *= alpha;
       }
     }
+    // no visible key so far for this head: weights 0, state unchanged
+    const bool live = m_run != -INFINITY;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_run) : 0.0f;
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
-    // V^T slices and O^T += V^T . P^T
+    // V^T slices (all products first, so the dependent conversions and
+    // accumulations below do not wait on each other), then O^T += V^T . P^T
+    f32x4_t vt[S::kOTiles];
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) {
-      f32x4_t vt;
-      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FP8) {
         const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
         const uint4 wv = t.v[u >> 1];
         const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
         const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
         const long a = (long)(((uint64_t)hi32 << 32) | lo32);
-        vt = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
+        vt[w] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
       } else {
         const uint4 wv = t.v[w >> 1];
         const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
-        vt = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+        vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
       }
-      const s16x4_t va = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[0], vt[1]), pack_bf16x2(vt[2], vt[3])));
-      oacc[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pt, oacc[w], 0, 0, 0);
     }
+    s16x4_t va[S::kOTiles];
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w)
+      va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) oacc[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt, oacc[w], 0, 0, 0);
   };
 
+  // Ring of NBUF staging slots per wave.  A slot is refilled as soon as its
+  // tile has been read into registers, so NBUF tiles are in flight while one
+  // is computed.  Loads are issued for every ring position (past the wave's
+  // last tile they move no bytes), which keeps the vmcnt arithmetic exact.
   if (my_tiles > 0) {
 #pragma unroll
-    for (int j = 0; j < PF; ++j) issue(j, j);
+    for (int j = 0; j < NBUF; ++j) issue(j, j);
     const int n_iter = (my_tiles + NBUF - 1) / NBUF * NBUF;
     for (int it = 0; it < n_iter; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
         const int i = it + j;
-        issue(i + PF, (j + PF) % NBUF);
-        wait_vmem<PF * 2 * S::kDma>(); // tile i has landed; PF newer tiles may still fly
-        if (i < my_tiles) {
-          TileRegs<DE, FP8> t;
-          read_stage(t, j);
-          compute(t, i);
-        }
+        wait_vmem<(NBUF - 1) * 2 * S::kDma>(); // tile i has landed; NBUF - 1 newer tiles may fly
+        TileRegs<DE, FP8> t;
+        read_stage(t, j); // returns with the reads complete
+        issue(i + NBUF, j);
+        if (i < my_tiles) compute(t, i);
       }
     }
+    wait_vmem<0>(); // no DMA may land in the staging area once it is reused
   }
   __syncthreads(); // staging area is reused for the per-wave states below
 
@@ -427,11 +498,9 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 } // namespace
 
 template <int D, int PACK, bool FP8>
-static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, hipStream_t stream) {
+static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
   constexpr int NB = Shape<D * PACK, FP8>::kNBuf;
-  dim3 grid(p.items, p.num_kv_heads / PACK);
-  hipLaunchKernelGGL((partial_mfma_kernel<D, PACK, FP8, NB>), grid, dim3(kThreads), 0, stream, p, w);
-  return hipGetLastError();
+  return launch_kernel(l, partial_mfma_kernel<D, PACK, FP8, NB>, dim3(p.items, p.num_kv_heads / PACK), p, w);
 }
 
 // KV heads per workgroup.  Two heads per pack would make every staged row at
@@ -445,18 +514,18 @@ int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pa
   return (allow_pack && seg < 256 && 2 * group <= 16 && num_kv_heads % 2 == 0) ? 2 : 1;
 }
 
-hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, hipStream_t stream) {
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, const Launch &l) {
   const bool pack2 = p.pack == 2;
   switch (head_dim) {
   case 64:
-    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, w, stream) : launch_mfma_d<64, 1, true>(p, w, stream);
-    return pack2 ? launch_mfma_d<64, 2, false>(p, w, stream) : launch_mfma_d<64, 1, false>(p, w, stream);
+    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, w, l) : launch_mfma_d<64, 1, true>(p, w, l);
+    return pack2 ? launch_mfma_d<64, 2, false>(p, w, l) : launch_mfma_d<64, 1, false>(p, w, l);
   case 128:
-    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, w, stream) : launch_mfma_d<128, 1, true>(p, w, stream);
-    return pack2 ? launch_mfma_d<128, 2, false>(p, w, stream) : launch_mfma_d<128, 1, false>(p, w, stream);
+    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, w, l) : launch_mfma_d<128, 1, true>(p, w, l);
+    return pack2 ? launch_mfma_d<128, 2, false>(p, w, l) : launch_mfma_d<128, 1, false>(p, w, l);
   case 256:
     if (pack2) return hipErrorInvalidValue;
-    return fp8 ? launch_mfma_d<256, 1, true>(p, w, stream) : launch_mfma_d<256, 1, false>(p, w, stream);
+    return fp8 ? launch_mfma_d<256, 1, true>(p, w, l) : launch_mfma_d<256, 1, false>(p, w, l);
   default: return hipErrorInvalidValue;
   }
 }

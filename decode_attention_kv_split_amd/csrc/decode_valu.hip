@@ -79,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = lane / RL; // row group
   const int lr = lane % RL; // lane within row
-  const int kvh = blockIdx.y;
   const int item = blockIdx.x;
+  const int kvh = blockIdx.y;
   const int g = p.group;
   const int Hk = p.num_kv_heads;
 
@@ -233,22 +233,15 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
 }
 
 template <int D, int KVT>
-hipError_t launch_valu_dk(const Params &p, const InlineWork &w, hipStream_t stream) {
-  dim3 grid(p.items, p.num_kv_heads);
+hipError_t launch_valu_dk(const Params &p, const InlineWork &w, const Launch &l) {
+  const dim3 grid(p.items, p.num_kv_heads);
   const int g = p.group;
-  if (g == 1)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 1>), grid, dim3(kThreads), 0, stream, p, w);
-  else if (g == 2)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 2>), grid, dim3(kThreads), 0, stream, p, w);
-  else if (g <= 4)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 4>), grid, dim3(kThreads), 0, stream, p, w);
-  else if (g <= 8)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 8>), grid, dim3(kThreads), 0, stream, p, w);
-  else if constexpr (KVT != DT_FP8)
-    hipLaunchKernelGGL((partial_valu_kernel<D, KVT, 16>), grid, dim3(kThreads), 0, stream, p, w);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (g == 1) return launch_kernel(l, partial_valu_kernel<D, KVT, 1>, grid, p, w);
+  if (g == 2) return launch_kernel(l, partial_valu_kernel<D, KVT, 2>, grid, p, w);
+  if (g <= 4) return launch_kernel(l, partial_valu_kernel<D, KVT, 4>, grid, p, w);
+  if (g <= 8) return launch_kernel(l, partial_valu_kernel<D, KVT, 8>, grid, p, w);
+  if constexpr (KVT != DT_FP8) return launch_kernel(l, partial_valu_kernel<D, KVT, 16>, grid, p, w);
+  return hipErrorInvalidValue;
 }
 
 } // namespace
@@ -256,27 +249,27 @@ hipError_t launch_valu_dk(const Params &p, const InlineWork &w, hipStream_t stre
 // Largest GQA group the vector kernel takes for a KV type.
 int valu_max_group(int kv_dtype) { return kv_dtype == DT_FP8 ? 8 : 16; }
 
-hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, hipStream_t stream) {
+hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, const Launch &l) {
   switch (kv_dtype) {
   case DT_F32:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_F32>(p, w, stream);
-    case 128: return launch_valu_dk<128, DT_F32>(p, w, stream);
-    case 256: return launch_valu_dk<256, DT_F32>(p, w, stream);
+    case 64: return launch_valu_dk<64, DT_F32>(p, w, l);
+    case 128: return launch_valu_dk<128, DT_F32>(p, w, l);
+    case 256: return launch_valu_dk<256, DT_F32>(p, w, l);
     }
     break;
   case DT_BF16:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_BF16>(p, w, stream);
-    case 128: return launch_valu_dk<128, DT_BF16>(p, w, stream);
-    case 256: return launch_valu_dk<256, DT_BF16>(p, w, stream);
+    case 64: return launch_valu_dk<64, DT_BF16>(p, w, l);
+    case 128: return launch_valu_dk<128, DT_BF16>(p, w, l);
+    case 256: return launch_valu_dk<256, DT_BF16>(p, w, l);
     }
     break;
   case DT_FP8:
     switch (head_dim) {
-    case 64: return launch_valu_dk<64, DT_FP8>(p, w, stream);
-    case 128: return launch_valu_dk<128, DT_FP8>(p, w, stream);
-    case 256: return launch_valu_dk<256, DT_FP8>(p, w, stream);
+    case 64: return launch_valu_dk<64, DT_FP8>(p, w, l);
+    case 128: return launch_valu_dk<128, DT_FP8>(p, w, l);
+    case 256: return launch_valu_dk<256, DT_FP8>(p, w, l);
     }
     break;
   }

@@ -21,6 +21,7 @@
 // sum), -inf when the chunk saw no key), I = items per KV head.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,10 +30,26 @@ namespace kvs {
 constexpr int kTile = 16;        // tokens per tile
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
+constexpr int64_t kMaxWorkgroups = (int64_t{1} << 24) - 1; // per partial launch (kept below 2^32 work-items)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// Where a kernel goes: its stream and, optionally, two events that the
+// kernel's own dispatch stamps with its start and end time (no extra marker
+// packets on the stream, so timing does not perturb what is timed).
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel, typename... Args>
+hipError_t launch_kernel(const Launch &l, Kernel kernel, dim3 grid, Args... args) {
+  hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, l.stream, l.start, l.stop, 0, args...);
+  return hipGetLastError();
+}
 
 struct Params {
   const void *q;

@@ -146,8 +146,7 @@ hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hi
   const int packs = p.num_kv_heads / p.pack;
   while (slices * 64 < head_dim && (int64_t)rows * packs * slices < 256) slices *= 2;
   dim3 grid(rows, packs, slices);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(kThreads), 0, stream, p, ml, head_dim, slices);
-  return hipGetLastError();
+  return launch_kernel(Launch{stream}, merge_kernel, grid, p, ml, head_dim, slices);
 }
 
 } // namespace kvs

@@ -117,15 +117,17 @@ typedef struct {
   void *o;    /* [batch, Hq, head_dim], q_dtype, round to nearest even */
   float *lse; /* [batch, Hq] natural-log LSE of the scaled scores, or NULL */
 
-  /* optional profiling: two hipEvent_t recorded on the stream right before
-   * and right after the partial-softmax kernel; NULL to skip */
+  /* optional profiling: two hipEvent_t (created by the caller) that the
+   * partial-softmax kernel's own dispatch stamps with its start and end time,
+   * so hipEventElapsedTime gives that kernel's duration; NULL to skip */
   void *prof_events[2];
 } kvs_decode_args;
 
 /* What a call will launch, computed on the host from kv_len_host. */
 typedef struct {
   int32_t kv_chunk;          /* tokens per split */
-  int32_t items_per_kv_head; /* sum over requests of splits; grid.x of the partial kernel */
+  int32_t items_per_kv_head; /* sum over requests of splits; the partial kernel runs
+                                items_per_kv_head * num_kv_heads / pack workgroups */
   int32_t max_splits;        /* largest number of splits of one request */
   int32_t needs_merge;       /* 1 if some request has more than one split */
   int32_t algo;              /* resolved kvs_algo (VALU, MFMA or MFMA_PACKED) */
@@ -135,7 +137,9 @@ typedef struct {
 
 /* Plan a call without launching anything.  Makes no HIP call when
  * args->num_cus > 0.  Validates the arguments like kvs_decode (except that
- * device pointers may be NULL) and fills *out. */
+ * device pointers may be NULL) and fills *out.  KVS_ERR_UNSUPPORTED when the
+ * partial kernel would need more than 2^24 - 1 workgroups (one launch holds
+ * fewer than 2^32 work-items): raise kv_chunk. */
 kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out);
 
 /* Workspace bytes kvs_decode needs for these arguments (0 on invalid

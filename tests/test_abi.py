@@ -104,6 +104,8 @@ BAD = [
     (dict(P=8, algo=kvs.KVS_ALGO_MFMA), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=kvs.KVS_F32, kv=kvs.KVS_F32, algo=kvs.KVS_ALGO_MFMA), kvs.KVS_ERR_UNSUPPORTED),
     (dict(kv=kvs.KVS_FP8_E4M3, Hq=32, Hk=2, algo=kvs.KVS_ALGO_VALU), kvs.KVS_ERR_UNSUPPORTED),
+    # 2^26 splits of 16 tokens x 32 KV heads: more workgroups than one launch holds
+    (dict(batch=1, P=0, Hq=32, Hk=32, lens=(1 << 30,), chunk=16), kvs.KVS_ERR_UNSUPPORTED),
 ]
 
 
