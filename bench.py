@@ -39,6 +39,12 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 # commands and raw figures).  A figure is reported only while the library
 # sources hash to the digest it was measured with; otherwise traffic is null.
 MEASURED_TRAFFIC = {
+    ("c4_paged_bf16_b64", "partial_mfma_kernel"):
+        {"bytes": 2299427875, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
+    ("c5_paged_fp8_b128", "partial_mfma_kernel"):
+        {"bytes": 1487846789, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
+    ("c3_llama2_7b_32k", "partial_mfma_kernel"):
+        {"bytes": 538181783, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
 }
 
 
