@@ -102,6 +102,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -116,6 +117,9 @@ class HipEvents:
         ms = ctypes.c_float()
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return float(ms.value)
+
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
 
     def destroy(self, evs):
         for e in evs:
@@ -197,8 +201,39 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"same seeded inputs"}
 
 
+def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
+    """Device time of single steps bracketed by events, once with each step
+    preceded by a read of 1 GiB (more than the 256 MB MALL and the L2s
+    together, so the step's inputs are evicted; reading leaves no dirty lines
+    to write back during the step) and once without, so that the difference
+    is the cache effect alone."""
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+
+    def timed(cold: bool):
+        evs = ev.create(2 * steps)
+        for i in range(steps):
+            if cold:
+                flush.max()
+            ev.record(evs[2 * i], stream)
+            step()
+            ev.record(evs[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        us = np.array([ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e3 for i in range(steps)])
+        ev.destroy(evs)
+        p10, p50, p90 = np.percentile(us, [10, 50, 90])
+        return {"step_us_p10_p50_p90": [round(float(x), 2) for x in (p10, p50, p90)],
+                "GBs_at_median": round(nbytes / (p50 * 1e-6) / 1e9, 1)}
+
+    out = {"steps": steps, "flushed": timed(True), "not_flushed": timed(False)}
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
-        with_cpu: bool = True, events: bool = True) -> dict:
+        with_cpu: bool = True, events: bool = True, cold: bool = False) -> dict:
     import torch
 
     import decode_attention_kv_split_amd as kvs
@@ -297,6 +332,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
         "probe_stream_read_GBs": round(probe_read_gbs(), 1),
         "input_gen_s": round(t_gen, 1),
     }
+    if cold:
+        out["cold_cache"] = cold_steps(step, stream, HipEvents(), nbytes, max(20, steps // 2))
     if not events:
         out["roofline"].update(achieved=None, frac=None, kernel_us=None, kernel_us_p10_p50_p90=None)
     if with_cpu:
@@ -316,6 +353,8 @@ def main():
     ap.add_argument("--no-events", action="store_true",
                     help="no per-launch kernel timing (the event stamps add host time per call, which "
                          "shows in the step time of launch-bound workloads); roofline timing fields become null")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single event-bracketed steps with and without a 1 GiB read before each (caches flushed)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run kvs_probe_copy of BYTES bytes (hardware byte-counter calibration)")
     args = ap.parse_args()
@@ -328,7 +367,7 @@ def main():
         sys.exit(2)
     name = CONFIG_ALIASES.get(args.config, args.config)
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
-              events=not args.no_events)
+              events=not args.no_events, cold=args.cold)
     print(json.dumps(res), flush=True)
 
 
