@@ -1,0 +1,282 @@
+"""CPU pins of the pre-attention oracle (encoders, QK-norm, rotary embedding,
+KV append).  Each pin is chosen so that a plausible mistake fails it: the
+planted-mistake tests at the end patch a wrong variant into the oracle and
+check that a pin catches it."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import append as A
+from oracle import codecs as C
+from workloads import make_append_inputs, small_variant
+
+
+# ------------------------------------------------------------------ encoders
+
+def test_bf16_encoder_round_trips_every_code():
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = C.bf16_to_f64(codes)
+    fin = np.isfinite(vals)
+    back = C.f64_to_bf16_codes(vals[fin])
+    # -0.0 keeps its sign through binary32
+    assert np.array_equal(back, codes[fin])
+
+
+def test_bf16_encoder_ties_go_to_even():
+    codes = np.arange(0x0001, 0x7F7F, 7, dtype=np.uint16)  # positive finite, skip the top
+    lo = C.bf16_to_f64(codes)
+    hi = C.bf16_to_f64(codes + 1)
+    mid = (lo + hi) / 2  # exact in binary64
+    got = C.f64_to_bf16_codes(mid)
+    want = np.where(codes % 2 == 0, codes, codes + 1)
+    assert np.array_equal(got, want)
+    # just off the midpoint goes to the nearer neighbour
+    assert np.array_equal(C.f64_to_bf16_codes(np.nextafter(mid, 0)), codes)
+    assert np.array_equal(C.f64_to_bf16_codes(np.nextafter(mid, np.inf)), codes + 1)
+
+
+def test_bf16_encoder_overflow_and_library_agreement():
+    mx = (2 - 2.0 ** -7) * 2.0 ** 127
+    assert C.f64_to_bf16_codes(np.array([mx]))[0] == 0x7F7F
+    assert C.f64_to_bf16_codes(np.array([(2 - 2.0 ** -8) * 2.0 ** 127]))[0] == 0x7F80  # tie, odd -> inf
+    x = np.random.default_rng(1).standard_normal(50000).astype(np.float32) * np.float32(37.0)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(C.f64_to_bf16_codes(x.astype(np.float64)), want)
+
+
+def test_fp8_encoder_round_trips_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = C.fp8_e4m3fn_to_f64(codes)
+    fin = np.isfinite(vals)
+    assert np.array_equal(C.f64_to_fp8_e4m3fn_codes(vals[fin]), codes[fin])
+    assert C.f64_to_fp8_e4m3fn_codes(np.array([np.nan]))[0] == 0x7F
+
+
+def test_fp8_encoder_ties_saturation_subnormals():
+    codes = np.arange(0x01, 0x7E, dtype=np.uint8)  # 0x7E = 448 is the largest finite
+    lo = C.fp8_e4m3fn_to_f64(codes)
+    hi = C.fp8_e4m3fn_to_f64(codes + 1)
+    got = C.f64_to_fp8_e4m3fn_codes((lo + hi) / 2)
+    assert np.array_equal(got, np.where(codes % 2 == 0, codes, codes + 1))
+    enc = lambda v: int(C.f64_to_fp8_e4m3fn_codes(np.array([v]))[0])
+    assert enc(448.0) == 0x7E and enc(464.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(2.0 ** -10) == 0x00          # half the smallest subnormal: tie to even (0)
+    assert enc(3 * 2.0 ** -10) == 0x02      # tie between codes 1 and 2
+    assert enc(2.0 ** -9) == 0x01 and enc(-2.0 ** -9) == 0x81
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+
+
+def test_fp8_encoder_agrees_with_torch_cast():
+    x = np.random.default_rng(2).standard_normal(20000).astype(np.float32) * np.float32(120.0)
+    want = torch.from_numpy(np.clip(x, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(C.f64_to_fp8_e4m3fn_codes(x.astype(np.float64)), want)
+
+
+# ------------------------------------------------------------------ QK-norm
+
+def test_rms_norm_closed_forms():
+    y = A.rms_norm(np.array([3.0, 4.0]), None, 0.0)
+    r = math.sqrt((9 + 16) / 2)
+    assert np.allclose(y, [3 / r, 4 / r], rtol=0, atol=1e-15)
+    x = np.random.default_rng(3).standard_normal((5, 128))
+    y = A.rms_norm(x, None, 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-13)
+    assert np.allclose(A.rms_norm(7.5 * x, None, 0.0), y, rtol=0, atol=1e-13)  # scale invariant
+    w = np.random.default_rng(4).standard_normal(128)
+    assert np.allclose(A.rms_norm(x, w, 0.0), y * w, rtol=0, atol=1e-13)
+    assert np.all(A.rms_norm(np.zeros(64), None, 1e-6) == 0.0)
+    # eps enters under the root: mean(x^2) = 1e-6 and eps = 1e-6 halve the square
+    z = np.full(16, 1e-3)
+    assert np.allclose(A.rms_norm(z, None, 1e-6), z / math.sqrt(2e-6), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ rotary embedding
+
+@pytest.mark.parametrize("interleave", [False, True])
+def test_rope_position_zero_is_identity_and_pairs_keep_norm(interleave):
+    x = np.random.default_rng(5).standard_normal((3, 128))
+    assert np.array_equal(A.rope(x, 0, 10000.0, interleave), x)
+    y = A.rope(x, 1234, 10000.0, interleave)
+    a, b = A._pairs(128, interleave)
+    assert np.allclose(x[:, a] ** 2 + x[:, b] ** 2, y[:, a] ** 2 + y[:, b] ** 2, rtol=1e-13)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rope_first_and_last_pair_closed_form(d):
+    p, theta = 777, 10000.0
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    y = A.rope(e0, p, theta)
+    assert y[0] == pytest.approx(math.cos(p), abs=1e-12) and y[d // 2] == pytest.approx(math.sin(p), abs=1e-12)
+    el = np.zeros(d)
+    el[d // 2 - 1] = 1.0
+    t = p * math.pow(theta, -(d - 2) / d)
+    y = A.rope(el, p, theta)
+    assert y[d // 2 - 1] == pytest.approx(math.cos(t), abs=1e-12) and y[d - 1] == pytest.approx(math.sin(t), abs=1e-12)
+    # interleaved: pair j is (2j, 2j+1)
+    y = A.rope(e0, p, theta, interleave=True)
+    assert y[0] == pytest.approx(math.cos(p), abs=1e-12) and y[1] == pytest.approx(math.sin(p), abs=1e-12)
+
+
+def _relative_position_holds(theta=1e6, d=128, interleave=False):
+    rng = np.random.default_rng(6)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in [(5, 3), (1000, 20), (40000, 39999), (7, 7)]:
+        lhs = A.rope(q, m, theta, interleave) @ A.rope(k, n, theta, interleave)
+        rhs = A.rope(q, m - n, theta, interleave) @ k
+        if abs(lhs - rhs) > 1e-9 * (1 + abs(rhs)):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("theta", [10000.0, 1000000.0])
+@pytest.mark.parametrize("interleave", [False, True])
+def test_rope_scores_depend_only_on_relative_position(theta, interleave):
+    assert _relative_position_holds(theta, 128, interleave)
+
+
+def test_rope_composes_and_interleave_is_a_permutation():
+    x = np.random.default_rng(7).standard_normal(128)
+    assert np.allclose(A.rope(A.rope(x, 300, 1e4), 45, 1e4), A.rope(x, 345, 1e4), rtol=0, atol=1e-12)
+    # interleaved RoPE = rotate-half RoPE conjugated by the pair permutation
+    d = 128
+    perm = np.empty(d, dtype=np.int64)  # position in the rotate-half layout of interleaved index
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    xi = np.random.default_rng(8).standard_normal(d)
+    xh = np.empty(d)
+    xh[perm] = xi
+    yh = A.rope(xh, 999, 1e4)
+    assert np.allclose(A.rope(xi, 999, 1e4, interleave=True), yh[perm], rtol=0, atol=1e-13)
+
+
+def test_rope_dual_theta_differ_only_past_the_first_pair():
+    x = np.random.default_rng(9).standard_normal(256)
+    a, b = A.rope(x, 500, 1e4), A.rope(x, 500, 1e6)
+    assert a[0] == b[0] and a[128] == b[128]   # frequency theta^0 = 1 in both
+    assert not np.allclose(a[1:128], b[1:128])
+
+
+# ------------------------------------------------------------------ append
+
+@pytest.mark.parametrize("name", ["c4_paged_bf16_b64", "c5_paged_fp8_b128", "c3_llama2_7b_32k", "c1_mha_f32"])
+def test_append_then_attend_equals_attention_over_the_extended_cache(name):
+    batch = 1 if name in ("c3_llama2_7b_32k", "c1_mha_f32") else 3
+    lens = [37] if batch == 1 else [0, 16, 45]
+    spec = small_variant(name, batch=batch, lengths=("list", lens))
+    ai = make_append_inputs(spec, seed=31, poison=True, theta=1e6 if name.startswith("c3") else 1e4)
+    s = spec
+    ref = A.append_reference(ai)
+    codes = A.append_codes(ref, s.q_dtype, s.kv_dtype)
+    k_pool, v_pool, kv_len = A.apply_append(ai, codes)
+    # only the new slots changed (raw bits: the f32 padding is NaN)
+    raw = lambda a: a.view(np.uint32) if a.dtype == np.float32 else a
+    axes = (1, 2) if s.page_size == 0 else (2, 3)
+    diff = np.argwhere(np.any(raw(k_pool) != raw(ai.cache.k), axis=axes) |
+                       np.any(raw(v_pool) != raw(ai.cache.v), axis=axes))
+    want = {A.cache_slot(b, int(ai.cache.kv_len[b]), s.page_size, ai.cache.page_indptr, ai.cache.page_indices)
+            for b in range(s.batch)}
+    want = {(r,) if sl is None else (r, sl) for r, sl in want}
+    assert {tuple(int(t) for t in x) for x in diff} <= want
+    # attention over the appended cache, through the decode oracle
+    ci = ai.cache
+    after = type(ci)(ci.spec, codes["q_out"], k_pool, v_pool, kv_len, ci.page_indptr, ci.page_indices,
+                     ci.k_scale, ci.v_scale)
+    o, lse = oracle.decode_reference(after)
+    # independently: old logical K/V plus the new row, attended directly
+    Q = C.decode_codes(codes["q_out"], s.q_dtype).reshape(s.batch, s.num_qo_heads, s.head_dim)
+    f = dict(k=ci.k, v=ci.v, kv_len=ci.kv_len, kv_dtype=s.kv_dtype, page_size=s.page_size,
+             page_indptr=ci.page_indptr, page_indices=ci.page_indices, k_scale=ci.k_scale, v_scale=ci.v_scale)
+    g = s.num_qo_heads // s.num_kv_heads
+    for b in range(s.batch):
+        K, V = oracle.request_kv(b, **f)
+        kn = C.decode_codes(codes["k"][b], s.kv_dtype)
+        vn = C.decode_codes(codes["v"][b], s.kv_dtype)
+        if s.kv_dtype == "fp8":
+            kn, vn = kn * ci.k_scale[b][:, None], vn * ci.v_scale[b][:, None]
+        K = np.concatenate([K, kn[None]])
+        V = np.concatenate([V, vn[None]])
+        for h in range(s.num_qo_heads):
+            o2, l2 = oracle.attend_direct(Q[b, h], K[:, h // g], V[:, h // g], s.sm_scale)
+            assert np.allclose(o[b, h], o2, rtol=0, atol=1e-12) and abs(lse[b, h] - l2) < 1e-12
+
+
+def test_new_token_sees_itself_without_rotation():
+    """Query and key of the same position: the rotations cancel in their dot
+    product, so it equals the dot product of the normalised vectors."""
+    spec = small_variant("c4_paged_bf16_b64", batch=2, lengths=("list", [100, 5000]))
+    ai = make_append_inputs(spec, seed=5, theta=1e4)
+    ref = A.append_reference(ai)
+    Qn = C.decode_codes(ai.q_new, "bf16").reshape(2, 32, 128)
+    Kn = C.decode_codes(ai.k_new, "bf16").reshape(2, 8, 128)
+    for b in range(2):
+        for h in range(32):
+            lhs = ref["q_out"][b, h] @ ref["k"][b, h // 4]
+            rhs = A.rms_norm(Qn[b, h], ai.q_norm_weight, ai.eps) @ A.rms_norm(Kn[b, h // 4], ai.k_norm_weight, ai.eps)
+            assert lhs == pytest.approx(rhs, rel=1e-12, abs=1e-12)
+
+
+def test_append_position_is_kv_len():
+    spec = small_variant("c4_paged_bf16_b64", batch=2, lengths=("list", [15, 16]))
+    ai = make_append_inputs(spec, seed=3, norm=False, theta=1e4)
+    ref = A.append_reference(ai)
+    K = C.decode_codes(ai.k_new, "bf16").reshape(2, 8, 128)
+    for b, L in enumerate([15, 16]):
+        assert np.allclose(ref["k"][b], A.rope(K[b], L, 1e4), rtol=0, atol=0)
+        page, slot = A.cache_slot(b, L, 16, ai.cache.page_indptr, ai.cache.page_indices)
+        assert slot == L % 16 and page == ai.cache.page_indices[ai.cache.page_indptr[b] + L // 16]
+    # request 1 (16 tokens) needs a second page for its new token
+    assert ai.cache.page_indptr[2] - ai.cache.page_indptr[1] == 2
+
+
+def test_fp8_append_quantises_with_the_existing_scale():
+    spec = small_variant("c5_paged_fp8_b128", batch=2, lengths=("list", [300, 40]))
+    ai = make_append_inputs(spec, seed=8, theta=1e4)
+    ref = A.append_reference(ai)
+    codes = A.append_codes(ref, "bf16", "fp8")
+    for b in range(2):
+        x = ref["k"][b] * ai.cache.k_scale[b][:, None]  # undo the division
+        dq = C.fp8_e4m3fn_to_f64(codes["k"][b]) * ai.cache.k_scale[b][:, None]
+        step = np.abs(x) * 2.0 ** -3 + 2.0 ** -9 * ai.cache.k_scale[b][:, None]
+        sat = np.abs(x) > 448 * ai.cache.k_scale[b][:, None]
+        assert np.all((np.abs(dq - x) <= step) | sat)
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def test_planted_rope_sign_error_is_caught(monkeypatch):
+    good = A.rope
+
+    def bad(x, pos, theta, interleave=False):
+        y = good(x, pos, theta, interleave)
+        a, b = A._pairs(np.asarray(x).shape[-1], interleave)
+        t = A.rope_angles(pos, np.asarray(x).shape[-1], theta)
+        x = np.asarray(x, dtype=np.float64)
+        y[..., a] = x[..., a] * np.cos(t) + x[..., b] * np.sin(t)  # wrong sign
+        return y
+
+    monkeypatch.setattr(A, "rope", bad)
+    assert not _relative_position_holds()
+
+
+def test_planted_frequency_exponent_error_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "rope_angles",
+                        lambda pos, d, theta: float(pos) * np.power(float(theta), -np.arange(d // 2) / d))
+    with pytest.raises(AssertionError):
+        test_rope_first_and_last_pair_closed_form(128)
+
+
+def test_planted_pairing_error_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "_pairs", lambda d, interleave: (np.arange(0, d, 2), np.arange(1, d, 2)))
+    with pytest.raises(AssertionError):
+        test_rope_first_and_last_pair_closed_form(128)
+
+
+def test_planted_position_error_is_caught(monkeypatch):
+    good = A.transform_head
+    monkeypatch.setattr(A, "transform_head", lambda x, pos, *r: good(x, pos + 1, *r))
+    with pytest.raises(AssertionError):
+        test_append_position_is_kv_len()

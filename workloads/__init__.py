@@ -42,6 +42,8 @@ __all__ = [
     "DecodeInputs",
     "make_inputs",
     "CONFIGS",
+    "AppendInputs",
+    "make_append_inputs",
     "config",
     "small_variant",
     "F32",
@@ -149,13 +151,15 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = False,
                 permute_pages: bool = True, perm_seed: Optional[int] = None,
-                lengths: Optional[np.ndarray] = None) -> DecodeInputs:
+                lengths: Optional[np.ndarray] = None, reserve_tokens: int = 0) -> DecodeInputs:
     """Draw one seeded workload.
 
     ``perm_seed`` (paged only) replaces the permutation stream's seed while
     keeping every value identical; ``permute_pages=False`` lays pages out in
     logical order (identity page table).  ``lengths`` overrides the length
-    draw (used by edge-case tests).
+    draw (used by edge-case tests).  ``reserve_tokens`` gives every request
+    room for that many more tokens (pages, or rows of a contiguous cache),
+    filled like the padding of a last page.
     """
     seed = spec.seed if seed is None else seed
     r_len, r_perm, r_q, r_k, r_v = _rng(seed)
@@ -200,9 +204,17 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
     del k_log, v_log
 
     if P == 0:
+        if reserve_tokens:
+            pad = np.zeros((reserve_tokens,) + k_codes.shape[1:], k_codes.dtype)
+            if poison:
+                fill = _POISON[spec.kv_dtype]
+                pad = (np.full(pad.shape, np.uint32(fill), np.uint32).view(np.float32) if spec.kv_dtype == F32
+                       else np.full(pad.shape, fill, pad.dtype))
+            k_codes = np.concatenate([k_codes, pad])
+            v_codes = np.concatenate([v_codes, pad])
         return DecodeInputs(spec, q_codes, k_codes, v_codes, kv_len, None, None, k_scale, v_scale)
 
-    n_pages = (kv_len.astype(np.int64) + P - 1) // P
+    n_pages = (kv_len.astype(np.int64) + reserve_tokens + P - 1) // P
     indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
     N = int(indptr[-1])
     perm = r_perm.permutation(N).astype(np.int32) if permute_pages else np.arange(N, dtype=np.int32)
@@ -277,3 +289,47 @@ def small_variant(name: str, *, batch: Optional[int] = None, lengths: Optional[t
         kw["seed"] = seed
     return dataclasses.replace(base, name=base.name + "_small", **kw)
 
+
+
+# ----------------------------------------------------------------------------
+# the step before attention: QK-norm, rotary embedding, KV append
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class AppendInputs:
+    """One decode step's new token for every request, and the cache it joins.
+
+    ``cache`` is a DecodeInputs whose requests each have room for one more
+    token; the new token goes to position kv_len[b].
+    """
+    cache: DecodeInputs
+    q_new: np.ndarray   # [B, Hq, d] codes of q's type
+    k_new: np.ndarray   # [B, Hk, d] codes of q's type
+    v_new: np.ndarray   # [B, Hk, d] codes of q's type
+    q_norm_weight: Optional[np.ndarray]  # float32 [d] or None (no QK-norm)
+    k_norm_weight: Optional[np.ndarray]
+    eps: float
+    theta: float        # 0: no rotary embedding
+    interleave: bool
+
+
+def make_append_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, norm: bool = True,
+                       theta: float = 10000.0, interleave: bool = False, eps: float = 1e-6,
+                       poison: bool = False, lengths: Optional[np.ndarray] = None) -> AppendInputs:
+    """Draw a cache like make_inputs (with one reserved slot per request) and
+    the new token: q, k, v ~ N(0, 1) in q's storage type; QK-norm weights
+    ~ N(1, 0.25) per dimension when ``norm``."""
+    seed = spec.seed if seed is None else seed
+    cache = make_inputs(spec, seed, poison=poison, lengths=lengths, reserve_tokens=1)
+    r_q, r_k, r_v, r_w = [np.random.Generator(np.random.PCG64(s))
+                          for s in np.random.SeedSequence([seed, 0xA11]).spawn(4)]
+    B, Hq, Hk, d = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    q = r_q.standard_normal((B, Hq, d), dtype=np.float32)
+    k = r_k.standard_normal((B, Hk, d), dtype=np.float32)
+    v = r_v.standard_normal((B, Hk, d), dtype=np.float32)
+    wq = wk = None
+    if norm:
+        wq = (1.0 + 0.25 * r_w.standard_normal(d)).astype(np.float32)
+        wk = (1.0 + 0.25 * r_w.standard_normal(d)).astype(np.float32)
+    return AppendInputs(cache, _store(q, spec.q_dtype), _store(k, spec.q_dtype), _store(v, spec.q_dtype),
+                        wq, wk, float(eps), float(theta), bool(interleave))
