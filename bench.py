@@ -341,12 +341,139 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     return out
 
 
+def append_bytes(ai) -> int:
+    """Bytes the pre-attention step must move once: q, k, v of the new token
+    in, q_out and the new K/V slots out, the norm weights, kv_len, each
+    request's page-table entry (and its indptr pair), fp8 scales."""
+    s = ai.cache.spec
+    B, Hq, Hk, d = s.batch, s.num_qo_heads, s.num_kv_heads, s.head_dim
+    bq, bkv = _BYTES[s.q_dtype], _BYTES[s.kv_dtype]
+    n = 2 * B * Hq * d * bq + 2 * B * Hk * d * bq + 2 * B * Hk * d * bkv + 4 * B
+    n += 4 * d * ((ai.q_norm_weight is not None) + (ai.k_norm_weight is not None))
+    if s.page_size:
+        n += 12 * B
+    if s.kv_dtype == "fp8":
+        n += 2 * 4 * B * Hk
+    return n
+
+
+def run_append_op(config_name: str, steps: int, warmup: int, with_decode: bool, with_cpu: bool,
+                  algo: str = "auto") -> dict:
+    """Time kvs_append alone (op 'append') or kvs_append followed by
+    kvs_decode over the extended cache (op 'step': the attention part of one
+    decode step of one layer).  Each call rewrites the same slot, so the
+    calls are identical; device kv_len stays the new token's position for the
+    append, and a second array holds kv_len + 1 for the decode."""
+    import torch
+
+    import decode_attention_kv_split_amd as kvs
+    from workloads import CONFIGS, make_append_inputs
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from kvs_testlib import _codes_to_torch, to_torch
+
+    kvs.load_library()
+    spec = CONFIGS[config_name]
+    theta = 1e6 if config_name == "c2_gemma3_1b" else 1e4
+    t_gen = time.perf_counter()
+    ai = make_append_inputs(spec, theta=theta)
+    t = to_torch(ai.cache)
+    t_gen = time.perf_counter() - t_gen
+    q = _codes_to_torch(ai.q_new, spec.q_dtype)
+    k = _codes_to_torch(ai.k_new, spec.q_dtype)
+    v = _codes_to_torch(ai.v_new, spec.q_dtype)
+    wq = torch.from_numpy(ai.q_norm_weight).cuda()
+    wk = torch.from_numpy(ai.k_norm_weight).cuda()
+    aa, keep_a = kvs.make_append_args(q, k, v, t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
+                                      page_indices=t.get("page_indices"), k_scale=t.get("k_scale"),
+                                      v_scale=t.get("v_scale"), q_norm_weight=wq, k_norm_weight=wk,
+                                      norm_eps=ai.eps, rope_theta=ai.theta, rope_interleave=ai.interleave)
+    kv_len1 = t["kv_len"] + 1
+    host1 = ai.cache.kv_len + 1
+    da, keep_d = kvs.make_args(keep_a[0], t["k"], t["v"], kv_len1, page_indptr=t.get("page_indptr"),
+                               page_indices=t.get("page_indices"), kv_len_host=host1,
+                               k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=spec.sm_scale,
+                               window=spec.window, algo=algo)
+    ws = torch.empty(max(kvs.kvs_decode_workspace_bytes(da), 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    every = max(1, steps // 20)
+    stamped = [i for i in range(steps) if i % every == 0]
+    ev = HipEvents()
+    evs = ev.create(2 * len(stamped))
+    pair = {i: (evs[2 * j], evs[2 * j + 1]) for j, i in enumerate(stamped)}
+
+    def step(e0=None, e1=None):
+        aa.prof_events[0], aa.prof_events[1] = e0, e1
+        st = kvs.kvs_append(aa, stream)
+        if st != kvs.KVS_OK:
+            raise kvs.KvsError(st, "kvs_append")
+        if with_decode:
+            st = kvs.kvs_decode(da, ws.data_ptr(), ws.numel(), stream)
+            if st != kvs.KVS_OK:
+                raise kvs.KvsError(st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(*pair.get(i, (None, None)))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = [ev.elapsed_ms(*pair[i]) for i in stamped]
+    ev.destroy(evs)
+    nb_append = append_bytes(ai)
+    nb = nb_append
+    if with_decode:
+        after = type(ai.cache)(spec, ai.cache.q, ai.cache.k, ai.cache.v, host1.astype(np.int32),
+                               ai.cache.page_indptr, ai.cache.page_indices, ai.cache.k_scale, ai.cache.v_scale)
+        nb += algorithmic_bytes(after)
+    ms = wall * 1e3 / steps
+    kus = float(np.mean(k_ms)) * 1e3
+    out = {
+        "metric": ("kvs_append (QK-norm + RoPE + KV append) " if not with_decode else
+                   "kvs_append + kvs_decode (attention part of one decode step) ") + "us/call and achieved HBM GB/s",
+        "value": round(nb / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "pct_of_peak": round(100.0 * nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{spec.q_dtype} q/k/v in, {spec.kv_dtype} cache, fp32 arithmetic (angles fp64)",
+        "data": "synthetic (seeded; N(0,1) new token, QK-norm weights N(1, 0.25), theta %g)" % theta,
+        "config": {"workload": config_name, "op": "step" if with_decode else "append", "batch": spec.batch,
+                   "num_qo_heads": spec.num_qo_heads, "num_kv_heads": spec.num_kv_heads,
+                   "head_dim": spec.head_dim, "page_size": spec.page_size, "kv_dtype": spec.kv_dtype},
+        "roofline": {"bound": "hbm", "kernel": "append_kernel", "achieved": round(nb_append / (kus * 1e-6) / 1e9, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(nb_append / (kus * 1e-6) / 1e9 / PEAK_HBM_GBS, 5),
+                     "traffic": None, "kernel_us": round(kus, 2), "algorithmic_bytes": nb_append,
+                     "kernel_launches_timed": len(stamped),
+                     "note": "a few MB per call: launch-latency-bound, far below the HBM roofline"},
+        "input_gen_s": round(t_gen, 1),
+    }
+    if with_cpu:
+        import oracle
+
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 5.0:
+            oracle.append_reference(ai)
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(nb_append * n / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"fp64 oracle append_reference over the whole batch, {n} calls, {dt:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=DEFAULT)
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "step"],
+                    help="decode: the split-KV decode attention (default); append: QK-norm + rotary "
+                         "embedding + KV append of the new token; step: append then decode")
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "mfma_packed", "valu"])
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -366,6 +493,11 @@ def main():
               "(each GPU would run its own requests or KV heads independently).", file=sys.stderr)
         sys.exit(2)
     name = CONFIG_ALIASES.get(args.config, args.config)
+    if args.op != "decode":
+        res = run_append_op(name, args.steps, args.warmup, args.op == "step", with_cpu=not args.no_cpu,
+                            algo=args.algo)
+        print(json.dumps(res), flush=True)
+        return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold)
     print(json.dumps(res), flush=True)

@@ -8,12 +8,14 @@ Low level (same names as the C ABI in ``include/kvsplit.h``):
     kvs_decode(args, workspace_ptr, workspace_bytes, stream) -> status
     kvs_decode_plan(args) -> KvsPlanInfo
     kvs_decode_workspace_bytes(args) -> int
+    kvs_append(args, stream) -> status
     kvs_status_string(status) -> str
     kvs_abi_version() -> int
 High level, on torch tensors already on the GPU:
     decode(...)              any layout, returns (o, lse)
     single_decode(q, k, v)   one request, contiguous cache
     batch_decode_paged(...)  paged cache
+    append(...)              QK-norm, rotary embedding and KV append of the new token
 """
 from __future__ import annotations
 
@@ -27,12 +29,15 @@ __all__ = [
     "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
     "KVS_ALGO_MFMA_PACKED",
-    "KvsDecodeArgs", "KvsPlanInfo", "KvsError",
+    "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
     "library_path", "load_library",
-    "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_status_string", "kvs_abi_version",
+    "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_append", "kvs_status_string",
+    "kvs_abi_version", "KVS_ABI_VERSION",
     "kvs_probe_stream_read", "kvs_probe_copy",
-    "decode", "single_decode", "batch_decode_paged",
+    "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
+
+KVS_ABI_VERSION = 2
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
@@ -88,6 +93,36 @@ class KvsPlanInfo(ctypes.Structure):
     ]
 
 
+class KvsAppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("q_in", ctypes.c_void_p),
+        ("k_in", ctypes.c_void_p),
+        ("v_in", ctypes.c_void_p),
+        ("q_out", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("page_indptr", ctypes.c_void_p),
+        ("page_indices", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("q_norm_weight", ctypes.c_void_p),
+        ("k_norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("rope_interleave", ctypes.c_int32),
+        ("prof_events", ctypes.c_void_p * 2),
+    ]
+
+
 class KvsError(RuntimeError):
     def __init__(self, status: int, what: str = "kvs_decode"):
         self.status = status
@@ -115,6 +150,8 @@ def load_library():
             lib.kvs_decode_plan.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.POINTER(KvsPlanInfo)]
             lib.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
             lib.kvs_decode_workspace_bytes.argtypes = [ctypes.POINTER(KvsDecodeArgs)]
+            lib.kvs_append.restype = ctypes.c_int
+            lib.kvs_append.argtypes = [ctypes.POINTER(KvsAppendArgs), ctypes.c_void_p]
             lib.kvs_status_string.restype = ctypes.c_char_p
             lib.kvs_status_string.argtypes = [ctypes.c_int]
             lib.kvs_abi_version.restype = ctypes.c_int
@@ -147,6 +184,10 @@ def kvs_decode_plan(args: KvsDecodeArgs) -> KvsPlanInfo:
 
 def kvs_decode_workspace_bytes(args: KvsDecodeArgs) -> int:
     return int(load_library().kvs_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def kvs_append(args: KvsAppendArgs, stream: int) -> int:
+    return int(load_library().kvs_append(ctypes.byref(args), ctypes.c_void_p(stream or None)))
 
 
 def kvs_status_string(status: int) -> str:
@@ -324,3 +365,78 @@ def batch_decode_paged(q, k_pages, v_pages, page_indptr, page_indices, kv_len, *
     return decode(q, k_pages, v_pages, kv_len, page_indptr=page_indptr, page_indices=page_indices,
                   kv_len_host=kv_len_host, sm_scale=sm_scale, window=window, kv_chunk=kv_chunk, algo=algo,
                   k_scale=k_scale, v_scale=v_scale)
+
+
+def make_append_args(q, k, v, k_cache, v_cache, kv_len, *, page_indptr=None, page_indices=None,
+                     k_scale=None, v_scale=None, q_norm_weight=None, k_norm_weight=None,
+                     norm_eps: float = 1e-6, rope_theta: float = 10000.0, rope_interleave: bool = False,
+                     q_out=None) -> Tuple[KvsAppendArgs, object]:
+    """Build the C argument block of kvs_append from torch tensors.
+
+    q [batch, Hq, d], k and v [batch, Hk, d] (q's dtype); the cache as for
+    decode (paged [num_pages, page_size, Hk, d] or contiguous
+    [capacity, Hk, d]); kv_len int32 [batch] on the device (the new token's
+    position).  q_out defaults to a new tensor; it may be q."""
+    import torch
+
+    device = q.device
+    B, Hq, d = q.shape
+    Hk = k.shape[1]
+    if k.shape != (B, Hk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [batch, num_kv_heads, head_dim] in q's dtype")
+    paged = page_indptr is not None
+    if paged:
+        num_pages, P, Hk2, d2 = k_cache.shape
+    else:
+        num_pages, Hk2, d2 = k_cache.shape
+        P = 0
+    if (Hk2, d2) != (Hk, d) or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("cache shape does not match the new token")
+    if kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("kv_len must be int32 [batch]")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_len, "kv_len"),
+                 (page_indptr, "page_indptr"), (page_indices, "page_indices"), (k_scale, "k_scale"),
+                 (v_scale, "v_scale"), (q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight"),
+                 (q_out, "q_out")):
+        _check_dev(t, n, device)
+    for w, n in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if w is not None and (w.dtype != torch.float32 or w.numel() != d):
+            raise ValueError(f"{n} must be float32 [head_dim]")
+    a = KvsAppendArgs()
+    a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = B, Hq, Hk, d
+    a.q_dtype = _dtype_code(q, "q")
+    a.kv_dtype = _dtype_code(k_cache, "kv")
+    a.page_size, a.num_pages = P, num_pages
+    a.q_in, a.k_in, a.v_in, a.q_out = _ptr(q), _ptr(k), _ptr(v), _ptr(q_out)
+    a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
+    a.page_indptr, a.page_indices = _ptr(page_indptr), _ptr(page_indices)
+    a.kv_len = _ptr(kv_len)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.q_norm_weight, a.k_norm_weight = _ptr(q_norm_weight), _ptr(k_norm_weight)
+    a.norm_eps = float(norm_eps)
+    a.rope_theta = float(rope_theta)
+    a.rope_interleave = int(bool(rope_interleave))
+    return a, (q_out,)
+
+
+def append(q, k, v, k_cache, v_cache, kv_len, *, page_indptr=None, page_indices=None, k_scale=None,
+           v_scale=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6,
+           rope_theta: float = 10000.0, rope_interleave: bool = False, q_out=None, stream=None):
+    """QK-norm and rotary embedding of the new token, and its K/V stored at
+    position kv_len[b] of each request's cache.  Returns q_out.  kv_len is
+    not changed."""
+    import torch
+
+    a, keep = make_append_args(q, k, v, k_cache, v_cache, kv_len, page_indptr=page_indptr,
+                               page_indices=page_indices, k_scale=k_scale, v_scale=v_scale,
+                               q_norm_weight=q_norm_weight, k_norm_weight=k_norm_weight, norm_eps=norm_eps,
+                               rope_theta=rope_theta, rope_interleave=rope_interleave, q_out=q_out)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
+    st = kvs_append(a, s)
+    if st != KVS_OK:
+        if st in (KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED):
+            raise ValueError(f"kvs_append: {kvs_status_string(st)}")
+        raise KvsError(st, "kvs_append")
+    return keep[0]

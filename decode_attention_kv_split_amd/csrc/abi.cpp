@@ -16,6 +16,7 @@ hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_di
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack);
+hipError_t launch_append(const kvs_append_args *a, const Launch &l);
 } // namespace kvs
 
 namespace {
@@ -88,6 +89,32 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   default:
     return KVS_ERR_INVALID_ARG;
   }
+  return KVS_OK;
+}
+
+// Host-only checks of kvs_append.
+kvs_status validate_append(const kvs_append_args *a) {
+  if (!a) return KVS_ERR_INVALID_ARG;
+  if (a->batch < 1 || a->num_qo_heads < 1 || a->num_kv_heads < 1) return KVS_ERR_INVALID_ARG;
+  if (a->num_qo_heads % a->num_kv_heads) return KVS_ERR_INVALID_ARG;
+  if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) return KVS_ERR_UNSUPPORTED;
+  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 2) return KVS_ERR_INVALID_ARG;
+  const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
+  if (!pair_ok) return KVS_ERR_UNSUPPORTED;
+  if (a->page_size < 0 || a->num_pages < 1) return KVS_ERR_INVALID_ARG;
+  if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
+  if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
+  if (!(a->norm_eps >= 0.0f) || !std::isfinite(a->norm_eps)) return KVS_ERR_INVALID_ARG;
+  if (!(a->rope_theta >= 0.0f) || !std::isfinite(a->rope_theta)) return KVS_ERR_INVALID_ARG;
+  if (a->rope_interleave != 0 && a->rope_interleave != 1) return KVS_ERR_INVALID_ARG;
+  if ((int64_t)a->batch * (a->num_qo_heads + a->num_kv_heads) > ((int64_t)1 << 32) / kvs::kThreads * kvs::kWaves)
+    return KVS_ERR_UNSUPPORTED; // one launch holds fewer than 2^32 work-items
+  if (!a->q_in || !a->k_in || !a->v_in || !a->q_out || !a->k_cache || !a->v_cache || !a->kv_len)
+    return KVS_ERR_INVALID_ARG;
+  if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
+  if (a->kv_dtype == KVS_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
   return KVS_OK;
 }
 
@@ -217,6 +244,14 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
     if (e != hipSuccess) return KVS_ERR_HIP;
   }
   return KVS_OK;
+}
+
+kvs_status kvs_append(const kvs_append_args *args, hipStream_t stream) {
+  const kvs_status st = validate_append(args);
+  if (st != KVS_OK) return st;
+  const kvs::Launch l{stream, reinterpret_cast<hipEvent_t>(args->prof_events[0]),
+                      reinterpret_cast<hipEvent_t>(args->prof_events[1])};
+  return kvs::launch_append(args, l) == hipSuccess ? KVS_OK : KVS_ERR_HIP;
 }
 
 const char *kvs_status_string(int s) {

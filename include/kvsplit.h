@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 1
+#define KVS_ABI_VERSION 2
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -156,6 +156,75 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
  * visible K/V values are finite. */
 kvs_status kvs_decode(const kvs_decode_args *args, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The step before attention: QK-norm, rotary embedding and KV append for the
+ * one new token of every request (one decode step of one layer).
+ *
+ * For request b with position p = kv_len[b] (the tokens already cached):
+ *   q_out[b,h,:]    = rope(norm(q_in[b,h,:], q_norm_weight), p)     h < Hq
+ *   K[b, p, kh, :]  = store(rope(norm(k_in[b,kh,:], k_norm_weight), p))
+ *   V[b, p, kh, :]  = store(v_in[b,kh,:])                          kh < Hk
+ * norm(x, w) = x / sqrt(mean(x^2) + norm_eps) * w over the head dimension,
+ *   skipped when the weight is NULL (QK-norm: the FlashInfer-from-JAX
+ *   tutorial page, Gemma 3 section);
+ * rope(x, p): dimension pair j (j < head_dim/2) turns by the angle
+ *   p * rope_theta^(-2j/head_dim), (x_a, x_b) -> (x_a cos - x_b sin,
+ *   x_a sin + x_b cos), with pairs (j, j + head_dim/2), or (2j, 2j + 1) when
+ *   rope_interleave = 1; skipped when rope_theta == 0 (apply_rope and the
+ *   per-layer theta -- 10,000 local, 1,000,000 global: same page, the
+ *   three-kernels and Gemma 3 sections);
+ * store: to kv_dtype, nearest even; FP8_E4M3 stores the nearest code of
+ *   x / k_scale[b,kh] (v_scale for V), saturating at +-448 ("Beyond the
+ *   Memory Wall", section "2. FlashInfer": appending to the growing, paged,
+ *   fp8 cache).
+ * Angles are formed in double precision; the rest runs in fp32.
+ *
+ * Layouts as for kvs_decode: q_in, q_out [batch, Hq, d]; k_in, v_in
+ * [batch, Hk, d]; the cache [num_pages, page_size, Hk, d] or, with
+ * page_size 0 (batch 1), [num_pages, Hk, d] where num_pages is then the
+ * capacity in tokens.  q_out may be q_in (in place).
+ * kv_len is read, not changed: the caller raises kv_len and kv_len_host by
+ * one before the decode call that should see the new token.
+ * Errors: argument checks run on the host before any HIP call, as for
+ * kvs_decode.  Not checked (device data): a request whose page list does
+ * not cover position p, or whose page id there is >= num_pages (contiguous:
+ * p >= capacity), gets q_out but no cache write.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;   /* 64, 128 or 256 */
+  int32_t q_dtype;    /* q_in, k_in, v_in, q_out: KVS_F32 or KVS_BF16 */
+  int32_t kv_dtype;   /* cache; pairs as for kvs_decode */
+  int32_t page_size;  /* 0: contiguous; else a power of two */
+  int32_t num_pages;  /* paged: pages in each pool; contiguous: capacity (tokens) */
+
+  const void *q_in;
+  const void *k_in;
+  const void *v_in;
+  void *q_out;
+  void *k_cache;
+  void *v_cache;
+  const int32_t *page_indptr;  /* paged only, as for kvs_decode */
+  const int32_t *page_indices; /* paged only */
+  const int32_t *kv_len;       /* device [batch]: position of the new token */
+  const float *k_scale;        /* FP8 cache only, [batch, Hk] */
+  const float *v_scale;
+  const float *q_norm_weight;  /* device [head_dim] fp32, or NULL: no q norm */
+  const float *k_norm_weight;  /* device [head_dim] fp32, or NULL: no k norm */
+  float norm_eps;              /* >= 0 */
+  float rope_theta;            /* 0: no rotary embedding; else > 0 */
+  int32_t rope_interleave;     /* 0 or 1 */
+
+  /* optional profiling: two hipEvent_t stamped by the kernel's own dispatch
+   * with its start and end; NULL to skip */
+  void *prof_events[2];
+} kvs_append_args;
+
+/* Run the step asynchronously on `stream`.  Allocates nothing. */
+kvs_status kvs_append(const kvs_append_args *args, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *kvs_status_string(int status);

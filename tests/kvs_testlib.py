@@ -88,3 +88,147 @@ def compare(o, lse, o_ref, lse_ref, kv_dtype, rows=None):
     rmax = float(np.max(rel)) if rel.size else 0.0
     assert rmax <= LSE_REL, f"lse relative error {rmax:.3e} > {LSE_REL}"
     return err, rmax
+
+
+# ----------------------------------------------------------------------------
+# the step before attention (kvs_append)
+# ----------------------------------------------------------------------------
+
+def _codes_to_torch(x, dt, device="cuda"):
+    import torch
+
+    if dt == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, np.uint8)).to(device)
+
+
+def _to_codes(t, dt):
+    import torch
+
+    t = t.detach().cpu()
+    if dt == "f32":
+        return t.numpy().astype(np.float32)
+    if dt == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.uint8).numpy()
+
+
+def run_append(ai, in_place: bool = False, tensors=None):
+    """Run kvs_append on an AppendInputs; returns (dict of numpy codes
+    q_out / k_pool / v_pool, the device tensors of the cache)."""
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    s = ai.cache.spec
+    t = tensors if tensors is not None else to_torch(ai.cache)
+    q = _codes_to_torch(ai.q_new, s.q_dtype)
+    k = _codes_to_torch(ai.k_new, s.q_dtype)
+    v = _codes_to_torch(ai.v_new, s.q_dtype)
+    wq = None if ai.q_norm_weight is None else torch.from_numpy(ai.q_norm_weight).cuda()
+    wk = None if ai.k_norm_weight is None else torch.from_numpy(ai.k_norm_weight).cuda()
+    q_out = kvs.append(q, k, v, t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
+                       page_indices=t.get("page_indices"), k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
+                       q_norm_weight=wq, k_norm_weight=wk, norm_eps=ai.eps, rope_theta=ai.theta,
+                       rope_interleave=ai.interleave, q_out=q if in_place else None)
+    torch.cuda.synchronize()
+    got = {"q_out": _to_codes(q_out, s.q_dtype), "k_pool": _to_codes(t["k"], s.kv_dtype),
+           "v_pool": _to_codes(t["v"], s.kv_dtype)}
+    return got, t
+
+
+# An fp32 kernel and the fp64 oracle may round a value that lies within this
+# relative distance of a tie between two codes to either neighbour.
+TIE_REL = 2.0 ** -16
+
+
+def check_codes(got, y, dtype, what="", mag=None):
+    """Stored codes against the oracle's float64 values y (same shape).
+
+    Each code must be the nearest-even code of y, except where y lies within
+    TIE_REL * max(|y|, mag) of the midpoint between that code and a
+    neighbour: there both neighbours are right for an fp32 computation.
+    ``mag`` bounds the size of the terms y is computed from (a rotated
+    element a c - b s carries the rounding of |a| + |b|, not of |y|).
+    Returns the number of elements that took the tie allowance (at most 1%)."""
+    import oracle
+
+    got = np.asarray(got)
+    y = np.asarray(y, dtype=np.float64)
+    assert got.shape == y.shape, (what, got.shape, y.shape)
+    scale = np.abs(y) if mag is None else np.maximum(np.abs(y), np.asarray(mag, np.float64))
+    if dtype == "f32":
+        err = np.abs(got.astype(np.float64) - y)
+        bad = err > TIE_REL * np.maximum(scale, 1.0)
+        assert not np.any(bad), f"{what}: fp32 error {float(np.max(err)):.3e}"
+        return 0
+    want = oracle.encode_codes(y, dtype)
+    diff = got != want
+    if not np.any(diff):
+        return 0
+    gv = oracle.decode_codes(got[diff], dtype)
+    wv = oracle.decode_codes(want[diff], dtype)
+    yd = y[diff]
+    if dtype == "fp8":
+        yd = np.clip(yd, -448.0, 448.0)
+    mid = (gv + wv) / 2
+    near_tie = np.abs(yd - mid) <= TIE_REL * np.maximum(scale[diff], 2.0 ** -6)
+    assert np.all(near_tie), (f"{what}: {int(np.sum(~near_tie))} codes differ away from a tie; "
+                              f"first y={yd[~near_tie][:4]} got={gv[~near_tie][:4]} want={wv[~near_tie][:4]}")
+    n = int(np.sum(diff))
+    assert n <= max(1, got.size // 100), f"{what}: {n} of {got.size} codes at ties"
+    return n
+
+
+def _term_size(ai, x, weight, norm):
+    """|a| + |b| of the rotation pair of every element of the rows x (the
+    terms whose rounding an fp32 rotation carries), |x| without rotation."""
+    import oracle
+    from oracle import append as A
+
+    z = np.abs(oracle.rms_norm(x, weight, ai.eps) if norm else np.asarray(x, np.float64))
+    if ai.theta <= 0:
+        return z
+    a, b = A._pairs(z.shape[-1], ai.interleave)
+    m = np.empty_like(z)
+    m[..., a] = z[..., a] + z[..., b]
+    m[..., b] = m[..., a]
+    return m
+
+
+def check_append(ai, got):
+    """Every output of kvs_append against the oracle: q_out, the new K/V
+    slots, and the rest of both pools unchanged bit for bit."""
+    import oracle
+
+    c = ai.cache
+    s = c.spec
+    B, Hq, Hk, d = s.batch, s.num_qo_heads, s.num_kv_heads, s.head_dim
+    ref = oracle.append_reference(ai)
+    Q = oracle.decode_codes(ai.q_new, s.q_dtype).reshape(B, Hq, d)
+    K = oracle.decode_codes(ai.k_new, s.q_dtype).reshape(B, Hk, d)
+    V = oracle.decode_codes(ai.v_new, s.q_dtype).reshape(B, Hk, d)
+    mq = _term_size(ai, Q, ai.q_norm_weight, ai.q_norm_weight is not None)
+    mk = _term_size(ai, K, ai.k_norm_weight, ai.k_norm_weight is not None)
+    mv = np.abs(V)
+    if s.kv_dtype == "fp8":
+        mk = mk / np.asarray(c.k_scale, np.float64)[:, :, None]
+        mv = mv / np.asarray(c.v_scale, np.float64)[:, :, None]
+    check_codes(got["q_out"], ref["q_out"], s.q_dtype, "q_out", mag=mq)
+    raw = lambda a: a.view(np.uint32) if a.dtype == np.float32 else a
+    k_pool, v_pool = got["k_pool"], got["v_pool"]
+    mask = np.ones(k_pool.shape[:-2], dtype=bool)  # [rows] or [pages, page_size]
+    for b in range(s.batch):
+        row, slot = oracle.cache_slot(b, int(c.kv_len[b]), s.page_size, c.page_indptr, c.page_indices)
+        kk = k_pool[row] if slot is None else k_pool[row, slot]
+        vv = v_pool[row] if slot is None else v_pool[row, slot]
+        check_codes(kk, ref["k"][b], s.kv_dtype, f"k[{b}]", mag=mk[b])
+        check_codes(vv, ref["v"][b], s.kv_dtype, f"v[{b}]", mag=mv[b])
+        if slot is None:
+            mask[row] = False
+        else:
+            mask[row, slot] = False
+    assert np.array_equal(raw(k_pool)[mask], raw(np.asarray(c.k))[mask]), "K pool changed outside the new slots"
+    assert np.array_equal(raw(v_pool)[mask], raw(np.asarray(c.v))[mask]), "V pool changed outside the new slots"
+    return ref

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = _declared_functions()
-    assert set(names) >= {"kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes",
+    assert set(names) >= {"kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_append",
                           "kvs_status_string", "kvs_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kvsplit.h but not exported"
@@ -41,18 +41,22 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == 1
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 2
+    assert re.search(r"#define KVS_ABI_VERSION 2\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
 def test_struct_layout_matches_header(tmp_path):
     fields = [f[0] for f in kvs.KvsDecodeArgs._fields_]
     pfields = [f[0] for f in kvs.KvsPlanInfo._fields_]
+    afields = [f[0] for f in kvs.KvsAppendArgs._fields_]
     prog = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){"]
     prog.append('printf("%zu\\n", sizeof(kvs_decode_args));')
     prog += [f'printf("%zu\\n", offsetof(kvs_decode_args, {f}));' for f in fields]
     prog.append('printf("%zu\\n", sizeof(kvs_plan_info));')
     prog += [f'printf("%zu\\n", offsetof(kvs_plan_info, {f}));' for f in pfields]
+    prog.append('printf("%zu\\n", sizeof(kvs_append_args));')
+    prog += [f'printf("%zu\\n", offsetof(kvs_append_args, {f}));' for f in afields]
     prog.append("return 0;}")
     c = tmp_path / "layout.c"
     c.write_text("\n".join(prog))
@@ -61,6 +65,7 @@ def test_struct_layout_matches_header(tmp_path):
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(kvs.KvsDecodeArgs)] + [getattr(kvs.KvsDecodeArgs, f).offset for f in fields]
     want += [ctypes.sizeof(kvs.KvsPlanInfo)] + [getattr(kvs.KvsPlanInfo, f).offset for f in pfields]
+    want += [ctypes.sizeof(kvs.KvsAppendArgs)] + [getattr(kvs.KvsAppendArgs, f).offset for f in afields]
     assert vals == want
 
 
@@ -207,3 +212,52 @@ def test_algo_resolution(lib):
                     algo=kvs.KVS_ALGO_MFMA_PACKED)
     with pytest.raises(kvs.KvsError):
         kvs.kvs_decode_plan(a)
+
+
+# ------------------------------------------------------------------ kvs_append
+
+def _append_args(batch=2, Hq=8, Hk=2, d=128, q=kvs.KVS_BF16, kv=kvs.KVS_BF16, P=16, num_pages=100,
+                 eps=1e-6, theta=1e4, interleave=0):
+    a = kvs.KvsAppendArgs()
+    a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = batch, Hq, Hk, d
+    a.q_dtype, a.kv_dtype, a.page_size, a.num_pages = q, kv, P, num_pages
+    fake = 0x1000
+    a.q_in = a.k_in = a.v_in = a.q_out = a.k_cache = a.v_cache = a.kv_len = fake
+    a.page_indptr = a.page_indices = fake if P else None
+    a.k_scale = a.v_scale = fake if kv == kvs.KVS_FP8_E4M3 else None
+    a.norm_eps, a.rope_theta, a.rope_interleave = eps, theta, interleave
+    return a
+
+
+BAD_APPEND = [
+    (dict(batch=0), kvs.KVS_ERR_INVALID_ARG),
+    (dict(Hq=6, Hk=4), kvs.KVS_ERR_INVALID_ARG),
+    (dict(d=96), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(q=kvs.KVS_F32, kv=kvs.KVS_BF16), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(q=5), kvs.KVS_ERR_INVALID_ARG),
+    (dict(P=0), kvs.KVS_ERR_INVALID_ARG),          # contiguous with batch 2
+    (dict(P=24), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(P=-16), kvs.KVS_ERR_INVALID_ARG),
+    (dict(num_pages=0), kvs.KVS_ERR_INVALID_ARG),
+    (dict(eps=-1.0), kvs.KVS_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), kvs.KVS_ERR_INVALID_ARG),
+    (dict(theta=-1.0), kvs.KVS_ERR_INVALID_ARG),
+    (dict(theta=float("inf")), kvs.KVS_ERR_INVALID_ARG),
+    (dict(interleave=2), kvs.KVS_ERR_INVALID_ARG),
+    (dict(batch=1 << 22, Hq=32, Hk=8), kvs.KVS_ERR_UNSUPPORTED),  # 2^22 * 40 rows exceed one launch
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_APPEND, ids=[str(b[0]) for b in BAD_APPEND])
+def test_append_validation_before_any_hip_call(lib, kw, status):
+    assert kvs.kvs_append(_append_args(**kw), 0) == status
+
+
+def test_append_null_pointers_rejected(lib):
+    for field in ("q_in", "k_in", "v_in", "q_out", "k_cache", "v_cache", "kv_len", "page_indptr", "page_indices"):
+        a = _append_args()
+        setattr(a, field, None)
+        assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_INVALID_ARG, field
+    a = _append_args(kv=kvs.KVS_FP8_E4M3)
+    a.v_scale = None
+    assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_INVALID_ARG
