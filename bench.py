@@ -233,7 +233,7 @@ def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
 
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
-        with_cpu: bool = True, events: bool = True, cold: bool = False) -> dict:
+        with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None) -> dict:
     import torch
 
     import decode_attention_kv_split_amd as kvs
@@ -252,7 +252,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                             page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                             k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
-                            window=s.window, kv_chunk=kv_chunk, algo=algo)
+                            window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max)
     plan = kvs.kvs_decode_plan(a)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -313,6 +313,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
             "max_splits": plan.max_splits, "parallelism": "single GPU",
+            "unified_max": unified_max,
         },
         "roofline": {
             "bound": "hbm",
@@ -476,6 +477,8 @@ def main():
                          "embedding + KV append of the new token; step: append then decode")
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "mfma_packed", "valu"])
     ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--unified-max", type=float, default=None,
+                    help="start every chunk's softmax from this reference max (scaled-score units)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-events", action="store_true",
                     help="no per-launch kernel timing (the event stamps add host time per call, which "
@@ -499,7 +502,7 @@ def main():
         print(json.dumps(res), flush=True)
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
-              events=not args.no_events, cold=args.cold)
+              events=not args.no_events, cold=args.cold, unified_max=args.unified_max)
     print(json.dumps(res), flush=True)
 
 

@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 2
+KVS_ABI_VERSION = 3
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
@@ -78,6 +78,8 @@ class KvsDecodeArgs(ctypes.Structure):
         ("o", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
         ("prof_events", ctypes.c_void_p * 2),
+        ("use_unified_max", ctypes.c_int32),
+        ("unified_max", ctypes.c_float),
     ]
 
 
@@ -259,7 +261,8 @@ def _workspace(nbytes: int, device, stream: int):
 
 def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None,
               k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
-              algo="auto", out=None, lse=None, num_cus: int = 0) -> Tuple[KvsDecodeArgs, object]:
+              algo="auto", out=None, lse=None, num_cus: int = 0,
+              unified_max: Optional[float] = None) -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
@@ -317,20 +320,22 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     a.algo = _ALGOS[algo] if isinstance(algo, str) else int(algo)
     a.num_cus = int(num_cus)
     a.o, a.lse = _ptr(out), _ptr(lse)
+    if unified_max is not None:
+        a.use_unified_max, a.unified_max = 1, float(unified_max)
     keep = (kvh, out, lse)
     return a, keep
 
 
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
-           workspace=None, stream=None):
+           workspace=None, stream=None, unified_max: Optional[float] = None):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
 
     a, keep = make_args(q, k, v, kv_len, page_indptr=page_indptr, page_indices=page_indices,
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
-                        window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse)
+                        window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

@@ -54,6 +54,8 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (a->kv_chunk < 0) return KVS_ERR_INVALID_ARG;
   if (a->num_cus < 0) return KVS_ERR_INVALID_ARG;
   if (!a->kv_len_host) return KVS_ERR_INVALID_ARG;
+  if (a->use_unified_max != 0 && a->use_unified_max != 1) return KVS_ERR_INVALID_ARG;
+  if (a->use_unified_max && !std::isfinite(a->unified_max)) return KVS_ERR_INVALID_ARG;
   for (int b = 0; b < a->batch; ++b) {
     const int L = a->kv_len_host[b];
     if (L < 0) return KVS_ERR_INVALID_ARG;
@@ -215,6 +217,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.items = pl.items;
   p.out_bf16 = a->q_dtype == KVS_BF16 ? 1 : 0;
   p.score_scale = a->sm_scale * kvs::kLog2e;
+  p.m_init = a->use_unified_max ? a->unified_max * kvs::kLog2e : -INFINITY;
 
   // host-planned work lists, passed inline when they fit
   kvs::InlineWork w;

@@ -72,6 +72,9 @@ constexpr int kKvLoadPolicy = 2;
 // Largest rise of a head's running max (log2 units) absorbed without a
 // rescale of its state; weights then stay below 2^8.
 constexpr float kLazy = 8.0f;
+// A starting reference this far (log2 units) above an empty state's first
+// tile max is moved down to it.
+constexpr float kDrop = 64.0f;
 
 // XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
 // operand reads at the same logical piece land in distinct LDS banks.
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   };
 
   // ---- running state ----
-  float m_run = -INFINITY; // log2 domain, per query head c16 (same in the 4 quarters)
+  float m_run = p.m_init;  // reference max, log2 domain, per query head c16 (same in the 4 quarters)
   float l_run = 0.0f;      // partial sum over this lane's tokens
   f32x4_t oacc[S::kOTiles];
 #pragma unroll
@@ -407,9 +410,13 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     // so weights stay below 2^kLazy and after the first tiles the rescale is
     // almost never needed.  m + log2(l) and acc / l do not depend on which
     // reference is used.
-    const bool grow = mx > m_run + kLazy; // m_run = -inf: any visible key
+    // m_run = -inf: any visible key grows it.  A given starting reference
+    // (unified max) far above a still-empty state's first scores is moved
+    // down to them, so no weight underflows.
+    const bool empty = l_run == 0.0f;
+    const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f; // m_run = -inf -> 0
+      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = grow ? mx : m_run;
       l_run *= alpha;
 #pragma unroll
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (c16 < gp) {
     if (q4 == 0) {
-      sm_m[wave][c16] = m_run;
+      sm_m[wave][c16] = l_tot > 0.0f ? m_run : -INFINITY; // an empty state keeps no reference
       sm_l[wave][c16] = l_tot;
     }
     float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;

@@ -75,6 +75,7 @@ struct Params {
   int window;
   int chunk;
   int items;      // work items per KV head
+  float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
   float score_scale; // sm_scale * log2(e)
 };
@@ -195,8 +196,10 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, const flo
         L += a * sm_l[w][h];
         acc += a * sm_o[(w * 16 + h) * OSTRIDE + d];
       }
-      val = acc / L * vscale;
-      lse2 = M + __log2f(L);
+      if (L > 0.0f) { // a finite reference with no visible key leaves L = 0: empty
+        val = acc / L * vscale;
+        lse2 = M + __log2f(L);
+      }
     }
     const int hq = kvg * gp + h;
     if (nb == 1) {

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 2
+#define KVS_ABI_VERSION 3
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -121,6 +121,18 @@ typedef struct {
    * partial-softmax kernel's own dispatch stamps with its start and end time,
    * so hipEventElapsedTime gives that kernel's duration; NULL to skip */
   void *prof_events[2];
+
+  /* optional unified max (the FlashDecoding++ explainer, section
+   * "asynchronous softmax and unified max value"): with use_unified_max = 1
+   * every chunk starts its softmax from the reference max unified_max (a
+   * bound on the scaled scores sm_scale * q.k, natural units, finite) instead
+   * of from the first tile's max.  A score more than 8 / log2(e) above the
+   * reference still moves it (with the usual rescale), and a chunk whose
+   * first visible scores lie far below it starts from them, so the result
+   * does not depend on the value beyond rounding.  Honoured by the
+   * matrix-core kernels; the vector kernel ignores it.  0: off. */
+  int32_t use_unified_max;
+  float unified_max;
 } kvs_decode_args;
 
 /* What a call will launch, computed on the host from kv_len_host. */

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 2
-    assert re.search(r"#define KVS_ABI_VERSION 2\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 3
+    assert re.search(r"#define KVS_ABI_VERSION 3\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -121,6 +121,19 @@ def test_validation_before_any_hip_call(lib, kw, status):
     with pytest.raises(kvs.KvsError):
         kvs.kvs_decode_plan(a)
     assert kvs.kvs_decode_workspace_bytes(a) == 0
+
+
+def test_unified_max_checks(lib):
+    a, keep = _args()
+    a.use_unified_max, a.unified_max = 1, float("nan")
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG
+    a.unified_max = float("inf")
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG
+    a.use_unified_max = 2
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG
+    a, keep = _args(ptrs=False)
+    a.use_unified_max, a.unified_max = 1, 5.0
+    assert kvs.kvs_decode_plan(a).items_per_kv_head >= 1
 
 
 def test_null_pointers_rejected(lib):

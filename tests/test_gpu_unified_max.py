@@ -1,0 +1,50 @@
+"""The unified-max option (a caller-given starting reference max for every
+chunk) against the fp64 oracle on the GPU: the result must not depend on
+the value given, whether it bounds the scores, lies far below them (every
+chunk then rescales as usual) or far above them (a still-empty chunk then
+starts from its first scores)."""
+import dataclasses
+
+import pytest
+
+import oracle
+from kvs_testlib import compare, run_library
+from workloads import make_inputs, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kvs.load_library()
+
+
+@pytest.mark.parametrize("phi", [3.0, -20.0, 30.0, 200.0])
+@pytest.mark.parametrize("name,lens", [
+    ("c4_paged_bf16_b64", [0, 1, 17, 300, 2049]),
+    ("c5_paged_fp8_b128", [5, 128, 1777]),
+    ("c3_llama2_7b_32k", [1000]),
+    ("c2_gemma3_1b", [3000]),
+])
+def test_unified_max_matches_oracle(phi, name, lens):
+    print(f"case unified max {name} phi={phi}", flush=True)
+    spec = small_variant(name, batch=len(lens), lengths=("list", lens))
+    inp = make_inputs(spec, poison=spec.page_size > 0)
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    for chunk in (0, 16):
+        o, lse = run_library(inp, unified_max=phi, kv_chunk=chunk)
+        compare(o, lse, o_ref, lse_ref, spec.kv_dtype)
+
+
+@pytest.mark.parametrize("phi", [0.0, 100.0])
+def test_unified_max_with_window_and_empty_chunks(phi):
+    print(f"case unified max window phi={phi}", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=3, lengths=("list", [50, 700, 0]), window=100)
+    inp = make_inputs(spec, poison=True)
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    o, lse = run_library(inp, unified_max=phi, kv_chunk=64)
+    compare(o, lse, o_ref, lse_ref, "bf16")
