@@ -14,13 +14,13 @@ the codecs) and invariants of the definition; see ``tests/test_oracle.py``,
 from .append import (append_codes, append_reference, apply_append, cache_slot, rms_norm, rope,
                      rope_angles, transform_head)
 from .codecs import (bf16_to_f64, decode_codes, encode_codes, f64_to_bf16_codes, f64_to_fp8_e4m3fn_codes,
-                     fp8_e4m3fn_to_f64, round_to_grid)
+                     fp8_e4m3fn_to_f64, int4_to_f64, round_to_grid)
 from .decode import (attend_chunked, attend_direct, chunk_state, decode_reference,
                      decode_reference_chunked, decode_reference_sampled, kv_head_of,
                      merge_states, request_kv, softmax_from_scores, visible_range)
 
 __all__ = [
-    "bf16_to_f64", "fp8_e4m3fn_to_f64", "decode_codes", "encode_codes", "f64_to_bf16_codes",
+    "bf16_to_f64", "fp8_e4m3fn_to_f64", "int4_to_f64", "decode_codes", "encode_codes", "f64_to_bf16_codes",
     "f64_to_fp8_e4m3fn_codes", "round_to_grid",
     "rms_norm", "rope", "rope_angles", "transform_head", "append_reference", "append_codes",
     "apply_append", "cache_slot",

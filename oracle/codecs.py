@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_to_f64", "fp8_e4m3fn_to_f64", "decode_codes",
+__all__ = ["bf16_to_f64", "fp8_e4m3fn_to_f64", "int4_to_f64", "decode_codes",
            "round_to_grid", "f64_to_bf16_codes", "f64_to_fp8_e4m3fn_codes", "encode_codes"]
 
 
@@ -43,14 +43,32 @@ def fp8_e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
+def int4_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Packed signed 4-bit integers: byte i of a row holds elements 2i (low
+    nibble) and 2i + 1 (high nibble), each a two's-complement value in
+    [-8, 7].  A [..., n] byte array decodes to [..., 2n] float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    lo = c & 0xF
+    hi = (c >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.float64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
 def decode_codes(codes: np.ndarray, dtype: str) -> np.ndarray:
-    """Raw storage codes ('f32', 'bf16', 'fp8') to float64."""
+    """Raw storage codes ('f32', 'bf16', 'fp8', 'int4') to float64 (int4:
+    the last axis doubles)."""
     if dtype == "f32":
         return np.asarray(codes, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         return bf16_to_f64(codes)
     if dtype == "fp8":
         return fp8_e4m3fn_to_f64(codes)
+    if dtype == "int4":
+        return int4_to_f64(codes)
     raise ValueError(f"unknown storage type {dtype!r}")
 
 

@@ -25,7 +25,9 @@ Sources (cited by page and section):
   (upppp.jp), section on the three kernels (single_decode);
 * paged KV cache -- "Beyond the Memory Wall", FlashInfer bullet list
   (PagedAttention);
-* fp8 KV cache -- same list (compressed KV cache);
+* fp8 and INT4 KV caches -- same list (compressed KV cache; the page names
+  FP8/INT4 without a layout: INT4 is read here as packed two's-complement
+  nibbles with a per-(request, KV head) scale, like fp8);
 * sliding (local) window -- the FlashInfer-from-JAX page, Gemma 3 section
   (local vs global attention layers); "Flashlight" explainer (gist.science),
   results (sliding-window variant).
@@ -193,7 +195,7 @@ def request_kv(b: int, *, k, v, kv_len, kv_dtype: str, page_size: int,
     Contiguous cache: k is [L, Hk, d].  Paged cache: k is
     [num_pages, page_size, Hk, d]; logical token t of request b sits in page
     page_indices[page_indptr[b] + t // page_size], slot t % page_size.
-    fp8 codes are multiplied by the per-(request, kv head) scale.
+    fp8 and int4 codes are multiplied by the per-(request, kv head) scale.
     """
     L = int(kv_len[b])
     t0, t1 = (0, L) if tokens is None else tokens
@@ -206,7 +208,7 @@ def request_kv(b: int, *, k, v, kv_len, kv_dtype: str, page_size: int,
         kr, vr = k[pages, slots], v[pages, slots]
     K = decode_codes(kr, kv_dtype)
     V = decode_codes(vr, kv_dtype)
-    if kv_dtype == "fp8":
+    if kv_dtype in ("fp8", "int4"):
         K = K * np.asarray(k_scale, np.float64)[b][None, :, None]
         V = V * np.asarray(v_scale, np.float64)[b][None, :, None]
     return K, V

@@ -49,12 +49,16 @@ __all__ = [
     "F32",
     "BF16",
     "FP8",
+    "INT4",
 ]
 
-F32, BF16, FP8 = "f32", "bf16", "fp8"
-_STORE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
-_POISON = {F32: np.float32(np.nan).view(np.uint32), BF16: 0x7FC0, FP8: 0x7F}
+F32, BF16, FP8, INT4 = "f32", "bf16", "fp8", "int4"
+_STORE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8, INT4: np.uint8}
+# int4 has no NaN: its padding is the largest code (7, 7), which dominates
+# any score it would wrongly enter
+_POISON = {F32: np.float32(np.nan).view(np.uint32), BF16: 0x7FC0, FP8: 0x7F, INT4: 0x77}
 FP8_MAX = 448.0
+INT4_MAX = 7.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -135,6 +139,13 @@ def _to_fp8_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def _to_int4_codes(x: np.ndarray) -> np.ndarray:
+    """[..., d] float32 already divided by its scale -> [..., d/2] packed
+    signed nibbles (nearest even, clamped to [-8, 7]; element 2i low)."""
+    q = np.clip(np.rint(x.astype(np.float64)), -8, 7).astype(np.int64) & 0xF
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+
+
 def _rms_normalize(x: np.ndarray) -> np.ndarray:
     """Per-head RMS normalisation over the last axis, eps 1e-6, unit weight."""
     ms = np.mean(np.square(x, dtype=np.float32), axis=-1, keepdims=True, dtype=np.float32)
@@ -183,7 +194,24 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
     q_codes = _store(q, spec.q_dtype)
     offs = np.concatenate([[0], np.cumsum(kv_len, dtype=np.int64)])
     k_scale = v_scale = None
-    if spec.kv_dtype == FP8:
+    if spec.kv_dtype == INT4:
+        if d % 2:
+            raise ValueError("int4 rows hold an even number of elements")
+        k_scale = np.ones((B, Hk), np.float32)
+        v_scale = np.ones((B, Hk), np.float32)
+        k_codes = np.empty(k_log.shape[:-1] + (d // 2,), np.uint8)
+        v_codes = np.empty(v_log.shape[:-1] + (d // 2,), np.uint8)
+        for b in range(B):
+            sl = slice(offs[b], offs[b + 1])
+            for src, codes, scale in ((k_log, k_codes, k_scale), (v_log, v_codes, v_scale)):
+                blk = src[sl]
+                if blk.shape[0] == 0:
+                    continue
+                amax = np.max(np.abs(blk), axis=(0, 2))
+                s = np.where(amax > 0, amax / np.float32(INT4_MAX), np.float32(1.0)).astype(np.float32)
+                scale[b] = s
+                codes[sl] = _to_int4_codes(blk / s[None, :, None])
+    elif spec.kv_dtype == FP8:
         k_scale = np.ones((B, Hk), np.float32)
         v_scale = np.ones((B, Hk), np.float32)
         k_codes = np.empty(k_log.shape, np.uint8)
@@ -219,7 +247,7 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
     N = int(indptr[-1])
     perm = r_perm.permutation(N).astype(np.int32) if permute_pages else np.arange(N, dtype=np.int32)
     store = _STORE[spec.kv_dtype]
-    pool_shape = (N, P, Hk, d)
+    pool_shape = (N, P, Hk, d // 2 if spec.kv_dtype == INT4 else d)
     if poison:
         fill = _POISON[spec.kv_dtype]
         if spec.kv_dtype == F32:
@@ -241,8 +269,8 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
         src_k = k_codes[offs[b]:offs[b + 1]]
         src_v = v_codes[offs[b]:offs[b + 1]]
         if full:
-            k_pool[pages[:full]] = src_k[:full * P].reshape(full, P, Hk, d)
-            v_pool[pages[:full]] = src_v[:full * P].reshape(full, P, Hk, d)
+            k_pool[pages[:full]] = src_k[:full * P].reshape((full, P) + src_k.shape[1:])
+            v_pool[pages[:full]] = src_v[:full * P].reshape((full, P) + src_v.shape[1:])
         if rem:
             k_pool[pages[full], :rem] = src_k[full * P:]
             v_pool[pages[full], :rem] = src_v[full * P:]
@@ -267,6 +295,11 @@ CONFIGS = {
     "c5_paged_fp8_b128": DecodeSpec("c5_paged_fp8_b128", 128, 64, 8, 128, 16, FP8, BF16,
                                     1.0 / math.sqrt(128.0),
                                     lengths=("lognormal", math.log(4096.0), 0.8, 128, 65536), seed=1004),
+    # INT4 KV (two's-complement nibbles, scale amax/7): the batch-128 shape
+    # of the fp8 workload with half its KV bytes
+    "c6_paged_int4_b128": DecodeSpec("c6_paged_int4_b128", 128, 64, 8, 128, 16, INT4, BF16,
+                                     1.0 / math.sqrt(128.0),
+                                     lengths=("lognormal", math.log(4096.0), 0.8, 128, 65536), seed=1005),
 }
 
 
