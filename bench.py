@@ -28,9 +28,10 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "decode-attention \u00b5s/step and achieved HBM GB/s (% of peak), paged GQA batch"
 CONFIG_ALIASES = {"c1": "c1_mha_f32", "c2": "c2_gemma3_1b", "c2w": "c2_gemma3_1b_w512",
-                  "c3": "c3_llama2_7b_32k", "c4": "c4_paged_bf16_b64", "c5": "c5_paged_fp8_b128"}
+                  "c3": "c3_llama2_7b_32k", "c4": "c4_paged_bf16_b64", "c5": "c5_paged_fp8_b128",
+                  "c6": "c6_paged_int4_b128"}
 DEFAULT = "c4_paged_bf16_b64"
-_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 
 # HBM bytes per launch of the partial kernel, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over the default command of
@@ -81,14 +82,14 @@ def algorithmic_bytes(inp) -> int:
     L = inp.kv_len.astype(np.int64)
     lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
     vis = int(np.sum(L - lo))
-    kv = 2 * vis * s.num_kv_heads * s.head_dim * b_kv
+    kv = int(2 * vis * s.num_kv_heads * s.head_dim * b_kv)
     qo = 2 * s.batch * s.num_qo_heads * s.head_dim * b_q + 4 * s.batch * s.num_qo_heads
     meta = 4 * s.batch
     if s.page_size:
         first = lo // s.page_size
         last = (L + s.page_size - 1) // s.page_size
         meta += 4 * (s.batch + 1) + 4 * int(np.sum(np.maximum(0, last - first)))
-    if s.kv_dtype == "fp8":
+    if s.kv_dtype in ("fp8", "int4"):
         meta += 2 * 4 * s.batch * s.num_kv_heads
     return kv + qo + meta
 
@@ -252,7 +253,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                             page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                             k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
-                            window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max)
+                            window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max,
+                            kv_dtype="int4" if s.kv_dtype == "int4" else None)
     plan = kvs.kvs_decode_plan(a)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream

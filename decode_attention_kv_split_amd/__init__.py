@@ -27,7 +27,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
-    "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
+    "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_INT4", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
     "KVS_ALGO_MFMA_PACKED",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
     "library_path", "load_library",
@@ -37,10 +37,10 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 3
+KVS_ABI_VERSION = 4
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
-KVS_F32, KVS_BF16, KVS_FP8_E4M3 = 0, 1, 2
+KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
 KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
 _ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
 
@@ -215,9 +215,16 @@ def kvs_probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream: int) -> int:
 # torch marshalling
 # ----------------------------------------------------------------------------
 
-def _dtype_code(t, what: str) -> int:
+_KV_NAMES = {"f32": KVS_F32, "bf16": KVS_BF16, "fp8": KVS_FP8_E4M3, "int4": KVS_INT4}
+
+
+def _dtype_code(t, what: str, name: Optional[str] = None) -> int:
+    """kvs_dtype of a tensor; ``name`` ('f32', 'bf16', 'fp8', 'int4') settles
+    byte tensors, which hold fp8 codes unless told they are packed INT4."""
     import torch
 
+    if name is not None:
+        return _KV_NAMES[name]
     if t.dtype == torch.float32:
         return KVS_F32
     if t.dtype == torch.bfloat16:
@@ -262,12 +269,13 @@ def _workspace(nbytes: int, device, stream: int):
 def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None,
               k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
               algo="auto", out=None, lse=None, num_cus: int = 0,
-              unified_max: Optional[float] = None) -> Tuple[KvsDecodeArgs, object]:
+              unified_max: Optional[float] = None, kv_dtype: Optional[str] = None) -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
     [num_pages, page_size, Hk, d]; kv_len: int32 [batch] on the device.
-    Returns (args, keepalive)."""
+    kv_dtype='int4' marks uint8 caches whose last axis holds d / 2 bytes of
+    packed nibbles.  Returns (args, keepalive)."""
     import numpy as np
     import torch
 
@@ -287,7 +295,10 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
         P, num_pages = 0, 0
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must have the same shape and dtype")
-    if dk != d:
+    if kv_dtype == "int4":
+        if k.dtype != torch.uint8 or 2 * dk != d:
+            raise ValueError("int4 k/v must be uint8 with head_dim / 2 bytes per row")
+    elif dk != d:
         raise ValueError("head_dim of q and k differ")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len"), (page_indptr, "page_indptr"),
                  (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale")):
@@ -307,7 +318,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     a = KvsDecodeArgs()
     a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = B, Hq, Hk, d
     a.q_dtype = _dtype_code(q, "q")
-    a.kv_dtype = _dtype_code(k, "kv")
+    a.kv_dtype = _dtype_code(k, "kv", kv_dtype)
     a.page_size, a.num_pages = P, num_pages
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.page_indptr, a.page_indices = _ptr(page_indptr), _ptr(page_indices)
@@ -328,14 +339,15 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
 
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
-           workspace=None, stream=None, unified_max: Optional[float] = None):
+           workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
 
     a, keep = make_args(q, k, v, kv_len, page_indptr=page_indptr, page_indices=page_indices,
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
-                        window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max)
+                        window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
+                        kv_dtype=kv_dtype)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

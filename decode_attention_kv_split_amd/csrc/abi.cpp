@@ -11,11 +11,12 @@
 #include "plan.h"
 
 namespace kvs {
-hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, const Launch &l);
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l);
 hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, const Launch &l);
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
-int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack);
+int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack);
+bool mfma_head_dim_ok(int head_dim, int kv_type);
 hipError_t launch_append(const kvs_append_args *a, const Launch &l);
 } // namespace kvs
 
@@ -42,9 +43,11 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if ((int64_t)a->num_kv_heads * a->head_dim * 4 * 16 >= ((int64_t)1 << 31)) return KVS_ERR_UNSUPPORTED;
   const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
-                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
-  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 2) return KVS_ERR_INVALID_ARG;
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_INT4);
+  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 3) return KVS_ERR_INVALID_ARG;
   if (!pair_ok) return KVS_ERR_UNSUPPORTED;
+  const bool scaled = a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4;
   if (a->page_size < 0) return KVS_ERR_INVALID_ARG;
   if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
@@ -64,12 +67,13 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (need_ptrs) {
     if (!a->q || !a->k || !a->v || !a->kv_len || !a->o) return KVS_ERR_INVALID_ARG;
     if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
-    if (a->kv_dtype == KVS_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
+    if (scaled && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
   }
-  // kernel family
+  // kernel family (INT4 runs on the matrix-core kernel only)
   const bool mfma_ok = a->kv_dtype != KVS_F32 && a->q_dtype == KVS_BF16 &&
-                       (a->page_size == 0 || a->page_size >= 16);
-  const bool valu_ok = group <= kvs::valu_max_group(a->kv_dtype);
+                       (a->page_size == 0 || a->page_size >= 16) &&
+                       kvs::mfma_head_dim_ok(a->head_dim, a->kv_dtype);
+  const bool valu_ok = a->kv_dtype != KVS_INT4 && group <= kvs::valu_max_group(a->kv_dtype);
   switch (a->algo) {
   case KVS_ALGO_AUTO:
     if (mfma_ok)
@@ -100,11 +104,11 @@ kvs_status validate_append(const kvs_append_args *a) {
   if (a->batch < 1 || a->num_qo_heads < 1 || a->num_kv_heads < 1) return KVS_ERR_INVALID_ARG;
   if (a->num_qo_heads % a->num_kv_heads) return KVS_ERR_INVALID_ARG;
   if (a->head_dim != 64 && a->head_dim != 128 && a->head_dim != 256) return KVS_ERR_UNSUPPORTED;
-  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 2) return KVS_ERR_INVALID_ARG;
+  if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 3) return KVS_ERR_INVALID_ARG;
   const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
-  if (!pair_ok) return KVS_ERR_UNSUPPORTED;
+  if (!pair_ok) return KVS_ERR_UNSUPPORTED; // INT4 caches are not written by this step
   if (a->page_size < 0 || a->num_pages < 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
@@ -191,8 +195,9 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.page_indptr = a->page_indptr;
   p.page_indices = a->page_indices;
   p.kv_len = a->kv_len;
-  p.k_scale = a->kv_dtype == KVS_FP8_E4M3 ? a->k_scale : nullptr;
-  p.v_scale = a->kv_dtype == KVS_FP8_E4M3 ? a->v_scale : nullptr;
+  const bool scaled = a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4;
+  p.k_scale = scaled ? a->k_scale : nullptr;
+  p.v_scale = scaled ? a->v_scale : nullptr;
   p.o = a->o;
   p.lse = a->lse;
   p.o_part = pl.workspace_bytes ? reinterpret_cast<float *>(workspace) : nullptr;
@@ -206,9 +211,8 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;
   p.group = a->num_qo_heads / a->num_kv_heads;
-  const bool fp8 = a->kv_dtype == KVS_FP8_E4M3;
   p.pack = algo == KVS_ALGO_VALU ? 1
-                                 : kvs::mfma_pack(a->head_dim, p.group, a->num_kv_heads, fp8,
+                                 : kvs::mfma_pack(a->head_dim, p.group, a->num_kv_heads, a->kv_dtype,
                                                   algo == KVS_ALGO_MFMA_PACKED);
   p.page_size = a->page_size;
   p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;
@@ -238,7 +242,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
                        reinterpret_cast<hipEvent_t>(a->prof_events[1])};
   hipError_t e;
   if (algo != KVS_ALGO_VALU)
-    e = kvs::launch_partial_mfma(p, w, a->head_dim, fp8, lp);
+    e = kvs::launch_partial_mfma(p, w, a->head_dim, a->kv_dtype, lp);
   else
     e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, lp);
   if (e != hipSuccess) return KVS_ERR_HIP;

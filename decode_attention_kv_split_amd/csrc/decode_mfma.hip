@@ -40,14 +40,15 @@
 namespace kvs {
 namespace {
 
-template <int DE, bool FP8>
+template <int DE, int KT>
 struct Shape {
-  static constexpr int kBytes = FP8 ? 1 : 2;
-  static constexpr int kRowBytes = DE * kBytes;            // one token's K (or V) row of the pack
+  static_assert(KT == DT_BF16 || KT == DT_FP8 || KT == DT_INT4, "KV type");
+  static constexpr int kEpp = KT == DT_BF16 ? 8 : (KT == DT_FP8 ? 16 : 32); // elements per 16-byte piece
+  static constexpr int kRowBytes = DE * 16 / kEpp;        // one token's K (or V) row of the pack
   static constexpr int kLaneVec = kRowBytes / 64;          // 16-byte pieces per lane per row
   static constexpr int kKSteps = DE / 32;                  // 16x16x32 products for S^T
   static constexpr int kOTiles = DE / 16;                  // 16-dim slices of O^T
-  static constexpr int kEpp = 16 / kBytes;                 // elements per 16-byte piece
+  static constexpr int kOutStride = KT == DT_INT4 ? 2 : 1; // distance between a lane's four O^T dims
   static_assert(kLaneVec >= 1, "row slice must hold at least 16 bytes");
   // LDS staging of a 16-token tile
   static constexpr int kPieces = kRowBytes / 16;           // 16-byte pieces per row
@@ -78,9 +79,9 @@ constexpr float kDrop = 64.0f;
 
 // XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
 // operand reads at the same logical piece land in distinct LDS banks.
-template <int DE, bool FP8>
+template <int DE, int KT>
 __device__ __forceinline__ int stage_swizzle(int r) {
-  using S = Shape<DE, FP8>;
+  using S = Shape<DE, KT>;
   return (r / S::kRowsPerBankPeriod) & (S::kPieces - 1);
 }
 
@@ -145,10 +146,10 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
                                            kKvLoadPolicy);
 }
 
-template <int DE, bool FP8>
+template <int DE, int KT>
 struct TileRegs {
-  uint4 k[Shape<DE, FP8>::kLaneVec];
-  uint4 v[Shape<DE, FP8>::kLaneVec];
+  uint4 k[Shape<DE, KT>::kLaneVec];
+  uint4 v[Shape<DE, KT>::kLaneVec];
 };
 
 __device__ __forceinline__ float xor16_max(float x) {
@@ -169,37 +170,70 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// First of the 8 pack dims that lane (q4) feeds to the S^T product in k-step j
-// (16x16x32: 8 reduction indices per lane).
-template <int DE, bool FP8>
-__device__ __forceinline__ int k_dim(int j, int q4) {
-  if constexpr (FP8)
-    return 16 * (4 * (j >> 1) + q4) + 8 * (j & 1);
-  else
-    return 8 * (4 * j + q4);
+// INT4: a dword holds 8 two's-complement nibbles n (element 2i in the low
+// nibble of byte i).  n ^ 8 = n + 8 lies in [0, 15], and the bf16 pattern
+// 0x43 : (n + 8) is exactly 128 + (n + 8) = n + 136, so one byte permute
+// builds two bf16 operands.  The products then carry an offset of 136 per
+// element, removed exactly afterwards (scores: 136 * sum of q over the head's
+// dims; outputs: 136 * the softmax sum).  kInt4Offset is that 136.
+constexpr float kInt4Offset = 136.0f;
+__device__ __forceinline__ uint32_t int4_even(uint32_t w) { return (w ^ 0x88888888u) & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t int4_odd(uint32_t w) { return ((w ^ 0x88888888u) >> 4) & 0x0F0F0F0Fu; }
+// bytes b0..b3 of x (each in [0, 15]) -> bf16 (128 + b0, 128 + b1), (128 + b2, 128 + b3)
+__device__ __forceinline__ uint32_t offset_bf16_lo(uint32_t x) { return __builtin_amdgcn_perm(0x43434343u, x, 0x04010400u); }
+__device__ __forceinline__ uint32_t offset_bf16_hi(uint32_t x) { return __builtin_amdgcn_perm(0x43434343u, x, 0x04030402u); }
+
+// Pack dim of element e (0..7) that lane (q4) feeds to the S^T product in
+// k-step j (16x16x32: 8 reduction indices per lane).  INT4 feeds the even
+// elements of a dword first, then the odd ones.
+template <int DE, int KT>
+__device__ __forceinline__ int k_elem_dim(int j, int q4, int e) {
+  if constexpr (KT == DT_FP8) {
+    return 16 * (4 * (j >> 1) + q4) + 8 * (j & 1) + e;
+  } else if constexpr (KT == DT_INT4) {
+    const int pc = j >> 2, dw = j & 3; // piece 4 pc + q4, dword dw of it
+    return 32 * (4 * pc + q4) + 8 * dw + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+  } else {
+    return 8 * (4 * j + q4) + e;
+  }
 }
 
-// First of the four consecutive pack dims lane (q4) holds in O^T slice w.
-template <int DE, bool FP8>
+// First of the four pack dims lane (q4) holds in O^T slice w; the four are
+// kOutStride apart.
+template <int DE, int KT>
 __device__ __forceinline__ int out_dim(int w, int q4) {
-  constexpr int per_piece = Shape<DE, FP8>::kEpp / 4; // slices per 16-byte piece
-  return (4 * (w / per_piece) + q4) * Shape<DE, FP8>::kEpp + 4 * (w % per_piece);
+  if constexpr (KT == DT_INT4) {
+    const int pc = w >> 3, dw = (w & 7) >> 1; // slice w: the even (w even) or odd nibbles of dword dw
+    return 32 * (4 * pc + q4) + 8 * dw + (w & 1);
+  } else {
+    constexpr int per_piece = Shape<DE, KT>::kEpp / 4; // slices per 16-byte piece
+    return (4 * (w / per_piece) + q4) * Shape<DE, KT>::kEpp + 4 * (w % per_piece);
+  }
 }
 
-template <int DE, bool FP8>
-__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, FP8> &t, int j) {
-  if constexpr (FP8) {
+__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <int DE, int KT>
+__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, KT> &t, int j) {
+  if constexpr (KT == DT_FP8) {
     const uint4 w = t.k[j >> 1];
     return (j & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+  } else if constexpr (KT == DT_INT4) {
+    const uint32_t w = dword_of(t.k[j >> 2], j & 3);
+    const uint32_t ev = int4_even(w), od = int4_odd(w);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(offset_bf16_lo(ev), offset_bf16_hi(ev), offset_bf16_lo(od),
+                                                   offset_bf16_hi(od)));
   } else {
     return __builtin_bit_cast(bf16x8_t, t.k[j]);
   }
 }
 
-template <int D, int PACK, bool FP8, int NBUF>
+template <int D, int PACK, int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, const InlineWork w) {
   constexpr int DE = D * PACK;
-  using S = Shape<DE, FP8>;
+  using S = Shape<DE, KT>;
   constexpr int OSTRIDE = D + 4;
   constexpr int kStageBytes = kWaves * NBUF * 2 * S::kTileBytes;
   constexpr int kEpiBytes = 2 * kWaves * 16 * 4 + kWaves * 16 * OSTRIDE * 4;
@@ -272,15 +306,29 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
                          ((size_t)b * p.num_qo_heads + (size_t)kvg * gp + c16) * D;
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j) {
-      const int kd = k_dim<DE, FP8>(j, q4);
-      if (c16 < gp && kd / D == my_kv)
-        qop[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
-      else
+      const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
+      if (c16 < gp && kd / D == my_kv) {
+        bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
+        if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+        qop[j] = x;
+      } else {
         qop[j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      }
     }
   }
   float cscale = p.score_scale;
-  if (FP8) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
+  if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
+  // INT4: the scores carry 136 * (sum of this head's q over the pack dims)
+  float qoff = 0.0f;
+  if constexpr (KT == DT_INT4) {
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qoff += (float)qop[j][e];
+    qoff += __shfl_xor(qoff, 16, 64);
+    qoff += __shfl_xor(qoff, 32, 64);
+    qoff *= kInt4Offset;
+  }
 
   // identity / selection operands of the V transposition
   const short one_bf16 = 0x3F80;
@@ -288,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
   long sel[2] = {0, 0};
-  if (FP8) {
+  if (KT == DT_FP8) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       uint64_t s = 0;
@@ -298,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
 
   // ---- addressing ----
-  const size_t row_bytes = (size_t)Hk * D * S::kBytes; // bytes between consecutive tokens
+  const size_t row_bytes = (size_t)Hk * (S::kRowBytes / PACK); // bytes between consecutive tokens
   const bool paged = p.page_size > 0;
   const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
   const int pshift = p.page_shift;
@@ -332,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 #pragma unroll
   for (int k = 0; k < S::kDma; ++k) {
     const int r = k * S::kRowsPerDma + lane / S::kPieces;
-    const int piece = (lane % S::kPieces) ^ stage_swizzle<DE, FP8>(r);
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<DE, KT>(r);
     dma_voff[k] = r * (int)row_bytes + kvg * S::kRowBytes + piece * 16; // < 2^31: checked on the host
   }
   char *wave_stage = smem + wave * NBUF * 2 * S::kTileBytes;
@@ -356,11 +404,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   uint32_t stage_addr[S::kLaneVec]; // LDS address of piece pc of the K tile in slot 0
   {
     const uint32_t base = lds_address(wave_stage) + c16 * S::kRowBytes;
-    const int swz = stage_swizzle<DE, FP8>(c16);
+    const int swz = stage_swizzle<DE, KT>(c16);
 #pragma unroll
     for (int pc = 0; pc < S::kLaneVec; ++pc) stage_addr[pc] = base + ((4 * pc + q4) ^ swz) * 16;
   }
-  auto read_stage = [&](TileRegs<DE, FP8> &t, int slot) {
+  auto read_stage = [&](TileRegs<DE, KT> &t, int slot) {
     const uint32_t so = slot * 2 * S::kTileBytes;
     if constexpr (S::kLaneVec == 1) {
       lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], stage_addr[0] + so);
@@ -375,11 +423,12 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // ---- running state ----
   float m_run = p.m_init;  // reference max, log2 domain, per query head c16 (same in the 4 quarters)
   float l_run = 0.0f;      // partial sum over this lane's tokens
+  float lb_run = 0.0f;     // INT4: the same sum of the bf16-rounded weights the P.V product sees
   f32x4_t oacc[S::kOTiles];
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w) oacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](TileRegs<DE, FP8> t, int i) {
+  auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (wave + i * kWaves) * kTile;
     if (ts < t_begin) { // rows before the window / chunk start hold keys of no interest
       const bool ok = ts + c16 >= t_begin;
@@ -391,7 +440,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, FP8>(t, j), qop[j], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), qop[j], s, 0, 0, 0);
+    if constexpr (KT == DT_INT4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] -= qoff; // remove the 136-per-element offset of K
+    }
     float sv[4];
     if (ts >= t_begin && ts + kTile <= t_end) { // every key of the tile is visible (uniform branch)
 #pragma unroll
@@ -419,6 +472,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = grow ? mx : m_run;
       l_run *= alpha;
+      if constexpr (KT == DT_INT4) lb_run *= alpha;
 #pragma unroll
       for (int w = 0; w < S::kOTiles; ++w) {
 #pragma unroll
@@ -431,14 +485,24 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_run) : 0.0f;
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+    if constexpr (KT == DT_INT4)
+      lb_run += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+                (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
     // V^T slices (all products first, so the dependent conversions and
     // accumulations below do not wait on each other), then O^T += V^T . P^T
     f32x4_t vt[S::kOTiles];
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) {
-      if constexpr (FP8) {
+      if constexpr (KT == DT_INT4) {
+        // even (w even) or odd nibbles of dword (w / 2) % 4 of piece w / 8, as 136 + n
+        const uint32_t dw = dword_of(t.v[w >> 3], (w >> 1) & 3);
+        const uint32_t nib = (w & 1) ? int4_odd(dw) : int4_even(dw);
+        const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
+        vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+      } else if constexpr (KT == DT_FP8) {
         const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
         const uint4 wv = t.v[u >> 1];
         const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
@@ -472,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       for (int j = 0; j < NBUF; ++j) {
         const int i = it + j;
         wait_vmem<(NBUF - 1) * 2 * S::kDma>(); // tile i has landed; NBUF - 1 newer tiles may fly
-        TileRegs<DE, FP8> t;
+        TileRegs<DE, KT> t;
         read_stage(t, j); // returns with the reads complete
         issue(i + NBUF, j);
         if (i < my_tiles) compute(t, i);
@@ -485,17 +549,30 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // ---- per-wave state to LDS (each query head keeps the dims of its KV head) ----
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  float lb_tot = 0.0f;
+  if constexpr (KT == DT_INT4) {
+    lb_tot = lb_run + __shfl_xor(lb_run, 16, 64);
+    lb_tot += __shfl_xor(lb_tot, 32, 64);
+  }
   if (c16 < gp) {
     if (q4 == 0) {
       sm_m[wave][c16] = l_tot > 0.0f ? m_run : -INFINITY; // an empty state keeps no reference
       sm_l[wave][c16] = l_tot;
     }
     float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
+    // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
+    const float voff = kInt4Offset * lb_tot;
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) {
-      const int od = out_dim<DE, FP8>(w, q4);
-      if (od / D == my_kv)
-        *reinterpret_cast<float4 *>(dst + od % D) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+      const int od = out_dim<DE, KT>(w, q4);
+      if (od / D == my_kv) {
+        if constexpr (S::kOutStride == 1) {
+          *reinterpret_cast<float4 *>(dst + od % D) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[od % D + r * S::kOutStride] = oacc[w][r] - voff;
+        }
+      }
     }
   }
   __syncthreads();
@@ -504,10 +581,10 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 
 } // namespace
 
-template <int D, int PACK, bool FP8>
+template <int D, int PACK, int KT>
 static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
-  constexpr int NB = Shape<D * PACK, FP8>::kNBuf;
-  return launch_kernel(l, partial_mfma_kernel<D, PACK, FP8, NB>, dim3(p.items, p.num_kv_heads / PACK), p, w);
+  constexpr int NB = Shape<D * PACK, KT>::kNBuf;
+  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB>, dim3(p.items, p.num_kv_heads / PACK), p, w);
 }
 
 // KV heads per workgroup.  Two heads per pack would make every staged row at
@@ -515,24 +592,40 @@ static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Laun
 // about 12% slower), but a packed tile then fills the LDS budget of two
 // staging slots per wave, and on MI355X that lost more than the longer rows
 // gained (batch-128 fp8 decode: 311 us unpacked, 407-424 us packed).  So the
-// default is one head per workgroup; KVS_ALGO_MFMA_PACKED asks for packs.
-int mfma_pack(int head_dim, int group, int num_kv_heads, bool fp8, bool allow_pack) {
-  const int seg = head_dim * (fp8 ? 1 : 2);
+// default is one head per workgroup; KVS_ALGO_MFMA_PACKED asks for packs
+// (not for INT4).
+int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack) {
+  if (kv_type == DT_INT4) return 1;
+  const int seg = head_dim * (kv_type == DT_FP8 ? 1 : 2);
   return (allow_pack && seg < 256 && 2 * group <= 16 && num_kv_heads % 2 == 0) ? 2 : 1;
 }
 
-hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, bool fp8, const Launch &l) {
+// Which head sizes the matrix-core kernel takes for a KV type (INT4 rows must
+// give each of the four lane quarters a 16-byte piece: head_dim >= 128).
+bool mfma_head_dim_ok(int head_dim, int kv_type) {
+  if (kv_type == DT_INT4) return head_dim == 128 || head_dim == 256;
+  return head_dim == 64 || head_dim == 128 || head_dim == 256;
+}
+
+hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
   const bool pack2 = p.pack == 2;
+  if (kv_type == DT_INT4) {
+    if (pack2) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_mfma_d<128, 1, DT_INT4>(p, w, l);
+    if (head_dim == 256) return launch_mfma_d<256, 1, DT_INT4>(p, w, l);
+    return hipErrorInvalidValue;
+  }
+  const bool fp8 = kv_type == DT_FP8;
   switch (head_dim) {
   case 64:
-    if (fp8) return pack2 ? launch_mfma_d<64, 2, true>(p, w, l) : launch_mfma_d<64, 1, true>(p, w, l);
-    return pack2 ? launch_mfma_d<64, 2, false>(p, w, l) : launch_mfma_d<64, 1, false>(p, w, l);
+    if (fp8) return pack2 ? launch_mfma_d<64, 2, DT_FP8>(p, w, l) : launch_mfma_d<64, 1, DT_FP8>(p, w, l);
+    return pack2 ? launch_mfma_d<64, 2, DT_BF16>(p, w, l) : launch_mfma_d<64, 1, DT_BF16>(p, w, l);
   case 128:
-    if (fp8) return pack2 ? launch_mfma_d<128, 2, true>(p, w, l) : launch_mfma_d<128, 1, true>(p, w, l);
-    return pack2 ? launch_mfma_d<128, 2, false>(p, w, l) : launch_mfma_d<128, 1, false>(p, w, l);
+    if (fp8) return pack2 ? launch_mfma_d<128, 2, DT_FP8>(p, w, l) : launch_mfma_d<128, 1, DT_FP8>(p, w, l);
+    return pack2 ? launch_mfma_d<128, 2, DT_BF16>(p, w, l) : launch_mfma_d<128, 1, DT_BF16>(p, w, l);
   case 256:
     if (pack2) return hipErrorInvalidValue;
-    return fp8 ? launch_mfma_d<256, 1, true>(p, w, l) : launch_mfma_d<256, 1, false>(p, w, l);
+    return fp8 ? launch_mfma_d<256, 1, DT_FP8>(p, w, l) : launch_mfma_d<256, 1, DT_BF16>(p, w, l);
   default: return hipErrorInvalidValue;
   }
 }

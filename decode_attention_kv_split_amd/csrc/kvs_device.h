@@ -34,7 +34,7 @@ constexpr int64_t kMaxWorkgroups = (int64_t{1} << 24) - 1; // per partial launch
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT4 = 3 }; // the kvs_dtype codes
 
 // Where a kernel goes: its stream and, optionally, two events that the
 // kernel's own dispatch stamps with its start and end time (no extra marker

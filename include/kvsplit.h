@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 3
+#define KVS_ABI_VERSION 4
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -65,9 +65,15 @@ typedef enum {
 } kvs_status;
 
 /* Element types.  q and o share q_dtype; K and V share kv_dtype.
- * Supported (q_dtype, kv_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * FP8_E4M3 is the OCP E4M3 ("fn") format: bias 7, max 448, NaN = S.1111.111. */
-typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_FP8_E4M3 = 2 } kvs_dtype;
+ * Supported (q_dtype, kv_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ * (BF16, INT4).
+ * FP8_E4M3 is the OCP E4M3 ("fn") format: bias 7, max 448, NaN = S.1111.111.
+ * INT4: signed 4-bit integers in [-8, 7] (two's complement), two per byte,
+ * element 2i in the low nibble of byte i, so a row of head_dim elements is
+ * head_dim / 2 bytes ("Beyond the Memory Wall", section "2. FlashInfer",
+ * names FP8 and INT4 KV caches; this packing is the reading taken).  INT4
+ * needs head_dim 128 or 256 and the matrix-core kernel (kvs_decode only). */
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_FP8_E4M3 = 2, KVS_INT4 = 3 } kvs_dtype;
 
 /* Kernel family for the per-chunk partial softmax.  AUTO picks MFMA for bf16
  * and fp8 KV with page_size 0 or >= 16 (query group packed into the columns
@@ -87,7 +93,8 @@ typedef struct {
   int32_t q_dtype;      /* kvs_dtype of q and o */
   int32_t kv_dtype;     /* kvs_dtype of K and V */
   int32_t page_size;    /* 0: contiguous K, V [kv_len, Hk, head_dim];
-                           > 0: paged pools [num_pages, page_size, Hk, head_dim] */
+                           > 0: paged pools [num_pages, page_size, Hk, head_dim]
+                           (INT4: the last axis is head_dim / 2 bytes) */
   int32_t num_pages;    /* paged: number of pages in each pool (for validation of
                            the host-side lengths only; page ids are not checked) */
 
@@ -102,8 +109,9 @@ typedef struct {
                                   (the current token included) */
   const int32_t *kv_len_host;  /* host copy of kv_len, used to plan the launch;
                                   must equal kv_len */
-  const float *k_scale;        /* FP8 only: [batch, Hk] dequantisation scale of K */
-  const float *v_scale;        /* FP8 only: [batch, Hk] dequantisation scale of V */
+  const float *k_scale;        /* FP8 and INT4 only: [batch, Hk] dequantisation scale
+                                  of K (stored code * scale = value) */
+  const float *v_scale;        /* FP8 and INT4 only: [batch, Hk] scale of V */
 
   /* scalars */
   float sm_scale;     /* > 0 and finite, multiplies <q, k> */
@@ -209,7 +217,7 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;   /* 64, 128 or 256 */
   int32_t q_dtype;    /* q_in, k_in, v_in, q_out: KVS_F32 or KVS_BF16 */
-  int32_t kv_dtype;   /* cache; pairs as for kvs_decode */
+  int32_t kv_dtype;   /* cache; pairs as for kvs_decode, INT4 not supported */
   int32_t page_size;  /* 0: contiguous; else a power of two */
   int32_t num_pages;  /* paged: pages in each pool; contiguous: capacity (tokens) */
 

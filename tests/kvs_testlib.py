@@ -12,7 +12,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # max |o - o_ref| over all elements, by KV storage type
-O_TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+O_TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int4": 6e-2}
 LSE_REL = 1e-3
 
 
@@ -52,7 +52,7 @@ def to_torch(inp, device="cuda"):
     if s.page_size:
         t["page_indptr"] = torch.from_numpy(inp.page_indptr.astype(np.int32)).to(device)
         t["page_indices"] = torch.from_numpy(inp.page_indices.astype(np.int32)).to(device)
-    if s.kv_dtype == "fp8":
+    if s.kv_dtype in ("fp8", "int4"):
         t["k_scale"] = torch.from_numpy(inp.k_scale).to(device)
         t["v_scale"] = torch.from_numpy(inp.v_scale).to(device)
     return t
@@ -68,7 +68,7 @@ def run_library(inp, tensors=None, **kw):
     o, lse = kvs.decode(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                         page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                         k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
-                        window=s.window, **kw)
+                        window=s.window, kv_dtype="int4" if s.kv_dtype == "int4" else None, **kw)
     torch.cuda.synchronize()
     return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
 

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 3
-    assert re.search(r"#define KVS_ABI_VERSION 3\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 4
+    assert re.search(r"#define KVS_ABI_VERSION 4\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -79,7 +79,7 @@ def _args(batch=2, Hq=8, Hk=2, d=128, q=kvs.KVS_BF16, kv=kvs.KVS_BF16, P=16, len
     if ptrs:
         a.q = a.k = a.v = a.kv_len = a.o = fake
         a.page_indptr = a.page_indices = fake if P else None
-        a.k_scale = a.v_scale = fake if kv == kvs.KVS_FP8_E4M3 else None
+        a.k_scale = a.v_scale = fake if kv in (kvs.KVS_FP8_E4M3, kvs.KVS_INT4) else None
     a.kv_len_host = host.ctypes.data
     a.sm_scale = 0.125
     a.window = window
@@ -109,6 +109,11 @@ BAD = [
     (dict(P=8, algo=kvs.KVS_ALGO_MFMA), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=kvs.KVS_F32, kv=kvs.KVS_F32, algo=kvs.KVS_ALGO_MFMA), kvs.KVS_ERR_UNSUPPORTED),
     (dict(kv=kvs.KVS_FP8_E4M3, Hq=32, Hk=2, algo=kvs.KVS_ALGO_VALU), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(kv=kvs.KVS_INT4, d=64), kvs.KVS_ERR_UNSUPPORTED),                 # INT4 needs head_dim >= 128
+    (dict(kv=kvs.KVS_INT4, algo=kvs.KVS_ALGO_VALU), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(kv=kvs.KVS_INT4, P=8), kvs.KVS_ERR_UNSUPPORTED),                  # matrix-core kernel: pages >= 16
+    (dict(q=kvs.KVS_F32, kv=kvs.KVS_INT4), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(kv=4), kvs.KVS_ERR_INVALID_ARG),
     # 2^26 splits of 16 tokens x 32 KV heads: more workgroups than one launch holds
     (dict(batch=1, P=0, Hq=32, Hk=32, lens=(1 << 30,), chunk=16), kvs.KVS_ERR_UNSUPPORTED),
 ]
@@ -248,6 +253,7 @@ BAD_APPEND = [
     (dict(d=96), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=kvs.KVS_F32, kv=kvs.KVS_BF16), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=5), kvs.KVS_ERR_INVALID_ARG),
+    (dict(kv=kvs.KVS_INT4), kvs.KVS_ERR_UNSUPPORTED),           # the step does not write INT4 caches
     (dict(P=0), kvs.KVS_ERR_INVALID_ARG),          # contiguous with batch 2
     (dict(P=24), kvs.KVS_ERR_UNSUPPORTED),
     (dict(P=-16), kvs.KVS_ERR_INVALID_ARG),
