@@ -79,6 +79,9 @@ class DecodeSpec:
     lengths: tuple = ("fixed", 512)
     qk_rmsnorm: bool = False
     seed: int = 1000
+    # new query tokens per request: ("fixed", n) | ("list", [n_b...]) | ("uniform", lo, hi);
+    # each is capped at the request's kv_len (its tokens are already cached)
+    q_len: tuple = ("fixed", 1)
 
     @property
     def group(self) -> int:
@@ -94,8 +97,9 @@ class DecodeInputs:
     kv_len: np.ndarray  # int32 [batch]
     page_indptr: Optional[np.ndarray]  # int32 [batch + 1] (paged only)
     page_indices: Optional[np.ndarray]  # int32 [nnz] (paged only)
-    k_scale: Optional[np.ndarray]  # float32 [batch, Hk] (fp8 only)
+    k_scale: Optional[np.ndarray]  # float32 [batch, Hk] (fp8 and int4 only)
     v_scale: Optional[np.ndarray]
+    qo_indptr: Optional[np.ndarray] = None  # int32 [batch + 1]: query rows of each request (None: one each)
 
     @property
     def num_pages(self) -> int:
@@ -183,7 +187,23 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
     if P == 0 and B != 1:
         raise ValueError("a contiguous cache holds one request")
 
-    q = r_q.standard_normal((B, Hq, d), dtype=np.float32)
+    qo_indptr = None
+    if spec.q_len == ("fixed", 1):
+        q = r_q.standard_normal((B, Hq, d), dtype=np.float32)
+    else:
+        r_ql = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x9E])))
+        kind = spec.q_len[0]
+        if kind == "fixed":
+            ql = np.full(B, int(spec.q_len[1]), np.int64)
+        elif kind == "list":
+            ql = np.asarray(spec.q_len[1], np.int64)
+        elif kind == "uniform":
+            ql = r_ql.integers(spec.q_len[1], spec.q_len[2], size=B, endpoint=True)
+        else:
+            raise ValueError(f"unknown query-length law {kind!r}")
+        ql = np.minimum(ql, kv_len.astype(np.int64))
+        qo_indptr = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        q = r_q.standard_normal((int(qo_indptr[-1]), Hq, d), dtype=np.float32)
     total = int(kv_len.sum())
     k_log = r_k.standard_normal((total, Hk, d), dtype=np.float32)
     v_log = r_v.standard_normal((total, Hk, d), dtype=np.float32)
@@ -240,7 +260,7 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
                        else np.full(pad.shape, fill, pad.dtype))
             k_codes = np.concatenate([k_codes, pad])
             v_codes = np.concatenate([v_codes, pad])
-        return DecodeInputs(spec, q_codes, k_codes, v_codes, kv_len, None, None, k_scale, v_scale)
+        return DecodeInputs(spec, q_codes, k_codes, v_codes, kv_len, None, None, k_scale, v_scale, qo_indptr)
 
     n_pages = (kv_len.astype(np.int64) + reserve_tokens + P - 1) // P
     indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
@@ -274,7 +294,7 @@ def make_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, poison: bool = 
         if rem:
             k_pool[pages[full], :rem] = src_k[full * P:]
             v_pool[pages[full], :rem] = src_v[full * P:]
-    return DecodeInputs(spec, q_codes, k_pool, v_pool, kv_len, indptr, perm, k_scale, v_scale)
+    return DecodeInputs(spec, q_codes, k_pool, v_pool, kv_len, indptr, perm, k_scale, v_scale, qo_indptr)
 
 
 # The five workloads.  Sizes follow the decode shapes the pages discuss: an
@@ -308,10 +328,13 @@ def config(name: str) -> DecodeSpec:
 
 
 def small_variant(name: str, *, batch: Optional[int] = None, lengths: Optional[tuple] = None,
-                  window: Optional[int] = None, seed: Optional[int] = None) -> DecodeSpec:
+                  window: Optional[int] = None, seed: Optional[int] = None,
+                  q_len: Optional[tuple] = None) -> DecodeSpec:
     """Same heads, head_dim, dtypes and layout as a named workload, smaller sizes."""
     base = CONFIGS[name]
     kw = {}
+    if q_len is not None:
+        kw["q_len"] = q_len
     if batch is not None:
         kw["batch"] = batch
     if lengths is not None:
