@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 4
+KVS_ABI_VERSION = 5
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
@@ -80,6 +80,8 @@ class KvsDecodeArgs(ctypes.Structure):
         ("prof_events", ctypes.c_void_p * 2),
         ("use_unified_max", ctypes.c_int32),
         ("unified_max", ctypes.c_float),
+        ("qo_indptr", ctypes.c_void_p),
+        ("qo_indptr_host", ctypes.c_void_p),
     ]
 
 
@@ -92,6 +94,7 @@ class KvsPlanInfo(ctypes.Structure):
         ("algo", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("col_groups", ctypes.c_int32),
     ]
 
 
@@ -269,20 +272,34 @@ def _workspace(nbytes: int, device, stream: int):
 def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None,
               k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
               algo="auto", out=None, lse=None, num_cus: int = 0,
-              unified_max: Optional[float] = None, kv_dtype: Optional[str] = None) -> Tuple[KvsDecodeArgs, object]:
+              unified_max: Optional[float] = None, kv_dtype: Optional[str] = None, qo_indptr=None,
+              qo_indptr_host=None) -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
     [num_pages, page_size, Hk, d]; kv_len: int32 [batch] on the device.
     kv_dtype='int4' marks uint8 caches whose last axis holds d / 2 bytes of
-    packed nibbles.  Returns (args, keepalive)."""
+    packed nibbles.  qo_indptr (int32 [batch + 1] on the device, with a host
+    copy) gives several query rows per request: q is then [total_q, Hq, d].
+    Returns (args, keepalive)."""
     import numpy as np
     import torch
 
     device = q.device
     if q.dim() != 3:
-        raise ValueError("q must be [batch, num_qo_heads, head_dim]")
-    B, Hq, d = q.shape
+        raise ValueError("q must be [batch (or total_q), num_qo_heads, head_dim]")
+    rows, Hq, d = q.shape
+    B = int(kv_len.numel())
+    qoh = None
+    if qo_indptr is not None:
+        src = qo_indptr_host if qo_indptr_host is not None else qo_indptr.cpu()
+        qoh = np.ascontiguousarray(np.asarray(src.cpu() if isinstance(src, torch.Tensor) else src, dtype=np.int32))
+        if qoh.shape != (B + 1,) or int(qoh[-1]) != rows:
+            raise ValueError("qo_indptr must be [batch + 1] ending at q's row count")
+        if qo_indptr.dtype != torch.int32 or qo_indptr.numel() != B + 1:
+            raise ValueError("qo_indptr must be int32 [batch + 1]")
+    elif rows != B:
+        raise ValueError("q must have one row per request without qo_indptr")
     paged = page_indptr is not None
     if paged:
         if k.dim() != 4:
@@ -301,7 +318,8 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     elif dk != d:
         raise ValueError("head_dim of q and k differ")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len"), (page_indptr, "page_indptr"),
-                 (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+                 (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (qo_indptr, "qo_indptr")):
         _check_dev(t, n, device)
     if kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("kv_len must be int32 [batch]")
@@ -310,9 +328,9 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     kvh = np.ascontiguousarray(np.asarray(kv_len_host.cpu() if isinstance(kv_len_host, torch.Tensor)
                                           else kv_len_host, dtype=np.int32))
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=q.dtype, device=device)
+        out = torch.empty((rows, Hq, d), dtype=q.dtype, device=device)
     if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=device)
+        lse = torch.empty((rows, Hq), dtype=torch.float32, device=device)
     _check_dev(out, "out", device)
     _check_dev(lse, "lse", device)
     a = KvsDecodeArgs()
@@ -333,13 +351,16 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     a.o, a.lse = _ptr(out), _ptr(lse)
     if unified_max is not None:
         a.use_unified_max, a.unified_max = 1, float(unified_max)
-    keep = (kvh, out, lse)
+    if qoh is not None:
+        a.qo_indptr, a.qo_indptr_host = _ptr(qo_indptr), qoh.ctypes.data
+    keep = (kvh, out, lse, qoh)
     return a, keep
 
 
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
-           workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None):
+           workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None,
+           qo_indptr=None, qo_indptr_host=None):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
@@ -347,7 +368,7 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
     a, keep = make_args(q, k, v, kv_len, page_indptr=page_indptr, page_indices=page_indices,
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
                         window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
-                        kv_dtype=kv_dtype)
+                        kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

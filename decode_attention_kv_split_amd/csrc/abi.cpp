@@ -3,8 +3,10 @@
 // log-sum-exp merge).  No device memory is allocated and nothing synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "kvsplit.h"
 #include "kvs_device.h"
@@ -64,16 +66,28 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
     if (L < 0) return KVS_ERR_INVALID_ARG;
     if (a->page_size > 0 && (int64_t)L > (int64_t)a->num_pages * a->page_size) return KVS_ERR_INVALID_ARG;
   }
+  // several queries per request: row offsets start at 0, never decrease, and
+  // a request has at most kv_len new tokens
+  const bool multi = a->qo_indptr_host != nullptr;
+  if (!multi && a->qo_indptr) return KVS_ERR_INVALID_ARG;
+  if (multi) {
+    if (a->qo_indptr_host[0] != 0) return KVS_ERR_INVALID_ARG;
+    for (int b = 0; b < a->batch; ++b) {
+      const int n = a->qo_indptr_host[b + 1] - a->qo_indptr_host[b];
+      if (n < 0 || n > a->kv_len_host[b]) return KVS_ERR_INVALID_ARG;
+    }
+  }
   if (need_ptrs) {
     if (!a->q || !a->k || !a->v || !a->kv_len || !a->o) return KVS_ERR_INVALID_ARG;
     if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
     if (scaled && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
+    if (multi && !a->qo_indptr) return KVS_ERR_INVALID_ARG;
   }
   // kernel family (INT4 runs on the matrix-core kernel only)
   const bool mfma_ok = a->kv_dtype != KVS_F32 && a->q_dtype == KVS_BF16 &&
                        (a->page_size == 0 || a->page_size >= 16) &&
                        kvs::mfma_head_dim_ok(a->head_dim, a->kv_dtype);
-  const bool valu_ok = a->kv_dtype != KVS_INT4 && group <= kvs::valu_max_group(a->kv_dtype);
+  const bool valu_ok = a->kv_dtype != KVS_INT4 && !multi && group <= kvs::valu_max_group(a->kv_dtype);
   switch (a->algo) {
   case KVS_ALGO_AUTO:
     if (mfma_ok)
@@ -86,6 +100,7 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   case KVS_ALGO_MFMA:
   case KVS_ALGO_MFMA_PACKED:
     if (!mfma_ok) return KVS_ERR_UNSUPPORTED;
+    if (a->algo == KVS_ALGO_MFMA_PACKED && multi) return KVS_ERR_UNSUPPORTED; // columns are (query, head) pairs
     *algo = a->algo;
     break;
   case KVS_ALGO_VALU:
@@ -138,17 +153,43 @@ kvs_status resolve_cus(const kvs_decode_args *a, int *cus) {
   return KVS_OK;
 }
 
-kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, int *algo, int *cus) {
+// Query rows per request and the column groups they need (several queries
+// per request only; otherwise nq stays empty and there is one group).
+struct Columns {
+  std::vector<int32_t> nq;
+  int col_groups = 1;
+  int cols = 0; // partial-result columns per KV head over all groups
+};
+
+Columns columns_of(const kvs_decode_args *a) {
+  Columns c;
+  const int group = a->num_qo_heads / a->num_kv_heads;
+  c.cols = group;
+  if (!a->qo_indptr_host) return c;
+  c.nq.resize(a->batch);
+  int most = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    c.nq[b] = a->qo_indptr_host[b + 1] - a->qo_indptr_host[b];
+    most = std::max(most, c.nq[b]);
+  }
+  c.col_groups = std::max(1, (int)(((int64_t)most * group + 15) / 16));
+  c.cols = c.col_groups * 16;
+  return c;
+}
+
+kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, int *algo, int *cus,
+                     Columns *cols_out = nullptr) {
   kvs_status st = validate(a, need_ptrs, algo);
   if (st != KVS_OK) return st;
   st = resolve_cus(a, cus);
   if (st != KVS_OK) return st;
-  const int group = a->num_qo_heads / a->num_kv_heads;
-  if (!kvs::make_plan(a->kv_len_host, a->batch, a->window, a->num_kv_heads, group, a->head_dim,
-                      a->kv_chunk, *cus, pl))
+  Columns c = columns_of(a);
+  if (!kvs::make_plan(a->kv_len_host, c.nq.empty() ? nullptr : c.nq.data(), a->batch, a->window,
+                      a->num_kv_heads, c.cols, c.col_groups, a->head_dim, a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
-  // grid.x (items) of kThreads work-items must stay below 2^32 work-items
-  if ((int64_t)pl->items * a->num_kv_heads > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
+  // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
+  if ((int64_t)pl->items * a->num_kv_heads * c.col_groups > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
+  if (cols_out) *cols_out = std::move(c);
   return KVS_OK;
 }
 
@@ -169,6 +210,7 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   out->algo = algo;
   out->num_cus = cus;
   out->workspace_bytes = pl.workspace_bytes;
+  out->col_groups = columns_of(args).col_groups;
   return KVS_OK;
 }
 
@@ -182,7 +224,8 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args) {
 kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   kvs::Plan pl;
   int algo = 0, cus = 0;
-  kvs_status st = plan_call(a, true, &pl, &algo, &cus);
+  Columns cols;
+  kvs_status st = plan_call(a, true, &pl, &algo, &cus, &cols);
   if (st != KVS_OK) return st;
   if (pl.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < pl.workspace_bytes) return KVS_ERR_WORKSPACE;
@@ -214,6 +257,9 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.pack = algo == KVS_ALGO_VALU ? 1
                                  : kvs::mfma_pack(a->head_dim, p.group, a->num_kv_heads, a->kv_dtype,
                                                   algo == KVS_ALGO_MFMA_PACKED);
+  p.qo_indptr = a->qo_indptr_host ? a->qo_indptr : nullptr;
+  p.col_groups = cols.col_groups;
+  p.cols = a->qo_indptr_host ? 16 : p.group * p.pack;
   p.page_size = a->page_size;
   p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;
   p.window = a->window;
@@ -230,7 +276,8 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   ml.n = -1;
   if (a->batch <= kvs::kInlineRequests && pl.items <= kvs::kInlineItems) {
     int n_merges = 0; // at most one entry per request, so it fits too
-    kvs::list_work(a->kv_len_host, a->batch, a->window, pl.chunk, w.item, ml.req, ml.first, &n_merges);
+    kvs::list_work(a->kv_len_host, cols.nq.empty() ? nullptr : cols.nq.data(), a->batch, a->window, pl.chunk,
+                   w.item, ml.req, ml.first, &n_merges);
     for (int b = 0; b < a->batch; ++b) w.req_len[b] = a->kv_len_host[b];
     w.n_items = pl.items;
     ml.n = n_merges;

@@ -256,11 +256,14 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // pages spread over the pool, which streamed faster on MI355X than grids
   // that run all heads of an item together (on one XCD or spread over XCDs).
   const int item = blockIdx.x;
-  const int kvg = blockIdx.y; // KV heads kvg*PACK .. kvg*PACK+PACK-1
+  const int kvg = blockIdx.y / p.col_groups; // KV heads kvg*PACK .. kvg*PACK+PACK-1
+  const int cg = blockIdx.y % p.col_groups;  // column group (several queries per request)
   const int g = p.group;
   const int gp = g * PACK;    // query heads of the pack (<= 16)
   const int Hk = p.num_kv_heads;
-  const int my_kv = c16 / g;  // KV head (within the pack) of query head c16
+  // KV head (within the pack) of this lane's column; (query, head) columns
+  // are only run with one KV head per workgroup
+  const int my_kv = p.qo_indptr ? 0 : c16 / g;
 
   // ---- which (request, split) is this workgroup? ----
   int b, split, nb, L;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     b = (int)(e >> 16);
     split = (int)(e & 0xFFFF);
     L = w.req_len[b];
-    nb = num_splits(L, p.window, p.chunk);
+    nb = num_splits(L, req_nq(p, b), p.window, p.chunk);
   } else {
     if (tid == 0) s_item[0] = -1;
     scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
@@ -285,29 +288,63 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     split = __builtin_amdgcn_readfirstlane(s_item[1]);
     nb = __builtin_amdgcn_readfirstlane(s_item[2]);
     if (b < 0) return; // kv_len on the device disagrees with the planned launch
-    if (p.meta && split == 0 && kvg == 0 && tid == 0) {
+    if (p.meta && split == 0 && blockIdx.y == 0 && tid == 0) {
       p.meta[2 * b] = s_item[3];
       p.meta[2 * b + 1] = nb;
     }
     L = p.kv_len[b];
   }
 
-  const int lo = visible_lo(L, p.window);
+  // ---- columns: query heads of the pack, or (query row, head) pairs ----
+  const int nq = req_nq(p, b);
+  if (p.qo_indptr && cg * 16 >= nq * g) return; // this column group is empty for the request
+  int qrow;   // row of q / o of this lane's column
+  int qhead;  // query head of this lane's column
+  bool col_ok;
+  int qi;     // query index within the request (0 with one query)
+  if (!p.qo_indptr) {
+    col_ok = c16 < gp;
+    qi = 0;
+    qrow = b;
+    qhead = kvg * gp + c16;
+  } else {
+    const int col = cg * 16 + c16;
+    col_ok = col < nq * g;
+    qi = col / g;
+    qrow = p.qo_indptr[b] + qi;
+    qhead = kvg * g + col % g;
+  }
+  // keys this column sees: up to its query's position, the last `window` of them
+  const int qpos = L - nq + qi;
+  const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
+  const int col_hi = qpos + 1;
+
+  const int lo = request_lo(L, nq, p.window);
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
   const int t_begin = max(lo, a0);
   const int t_end = min(L, a0 + p.chunk);
   const int ntiles = t_end > t_begin ? (t_end - a0 + kTile - 1) / kTile : 0;
+  // per-column visible range within the chunk, and the range every column sees
+  const int lane_lo = max(t_begin, col_lo);
+  const int lane_hi = min(t_end, col_hi);
+  int all_lo = col_ok ? lane_lo : t_begin, all_hi = col_ok ? lane_hi : t_end;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // ---- Q^T operand: block diagonal over the pack, zero columns past gp ----
   bf16x8_t qop[S::kKSteps];
   {
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) +
-                         ((size_t)b * p.num_qo_heads + (size_t)kvg * gp + c16) * D;
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j) {
       const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
-      if (c16 < gp && kd / D == my_kv) {
+      if (col_ok && kd / D == my_kv) {
         bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
         if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
         qop[j] = x;
@@ -446,14 +483,14 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       for (int r = 0; r < 4; ++r) s[r] -= qoff; // remove the 136-per-element offset of K
     }
     float sv[4];
-    if (ts >= t_begin && ts + kTile <= t_end) { // every key of the tile is visible (uniform branch)
+    if (ts >= all_lo && ts + kTile <= all_hi) { // every column sees every key of the tile (uniform branch)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = ts + 4 * q4 + r;
-        sv[r] = (tok >= t_begin && tok < t_end) ? s[r] * cscale : -INFINITY;
+        sv[r] = (tok >= lane_lo && tok < lane_hi) ? s[r] * cscale : -INFINITY;
       }
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
@@ -554,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     lb_tot = lb_run + __shfl_xor(lb_run, 16, 64);
     lb_tot += __shfl_xor(lb_tot, 32, 64);
   }
-  if (c16 < gp) {
+  if (col_ok) {
     if (q4 == 0) {
       sm_m[wave][c16] = l_tot > 0.0f ? m_run : -INFINITY; // an empty state keeps no reference
       sm_l[wave][c16] = l_tot;
@@ -576,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     }
   }
   __syncthreads();
-  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, item, nb);
+  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg, item, nb);
 }
 
 } // namespace
@@ -584,7 +621,8 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 template <int D, int PACK, int KT>
 static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
   constexpr int NB = Shape<D * PACK, KT>::kNBuf;
-  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB>, dim3(p.items, p.num_kv_heads / PACK), p, w);
+  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB>,
+                       dim3(p.items, p.num_kv_heads / PACK * p.col_groups), p, w);
 }
 
 // KV heads per workgroup.  Two heads per pack would make every staged row at

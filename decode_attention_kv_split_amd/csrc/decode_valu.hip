@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
     b = (int)(e >> 16);
     split = (int)(e & 0xFFFF);
     L = w.req_len[b];
-    nb = num_splits(L, p.window, p.chunk);
+    nb = num_splits(L, 1, p.window, p.chunk);
   } else {
     if (tid == 0) s_item[0] = -1;
     scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
     }
   }
   __syncthreads();
-  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, item, nb);
+  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, 0, item, nb);
 }
 
 template <int D, int KVT>

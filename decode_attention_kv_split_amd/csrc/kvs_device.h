@@ -1,24 +1,30 @@
 // Device-side pieces shared by the split-KV decode kernels (gfx950).
 //
-// Work decomposition.  The visible keys of request b start at
-// lo_b = max(0, L_b - window) (window > 0) and end at L_b.  Tokens are grouped
-// in tiles of 16 aligned to absolute token positions; the chunks of a request
-// start at A_b = lo_b rounded down to 16 and are kv_chunk tokens long (a
-// multiple of 16), so request b has n_b = max(1, ceil((L_b - A_b) / kv_chunk))
-// splits.  Work items of one KV head are numbered request by request; grid.x
-// runs over them and grid.y over KV heads.  Both kernels derive (request,
-// split) from kv_len on the device, so no work list crosses the PCIe bus.
+// Work decomposition.  Request b has nq_b query rows (one in decode; its
+// nq_b newest tokens with several) and L_b keys; the keys any of its queries
+// sees start at lo_b = max(0, L_b - nq_b + 1 - window) (window > 0) and end
+// at L_b.  Tokens are grouped in tiles of 16 aligned to absolute token
+// positions; the chunks of a request start at A_b = lo_b rounded down to 16
+// and are kv_chunk tokens long (a multiple of 16), so request b has
+// n_b = max(1, ceil((L_b - A_b) / kv_chunk)) splits.  Work items of one KV
+// head are numbered request by request; grid.x runs over them, grid.y over
+// (KV-head pack, column group).  The host passes the item list in the kernel
+// arguments when it fits; otherwise both kernels derive (request, split)
+// from kv_len on the device.
 //
 // The workgroup that runs split 0 of KV head 0 of a request records the
 // request's first work item and split count in meta[2b], meta[2b+1]; the merge
 // kernel reads them instead of scanning the batch again.
 //
-// A workgroup may serve `pack` adjacent KV heads (its query heads are the
-// gp = g * pack consecutive heads kvg * gp ...).  Partial results of split x
-// of pack kvg live in the workspace: o_part[((kvg * I + x) * gp + h) * D + d]
-// (fp32, already divided by the chunk's sum and multiplied by the V scale)
-// and lse_part[(kvg * I + x) * gp + h] (log2 domain: chunk max + log2(chunk
-// sum), -inf when the chunk saw no key), I = items per KV head.
+// Columns.  A workgroup computes up to 16 columns of query rows: with one
+// query per request, the gp = g * pack query heads of `pack` adjacent KV
+// heads; with several, the (query row, head) pairs cg * 16 .. cg * 16 + 15 of
+// one KV head (column c = row * g + head), in column group cg.  Partial
+// results of split x of slot (pack kvg, column group cg) live in the
+// workspace: o_part[((S * I + x) * cols + h) * D + d] with S = kvg *
+// col_groups + cg (fp32, already divided by the chunk's sum and multiplied by
+// the V scale) and lse_part[(S * I + x) * cols + h] (log2 domain: chunk max +
+// log2(chunk sum), -inf when the chunk saw no key), I = items per KV head.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -75,6 +81,9 @@ struct Params {
   int window;
   int chunk;
   int items;      // work items per KV head
+  const int *qo_indptr; // [batch + 1] query rows of each request; null: one row each
+  int col_groups; // groups of 16 (query, head) columns per KV head (1 for one query)
+  int cols;       // columns per partial slot: group * pack (one query) or 16
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
   float score_scale; // sm_scale * log2(e)
@@ -124,15 +133,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_ev));
 }
 
-__device__ __forceinline__ int visible_lo(int L, int window) {
-  return window > 0 ? max(0, L - window) : 0;
+// Query rows of request b (its new tokens, the last ones of its cache).
+__device__ __forceinline__ int req_nq(const Params &p, int b) {
+  return p.qo_indptr ? p.qo_indptr[b + 1] - p.qo_indptr[b] : 1;
 }
 
-// Number of splits of a request with L keys.
-__device__ __forceinline__ int num_splits(int L, int window, int chunk) {
-  const int a = visible_lo(L, window) & ~(kTile - 1);
+// First key any of a request's nq queries sees: its first query sits at
+// position L - nq and sees the last `window` keys up to itself.
+__device__ __forceinline__ int request_lo(int L, int nq, int window) {
+  return window > 0 ? max(0, L - nq + 1 - window) : 0;
+}
+
+__device__ __forceinline__ int visible_lo(int L, int window) { return request_lo(L, 1, window); }
+
+// Number of splits of a request with L keys and nq queries.
+__device__ __forceinline__ int num_splits(int L, int nq, int window, int chunk) {
+  const int a = request_lo(L, nq, window) & ~(kTile - 1);
   const int span = L - a;
   return span <= 0 ? 1 : (span + chunk - 1) / chunk;
+}
+
+// Where column h of (request b, KV-head pack kvg, column group cg) goes:
+// output row and query head, or false for a padding column.  One query per
+// request: the columns are the pack's query heads.  Several: column
+// cg * 16 + h is (query row (cg * 16 + h) / g, head (cg * 16 + h) % g).
+__device__ __forceinline__ bool column_target(const Params &p, int b, int kvg, int cg, int h, int &row, int &head) {
+  if (!p.qo_indptr) {
+    row = b;
+    head = kvg * p.cols + h;
+    return h < p.cols;
+  }
+  const int col = cg * 16 + h;
+  const int q0 = p.qo_indptr[b];
+  if (col >= (p.qo_indptr[b + 1] - q0) * p.group) return false;
+  row = q0 + col / p.group;
+  head = kvg * p.group + col % p.group;
+  return true;
 }
 
 // Exclusive scan of per-request split counts over the whole batch, done by one
@@ -146,7 +182,7 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
   int base = 0;
   for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
     const int b = b0 + tid;
-    const int nb = b < p.batch ? num_splits(p.kv_len[b], p.window, p.chunk) : 0;
+    const int nb = b < p.batch ? num_splits(p.kv_len[b], req_nq(p, b), p.window, p.chunk) : 0;
     // inclusive wave scan
     int incl = nb;
 #pragma unroll
@@ -176,13 +212,14 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
 template <int D, int OSTRIDE>
 __device__ __forceinline__ void merge_waves_and_store(const Params &p, const float (*sm_m)[16],
                                                       const float (*sm_l)[16], const float *sm_o,
-                                                      int b, int kvg, int item, int nb) {
+                                                      int b, int kvg, int cg, int item, int nb) {
   const int g = p.group;
-  const int gp = g * p.pack;
-  for (int idx = threadIdx.x; idx < gp * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < p.cols * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
-    const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + kvg * p.pack + h / g] : 1.0f;
+    int row, hq;
+    if (!column_target(p, b, kvg, cg, h, row, hq)) continue; // padding column
+    const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + hq / g] : 1.0f;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -201,18 +238,17 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, const flo
         lse2 = M + __log2f(L);
       }
     }
-    const int hq = kvg * gp + h;
     if (nb == 1) {
-      const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
+      const size_t off = ((size_t)row * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16)
         reinterpret_cast<uint16_t *>(p.o)[off] = f32_to_bf16_bits(val);
       else
         reinterpret_cast<float *>(p.o)[off] = val;
-      if (d == 0 && p.lse) p.lse[(size_t)b * p.num_qo_heads + hq] = lse2 * kLn2;
+      if (d == 0 && p.lse) p.lse[(size_t)row * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
-      const size_t slot = (size_t)kvg * p.items + item;
-      p.o_part[(slot * gp + h) * D + d] = val;
-      if (d == 0) p.lse_part[slot * gp + h] = lse2;
+      const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
+      p.o_part[(slot * p.cols + h) * D + d] = val;
+      if (d == 0) p.lse_part[slot * p.cols + h] = lse2;
     }
   }
 }

@@ -66,7 +66,8 @@ __device__ __forceinline__ void combine(MergeState &a, const MergeState &b) {
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const InlineMerge ml, int D, int slices) {
   __shared__ MergeState s_st[kThreads];
-  const int kvg = blockIdx.y; // KV-head pack
+  const int kvg = blockIdx.y / p.col_groups; // KV-head pack
+  const int cg = blockIdx.y % p.col_groups;  // column group
   const int slice = blockIdx.z;
   int b, first, nb;
   if (ml.n >= 0) { // requests with several splits, listed by the host
@@ -79,9 +80,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
     nb = p.meta[2 * b + 1];
   }
   if (nb <= 1) return;
-  const int g = p.group * p.pack; // query heads merged by this workgroup
+  const int g = p.cols; // columns merged by this workgroup (query heads or (query, head) pairs)
   const int tid = threadIdx.x;
-  const size_t slot0 = (size_t)kvg * p.items + first;
+  const size_t slot0 = (size_t)blockIdx.y * p.items + first;
   const int Ds = D / slices;
   const int d0 = slice * Ds;
   const int F = g * Ds / 4;                        // float4 outputs of this workgroup
@@ -91,14 +92,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
   const float *lp = p.lse_part + slot0 * g;
   for (int f0 = 0; f0 < F; f0 += kThreads) {
     const int t = f0 + (SG > 1 ? tid % F : tid);
-    const int cg = SG > 1 ? tid / F : 0;
-    const bool active = t < F && cg < SG;
+    const int tg = SG > 1 ? tid / F : 0;       // thread group: which splits this thread folds
+    const bool active = t < F && tg < SG;
     const int h = t / (Ds / 4);
     const int d = d0 + 4 * (t % (Ds / 4));
     MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
     if (active) {
       const float4 *src = op + ((size_t)h * D + d) / 4;
-      for (int c0 = cg; c0 < nb; c0 += SG * kBatch) {
+      for (int c0 = tg; c0 < nb; c0 += SG * kBatch) {
         float lc[kBatch];
         float4 v[kBatch];
 #pragma unroll
@@ -117,11 +118,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
       if (tid < F)
         for (int j = 1; j < SG; ++j) combine(st, s_st[tid + j * F]);
     }
-    if (active && cg == 0) {
+    int row, hq;
+    if (active && tg == 0 && column_target(p, b, kvg, cg, h, row, hq)) {
       const float inv = st.w > 0.0f ? 1.0f / st.w : 0.0f;
       const float4 o = make_float4(st.acc.x * inv, st.acc.y * inv, st.acc.z * inv, st.acc.w * inv);
-      const int hq = kvg * g + h;
-      const size_t off = ((size_t)b * p.num_qo_heads + hq) * D + d;
+      const size_t off = ((size_t)row * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16) {
         *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
             make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + off) = o;
       }
       if (d == 0 && p.lse)
-        p.lse[(size_t)b * p.num_qo_heads + hq] = st.m == -INFINITY ? -INFINITY : (st.m + __log2f(st.w)) * kLn2;
+        p.lse[(size_t)row * p.num_qo_heads + hq] = st.m == -INFINITY ? -INFINITY : (st.m + __log2f(st.w)) * kLn2;
     }
   }
 }
@@ -143,7 +144,7 @@ hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hi
   // to head_dim / 64 slices while there are fewer than ~256 (request, pack)
   // pairs
   int slices = 1;
-  const int packs = p.num_kv_heads / p.pack;
+  const int packs = p.num_kv_heads / p.pack * p.col_groups;
   while (slices * 64 < head_dim && (int64_t)rows * packs * slices < 256) slices *= 2;
   dim3 grid(rows, packs, slices);
   return launch_kernel(Launch{stream}, merge_kernel, grid, p, ml, head_dim, slices);

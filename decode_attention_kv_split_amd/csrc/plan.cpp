@@ -6,15 +6,18 @@ namespace kvs {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, int group, int head_dim,
-               int forced_chunk, int num_cus, Plan *out) {
+// First key any query of a request sees (its first query sits at L - nq).
+static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(0, L - nq + 1 - window) : 0; }
+
+bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
+               int col_groups, int head_dim, int forced_chunk, int num_cus, Plan *out) {
   Plan pl;
   // span of request b: from its first 16-aligned visible tile to its last key
   int64_t total = 0;
   for (int b = 0; b < batch; ++b) {
     const int L = kv_len[b];
     if (L < 0) return false;
-    const int lo = window > 0 ? std::max(0, L - window) : 0;
+    const int lo = request_lo(L, nq ? nq[b] : 1, window);
     total += L - (lo & ~15);
   }
   int64_t chunk;
@@ -22,7 +25,7 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
     chunk = ((int64_t)forced_chunk + 15) / 16 * 16;
   } else {
     const int64_t target = (int64_t)kItemsPerCu * std::max(1, num_cus);
-    chunk = (total * num_kv_heads + target - 1) / target;
+    chunk = (total * num_kv_heads * col_groups + target - 1) / target;
     chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
     chunk = std::max<int64_t>(chunk, kMinChunk);
   }
@@ -32,7 +35,7 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
   int max_splits = 0;
   for (int b = 0; b < batch; ++b) {
     const int L = kv_len[b];
-    const int lo = window > 0 ? std::max(0, L - window) : 0;
+    const int lo = request_lo(L, nq ? nq[b] : 1, window);
     const int64_t span = L - (lo & ~15);
     const int64_t n = span <= 0 ? 1 : (span + chunk - 1) / chunk;
     items += n;
@@ -43,7 +46,7 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
   pl.max_splits = max_splits;
   pl.needs_merge = max_splits > 1;
   if (pl.needs_merge) {
-    const size_t slots = (size_t)items * num_kv_heads * group;
+    const size_t slots = (size_t)items * num_kv_heads * cols;
     pl.o_part_bytes = align256(slots * head_dim * sizeof(float));
     pl.lse_part_bytes = align256(slots * sizeof(float));
     pl.meta_bytes = align256((size_t)batch * 2 * sizeof(int));
@@ -53,12 +56,12 @@ bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, i
   return true;
 }
 
-void list_work(const int32_t *kv_len, int batch, int window, int chunk, uint32_t *items,
+void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint32_t *items,
                uint32_t *merge_req, uint32_t *merge_first, int *n_merges) {
   int x = 0, m = 0;
   for (int b = 0; b < batch; ++b) {
     const int L = kv_len[b];
-    const int lo = window > 0 ? std::max(0, L - window) : 0;
+    const int lo = request_lo(L, nq ? nq[b] : 1, window);
     const int64_t span = L - (lo & ~15);
     const int n = span <= 0 ? 1 : (int)((span + chunk - 1) / chunk);
     if (n > 1 && merge_req) {

@@ -36,11 +36,17 @@ constexpr int kMaxChunk = 4096;
 // InlineMerge): items[x] = (request << 16) | split for the items of one KV
 // head in device order; merges = (request << 16) | splits and the request's
 // first item, for requests with more than one split.
-void list_work(const int32_t *kv_len, int batch, int window, int chunk, uint32_t *items,
+// nq: query rows per request (null: one each); a request's keys start at the
+// first key its first query sees.
+void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint32_t *items,
                uint32_t *merge_req, uint32_t *merge_first, int *n_merges);
 
-// kv_len: host lengths [batch]; returns false if a length is negative.
-bool make_plan(const int32_t *kv_len, int batch, int window, int num_kv_heads, int group, int head_dim,
-               int forced_chunk, int num_cus, Plan *out);
+// kv_len: host lengths [batch]; nq: query rows per request or null (one
+// each); cols: partial-result columns per KV head over all column groups
+// (the group size with one query per request, col_groups * 16 with
+// several); col_groups: workgroups per (item, KV head).  Returns false if a
+// length is negative.
+bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
+               int col_groups, int head_dim, int forced_chunk, int num_cus, Plan *out);
 
 } // namespace kvs

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 4
+#define KVS_ABI_VERSION 5
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -141,6 +141,23 @@ typedef struct {
    * matrix-core kernels; the vector kernel ignores it.  0: off. */
   int32_t use_unified_max;
   float unified_max;
+
+  /* optional: several new query tokens per request (append / prefill
+   * attention).  NULL (both): one query per request, the decode step above.
+   * Otherwise q, o and lse hold total_q = qo_indptr[batch] rows
+   * ([total_q, Hq, head_dim] and [total_q, Hq]); request b's rows are
+   * qo_indptr[b] .. qo_indptr[b+1] - 1, its n_b = qo_indptr[b+1] -
+   * qo_indptr[b] (0 <= n_b <= kv_len[b]) newest cached tokens.  Row i of the
+   * request sits at position p = kv_len[b] - n_b + i and sees the keys
+   * max(0, p - window + 1) .. p (window > 0), else 0 .. p: the causal mask of
+   * "Forcing Flash Attention onto TPU", section "standard causal
+   * attention".  Runs on the matrix-core kernel (bf16 / fp8 / INT4 KV, not
+   * KVS_ALGO_MFMA_PACKED).  Each workgroup computes 16 (row, head) columns of
+   * one KV head, so K/V are read once per ceil(n_b * group / 16) column
+   * groups: efficient for short appends (speculative tokens, small chunks),
+   * bandwidth-heavy for long prefill. */
+  const int32_t *qo_indptr;      /* device [batch + 1] */
+  const int32_t *qo_indptr_host; /* host copy (plans the launch); must equal qo_indptr */
 } kvs_decode_args;
 
 /* What a call will launch, computed on the host from kv_len_host. */
@@ -153,6 +170,7 @@ typedef struct {
   int32_t algo;              /* resolved kvs_algo (VALU, MFMA or MFMA_PACKED) */
   int32_t num_cus;           /* CU count the plan was made for */
   size_t workspace_bytes;    /* bytes kvs_decode needs for this plan */
+  int32_t col_groups;        /* workgroups per (item, KV head): 1 unless several queries per request */
 } kvs_plan_info;
 
 /* Plan a call without launching anything.  Makes no HIP call when

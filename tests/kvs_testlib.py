@@ -55,6 +55,8 @@ def to_torch(inp, device="cuda"):
     if s.kv_dtype in ("fp8", "int4"):
         t["k_scale"] = torch.from_numpy(inp.k_scale).to(device)
         t["v_scale"] = torch.from_numpy(inp.v_scale).to(device)
+    if getattr(inp, "qo_indptr", None) is not None:
+        t["qo_indptr"] = torch.from_numpy(inp.qo_indptr.astype(np.int32)).to(device)
     return t
 
 
@@ -68,7 +70,9 @@ def run_library(inp, tensors=None, **kw):
     o, lse = kvs.decode(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                         page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                         k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
-                        window=s.window, kv_dtype="int4" if s.kv_dtype == "int4" else None, **kw)
+                        window=s.window, kv_dtype="int4" if s.kv_dtype == "int4" else None,
+                        qo_indptr=t.get("qo_indptr"),
+                        qo_indptr_host=getattr(inp, "qo_indptr", None), **kw)
     torch.cuda.synchronize()
     return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
 

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 4
-    assert re.search(r"#define KVS_ABI_VERSION 4\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 5
+    assert re.search(r"#define KVS_ABI_VERSION 5\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -126,6 +126,28 @@ def test_validation_before_any_hip_call(lib, kw, status):
     with pytest.raises(kvs.KvsError):
         kvs.kvs_decode_plan(a)
     assert kvs.kvs_decode_workspace_bytes(a) == 0
+
+
+def test_query_row_checks(lib):
+    """Several queries per request: offsets from 0, non-decreasing, at most
+    kv_len new tokens each; the matrix-core kernel only."""
+    def with_rows(rows, **kw):
+        a, keep = _args(**kw)
+        qo = np.asarray(rows, np.int32)
+        a.qo_indptr, a.qo_indptr_host = 0x2000, qo.ctypes.data
+        return a, (keep, qo)
+    a, keep = with_rows([0, 3, 10])                     # lens (100, 3000): fine
+    assert kvs.kvs_decode_plan(a).col_groups == (7 * 4 + 15) // 16
+    for rows in ([1, 3, 10], [0, 5, 4], [0, 101, 200]):  # start, decrease, more than kv_len
+        a, keep = with_rows(rows)
+        assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG, rows
+    a, keep = with_rows([0, 3, 10], algo=kvs.KVS_ALGO_VALU)
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_UNSUPPORTED
+    a, keep = with_rows([0, 3, 10], algo=kvs.KVS_ALGO_MFMA_PACKED)
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_UNSUPPORTED
+    a, keep = _args()
+    a.qo_indptr = 0x2000                                # device offsets without the host copy
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG
 
 
 def test_unified_max_checks(lib):

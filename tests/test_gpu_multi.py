@@ -1,0 +1,98 @@
+"""Several new query tokens per request (append / prefill attention) on the
+GPU against the fp64 oracle: query row i of a request with n new tokens sits
+at position kv_len - n + i and sees the keys up to it (the last W with a
+window).  Tolerances as for decode (by KV type)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from kvs_testlib import compare, run_library
+from workloads import CONFIGS, DecodeSpec, make_inputs, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kvs.load_library()
+
+
+def _check(inp, **kw):
+    o, lse = run_library(inp, **kw)
+    o_ref, lse_ref = oracle.attention_reference(inp)
+    return compare(o, lse, o_ref, lse_ref, inp.spec.kv_dtype)
+
+
+@pytest.mark.parametrize("chunk", [0, 16, 64])
+def test_append_rows_paged_bf16(chunk):
+    """1, 2, 4 and 5 new tokens with 4 query heads per KV head: 4 to 20
+    columns, so one or two column groups."""
+    print(f"case multi bf16 chunk={chunk}", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=4, lengths=("list", [20, 300, 1000, 2049]),
+                         q_len=("list", [1, 2, 4, 5]))
+    _check(make_inputs(spec, poison=True), kv_chunk=chunk)
+
+
+@pytest.mark.parametrize("name", ["c5_paged_fp8_b128", "c6_paged_int4_b128"])
+def test_append_rows_quantised(name):
+    print(f"case multi {name}", flush=True)
+    spec = small_variant(name, batch=4, lengths=("list", [3, 64, 700, 1500]), q_len=("list", [3, 0, 7, 1]))
+    _check(make_inputs(spec, poison=True))
+
+
+def test_whole_request_prefill_and_empty_rows():
+    """A request whose every token is new (n = kv_len), one with none, one
+    with a single token."""
+    print("case multi prefill mix", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=3, lengths=("list", [37, 500, 16]), q_len=("list", [37, 0, 1]))
+    _check(make_inputs(spec, poison=True), kv_chunk=16)
+
+
+@pytest.mark.parametrize("window", [-1, 1, 16, 100])
+def test_contiguous_prefill_mha(window):
+    """Llama-shaped MHA (g = 1): 300 new rows are 300 columns per KV head,
+    19 column groups; causal, with and without a window."""
+    print(f"case multi prefill window={window}", flush=True)
+    spec = dataclasses.replace(small_variant("c3_llama2_7b_32k", lengths=("fixed", 300), q_len=("fixed", 300)),
+                               window=window)
+    _check(make_inputs(spec))
+
+
+def test_gemma_shaped_prefill_with_window():
+    print("case multi gemma prefill", flush=True)
+    spec = dataclasses.replace(small_variant("c2_gemma3_1b", lengths=("fixed", 200), q_len=("fixed", 64)),
+                               window=32)
+    _check(make_inputs(spec))
+
+
+@pytest.mark.parametrize("g", [1, 2, 8, 16])
+def test_group_sizes(g):
+    print(f"case multi g={g}", flush=True)
+    spec = DecodeSpec("multi", 3, 2 * g, 2, 128, 16, "bf16", "bf16", 128 ** -0.5,
+                      lengths=("list", [40, 333, 900]), q_len=("list", [5, 1, 9]), seed=31 + g)
+    _check(make_inputs(spec, poison=True))
+
+
+def test_unified_max_with_rows():
+    print("case multi unified max", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=3, lengths=("list", [40, 333, 900]), q_len=("list", [5, 1, 9]))
+    _check(make_inputs(spec, poison=True), unified_max=200.0)
+
+
+def test_speculative_append_full_batch_sampled():
+    """The batch-64 paged workload with 4 new tokens per request, in the
+    launch configuration of a full batch; six requests' rows against the oracle."""
+    print("case multi full c4 q_len 4", flush=True)
+    spec = dataclasses.replace(CONFIGS["c4_paged_bf16_b64"], q_len=("fixed", 4))
+    inp = make_inputs(spec)
+    o, lse = run_library(inp)
+    reqs = [0, 1, 17, 33, int(np.argmax(inp.kv_len)), 63]
+    o_ref, lse_ref = oracle.attention_reference(inp, requests=reqs)
+    rows = np.concatenate([np.arange(inp.qo_indptr[b], inp.qo_indptr[b + 1]) for b in reqs])
+    compare(o[rows], lse[rows], o_ref[rows], lse_ref[rows], "bf16")
