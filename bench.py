@@ -73,22 +73,40 @@ def measured_traffic(config_name: str, kernel: str):
     return rec["bytes"]
 
 
+def query_rows(inp) -> np.ndarray:
+    """New query tokens of each request (1 each for decode)."""
+    if inp.qo_indptr is None:
+        return np.ones(inp.spec.batch, np.int64)
+    return np.diff(np.asarray(inp.qo_indptr, np.int64))
+
+
+def visible_lo(inp) -> np.ndarray:
+    """First key any query row of each request sees."""
+    s = inp.spec
+    L = inp.kv_len.astype(np.int64)
+    first_q = L - query_rows(inp)  # position of the first new row
+    return np.maximum(0, first_q + 1 - s.window) if s.window > 0 else np.zeros_like(L)
+
+
 def algorithmic_bytes(inp) -> int:
-    """Bytes the method must move once: K and V of every visible (token, KV
-    head), q, o, lse, kv_len, the page-table entries it reads and the fp8
-    scales."""
+    """Bytes the method must move once: K and V of every (token, KV head)
+    some query row sees (once, however many rows see it), q, o, lse of every
+    row, kv_len, the page-table entries it reads and the quantisation
+    scales (and qo_indptr with several rows per request)."""
     s = inp.spec
     b_kv, b_q = _BYTES[s.kv_dtype], _BYTES[s.q_dtype]
     L = inp.kv_len.astype(np.int64)
-    lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
-    vis = int(np.sum(L - lo))
+    nq = query_rows(inp)
+    lo = np.minimum(visible_lo(inp), L)
+    vis = int(np.sum(np.where(nq > 0, L - lo, 0)))
+    rows = int(nq.sum())
     kv = int(2 * vis * s.num_kv_heads * s.head_dim * b_kv)
-    qo = 2 * s.batch * s.num_qo_heads * s.head_dim * b_q + 4 * s.batch * s.num_qo_heads
-    meta = 4 * s.batch
+    qo = 2 * rows * s.num_qo_heads * s.head_dim * b_q + 4 * rows * s.num_qo_heads
+    meta = 4 * s.batch + (4 * (s.batch + 1) if inp.qo_indptr is not None else 0)
     if s.page_size:
         first = lo // s.page_size
         last = (L + s.page_size - 1) // s.page_size
-        meta += 4 * (s.batch + 1) + 4 * int(np.sum(np.maximum(0, last - first)))
+        meta += 4 * (s.batch + 1) + 4 * int(np.sum(np.where(nq > 0, np.maximum(0, last - first), 0)))
     if s.kv_dtype in ("fp8", "int4"):
         meta += 2 * 4 * s.batch * s.num_kv_heads
     return kv + qo + meta
@@ -184,15 +202,20 @@ def cpu_baseline(inp, budget_s: float = 12.0):
         threads = os.cpu_count() or 1
     s = inp.spec
     L = inp.kv_len.astype(np.int64)
-    lo = np.maximum(0, L - s.window) if s.window > 0 else np.zeros_like(L)
-    vis_all = max(1, int(np.sum(L - lo)))
+    nq = query_rows(inp)
+    lo = np.minimum(visible_lo(inp), L)
+    seen = np.where(nq > 0, L - lo, 0)
+    vis_all = max(1, int(np.sum(seen)))
     vis = 0
     n_req = 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b = n_req % s.batch
-        oracle.decode_reference(inp, requests=[b])
-        vis += int(L[b] - lo[b])
+        if inp.qo_indptr is None:
+            oracle.decode_reference(inp, requests=[b])
+        else:
+            oracle.attention_reference(inp, requests=[b])
+        vis += int(seen[b])
         n_req += 1
     dt = time.perf_counter() - t0
     frac_bytes = algorithmic_bytes(inp) * (vis / vis_all)
@@ -234,7 +257,10 @@ def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
 
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
-        with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None) -> dict:
+        with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
+        q_len: int = 1) -> dict:
+    import dataclasses
+
     import torch
 
     import decode_attention_kv_split_amd as kvs
@@ -245,6 +271,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
 
     kvs.load_library()
     spec = CONFIGS[config_name]
+    if q_len != 1:
+        spec = dataclasses.replace(spec, q_len=("fixed", q_len))
     t_gen = time.perf_counter()
     inp = make_inputs(spec)
     t = to_torch(inp)
@@ -254,7 +282,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
                             page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                             k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
                             window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max,
-                            kv_dtype="int4" if s.kv_dtype == "int4" else None)
+                            kv_dtype="int4" if s.kv_dtype == "int4" else None,
+                            qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr)
     plan = kvs.kvs_decode_plan(a)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -315,7 +344,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
             "max_splits": plan.max_splits, "parallelism": "single GPU",
-            "unified_max": unified_max,
+            "unified_max": unified_max, "q_len": q_len,
         },
         "roofline": {
             "bound": "hbm",
@@ -324,7 +353,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(config_name, kernel),
+            "traffic": measured_traffic(config_name, kernel) if q_len == 1 else None,
             "kernel_us": round(part_avg * 1e3, 2),
             "kernel_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
             "kernel_launches_timed": len(stamped),
@@ -481,6 +510,9 @@ def main():
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--unified-max", type=float, default=None,
                     help="start every chunk's softmax from this reference max (scaled-score units)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new query tokens per request (1: decode; more: append / speculative-verify attention, "
+                         "each row causal over the cache)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-events", action="store_true",
                     help="no per-launch kernel timing (the event stamps add host time per call, which "
@@ -504,7 +536,7 @@ def main():
         print(json.dumps(res), flush=True)
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
-              events=not args.no_events, cold=args.cold, unified_max=args.unified_max)
+              events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len)
     print(json.dumps(res), flush=True)
 
 

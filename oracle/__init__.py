@@ -16,7 +16,7 @@ from .append import (append_codes, append_reference, apply_append, cache_slot, r
 from .codecs import (bf16_to_f64, decode_codes, encode_codes, f64_to_bf16_codes, f64_to_fp8_e4m3fn_codes,
                      fp8_e4m3fn_to_f64, int4_to_f64, round_to_grid)
 from .multi import attention_reference, query_position, query_range
-from .decode import (attend_chunked, attend_direct, chunk_state, decode_reference,
+from .decode import (attend_chunked, attend_direct, cap_scores, chunk_state, decode_reference,
                      decode_reference_chunked, decode_reference_sampled, kv_head_of,
                      merge_states, request_kv, softmax_from_scores, visible_range)
 
@@ -25,7 +25,7 @@ __all__ = [
     "f64_to_fp8_e4m3fn_codes", "round_to_grid",
     "rms_norm", "rope", "rope_angles", "transform_head", "append_reference", "append_codes",
     "apply_append", "cache_slot",
-    "attend_direct", "attend_chunked", "chunk_state", "merge_states", "softmax_from_scores",
+    "attend_direct", "attend_chunked", "cap_scores", "chunk_state", "merge_states", "softmax_from_scores",
     "decode_reference", "decode_reference_chunked", "decode_reference_sampled",
     "kv_head_of", "visible_range", "request_kv",
     "attention_reference", "query_position", "query_range",

@@ -8,7 +8,8 @@ What is computed (for request b, query head h, kv head h // g):
 
 * the visible keys J_b = { t : lo_b <= t <= L_b - 1 }, lo_b = max(0, L_b - W)
   for a window W > 0, else 0;
-* scores s_t = sm_scale * <q[b, h], K[b, t, h // g]>;
+* scores s_t = sm_scale * <q[b, h], K[b, t, h // g]>, soft-capped to
+  c * tanh(s_t / c) when a cap c > 0 is given;
 * lse = m + ln sum_t exp(s_t - m), m = max_t s_t (natural log, of the scaled
   scores);
 * o = sum_t exp(s_t - lse) V[b, t, h // g];
@@ -31,6 +32,12 @@ Sources (cited by page and section):
 * sliding (local) window -- the FlashInfer-from-JAX page, Gemma 3 section
   (local vs global attention layers); "Flashlight" explainer (gist.science),
   results (sliding-window variant).
+* logit soft-capping -- named, without a formula, by the FlashInfer-from-JAX
+  page (Gemma 3 section: QK-norm takes the place of Gemma 2's soft-capping)
+  and by the "Flashlight" explainer (results: Softcap among the score_mod
+  variants).  The reading is Gemma 2's published definition, applied to the
+  scaled score: s -> c * tanh(s / c), which keeps every score inside
+  (-c, c) and leaves small scores almost unchanged.
 
 Two independent forms:
 
@@ -60,6 +67,7 @@ from .codecs import decode_codes
 
 __all__ = [
     "kv_head_of",
+    "cap_scores",
     "visible_range",
     "softmax_from_scores",
     "attend_direct",
@@ -108,9 +116,19 @@ def softmax_from_scores(scores: np.ndarray, values: np.ndarray) -> Tuple[np.ndar
     return o, lse
 
 
-def attend_direct(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) -> Tuple[np.ndarray, float]:
+def cap_scores(scores: np.ndarray, soft_cap: float) -> np.ndarray:
+    """Logit soft-capping: c * tanh(s / c) for a cap c > 0; unchanged for
+    c = 0 (no cap)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    if soft_cap and soft_cap > 0:
+        return soft_cap * np.tanh(scores / soft_cap)
+    return scores
+
+
+def attend_direct(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
+                  soft_cap: float = 0.0) -> Tuple[np.ndarray, float]:
     """One query row q [d] against visible keys K [n, d] and values V [n, d]."""
-    scores = sm_scale * (np.asarray(K, np.float64) @ np.asarray(q, np.float64))
+    scores = cap_scores(sm_scale * (np.asarray(K, np.float64) @ np.asarray(q, np.float64)), soft_cap)
     return softmax_from_scores(scores, V)
 
 
@@ -119,7 +137,7 @@ def attend_direct(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float) 
 # ----------------------------------------------------------------------------
 
 def chunk_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
-                tile: int = 16) -> Tuple[float, float, np.ndarray]:
+                tile: int = 16, soft_cap: float = 0.0) -> Tuple[float, float, np.ndarray]:
     """Running (max, sum, acc) after streaming K/V tiles of one chunk."""
     d = V.shape[1]
     running_max = -math.inf
@@ -128,7 +146,7 @@ def chunk_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
     for t0 in range(0, K.shape[0], tile):
         k_tile = np.asarray(K[t0:t0 + tile], np.float64)
         v_tile = np.asarray(V[t0:t0 + tile], np.float64)
-        scores = sm_scale * (k_tile @ np.asarray(q, np.float64))
+        scores = cap_scores(sm_scale * (k_tile @ np.asarray(q, np.float64)), soft_cap)
         new_max = max(running_max, float(np.max(scores))) if scores.size else running_max
         rescale = math.exp(running_max - new_max) if math.isfinite(running_max) else 0.0
         weights = np.exp(scores - new_max) if math.isfinite(new_max) else np.zeros_like(scores)
@@ -168,7 +186,7 @@ def _chunk_to_lse_o(state: Tuple[float, float, np.ndarray]) -> Tuple[float, np.n
 
 
 def attend_chunked(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
-                   chunk_sizes: Sequence[int], tile: int = 16) -> Tuple[np.ndarray, float]:
+                   chunk_sizes: Sequence[int], tile: int = 16, soft_cap: float = 0.0) -> Tuple[np.ndarray, float]:
     """O2 over consecutive chunks whose sizes sum to len(K)."""
     n = K.shape[0]
     if sum(chunk_sizes) != n:
@@ -178,7 +196,7 @@ def attend_chunked(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
     states = []
     t0 = 0
     for c in chunk_sizes:
-        states.append(_chunk_to_lse_o(chunk_state(q, K[t0:t0 + c], V[t0:t0 + c], sm_scale, tile)))
+        states.append(_chunk_to_lse_o(chunk_state(q, K[t0:t0 + c], V[t0:t0 + c], sm_scale, tile, soft_cap)))
         t0 += c
     return merge_states(states)
 
@@ -245,10 +263,11 @@ def decode_reference(inp, *, form: str = "direct",
         for h in range(Hq):
             kh = kv_head_of(h, g)
             if form == "direct":
-                o[b, h], lse[b, h] = attend_direct(Q[b, h], K[:, kh], V[:, kh], s.sm_scale)
+                o[b, h], lse[b, h] = attend_direct(Q[b, h], K[:, kh], V[:, kh], s.sm_scale, s.soft_cap)
             elif form == "chunked":
                 sizes = chunker(n) if chunker is not None else [n]
-                o[b, h], lse[b, h] = attend_chunked(Q[b, h], K[:, kh], V[:, kh], s.sm_scale, sizes)
+                o[b, h], lse[b, h] = attend_chunked(Q[b, h], K[:, kh], V[:, kh], s.sm_scale, sizes,
+                                                    soft_cap=s.soft_cap)
             else:
                 raise ValueError(form)
     return o, lse
@@ -272,5 +291,5 @@ def decode_reference_sampled(inp, picks: Sequence[Tuple[int, int]]) -> List[Tupl
             cache = {b: request_kv(b, tokens=(lo, hi), **f)}
         K, V = cache[b]
         kh = kv_head_of(h, g)
-        out.append(attend_direct(Q[b, h], K[:, kh], V[:, kh], s.sm_scale))
+        out.append(attend_direct(Q[b, h], K[:, kh], V[:, kh], s.sm_scale, s.soft_cap))
     return out

@@ -59,5 +59,5 @@ def attention_reference(inp, requests: Optional[Sequence[int]] = None) -> Tuple[
             r = int(indptr[b]) + i
             for h in range(Hq):
                 kh = kv_head_of(h, g)
-                o[r, h], lse[r, h] = attend_direct(Q[r, h], K[lo:hi, kh], V[lo:hi, kh], s.sm_scale)
+                o[r, h], lse[r, h] = attend_direct(Q[r, h], K[lo:hi, kh], V[lo:hi, kh], s.sm_scale, s.soft_cap)
     return o, lse

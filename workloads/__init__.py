@@ -82,6 +82,8 @@ class DecodeSpec:
     # new query tokens per request: ("fixed", n) | ("list", [n_b...]) | ("uniform", lo, hi);
     # each is capped at the request's kv_len (its tokens are already cached)
     q_len: tuple = ("fixed", 1)
+    # logit soft-cap c (scores become c * tanh(s / c)); 0 = none
+    soft_cap: float = 0.0
 
     @property
     def group(self) -> int:
