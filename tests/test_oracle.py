@@ -430,7 +430,7 @@ def test_planted_window_off_by_one_is_caught(monkeypatch):
 def test_planted_rescale_sign_is_caught(monkeypatch):
     real = od.chunk_state
 
-    def wrong(q, K, V, sm, tile=16):
+    def wrong(q, K, V, sm, tile=16, soft_cap=0.0):
         d = V.shape[1]
         m, l, acc = -math.inf, 0.0, np.zeros(d)
         for t0 in range(0, K.shape[0], tile):
@@ -450,7 +450,7 @@ def test_planted_rescale_sign_is_caught(monkeypatch):
 
 def test_planted_dropped_scale_is_caught(monkeypatch):
     real = od.attend_direct
-    monkeypatch.setattr(od, "attend_direct", lambda q, K, V, sm: real(q, K, V, 1.0))
+    monkeypatch.setattr(od, "attend_direct", lambda q, K, V, sm, soft_cap=0.0: real(q, K, V, 1.0, soft_cap))
     monkeypatch.setattr(oracle, "attend_direct", od.attend_direct)
     assert _fails(test_bruteforce_decimal, 1)
 
