@@ -258,7 +258,7 @@ def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
-        q_len: int = 1) -> dict:
+        q_len: int = 1, soft_cap: float = 0.0) -> dict:
     import dataclasses
 
     import torch
@@ -273,6 +273,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     spec = CONFIGS[config_name]
     if q_len != 1:
         spec = dataclasses.replace(spec, q_len=("fixed", q_len))
+    if soft_cap:
+        spec = dataclasses.replace(spec, soft_cap=soft_cap)
     t_gen = time.perf_counter()
     inp = make_inputs(spec)
     t = to_torch(inp)
@@ -283,7 +285,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
                             k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,
                             window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max,
                             kv_dtype="int4" if s.kv_dtype == "int4" else None,
-                            qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr)
+                            qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr,
+                            logits_soft_cap=spec.soft_cap)
     plan = kvs.kvs_decode_plan(a)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -344,7 +347,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
             "max_splits": plan.max_splits, "parallelism": "single GPU",
-            "unified_max": unified_max, "q_len": q_len,
+            "unified_max": unified_max, "q_len": q_len, "soft_cap": spec.soft_cap,
         },
         "roofline": {
             "bound": "hbm",
@@ -353,7 +356,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(config_name, kernel) if q_len == 1 else None,
+            "traffic": measured_traffic(config_name, kernel) if q_len == 1 and not soft_cap else None,
             "kernel_us": round(part_avg * 1e3, 2),
             "kernel_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
             "kernel_launches_timed": len(stamped),
@@ -513,6 +516,8 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="new query tokens per request (1: decode; more: append / speculative-verify attention, "
                          "each row causal over the cache)")
+    ap.add_argument("--soft-cap", type=float, default=0.0,
+                    help="logit soft-cap c: scores become c * tanh(s / c) (0: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-events", action="store_true",
                     help="no per-launch kernel timing (the event stamps add host time per call, which "
@@ -536,7 +541,8 @@ def main():
         print(json.dumps(res), flush=True)
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
-              events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len)
+              events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
+              soft_cap=args.soft_cap)
     print(json.dumps(res), flush=True)
 
 

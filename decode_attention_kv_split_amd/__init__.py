@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 5
+KVS_ABI_VERSION = 6
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
@@ -82,6 +82,7 @@ class KvsDecodeArgs(ctypes.Structure):
         ("unified_max", ctypes.c_float),
         ("qo_indptr", ctypes.c_void_p),
         ("qo_indptr_host", ctypes.c_void_p),
+        ("logits_soft_cap", ctypes.c_float),
     ]
 
 
@@ -273,7 +274,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
               k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
               algo="auto", out=None, lse=None, num_cus: int = 0,
               unified_max: Optional[float] = None, kv_dtype: Optional[str] = None, qo_indptr=None,
-              qo_indptr_host=None) -> Tuple[KvsDecodeArgs, object]:
+              qo_indptr_host=None, logits_soft_cap: float = 0.0) -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
@@ -281,6 +282,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     kv_dtype='int4' marks uint8 caches whose last axis holds d / 2 bytes of
     packed nibbles.  qo_indptr (int32 [batch + 1] on the device, with a host
     copy) gives several query rows per request: q is then [total_q, Hq, d].
+    logits_soft_cap c > 0 caps the scaled scores to c * tanh(s / c).
     Returns (args, keepalive)."""
     import numpy as np
     import torch
@@ -353,6 +355,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
         a.use_unified_max, a.unified_max = 1, float(unified_max)
     if qoh is not None:
         a.qo_indptr, a.qo_indptr_host = _ptr(qo_indptr), qoh.ctypes.data
+    a.logits_soft_cap = float(logits_soft_cap)
     keep = (kvh, out, lse, qoh)
     return a, keep
 
@@ -360,7 +363,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
            workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None,
-           qo_indptr=None, qo_indptr_host=None):
+           qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
@@ -368,7 +371,8 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
     a, keep = make_args(q, k, v, kv_len, page_indptr=page_indptr, page_indices=page_indices,
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
                         window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
-                        kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host)
+                        kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host,
+                        logits_soft_cap=logits_soft_cap)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

@@ -61,6 +61,7 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (!a->kv_len_host) return KVS_ERR_INVALID_ARG;
   if (a->use_unified_max != 0 && a->use_unified_max != 1) return KVS_ERR_INVALID_ARG;
   if (a->use_unified_max && !std::isfinite(a->unified_max)) return KVS_ERR_INVALID_ARG;
+  if (!(a->logits_soft_cap >= 0.0f) || !std::isfinite(a->logits_soft_cap)) return KVS_ERR_INVALID_ARG;
   for (int b = 0; b < a->batch; ++b) {
     const int L = a->kv_len_host[b];
     if (L < 0) return KVS_ERR_INVALID_ARG;
@@ -266,7 +267,10 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.chunk = pl.chunk;
   p.items = pl.items;
   p.out_bf16 = a->q_dtype == KVS_BF16 ? 1 : 0;
-  p.score_scale = a->sm_scale * kvs::kLog2e;
+  // with a soft cap c the kernels form tanh(sm_scale / c * qk) * c * log2(e)
+  const bool capped = a->logits_soft_cap > 0.0f;
+  p.score_scale = capped ? a->sm_scale / a->logits_soft_cap : a->sm_scale * kvs::kLog2e;
+  p.cap_out = capped ? a->logits_soft_cap * kvs::kLog2e : 0.0f;
   p.m_init = a->use_unified_max ? a->unified_max * kvs::kLog2e : -INFINITY;
 
   // host-planned work lists, passed inline when they fit

@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
   float cscale = p.score_scale;
   if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
+  const float cap_out = p.cap_out;
   // INT4: the scores carry 136 * (sum of this head's q over the pack dims)
   float qoff = 0.0f;
   if constexpr (KT == DT_INT4) {
@@ -483,14 +484,17 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       for (int r = 0; r < 4; ++r) s[r] -= qoff; // remove the 136-per-element offset of K
     }
     float sv[4];
-    if (ts >= all_lo && ts + kTile <= all_hi) { // every column sees every key of the tile (uniform branch)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
-    } else {
+    for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+    if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
+    }
+    if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = ts + 4 * q4 + r;
-        sv[r] = (tok >= lane_lo && tok < lane_hi) ? s[r] * cscale : -INFINITY;
+        if (tok < lane_lo || tok >= lane_hi) sv[r] = -INFINITY;
       }
     }
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));

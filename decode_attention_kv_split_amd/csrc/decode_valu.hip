@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
         for (int e = 0; e < EPL; ++e) s = fmaf(qv[h][e], kf[e], s);
 #pragma unroll
         for (int off = 1; off < RL; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (p.cap_out > 0.0f) s = tanhf(s) * p.cap_out; // logit soft-cap, log2 units
         if (valid) {
           const float m_new = fmaxf(m_run[h], s);
           const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);

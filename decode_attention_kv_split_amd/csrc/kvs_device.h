@@ -86,7 +86,8 @@ struct Params {
   int cols;       // columns per partial slot: group * pack (one query) or 16
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
-  float score_scale; // sm_scale * log2(e)
+  float score_scale; // sm_scale * log2(e); with a soft cap c: sm_scale / c
+  float cap_out;     // soft cap: scores become tanh(score_scale * qk) * cap_out, cap_out = c * log2(e); 0: no cap
 };
 
 // Work lists planned on the host from kv_len_host and passed in the kernel

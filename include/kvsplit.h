@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 5
+#define KVS_ABI_VERSION 6
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -158,6 +158,16 @@ typedef struct {
    * bandwidth-heavy for long prefill. */
   const int32_t *qo_indptr;      /* device [batch + 1] */
   const int32_t *qo_indptr_host; /* host copy (plans the launch); must equal qo_indptr */
+
+  /* optional logit soft-capping, a score transform the FlashInfer-from-JAX
+   * page (Gemma 3 section: what QK-norm replaced) and the "Flashlight"
+   * explainer (results: the Softcap variant) name without a formula; the
+   * reading is Gemma 2's definition on the scaled score:
+   * s -> c * tanh(s / c), for c = logits_soft_cap > 0 (finite).  0: none.
+   * Scores then stay inside (-c, c); lse is that of the capped scores.  Both
+   * kernels; combines with windows, several query rows and the unified max
+   * (give unified_max in capped units, at most c). */
+  float logits_soft_cap;
 } kvs_decode_args;
 
 /* What a call will launch, computed on the host from kv_len_host. */

@@ -67,6 +67,7 @@ def run_library(inp, tensors=None, **kw):
 
     s = inp.spec
     t = tensors if tensors is not None else to_torch(inp)
+    kw.setdefault("logits_soft_cap", s.soft_cap)
     o, lse = kvs.decode(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                         page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                         k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=s.sm_scale,

@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 5
-    assert re.search(r"#define KVS_ABI_VERSION 5\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 6
+    assert re.search(r"#define KVS_ABI_VERSION 6\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -161,6 +161,17 @@ def test_unified_max_checks(lib):
     a, keep = _args(ptrs=False)
     a.use_unified_max, a.unified_max = 1, 5.0
     assert kvs.kvs_decode_plan(a).items_per_kv_head >= 1
+
+
+def test_soft_cap_checks(lib):
+    for bad in (-1.0, float("nan"), float("inf"), -0.5e-30):
+        a, keep = _args()
+        a.logits_soft_cap = bad
+        assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG, bad
+    for algo in (kvs.KVS_ALGO_AUTO, kvs.KVS_ALGO_VALU):
+        a, keep = _args(ptrs=False, algo=algo)
+        a.logits_soft_cap = 50.0
+        assert kvs.kvs_decode_plan(a).items_per_kv_head >= 1
 
 
 def test_null_pointers_rejected(lib):
