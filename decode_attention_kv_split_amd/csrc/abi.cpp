@@ -18,6 +18,7 @@ hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_di
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack);
+int mfma_col_share(int head_dim, int col_groups);
 bool mfma_head_dim_ok(int head_dim, int kv_type);
 hipError_t launch_append(const kvs_append_args *a, const Launch &l);
 } // namespace kvs
@@ -159,7 +160,9 @@ kvs_status resolve_cus(const kvs_decode_args *a, int *cus) {
 struct Columns {
   std::vector<int32_t> nq;
   int col_groups = 1;
-  int cols = 0; // partial-result columns per KV head over all groups
+  int col_share = 1;  // groups per partial workgroup
+  int col_blocks = 1; // partial workgroups per (item, KV head) along the columns
+  int cols = 0;       // partial-result columns per KV head over all groups
 };
 
 Columns columns_of(const kvs_decode_args *a) {
@@ -174,6 +177,8 @@ Columns columns_of(const kvs_decode_args *a) {
     most = std::max(most, c.nq[b]);
   }
   c.col_groups = std::max(1, (int)(((int64_t)most * group + 15) / 16));
+  c.col_share = kvs::mfma_col_share(a->head_dim, c.col_groups);
+  c.col_blocks = (c.col_groups + c.col_share - 1) / c.col_share;
   c.cols = c.col_groups * 16;
   return c;
 }
@@ -186,9 +191,10 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   if (st != KVS_OK) return st;
   Columns c = columns_of(a);
   if (!kvs::make_plan(a->kv_len_host, c.nq.empty() ? nullptr : c.nq.data(), a->batch, a->window,
-                      a->num_kv_heads, c.cols, c.col_groups, a->head_dim, a->kv_chunk, *cus, pl))
+                      a->num_kv_heads, c.cols, c.col_blocks, a->head_dim, a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
+  // (the merge runs one workgroup per column group)
   if ((int64_t)pl->items * a->num_kv_heads * c.col_groups > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
   if (cols_out) *cols_out = std::move(c);
   return KVS_OK;
@@ -260,6 +266,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
                                                   algo == KVS_ALGO_MFMA_PACKED);
   p.qo_indptr = a->qo_indptr_host ? a->qo_indptr : nullptr;
   p.col_groups = cols.col_groups;
+  p.col_share = cols.col_share;
   p.cols = a->qo_indptr_host ? 16 : p.group * p.pack;
   p.page_size = a->page_size;
   p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;

@@ -230,8 +230,13 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, KT> &t, int j) 
   }
 }
 
-template <int D, int PACK, int KT, int NBUF>
+// CG: column groups (16 columns each) a wave computes on every staged tile;
+// more than one only with several query rows per request and one KV head per
+// workgroup.  The groups share the K operand and the V^T products, so K/V
+// are read once for all of them.
+template <int D, int PACK, int KT, int NBUF, int CG>
 __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, const InlineWork w) {
+  static_assert(CG == 1 || PACK == 1, "column groups of (query row, head) pairs take one KV head");
   constexpr int DE = D * PACK;
   using S = Shape<DE, KT>;
   constexpr int OSTRIDE = D + 4;
@@ -256,8 +261,9 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // pages spread over the pool, which streamed faster on MI355X than grids
   // that run all heads of an item together (on one XCD or spread over XCDs).
   const int item = blockIdx.x;
-  const int kvg = blockIdx.y / p.col_groups; // KV heads kvg*PACK .. kvg*PACK+PACK-1
-  const int cg = blockIdx.y % p.col_groups;  // column group (several queries per request)
+  const int col_blocks = (p.col_groups + CG - 1) / CG; // workgroups per (item, KV head pack)
+  const int kvg = blockIdx.y / col_blocks;             // KV heads kvg*PACK .. kvg*PACK+PACK-1
+  const int cg0 = blockIdx.y % col_blocks * CG;        // first column group (several queries per request)
   const int g = p.group;
   const int gp = g * PACK;    // query heads of the pack (<= 16)
   const int Hk = p.num_kv_heads;
@@ -297,37 +303,45 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 
   // ---- columns: query heads of the pack, or (query row, head) pairs ----
   const int nq = req_nq(p, b);
-  if (p.qo_indptr && cg * 16 >= nq * g) return; // this column group is empty for the request
-  int qrow;   // row of q / o of this lane's column
-  int qhead;  // query head of this lane's column
-  bool col_ok;
-  int qi;     // query index within the request (0 with one query)
-  if (!p.qo_indptr) {
-    col_ok = c16 < gp;
-    qi = 0;
-    qrow = b;
-    qhead = kvg * gp + c16;
-  } else {
-    const int col = cg * 16 + c16;
-    col_ok = col < nq * g;
-    qi = col / g;
-    qrow = p.qo_indptr[b] + qi;
-    qhead = kvg * g + col % g;
-  }
-  // keys this column sees: up to its query's position, the last `window` of them
-  const int qpos = L - nq + qi;
-  const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
-  const int col_hi = qpos + 1;
-
+  if (p.qo_indptr && cg0 * 16 >= nq * g) return; // no column of this workgroup has a query row
   const int lo = request_lo(L, nq, p.window);
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
   const int t_begin = max(lo, a0);
   const int t_end = min(L, a0 + p.chunk);
   const int ntiles = t_end > t_begin ? (t_end - a0 + kTile - 1) / kTile : 0;
-  // per-column visible range within the chunk, and the range every column sees
-  const int lane_lo = max(t_begin, col_lo);
-  const int lane_hi = min(t_end, col_hi);
-  int all_lo = col_ok ? lane_lo : t_begin, all_hi = col_ok ? lane_hi : t_end;
+  int qrow[CG];       // row of q / o of this lane's column, per group
+  int qhead[CG];      // query head of this lane's column, per group
+  bool col_ok[CG];    // the column holds a (query, head) of the request
+  bool grp_on[CG];    // the group holds any (the same in every lane)
+  int lane_lo[CG], lane_hi[CG]; // keys of the chunk this lane's column sees
+  int all_lo = t_begin, all_hi = t_end; // keys every column of every group sees
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    int qi; // query index within the request (0 with one query)
+    if (!p.qo_indptr) {
+      col_ok[c] = c16 < gp;
+      grp_on[c] = true;
+      qi = 0;
+      qrow[c] = b;
+      qhead[c] = kvg * gp + c16;
+    } else {
+      const int col = (cg0 + c) * 16 + c16;
+      col_ok[c] = col < nq * g;
+      grp_on[c] = (cg0 + c) * 16 < nq * g;
+      qi = col / g;
+      qrow[c] = p.qo_indptr[b] + qi;
+      qhead[c] = kvg * g + col % g;
+    }
+    // keys this column sees: up to its query's position, the last `window` of them
+    const int qpos = L - nq + qi;
+    const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
+    lane_lo[c] = max(t_begin, col_lo);
+    lane_hi[c] = min(t_end, qpos + 1);
+    if (col_ok[c]) {
+      all_lo = max(all_lo, lane_lo[c]);
+      all_hi = min(all_hi, lane_hi[c]);
+    }
+  }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
     all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
@@ -338,18 +352,19 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // ---- Q^T operand: block diagonal over the pack, zero columns past gp ----
-  bf16x8_t qop[S::kKSteps];
-  {
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
+  bf16x8_t qop[CG][S::kKSteps];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow[c] * p.num_qo_heads + qhead[c]) * D;
 #pragma unroll
     for (int j = 0; j < S::kKSteps; ++j) {
       const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
-      if (col_ok && kd / D == my_kv) {
+      if (col_ok[c] && kd / D == my_kv) {
         bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
         if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
-        qop[j] = x;
+        qop[c][j] = x;
       } else {
-        qop[j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+        qop[c][j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
       }
     }
   }
@@ -357,15 +372,19 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
   const float cap_out = p.cap_out;
   // INT4: the scores carry 136 * (sum of this head's q over the pack dims)
-  float qoff = 0.0f;
-  if constexpr (KT == DT_INT4) {
+  float qoff[CG];
 #pragma unroll
-    for (int j = 0; j < S::kKSteps; ++j)
+  for (int c = 0; c < CG; ++c) {
+    qoff[c] = 0.0f;
+    if constexpr (KT == DT_INT4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qoff += (float)qop[j][e];
-    qoff += __shfl_xor(qoff, 16, 64);
-    qoff += __shfl_xor(qoff, 32, 64);
-    qoff *= kInt4Offset;
+      for (int j = 0; j < S::kKSteps; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qoff[c] += (float)qop[c][j][e];
+      qoff[c] += __shfl_xor(qoff[c], 16, 64);
+      qoff[c] += __shfl_xor(qoff[c], 32, 64);
+      qoff[c] *= kInt4Offset;
+    }
   }
 
   // identity / selection operands of the V transposition
@@ -459,12 +478,19 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   };
 
   // ---- running state ----
-  float m_run = p.m_init;  // reference max, log2 domain, per query head c16 (same in the 4 quarters)
-  float l_run = 0.0f;      // partial sum over this lane's tokens
-  float lb_run = 0.0f;     // INT4: the same sum of the bf16-rounded weights the P.V product sees
-  f32x4_t oacc[S::kOTiles];
+  // per column group c:
+  float m_run[CG];  // reference max, log2 domain, per column c16 (same in the 4 quarters)
+  float l_run[CG];  // partial sum over this lane's tokens
+  float lb_run[CG]; // INT4: the same sum of the bf16-rounded weights the P.V product sees
+  f32x4_t oacc[CG][S::kOTiles];
 #pragma unroll
-  for (int w = 0; w < S::kOTiles; ++w) oacc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CG; ++c) {
+    m_run[c] = p.m_init;
+    l_run[c] = 0.0f;
+    lb_run[c] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) oacc[c][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (wave + i * kWaves) * kTile;
@@ -474,63 +500,68 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       for (int k = 0; k < S::kLaneVec; ++k)
         if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
     }
-    // S^T = K . Q^T
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    s16x4_t pt[CG]; // P^T operand of each group
 #pragma unroll
-    for (int j = 0; j < S::kKSteps; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), qop[j], s, 0, 0, 0);
-    if constexpr (KT == DT_INT4) {
+    for (int c = 0; c < CG; ++c) {
+      if (c > 0 && !grp_on[c]) continue; // the same in every lane
+      // S^T = K . Q^T
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] -= qoff; // remove the 136-per-element offset of K
-    }
-    float sv[4];
+      for (int j = 0; j < S::kKSteps; ++j)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), qop[c][j], s, 0, 0, 0);
+      if constexpr (KT == DT_INT4) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
-    if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
-    }
-    if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = ts + 4 * q4 + r;
-        if (tok < lane_lo || tok >= lane_hi) sv[r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) s[r] -= qoff[c]; // remove the 136-per-element offset of K
       }
-    }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = xor32_max(xor16_max(mx));
-    // Lazy rescale: the reference max m_run moves (and the state is rescaled
-    // by 2^(m_run - m_new)) only when a score exceeds it by more than kLazy,
-    // so weights stay below 2^kLazy and after the first tiles the rescale is
-    // almost never needed.  m + log2(l) and acc / l do not depend on which
-    // reference is used.
-    // m_run = -inf: any visible key grows it.  A given starting reference
-    // (unified max) far above a still-empty state's first scores is moved
-    // down to them, so no weight underflows.
-    const bool empty = l_run == 0.0f;
-    const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
-      m_run = grow ? mx : m_run;
-      l_run *= alpha;
-      if constexpr (KT == DT_INT4) lb_run *= alpha;
+      float sv[4];
 #pragma unroll
-      for (int w = 0; w < S::kOTiles; ++w) {
+      for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+      if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[w][r] *= alpha;
+        for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
       }
-    }
-    // no visible key so far for this head: weights 0, state unchanged
-    const bool live = m_run != -INFINITY;
-    float pr[4];
+      if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_run) : 0.0f;
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-    const s16x4_t pt = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-    if constexpr (KT == DT_INT4)
-      lb_run += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-                (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+        for (int r = 0; r < 4; ++r) {
+          const int tok = ts + 4 * q4 + r;
+          if (tok < lane_lo[c] || tok >= lane_hi[c]) sv[r] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = xor32_max(xor16_max(mx));
+      // Lazy rescale: the reference max m_run moves (and the state is rescaled
+      // by 2^(m_run - m_new)) only when a score exceeds it by more than kLazy,
+      // so weights stay below 2^kLazy and after the first tiles the rescale is
+      // almost never needed.  m + log2(l) and acc / l do not depend on which
+      // reference is used.
+      // m_run = -inf: any visible key grows it.  A given starting reference
+      // (unified max) far above a still-empty state's first scores is moved
+      // down to them, so no weight underflows.
+      const bool empty = l_run[c] == 0.0f;
+      const bool grow = mx > m_run[c] + kLazy || (empty && mx != -INFINITY && mx < m_run[c] - kDrop);
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - mx)) : 1.0f;
+        m_run[c] = grow ? mx : m_run[c];
+        l_run[c] *= alpha;
+        if constexpr (KT == DT_INT4) lb_run[c] *= alpha;
+#pragma unroll
+        for (int w = 0; w < S::kOTiles; ++w) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[c][w][r] *= alpha;
+        }
+      }
+      // no visible key so far for this column: weights 0, state unchanged
+      const bool live = m_run[c] != -INFINITY;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_run[c]) : 0.0f;
+      l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+      pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+      if constexpr (KT == DT_INT4)
+        lb_run[c] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+    }
     // V^T slices (all products first, so the dependent conversions and
     // accumulations below do not wait on each other), then O^T += V^T . P^T
     f32x4_t vt[S::kOTiles];
@@ -561,7 +592,12 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     for (int w = 0; w < S::kOTiles; ++w)
       va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
 #pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) oacc[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt, oacc[w], 0, 0, 0);
+    for (int c = 0; c < CG; ++c) {
+      if (c > 0 && !grp_on[c]) continue;
+#pragma unroll
+      for (int w = 0; w < S::kOTiles; ++w)
+        oacc[c][w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt[c], oacc[c][w], 0, 0, 0);
+    }
   };
 
   // Ring of NBUF staging slots per wave.  A slot is refilled as soon as its
@@ -587,37 +623,46 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
   __syncthreads(); // staging area is reused for the per-wave states below
 
-  // ---- per-wave state to LDS (each query head keeps the dims of its KV head) ----
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  float lb_tot = 0.0f;
-  if constexpr (KT == DT_INT4) {
-    lb_tot = lb_run + __shfl_xor(lb_run, 16, 64);
-    lb_tot += __shfl_xor(lb_tot, 32, 64);
-  }
-  if (col_ok) {
-    if (q4 == 0) {
-      sm_m[wave][c16] = l_tot > 0.0f ? m_run : -INFINITY; // an empty state keeps no reference
-      sm_l[wave][c16] = l_tot;
+  // ---- per-wave states to LDS (each query head keeps the dims of its KV head),
+  // merged over the waves and stored one column group at a time ----
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0) {
+      if (!grp_on[c]) break; // the same in every lane of the workgroup
+      __syncthreads();       // the previous group's merge has read the states
     }
-    float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
-    // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
-    const float voff = kInt4Offset * lb_tot;
+    float l_tot = l_run[c] + __shfl_xor(l_run[c], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    float lb_tot = 0.0f;
+    if constexpr (KT == DT_INT4) {
+      lb_tot = lb_run[c] + __shfl_xor(lb_run[c], 16, 64);
+      lb_tot += __shfl_xor(lb_tot, 32, 64);
+    }
+    if (col_ok[c]) {
+      if (q4 == 0) {
+        sm_m[wave][c16] = l_tot > 0.0f ? m_run[c] : -INFINITY; // an empty state keeps no reference
+        sm_l[wave][c16] = l_tot;
+      }
+      float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
+      // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
+      const float voff = kInt4Offset * lb_tot;
 #pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) {
-      const int od = out_dim<DE, KT>(w, q4);
-      if (od / D == my_kv) {
-        if constexpr (S::kOutStride == 1) {
-          *reinterpret_cast<float4 *>(dst + od % D) = make_float4(oacc[w][0], oacc[w][1], oacc[w][2], oacc[w][3]);
-        } else {
+      for (int w = 0; w < S::kOTiles; ++w) {
+        const int od = out_dim<DE, KT>(w, q4);
+        if (od / D == my_kv) {
+          if constexpr (S::kOutStride == 1) {
+            *reinterpret_cast<float4 *>(dst + od % D) =
+                make_float4(oacc[c][w][0], oacc[c][w][1], oacc[c][w][2], oacc[c][w][3]);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dst[od % D + r * S::kOutStride] = oacc[w][r] - voff;
+            for (int r = 0; r < 4; ++r) dst[od % D + r * S::kOutStride] = oacc[c][w][r] - voff;
+          }
         }
       }
     }
+    __syncthreads();
+    merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
-  __syncthreads();
-  merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg, item, nb);
 }
 
 } // namespace
@@ -625,9 +670,21 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 template <int D, int PACK, int KT>
 static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
   constexpr int NB = Shape<D * PACK, KT>::kNBuf;
-  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB>,
+  if constexpr (PACK == 1 && D <= 128) {
+    if (p.col_share == 2)
+      return launch_kernel(l, partial_mfma_kernel<D, 1, KT, NB, 2>,
+                           dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
+  }
+  if (p.col_share != 1) return hipErrorInvalidValue;
+  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB, 1>,
                        dim3(p.items, p.num_kv_heads / PACK * p.col_groups), p, w);
 }
+
+// Column groups of (query row, head) pairs one workgroup computes on each
+// staged tile (several query rows per request): two halve the K/V reads of
+// longer appends; head_dim 256 keeps one, its accumulators would not fit in
+// registers twice.
+int mfma_col_share(int head_dim, int col_groups) { return col_groups >= 2 && head_dim <= 128 ? 2 : 1; }
 
 // KV heads per workgroup.  Two heads per pack would make every staged row at
 // least 256 contiguous bytes for fp8 head_dim 128 (128-byte segments stream

@@ -83,6 +83,7 @@ struct Params {
   int items;      // work items per KV head
   const int *qo_indptr; // [batch + 1] query rows of each request; null: one row each
   int col_groups; // groups of 16 (query, head) columns per KV head (1 for one query)
+  int col_share;  // column groups one partial workgroup computes together (1 or 2)
   int cols;       // columns per partial slot: group * pack (one query) or 16
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16

@@ -10,7 +10,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(0, L - nq + 1 - window) : 0; }
 
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_groups, int head_dim, int forced_chunk, int num_cus, Plan *out) {
+               int col_blocks, int head_dim, int forced_chunk, int num_cus, Plan *out) {
   Plan pl;
   // span of request b: from its first 16-aligned visible tile to its last key
   int64_t total = 0;
@@ -25,7 +25,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
     chunk = ((int64_t)forced_chunk + 15) / 16 * 16;
   } else {
     const int64_t target = (int64_t)kItemsPerCu * std::max(1, num_cus);
-    chunk = (total * num_kv_heads * col_groups + target - 1) / target;
+    chunk = (total * num_kv_heads * col_blocks + target - 1) / target;
     chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
     chunk = std::max<int64_t>(chunk, kMinChunk);
   }

@@ -44,9 +44,9 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
 // kv_len: host lengths [batch]; nq: query rows per request or null (one
 // each); cols: partial-result columns per KV head over all column groups
 // (the group size with one query per request, col_groups * 16 with
-// several); col_groups: workgroups per (item, KV head).  Returns false if a
-// length is negative.
+// several); col_blocks: partial workgroups per (item, KV head).  Returns
+// false if a length is negative.
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_groups, int head_dim, int forced_chunk, int num_cus, Plan *out);
+               int col_blocks, int head_dim, int forced_chunk, int num_cus, Plan *out);
 
 } // namespace kvs
