@@ -37,27 +37,32 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over the default command of
 # each workload, each scaled by the factor the same counter gives for
 # kvs_probe_copy of 1 GiB (the counter summaries under profiles/ hold the
-# commands and raw figures).  A figure is reported only while the library
-# sources hash to the digest it was measured with; otherwise traffic is null.
+# commands and raw figures).  A figure is reported only while the sources
+# that decide the partial kernel's memory traffic hash to the digest it was
+# measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299427875, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
+        {"bytes": 2299473045, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487846789, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
+        {"bytes": 1487903115, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538181783, "digest": "d830e649a15563efcb172d4bdac2ac89d9510fc2554b63e385fa353005b34731"},
+        {"bytes": 538227053, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
 }
 
 
-def library_digest() -> str:
-    """SHA-256 over the library's device and host sources and build flags."""
+# Sources that decide what the matrix-core partial kernel reads and writes:
+# the kernel, its shared device code, the planner (chunk sizes, workspace),
+# the host code that fills its parameters, and the build flags.
+DIGEST_SOURCES = ["build.py", "csrc/decode_mfma.hip", "csrc/kvs_device.h", "csrc/plan.cpp", "csrc/plan.h",
+                  "csrc/abi.cpp"]
+
+
+def partial_kernel_digest() -> str:
+    """SHA-256 over DIGEST_SOURCES."""
     import hashlib
 
     pkg = os.path.join(ROOT, "decode_attention_kv_split_amd")
-    files = [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "kvsplit.h")]
-    csrc = os.path.join(pkg, "csrc")
-    files += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
-              if f.endswith((".hip", ".h", ".cpp"))]
+    files = [os.path.join(pkg, f) for f in DIGEST_SOURCES]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -68,7 +73,7 @@ def library_digest() -> str:
 
 def measured_traffic(config_name: str, kernel: str):
     rec = MEASURED_TRAFFIC.get((config_name, kernel))
-    if rec is None or rec["digest"] != library_digest():
+    if rec is None or rec["digest"] != partial_kernel_digest():
         return None
     return rec["bytes"]
 
@@ -363,7 +368,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "algorithmic_bytes": nbytes,
         },
         "device": {"name": props.name, "cus": props.multi_processor_count, "host": platform.node()},
-        "library_digest": library_digest()[:16],
+        "partial_kernel_digest": partial_kernel_digest()[:16],
         "probe_stream_read_GBs": round(probe_read_gbs(), 1),
         "input_gen_s": round(t_gen, 1),
     }
