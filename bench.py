@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix throughput, published
 METRIC = "decode-attention \u00b5s/step and achieved HBM GB/s (% of peak), paged GQA batch"
 CONFIG_ALIASES = {"c1": "c1_mha_f32", "c2": "c2_gemma3_1b", "c2w": "c2_gemma3_1b_w512",
                   "c3": "c3_llama2_7b_32k", "c4": "c4_paged_bf16_b64", "c5": "c5_paged_fp8_b128",
@@ -115,6 +116,24 @@ def algorithmic_bytes(inp) -> int:
     if s.kv_dtype in ("fp8", "int4"):
         meta += 2 * 4 * s.batch * s.num_kv_heads
     return kv + qo + meta
+
+
+def attention_flops(inp) -> int:
+    """Multiply-adds of the two products, 2 flops each: for every (query
+    row, query head) and every key the row sees, head_dim for the score and
+    head_dim for the weighted sum of V (4 * head_dim flops per pair)."""
+    s = inp.spec
+    L = inp.kv_len.astype(np.int64)
+    nq = query_rows(inp)
+    pairs = 0
+    for b in range(s.batch):
+        n = int(nq[b])
+        if n == 0:
+            continue
+        pos = L[b] - n + np.arange(n, dtype=np.int64)       # position of each row
+        lo = np.maximum(0, pos - s.window + 1) if s.window > 0 else np.zeros(n, np.int64)
+        pairs += int(np.sum(pos + 1 - lo))
+    return 4 * s.head_dim * s.num_qo_heads * pairs
 
 
 class HipEvents:
@@ -263,7 +282,7 @@ def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
-        q_len: int = 1, soft_cap: float = 0.0) -> dict:
+        q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0) -> dict:
     import dataclasses
 
     import torch
@@ -280,6 +299,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
         spec = dataclasses.replace(spec, q_len=("fixed", q_len))
     if soft_cap:
         spec = dataclasses.replace(spec, soft_cap=soft_cap)
+    if kv_len:
+        spec = dataclasses.replace(spec, lengths=("fixed", kv_len))
     t_gen = time.perf_counter()
     inp = make_inputs(spec)
     t = to_torch(inp)
@@ -330,6 +351,9 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     achieved = nbytes / (part_avg * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(0)
     kernel = ("partial_mfma_kernel" if plan.algo == kvs.KVS_ALGO_MFMA else "partial_valu_kernel")
+    flops = attention_flops(inp)
+    # machine balance: bf16 matrix flops per HBM byte at the two published peaks
+    mfma_bound = flops / nbytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -353,6 +377,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
             "max_splits": plan.max_splits, "parallelism": "single GPU",
             "unified_max": unified_max, "q_len": q_len, "soft_cap": spec.soft_cap,
+            "kv_len_override": kv_len or None,
         },
         "roofline": {
             "bound": "hbm",
@@ -361,17 +386,23 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(config_name, kernel) if q_len == 1 and not soft_cap else None,
+            "traffic": measured_traffic(config_name, kernel) if q_len == 1 and not soft_cap and not kv_len else None,
             "kernel_us": round(part_avg * 1e3, 2),
             "kernel_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
             "kernel_launches_timed": len(stamped),
             "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops,
+            "matrix_tflops": round(flops / (part_avg * 1e-3) / 1e12, 2),
         },
         "device": {"name": props.name, "cus": props.multi_processor_count, "host": platform.node()},
         "partial_kernel_digest": partial_kernel_digest()[:16],
         "probe_stream_read_GBs": round(probe_read_gbs(), 1),
         "input_gen_s": round(t_gen, 1),
     }
+    if mfma_bound:  # long prefills: the contraction, not HBM, bounds the kernel
+        tf = flops / (part_avg * 1e-3) / 1e12
+        out["roofline"].update(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                               frac=round(tf / PEAK_BF16_TFLOPS, 4))
     if cold:
         out["cold_cache"] = cold_steps(step, stream, HipEvents(), nbytes, max(20, steps // 2))
     if not events:
@@ -521,6 +552,8 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="new query tokens per request (1: decode; more: append / speculative-verify attention, "
                          "each row causal over the cache)")
+    ap.add_argument("--kv-len", type=int, default=0,
+                    help="give every request this cache length (0: the workload's own lengths)")
     ap.add_argument("--soft-cap", type=float, default=0.0,
                     help="logit soft-cap c: scores become c * tanh(s / c) (0: none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -547,7 +580,7 @@ def main():
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
-              soft_cap=args.soft_cap)
+              soft_cap=args.soft_cap, kv_len=args.kv_len)
     print(json.dumps(res), flush=True)
 
 

@@ -308,13 +308,13 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
   const int t_begin = max(lo, a0);
   const int t_end = min(L, a0 + p.chunk);
-  const int ntiles = t_end > t_begin ? (t_end - a0 + kTile - 1) / kTile : 0;
   int qrow[CG];       // row of q / o of this lane's column, per group
   int qhead[CG];      // query head of this lane's column, per group
   bool col_ok[CG];    // the column holds a (query, head) of the request
   bool grp_on[CG];    // the group holds any (the same in every lane)
   int lane_lo[CG], lane_hi[CG]; // keys of the chunk this lane's column sees
   int all_lo = t_begin, all_hi = t_end; // keys every column of every group sees
+  int any_lo = t_end, any_hi = t_begin; // keys some column sees
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     int qi; // query index within the request (0 with one query)
@@ -340,15 +340,28 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     if (col_ok[c]) {
       all_lo = max(all_lo, lane_lo[c]);
       all_hi = min(all_hi, lane_hi[c]);
+      if (lane_lo[c] < lane_hi[c]) {
+        any_lo = min(any_lo, lane_lo[c]);
+        any_hi = max(any_hi, lane_hi[c]);
+      }
     }
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
     all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
     all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+    any_lo = min(any_lo, __shfl_xor(any_lo, o, 64));
+    any_hi = max(any_hi, __shfl_xor(any_hi, o, 64));
   }
   all_lo = __builtin_amdgcn_readfirstlane(all_lo);
   all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  // Only the tiles holding keys some column sees are streamed: with several
+  // rows per request (a causal prefill) the early rows stop long before the
+  // chunk does.  With one query per request this is the whole chunk.
+  const int w_lo = __builtin_amdgcn_readfirstlane(any_lo);
+  const int w_hi = __builtin_amdgcn_readfirstlane(any_hi);
+  const int ft = w_hi > w_lo ? (w_lo - a0) / kTile : 0; // first tile, counted from the chunk start
+  const int ntiles = w_hi > w_lo ? (w_hi - a0 + kTile - 1) / kTile - ft : 0;
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // ---- Q^T operand: block diagonal over the pack, zero columns past gp ----
@@ -416,12 +429,12 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // them with v_readlane and never waits on memory for an address.
   uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
   if (lane < my_tiles) {
-    const int ts = a0 + (wave + lane * kWaves) * kTile;
+    const int ts = a0 + (ft + wave + lane * kWaves) * kTile;
     const size_t row0 = paged ? (size_t)pages[ts >> pshift] * p.page_size + (ts & pmask) : (size_t)ts;
     const size_t off = row0 * row_bytes;
     voff_lo = (uint32_t)off;
     voff_hi = (uint32_t)(off >> 32);
-    vbytes = (uint32_t)(min(kTile, t_end - ts) * (int)row_bytes);
+    vbytes = (uint32_t)(min(kTile, w_hi - ts) * (int)row_bytes);
   }
   // K/V tiles go from HBM straight into this wave's LDS slots with 16-byte
   // DMA loads in cache-line order (each load covers whole row segments of the
@@ -493,9 +506,9 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
-    const int ts = a0 + (wave + i * kWaves) * kTile;
-    if (ts < t_begin) { // rows before the window / chunk start hold keys of no interest
-      const bool ok = ts + c16 >= t_begin;
+    const int ts = a0 + (ft + wave + i * kWaves) * kTile;
+    if (ts < w_lo) { // rows before the first key any column sees hold keys of no interest
+      const bool ok = ts + c16 >= w_lo;
 #pragma unroll
       for (int k = 0; k < S::kLaneVec; ++k)
         if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);

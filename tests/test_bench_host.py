@@ -73,3 +73,16 @@ def test_quantised_bytes():
     assert bench.algorithmic_bytes(fp8) == 2 * 150 * 2 * 64 + 2 * 3 * 8 * 64 * 2 + 4 * 24 + meta
     assert bench.algorithmic_bytes(int4) == 2 * 150 * 2 * 64 + 2 * 3 * 8 * 128 * 2 + 4 * 24 + meta
     assert np.all(bench.query_rows(fp8) == 1)
+
+
+def test_attention_flops_count_every_visible_pair():
+    # decode: each (request, head) sees L keys; 4 * d flops per pair
+    inp = make_inputs(_spec())
+    assert bench.attention_flops(inp) == 4 * 64 * 8 * sum(LENS)
+    # rows 3, 0, 5 with window 8: request 0 (L 10) rows at 7, 8, 9 see 8 keys each;
+    # request 2 (L 100) rows at 95..99 see 8 each
+    rows = make_inputs(_spec(window=8, q_len=("list", [3, 0, 5])))
+    assert bench.attention_flops(rows) == 4 * 64 * 8 * (3 * 8 + 5 * 8)
+    # a causal prefill of n = L rows sees 1 + 2 + ... + L pairs
+    pre = make_inputs(_spec(batch=1, page_size=0, lengths=("fixed", 100), q_len=("fixed", 100)))
+    assert bench.attention_flops(pre) == 4 * 64 * 8 * (100 * 101 // 2)
