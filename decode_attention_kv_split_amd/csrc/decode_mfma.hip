@@ -35,6 +35,12 @@
 // "Flash Attention in JAX"; chunk results are merged by log-sum-exp (FlashDecoding++
 // explainer, asynchronous-softmax section: partial softmax per tile, then an
 // update with the previous max and sum).
+//
+// Several query rows per request turn the columns into (query row, head)
+// pairs.  Up to two groups of 16 such columns run in the kernel above (both
+// on each staged tile); from three groups on, partial_rows_kernel (further
+// down) lets its four waves share each staged tile instead of splitting the
+// keys, so a workgroup reads the keys once for 128 columns.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -230,6 +236,294 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, KT> &t, int j) 
   }
 }
 
+// Which (request b, split) work item `item` is, with the request's split
+// count nb and length L: from the host-planned list, else by a scan of the
+// device lengths (which also records each request's first item and split
+// count for the merge).  Returns false, the same in every thread, when the
+// device lengths disagree with the planned launch.  Every thread calls it.
+__device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w, int item, int *s_scan, int *s_item,
+                                            int &b, int &split, int &nb, int &L) {
+  if (w.n_items > 0) { // planned on the host
+    const uint32_t e = w.item[item];
+    b = (int)(e >> 16);
+    split = (int)(e & 0xFFFF);
+    L = w.req_len[b];
+    nb = num_splits(L, req_nq(p, b), p.window, p.chunk);
+    return true;
+  }
+  if (threadIdx.x == 0) s_item[0] = -1;
+  scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
+    if (item >= first && item < first + nbb) {
+      s_item[0] = bb;
+      s_item[1] = item - first;
+      s_item[2] = nbb;
+      s_item[3] = first;
+    }
+  });
+  __syncthreads();
+  b = __builtin_amdgcn_readfirstlane(s_item[0]);
+  split = __builtin_amdgcn_readfirstlane(s_item[1]);
+  nb = __builtin_amdgcn_readfirstlane(s_item[2]);
+  if (b < 0) return false;
+  if (p.meta && split == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    p.meta[2 * b] = s_item[3];
+    p.meta[2 * b + 1] = nb;
+  }
+  L = p.kv_len[b];
+  return true;
+}
+
+// Operands of the V transposition for lane (c16, q4): a bf16 identity
+// (16x16x16 products) and, for fp8, 0/1 selections of one code per
+// 16x16x32 product (the fp8 pattern 0x38 is 1.0).
+template <int KT>
+__device__ __forceinline__ void transpose_operands(int c16, int q4, s16x4_t &ident, long (&sel)[2]) {
+  const short one_bf16 = 0x3F80;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
+  sel[0] = sel[1] = 0;
+  if (KT == DT_FP8) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint64_t s = 0;
+      if (q4 == (c16 >> 2)) s = (uint64_t)0x38 << (8 * (4 * hh + (c16 & 3)));
+      sel[hh] = (long)s;
+    }
+  }
+}
+
+// ---- column groups: per-lane state shared by the two partial kernels ----
+// A wave computes CG groups of 16 matrix columns; lane (c16, q4) holds column
+// c16 of every group.  A column is a query head of the pack (one query per
+// request) or a (query row, head) pair (several rows per request).
+template <int DE, int KT, int CG>
+struct ColumnSet {
+  using S = Shape<DE, KT>;
+  bf16x8_t q[CG][S::kKSteps]; // Q^T operand, zero where the column sees no dims
+  float qoff[CG];             // INT4: the scores carry 136 * (sum of the column's q)
+  bool ok[CG];                // the lane's column holds a (query, head) of the request
+  bool on[CG];                // the group holds any (the same in every lane)
+  int row[CG], head[CG];      // q / o row and query head of the lane's column
+  int lo[CG], hi[CG];         // keys of the chunk the lane's column sees
+  float m[CG];                // reference max, log2 domain (the same in the 4 quarters)
+  float l[CG];                // partial sum over the lane's tokens
+  float lb[CG];               // INT4: the same sum of the bf16-rounded weights P.V saw
+  f32x4_t acc[CG][S::kOTiles];
+};
+
+// Which (query, head) each lane's column is, and the keys of [t_begin,
+// t_end) it sees: up to its query's position, the last `window` of them.
+// cg0: the set's first column group; gp: query heads per pack.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void set_columns(ColumnSet<DE, KT, CG> &cs, const Params &p, int b, int L, int nq,
+                                            int kvg, int cg0, int gp, int t_begin, int t_end, int c16) {
+  const int g = p.group;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    int qi; // query index within the request (0 with one query)
+    if (!p.qo_indptr) {
+      cs.ok[c] = c16 < gp;
+      cs.on[c] = true;
+      qi = 0;
+      cs.row[c] = b;
+      cs.head[c] = kvg * gp + c16;
+    } else {
+      const int col = (cg0 + c) * 16 + c16;
+      cs.ok[c] = col < nq * g;
+      cs.on[c] = (cg0 + c) * 16 < nq * g;
+      qi = col / g;
+      cs.row[c] = p.qo_indptr[b] + qi;
+      cs.head[c] = kvg * g + col % g;
+    }
+    const int qpos = L - nq + qi;
+    const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
+    cs.lo[c] = max(t_begin, col_lo);
+    cs.hi[c] = min(t_end, qpos + 1);
+  }
+}
+
+// Keys every column of the set sees, [all_lo, all_hi) (tiles inside need no
+// per-key mask), and keys some column sees, [any_lo, any_hi); uniform.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void column_ranges(const ColumnSet<DE, KT, CG> &cs, int t_begin, int t_end, int &all_lo,
+                                              int &all_hi, int &any_lo, int &any_hi) {
+  all_lo = t_begin;
+  all_hi = t_end;
+  any_lo = t_end;
+  any_hi = t_begin;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (cs.ok[c]) {
+      all_lo = max(all_lo, cs.lo[c]);
+      all_hi = min(all_hi, cs.hi[c]);
+      if (cs.lo[c] < cs.hi[c]) {
+        any_lo = min(any_lo, cs.lo[c]);
+        any_hi = max(any_hi, cs.hi[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+    any_lo = min(any_lo, __shfl_xor(any_lo, o, 64));
+    any_hi = max(any_hi, __shfl_xor(any_hi, o, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  any_lo = __builtin_amdgcn_readfirstlane(any_lo);
+  any_hi = __builtin_amdgcn_readfirstlane(any_hi);
+}
+
+// Q^T operand of each group (block diagonal over the pack: column c16 only
+// sees the dims of its own KV head my_kv), its INT4 offset, and an empty
+// softmax state starting from the reference max m_init.
+template <int D, int DE, int KT, int CG>
+__device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Params &p, int q4, int my_kv) {
+  using S = Shape<DE, KT>;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const uint16_t *qb =
+        reinterpret_cast<const uint16_t *>(p.q) + ((size_t)cs.row[c] * p.num_qo_heads + cs.head[c]) * D;
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j) {
+      const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
+      if (cs.ok[c] && kd / D == my_kv) {
+        bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
+        if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+        cs.q[c][j] = x;
+      } else {
+        cs.q[c][j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      }
+    }
+    cs.qoff[c] = 0.0f;
+    if constexpr (KT == DT_INT4) {
+#pragma unroll
+      for (int j = 0; j < S::kKSteps; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs.qoff[c] += (float)cs.q[c][j][e];
+      cs.qoff[c] += __shfl_xor(cs.qoff[c], 16, 64);
+      cs.qoff[c] += __shfl_xor(cs.qoff[c], 32, 64);
+      cs.qoff[c] *= kInt4Offset;
+    }
+    cs.m[c] = p.m_init;
+    cs.l[c] = 0.0f;
+    cs.lb[c] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) cs.acc[c][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One staged 16-token tile (first key ts) through every column group:
+// S^T = K . Q^T, per-key masks where some column misses some key of the tile,
+// the soft-cap, the online softmax with a lazy rescale, then O^T += V^T . P^T
+// with the V^T slices shared by the groups.  ident / sel: the identity and
+// 0/1 selection operands of the V transposition.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &t, int ts, int all_lo,
+                                            int all_hi, float cscale, float cap_out, s16x4_t ident,
+                                            const long (&sel)[2], int q4) {
+  using S = Shape<DE, KT>;
+  s16x4_t pt[CG]; // P^T operand of each group
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue; // the same in every lane
+    // S^T = K . Q^T
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), cs.q[c][j], s, 0, 0, 0);
+    if constexpr (KT == DT_INT4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] -= cs.qoff[c]; // remove the 136-per-element offset of K
+    }
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+    if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
+    }
+    if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = ts + 4 * q4 + r;
+        if (tok < cs.lo[c] || tok >= cs.hi[c]) sv[r] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = xor32_max(xor16_max(mx));
+    // Lazy rescale: the reference max m moves (and the state is rescaled
+    // by 2^(m - m_new)) only when a score exceeds it by more than kLazy,
+    // so weights stay below 2^kLazy and after the first tiles the rescale is
+    // almost never needed.  m + log2(l) and acc / l do not depend on which
+    // reference is used.
+    // m = -inf: any visible key grows it.  A given starting reference
+    // (unified max) far above a still-empty state's first scores is moved
+    // down to them, so no weight underflows.
+    const bool empty = cs.l[c] == 0.0f;
+    const bool grow = mx > cs.m[c] + kLazy || (empty && mx != -INFINITY && mx < cs.m[c] - kDrop);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(cs.m[c] - mx)) : 1.0f;
+      cs.m[c] = grow ? mx : cs.m[c];
+      cs.l[c] *= alpha;
+      if constexpr (KT == DT_INT4) cs.lb[c] *= alpha;
+#pragma unroll
+      for (int w = 0; w < S::kOTiles; ++w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cs.acc[c][w][r] *= alpha;
+      }
+    }
+    // no visible key so far for this column: weights 0, state unchanged
+    const bool live = cs.m[c] != -INFINITY;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - cs.m[c]) : 0.0f;
+    cs.l[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+    pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+    if constexpr (KT == DT_INT4)
+      cs.lb[c] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+                   (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+  }
+  // V^T slices (all products first, so the dependent conversions and
+  // accumulations below do not wait on each other), then O^T += V^T . P^T
+  f32x4_t vt[S::kOTiles];
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < S::kOTiles; ++w) {
+    if constexpr (KT == DT_INT4) {
+      // even (w even) or odd nibbles of dword (w / 2) % 4 of piece w / 8, as 136 + n
+      const uint32_t dw = dword_of(t.v[w >> 3], (w >> 1) & 3);
+      const uint32_t nib = (w & 1) ? int4_odd(dw) : int4_even(dw);
+      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+    } else if constexpr (KT == DT_FP8) {
+      const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
+      const uint4 wv = t.v[u >> 1];
+      const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
+      const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
+      const long a = (long)(((uint64_t)hi32 << 32) | lo32);
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
+    } else {
+      const uint4 wv = t.v[w >> 1];
+      const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+    }
+  }
+  s16x4_t va[S::kOTiles];
+#pragma unroll
+  for (int w = 0; w < S::kOTiles; ++w)
+    va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w)
+      cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt[c], cs.acc[c][w], 0, 0, 0);
+  }
+}
+
 // CG: column groups (16 columns each) a wave computes on every staged tile;
 // more than one only with several query rows per request and one KV head per
 // workgroup.  The groups share the K operand and the V^T products, so K/V
@@ -273,33 +567,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 
   // ---- which (request, split) is this workgroup? ----
   int b, split, nb, L;
-  if (w.n_items > 0) { // planned on the host
-    const uint32_t e = w.item[item];
-    b = (int)(e >> 16);
-    split = (int)(e & 0xFFFF);
-    L = w.req_len[b];
-    nb = num_splits(L, req_nq(p, b), p.window, p.chunk);
-  } else {
-    if (tid == 0) s_item[0] = -1;
-    scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
-      if (item >= first && item < first + nbb) {
-        s_item[0] = bb;
-        s_item[1] = item - first;
-        s_item[2] = nbb;
-        s_item[3] = first;
-      }
-    });
-    __syncthreads();
-    b = __builtin_amdgcn_readfirstlane(s_item[0]);
-    split = __builtin_amdgcn_readfirstlane(s_item[1]);
-    nb = __builtin_amdgcn_readfirstlane(s_item[2]);
-    if (b < 0) return; // kv_len on the device disagrees with the planned launch
-    if (p.meta && split == 0 && blockIdx.y == 0 && tid == 0) {
-      p.meta[2 * b] = s_item[3];
-      p.meta[2 * b + 1] = nb;
-    }
-    L = p.kv_len[b];
-  }
+  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
 
   // ---- columns: query heads of the pack, or (query row, head) pairs ----
   const int nq = req_nq(p, b);
@@ -308,112 +576,25 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
   const int t_begin = max(lo, a0);
   const int t_end = min(L, a0 + p.chunk);
-  int qrow[CG];       // row of q / o of this lane's column, per group
-  int qhead[CG];      // query head of this lane's column, per group
-  bool col_ok[CG];    // the column holds a (query, head) of the request
-  bool grp_on[CG];    // the group holds any (the same in every lane)
-  int lane_lo[CG], lane_hi[CG]; // keys of the chunk this lane's column sees
-  int all_lo = t_begin, all_hi = t_end; // keys every column of every group sees
-  int any_lo = t_end, any_hi = t_begin; // keys some column sees
-#pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    int qi; // query index within the request (0 with one query)
-    if (!p.qo_indptr) {
-      col_ok[c] = c16 < gp;
-      grp_on[c] = true;
-      qi = 0;
-      qrow[c] = b;
-      qhead[c] = kvg * gp + c16;
-    } else {
-      const int col = (cg0 + c) * 16 + c16;
-      col_ok[c] = col < nq * g;
-      grp_on[c] = (cg0 + c) * 16 < nq * g;
-      qi = col / g;
-      qrow[c] = p.qo_indptr[b] + qi;
-      qhead[c] = kvg * g + col % g;
-    }
-    // keys this column sees: up to its query's position, the last `window` of them
-    const int qpos = L - nq + qi;
-    const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
-    lane_lo[c] = max(t_begin, col_lo);
-    lane_hi[c] = min(t_end, qpos + 1);
-    if (col_ok[c]) {
-      all_lo = max(all_lo, lane_lo[c]);
-      all_hi = min(all_hi, lane_hi[c]);
-      if (lane_lo[c] < lane_hi[c]) {
-        any_lo = min(any_lo, lane_lo[c]);
-        any_hi = max(any_hi, lane_hi[c]);
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
-    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
-    any_lo = min(any_lo, __shfl_xor(any_lo, o, 64));
-    any_hi = max(any_hi, __shfl_xor(any_hi, o, 64));
-  }
-  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
-  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  ColumnSet<DE, KT, CG> cs;
+  set_columns(cs, p, b, L, nq, kvg, cg0, gp, t_begin, t_end, c16);
+  // keys every column sees (no per-key mask) and keys some column sees
+  int all_lo, all_hi, w_lo, w_hi;
+  column_ranges(cs, t_begin, t_end, all_lo, all_hi, w_lo, w_hi);
   // Only the tiles holding keys some column sees are streamed: with several
   // rows per request (a causal prefill) the early rows stop long before the
   // chunk does.  With one query per request this is the whole chunk.
-  const int w_lo = __builtin_amdgcn_readfirstlane(any_lo);
-  const int w_hi = __builtin_amdgcn_readfirstlane(any_hi);
   const int ft = w_hi > w_lo ? (w_lo - a0) / kTile : 0; // first tile, counted from the chunk start
   const int ntiles = w_hi > w_lo ? (w_hi - a0 + kTile - 1) / kTile - ft : 0;
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  load_columns<D>(cs, p, q4, my_kv);
 
-  // ---- Q^T operand: block diagonal over the pack, zero columns past gp ----
-  bf16x8_t qop[CG][S::kKSteps];
-#pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow[c] * p.num_qo_heads + qhead[c]) * D;
-#pragma unroll
-    for (int j = 0; j < S::kKSteps; ++j) {
-      const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
-      if (col_ok[c] && kd / D == my_kv) {
-        bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
-        if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
-        qop[c][j] = x;
-      } else {
-        qop[c][j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-      }
-    }
-  }
   float cscale = p.score_scale;
   if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
   const float cap_out = p.cap_out;
-  // INT4: the scores carry 136 * (sum of this head's q over the pack dims)
-  float qoff[CG];
-#pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    qoff[c] = 0.0f;
-    if constexpr (KT == DT_INT4) {
-#pragma unroll
-      for (int j = 0; j < S::kKSteps; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qoff[c] += (float)qop[c][j][e];
-      qoff[c] += __shfl_xor(qoff[c], 16, 64);
-      qoff[c] += __shfl_xor(qoff[c], 32, 64);
-      qoff[c] *= kInt4Offset;
-    }
-  }
-
-  // identity / selection operands of the V transposition
-  const short one_bf16 = 0x3F80;
   s16x4_t ident;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
-  long sel[2] = {0, 0};
-  if (KT == DT_FP8) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint64_t s = 0;
-      if (q4 == (c16 >> 2)) s = (uint64_t)0x38 << (8 * (4 * hh + (c16 & 3)));
-      sel[hh] = (long)s;
-    }
-  }
+  long sel[2];
+  transpose_operands<KT>(c16, q4, ident, sel);
 
   // ---- addressing ----
   const size_t row_bytes = (size_t)Hk * (S::kRowBytes / PACK); // bytes between consecutive tokens
@@ -490,21 +671,6 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     }
   };
 
-  // ---- running state ----
-  // per column group c:
-  float m_run[CG];  // reference max, log2 domain, per column c16 (same in the 4 quarters)
-  float l_run[CG];  // partial sum over this lane's tokens
-  float lb_run[CG]; // INT4: the same sum of the bf16-rounded weights the P.V product sees
-  f32x4_t oacc[CG][S::kOTiles];
-#pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    m_run[c] = p.m_init;
-    l_run[c] = 0.0f;
-    lb_run[c] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) oacc[c][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
   auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (ft + wave + i * kWaves) * kTile;
     if (ts < w_lo) { // rows before the first key any column sees hold keys of no interest
@@ -513,104 +679,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       for (int k = 0; k < S::kLaneVec; ++k)
         if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
     }
-    s16x4_t pt[CG]; // P^T operand of each group
-#pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      if (c > 0 && !grp_on[c]) continue; // the same in every lane
-      // S^T = K . Q^T
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < S::kKSteps; ++j)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), qop[c][j], s, 0, 0, 0);
-      if constexpr (KT == DT_INT4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] -= qoff[c]; // remove the 136-per-element offset of K
-      }
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
-      if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
-      }
-      if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = ts + 4 * q4 + r;
-          if (tok < lane_lo[c] || tok >= lane_hi[c]) sv[r] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = xor32_max(xor16_max(mx));
-      // Lazy rescale: the reference max m_run moves (and the state is rescaled
-      // by 2^(m_run - m_new)) only when a score exceeds it by more than kLazy,
-      // so weights stay below 2^kLazy and after the first tiles the rescale is
-      // almost never needed.  m + log2(l) and acc / l do not depend on which
-      // reference is used.
-      // m_run = -inf: any visible key grows it.  A given starting reference
-      // (unified max) far above a still-empty state's first scores is moved
-      // down to them, so no weight underflows.
-      const bool empty = l_run[c] == 0.0f;
-      const bool grow = mx > m_run[c] + kLazy || (empty && mx != -INFINITY && mx < m_run[c] - kDrop);
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run[c] - mx)) : 1.0f;
-        m_run[c] = grow ? mx : m_run[c];
-        l_run[c] *= alpha;
-        if constexpr (KT == DT_INT4) lb_run[c] *= alpha;
-#pragma unroll
-        for (int w = 0; w < S::kOTiles; ++w) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[c][w][r] *= alpha;
-        }
-      }
-      // no visible key so far for this column: weights 0, state unchanged
-      const bool live = m_run[c] != -INFINITY;
-      float pr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - m_run[c]) : 0.0f;
-      l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-      pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-      if constexpr (KT == DT_INT4)
-        lb_run[c] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-                     (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
-    }
-    // V^T slices (all products first, so the dependent conversions and
-    // accumulations below do not wait on each other), then O^T += V^T . P^T
-    f32x4_t vt[S::kOTiles];
-    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) {
-      if constexpr (KT == DT_INT4) {
-        // even (w even) or odd nibbles of dword (w / 2) % 4 of piece w / 8, as 136 + n
-        const uint32_t dw = dword_of(t.v[w >> 3], (w >> 1) & 3);
-        const uint32_t nib = (w & 1) ? int4_odd(dw) : int4_even(dw);
-        const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
-        vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
-      } else if constexpr (KT == DT_FP8) {
-        const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
-        const uint4 wv = t.v[u >> 1];
-        const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
-        const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
-        const long a = (long)(((uint64_t)hi32 << 32) | lo32);
-        vt[w] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
-      } else {
-        const uint4 wv = t.v[w >> 1];
-        const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
-        vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
-      }
-    }
-    s16x4_t va[S::kOTiles];
-#pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w)
-      va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
-#pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      if (c > 0 && !grp_on[c]) continue;
-#pragma unroll
-      for (int w = 0; w < S::kOTiles; ++w)
-        oacc[c][w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt[c], oacc[c][w], 0, 0, 0);
-    }
+    tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
   };
 
   // Ring of NBUF staging slots per wave.  A slot is refilled as soon as its
@@ -641,19 +710,19 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     if (c > 0) {
-      if (!grp_on[c]) break; // the same in every lane of the workgroup
+      if (!cs.on[c]) break; // the same in every lane of the workgroup
       __syncthreads();       // the previous group's merge has read the states
     }
-    float l_tot = l_run[c] + __shfl_xor(l_run[c], 16, 64);
+    float l_tot = cs.l[c] + __shfl_xor(cs.l[c], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     float lb_tot = 0.0f;
     if constexpr (KT == DT_INT4) {
-      lb_tot = lb_run[c] + __shfl_xor(lb_run[c], 16, 64);
+      lb_tot = cs.lb[c] + __shfl_xor(cs.lb[c], 16, 64);
       lb_tot += __shfl_xor(lb_tot, 32, 64);
     }
-    if (col_ok[c]) {
+    if (cs.ok[c]) {
       if (q4 == 0) {
-        sm_m[wave][c16] = l_tot > 0.0f ? m_run[c] : -INFINITY; // an empty state keeps no reference
+        sm_m[wave][c16] = l_tot > 0.0f ? cs.m[c] : -INFINITY; // an empty state keeps no reference
         sm_l[wave][c16] = l_tot;
       }
       float *dst = sm_o + (wave * 16 + c16) * OSTRIDE;
@@ -665,10 +734,10 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
         if (od / D == my_kv) {
           if constexpr (S::kOutStride == 1) {
             *reinterpret_cast<float4 *>(dst + od % D) =
-                make_float4(oacc[c][w][0], oacc[c][w][1], oacc[c][w][2], oacc[c][w][3]);
+                make_float4(cs.acc[c][w][0], cs.acc[c][w][1], cs.acc[c][w][2], cs.acc[c][w][3]);
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[od % D + r * S::kOutStride] = oacc[c][w][r] - voff;
+            for (int r = 0; r < 4; ++r) dst[od % D + r * S::kOutStride] = cs.acc[c][w][r] - voff;
           }
         }
       }
@@ -678,26 +747,265 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   }
 }
 
+// Several query rows per request and many column groups (a long append or a
+// prefill): the four waves share every staged K/V tile instead of splitting
+// the keys.  Wave w computes column groups cgw + CG * w .. cgw + CG * w + CG - 1
+// of one KV head, so a workgroup covers 16 * CG * kWaves columns and reads
+// each K/V byte of its chunk once for all of them.  Keys advance in blocks of
+// kWaves 16-token tiles: each wave stages one tile of the block into LDS
+// (DMA), a barrier publishes the block, every wave runs the block's tiles
+// through its column groups, and a second barrier frees the slot for the
+// block NBUF further on.  A wave's columns are its own, so it writes its
+// results with no merge across waves.
+template <int D, int KT, int NBUF, int CG>
+__global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, const InlineWork w) {
+  using S = Shape<D, KT>;
+  constexpr int kGroups = kWaves * CG;                   // column groups per workgroup
+  constexpr int kBlock = kWaves * kTile;                 // keys per staged block
+  constexpr int kSlotBytes = kWaves * 2 * S::kTileBytes; // K and V of a block
+
+  __shared__ int s_scan[2 * 64];
+  __shared__ int s_item[4];
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * kSlotBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int item = blockIdx.x;
+  const int row_blocks = (p.col_groups + kGroups - 1) / kGroups; // workgroups per (item, KV head)
+  const int kvg = blockIdx.y / row_blocks;                       // KV head
+  const int cgw = blockIdx.y % row_blocks * kGroups;             // first column group of the workgroup
+  const int g = p.group;
+  const int Hk = p.num_kv_heads;
+
+  int b, split, nb, L;
+  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  const int nq = req_nq(p, b);
+  if (cgw * 16 >= nq * g) return; // no column of this workgroup has a query row (uniform)
+  const int lo = request_lo(L, nq, p.window);
+  const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
+  const int t_begin = max(lo, a0);
+  const int t_end = min(L, a0 + p.chunk);
+  // keys some column of the workgroup sees: from the first key of its first
+  // query row to the position of its last (both grow with the row)
+  const int q_first = cgw * 16 / g;
+  const int q_last = (min(nq * g, (cgw + kGroups) * 16) - 1) / g;
+  const int wg_lo = max(t_begin, p.window > 0 ? max(0, L - nq + q_first - p.window + 1) : 0);
+  const int wg_hi = min(t_end, L - nq + q_last + 1);
+  const int fb = wg_hi > wg_lo ? (wg_lo - a0) / kBlock : 0; // first block, counted from the chunk start
+  const int nblocks = wg_hi > wg_lo ? (wg_hi - a0 + kBlock - 1) / kBlock - fb : 0;
+  const int k0 = a0 + fb * kBlock; // first key of block 0
+
+  // ---- this wave's column groups ----
+  ColumnSet<D, KT, CG> cs;
+  set_columns(cs, p, b, L, nq, kvg, cgw + wave * CG, g, t_begin, t_end, c16);
+  int all_lo, all_hi, wv_lo, wv_hi; // keys every / some column of the wave sees
+  column_ranges(cs, t_begin, t_end, all_lo, all_hi, wv_lo, wv_hi);
+  load_columns<D>(cs, p, q4, 0);
+  float cscale = p.score_scale;
+  if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg];
+  const float cap_out = p.cap_out;
+  s16x4_t ident;
+  long sel[2];
+  transpose_operands<KT>(c16, q4, ident, sel);
+
+  // ---- addressing: this wave's tile of block i, one block per lane ----
+  // (a block holds kBlock keys and chunks at most 64 * kBlock, so 64 lanes
+  // cover every block; tiles holding no key the workgroup sees move no bytes)
+  const size_t row_bytes = (size_t)Hk * S::kRowBytes;
+  const bool paged = p.page_size > 0;
+  const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
+  uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
+  if (lane < nblocks) {
+    const int ts = k0 + lane * kBlock + wave * kTile;
+    if (ts < wg_hi && ts + kTile > wg_lo) {
+      const size_t row0 =
+          paged ? (size_t)pages[ts >> p.page_shift] * p.page_size + (ts & (p.page_size - 1)) : (size_t)ts;
+      const size_t off = row0 * row_bytes;
+      voff_lo = (uint32_t)off;
+      voff_hi = (uint32_t)(off >> 32);
+      vbytes = (uint32_t)(min(kTile, wg_hi - ts) * (int)row_bytes);
+    }
+  }
+  const char *kpool = reinterpret_cast<const char *>(p.k);
+  const char *vpool = reinterpret_cast<const char *>(p.v);
+  int dma_voff[S::kDma]; // lane's byte offset within a tile, per DMA load
+#pragma unroll
+  for (int k = 0; k < S::kDma; ++k) {
+    const int r = k * S::kRowsPerDma + lane / S::kPieces;
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<D, KT>(r);
+    dma_voff[k] = r * (int)row_bytes + kvg * S::kRowBytes + piece * 16; // < 2^31: checked on the host
+  }
+  // tile u of slot s sits at smem + (s * kWaves + u) * 2 * kTileBytes (K, then V)
+  auto issue = [&](int i, int slot) {
+    const int li = min(i, 63);
+    const size_t base = ((size_t)__builtin_amdgcn_readlane(voff_hi, li) << 32) | __builtin_amdgcn_readlane(voff_lo, li);
+    const int nbytes = i < nblocks ? (int)__builtin_amdgcn_readlane(vbytes, li) : 0;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
+    char *kst = smem + (slot * kWaves + wave) * 2 * S::kTileBytes;
+    char *vst = kst + S::kTileBytes;
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, vst + 1024 * k, dma_voff[k]);
+  };
+  uint32_t stage_addr[S::kLaneVec]; // LDS address of piece pc of tile 0 of slot 0
+  {
+    const uint32_t base = lds_address(smem) + c16 * S::kRowBytes;
+    const int swz = stage_swizzle<D, KT>(c16);
+#pragma unroll
+    for (int pc = 0; pc < S::kLaneVec; ++pc) stage_addr[pc] = base + ((4 * pc + q4) ^ swz) * 16;
+  }
+  auto read_stage = [&](TileRegs<D, KT> &t, int slot, int u) {
+    const uint32_t so = (slot * kWaves + u) * 2 * S::kTileBytes;
+    if constexpr (S::kLaneVec == 1) {
+      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], stage_addr[0] + so);
+    } else {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2)
+        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], stage_addr[pc] + so,
+                                    stage_addr[pc + 1] + so);
+    }
+  };
+
+  // ---- ring of NBUF block slots shared by the waves ----
+  if (nblocks > 0) { // the same in every wave
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) issue(j, j);
+    const int n_iter = (nblocks + NBUF - 1) / NBUF * NBUF;
+    for (int it = 0; it < n_iter; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int i = it + j;
+        wait_vmem<(NBUF - 1) * 2 * S::kDma>(); // this wave's tile of block i has landed
+        __syncthreads();                       // ... and every other wave's
+        if (i < nblocks) {
+#pragma unroll
+          for (int u = 0; u < kWaves; ++u) {
+            const int ts = k0 + i * kBlock + u * kTile;
+            if (ts < wv_hi && ts + kTile > wv_lo) { // the wave's columns see keys of this tile
+              TileRegs<D, KT> t;
+              read_stage(t, j, u);
+              if (ts < wv_lo) { // rows before the wave's first key hold keys of no interest
+                const bool ok = ts + c16 >= wv_lo;
+#pragma unroll
+                for (int k = 0; k < S::kLaneVec; ++k)
+                  if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+              }
+              tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+            }
+          }
+        }
+        __syncthreads(); // every wave has read slot j
+        issue(i + NBUF, j);
+      }
+    }
+    wait_vmem<0>(); // no DMA may land in LDS after the workgroup ends
+  }
+
+  // ---- results of this wave's columns: final output, or the split's partial ----
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (!cs.on[c]) continue; // the same in every lane of the wave
+    float l_tot = cs.l[c] + __shfl_xor(cs.l[c], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    float lb_tot = 0.0f;
+    if constexpr (KT == DT_INT4) {
+      lb_tot = cs.lb[c] + __shfl_xor(cs.lb[c], 16, 64);
+      lb_tot += __shfl_xor(lb_tot, 32, 64);
+    }
+    if (!cs.ok[c]) continue;
+    const bool live = l_tot > 0.0f; // a finite reference with no visible key leaves l = 0: empty
+    const float vscale = p.v_scale ? p.v_scale[b * Hk + kvg] : 1.0f;
+    const float inv = live ? vscale / l_tot : 0.0f;
+    const float lse2 = live ? cs.m[c] + __log2f(l_tot) : -INFINITY;
+    // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
+    const float voff = kInt4Offset * lb_tot;
+    if (nb == 1) {
+      const size_t rowoff = ((size_t)cs.row[c] * p.num_qo_heads + cs.head[c]) * D;
+#pragma unroll
+      for (int wt = 0; wt < S::kOTiles; ++wt) {
+        const int od = out_dim<D, KT>(wt, q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float val = (cs.acc[c][wt][r] - voff) * inv;
+          const size_t off = rowoff + od + r * S::kOutStride;
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t *>(p.o)[off] = f32_to_bf16_bits(val);
+          else
+            reinterpret_cast<float *>(p.o)[off] = val;
+        }
+      }
+      if (q4 == 0 && p.lse) p.lse[(size_t)cs.row[c] * p.num_qo_heads + cs.head[c]] = lse2 * kLn2;
+    } else {
+      const int cg = cgw + wave * CG + c;
+      const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
+      float *dst = p.o_part + (slot * p.cols + c16) * D;
+#pragma unroll
+      for (int wt = 0; wt < S::kOTiles; ++wt) {
+        const int od = out_dim<D, KT>(wt, q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[od + r * S::kOutStride] = (cs.acc[c][wt][r] - voff) * inv;
+      }
+      if (q4 == 0) p.lse_part[slot * p.cols + c16] = lse2;
+    }
+  }
+}
+
 } // namespace
+
+// Column groups one wave of the shared-tile kernel computes: two for
+// head_dim <= 128; head_dim 256 keeps one, its accumulators would not fit in
+// registers twice.
+template <int D>
+constexpr int rows_cg() { return D <= 128 ? 2 : 1; }
+
+// Block slots of the shared-tile kernel: about 64 KB of LDS per workgroup
+// (two workgroups per CU), two to four slots.
+template <int D, int KT>
+constexpr int rows_nbuf() {
+  constexpr int slot = kWaves * 2 * Shape<D, KT>::kTileBytes;
+  return 65536 / slot < 2 ? 2 : (65536 / slot > 4 ? 4 : 65536 / slot);
+}
 
 template <int D, int PACK, int KT>
 static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
   constexpr int NB = Shape<D * PACK, KT>::kNBuf;
-  if constexpr (PACK == 1 && D <= 128) {
-    if (p.col_share == 2)
-      return launch_kernel(l, partial_mfma_kernel<D, 1, KT, NB, 2>,
-                           dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
+  if constexpr (PACK == 1) {
+    constexpr int kGroups = kWaves * rows_cg<D>();
+    if (p.col_share == kGroups)
+      return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>,
+                           dim3(p.items, p.num_kv_heads * ((p.col_groups + kGroups - 1) / kGroups)), p, w);
+    if constexpr (D <= 128) {
+      if (p.col_share == 2)
+        return launch_kernel(l, partial_mfma_kernel<D, 1, KT, NB, 2>,
+                             dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
+    }
   }
   if (p.col_share != 1) return hipErrorInvalidValue;
   return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB, 1>,
                        dim3(p.items, p.num_kv_heads / PACK * p.col_groups), p, w);
 }
 
-// Column groups of (query row, head) pairs one workgroup computes on each
-// staged tile (several query rows per request): two halve the K/V reads of
-// longer appends; head_dim 256 keeps one, its accumulators would not fit in
-// registers twice.
-int mfma_col_share(int head_dim, int col_groups) { return col_groups >= 2 && head_dim <= 128 ? 2 : 1; }
+// Column groups from which several query rows per request go to the
+// shared-tile kernel.
+constexpr int kRowsMinGroups = 3;
+
+// Column groups of (query row, head) pairs one partial workgroup computes
+// (several query rows per request).  Two: the chunk-splitting kernel runs
+// both on each staged tile (head_dim <= 128), halving the K/V reads of short
+// appends.  From three groups on: the shared-tile kernel, whose workgroup
+// covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
+// all of them.
+int mfma_col_share(int head_dim, int col_groups) {
+  if (col_groups >= kRowsMinGroups) return kWaves * (head_dim <= 128 ? 2 : 1);
+  return col_groups >= 2 && head_dim <= 128 ? 2 : 1;
+}
 
 // KV heads per workgroup.  Two heads per pack would make every staged row at
 // least 256 contiguous bytes for fp8 head_dim 128 (128-byte segments stream

@@ -96,3 +96,40 @@ def test_speculative_append_full_batch_sampled():
     o_ref, lse_ref = oracle.attention_reference(inp, requests=reqs)
     rows = np.concatenate([np.arange(inp.qo_indptr[b], inp.qo_indptr[b + 1]) for b in reqs])
     compare(o[rows], lse[rows], o_ref[rows], lse_ref[rows], "bf16")
+
+
+@pytest.mark.parametrize("chunk", [0, 16, 64, 1024])
+def test_shared_tile_kernel_split_requests(chunk):
+    """3 to 4 column groups per KV head (12 and 16 rows, 4 heads per KV
+    head): the shared-tile kernel, with requests split over several chunks
+    and merged, next to a one-row and an empty request."""
+    print(f"case multi shared-tile chunk={chunk}", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=4, lengths=("list", [20, 300, 1000, 2049]),
+                         q_len=("list", [12, 1, 16, 0]))
+    _check(make_inputs(spec, poison=True), kv_chunk=chunk)
+
+
+@pytest.mark.parametrize("name", ["c5_paged_fp8_b128", "c6_paged_int4_b128", "c2_gemma3_1b"])
+def test_shared_tile_kernel_kv_types_and_head_dims(name):
+    print(f"case multi shared-tile {name}", flush=True)
+    if name == "c2_gemma3_1b":  # head_dim 256: one column group per wave
+        spec = small_variant(name, lengths=("fixed", 700), q_len=("fixed", 100))
+        _check(make_inputs(spec), kv_chunk=128)
+    else:
+        spec = small_variant(name, batch=3, lengths=("list", [40, 700, 1500]), q_len=("list", [40, 9, 33]))
+        _check(make_inputs(spec, poison=True), kv_chunk=256)
+
+
+def test_shared_tile_long_prefill_sampled():
+    """A fresh 2048-token MHA prefill (128 column groups per head) against
+    the oracle on sampled rows: the first, a middle one and the last rows
+    of several 128-column workgroups."""
+    print("case multi shared-tile prefill 2048", flush=True)
+    spec = small_variant("c3_llama2_7b_32k", lengths=("fixed", 2048), q_len=("fixed", 2048))
+    inp = make_inputs(spec)
+    o, lse = run_library(inp)
+    # each sampled row r sees keys 0 .. r: decode over the first r + 1 tokens
+    for r in [0, 1, 15, 127, 128, 1000, 1023, 2046, 2047]:
+        one = dataclasses.replace(inp, q=inp.q[r:r + 1], qo_indptr=None, kv_len=np.array([r + 1], np.int32))
+        o_ref, lse_ref = oracle.decode_reference(one)
+        compare(o[r:r + 1], lse[r:r + 1], o_ref, lse_ref, "bf16")
