@@ -18,7 +18,7 @@ hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_di
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack);
-int mfma_col_share(int head_dim, int col_groups);
+int mfma_col_share(int head_dim, int kv_type, int col_groups);
 bool mfma_head_dim_ok(int head_dim, int kv_type);
 hipError_t launch_append(const kvs_append_args *a, const Launch &l);
 } // namespace kvs
@@ -177,7 +177,7 @@ Columns columns_of(const kvs_decode_args *a) {
     most = std::max(most, c.nq[b]);
   }
   c.col_groups = std::max(1, (int)(((int64_t)most * group + 15) / 16));
-  c.col_share = kvs::mfma_col_share(a->head_dim, c.col_groups);
+  c.col_share = kvs::mfma_col_share(a->head_dim, a->kv_dtype, c.col_groups);
   c.col_blocks = (c.col_groups + c.col_share - 1) / c.col_share;
   c.cols = c.col_groups * 16;
   return c;

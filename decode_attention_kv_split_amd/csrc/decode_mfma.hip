@@ -993,8 +993,13 @@ static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Laun
 }
 
 // Column groups from which several query rows per request go to the
-// shared-tile kernel.
-constexpr int kRowsMinGroups = 3;
+// shared-tile kernel.  Below 8 groups some of its waves idle; that pays for
+// bf16, whose second read of the keys costs more than the idle waves, from 3
+// groups on, but for the compute-heavier fp8 and INT4 tiles only once three
+// of the four waves have work (batch-128 fp8, 8 rows of 8 heads = 4 groups:
+// 656 us with the chunk-splitting kernel, 980 us shared-tile).
+constexpr int kRowsMinGroupsBf16 = 3;
+constexpr int kRowsMinGroupsQuant = 5;
 
 // Column groups of (query row, head) pairs one partial workgroup computes
 // (several query rows per request).  Two: the chunk-splitting kernel runs
@@ -1002,8 +1007,9 @@ constexpr int kRowsMinGroups = 3;
 // appends.  From three groups on: the shared-tile kernel, whose workgroup
 // covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
 // all of them.
-int mfma_col_share(int head_dim, int col_groups) {
-  if (col_groups >= kRowsMinGroups) return kWaves * (head_dim <= 128 ? 2 : 1);
+int mfma_col_share(int head_dim, int kv_type, int col_groups) {
+  if (col_groups >= (kv_type == DT_BF16 ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
+    return kWaves * (head_dim <= 128 ? 2 : 1);
   return col_groups >= 2 && head_dim <= 128 ? 2 : 1;
 }
 
