@@ -158,11 +158,18 @@ struct TileRegs {
   uint4 v[Shape<DE, KT>::kLaneVec];
 };
 
+// Max of x over lanes l and l ^ 16 (l ^ 32) with gfx950's lane swaps: swapping
+// the odd 16-lane rows of one copy of x with the even rows of another (the
+// upper 32 lanes of one with the lower 32 of the other) leaves each lane the
+// two values whose max it needs.  VALU instructions, where a lane shuffle
+// would go through the LDS unit and wait for it.
 __device__ __forceinline__ float xor16_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 16, 64));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // 8 consecutive fp8 codes (two dwords) -> 8 bf16 (exact).
