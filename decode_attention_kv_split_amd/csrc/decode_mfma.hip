@@ -421,80 +421,107 @@ __device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Pa
   }
 }
 
-// One staged 16-token tile (first key ts) through every column group:
-// S^T = K . Q^T, per-key masks where some column misses some key of the tile,
-// the soft-cap, the online softmax with a lazy rescale, then O^T += V^T . P^T
-// with the V^T slices shared by the groups.  ident / sel: the identity and
-// 0/1 selection operands of the V transposition.
-template <int DE, int KT, int CG>
-__device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &t, int ts, int all_lo,
-                                            int all_hi, float cscale, float cap_out, s16x4_t ident,
-                                            const long (&sel)[2], int q4) {
-  using S = Shape<DE, KT>;
-  s16x4_t pt[CG]; // P^T operand of each group
+// Zero the V rows of a staged tile (first key ts) that lie before key lo:
+// they hold keys no column of the wave sees, whose weight is 0, and a
+// non-finite value there must not reach the P.V product.
+template <int DE, int KT>
+__device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16) {
+  if (ts < lo) {
+    const bool ok = ts + c16 >= lo;
 #pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    if (c > 0 && !cs.on[c]) continue; // the same in every lane
-    // S^T = K . Q^T
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < S::kKSteps; ++j)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), cs.q[c][j], s, 0, 0, 0);
-    if constexpr (KT == DT_INT4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] -= cs.qoff[c]; // remove the 136-per-element offset of K
-    }
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
-    if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
-    }
-    if (ts < all_lo || ts + kTile > all_hi) { // some column misses some key of the tile (uniform branch)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = ts + 4 * q4 + r;
-        if (tok < cs.lo[c] || tok >= cs.hi[c]) sv[r] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = xor32_max(xor16_max(mx));
-    // Lazy rescale: the reference max m moves (and the state is rescaled
-    // by 2^(m - m_new)) only when a score exceeds it by more than kLazy,
-    // so weights stay below 2^kLazy and after the first tiles the rescale is
-    // almost never needed.  m + log2(l) and acc / l do not depend on which
-    // reference is used.
-    // m = -inf: any visible key grows it.  A given starting reference
-    // (unified max) far above a still-empty state's first scores is moved
-    // down to them, so no weight underflows.
-    const bool empty = cs.l[c] == 0.0f;
-    const bool grow = mx > cs.m[c] + kLazy || (empty && mx != -INFINITY && mx < cs.m[c] - kDrop);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(cs.m[c] - mx)) : 1.0f;
-      cs.m[c] = grow ? mx : cs.m[c];
-      cs.l[c] *= alpha;
-      if constexpr (KT == DT_INT4) cs.lb[c] *= alpha;
-#pragma unroll
-      for (int w = 0; w < S::kOTiles; ++w) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cs.acc[c][w][r] *= alpha;
-      }
-    }
-    // no visible key so far for this column: weights 0, state unchanged
-    const bool live = cs.m[c] != -INFINITY;
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - cs.m[c]) : 0.0f;
-    cs.l[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-    pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-    if constexpr (KT == DT_INT4)
-      cs.lb[c] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-                   (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+    for (int k = 0; k < Shape<DE, KT>::kLaneVec; ++k)
+      if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
   }
-  // V^T slices (all products first, so the dependent conversions and
-  // accumulations below do not wait on each other), then O^T += V^T . P^T
+}
+
+// Scaled scores of one staged 16-token tile (first key ts) for column group c:
+// lane (c16, q4) gets keys ts + 4 * q4 + r (r = 0..3) of its column in log2
+// units, soft-capped, and -inf where the column does not see the key (only
+// tested when the tile is not seen whole by every column).
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void tile_scores(const ColumnSet<DE, KT, CG> &cs, int c, const TileRegs<DE, KT> &t, int ts,
+                                            bool whole, float cscale, float cap_out, int q4, float *sv) {
+  using S = Shape<DE, KT>;
+  // S^T = K . Q^T
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < S::kKSteps; ++j)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), cs.q[c][j], s, 0, 0, 0);
+  if constexpr (KT == DT_INT4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] -= cs.qoff[c]; // remove the 136-per-element offset of K
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+  if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
+  }
+  if (!whole) { // some column misses some key of the tile (uniform branch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = ts + 4 * q4 + r;
+      if (tok < cs.lo[c] || tok >= cs.hi[c]) sv[r] = -INFINITY;
+    }
+  }
+}
+
+// Online-softmax step of column group c over NS new scores per lane: the
+// weights, bf16-packed in pairs into pk[NS / 2], and the running state.
+template <int NS, int DE, int KT, int CG>
+__device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, const float *sv, uint32_t *pk) {
+  using S = Shape<DE, KT>;
+  float mx = sv[0];
+#pragma unroll
+  for (int r = 1; r < NS; ++r) mx = fmaxf(mx, sv[r]);
+  mx = xor32_max(xor16_max(mx));
+  // Lazy rescale: the reference max m moves (and the state is rescaled by
+  // 2^(m - m_new)) only when a score exceeds it by more than kLazy, so
+  // weights stay below 2^kLazy and after the first tiles the rescale is
+  // almost never needed.  m + log2(l) and acc / l do not depend on which
+  // reference is used.
+  // m = -inf: any visible key grows it.  A given starting reference (unified
+  // max) far above a still-empty state's first scores is moved down to
+  // them, so no weight underflows.
+  const bool empty = cs.l[c] == 0.0f;
+  const bool grow = mx > cs.m[c] + kLazy || (empty && mx != -INFINITY && mx < cs.m[c] - kDrop);
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(cs.m[c] - mx)) : 1.0f;
+    cs.m[c] = grow ? mx : cs.m[c];
+    cs.l[c] *= alpha;
+    if constexpr (KT == DT_INT4) cs.lb[c] *= alpha;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs.acc[c][w][r] *= alpha;
+    }
+  }
+  // no visible key so far for this column: weights 0, state unchanged
+  const bool live = cs.m[c] != -INFINITY;
+  float pr[NS];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - cs.m[c]) : 0.0f;
+  float sum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NS; r += 4) sum += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+  cs.l[c] += sum;
+#pragma unroll
+  for (int r = 0; r < NS; r += 2) pk[r / 2] = pack_bf16x2(pr[r], pr[r + 1]);
+  if constexpr (KT == DT_INT4) {
+    float sb = 0.0f; // the weights as the P.V product sees them
+#pragma unroll
+    for (int r = 0; r < NS / 2; ++r) sb += __uint_as_float(pk[r] << 16) + __uint_as_float(pk[r] & 0xFFFF0000u);
+    cs.lb[c] += sb;
+  }
+}
+
+// V^T slices of a staged tile as bf16 operands: va[w] holds, in lane
+// (c16, q4), keys 4 * q4 + r of dimension c16 of the 16-dim slice w.
+template <int DE, int KT>
+__device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, const long (&sel)[2],
+                                         s16x4_t *va) {
+  using S = Shape<DE, KT>;
+  // all products first, so the dependent conversions do not wait on each other
   f32x4_t vt[S::kOTiles];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -518,16 +545,79 @@ __device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const Til
       vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
     }
   }
-  s16x4_t va[S::kOTiles];
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w)
     va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
+}
+
+// One staged 16-token tile (first key ts) through every column group:
+// scores, online-softmax step, then O^T += V^T . P^T with the V^T slices
+// shared by the groups.  [all_lo, all_hi): keys every column sees.
+// ident / sel: the identity and 0/1 selection operands of the V transposition.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &t, int ts, int all_lo,
+                                            int all_hi, float cscale, float cap_out, s16x4_t ident,
+                                            const long (&sel)[2], int q4) {
+  using S = Shape<DE, KT>;
+  const bool whole = ts >= all_lo && ts + kTile <= all_hi;
+  s16x4_t pt[CG]; // P^T operand of each group
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue; // the same in every lane
+    float sv[4];
+    tile_scores(cs, c, t, ts, whole, cscale, cap_out, q4, sv);
+    uint32_t pk[2];
+    softmax_step<4>(cs, c, sv, pk);
+    pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(pk[0], pk[1]));
+  }
+  s16x4_t va[S::kOTiles];
+  v_slices(t, ident, sel, va);
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     if (c > 0 && !cs.on[c]) continue;
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w)
       cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt[c], cs.acc[c][w], 0, 0, 0);
+  }
+}
+
+// Two staged tiles (first keys tsa, tsb) at once: one softmax step over the
+// 32 keys and one O^T += V^T . P^T product per 16-dim slice with k = 32
+// (v_mfma_f32_16x16x32_bf16, twice the work of the 16x16x16 form per
+// instruction).  Lane quarter q4 feeds reduction indices 8 q4 .. 8 q4 + 7 of
+// both operands as keys 4 q4 .. 4 q4 + 3 of the first tile, then the same
+// keys of the second, so V^T and P^T agree on the key of every index.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &ta, int tsa,
+                                            const TileRegs<DE, KT> &tb, int tsb, int all_lo, int all_hi,
+                                            float cscale, float cap_out, s16x4_t ident, const long (&sel)[2],
+                                            int q4) {
+  using S = Shape<DE, KT>;
+  const bool whole_a = tsa >= all_lo && tsa + kTile <= all_hi;
+  const bool whole_b = tsb >= all_lo && tsb + kTile <= all_hi;
+  bf16x8_t pt[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue; // the same in every lane
+    float sv[8];
+    tile_scores(cs, c, ta, tsa, whole_a, cscale, cap_out, q4, sv);
+    tile_scores(cs, c, tb, tsb, whole_b, cscale, cap_out, q4, sv + 4);
+    uint32_t pk[4];
+    softmax_step<8>(cs, c, sv, pk);
+    pt[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  }
+  s16x4_t va[S::kOTiles], vb[S::kOTiles];
+  v_slices(ta, ident, sel, va);
+  v_slices(tb, ident, sel, vb);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) {
+      const uint2 a = __builtin_bit_cast(uint2, va[w]), bv = __builtin_bit_cast(uint2, vb[w]);
+      const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, bv.x, bv.y));
+      cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pt[c], cs.acc[c][w], 0, 0, 0);
+    }
   }
 }
 
@@ -680,12 +770,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (ft + wave + i * kWaves) * kTile;
-    if (ts < w_lo) { // rows before the first key any column sees hold keys of no interest
-      const bool ok = ts + c16 >= w_lo;
-#pragma unroll
-      for (int k = 0; k < S::kLaneVec; ++k)
-        if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
-    }
+    zero_v_before(t, ts, w_lo, c16); // rows before the first key any column sees
     tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
   };
 
@@ -770,6 +855,12 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
   constexpr int kGroups = kWaves * CG;                   // column groups per workgroup
   constexpr int kBlock = kWaves * kTile;                 // keys per staged block
   constexpr int kSlotBytes = kWaves * 2 * S::kTileBytes; // K and V of a block
+  // Tiles two at a time (pair_update) only where one column group per wave
+  // leaves the registers for a second tile: with two groups (head_dim <= 128)
+  // the pair form reached the register limit and ran slower (a 32k-token MHA
+  // cache with 2048 new rows: 359 against 493 TFLOP/s), with one (head_dim
+  // 256) it ran faster (8192-row prefill: 162 against 147 TFLOP/s).
+  constexpr bool kPairs = CG == 1;
 
   __shared__ int s_scan[2 * 64];
   __shared__ int s_item[4];
@@ -892,19 +983,31 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
         wait_vmem<(NBUF - 1) * 2 * S::kDma>(); // this wave's tile of block i has landed
         __syncthreads();                       // ... and every other wave's
         if (i < nblocks) {
+          if constexpr (kPairs) {
+            // the block's tiles two at a time: one softmax step and one
+            // k = 32 product per pair
 #pragma unroll
-          for (int u = 0; u < kWaves; ++u) {
-            const int ts = k0 + i * kBlock + u * kTile;
-            if (ts < wv_hi && ts + kTile > wv_lo) { // the wave's columns see keys of this tile
-              TileRegs<D, KT> t;
-              read_stage(t, j, u);
-              if (ts < wv_lo) { // rows before the wave's first key hold keys of no interest
-                const bool ok = ts + c16 >= wv_lo;
-#pragma unroll
-                for (int k = 0; k < S::kLaneVec; ++k)
-                  if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < kWaves; u += 2) {
+              const int tsa = k0 + i * kBlock + u * kTile, tsb = tsa + kTile;
+              if (tsa < wv_hi && tsb + kTile > wv_lo) { // the wave's columns see keys of this pair
+                TileRegs<D, KT> ta, tb;
+                read_stage(ta, j, u);
+                read_stage(tb, j, u + 1);
+                zero_v_before(ta, tsa, wv_lo, c16);
+                zero_v_before(tb, tsb, wv_lo, c16);
+                pair_update(cs, ta, tsa, tb, tsb, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
               }
-              tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < kWaves; ++u) {
+              const int ts = k0 + i * kBlock + u * kTile;
+              if (ts < wv_hi && ts + kTile > wv_lo) { // the wave's columns see keys of this tile
+                TileRegs<D, KT> t;
+                read_stage(t, j, u);
+                zero_v_before(t, ts, wv_lo, c16);
+                tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+              }
             }
           }
         }
