@@ -43,11 +43,11 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299473045, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
+        {"bytes": 2299468655, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487903115, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
+        {"bytes": 1487904166, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538227053, "digest": "4bbdefcd5eb2bc66689dc1d048100c31eba44e6d4aa3d303ea7670d631986636"},
+        {"bytes": 538222930, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
 }
 
 
