@@ -133,3 +133,44 @@ def test_shared_tile_long_prefill_sampled():
         one = dataclasses.replace(inp, q=inp.q[r:r + 1], qo_indptr=None, kv_len=np.array([r + 1], np.int32))
         o_ref, lse_ref = oracle.decode_reference(one)
         compare(o[r:r + 1], lse[r:r + 1], o_ref, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("q_len", [("uniform", 0, 3), ("uniform", 2, 12)])
+def test_rows_large_batch_device_planned(q_len):
+    """300 requests: the work list comes from kv_len on the device (scan),
+    with 0-3 rows (the decode kernel) or 2-12 rows per request (the
+    shared-tile kernel, up to 3 groups of 16 at 4 heads per KV head)."""
+    print(f"case multi large batch {q_len}", flush=True)
+    spec = DecodeSpec("bigrows", 300, 8, 2, 128, 16, "bf16", "bf16", 0.1, lengths=("uniform", 12, 700),
+                      q_len=q_len, seed=41)
+    inp = make_inputs(spec, poison=True)
+    for chunk in (0, 64):
+        _check(inp, kv_chunk=chunk)
+
+
+def test_rows_many_items_device_planned():
+    """More than 448 work items per KV head (16-token chunks of an 8192-key
+    request) with 40 and 3 new rows."""
+    print("case multi many items", flush=True)
+    spec = DecodeSpec("itemsrows", 2, 8, 2, 128, 16, "bf16", "bf16", 0.1, lengths=("list", [8192, 300]),
+                      q_len=("list", [40, 3]), seed=42)
+    _check(make_inputs(spec, poison=True), kv_chunk=16)
+
+
+@pytest.mark.parametrize("P", [32, 64])
+@pytest.mark.parametrize("rows", [[3, 1, 5], [20, 9, 33]])
+def test_rows_page_sizes(P, rows):
+    print(f"case multi page {P} rows {rows}", flush=True)
+    spec = DecodeSpec("pagesrows", 3, 8, 2, 128, P, "bf16", "bf16", 0.1, lengths=("list", [40, 900, 2000]),
+                      q_len=("list", rows), seed=P + rows[0])
+    _check(make_inputs(spec, poison=True))
+
+
+@pytest.mark.parametrize("W", [1, 17, 64, 300])
+def test_rows_window_fp8_shared_tile(W):
+    """fp8 with 8 heads per KV head and 20-40 rows (the shared-tile kernel)
+    under a sliding window."""
+    print(f"case multi window fp8 {W}", flush=True)
+    spec = dataclasses.replace(small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [40, 700, 1500]),
+                                             q_len=("list", [40, 20, 33])), window=W)
+    _check(make_inputs(spec, poison=True))
