@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 6
+KVS_ABI_VERSION = 7
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
@@ -96,6 +96,7 @@ class KvsPlanInfo(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("col_groups", ctypes.c_int32),
+        ("col_share", ctypes.c_int32),
     ]
 
 

@@ -18,6 +18,7 @@ hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_di
 hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack);
+bool mfma_packable(int head_dim, int group, int num_kv_heads, int kv_type);
 int mfma_col_share(int head_dim, int kv_type, int col_groups);
 bool mfma_head_dim_ok(int head_dim, int kv_type);
 hipError_t launch_append(const kvs_append_args *a, const Launch &l);
@@ -93,7 +94,10 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   switch (a->algo) {
   case KVS_ALGO_AUTO:
     if (mfma_ok)
-      *algo = KVS_ALGO_MFMA;
+      *algo = a->kv_dtype == KVS_INT4 && !multi &&
+                      kvs::mfma_packable(a->head_dim, group, a->num_kv_heads, a->kv_dtype)
+                  ? KVS_ALGO_MFMA_PACKED
+                  : KVS_ALGO_MFMA;
     else if (valu_ok)
       *algo = KVS_ALGO_VALU;
     else
@@ -217,7 +221,9 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   out->algo = algo;
   out->num_cus = cus;
   out->workspace_bytes = pl.workspace_bytes;
-  out->col_groups = columns_of(args).col_groups;
+  const Columns c = columns_of(args);
+  out->col_groups = c.col_groups;
+  out->col_share = c.col_share;
   return KVS_OK;
 }
 

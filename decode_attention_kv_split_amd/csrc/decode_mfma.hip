@@ -1128,12 +1128,17 @@ int mfma_col_share(int head_dim, int kv_type, int col_groups) {
 // about 12% slower), but a packed tile then fills the LDS budget of two
 // staging slots per wave, and on MI355X that lost more than the longer rows
 // gained (batch-128 fp8 decode: 311 us unpacked, 407-424 us packed).  So the
-// default is one head per workgroup; KVS_ALGO_MFMA_PACKED asks for packs
-// (not for INT4).
+// default is one head per workgroup; KVS_ALGO_MFMA_PACKED asks for packs.
+// INT4 head_dim 128 is different: one head's row is 64 bytes, half a
+// 128-byte line, so unpacked each line reaches the chip once per head (the
+// batch-128 INT4 step fetched 2.01x its bytes), and a packed INT4 tile still
+// fits three staging slots per wave.
+bool mfma_packable(int head_dim, int group, int num_kv_heads, int kv_type) {
+  const bool seg_ok = kv_type == DT_INT4 ? head_dim == 128 : head_dim * (kv_type == DT_FP8 ? 1 : 2) < 256;
+  return seg_ok && 2 * group <= 16 && num_kv_heads % 2 == 0;
+}
 int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack) {
-  if (kv_type == DT_INT4) return 1;
-  const int seg = head_dim * (kv_type == DT_FP8 ? 1 : 2);
-  return (allow_pack && seg < 256 && 2 * group <= 16 && num_kv_heads % 2 == 0) ? 2 : 1;
+  return allow_pack && mfma_packable(head_dim, group, num_kv_heads, kv_type) ? 2 : 1;
 }
 
 // Which head sizes the matrix-core kernel takes for a KV type (INT4 rows must
@@ -1146,8 +1151,8 @@ bool mfma_head_dim_ok(int head_dim, int kv_type) {
 hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
   const bool pack2 = p.pack == 2;
   if (kv_type == DT_INT4) {
+    if (head_dim == 128) return pack2 ? launch_mfma_d<128, 2, DT_INT4>(p, w, l) : launch_mfma_d<128, 1, DT_INT4>(p, w, l);
     if (pack2) return hipErrorInvalidValue;
-    if (head_dim == 128) return launch_mfma_d<128, 1, DT_INT4>(p, w, l);
     if (head_dim == 256) return launch_mfma_d<256, 1, DT_INT4>(p, w, l);
     return hipErrorInvalidValue;
   }

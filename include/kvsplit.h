@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 6
+#define KVS_ABI_VERSION 7
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -75,13 +75,15 @@ typedef enum {
  * needs head_dim 128 or 256 and the matrix-core kernel (kvs_decode only). */
 typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_FP8_E4M3 = 2, KVS_INT4 = 3 } kvs_dtype;
 
-/* Kernel family for the per-chunk partial softmax.  AUTO picks MFMA for bf16
- * and fp8 KV with page_size 0 or >= 16 (query group packed into the columns
- * of 16x16 matrix tiles) and VALU otherwise (fp32 KV, small pages: one KV
- * row per 4..64 lanes, fp32 FMA).  MFMA_PACKED is the matrix-core kernel with
+/* Kernel family for the per-chunk partial softmax.  AUTO picks MFMA for bf16,
+ * fp8 and INT4 KV with page_size 0 or >= 16 (query group packed into the
+ * columns of 16x16 matrix tiles) and VALU otherwise (fp32 KV, small pages:
+ * one KV row per 4..64 lanes, fp32 FMA); for INT4 head_dim 128 with one query
+ * per request it picks MFMA_PACKED where that applies (a 64-byte INT4 head
+ * row is half a 128-byte line).  MFMA_PACKED is the matrix-core kernel with
  * two adjacent KV heads per workgroup when 2 * group <= 16, the head count is
  * even and one head's row is shorter than 256 bytes (fp8 head_dim 128,
- * head_dim 64); otherwise it is MFMA. */
+ * head_dim 64, INT4 head_dim 128); otherwise it is MFMA. */
 typedef enum { KVS_ALGO_AUTO = 0, KVS_ALGO_VALU = 1, KVS_ALGO_MFMA = 2, KVS_ALGO_MFMA_PACKED = 3 } kvs_algo;
 
 typedef struct {
@@ -180,7 +182,11 @@ typedef struct {
   int32_t algo;              /* resolved kvs_algo (VALU, MFMA or MFMA_PACKED) */
   int32_t num_cus;           /* CU count the plan was made for */
   size_t workspace_bytes;    /* bytes kvs_decode needs for this plan */
-  int32_t col_groups;        /* workgroups per (item, KV head): 1 unless several queries per request */
+  int32_t col_groups;        /* groups of 16 (query row, head) columns per KV head: 1 unless
+                                several queries per request */
+  int32_t col_share;         /* column groups one partial workgroup computes: 1 (one query per
+                                request), 2, or 4 / 8 (several rows per request on the
+                                shared-tile kernel, partial_rows_kernel) */
 } kvs_plan_info;
 
 /* Plan a call without launching anything.  Makes no HIP call when

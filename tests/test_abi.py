@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 6
-    assert re.search(r"#define KVS_ABI_VERSION 6\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 7
+    assert re.search(r"#define KVS_ABI_VERSION 7\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -138,6 +138,15 @@ def test_query_row_checks(lib):
         return a, (keep, qo)
     a, keep = with_rows([0, 3, 10])                     # lens (100, 3000): fine
     assert kvs.kvs_decode_plan(a).col_groups == (7 * 4 + 15) // 16
+    assert kvs.kvs_decode_plan(a).col_share == 2   # two groups: the decode kernel runs both
+    a, keep = with_rows([0, 12, 20])                    # 12 rows x 4 heads: 3 groups
+    assert kvs.kvs_decode_plan(a).col_share == 8        # bf16: the shared-tile kernel, 8 groups a workgroup
+    a, keep = with_rows([0, 12, 20], kv=kvs.KVS_FP8_E4M3)
+    assert kvs.kvs_decode_plan(a).col_share == 2        # fp8 takes the shared-tile kernel from 5 groups
+    a, keep = with_rows([0, 20, 40], kv=kvs.KVS_FP8_E4M3)
+    assert kvs.kvs_decode_plan(a).col_share == 8
+    a, keep = with_rows([0, 12, 20], d=256)
+    assert kvs.kvs_decode_plan(a).col_share == 4        # head_dim 256: one group per wave
     for rows in ([1, 3, 10], [0, 5, 4], [0, 101, 200]):  # start, decrease, more than kv_len
         a, keep = with_rows(rows)
         assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG, rows
@@ -313,3 +322,20 @@ def test_append_null_pointers_rejected(lib):
     a = _append_args(kv=kvs.KVS_FP8_E4M3)
     a.v_scale = None
     assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_INVALID_ARG
+
+
+def test_int4_packs_two_heads_when_it_can(lib):
+    """AUTO resolves INT4 head_dim 128 with one query per request to the
+    two-heads-per-workgroup kernel (a 64-byte head row is half a line)."""
+    a, keep = _args(kv=kvs.KVS_INT4, ptrs=False)                 # 8 query / 2 KV heads
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA_PACKED
+    a, keep = _args(kv=kvs.KVS_INT4, Hq=32, Hk=2, ptrs=False)    # group 16: 32 columns do not fit
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+    a, keep = _args(kv=kvs.KVS_INT4, Hq=9, Hk=3, ptrs=False)     # odd KV head count
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+    a, keep = _args(kv=kvs.KVS_INT4, d=256, ptrs=False)          # 128-byte rows: whole lines already
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+    a, keep = _args(kv=kvs.KVS_INT4, algo=kvs.KVS_ALGO_MFMA, ptrs=False)  # asked for one head
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+    a, keep = _args(kv=kvs.KVS_FP8_E4M3, ptrs=False)             # fp8 stays unpacked by default
+    assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
