@@ -152,10 +152,106 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
                                            kKvLoadPolicy);
 }
 
+// bf16 tiles up to 128 pack dims take V^T straight from LDS (transposing
+// reads); wider ones, fp8 and INT4 transpose V with a matrix product.  At
+// head_dim 256 the transposed slices, read together with K, held registers
+// the pair-wise prefill kernel needed (8192-row prefill: 147 against 158
+// TFLOP/s); at head_dim 128 they gained (2048 rows on a 32k cache: 499
+// against 480 TFLOP/s), decode unchanged.
+template <int DE, int KT>
+constexpr bool vt_from_lds() { return KT == DT_BF16 && DE <= 128; }
+
 template <int DE, int KT>
 struct TileRegs {
-  uint4 k[Shape<DE, KT>::kLaneVec];
-  uint4 v[Shape<DE, KT>::kLaneVec];
+  uint4 k[Shape<DE, KT>::kLaneVec];    // K pieces 4 * pc + q4 of row c16
+  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (fp8, INT4)
+  s16x4_t vt[Shape<DE, KT>::kOTiles];  // V^T slices read transposed from LDS (vt_from_lds)
+};
+
+// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, lane i receives 16-bit element i % 4 of the 8 bytes addressed by
+// lane 4 r + i / 4, for r = 0..3.  Four V^T slices per block (two lane
+// addresses, each with a second slice 8 bytes further), waited for inside
+// the block like the other staged reads.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read_vt4(s16x4_t &v0, s16x4_t &v1, s16x4_t &v2, s16x4_t &v3, uint32_t a0,
+                                             uint32_t a1) {
+  u32x2_t r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                   "ds_read_b64_tr_b16 %1, %4 offset:8\n\t"
+                   "ds_read_b64_tr_b16 %2, %5\n\t"
+                   "ds_read_b64_tr_b16 %3, %5 offset:8\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(a0), "v"(a1)
+                   : "memory");
+  v0 = __builtin_bit_cast(s16x4_t, r0);
+  v1 = __builtin_bit_cast(s16x4_t, r1);
+  v2 = __builtin_bit_cast(s16x4_t, r2);
+  v3 = __builtin_bit_cast(s16x4_t, r3);
+}
+// K pieces only (two per block)
+__device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, uint32_t a1) {
+  u32x4_t r0, r1;
+  __asm__ volatile("ds_read_b128 %0, %2\n\t"
+                   "ds_read_b128 %1, %3\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1)
+                   : "v"(a0), "v"(a1)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, r0);
+  k1 = __builtin_bit_cast(uint4, r1);
+}
+
+// Lane addresses of a staged tile (K rows, then V rows kTileBytes further;
+// 16-byte pieces XOR-swizzled per row) and the reads that turn it into the
+// operand registers of lane (c16, q4).  K (and fp8 / INT4 V): pieces 4 pc + q4
+// of row c16.  bf16 V: V^T slice w straight from LDS with transposing reads;
+// lane 16 q4 + 4 r + c points at the four dims of slice w that output rows
+// 4 c .. 4 c + 3 hold (out_dim) in token row 4 q4 + r, so lane (i, q4) gets
+// keys 4 q4 .. 4 q4 + 3 of dim row i, the A-operand layout of the P.V product.
+template <int DE, int KT>
+struct StageReader {
+  using S = Shape<DE, KT>;
+  static constexpr bool kVt = vt_from_lds<DE, KT>();
+  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : 1;
+  uint32_t k_addr[S::kLaneVec];
+  uint32_t vt_addr[kVtAddr];
+  __device__ __forceinline__ void init(uint32_t tile0, int lane) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    const int swz = stage_swizzle<DE, KT>(c16);
+#pragma unroll
+    for (int pc = 0; pc < S::kLaneVec; ++pc)
+      k_addr[pc] = tile0 + c16 * S::kRowBytes + ((4 * pc + q4) ^ swz) * 16;
+    if constexpr (kVt) {
+      const int r = (lane >> 2) & 3, c = lane & 3;
+      const int row = 4 * q4 + r;
+      const int vswz = stage_swizzle<DE, KT>(row);
+#pragma unroll
+      for (int h = 0; h < kVtAddr; ++h) {
+        // slices 2 h and 2 h + 1: source piece 4 h + c, bytes 0 and 8 of it
+        vt_addr[h] = tile0 + S::kTileBytes + row * S::kRowBytes + ((4 * h + c) ^ vswz) * 16;
+      }
+    }
+  }
+  // t <- the tile whose K rows start `off` bytes after tile0 (reads complete on return)
+  __device__ __forceinline__ void read(TileRegs<DE, KT> &t, uint32_t off) const {
+    if constexpr (kVt) {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2) lds_read_k2(t.k[pc], t.k[pc + 1], k_addr[pc] + off, k_addr[pc + 1] + off);
+#pragma unroll
+      for (int h = 0; h < kVtAddr; h += 2)
+        lds_read_vt4(t.vt[2 * h], t.vt[2 * h + 1], t.vt[2 * h + 2], t.vt[2 * h + 3], vt_addr[h] + off,
+                     vt_addr[h + 1] + off);
+    } else if constexpr (S::kLaneVec == 1) {
+      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], k_addr[0] + off);
+    } else {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2)
+        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], k_addr[pc] + off,
+                                    k_addr[pc + 1] + off);
+    }
+  }
 };
 
 // Max of x over lanes l and l ^ 16 (l ^ 32) with gfx950's lane swaps: swapping
@@ -425,12 +521,20 @@ __device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Pa
 // they hold keys no column of the wave sees, whose weight is 0, and a
 // non-finite value there must not reach the P.V product.
 template <int DE, int KT>
-__device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16) {
+__device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16, int q4) {
   if (ts < lo) {
-    const bool ok = ts + c16 >= lo;
+    if constexpr (vt_from_lds<DE, KT>()) { // V^T: lane (c16, q4) holds keys ts + 4 q4 + e
 #pragma unroll
-    for (int k = 0; k < Shape<DE, KT>::kLaneVec; ++k)
-      if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+      for (int w = 0; w < Shape<DE, KT>::kOTiles; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ts + 4 * q4 + e < lo) t.vt[w][e] = 0;
+    } else { // V rows: lane (c16, q4) holds row c16
+      const bool ok = ts + c16 >= lo;
+#pragma unroll
+      for (int k = 0; k < Shape<DE, KT>::kLaneVec; ++k)
+        if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -521,6 +625,11 @@ template <int DE, int KT>
 __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, const long (&sel)[2],
                                          s16x4_t *va) {
   using S = Shape<DE, KT>;
+  if constexpr (vt_from_lds<DE, KT>()) { // read transposed from LDS already
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) va[w] = t.vt[w];
+    return;
+  }
   // all products first, so the dependent conversions do not wait on each other
   f32x4_t vt[S::kOTiles];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -749,28 +858,13 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   };
   // operand registers of a staged tile: lane (c16, q4) takes pieces 4*pc + q4
   // of row c16 (the same pieces the operand layout below expects)
-  uint32_t stage_addr[S::kLaneVec]; // LDS address of piece pc of the K tile in slot 0
-  {
-    const uint32_t base = lds_address(wave_stage) + c16 * S::kRowBytes;
-    const int swz = stage_swizzle<DE, KT>(c16);
-#pragma unroll
-    for (int pc = 0; pc < S::kLaneVec; ++pc) stage_addr[pc] = base + ((4 * pc + q4) ^ swz) * 16;
-  }
-  auto read_stage = [&](TileRegs<DE, KT> &t, int slot) {
-    const uint32_t so = slot * 2 * S::kTileBytes;
-    if constexpr (S::kLaneVec == 1) {
-      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], stage_addr[0] + so);
-    } else {
-#pragma unroll
-      for (int pc = 0; pc < S::kLaneVec; pc += 2)
-        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], stage_addr[pc] + so,
-                                    stage_addr[pc + 1] + so);
-    }
-  };
+  StageReader<DE, KT> stage; // lane addresses of the tile in slot 0
+  stage.init(lds_address(wave_stage), lane);
+  auto read_stage = [&](TileRegs<DE, KT> &t, int slot) { stage.read(t, slot * 2 * S::kTileBytes); };
 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (ft + wave + i * kWaves) * kTile;
-    zero_v_before(t, ts, w_lo, c16); // rows before the first key any column sees
+    zero_v_before(t, ts, w_lo, c16, q4); // rows before the first key any column sees
     tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
   };
 
@@ -952,23 +1046,10 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
 #pragma unroll
     for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, vst + 1024 * k, dma_voff[k]);
   };
-  uint32_t stage_addr[S::kLaneVec]; // LDS address of piece pc of tile 0 of slot 0
-  {
-    const uint32_t base = lds_address(smem) + c16 * S::kRowBytes;
-    const int swz = stage_swizzle<D, KT>(c16);
-#pragma unroll
-    for (int pc = 0; pc < S::kLaneVec; ++pc) stage_addr[pc] = base + ((4 * pc + q4) ^ swz) * 16;
-  }
+  StageReader<D, KT> stage; // lane addresses of tile 0 of slot 0
+  stage.init(lds_address(smem), lane);
   auto read_stage = [&](TileRegs<D, KT> &t, int slot, int u) {
-    const uint32_t so = (slot * kWaves + u) * 2 * S::kTileBytes;
-    if constexpr (S::kLaneVec == 1) {
-      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], stage_addr[0] + so);
-    } else {
-#pragma unroll
-      for (int pc = 0; pc < S::kLaneVec; pc += 2)
-        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], stage_addr[pc] + so,
-                                    stage_addr[pc + 1] + so);
-    }
+    stage.read(t, (slot * kWaves + u) * 2 * S::kTileBytes);
   };
 
   // ---- ring of NBUF block slots shared by the waves ----
@@ -993,8 +1074,8 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
                 TileRegs<D, KT> ta, tb;
                 read_stage(ta, j, u);
                 read_stage(tb, j, u + 1);
-                zero_v_before(ta, tsa, wv_lo, c16);
-                zero_v_before(tb, tsb, wv_lo, c16);
+                zero_v_before(ta, tsa, wv_lo, c16, q4);
+                zero_v_before(tb, tsb, wv_lo, c16, q4);
                 pair_update(cs, ta, tsa, tb, tsb, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
               }
             }
@@ -1005,7 +1086,7 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
               if (ts < wv_hi && ts + kTile > wv_lo) { // the wave's columns see keys of this tile
                 TileRegs<D, KT> t;
                 read_stage(t, j, u);
-                zero_v_before(t, ts, wv_lo, c16);
+                zero_v_before(t, ts, wv_lo, c16, q4);
                 tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
               }
             }
