@@ -43,11 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299468655, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
+        {"bytes": 2299464788, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487904166, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
+        {"bytes": 1487907700, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538222930, "digest": "dbc985f1d93caa5224eaa56e0276a1248322d0e383fe7ea4d4d249448f183101"},
+        {"bytes": 538218854, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
+    ("c6_paged_int4_b128", "partial_mfma_kernel"):
+        {"bytes": 680906590, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
 }
 
 
