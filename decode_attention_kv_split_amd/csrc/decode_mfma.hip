@@ -1,4 +1,4 @@
-// Split-KV partial softmax for bf16 / fp8-e4m3 KV on gfx950 matrix cores.
+// Split-KV partial softmax for bf16 / fp8-e4m3 / INT4 KV on gfx950 matrix cores.
 //
 // One workgroup (4 waves) owns one chunk of one (request, KV-head pack); wave
 // w takes the chunk's 16-token tiles w, w+4, w+8, ...  A pack is PACK
@@ -15,17 +15,20 @@
 //     the operand layout of a matrix whose rows are tokens and whose
 //     reduction index runs over the pack's head dimensions.
 //   * scores S^T[token][query head] = K . Q^T with v_mfma_f32_16x16x32_bf16
-//     (fp8 K converted to bf16 first, exactly); Q^T is block diagonal, query
-//     head c16 only sees the dims of its own KV head.  Lane ends up with
-//     tokens 4*q4 + r (r = 0..3) of query head c16.
+//     (fp8 K converted to bf16 first, exactly; INT4 K as 136 + n, the offset
+//     removed afterwards); Q^T is block diagonal, query head c16 only sees
+//     the dims of its own KV head.  Lane ends up with tokens 4*q4 + r
+//     (r = 0..3) of query head c16.
 //   * online softmax per query head in the log2 domain: tile max over the 16
-//     tokens (in-lane over r, then across the four quarters); the reference
-//     max moves, with a rescale of the running state, only when the tile max
-//     exceeds it by more than 8; weights p = exp2(s - reference), running sum.
-//   * V^T: multiplying the V tile by an identity (bf16, 16x16x16) or by a
-//     0/1 selection (fp8, 16x16x32 fp8) puts tokens 4*q4 + r of one head
-//     dimension in lane c16 -- the operand layout the next product needs --
-//     and, for fp8, decodes the codes exactly into fp32.
+//     tokens (in-lane over r, then across the four quarters with lane
+//     swaps); the reference max moves, with a rescale of the running state,
+//     only when the tile max exceeds it by more than 8; weights
+//     p = exp2(s - reference), running sum.
+//   * V^T with tokens 4*q4 + r of one head dimension in lane c16 -- the
+//     operand layout the next product needs: bf16 (pack width <= 128) reads
+//     it straight from LDS with transposing reads; otherwise the V tile is
+//     multiplied by an identity (bf16, INT4: 16x16x16) or by a 0/1 selection
+//     (fp8, 16x16x32 fp8, which also decodes the codes exactly into fp32).
 //   * O^T[dim][query head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane
 //     keeps four consecutive dims per 16-dim slice w (see out_dim) of query
 //     head c16, so the running max, sum and rescale of a head never leave its
