@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299464788, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
+        {"bytes": 2299464788, "digest": "e90a865367185110c2b97e78f84d4caf584be0fc6b9296dac67a91a979d4c745"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487907700, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
+        {"bytes": 1487907700, "digest": "e90a865367185110c2b97e78f84d4caf584be0fc6b9296dac67a91a979d4c745"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538218854, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
+        {"bytes": 538218854, "digest": "e90a865367185110c2b97e78f84d4caf584be0fc6b9296dac67a91a979d4c745"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680906590, "digest": "7b4b31b9801ebd7533cc57f732d88fb7f00072432439a387184b757dccd87d42"},
+        {"bytes": 680906590, "digest": "e90a865367185110c2b97e78f84d4caf584be0fc6b9296dac67a91a979d4c745"},
 }
 
 
@@ -60,17 +60,30 @@ DIGEST_SOURCES = ["build.py", "csrc/decode_mfma.hip", "csrc/kvs_device.h", "csrc
                   "csrc/abi.cpp"]
 
 
+def code_text(name: str, text: str) -> str:
+    """Source text without comments and blank space, so that the digest
+    changes with the code and not with its comments."""
+    import re
+
+    if name.endswith(".py"):
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def partial_kernel_digest() -> str:
-    """SHA-256 over DIGEST_SOURCES."""
+    """SHA-256 over the code of DIGEST_SOURCES (comments and blank space
+    removed)."""
     import hashlib
 
     pkg = os.path.join(ROOT, "decode_attention_kv_split_amd")
-    files = [os.path.join(pkg, f) for f in DIGEST_SOURCES]
     h = hashlib.sha256()
-    for f in files:
+    for f in DIGEST_SOURCES:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(pkg, f), encoding="utf-8") as fh:
+            h.update(code_text(f, fh.read()).encode())
     return h.hexdigest()
 
 

@@ -86,3 +86,13 @@ def test_attention_flops_count_every_visible_pair():
     # a causal prefill of n = L rows sees 1 + 2 + ... + L pairs
     pre = make_inputs(_spec(batch=1, page_size=0, lengths=("fixed", 100), q_len=("fixed", 100)))
     assert bench.attention_flops(pre) == 4 * 64 * 8 * (100 * 101 // 2)
+
+
+def test_traffic_digest_follows_code_not_comments():
+    src = "int f(int x) { // doubles x\n  return 2 * x; /* a\n  note */\n}\n"
+    same = "// header\nint f(int x) {\n\n  return 2 * x;   // twice\n}\n"
+    other = "int f(int x) { return 3 * x; }\n"
+    assert bench.code_text("k.hip", src) == bench.code_text("k.hip", same)
+    assert bench.code_text("k.hip", src) != bench.code_text("k.hip", other)
+    assert bench.code_text("b.py", "# flags\nFLAGS = ['-O3']\n") == bench.code_text("b.py", "FLAGS = ['-O3']\n")
+    assert len(bench.partial_kernel_digest()) == 64
