@@ -193,22 +193,55 @@ __device__ __forceinline__ void lds_read_vt4(s16x4_t &v0, s16x4_t &v1, s16x4_t &
   v2 = __builtin_bit_cast(s16x4_t, r2);
   v3 = __builtin_bit_cast(s16x4_t, r3);
 }
-// Four transposing reads at four lane addresses
-__device__ __forceinline__ void lds_read_tr_x4(s16x4_t &v0, s16x4_t &v1, s16x4_t &v2, s16x4_t &v3, uint32_t a0,
-                                               uint32_t a1, uint32_t a2, uint32_t a3) {
-  u32x2_t r0, r1, r2, r3;
-  __asm__ volatile("ds_read_b64_tr_b16 %0, %4\n\t"
-                   "ds_read_b64_tr_b16 %1, %5\n\t"
-                   "ds_read_b64_tr_b16 %2, %6\n\t"
-                   "ds_read_b64_tr_b16 %3, %7\n\t"
+// Eight 16-byte reads at eight lane addresses, one wait
+__device__ __forceinline__ void lds_read_x8(uint4 (&k)[8], const uint32_t (&a)[8], uint32_t off) {
+  u32x4_t r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile("ds_read_b128 %0, %8\n\t"
+                   "ds_read_b128 %1, %9\n\t"
+                   "ds_read_b128 %2, %10\n\t"
+                   "ds_read_b128 %3, %11\n\t"
+                   "ds_read_b128 %4, %12\n\t"
+                   "ds_read_b128 %5, %13\n\t"
+                   "ds_read_b128 %6, %14\n\t"
+                   "ds_read_b128 %7, %15\n\t"
                    "s_waitcnt lgkmcnt(0)"
-                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-                   : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off), "v"(a[4] + off),
+                     "v"(a[5] + off), "v"(a[6] + off), "v"(a[7] + off)
                    : "memory");
-  v0 = __builtin_bit_cast(s16x4_t, r0);
-  v1 = __builtin_bit_cast(s16x4_t, r1);
-  v2 = __builtin_bit_cast(s16x4_t, r2);
-  v3 = __builtin_bit_cast(s16x4_t, r3);
+  k[0] = __builtin_bit_cast(uint4, r0);
+  k[1] = __builtin_bit_cast(uint4, r1);
+  k[2] = __builtin_bit_cast(uint4, r2);
+  k[3] = __builtin_bit_cast(uint4, r3);
+  k[4] = __builtin_bit_cast(uint4, r4);
+  k[5] = __builtin_bit_cast(uint4, r5);
+  k[6] = __builtin_bit_cast(uint4, r6);
+  k[7] = __builtin_bit_cast(uint4, r7);
+}
+// Eight transposing reads at eight lane addresses, one wait
+__device__ __forceinline__ void lds_read_tr_x8(s16x4_t (&v)[8], const uint32_t (&a)[8], uint32_t off) {
+  u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile("ds_read_b64_tr_b16 %0, %8\n\t"
+                   "ds_read_b64_tr_b16 %1, %9\n\t"
+                   "ds_read_b64_tr_b16 %2, %10\n\t"
+                   "ds_read_b64_tr_b16 %3, %11\n\t"
+                   "ds_read_b64_tr_b16 %4, %12\n\t"
+                   "ds_read_b64_tr_b16 %5, %13\n\t"
+                   "ds_read_b64_tr_b16 %6, %14\n\t"
+                   "ds_read_b64_tr_b16 %7, %15\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off), "v"(a[4] + off),
+                     "v"(a[5] + off), "v"(a[6] + off), "v"(a[7] + off)
+                   : "memory");
+  v[0] = __builtin_bit_cast(s16x4_t, r0);
+  v[1] = __builtin_bit_cast(s16x4_t, r1);
+  v[2] = __builtin_bit_cast(s16x4_t, r2);
+  v[3] = __builtin_bit_cast(s16x4_t, r3);
+  v[4] = __builtin_bit_cast(s16x4_t, r4);
+  v[5] = __builtin_bit_cast(s16x4_t, r5);
+  v[6] = __builtin_bit_cast(s16x4_t, r6);
+  v[7] = __builtin_bit_cast(s16x4_t, r7);
 }
 // K pieces only (two per block)
 __device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, uint32_t a1) {
@@ -1332,7 +1365,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // 32 sl + 16 (G % 2) + 4 c .. + 3, i.e. piece 4 sl + 2 (G % 2) + c / 2, bytes
   // (c % 2) * 8 of it; lane i of the group then holds keys
   // 8 hh + 4 (G / 2) + 0..3 of dim 32 sl + 16 (G % 2) + i.
-  uint32_t vt_addr[2][4];
+  uint32_t vt_addr[8]; // [4 hh + sl]
   {
     const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
 #pragma unroll
@@ -1341,7 +1374,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       for (int sl = 0; sl < 4; ++sl) {
         const int row = 8 * hh + 4 * (G >> 1) + r;
         const int piece = 4 * sl + 2 * (G & 1) + (c >> 1);
-        vt_addr[hh][sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ (row & 15)) * 16) + (c & 1) * 8;
+        vt_addr[4 * hh + sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ (row & 15)) * 16) + (c & 1) * 8;
       }
   }
 
@@ -1349,22 +1382,16 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   auto tile32 = [&](int ts, uint32_t to) {
     // ---- S^T = K . Q^T ----
     uint4 kr[8];
-#pragma unroll
-    for (int s = 0; s < 8; s += 2) lds_read_k2(kr[s], kr[s + 1], k_addr[s] + to, k_addr[s + 1] + to);
+    lds_read_x8(kr, k_addr, to);
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[s], st, 0, 0, 0);
-    // V^T slices, read while the products run: [t][hh][sl]
-    s16x4_t vt[2][2][4];
+    // V^T slices, read while the products run: vt[t][4 hh + sl]
+    s16x4_t vt[2][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        lds_read_tr_x4(vt[t][hh][0], vt[t][hh][1], vt[t][hh][2], vt[t][hh][3], vt_addr[hh][0] + to + t * 16 * kRowBytes,
-                     vt_addr[hh][1] + to + t * 16 * kRowBytes, vt_addr[hh][2] + to + t * 16 * kRowBytes,
-                     vt_addr[hh][3] + to + t * 16 * kRowBytes);
+    for (int t = 0; t < 2; ++t) lds_read_tr_x8(vt[t], vt_addr, to + t * 16 * kRowBytes);
     // ---- scores: register v holds key ts + 8 (v / 4) + 4 h2 + v % 4 ----
     float sv[16];
 #pragma unroll
@@ -1414,7 +1441,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
-        const uint2 a = __builtin_bit_cast(uint2, vt[t][0][sl]), c = __builtin_bit_cast(uint2, vt[t][1][sl]);
+        const uint2 a = __builtin_bit_cast(uint2, vt[t][sl]), c = __builtin_bit_cast(uint2, vt[t][4 + sl]);
         const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, c.x, c.y));
         acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v8, pt, acc[sl], 0, 0, 0);
       }
