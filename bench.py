@@ -53,11 +53,11 @@ MEASURED_TRAFFIC = {
 }
 
 
-# Sources that decide what the matrix-core partial kernel reads and writes:
-# the kernel, its shared device code, the planner (chunk sizes, workspace),
-# the host code that fills its parameters, and the build flags.
-DIGEST_SOURCES = ["build.py", "csrc/decode_mfma.hip", "csrc/kvs_device.h", "csrc/plan.cpp", "csrc/plan.h",
-                  "csrc/abi.cpp"]
+# Sources that decide what the matrix-core decode partial kernel reads and
+# writes: the kernel, its shared device code, the planner (chunk sizes,
+# workspace), the host code that fills its parameters, and the build flags.
+DIGEST_SOURCES = ["build.py", "csrc/decode_mfma.hip", "csrc/mfma_tiles.h", "csrc/kvs_device.h", "csrc/plan.cpp",
+                  "csrc/plan.h", "csrc/abi.cpp"]
 
 
 def code_text(name: str, text: str) -> str:

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libkvsplit.so")
-SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "merge.hip", "append.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "rows_mfma.hip", "decode_valu.hip", "merge.hip", "append.hip",
+           "probe.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,755 @@
+// Device building blocks of the matrix-core partial kernels (decode_mfma.hip:
+// one or two query rows' worth of columns per wave, keys split over the
+// waves; rows_mfma.hip: several query rows per request, staged tiles shared
+// by the waves): tile shapes and their LDS staging, operand layouts of the
+// 16x16 matrix instructions, the per-lane column state, and the per-tile
+// online-softmax update.
+#pragma once
+
+#include "kvs_device.h"
+
+namespace kvs {
+namespace tiles {
+
+
+template <int DE, int KT>
+struct Shape {
+  static_assert(KT == DT_BF16 || KT == DT_FP8 || KT == DT_INT4, "KV type");
+  static constexpr int kEpp = KT == DT_BF16 ? 8 : (KT == DT_FP8 ? 16 : 32); // elements per 16-byte piece
+  static constexpr int kRowBytes = DE * 16 / kEpp;        // one token's K (or V) row of the pack
+  static constexpr int kLaneVec = kRowBytes / 64;          // 16-byte pieces per lane per row
+  static constexpr int kKSteps = DE / 32;                  // 16x16x32 products for S^T
+  static constexpr int kOTiles = DE / 16;                  // 16-dim slices of O^T
+  static constexpr int kOutStride = KT == DT_INT4 ? 2 : 1; // distance between a lane's four O^T dims
+  static_assert(kLaneVec >= 1, "row slice must hold at least 16 bytes");
+  // LDS staging of a 16-token tile
+  static constexpr int kPieces = kRowBytes / 16;           // 16-byte pieces per row
+  static constexpr int kRowsPerDma = 1024 / kRowBytes;     // rows one 64-lane x 16-byte load covers
+  static constexpr int kDma = kTile * kRowBytes / 1024;    // loads per tile (K or V)
+  static constexpr int kTileBytes = kTile * kRowBytes;     // K (or V) bytes of a tile
+  static constexpr int kRowsPerBankPeriod = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  // tiles staged per wave: about 12 KB of K+V in LDS per wave (three
+  // workgroups per CU for fp8 head_dim 128), two to eight
+  static constexpr int kFit = 12288 / (2 * kTileBytes);
+  static constexpr int kNBuf = kFit < 2 ? 2 : (kFit > 8 ? 8 : kFit);
+};
+
+// Word 3 of a raw buffer descriptor on CDNA (gfx9 family): 32-bit data format,
+// no swizzling; with stride 0 the size field is a byte count and lanes whose
+// offset falls outside it read zero.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the K/V loads: non-temporal.  Every K/V byte is read once
+// per call, and streaming loads measured about 10% more HBM bandwidth than
+// default-policy loads on MI355X (6.7 vs 6.0 TB/s on a plain read).
+constexpr int kKvLoadPolicy = 2;
+// Largest rise of a head's running max (log2 units) absorbed without a
+// rescale of its state; weights then stay below 2^8.
+constexpr float kLazy = 8.0f;
+// A starting reference this far (log2 units) above an empty state's first
+// tile max is moved down to it.
+constexpr float kDrop = 64.0f;
+
+// XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
+// operand reads at the same logical piece land in distinct LDS banks.
+template <int DE, int KT>
+__device__ __forceinline__ int stage_swizzle(int r) {
+  using S = Shape<DE, KT>;
+  return (r / S::kRowsPerBankPeriod) & (S::kPieces - 1);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (LDS DMA loads included); nothing else is waited for.  The compiler does
+// not order LDS reads after the DMA that fills them, so the staged-tile reads
+// follow this explicit wait and a compiler barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __asm__ volatile("" ::: "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// Reads of a staged tile.  Each asm block issues the K and V pieces at one or
+// two lane addresses (V sits VOFF bytes after K) and waits for them
+// (lgkmcnt 0) before it ends, so the registers are complete when the block
+// returns and the slot may be refilled at once.  Written out because the
+// compiler's own wait insertion cannot tell, across the main loop's back edge,
+// which DMA load filled which slot, and would otherwise drain every load in
+// flight there; the explicit vmcnt wait before each read orders DMA and read.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+template <int VOFF>
+__device__ __forceinline__ void lds_read_kv1(uint4 &k0, uint4 &v0, uint32_t a0) {
+  u32x4_t rk0, rv0;
+  __asm__ volatile("ds_read_b128 %0, %2\n\t"
+                   "ds_read_b128 %1, %2 offset:%3\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk0), "=&v"(rv0)
+                   : "v"(a0), "i"(VOFF)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk0);
+  v0 = __builtin_bit_cast(uint4, rv0);
+}
+template <int VOFF>
+__device__ __forceinline__ void lds_read_kv2(uint4 &k0, uint4 &v0, uint4 &k1, uint4 &v1, uint32_t a0, uint32_t a1) {
+  u32x4_t rk0, rv0, rk1, rv1;
+  __asm__ volatile("ds_read_b128 %0, %4\n\t"
+                   "ds_read_b128 %1, %4 offset:%6\n\t"
+                   "ds_read_b128 %2, %5\n\t"
+                   "ds_read_b128 %3, %5 offset:%6\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk0), "=&v"(rv0), "=&v"(rk1), "=&v"(rv1)
+                   : "v"(a0), "v"(a1), "i"(VOFF)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk0);
+  v0 = __builtin_bit_cast(uint4, rv0);
+  k1 = __builtin_bit_cast(uint4, rk1);
+  v1 = __builtin_bit_cast(uint4, rv1);
+}
+
+// One 16-byte-per-lane DMA load from a buffer into LDS: lane i's bytes land
+// at lds + 16 * i.  (Kept out of the kernel body: the host compilation pass
+// must not see the LDS address-space cast.)
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0,
+                                           kKvLoadPolicy);
+}
+
+// bf16 tiles up to 128 pack dims take V^T straight from LDS (transposing
+// reads); wider ones, fp8 and INT4 transpose V with a matrix product.  At
+// head_dim 256 the transposed slices, read together with K, held registers
+// the pair-wise prefill kernel needed (8192-row prefill: 147 against 158
+// TFLOP/s); at head_dim 128 they gained (2048 rows on a 32k cache: 499
+// against 480 TFLOP/s), decode unchanged.
+template <int DE, int KT>
+constexpr bool vt_from_lds() { return KT == DT_BF16 && DE <= 128; }
+
+template <int DE, int KT>
+struct TileRegs {
+  uint4 k[Shape<DE, KT>::kLaneVec];    // K pieces 4 * pc + q4 of row c16
+  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (fp8, INT4)
+  s16x4_t vt[Shape<DE, KT>::kOTiles];  // V^T slices read transposed from LDS (vt_from_lds)
+};
+
+// Transposing LDS reads (gfx950 ds_read_b64_tr_b16): within each 16-lane
+// group, lane i receives 16-bit element i % 4 of the 8 bytes addressed by
+// lane 4 r + i / 4, for r = 0..3.  Four V^T slices per block (two lane
+// addresses, each with a second slice 8 bytes further), waited for inside
+// the block like the other staged reads.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void lds_read_vt4(s16x4_t &v0, s16x4_t &v1, s16x4_t &v2, s16x4_t &v3, uint32_t a0,
+                                             uint32_t a1) {
+  u32x2_t r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                   "ds_read_b64_tr_b16 %1, %4 offset:8\n\t"
+                   "ds_read_b64_tr_b16 %2, %5\n\t"
+                   "ds_read_b64_tr_b16 %3, %5 offset:8\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(a0), "v"(a1)
+                   : "memory");
+  v0 = __builtin_bit_cast(s16x4_t, r0);
+  v1 = __builtin_bit_cast(s16x4_t, r1);
+  v2 = __builtin_bit_cast(s16x4_t, r2);
+  v3 = __builtin_bit_cast(s16x4_t, r3);
+}
+// Eight 16-byte reads at eight lane addresses, one wait
+__device__ __forceinline__ void lds_read_x8(uint4 (&k)[8], const uint32_t (&a)[8], uint32_t off) {
+  u32x4_t r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile("ds_read_b128 %0, %8\n\t"
+                   "ds_read_b128 %1, %9\n\t"
+                   "ds_read_b128 %2, %10\n\t"
+                   "ds_read_b128 %3, %11\n\t"
+                   "ds_read_b128 %4, %12\n\t"
+                   "ds_read_b128 %5, %13\n\t"
+                   "ds_read_b128 %6, %14\n\t"
+                   "ds_read_b128 %7, %15\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off), "v"(a[4] + off),
+                     "v"(a[5] + off), "v"(a[6] + off), "v"(a[7] + off)
+                   : "memory");
+  k[0] = __builtin_bit_cast(uint4, r0);
+  k[1] = __builtin_bit_cast(uint4, r1);
+  k[2] = __builtin_bit_cast(uint4, r2);
+  k[3] = __builtin_bit_cast(uint4, r3);
+  k[4] = __builtin_bit_cast(uint4, r4);
+  k[5] = __builtin_bit_cast(uint4, r5);
+  k[6] = __builtin_bit_cast(uint4, r6);
+  k[7] = __builtin_bit_cast(uint4, r7);
+}
+// Eight transposing reads at eight lane addresses, one wait
+__device__ __forceinline__ void lds_read_tr_x8(s16x4_t (&v)[8], const uint32_t (&a)[8], uint32_t off) {
+  u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile("ds_read_b64_tr_b16 %0, %8\n\t"
+                   "ds_read_b64_tr_b16 %1, %9\n\t"
+                   "ds_read_b64_tr_b16 %2, %10\n\t"
+                   "ds_read_b64_tr_b16 %3, %11\n\t"
+                   "ds_read_b64_tr_b16 %4, %12\n\t"
+                   "ds_read_b64_tr_b16 %5, %13\n\t"
+                   "ds_read_b64_tr_b16 %6, %14\n\t"
+                   "ds_read_b64_tr_b16 %7, %15\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off), "v"(a[4] + off),
+                     "v"(a[5] + off), "v"(a[6] + off), "v"(a[7] + off)
+                   : "memory");
+  v[0] = __builtin_bit_cast(s16x4_t, r0);
+  v[1] = __builtin_bit_cast(s16x4_t, r1);
+  v[2] = __builtin_bit_cast(s16x4_t, r2);
+  v[3] = __builtin_bit_cast(s16x4_t, r3);
+  v[4] = __builtin_bit_cast(s16x4_t, r4);
+  v[5] = __builtin_bit_cast(s16x4_t, r5);
+  v[6] = __builtin_bit_cast(s16x4_t, r6);
+  v[7] = __builtin_bit_cast(s16x4_t, r7);
+}
+// K pieces only (two per block)
+__device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, uint32_t a1) {
+  u32x4_t r0, r1;
+  __asm__ volatile("ds_read_b128 %0, %2\n\t"
+                   "ds_read_b128 %1, %3\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1)
+                   : "v"(a0), "v"(a1)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, r0);
+  k1 = __builtin_bit_cast(uint4, r1);
+}
+
+// Lane addresses of a staged tile (K rows, then V rows kTileBytes further;
+// 16-byte pieces XOR-swizzled per row) and the reads that turn it into the
+// operand registers of lane (c16, q4).  K (and fp8 / INT4 V): pieces 4 pc + q4
+// of row c16.  bf16 V: V^T slice w straight from LDS with transposing reads;
+// lane 16 q4 + 4 r + c points at the four dims of slice w that output rows
+// 4 c .. 4 c + 3 hold (out_dim) in token row 4 q4 + r, so lane (i, q4) gets
+// keys 4 q4 .. 4 q4 + 3 of dim row i, the A-operand layout of the P.V product.
+template <int DE, int KT>
+struct StageReader {
+  using S = Shape<DE, KT>;
+  static constexpr bool kVt = vt_from_lds<DE, KT>();
+  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : 1;
+  uint32_t k_addr[S::kLaneVec];
+  uint32_t vt_addr[kVtAddr];
+  __device__ __forceinline__ void init(uint32_t tile0, int lane) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    const int swz = stage_swizzle<DE, KT>(c16);
+#pragma unroll
+    for (int pc = 0; pc < S::kLaneVec; ++pc)
+      k_addr[pc] = tile0 + c16 * S::kRowBytes + ((4 * pc + q4) ^ swz) * 16;
+    if constexpr (kVt) {
+      const int r = (lane >> 2) & 3, c = lane & 3;
+      const int row = 4 * q4 + r;
+      const int vswz = stage_swizzle<DE, KT>(row);
+#pragma unroll
+      for (int h = 0; h < kVtAddr; ++h) {
+        // slices 2 h and 2 h + 1: source piece 4 h + c, bytes 0 and 8 of it
+        vt_addr[h] = tile0 + S::kTileBytes + row * S::kRowBytes + ((4 * h + c) ^ vswz) * 16;
+      }
+    }
+  }
+  // t <- the tile whose K rows start `off` bytes after tile0 (reads complete on return)
+  __device__ __forceinline__ void read(TileRegs<DE, KT> &t, uint32_t off) const {
+    if constexpr (kVt) {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2) lds_read_k2(t.k[pc], t.k[pc + 1], k_addr[pc] + off, k_addr[pc + 1] + off);
+#pragma unroll
+      for (int h = 0; h < kVtAddr; h += 2)
+        lds_read_vt4(t.vt[2 * h], t.vt[2 * h + 1], t.vt[2 * h + 2], t.vt[2 * h + 3], vt_addr[h] + off,
+                     vt_addr[h + 1] + off);
+    } else if constexpr (S::kLaneVec == 1) {
+      lds_read_kv1<S::kTileBytes>(t.k[0], t.v[0], k_addr[0] + off);
+    } else {
+#pragma unroll
+      for (int pc = 0; pc < S::kLaneVec; pc += 2)
+        lds_read_kv2<S::kTileBytes>(t.k[pc], t.v[pc], t.k[pc + 1], t.v[pc + 1], k_addr[pc] + off,
+                                    k_addr[pc + 1] + off);
+    }
+  }
+};
+
+// Max of x over lanes l and l ^ 16 (l ^ 32) with gfx950's lane swaps: swapping
+// the odd 16-lane rows of one copy of x with the even rows of another (the
+// upper 32 lanes of one with the lower 32 of the other) leaves each lane the
+// two values whose max it needs.  VALU instructions, where a lane shuffle
+// would go through the LDS unit and wait for it.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 8 consecutive fp8 codes (two dwords) -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+// INT4: a dword holds 8 two's-complement nibbles n (element 2i in the low
+// nibble of byte i).  n ^ 8 = n + 8 lies in [0, 15], and the bf16 pattern
+// 0x43 : (n + 8) is exactly 128 + (n + 8) = n + 136, so one byte permute
+// builds two bf16 operands.  The products then carry an offset of 136 per
+// element, removed exactly afterwards (scores: 136 * sum of q over the head's
+// dims; outputs: 136 * the softmax sum).  kInt4Offset is that 136.
+constexpr float kInt4Offset = 136.0f;
+__device__ __forceinline__ uint32_t int4_even(uint32_t w) { return (w ^ 0x88888888u) & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t int4_odd(uint32_t w) { return ((w ^ 0x88888888u) >> 4) & 0x0F0F0F0Fu; }
+// bytes b0..b3 of x (each in [0, 15]) -> bf16 (128 + b0, 128 + b1), (128 + b2, 128 + b3)
+__device__ __forceinline__ uint32_t offset_bf16_lo(uint32_t x) { return __builtin_amdgcn_perm(0x43434343u, x, 0x04010400u); }
+__device__ __forceinline__ uint32_t offset_bf16_hi(uint32_t x) { return __builtin_amdgcn_perm(0x43434343u, x, 0x04030402u); }
+
+// Pack dim of element e (0..7) that lane (q4) feeds to the S^T product in
+// k-step j (16x16x32: 8 reduction indices per lane).  INT4 feeds the even
+// elements of a dword first, then the odd ones.
+template <int DE, int KT>
+__device__ __forceinline__ int k_elem_dim(int j, int q4, int e) {
+  if constexpr (KT == DT_FP8) {
+    return 16 * (4 * (j >> 1) + q4) + 8 * (j & 1) + e;
+  } else if constexpr (KT == DT_INT4) {
+    const int pc = j >> 2, dw = j & 3; // piece 4 pc + q4, dword dw of it
+    return 32 * (4 * pc + q4) + 8 * dw + (e < 4 ? 2 * e : 2 * (e - 4) + 1);
+  } else {
+    return 8 * (4 * j + q4) + e;
+  }
+}
+
+// First of the four pack dims lane (q4) holds in O^T slice w; the four are
+// kOutStride apart.
+template <int DE, int KT>
+__device__ __forceinline__ int out_dim(int w, int q4) {
+  if constexpr (KT == DT_INT4) {
+    const int pc = w >> 3, dw = (w & 7) >> 1; // slice w: the even (w even) or odd nibbles of dword dw
+    return 32 * (4 * pc + q4) + 8 * dw + (w & 1);
+  } else {
+    constexpr int per_piece = Shape<DE, KT>::kEpp / 4; // slices per 16-byte piece
+    return (4 * (w / per_piece) + q4) * Shape<DE, KT>::kEpp + 4 * (w % per_piece);
+  }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <int DE, int KT>
+__device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, KT> &t, int j) {
+  if constexpr (KT == DT_FP8) {
+    const uint4 w = t.k[j >> 1];
+    return (j & 1) ? fp8x8_to_bf16x8(w.z, w.w) : fp8x8_to_bf16x8(w.x, w.y);
+  } else if constexpr (KT == DT_INT4) {
+    const uint32_t w = dword_of(t.k[j >> 2], j & 3);
+    const uint32_t ev = int4_even(w), od = int4_odd(w);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(offset_bf16_lo(ev), offset_bf16_hi(ev), offset_bf16_lo(od),
+                                                   offset_bf16_hi(od)));
+  } else {
+    return __builtin_bit_cast(bf16x8_t, t.k[j]);
+  }
+}
+
+// Which (request b, split) work item `item` is, with the request's split
+// count nb and length L: from the host-planned list, else by a scan of the
+// device lengths (which also records each request's first item and split
+// count for the merge).  Returns false, the same in every thread, when the
+// device lengths disagree with the planned launch.  Every thread calls it.
+__device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w, int item, int *s_scan, int *s_item,
+                                            int &b, int &split, int &nb, int &L) {
+  if (w.n_items > 0) { // planned on the host
+    const uint32_t e = w.item[item];
+    b = (int)(e >> 16);
+    split = (int)(e & 0xFFFF);
+    L = w.req_len[b];
+    nb = num_splits(L, req_nq(p, b), p.window, p.chunk);
+    return true;
+  }
+  if (threadIdx.x == 0) s_item[0] = -1;
+  scan_requests(p, s_scan, [&](int bb, int first, int nbb) {
+    if (item >= first && item < first + nbb) {
+      s_item[0] = bb;
+      s_item[1] = item - first;
+      s_item[2] = nbb;
+      s_item[3] = first;
+    }
+  });
+  __syncthreads();
+  b = __builtin_amdgcn_readfirstlane(s_item[0]);
+  split = __builtin_amdgcn_readfirstlane(s_item[1]);
+  nb = __builtin_amdgcn_readfirstlane(s_item[2]);
+  if (b < 0) return false;
+  if (p.meta && split == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    p.meta[2 * b] = s_item[3];
+    p.meta[2 * b + 1] = nb;
+  }
+  L = p.kv_len[b];
+  return true;
+}
+
+// Operands of the V transposition for lane (c16, q4): a bf16 identity
+// (16x16x16 products) and, for fp8, 0/1 selections of one code per
+// 16x16x32 product (the fp8 pattern 0x38 is 1.0).
+template <int KT>
+__device__ __forceinline__ void transpose_operands(int c16, int q4, s16x4_t &ident, long (&sel)[2]) {
+  const short one_bf16 = 0x3F80;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
+  sel[0] = sel[1] = 0;
+  if (KT == DT_FP8) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint64_t s = 0;
+      if (q4 == (c16 >> 2)) s = (uint64_t)0x38 << (8 * (4 * hh + (c16 & 3)));
+      sel[hh] = (long)s;
+    }
+  }
+}
+
+// ---- column groups: per-lane state shared by the two partial kernels ----
+// A wave computes CG groups of 16 matrix columns; lane (c16, q4) holds column
+// c16 of every group.  A column is a query head of the pack (one query per
+// request) or a (query row, head) pair (several rows per request).
+template <int DE, int KT, int CG>
+struct ColumnSet {
+  using S = Shape<DE, KT>;
+  bf16x8_t q[CG][S::kKSteps]; // Q^T operand, zero where the column sees no dims
+  float qoff[CG];             // INT4: the scores carry 136 * (sum of the column's q)
+  bool ok[CG];                // the lane's column holds a (query, head) of the request
+  bool on[CG];                // the group holds any (the same in every lane)
+  int row[CG], head[CG];      // q / o row and query head of the lane's column
+  int lo[CG], hi[CG];         // keys of the chunk the lane's column sees
+  float m[CG];                // reference max, log2 domain (the same in the 4 quarters)
+  float l[CG];                // partial sum over the lane's tokens
+  float lb[CG];               // INT4: the same sum of the bf16-rounded weights P.V saw
+  f32x4_t acc[CG][S::kOTiles];
+};
+
+// Which (query, head) each lane's column is, and the keys of [t_begin,
+// t_end) it sees: up to its query's position, the last `window` of them.
+// cg0: the set's first column group; gp: query heads per pack.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void set_columns(ColumnSet<DE, KT, CG> &cs, const Params &p, int b, int L, int nq,
+                                            int kvg, int cg0, int gp, int t_begin, int t_end, int c16) {
+  const int g = p.group;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    int qi; // query index within the request (0 with one query)
+    if (!p.qo_indptr) {
+      cs.ok[c] = c16 < gp;
+      cs.on[c] = true;
+      qi = 0;
+      cs.row[c] = b;
+      cs.head[c] = kvg * gp + c16;
+    } else {
+      const int col = (cg0 + c) * 16 + c16;
+      cs.ok[c] = col < nq * g;
+      cs.on[c] = (cg0 + c) * 16 < nq * g;
+      qi = col / g;
+      cs.row[c] = p.qo_indptr[b] + qi;
+      cs.head[c] = kvg * g + col % g;
+    }
+    const int qpos = L - nq + qi;
+    const int col_lo = p.window > 0 ? max(0, qpos - p.window + 1) : 0;
+    cs.lo[c] = max(t_begin, col_lo);
+    cs.hi[c] = min(t_end, qpos + 1);
+  }
+}
+
+// Keys every column of the set sees, [all_lo, all_hi) (tiles inside need no
+// per-key mask), and keys some column sees, [any_lo, any_hi); uniform.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void column_ranges(const ColumnSet<DE, KT, CG> &cs, int t_begin, int t_end, int &all_lo,
+                                              int &all_hi, int &any_lo, int &any_hi) {
+  all_lo = t_begin;
+  all_hi = t_end;
+  any_lo = t_end;
+  any_hi = t_begin;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (cs.ok[c]) {
+      all_lo = max(all_lo, cs.lo[c]);
+      all_hi = min(all_hi, cs.hi[c]);
+      if (cs.lo[c] < cs.hi[c]) {
+        any_lo = min(any_lo, cs.lo[c]);
+        any_hi = max(any_hi, cs.hi[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+    any_lo = min(any_lo, __shfl_xor(any_lo, o, 64));
+    any_hi = max(any_hi, __shfl_xor(any_hi, o, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  any_lo = __builtin_amdgcn_readfirstlane(any_lo);
+  any_hi = __builtin_amdgcn_readfirstlane(any_hi);
+}
+
+// Q^T operand of each group (block diagonal over the pack: column c16 only
+// sees the dims of its own KV head my_kv), its INT4 offset, and an empty
+// softmax state starting from the reference max m_init.
+template <int D, int DE, int KT, int CG>
+__device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Params &p, int q4, int my_kv) {
+  using S = Shape<DE, KT>;
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const uint16_t *qb =
+        reinterpret_cast<const uint16_t *>(p.q) + ((size_t)cs.row[c] * p.num_qo_heads + cs.head[c]) * D;
+#pragma unroll
+    for (int j = 0; j < S::kKSteps; ++j) {
+      const int kd = k_elem_dim<DE, KT>(j, q4, 0); // the k-step's 8 dims are kd .. kd + 7
+      if (cs.ok[c] && kd / D == my_kv) {
+        bf16x8_t x = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + (kd % D)));
+        if constexpr (KT == DT_INT4) x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+        cs.q[c][j] = x;
+      } else {
+        cs.q[c][j] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      }
+    }
+    cs.qoff[c] = 0.0f;
+    if constexpr (KT == DT_INT4) {
+#pragma unroll
+      for (int j = 0; j < S::kKSteps; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs.qoff[c] += (float)cs.q[c][j][e];
+      cs.qoff[c] += __shfl_xor(cs.qoff[c], 16, 64);
+      cs.qoff[c] += __shfl_xor(cs.qoff[c], 32, 64);
+      cs.qoff[c] *= kInt4Offset;
+    }
+    cs.m[c] = p.m_init;
+    cs.l[c] = 0.0f;
+    cs.lb[c] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) cs.acc[c][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Zero the V rows of a staged tile (first key ts) that lie before key lo:
+// they hold keys no column of the wave sees, whose weight is 0, and a
+// non-finite value there must not reach the P.V product.
+template <int DE, int KT>
+__device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16, int q4) {
+  if (ts < lo) {
+    if constexpr (vt_from_lds<DE, KT>()) { // V^T: lane (c16, q4) holds keys ts + 4 q4 + e
+#pragma unroll
+      for (int w = 0; w < Shape<DE, KT>::kOTiles; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ts + 4 * q4 + e < lo) t.vt[w][e] = 0;
+    } else { // V rows: lane (c16, q4) holds row c16
+      const bool ok = ts + c16 >= lo;
+#pragma unroll
+      for (int k = 0; k < Shape<DE, KT>::kLaneVec; ++k)
+        if (!ok) t.v[k] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Scaled scores of one staged 16-token tile (first key ts) for column group c:
+// lane (c16, q4) gets keys ts + 4 * q4 + r (r = 0..3) of its column in log2
+// units, soft-capped, and -inf where the column does not see the key (only
+// tested when the tile is not seen whole by every column).
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void tile_scores(const ColumnSet<DE, KT, CG> &cs, int c, const TileRegs<DE, KT> &t, int ts,
+                                            bool whole, float cscale, float cap_out, int q4, float *sv) {
+  using S = Shape<DE, KT>;
+  // S^T = K . Q^T
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < S::kKSteps; ++j)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<DE, KT>(t, j), cs.q[c][j], s, 0, 0, 0);
+  if constexpr (KT == DT_INT4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] -= cs.qoff[c]; // remove the 136-per-element offset of K
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = s[r] * cscale;
+  if (cap_out > 0.0f) { // logit soft-cap: c * tanh(s / c), in log2 units (uniform branch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = tanhf(sv[r]) * cap_out;
+  }
+  if (!whole) { // some column misses some key of the tile (uniform branch)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = ts + 4 * q4 + r;
+      if (tok < cs.lo[c] || tok >= cs.hi[c]) sv[r] = -INFINITY;
+    }
+  }
+}
+
+// Online-softmax step of column group c over NS new scores per lane: the
+// weights, bf16-packed in pairs into pk[NS / 2], and the running state.
+template <int NS, int DE, int KT, int CG>
+__device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, const float *sv, uint32_t *pk) {
+  using S = Shape<DE, KT>;
+  float mx = sv[0];
+#pragma unroll
+  for (int r = 1; r < NS; ++r) mx = fmaxf(mx, sv[r]);
+  mx = xor32_max(xor16_max(mx));
+  // Lazy rescale: the reference max m moves (and the state is rescaled by
+  // 2^(m - m_new)) only when a score exceeds it by more than kLazy, so
+  // weights stay below 2^kLazy and after the first tiles the rescale is
+  // almost never needed.  m + log2(l) and acc / l do not depend on which
+  // reference is used.
+  // m = -inf: any visible key grows it.  A given starting reference (unified
+  // max) far above a still-empty state's first scores is moved down to
+  // them, so no weight underflows.
+  const bool empty = cs.l[c] == 0.0f;
+  const bool grow = mx > cs.m[c] + kLazy || (empty && mx != -INFINITY && mx < cs.m[c] - kDrop);
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(cs.m[c] - mx)) : 1.0f;
+    cs.m[c] = grow ? mx : cs.m[c];
+    cs.l[c] *= alpha;
+    if constexpr (KT == DT_INT4) cs.lb[c] *= alpha;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs.acc[c][w][r] *= alpha;
+    }
+  }
+  // no visible key so far for this column: weights 0, state unchanged
+  const bool live = cs.m[c] != -INFINITY;
+  float pr[NS];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) pr[r] = live ? __builtin_amdgcn_exp2f(sv[r] - cs.m[c]) : 0.0f;
+  float sum = 0.0f;
+#pragma unroll
+  for (int r = 0; r < NS; r += 4) sum += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+  cs.l[c] += sum;
+#pragma unroll
+  for (int r = 0; r < NS; r += 2) pk[r / 2] = pack_bf16x2(pr[r], pr[r + 1]);
+  if constexpr (KT == DT_INT4) {
+    float sb = 0.0f; // the weights as the P.V product sees them
+#pragma unroll
+    for (int r = 0; r < NS / 2; ++r) sb += __uint_as_float(pk[r] << 16) + __uint_as_float(pk[r] & 0xFFFF0000u);
+    cs.lb[c] += sb;
+  }
+}
+
+// V^T slices of a staged tile as bf16 operands: va[w] holds, in lane
+// (c16, q4), keys 4 * q4 + r of dimension c16 of the 16-dim slice w.
+template <int DE, int KT>
+__device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, const long (&sel)[2],
+                                         s16x4_t *va) {
+  using S = Shape<DE, KT>;
+  if constexpr (vt_from_lds<DE, KT>()) { // read transposed from LDS already
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) va[w] = t.vt[w];
+    return;
+  }
+  // all products first, so the dependent conversions do not wait on each other
+  f32x4_t vt[S::kOTiles];
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < S::kOTiles; ++w) {
+    if constexpr (KT == DT_INT4) {
+      // even (w even) or odd nibbles of dword (w / 2) % 4 of piece w / 8, as 136 + n
+      const uint32_t dw = dword_of(t.v[w >> 3], (w >> 1) & 3);
+      const uint32_t nib = (w & 1) ? int4_odd(dw) : int4_even(dw);
+      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+    } else if constexpr (KT == DT_FP8) {
+      const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
+      const uint4 wv = t.v[u >> 1];
+      const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
+      const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
+      const long a = (long)(((uint64_t)hi32 << 32) | lo32);
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
+    } else {
+      const uint4 wv = t.v[w >> 1];
+      const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
+      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < S::kOTiles; ++w)
+    va[w] = __builtin_bit_cast(s16x4_t, make_uint2(pack_bf16x2(vt[w][0], vt[w][1]), pack_bf16x2(vt[w][2], vt[w][3])));
+}
+
+// One staged 16-token tile (first key ts) through every column group:
+// scores, online-softmax step, then O^T += V^T . P^T with the V^T slices
+// shared by the groups.  [all_lo, all_hi): keys every column sees.
+// ident / sel: the identity and 0/1 selection operands of the V transposition.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &t, int ts, int all_lo,
+                                            int all_hi, float cscale, float cap_out, s16x4_t ident,
+                                            const long (&sel)[2], int q4) {
+  using S = Shape<DE, KT>;
+  const bool whole = ts >= all_lo && ts + kTile <= all_hi;
+  s16x4_t pt[CG]; // P^T operand of each group
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue; // the same in every lane
+    float sv[4];
+    tile_scores(cs, c, t, ts, whole, cscale, cap_out, q4, sv);
+    uint32_t pk[2];
+    softmax_step<4>(cs, c, sv, pk);
+    pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(pk[0], pk[1]));
+  }
+  s16x4_t va[S::kOTiles];
+  v_slices(t, ident, sel, va);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w)
+      cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[w], pt[c], cs.acc[c][w], 0, 0, 0);
+  }
+}
+
+// Two staged tiles (first keys tsa, tsb) at once: one softmax step over the
+// 32 keys and one O^T += V^T . P^T product per 16-dim slice with k = 32
+// (v_mfma_f32_16x16x32_bf16, twice the work of the 16x16x16 form per
+// instruction).  Lane quarter q4 feeds reduction indices 8 q4 .. 8 q4 + 7 of
+// both operands as keys 4 q4 .. 4 q4 + 3 of the first tile, then the same
+// keys of the second, so V^T and P^T agree on the key of every index.
+template <int DE, int KT, int CG>
+__device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &ta, int tsa,
+                                            const TileRegs<DE, KT> &tb, int tsb, int all_lo, int all_hi,
+                                            float cscale, float cap_out, s16x4_t ident, const long (&sel)[2],
+                                            int q4) {
+  using S = Shape<DE, KT>;
+  const bool whole_a = tsa >= all_lo && tsa + kTile <= all_hi;
+  const bool whole_b = tsb >= all_lo && tsb + kTile <= all_hi;
+  bf16x8_t pt[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue; // the same in every lane
+    float sv[8];
+    tile_scores(cs, c, ta, tsa, whole_a, cscale, cap_out, q4, sv);
+    tile_scores(cs, c, tb, tsb, whole_b, cscale, cap_out, q4, sv + 4);
+    uint32_t pk[4];
+    softmax_step<8>(cs, c, sv, pk);
+    pt[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  }
+  s16x4_t va[S::kOTiles], vb[S::kOTiles];
+  v_slices(ta, ident, sel, va);
+  v_slices(tb, ident, sel, vb);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (c > 0 && !cs.on[c]) continue;
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) {
+      const uint2 a = __builtin_bit_cast(uint2, va[w]), bv = __builtin_bit_cast(uint2, vb[w]);
+      const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, bv.x, bv.y));
+      cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pt[c], cs.acc[c][w], 0, 0, 0);
+    }
+  }
+}
+
+} // namespace tiles
+
+// Launches the multi-row partial kernels (rows_mfma.hip) for a plan whose
+// workgroups cover 4 or 8 column groups (Params::col_share).
+hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l);
+
+} // namespace kvs

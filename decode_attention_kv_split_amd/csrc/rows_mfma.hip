@@ -1,0 +1,597 @@
+// Partial softmax for several query rows per request (append / prefill
+// attention) on gfx950 matrix cores, for plans whose workgroups cover four or
+// eight groups of 16 (query row, head) columns of one KV head.  The four
+// waves of a workgroup own different columns and share every staged K/V
+// block, so the keys are read once for all of them: partial_rows_kernel with
+// the 16x16 operand layouts of mfma_tiles.h, and partial_prefill_kernel with
+// 32x32 tiles for bf16 head_dim 128.
+#include "mfma_tiles.h"
+
+namespace kvs {
+namespace {
+using namespace tiles;
+
+// Several query rows per request and many column groups (a long append or a
+// prefill): the four waves share every staged K/V tile instead of splitting
+// the keys.  Wave w computes column groups cgw + CG * w .. cgw + CG * w + CG - 1
+// of one KV head, so a workgroup covers 16 * CG * kWaves columns and reads
+// each K/V byte of its chunk once for all of them.  Keys advance in blocks of
+// kWaves 16-token tiles: each wave stages one tile of the block into LDS
+// (DMA), a barrier publishes the block, every wave runs the block's tiles
+// through its column groups, and a second barrier frees the slot for the
+// block NBUF further on.  A wave's columns are its own, so it writes its
+// results with no merge across waves.
+template <int D, int KT, int NBUF, int CG>
+__global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, const InlineWork w) {
+  using S = Shape<D, KT>;
+  constexpr int kGroups = kWaves * CG;                   // column groups per workgroup
+  constexpr int kBlock = kWaves * kTile;                 // keys per staged block
+  constexpr int kSlotBytes = kWaves * 2 * S::kTileBytes; // K and V of a block
+  // Tiles two at a time (pair_update) only where one column group per wave
+  // leaves the registers for a second tile: with two groups (head_dim <= 128)
+  // the pair form reached the register limit and ran slower (a 32k-token MHA
+  // cache with 2048 new rows: 359 against 493 TFLOP/s), with one (head_dim
+  // 256) it ran faster (8192-row prefill: 162 against 147 TFLOP/s).
+  constexpr bool kPairs = CG == 1;
+
+  __shared__ int s_scan[2 * 64];
+  __shared__ int s_item[4];
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * kSlotBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int item = blockIdx.x;
+  const int row_blocks = (p.col_groups + kGroups - 1) / kGroups; // workgroups per (item, KV head)
+  const int kvg = blockIdx.y / row_blocks;                       // KV head
+  const int cgw = blockIdx.y % row_blocks * kGroups;             // first column group of the workgroup
+  const int g = p.group;
+  const int Hk = p.num_kv_heads;
+
+  int b, split, nb, L;
+  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  const int nq = req_nq(p, b);
+  if (cgw * 16 >= nq * g) return; // no column of this workgroup has a query row (uniform)
+  const int lo = request_lo(L, nq, p.window);
+  const int a0 = (lo & ~(kTile - 1)) + split * p.chunk; // aligned chunk start
+  const int t_begin = max(lo, a0);
+  const int t_end = min(L, a0 + p.chunk);
+  // keys some column of the workgroup sees: from the first key of its first
+  // query row to the position of its last (both grow with the row)
+  const int q_first = cgw * 16 / g;
+  const int q_last = (min(nq * g, (cgw + kGroups) * 16) - 1) / g;
+  const int wg_lo = max(t_begin, p.window > 0 ? max(0, L - nq + q_first - p.window + 1) : 0);
+  const int wg_hi = min(t_end, L - nq + q_last + 1);
+  const int fb = wg_hi > wg_lo ? (wg_lo - a0) / kBlock : 0; // first block, counted from the chunk start
+  const int nblocks = wg_hi > wg_lo ? (wg_hi - a0 + kBlock - 1) / kBlock - fb : 0;
+  const int k0 = a0 + fb * kBlock; // first key of block 0
+
+  // ---- this wave's column groups ----
+  ColumnSet<D, KT, CG> cs;
+  set_columns(cs, p, b, L, nq, kvg, cgw + wave * CG, g, t_begin, t_end, c16);
+  int all_lo, all_hi, wv_lo, wv_hi; // keys every / some column of the wave sees
+  column_ranges(cs, t_begin, t_end, all_lo, all_hi, wv_lo, wv_hi);
+  load_columns<D>(cs, p, q4, 0);
+  float cscale = p.score_scale;
+  if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg];
+  const float cap_out = p.cap_out;
+  s16x4_t ident;
+  long sel[2];
+  transpose_operands<KT>(c16, q4, ident, sel);
+
+  // ---- addressing: this wave's tile of block i, one block per lane ----
+  // (a block holds kBlock keys and chunks at most 64 * kBlock, so 64 lanes
+  // cover every block; tiles holding no key the workgroup sees move no bytes)
+  const size_t row_bytes = (size_t)Hk * S::kRowBytes;
+  const bool paged = p.page_size > 0;
+  const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
+  uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
+  if (lane < nblocks) {
+    const int ts = k0 + lane * kBlock + wave * kTile;
+    if (ts < wg_hi && ts + kTile > wg_lo) {
+      const size_t row0 =
+          paged ? (size_t)pages[ts >> p.page_shift] * p.page_size + (ts & (p.page_size - 1)) : (size_t)ts;
+      const size_t off = row0 * row_bytes;
+      voff_lo = (uint32_t)off;
+      voff_hi = (uint32_t)(off >> 32);
+      vbytes = (uint32_t)(min(kTile, wg_hi - ts) * (int)row_bytes);
+    }
+  }
+  const char *kpool = reinterpret_cast<const char *>(p.k);
+  const char *vpool = reinterpret_cast<const char *>(p.v);
+  int dma_voff[S::kDma]; // lane's byte offset within a tile, per DMA load
+#pragma unroll
+  for (int k = 0; k < S::kDma; ++k) {
+    const int r = k * S::kRowsPerDma + lane / S::kPieces;
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<D, KT>(r);
+    dma_voff[k] = r * (int)row_bytes + kvg * S::kRowBytes + piece * 16; // < 2^31: checked on the host
+  }
+  // tile u of slot s sits at smem + (s * kWaves + u) * 2 * kTileBytes (K, then V)
+  auto issue = [&](int i, int slot) {
+    const int li = min(i, 63);
+    const size_t base = ((size_t)__builtin_amdgcn_readlane(voff_hi, li) << 32) | __builtin_amdgcn_readlane(voff_lo, li);
+    const int nbytes = i < nblocks ? (int)__builtin_amdgcn_readlane(vbytes, li) : 0;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
+    char *kst = smem + (slot * kWaves + wave) * 2 * S::kTileBytes;
+    char *vst = kst + S::kTileBytes;
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, vst + 1024 * k, dma_voff[k]);
+  };
+  StageReader<D, KT> stage; // lane addresses of tile 0 of slot 0
+  stage.init(lds_address(smem), lane);
+  auto read_stage = [&](TileRegs<D, KT> &t, int slot, int u) {
+    stage.read(t, (slot * kWaves + u) * 2 * S::kTileBytes);
+  };
+
+  // ---- ring of NBUF block slots shared by the waves ----
+  if (nblocks > 0) { // the same in every wave
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) issue(j, j);
+    const int n_iter = (nblocks + NBUF - 1) / NBUF * NBUF;
+    for (int it = 0; it < n_iter; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int i = it + j;
+        wait_vmem<(NBUF - 1) * 2 * S::kDma>(); // this wave's tile of block i has landed
+        __syncthreads();                       // ... and every other wave's
+        if (i < nblocks) {
+          if constexpr (kPairs) {
+            // the block's tiles two at a time: one softmax step and one
+            // k = 32 product per pair
+#pragma unroll
+            for (int u = 0; u < kWaves; u += 2) {
+              const int tsa = k0 + i * kBlock + u * kTile, tsb = tsa + kTile;
+              if (tsa < wv_hi && tsb + kTile > wv_lo) { // the wave's columns see keys of this pair
+                TileRegs<D, KT> ta, tb;
+                read_stage(ta, j, u);
+                read_stage(tb, j, u + 1);
+                zero_v_before(ta, tsa, wv_lo, c16, q4);
+                zero_v_before(tb, tsb, wv_lo, c16, q4);
+                pair_update(cs, ta, tsa, tb, tsb, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < kWaves; ++u) {
+              const int ts = k0 + i * kBlock + u * kTile;
+              if (ts < wv_hi && ts + kTile > wv_lo) { // the wave's columns see keys of this tile
+                TileRegs<D, KT> t;
+                read_stage(t, j, u);
+                zero_v_before(t, ts, wv_lo, c16, q4);
+                tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+              }
+            }
+          }
+        }
+        __syncthreads(); // every wave has read slot j
+        issue(i + NBUF, j);
+      }
+    }
+    wait_vmem<0>(); // no DMA may land in LDS after the workgroup ends
+  }
+
+  // ---- results of this wave's columns: final output, or the split's partial ----
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    if (!cs.on[c]) continue; // the same in every lane of the wave
+    float l_tot = cs.l[c] + __shfl_xor(cs.l[c], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    float lb_tot = 0.0f;
+    if constexpr (KT == DT_INT4) {
+      lb_tot = cs.lb[c] + __shfl_xor(cs.lb[c], 16, 64);
+      lb_tot += __shfl_xor(lb_tot, 32, 64);
+    }
+    if (!cs.ok[c]) continue;
+    const bool live = l_tot > 0.0f; // a finite reference with no visible key leaves l = 0: empty
+    const float vscale = p.v_scale ? p.v_scale[b * Hk + kvg] : 1.0f;
+    const float inv = live ? vscale / l_tot : 0.0f;
+    const float lse2 = live ? cs.m[c] + __log2f(l_tot) : -INFINITY;
+    // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
+    const float voff = kInt4Offset * lb_tot;
+    if (nb == 1) {
+      const size_t rowoff = ((size_t)cs.row[c] * p.num_qo_heads + cs.head[c]) * D;
+#pragma unroll
+      for (int wt = 0; wt < S::kOTiles; ++wt) {
+        const int od = out_dim<D, KT>(wt, q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float val = (cs.acc[c][wt][r] - voff) * inv;
+          const size_t off = rowoff + od + r * S::kOutStride;
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t *>(p.o)[off] = f32_to_bf16_bits(val);
+          else
+            reinterpret_cast<float *>(p.o)[off] = val;
+        }
+      }
+      if (q4 == 0 && p.lse) p.lse[(size_t)cs.row[c] * p.num_qo_heads + cs.head[c]] = lse2 * kLn2;
+    } else {
+      const int cg = cgw + wave * CG + c;
+      const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
+      float *dst = p.o_part + (slot * p.cols + c16) * D;
+#pragma unroll
+      for (int wt = 0; wt < S::kOTiles; ++wt) {
+        const int od = out_dim<D, KT>(wt, q4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[od + r * S::kOutStride] = (cs.acc[c][wt][r] - voff) * inv;
+      }
+      if (q4 == 0) p.lse_part[slot * p.cols + c16] = lse2;
+    }
+  }
+}
+
+// Several query rows per request, bf16 KV, head_dim 128, from three groups
+// of 16 columns on: 32x32 matrix tiles.  Each wave owns 32 (query row, head)
+// columns of one KV head and the workgroup's four waves share every staged
+// 64-key block (one 16-row part staged by each wave, barriers around it, as
+// in partial_rows_kernel).  Per 32-key tile and wave:
+//   * S^T[key][column] = K . Q^T with v_mfma_f32_32x32x16_bf16 over 8 steps
+//     of 16 dims: lane (i, h) = (l % 32, l / 32) feeds K row i, dims
+//     16 s + 8 h .. + 7, read from LDS; the result holds, in lane (j, h),
+//     keys 8 (v / 4) + 4 h + v % 4 (register v) of column j.
+//   * online softmax per column over its 32 keys, which sit in lanes j and
+//     j + 32: in-lane max over 16 scores, one lane swap.
+//   * O^T[dim][column] += V^T . P^T with the same instruction (k = 16 keys),
+//     twice per tile: for half t of the tile, lane (j, h) supplies its own
+//     registers 8 t .. 8 t + 7 as P^T (keys 16 t + 8 (e / 4) + 4 h + e % 4),
+//     and V^T comes straight from LDS with transposing reads in that key
+//     order (two reads of four consecutive keys per operand).
+// 32-key tiles halve the cross-lane steps per key and run the P.V product
+// at the full rate of the 32x32x16 form.
+template <int NBUF>
+__global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params p, const InlineWork w) {
+  constexpr int D = 128;
+  using S = Shape<D, DT_BF16>;                    // 256-byte rows, 16 pieces
+  constexpr int kRowBytes = S::kRowBytes;         // one key's K (or V) row of the head
+  constexpr int kBlock = kWaves * kTile;          // 64 keys staged per block
+  constexpr int kHalf = kBlock * kRowBytes;       // K (or V) bytes of a block
+  constexpr int kGroups = kWaves * 2;             // 16-column groups per workgroup
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+  __shared__ int s_scan[2 * 64];
+  __shared__ int s_item[4];
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * 2 * kHalf];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j32 = lane & 31; // column of the lane (S^T, O^T) / row (K, V^T operands)
+  const int h2 = lane >> 5;  // half of the wave
+  const int item = blockIdx.x;
+  const int row_blocks = (p.col_groups + kGroups - 1) / kGroups;
+  const int kvg = blockIdx.y / row_blocks;
+  const int cgw = blockIdx.y % row_blocks * kGroups; // first 16-column group of the workgroup
+  const int g = p.group;
+  const int Hk = p.num_kv_heads;
+
+  int b, split, nb, L;
+  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  const int nq = req_nq(p, b);
+  if (cgw * 16 >= nq * g) return; // uniform over the workgroup
+  const int lo = request_lo(L, nq, p.window);
+  const int a0 = (lo & ~(kTile - 1)) + split * p.chunk;
+  const int t_begin = max(lo, a0);
+  const int t_end = min(L, a0 + p.chunk);
+  // keys some column of the workgroup sees (rows and their keys both grow with the column)
+  const int q_first = cgw * 16 / g;
+  const int q_last = (min(nq * g, (cgw + kGroups) * 16) - 1) / g;
+  const int wg_lo = max(t_begin, p.window > 0 ? max(0, L - nq + q_first - p.window + 1) : 0);
+  const int wg_hi = min(t_end, L - nq + q_last + 1);
+  const int fb = wg_hi > wg_lo ? (wg_lo - a0) / kBlock : 0;
+  const int nblocks = wg_hi > wg_lo ? (wg_hi - a0 + kBlock - 1) / kBlock - fb : 0;
+  const int k0 = a0 + fb * kBlock;
+
+  // ---- this lane's column ----
+  const int col = cgw * 16 + wave * 32 + j32;
+  const bool ok = col < nq * g;
+  const bool wave_on = (cgw * 16 + wave * 32) < nq * g; // the same in every lane of the wave
+  const int qi = col / g;
+  const int qrow = p.qo_indptr[b] + qi;
+  const int qhead = kvg * g + col % g;
+  const int qpos = L - nq + qi;
+  const int c_lo = max(t_begin, p.window > 0 ? max(0, qpos - p.window + 1) : 0);
+  const int c_hi = min(t_end, qpos + 1);
+  int all_lo = t_begin, all_hi = t_end, wv_lo = t_end, wv_hi = t_begin;
+  if (ok) {
+    all_lo = c_lo;
+    all_hi = c_hi;
+    if (c_lo < c_hi) {
+      wv_lo = c_lo;
+      wv_hi = c_hi;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+    wv_lo = min(wv_lo, __shfl_xor(wv_lo, o, 64));
+    wv_hi = max(wv_hi, __shfl_xor(wv_hi, o, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  wv_lo = __builtin_amdgcn_readfirstlane(wv_lo);
+  wv_hi = __builtin_amdgcn_readfirstlane(wv_hi);
+
+  // Q^T operand: step s holds dims 16 s + 8 h2 .. + 7 of the column's query
+  bf16x8_t qop[8];
+  {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + 16 * s + 8 * h2))
+                  : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+  }
+  const float cscale = p.score_scale;
+  const float cap_out = p.cap_out;
+  float m_run = p.m_init, l_run = 0.0f;
+  f32x16_t acc[4]; // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[sl][v] = 0.0f;
+
+  // ---- staging: this wave's 16-row part of block i, one block per lane ----
+  const size_t row_bytes = (size_t)Hk * kRowBytes;
+  const bool paged = p.page_size > 0;
+  const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
+  uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
+  if (lane < nblocks) {
+    const int ts = k0 + lane * kBlock + wave * kTile;
+    if (ts < wg_hi && ts + kTile > wg_lo) {
+      const size_t row0 =
+          paged ? (size_t)pages[ts >> p.page_shift] * p.page_size + (ts & (p.page_size - 1)) : (size_t)ts;
+      const size_t off = row0 * row_bytes;
+      voff_lo = (uint32_t)off;
+      voff_hi = (uint32_t)(off >> 32);
+      vbytes = (uint32_t)(min(kTile, wg_hi - ts) * (int)row_bytes);
+    }
+  }
+  const char *kpool = reinterpret_cast<const char *>(p.k);
+  const char *vpool = reinterpret_cast<const char *>(p.v);
+  // lane i of load k: row 4 k + i / 16 of the part, position i % 16, which
+  // holds source piece position ^ (row % 16) (rows of a block keep the
+  // swizzle of their position modulo 16)
+  int dma_voff[S::kDma];
+#pragma unroll
+  for (int k = 0; k < S::kDma; ++k) {
+    const int r = k * S::kRowsPerDma + lane / S::kPieces;
+    const int piece = (lane % S::kPieces) ^ (r & 15);
+    dma_voff[k] = r * (int)row_bytes + kvg * kRowBytes + piece * 16;
+  }
+  auto issue = [&](int i, int slot) {
+    const int li = min(i, 63);
+    const size_t base = ((size_t)__builtin_amdgcn_readlane(voff_hi, li) << 32) | __builtin_amdgcn_readlane(voff_lo, li);
+    const int nbytes = i < nblocks ? (int)__builtin_amdgcn_readlane(vbytes, li) : 0;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
+    char *kst = smem + slot * 2 * kHalf + wave * kTile * kRowBytes;
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+#pragma unroll
+    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, kst + kHalf + 1024 * k, dma_voff[k]);
+  };
+  // K operand of step s: row j32 of the tile, piece 2 s + h2
+  uint32_t k_addr[8];
+  {
+    const uint32_t base = lds_address(smem) + j32 * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) k_addr[s] = base + ((2 * s + h2) ^ (j32 & 15)) * 16;
+  }
+  // V^T operand reads (ds_read_b64_tr_b16): lane l = 16 G + 4 r + c of group G
+  // points at key row 8 hh + 4 (G / 2) + r (+ 16 t, an immediate), dims
+  // 32 sl + 16 (G % 2) + 4 c .. + 3, i.e. piece 4 sl + 2 (G % 2) + c / 2, bytes
+  // (c % 2) * 8 of it; lane i of the group then holds keys
+  // 8 hh + 4 (G / 2) + 0..3 of dim 32 sl + 16 (G % 2) + i.
+  uint32_t vt_addr[8]; // [4 hh + sl]
+  {
+    const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int row = 8 * hh + 4 * (G >> 1) + r;
+        const int piece = 4 * sl + 2 * (G & 1) + (c >> 1);
+        vt_addr[4 * hh + sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ (row & 15)) * 16) + (c & 1) * 8;
+      }
+  }
+
+  // one 32-key tile (first key ts) at byte offset `to` of the staged block
+  auto tile32 = [&](int ts, uint32_t to) {
+    // ---- S^T = K . Q^T ----
+    uint4 kr[8];
+    lds_read_x8(kr, k_addr, to);
+    f32x16_t st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[s], st, 0, 0, 0);
+    // V^T slices, read while the products run: vt[t][4 hh + sl]
+    s16x4_t vt[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) lds_read_tr_x8(vt[t], vt_addr, to + t * 16 * kRowBytes);
+    // ---- scores: register v holds key ts + 8 (v / 4) + 4 h2 + v % 4 ----
+    float sv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = st[v] * cscale;
+    if (cap_out > 0.0f) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = tanhf(sv[v]) * cap_out;
+    }
+    if (ts < all_lo || ts + 2 * kTile > all_hi) { // some column misses some key (uniform)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tok = ts + 8 * (v >> 2) + 4 * h2 + (v & 3);
+        if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+    mx = xor32_max(mx);
+    // lazy rescale (as in the 16x16 kernels): the reference moves only when a
+    // score exceeds it by more than kLazy
+    const bool empty = l_run == 0.0f;
+    const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[sl][v] *= alpha;
+    }
+    const bool live = m_run != -INFINITY;
+    uint32_t pk[8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = live ? __builtin_amdgcn_exp2f(sv[v] - m_run) : 0.0f;
+      const float p1 = live ? __builtin_amdgcn_exp2f(sv[v + 1] - m_run) : 0.0f;
+      sum += p0 + p1;
+      pk[v / 2] = pack_bf16x2(p0, p1);
+    }
+    l_run += sum;
+    // ---- O^T += V^T . P^T, k = 16 keys per product ----
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const uint2 a = __builtin_bit_cast(uint2, vt[t][sl]), c = __builtin_bit_cast(uint2, vt[t][4 + sl]);
+        const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, c.x, c.y));
+        acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v8, pt, acc[sl], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- ring of NBUF block slots shared by the waves ----
+  if (nblocks > 0) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) issue(j, j);
+    const int n_iter = (nblocks + NBUF - 1) / NBUF * NBUF;
+    for (int it = 0; it < n_iter; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int i = it + j;
+        wait_vmem<(NBUF - 1) * 2 * S::kDma>();
+        __syncthreads();
+        if (i < nblocks && wave_on) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int ts = k0 + i * kBlock + u * 2 * kTile;
+            if (ts < wv_hi && ts + 2 * kTile > wv_lo) tile32(ts, j * 2 * kHalf + u * 2 * kTile * kRowBytes);
+          }
+        }
+        __syncthreads();
+        issue(i + NBUF, j);
+      }
+    }
+    wait_vmem<0>();
+  }
+
+  // ---- this lane's column: final output, or the split's partial ----
+  if (!wave_on) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!ok) return;
+  const bool live = l_tot > 0.0f;
+  const float inv = live ? 1.0f / l_tot : 0.0f;
+  const float lse2 = live ? m_run + __log2f(l_tot) : -INFINITY;
+  if (nb == 1) {
+    uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * sl + 8 * q + 4 * h2;
+        *reinterpret_cast<uint2 *>(orow + d0) =
+            make_uint2(pack_bf16x2(acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv),
+                       pack_bf16x2(acc[sl][4 * q + 2] * inv, acc[sl][4 * q + 3] * inv));
+      }
+    if (h2 == 0 && p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
+  } else {
+    const int cg = col / 16;
+    const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
+    float *dst = p.o_part + (slot * p.cols + col % 16) * D;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * sl + 8 * q + 4 * h2;
+        *reinterpret_cast<float4 *>(dst + d0) =
+            make_float4(acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv, acc[sl][4 * q + 3] * inv);
+      }
+    if (h2 == 0) p.lse_part[slot * p.cols + col % 16] = lse2;
+  }
+}
+
+// Column groups one wave of the shared-tile kernel computes: two for
+// head_dim <= 128; head_dim 256 keeps one, its accumulators would not fit in
+// registers twice.
+template <int D>
+constexpr int rows_cg() { return D <= 128 ? 2 : 1; }
+
+// Block slots of the shared-tile kernel: about 64 KB of LDS per workgroup
+// (two workgroups per CU), two to four slots.
+template <int D, int KT>
+constexpr int rows_nbuf() {
+  constexpr int slot = kWaves * 2 * Shape<D, KT>::kTileBytes;
+  return 65536 / slot < 2 ? 2 : (65536 / slot > 4 ? 4 : 65536 / slot);
+}
+
+} // namespace
+
+// Column groups from which several query rows per request go to the
+// shared-tile kernel.  Below 8 groups some of its waves idle; that pays for
+// bf16, whose second read of the keys costs more than the idle waves, from 3
+// groups on, but for the compute-heavier fp8 and INT4 tiles only once three
+// of the four waves have work (batch-128 fp8, 8 rows of 8 heads = 4 groups:
+// 656 us with the chunk-splitting kernel, 980 us shared-tile).
+constexpr int kRowsMinGroupsBf16 = 3;
+constexpr int kRowsMinGroupsQuant = 5;
+
+// Column groups of (query row, head) pairs one partial workgroup computes
+// (several query rows per request).  Two: the chunk-splitting kernel runs
+// both on each staged tile (head_dim <= 128), halving the K/V reads of short
+// appends.  From three groups on: the shared-tile kernel, whose workgroup
+// covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
+// all of them.
+int mfma_col_share(int head_dim, int kv_type, int col_groups) {
+  if (col_groups >= (kv_type == DT_BF16 ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
+    return kWaves * (head_dim <= 128 ? 2 : 1);
+  return col_groups >= 2 && head_dim <= 128 ? 2 : 1;
+}
+
+template <int D, int KT>
+static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Launch &l) {
+  constexpr int kGroups = kWaves * rows_cg<D>();
+  if (p.col_share != kGroups || p.pack != 1) return hipErrorInvalidValue;
+  const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + kGroups - 1) / kGroups));
+  if constexpr (D == 128 && KT == DT_BF16) return launch_kernel(l, partial_prefill_kernel<2>, grid, p, w);
+  return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
+}
+
+hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
+  if (kv_type == DT_INT4) {
+    if (head_dim == 128) return launch_rows_d<128, DT_INT4>(p, w, l);
+    if (head_dim == 256) return launch_rows_d<256, DT_INT4>(p, w, l);
+    return hipErrorInvalidValue;
+  }
+  const bool fp8 = kv_type == DT_FP8;
+  switch (head_dim) {
+  case 64: return fp8 ? launch_rows_d<64, DT_FP8>(p, w, l) : launch_rows_d<64, DT_BF16>(p, w, l);
+  case 128: return fp8 ? launch_rows_d<128, DT_FP8>(p, w, l) : launch_rows_d<128, DT_BF16>(p, w, l);
+  case 256: return fp8 ? launch_rows_d<256, DT_FP8>(p, w, l) : launch_rows_d<256, DT_BF16>(p, w, l);
+  default: return hipErrorInvalidValue;
+  }
+}
+
+} // namespace kvs
