@@ -181,6 +181,49 @@ __device__ __forceinline__ void lds_read_x8(uint4 (&k)[8], const uint32_t (&a)[8
   k[6] = __builtin_bit_cast(uint4, r6);
   k[7] = __builtin_bit_cast(uint4, r7);
 }
+// Four 16-byte reads at the first four of the lane addresses a, one wait
+__device__ __forceinline__ void lds_read_x4(uint4 (&k)[4], const uint32_t *a, uint32_t off) {
+  u32x4_t r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b128 %0, %4\n\t"
+                   "ds_read_b128 %1, %5\n\t"
+                   "ds_read_b128 %2, %6\n\t"
+                   "ds_read_b128 %3, %7\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off)
+                   : "memory");
+  k[0] = __builtin_bit_cast(uint4, r0);
+  k[1] = __builtin_bit_cast(uint4, r1);
+  k[2] = __builtin_bit_cast(uint4, r2);
+  k[3] = __builtin_bit_cast(uint4, r3);
+}
+// Eight 8-bit transposing reads (gfx950 ds_read_b64_tr_b8) at eight lane
+// addresses, one wait: within each 16-lane group, lane i receives byte i % 8
+// of the 8 bytes addressed by lane 2 r + i / 8, for r = 0..7.
+__device__ __forceinline__ void lds_read_tr8_x8(uint2 (&v)[8], const uint32_t (&a)[8], uint32_t off) {
+  u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
+  __asm__ volatile("ds_read_b64_tr_b8 %0, %8\n\t"
+                   "ds_read_b64_tr_b8 %1, %9\n\t"
+                   "ds_read_b64_tr_b8 %2, %10\n\t"
+                   "ds_read_b64_tr_b8 %3, %11\n\t"
+                   "ds_read_b64_tr_b8 %4, %12\n\t"
+                   "ds_read_b64_tr_b8 %5, %13\n\t"
+                   "ds_read_b64_tr_b8 %6, %14\n\t"
+                   "ds_read_b64_tr_b8 %7, %15\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off), "v"(a[4] + off),
+                     "v"(a[5] + off), "v"(a[6] + off), "v"(a[7] + off)
+                   : "memory");
+  v[0] = __builtin_bit_cast(uint2, r0);
+  v[1] = __builtin_bit_cast(uint2, r1);
+  v[2] = __builtin_bit_cast(uint2, r2);
+  v[3] = __builtin_bit_cast(uint2, r3);
+  v[4] = __builtin_bit_cast(uint2, r4);
+  v[5] = __builtin_bit_cast(uint2, r5);
+  v[6] = __builtin_bit_cast(uint2, r6);
+  v[7] = __builtin_bit_cast(uint2, r7);
+}
 // Eight transposing reads at eight lane addresses, one wait
 __device__ __forceinline__ void lds_read_tr_x8(s16x4_t (&v)[8], const uint32_t (&a)[8], uint32_t off) {
   u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;

@@ -244,10 +244,19 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
 //     order (two reads of four consecutive keys per operand).
 // 32-key tiles halve the cross-lane steps per key and run the P.V product
 // at the full rate of the 32x32x16 form.
-template <int NBUF>
+// fp8 KV: K pieces are converted to bf16 for the score product (lane half
+// h takes whole 16-byte pieces 2 m + h, dims ordered to match the query's),
+// V^T comes from 8-bit transposing reads (eight consecutive rows of a dim
+// per lane) and is converted likewise.  So that eight consecutive staged rows
+// are exactly the keys of a lane's P^T operand, operand row i of K reads the
+// staged row pi(i), pi swapping bits 3 and 2 of the row within each 16; score
+// row R then belongs to key pi(R).
+template <int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params p, const InlineWork w) {
+  static_assert(KT == DT_BF16 || KT == DT_FP8, "bf16 or fp8 KV");
+  constexpr bool kFp8 = KT == DT_FP8;
   constexpr int D = 128;
-  using S = Shape<D, DT_BF16>;                    // 256-byte rows, 16 pieces
+  using S = Shape<D, KT>;                         // bf16: 256-byte rows, 16 pieces; fp8: 128, 8
   constexpr int kRowBytes = S::kRowBytes;         // one key's K (or V) row of the head
   constexpr int kBlock = kWaves * kTile;          // 64 keys staged per block
   constexpr int kHalf = kBlock * kRowBytes;       // K (or V) bytes of a block
@@ -318,16 +327,19 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   wv_lo = __builtin_amdgcn_readfirstlane(wv_lo);
   wv_hi = __builtin_amdgcn_readfirstlane(wv_hi);
 
-  // Q^T operand: step s holds dims 16 s + 8 h2 .. + 7 of the column's query
+  // Q^T operand of step s: dims 16 s + 8 h2 .. + 7 of the column's query
+  // (fp8: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .., the order of its K pieces)
   bf16x8_t qop[8];
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + 16 * s + 8 * h2))
+    for (int s = 0; s < 8; ++s) {
+      const int d0 = kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2;
+      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
                   : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    }
   }
-  const float cscale = p.score_scale;
+  const float cscale = kFp8 ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
   const float cap_out = p.cap_out;
   float m_run = p.m_init, l_run = 0.0f;
   f32x16_t acc[4]; // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
@@ -354,14 +366,14 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   }
   const char *kpool = reinterpret_cast<const char *>(p.k);
   const char *vpool = reinterpret_cast<const char *>(p.v);
-  // lane i of load k: row 4 k + i / 16 of the part, position i % 16, which
-  // holds source piece position ^ (row % 16) (rows of a block keep the
-  // swizzle of their position modulo 16)
+  // lane i of load k: row k * kRowsPerDma + i / kPieces of the part, position
+  // i % kPieces, which holds source piece position ^ swizzle(row) (rows of a
+  // block keep the swizzle of their position within the part)
   int dma_voff[S::kDma];
 #pragma unroll
   for (int k = 0; k < S::kDma; ++k) {
     const int r = k * S::kRowsPerDma + lane / S::kPieces;
-    const int piece = (lane % S::kPieces) ^ (r & 15);
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<D, KT>(r);
     dma_voff[k] = r * (int)row_bytes + kvg * kRowBytes + piece * 16;
   }
   auto issue = [&](int i, int slot) {
@@ -378,12 +390,31 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, kst + kHalf + 1024 * k, dma_voff[k]);
   };
-  // K operand of step s: row j32 of the tile, piece 2 s + h2
+  // K operand: bf16, step s: row j32 of the tile, piece 2 s + h2; fp8: row
+  // pi(j32), piece 2 m + h2 for steps 2 m and 2 m + 1
   uint32_t k_addr[8];
+  const int krow = kFp8 ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
   {
-    const uint32_t base = lds_address(smem) + j32 * kRowBytes;
+    const uint32_t base = lds_address(smem) + krow * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) k_addr[s] = base + ((2 * s + h2) ^ (j32 & 15)) * 16;
+    for (int s = 0; s < 8; ++s) k_addr[s] = base + (((kFp8 ? s & 3 : s) * 2 + h2) ^ stage_swizzle<D, KT>(krow)) * 16;
+  }
+  // fp8 V^T reads (ds_read_b64_tr_b8): lane 16 G + 2 r + c of group G points at
+  // staged row 8 (G / 2) + r (+ 16 t), dims 32 sl + 16 (G % 2) + 8 c .. + 7
+  // (piece 2 sl + G % 2, bytes 8 c of it); lane i of the group then holds rows
+  // 8 (G / 2) + 0..7 of dim 32 sl + 16 (G % 2) + i.
+  uint32_t vt8_addr[8]; // [4 t + sl]
+  if constexpr (kFp8) {
+    const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int row = 16 * t + 8 * (G >> 1) + r;
+        const int piece = 2 * sl + (G & 1);
+        vt8_addr[4 * t + sl] =
+            lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row)) * 16) + c * 8;
+      }
   }
   // V^T operand reads (ds_read_b64_tr_b16): lane l = 16 G + 4 r + c of group G
   // points at key row 8 hh + 4 (G / 2) + r (+ 16 t, an immediate), dims
@@ -391,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // (c % 2) * 8 of it; lane i of the group then holds keys
   // 8 hh + 4 (G / 2) + 0..3 of dim 32 sl + 16 (G % 2) + i.
   uint32_t vt_addr[8]; // [4 hh + sl]
-  {
+  if constexpr (!kFp8) {
     const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -406,17 +437,47 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // one 32-key tile (first key ts) at byte offset `to` of the staged block
   auto tile32 = [&](int ts, uint32_t to) {
     // ---- S^T = K . Q^T ----
-    uint4 kr[8];
-    lds_read_x8(kr, k_addr, to);
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
+    bf16x8_t kop[8];
+    if constexpr (kFp8) {
+      uint4 kr[4];
+      lds_read_x4(kr, k_addr, to);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[s], st, 0, 0, 0);
-    // V^T slices, read while the products run: vt[t][4 hh + sl]
-    s16x4_t vt[2][8];
+      for (int m = 0; m < 4; ++m) {
+        kop[2 * m] = fp8x8_to_bf16x8(kr[m].x, kr[m].y);
+        kop[2 * m + 1] = fp8x8_to_bf16x8(kr[m].z, kr[m].w);
+      }
+    } else {
+      uint4 kr[8];
+      lds_read_x8(kr, k_addr, to);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) lds_read_tr_x8(vt[t], vt_addr, to + t * 16 * kRowBytes);
+      for (int s = 0; s < 8; ++s) kop[s] = __builtin_bit_cast(bf16x8_t, kr[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[s], st, 0, 0, 0);
+    // V^T operands, read while the products run: vop[t][sl]
+    bf16x8_t vop[2][4];
+    if constexpr (kFp8) {
+      uint2 v8[8];
+      lds_read_tr8_x8(v8, vt8_addr, to);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) vop[t][sl] = fp8x8_to_bf16x8(v8[4 * t + sl].x, v8[4 * t + sl].y);
+    } else {
+      s16x4_t vt[2][8]; // [t][4 hh + sl]
+#pragma unroll
+      for (int t = 0; t < 2; ++t) lds_read_tr_x8(vt[t], vt_addr, to + t * 16 * kRowBytes);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const uint2 a = __builtin_bit_cast(uint2, vt[t][sl]), c = __builtin_bit_cast(uint2, vt[t][4 + sl]);
+          vop[t][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, c.x, c.y));
+        }
+    }
     // ---- scores: register v holds key ts + 8 (v / 4) + 4 h2 + v % 4 ----
     float sv[16];
 #pragma unroll
@@ -428,7 +489,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     if (ts < all_lo || ts + 2 * kTile > all_hi) { // some column misses some key (uniform)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tok = ts + 8 * (v >> 2) + 4 * h2 + (v & 3);
+        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8: key pi(row)
+        const int tok = ts + (kFp8 ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
         if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
       }
     }
@@ -465,11 +527,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     for (int t = 0; t < 2; ++t) {
       const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const uint2 a = __builtin_bit_cast(uint2, vt[t][sl]), c = __builtin_bit_cast(uint2, vt[t][4 + sl]);
-        const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, c.x, c.y));
-        acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v8, pt, acc[sl], 0, 0, 0);
-      }
+      for (int sl = 0; sl < 4; ++sl) acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][sl], pt, acc[sl], 0, 0, 0);
     }
   };
 
@@ -503,7 +561,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!ok) return;
   const bool live = l_tot > 0.0f;
-  const float inv = live ? 1.0f / l_tot : 0.0f;
+  const float vscale = kFp8 ? p.v_scale[b * Hk + kvg] : 1.0f;
+  const float inv = live ? vscale / l_tot : 0.0f;
   const float lse2 = live ? m_run + __log2f(l_tot) : -INFINITY;
   if (nb == 1) {
     uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
@@ -565,7 +624,9 @@ constexpr int kRowsMinGroupsQuant = 5;
 // covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
 // all of them.
 int mfma_col_share(int head_dim, int kv_type, int col_groups) {
-  if (col_groups >= (kv_type == DT_BF16 ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
+  // bf16 and fp8 at head_dim 128 take the 32x32 prefill kernel there
+  const bool tiles32 = head_dim == 128 && (kv_type == DT_BF16 || kv_type == DT_FP8);
+  if (col_groups >= (kv_type == DT_BF16 || tiles32 ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
     return kWaves * (head_dim <= 128 ? 2 : 1);
   return col_groups >= 2 && head_dim <= 128 ? 2 : 1;
 }
@@ -575,7 +636,8 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
   constexpr int kGroups = kWaves * rows_cg<D>();
   if (p.col_share != kGroups || p.pack != 1) return hipErrorInvalidValue;
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + kGroups - 1) / kGroups));
-  if constexpr (D == 128 && KT == DT_BF16) return launch_kernel(l, partial_prefill_kernel<2>, grid, p, w);
+  if constexpr (D == 128 && (KT == DT_BF16 || KT == DT_FP8))
+    return launch_kernel(l, partial_prefill_kernel<KT, KT == DT_FP8 ? 4 : 2>, grid, p, w);
   return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
 }
 

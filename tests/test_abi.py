@@ -142,8 +142,10 @@ def test_query_row_checks(lib):
     a, keep = with_rows([0, 12, 20])                    # 12 rows x 4 heads: 3 groups
     assert kvs.kvs_decode_plan(a).col_share == 8        # bf16: the shared-tile kernel, 8 groups a workgroup
     a, keep = with_rows([0, 12, 20], kv=kvs.KVS_FP8_E4M3)
-    assert kvs.kvs_decode_plan(a).col_share == 2        # fp8 takes the shared-tile kernel from 5 groups
-    a, keep = with_rows([0, 20, 40], kv=kvs.KVS_FP8_E4M3)
+    assert kvs.kvs_decode_plan(a).col_share == 8        # fp8 at head_dim 128: the 32x32 kernel from 3 groups
+    a, keep = with_rows([0, 12, 20], kv=kvs.KVS_FP8_E4M3, d=64)
+    assert kvs.kvs_decode_plan(a).col_share == 2        # other fp8 shapes: the shared-tile kernel from 5 groups
+    a, keep = with_rows([0, 20, 40], kv=kvs.KVS_FP8_E4M3, d=64)
     assert kvs.kvs_decode_plan(a).col_share == 8
     a, keep = with_rows([0, 12, 20], d=256)
     assert kvs.kvs_decode_plan(a).col_share == 4        # head_dim 256: one group per wave
