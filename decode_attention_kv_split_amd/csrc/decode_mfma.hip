@@ -26,11 +26,13 @@
 //     p = exp2(s - reference), running sum.
 //   * V^T with tokens 4*q4 + r of one head dimension in lane c16 -- the
 //     operand layout the next product needs: bf16 (pack width <= 128) reads
-//     it straight from LDS with transposing reads; otherwise the V tile is
-//     multiplied by an identity (bf16, INT4: 16x16x16) or by a 0/1 selection
-//     (fp8, 16x16x32 fp8, which also decodes the codes exactly into fp32).
+//     it straight from LDS with 16-bit transposing reads, INT4 with 8-bit
+//     ones (4 keys x 4 dims of nibbles per lane, turned into 136 + n by byte
+//     permutes); otherwise the V tile is multiplied by an identity (bf16,
+//     16x16x16) or by a 0/1 selection (fp8, 16x16x32 fp8, which also decodes
+//     the codes exactly into fp32).
 //   * O^T[dim][query head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane
-//     keeps four consecutive dims per 16-dim slice w (see out_dim) of query
+//     keeps four dims per 16-dim slice w (see out_dim) of query
 //     head c16, so the running max, sum and rescale of a head never leave its
 //     lane; dims of the other KV head of the pack are dropped at the end.
 // The first product, the online update and the rescaled accumulation follow

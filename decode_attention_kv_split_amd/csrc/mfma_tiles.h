@@ -118,20 +118,25 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
                                            kKvLoadPolicy);
 }
 
-// bf16 tiles up to 128 pack dims take V^T straight from LDS (transposing
-// reads); wider ones, fp8 and INT4 transpose V with a matrix product.  At
+// bf16 tiles up to 128 pack dims take V^T straight from LDS (16-bit
+// transposing reads), INT4 tiles from 8-bit transposing reads (vt_int4);
+// wider bf16 tiles and fp8 transpose V with a matrix product.  At
 // head_dim 256 the transposed slices, read together with K, held registers
 // the pair-wise prefill kernel needed (8192-row prefill: 147 against 158
 // TFLOP/s); at head_dim 128 they gained (2048 rows on a 32k cache: 499
 // against 480 TFLOP/s), decode unchanged.
 template <int DE, int KT>
 constexpr bool vt_from_lds() { return KT == DT_BF16 && DE <= 128; }
+template <int KT>
+constexpr bool vt_int4() { return KT == DT_INT4; }
 
 template <int DE, int KT>
 struct TileRegs {
+  static constexpr int kNibBlocks = KT == DT_INT4 ? DE / 64 : 1;
   uint4 k[Shape<DE, KT>::kLaneVec];    // K pieces 4 * pc + q4 of row c16
-  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (fp8, INT4)
+  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (fp8)
   s16x4_t vt[Shape<DE, KT>::kOTiles];  // V^T slices read transposed from LDS (vt_from_lds)
+  uint2 vn[kNibBlocks];                // INT4: V codes of 4 keys x 4 dims per 64-dim block (vt_int4)
 };
 
 // Transposing LDS reads (gfx950 ds_read_b64_tr_b16): within each 16-lane
@@ -249,6 +254,44 @@ __device__ __forceinline__ void lds_read_tr_x8(s16x4_t (&v)[8], const uint32_t (
   v[6] = __builtin_bit_cast(s16x4_t, r6);
   v[7] = __builtin_bit_cast(s16x4_t, r7);
 }
+// INT4 tiles: the lane's K pieces and one 8-bit transposing read
+// (ds_read_b64_tr_b8, layout as for lds_read_tr8_x8) per 64-dim block of V,
+// one wait.
+__device__ __forceinline__ void lds_read_k1_tr8x2(uint4 &k0, uint2 (&v)[2], uint32_t ak, uint32_t a0, uint32_t a1) {
+  u32x4_t rk;
+  u32x2_t r0, r1;
+  __asm__ volatile("ds_read_b128 %0, %3\n\t"
+                   "ds_read_b64_tr_b8 %1, %4\n\t"
+                   "ds_read_b64_tr_b8 %2, %5\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk), "=&v"(r0), "=&v"(r1)
+                   : "v"(ak), "v"(a0), "v"(a1)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk);
+  v[0] = __builtin_bit_cast(uint2, r0);
+  v[1] = __builtin_bit_cast(uint2, r1);
+}
+__device__ __forceinline__ void lds_read_k2_tr8x4(uint4 &k0, uint4 &k1, uint2 (&v)[4], uint32_t ak0, uint32_t ak1,
+                                                  uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  u32x4_t rk0, rk1;
+  u32x2_t r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b128 %0, %6\n\t"
+                   "ds_read_b128 %1, %7\n\t"
+                   "ds_read_b64_tr_b8 %2, %8\n\t"
+                   "ds_read_b64_tr_b8 %3, %9\n\t"
+                   "ds_read_b64_tr_b8 %4, %10\n\t"
+                   "ds_read_b64_tr_b8 %5, %11\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(rk0), "=&v"(rk1), "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(ak0), "v"(ak1), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+                   : "memory");
+  k0 = __builtin_bit_cast(uint4, rk0);
+  k1 = __builtin_bit_cast(uint4, rk1);
+  v[0] = __builtin_bit_cast(uint2, r0);
+  v[1] = __builtin_bit_cast(uint2, r1);
+  v[2] = __builtin_bit_cast(uint2, r2);
+  v[3] = __builtin_bit_cast(uint2, r3);
+}
 // K pieces only (two per block)
 __device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, uint32_t a1) {
   u32x4_t r0, r1;
@@ -269,11 +312,18 @@ __device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, u
 // lane 16 q4 + 4 r + c points at the four dims of slice w that output rows
 // 4 c .. 4 c + 3 hold (out_dim) in token row 4 q4 + r, so lane (i, q4) gets
 // keys 4 q4 .. 4 q4 + 3 of dim row i, the A-operand layout of the P.V product.
+// INT4 V: one 8-bit transposing read per 64-dim block (32 bytes of a row);
+// lane 16 q4 + 2 r + h points at token row 4 q4 + r % 4, bytes
+// 16 (r / 4) + 8 h .. + 7 of the block, so lane i of quarter q4 gets byte i
+// (dims 2 i, 2 i + 1) of keys 4 q4 + 0..3 in its low dword and byte 16 + i
+// (dims 32 + 2 i, 33 + 2 i) of the same keys in its high dword.
 template <int DE, int KT>
 struct StageReader {
   using S = Shape<DE, KT>;
   static constexpr bool kVt = vt_from_lds<DE, KT>();
-  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : 1;
+  static constexpr bool kVn = vt_int4<KT>();
+  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : (kVn ? DE / 64 : 1);
+  static_assert(!kVn || DE == 128 || DE == 256, "INT4 rows of 64 or 128 bytes");
   uint32_t k_addr[S::kLaneVec];
   uint32_t vt_addr[kVtAddr];
   __device__ __forceinline__ void init(uint32_t tile0, int lane) {
@@ -282,6 +332,14 @@ struct StageReader {
 #pragma unroll
     for (int pc = 0; pc < S::kLaneVec; ++pc)
       k_addr[pc] = tile0 + c16 * S::kRowBytes + ((4 * pc + q4) ^ swz) * 16;
+    if constexpr (kVn) {
+      const int r = c16 >> 1, h = c16 & 1;
+      const int row = 4 * q4 + (r & 3);
+      const int vswz = stage_swizzle<DE, KT>(row);
+#pragma unroll
+      for (int blk = 0; blk < kVtAddr; ++blk)
+        vt_addr[blk] = tile0 + S::kTileBytes + row * S::kRowBytes + (((2 * blk + (r >> 2)) ^ vswz) * 16) + 8 * h;
+    }
     if constexpr (kVt) {
       const int r = (lane >> 2) & 3, c = lane & 3;
       const int row = 4 * q4 + r;
@@ -295,7 +353,13 @@ struct StageReader {
   }
   // t <- the tile whose K rows start `off` bytes after tile0 (reads complete on return)
   __device__ __forceinline__ void read(TileRegs<DE, KT> &t, uint32_t off) const {
-    if constexpr (kVt) {
+    if constexpr (kVn) {
+      if constexpr (DE == 128)
+        lds_read_k1_tr8x2(t.k[0], t.vn, k_addr[0] + off, vt_addr[0] + off, vt_addr[1] + off);
+      else
+        lds_read_k2_tr8x4(t.k[0], t.k[1], t.vn, k_addr[0] + off, k_addr[1] + off, vt_addr[0] + off,
+                          vt_addr[1] + off, vt_addr[2] + off, vt_addr[3] + off);
+    } else if constexpr (kVt) {
 #pragma unroll
       for (int pc = 0; pc < S::kLaneVec; pc += 2) lds_read_k2(t.k[pc], t.k[pc + 1], k_addr[pc] + off, k_addr[pc + 1] + off);
 #pragma unroll
@@ -371,8 +435,9 @@ __device__ __forceinline__ int k_elem_dim(int j, int q4, int e) {
 template <int DE, int KT>
 __device__ __forceinline__ int out_dim(int w, int q4) {
   if constexpr (KT == DT_INT4) {
-    const int pc = w >> 3, dw = (w & 7) >> 1; // slice w: the even (w even) or odd nibbles of dword dw
-    return 32 * (4 * pc + q4) + 8 * dw + (w & 1);
+    // slice w of 64-dim block w / 4: the even (w even) or odd dims of its
+    // first (w % 4 < 2) or second 32 dims; matrix row m is dim 2 m (+ 1)
+    return 64 * (w >> 2) + 32 * ((w >> 1) & 1) + (w & 1) + 8 * q4;
   } else {
     constexpr int per_piece = Shape<DE, KT>::kEpp / 4; // slices per 16-byte piece
     return (4 * (w / per_piece) + q4) * Shape<DE, KT>::kEpp + 4 * (w % per_piece);
@@ -436,7 +501,7 @@ __device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w
 }
 
 // Operands of the V transposition for lane (c16, q4): a bf16 identity
-// (16x16x16 products) and, for fp8, 0/1 selections of one code per
+// (16x16x16 products; bf16 at head_dim 256) and, for fp8, 0/1 selections of one code per
 // 16x16x32 product (the fp8 pattern 0x38 is 1.0).
 template <int KT>
 __device__ __forceinline__ void transpose_operands(int c16, int q4, s16x4_t &ident, long (&sel)[2]) {
@@ -581,6 +646,7 @@ __device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Pa
 // non-finite value there must not reach the P.V product.
 template <int DE, int KT>
 __device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16, int q4) {
+  if constexpr (KT == DT_INT4) return; // every INT4 code is a finite value
   if (ts < lo) {
     if constexpr (vt_from_lds<DE, KT>()) { // V^T: lane (c16, q4) holds keys ts + 4 q4 + e
 #pragma unroll
@@ -679,7 +745,8 @@ __device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, c
 }
 
 // V^T slices of a staged tile as bf16 operands: va[w] holds, in lane
-// (c16, q4), keys 4 * q4 + r of dimension c16 of the 16-dim slice w.
+// (c16, q4), keys 4 * q4 + r of matrix row c16 of slice w (the 16 dims
+// out_dim describes).
 template <int DE, int KT>
 __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, const long (&sel)[2],
                                          s16x4_t *va) {
@@ -689,18 +756,25 @@ __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t iden
     for (int w = 0; w < S::kOTiles; ++w) va[w] = t.vt[w];
     return;
   }
+  if constexpr (vt_int4<KT>()) { // 4 keys x 4 dims per read: nibbles -> 136 + n
+#pragma unroll
+    for (int blk = 0; blk < DE / 64; ++blk) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t x = hf ? t.vn[blk].y : t.vn[blk].x;
+        const uint32_t ev = int4_even(x), od = int4_odd(x);
+        va[4 * blk + 2 * hf] = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(ev), offset_bf16_hi(ev)));
+        va[4 * blk + 2 * hf + 1] = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(od), offset_bf16_hi(od)));
+      }
+    }
+    return;
+  }
   // all products first, so the dependent conversions do not wait on each other
   f32x4_t vt[S::kOTiles];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w) {
-    if constexpr (KT == DT_INT4) {
-      // even (w even) or odd nibbles of dword (w / 2) % 4 of piece w / 8, as 136 + n
-      const uint32_t dw = dword_of(t.v[w >> 3], (w >> 1) & 3);
-      const uint32_t nib = (w & 1) ? int4_odd(dw) : int4_even(dw);
-      const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
-      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
-    } else if constexpr (KT == DT_FP8) {
+    if constexpr (KT == DT_FP8) {
       const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
       const uint4 wv = t.v[u >> 1];
       const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
