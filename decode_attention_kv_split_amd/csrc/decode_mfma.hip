@@ -26,11 +26,10 @@
 //     p = exp2(s - reference), running sum.
 //   * V^T with tokens 4*q4 + r of one head dimension in lane c16 -- the
 //     operand layout the next product needs: bf16 (pack width <= 128) reads
-//     it straight from LDS with 16-bit transposing reads, INT4 with 8-bit
-//     ones (4 keys x 4 dims of nibbles per lane, turned into 136 + n by byte
-//     permutes); otherwise the V tile is multiplied by an identity (bf16,
-//     16x16x16) or by a 0/1 selection (fp8, 16x16x32 fp8, which also decodes
-//     the codes exactly into fp32).
+//     it straight from LDS with 16-bit transposing reads; fp8 and INT4 with
+//     8-bit ones (4 keys of 2 fp8 dims or 4 INT4 dims per lane), converted
+//     exactly to bf16 (fp8) or to 136 + n by byte permutes (INT4); wider bf16
+//     tiles are multiplied by an identity (16x16x16).
 //   * O^T[dim][query head] += V^T . P^T with v_mfma_f32_16x16x16_bf16; lane
 //     keeps four dims per 16-dim slice w (see out_dim) of query
 //     head c16, so the running max, sum and rescale of a head never leave its
@@ -121,9 +120,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   float cscale = p.score_scale;
   if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg * PACK + min(my_kv, PACK - 1)];
   const float cap_out = p.cap_out;
-  s16x4_t ident;
-  long sel[2];
-  transpose_operands<KT>(c16, q4, ident, sel);
+  const s16x4_t ident = transpose_identity(c16, q4);
 
   // ---- addressing ----
   const size_t row_bytes = (size_t)Hk * (S::kRowBytes / PACK); // bytes between consecutive tokens
@@ -188,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
     const int ts = a0 + (ft + wave + i * kWaves) * kTile;
     zero_v_before(t, ts, w_lo, c16, q4); // rows before the first key any column sees
-    tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+    tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, q4);
   };
 
   // Ring of NBUF staging slots per wave.  A slot is refilled as soon as its

@@ -119,8 +119,8 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
 }
 
 // bf16 tiles up to 128 pack dims take V^T straight from LDS (16-bit
-// transposing reads), INT4 tiles from 8-bit transposing reads (vt_int4);
-// wider bf16 tiles and fp8 transpose V with a matrix product.  At
+// transposing reads), fp8 and INT4 tiles from 8-bit transposing reads
+// (vt_tr8); wider bf16 tiles transpose V with a matrix product.  At
 // head_dim 256 the transposed slices, read together with K, held registers
 // the pair-wise prefill kernel needed (8192-row prefill: 147 against 158
 // TFLOP/s); at head_dim 128 they gained (2048 rows on a 32k cache: 499
@@ -128,15 +128,15 @@ __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, char *lds
 template <int DE, int KT>
 constexpr bool vt_from_lds() { return KT == DT_BF16 && DE <= 128; }
 template <int KT>
-constexpr bool vt_int4() { return KT == DT_INT4; }
+constexpr bool vt_tr8() { return KT == DT_FP8 || KT == DT_INT4; }
 
 template <int DE, int KT>
 struct TileRegs {
-  static constexpr int kNibBlocks = KT == DT_INT4 ? DE / 64 : 1;
+  static constexpr int kTr8Blocks = vt_tr8<KT>() ? Shape<DE, KT>::kRowBytes / 32 : 1;
   uint4 k[Shape<DE, KT>::kLaneVec];    // K pieces 4 * pc + q4 of row c16
-  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (fp8)
+  uint4 v[Shape<DE, KT>::kLaneVec];    // V pieces (bf16 beyond 128 pack dims)
   s16x4_t vt[Shape<DE, KT>::kOTiles];  // V^T slices read transposed from LDS (vt_from_lds)
-  uint2 vn[kNibBlocks];                // INT4: V codes of 4 keys x 4 dims per 64-dim block (vt_int4)
+  uint2 vn[kTr8Blocks];                // fp8 / INT4: V codes of 4 keys per 32-byte block (vt_tr8)
 };
 
 // Transposing LDS reads (gfx950 ds_read_b64_tr_b16): within each 16-lane
@@ -254,8 +254,8 @@ __device__ __forceinline__ void lds_read_tr_x8(s16x4_t (&v)[8], const uint32_t (
   v[6] = __builtin_bit_cast(s16x4_t, r6);
   v[7] = __builtin_bit_cast(s16x4_t, r7);
 }
-// INT4 tiles: the lane's K pieces and one 8-bit transposing read
-// (ds_read_b64_tr_b8, layout as for lds_read_tr8_x8) per 64-dim block of V,
+// fp8 / INT4 tiles: the lane's K pieces and one 8-bit transposing read
+// (ds_read_b64_tr_b8, layout as for lds_read_tr8_x8) per 32-byte block of V,
 // one wait.
 __device__ __forceinline__ void lds_read_k1_tr8x2(uint4 &k0, uint2 (&v)[2], uint32_t ak, uint32_t a0, uint32_t a1) {
   u32x4_t rk;
@@ -312,18 +312,19 @@ __device__ __forceinline__ void lds_read_k2(uint4 &k0, uint4 &k1, uint32_t a0, u
 // lane 16 q4 + 4 r + c points at the four dims of slice w that output rows
 // 4 c .. 4 c + 3 hold (out_dim) in token row 4 q4 + r, so lane (i, q4) gets
 // keys 4 q4 .. 4 q4 + 3 of dim row i, the A-operand layout of the P.V product.
-// INT4 V: one 8-bit transposing read per 64-dim block (32 bytes of a row);
+// fp8 / INT4 V: one 8-bit transposing read per 32-byte block of a row;
 // lane 16 q4 + 2 r + h points at token row 4 q4 + r % 4, bytes
 // 16 (r / 4) + 8 h .. + 7 of the block, so lane i of quarter q4 gets byte i
-// (dims 2 i, 2 i + 1) of keys 4 q4 + 0..3 in its low dword and byte 16 + i
-// (dims 32 + 2 i, 33 + 2 i) of the same keys in its high dword.
+// of the block for keys 4 q4 + 0..3 in its low dword and byte 16 + i of the
+// same keys in its high dword (fp8: dims i and 16 + i of the block; INT4:
+// dims 2 i, 2 i + 1 and 32 + 2 i, 33 + 2 i).
 template <int DE, int KT>
 struct StageReader {
   using S = Shape<DE, KT>;
   static constexpr bool kVt = vt_from_lds<DE, KT>();
-  static constexpr bool kVn = vt_int4<KT>();
-  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : (kVn ? DE / 64 : 1);
-  static_assert(!kVn || DE == 128 || DE == 256, "INT4 rows of 64 or 128 bytes");
+  static constexpr bool kVn = vt_tr8<KT>();
+  static constexpr int kVtAddr = kVt ? S::kOTiles / 2 : (kVn ? S::kRowBytes / 32 : 1);
+  static_assert(!kVn || (S::kRowBytes >= 64 && S::kRowBytes <= 256), "rows of 64 to 256 bytes");
   uint32_t k_addr[S::kLaneVec];
   uint32_t vt_addr[kVtAddr];
   __device__ __forceinline__ void init(uint32_t tile0, int lane) {
@@ -354,11 +355,18 @@ struct StageReader {
   // t <- the tile whose K rows start `off` bytes after tile0 (reads complete on return)
   __device__ __forceinline__ void read(TileRegs<DE, KT> &t, uint32_t off) const {
     if constexpr (kVn) {
-      if constexpr (DE == 128)
-        lds_read_k1_tr8x2(t.k[0], t.vn, k_addr[0] + off, vt_addr[0] + off, vt_addr[1] + off);
-      else
-        lds_read_k2_tr8x4(t.k[0], t.k[1], t.vn, k_addr[0] + off, k_addr[1] + off, vt_addr[0] + off,
-                          vt_addr[1] + off, vt_addr[2] + off, vt_addr[3] + off);
+      if constexpr (S::kLaneVec == 1) {
+        uint2 (&vn)[2] = *reinterpret_cast<uint2 (*)[2]>(&t.vn[0]);
+        lds_read_k1_tr8x2(t.k[0], vn, k_addr[0] + off, vt_addr[0] + off, vt_addr[1] + off);
+      } else {
+#pragma unroll
+        for (int pc = 0; pc < S::kLaneVec; pc += 2) {
+          uint2 (&vn)[4] = *reinterpret_cast<uint2 (*)[4]>(&t.vn[2 * pc]);
+          lds_read_k2_tr8x4(t.k[pc], t.k[pc + 1], vn, k_addr[pc] + off, k_addr[pc + 1] + off,
+                            vt_addr[2 * pc] + off, vt_addr[2 * pc + 1] + off, vt_addr[2 * pc + 2] + off,
+                            vt_addr[2 * pc + 3] + off);
+        }
+      }
     } else if constexpr (kVt) {
 #pragma unroll
       for (int pc = 0; pc < S::kLaneVec; pc += 2) lds_read_k2(t.k[pc], t.k[pc + 1], k_addr[pc] + off, k_addr[pc + 1] + off);
@@ -438,6 +446,8 @@ __device__ __forceinline__ int out_dim(int w, int q4) {
     // slice w of 64-dim block w / 4: the even (w even) or odd dims of its
     // first (w % 4 < 2) or second 32 dims; matrix row m is dim 2 m (+ 1)
     return 64 * (w >> 2) + 32 * ((w >> 1) & 1) + (w & 1) + 8 * q4;
+  } else if constexpr (KT == DT_FP8) {
+    return 16 * w + 4 * q4; // slice w: byte 16 (w % 2) + m of 32-byte block w / 2 is row m
   } else {
     constexpr int per_piece = Shape<DE, KT>::kEpp / 4; // slices per 16-byte piece
     return (4 * (w / per_piece) + q4) * Shape<DE, KT>::kEpp + 4 * (w % per_piece);
@@ -500,23 +510,14 @@ __device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w
   return true;
 }
 
-// Operands of the V transposition for lane (c16, q4): a bf16 identity
-// (16x16x16 products; bf16 at head_dim 256) and, for fp8, 0/1 selections of one code per
-// 16x16x32 product (the fp8 pattern 0x38 is 1.0).
-template <int KT>
-__device__ __forceinline__ void transpose_operands(int c16, int q4, s16x4_t &ident, long (&sel)[2]) {
+// The bf16 identity operand of lane (c16, q4) for the V transposition by a
+// 16x16x16 product (bf16 tiles wider than 128 pack dims).
+__device__ __forceinline__ s16x4_t transpose_identity(int c16, int q4) {
   const short one_bf16 = 0x3F80;
+  s16x4_t ident;
 #pragma unroll
   for (int e = 0; e < 4; ++e) ident[e] = (4 * q4 + e == c16) ? one_bf16 : (short)0;
-  sel[0] = sel[1] = 0;
-  if (KT == DT_FP8) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      uint64_t s = 0;
-      if (q4 == (c16 >> 2)) s = (uint64_t)0x38 << (8 * (4 * hh + (c16 & 3)));
-      sel[hh] = (long)s;
-    }
-  }
+  return ident;
 }
 
 // ---- column groups: per-lane state shared by the two partial kernels ----
@@ -648,7 +649,17 @@ template <int DE, int KT>
 __device__ __forceinline__ void zero_v_before(TileRegs<DE, KT> &t, int ts, int lo, int c16, int q4) {
   if constexpr (KT == DT_INT4) return; // every INT4 code is a finite value
   if (ts < lo) {
-    if constexpr (vt_from_lds<DE, KT>()) { // V^T: lane (c16, q4) holds keys ts + 4 q4 + e
+    if constexpr (vt_tr8<KT>()) { // fp8 V codes: byte e of each dword is key ts + 4 q4 + e
+      uint32_t keep = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ts + 4 * q4 + e >= lo) keep |= 0xFFu << (8 * e);
+#pragma unroll
+      for (int k = 0; k < TileRegs<DE, KT>::kTr8Blocks; ++k) {
+        t.vn[k].x &= keep;
+        t.vn[k].y &= keep;
+      }
+    } else if constexpr (vt_from_lds<DE, KT>()) { // V^T: lane (c16, q4) holds keys ts + 4 q4 + e
 #pragma unroll
       for (int w = 0; w < Shape<DE, KT>::kOTiles; ++w)
 #pragma unroll
@@ -748,15 +759,29 @@ __device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, c
 // (c16, q4), keys 4 * q4 + r of matrix row c16 of slice w (the 16 dims
 // out_dim describes).
 template <int DE, int KT>
-__device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, const long (&sel)[2],
-                                         s16x4_t *va) {
+__device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, s16x4_t *va) {
   using S = Shape<DE, KT>;
   if constexpr (vt_from_lds<DE, KT>()) { // read transposed from LDS already
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) va[w] = t.vt[w];
     return;
   }
-  if constexpr (vt_int4<KT>()) { // 4 keys x 4 dims per read: nibbles -> 136 + n
+  if constexpr (KT == DT_FP8) { // 4 keys x 2 dims per read: codes -> bf16, exactly
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+#pragma unroll
+    for (int blk = 0; blk < TileRegs<DE, KT>::kTr8Blocks; ++blk) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t x = hf ? t.vn[blk].y : t.vn[blk].x;
+        const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+        const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+        va[2 * blk + hf] = __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, a),
+                                                                  __builtin_bit_cast(uint32_t, b)));
+      }
+    }
+    return;
+  }
+  if constexpr (KT == DT_INT4) { // 4 keys x 4 dims per read: nibbles -> 136 + n
 #pragma unroll
     for (int blk = 0; blk < DE / 64; ++blk) {
 #pragma unroll
@@ -769,23 +794,15 @@ __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t iden
     }
     return;
   }
-  // all products first, so the dependent conversions do not wait on each other
+  // bf16 beyond 128 pack dims: V times an identity, all products first, so
+  // the dependent conversions do not wait on each other
   f32x4_t vt[S::kOTiles];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w) {
-    if constexpr (KT == DT_FP8) {
-      const int u = w >> 1, hh = w & 1; // 8-byte group u of the lane slice
-      const uint4 wv = t.v[u >> 1];
-      const uint32_t lo32 = (u & 1) ? wv.z : wv.x;
-      const uint32_t hi32 = (u & 1) ? wv.w : wv.y;
-      const long a = (long)(((uint64_t)hi32 << 32) | lo32);
-      vt[w] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[hh], zero, 0, 0, 0);
-    } else {
-      const uint4 wv = t.v[w >> 1];
-      const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
-      vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
-    }
+    const uint4 wv = t.v[w >> 1];
+    const s16x4_t a = __builtin_bit_cast(s16x4_t, (w & 1) ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
+    vt[w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, ident, zero, 0, 0, 0);
   }
 #pragma unroll
   for (int w = 0; w < S::kOTiles; ++w)
@@ -795,11 +812,10 @@ __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t iden
 // One staged 16-token tile (first key ts) through every column group:
 // scores, online-softmax step, then O^T += V^T . P^T with the V^T slices
 // shared by the groups.  [all_lo, all_hi): keys every column sees.
-// ident / sel: the identity and 0/1 selection operands of the V transposition.
+// ident: the identity operand of the V transposition (transpose_identity).
 template <int DE, int KT, int CG>
 __device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &t, int ts, int all_lo,
-                                            int all_hi, float cscale, float cap_out, s16x4_t ident,
-                                            const long (&sel)[2], int q4) {
+                                            int all_hi, float cscale, float cap_out, s16x4_t ident, int q4) {
   using S = Shape<DE, KT>;
   const bool whole = ts >= all_lo && ts + kTile <= all_hi;
   s16x4_t pt[CG]; // P^T operand of each group
@@ -813,7 +829,7 @@ __device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const Til
     pt[c] = __builtin_bit_cast(s16x4_t, make_uint2(pk[0], pk[1]));
   }
   s16x4_t va[S::kOTiles];
-  v_slices(t, ident, sel, va);
+  v_slices(t, ident, va);
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     if (c > 0 && !cs.on[c]) continue;
@@ -832,8 +848,7 @@ __device__ __forceinline__ void tile_update(ColumnSet<DE, KT, CG> &cs, const Til
 template <int DE, int KT, int CG>
 __device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const TileRegs<DE, KT> &ta, int tsa,
                                             const TileRegs<DE, KT> &tb, int tsb, int all_lo, int all_hi,
-                                            float cscale, float cap_out, s16x4_t ident, const long (&sel)[2],
-                                            int q4) {
+                                            float cscale, float cap_out, s16x4_t ident, int q4) {
   using S = Shape<DE, KT>;
   const bool whole_a = tsa >= all_lo && tsa + kTile <= all_hi;
   const bool whole_b = tsb >= all_lo && tsb + kTile <= all_hi;
@@ -849,8 +864,8 @@ __device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const Til
     pt[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   }
   s16x4_t va[S::kOTiles], vb[S::kOTiles];
-  v_slices(ta, ident, sel, va);
-  v_slices(tb, ident, sel, vb);
+  v_slices(ta, ident, va);
+  v_slices(tb, ident, vb);
 #pragma unroll
   for (int c = 0; c < CG; ++c) {
     if (c > 0 && !cs.on[c]) continue;

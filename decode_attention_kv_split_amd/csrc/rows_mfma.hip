@@ -77,9 +77,7 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
   float cscale = p.score_scale;
   if (KT != DT_BF16) cscale *= p.k_scale[b * Hk + kvg];
   const float cap_out = p.cap_out;
-  s16x4_t ident;
-  long sel[2];
-  transpose_operands<KT>(c16, q4, ident, sel);
+  const s16x4_t ident = transpose_identity(c16, q4);
 
   // ---- addressing: this wave's tile of block i, one block per lane ----
   // (a block holds kBlock keys and chunks at most 64 * kBlock, so 64 lanes
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
                 read_stage(tb, j, u + 1);
                 zero_v_before(ta, tsa, wv_lo, c16, q4);
                 zero_v_before(tb, tsb, wv_lo, c16, q4);
-                pair_update(cs, ta, tsa, tb, tsb, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+                pair_update(cs, ta, tsa, tb, tsb, all_lo, all_hi, cscale, cap_out, ident, q4);
               }
             }
           } else {
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
                 TileRegs<D, KT> t;
                 read_stage(t, j, u);
                 zero_v_before(t, ts, wv_lo, c16, q4);
-                tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, sel, q4);
+                tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, q4);
               }
             }
           }
