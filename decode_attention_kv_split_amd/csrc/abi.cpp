@@ -167,6 +167,7 @@ struct Columns {
   int col_share = 1;  // groups per partial workgroup
   int col_blocks = 1; // partial workgroups per (item, KV head) along the columns
   int cols = 0;       // partial-result columns per KV head over all groups
+  int most = 1;       // query rows of the longest request
 };
 
 Columns columns_of(const kvs_decode_args *a) {
@@ -180,6 +181,7 @@ Columns columns_of(const kvs_decode_args *a) {
     c.nq[b] = a->qo_indptr_host[b + 1] - a->qo_indptr_host[b];
     most = std::max(most, c.nq[b]);
   }
+  c.most = most;
   c.col_groups = std::max(1, (int)(((int64_t)most * group + 15) / 16));
   c.col_share = kvs::mfma_col_share(a->head_dim, a->kv_dtype, c.col_groups);
   c.col_blocks = (c.col_groups + c.col_share - 1) / c.col_share;
@@ -274,6 +276,11 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.col_groups = cols.col_groups;
   p.col_share = cols.col_share;
   p.cols = a->qo_indptr_host ? 16 : p.group * p.pack;
+  // The chunks of a request differ in work only when its query rows reach
+  // over more than one chunk (the early rows stop before the late chunks);
+  // only then do the multi-row kernels deal their workgroups to the XCDs by
+  // work rather than in launch order, which keeps one chunk per XCD.
+  p.rows_xcd_order = cols.most > pl.chunk ? 1 : 0;
   p.page_size = a->page_size;
   p.page_shift = a->page_size > 0 ? log2i(a->page_size) : 0;
   p.window = a->window;

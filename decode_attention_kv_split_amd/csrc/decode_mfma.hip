@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 
   // ---- which (request, split) is this workgroup? ----
   int b, split, nb, L;
-  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  if (!locate_item(p, w, item, blockIdx.y == 0, s_scan, s_item, b, split, nb, L)) return;
 
   // ---- columns: query heads of the pack, or (query row, head) pairs ----
   const int nq = req_nq(p, b);

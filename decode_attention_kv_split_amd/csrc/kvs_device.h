@@ -85,6 +85,7 @@ struct Params {
   int col_groups; // groups of 16 (query, head) columns per KV head (1 for one query)
   int col_share;  // column groups one partial workgroup computes together (1 or 2)
   int cols;       // columns per partial slot: group * pack (one query) or 16
+  int rows_xcd_order; // multi-row kernels: workgroups in the XCD-balanced order (rows_order)
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
   float score_scale; // sm_scale * log2(e); with a soft cap c: sm_scale / c

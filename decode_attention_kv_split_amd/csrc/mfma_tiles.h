@@ -478,8 +478,10 @@ __device__ __forceinline__ bf16x8_t k_operand(const TileRegs<DE, KT> &t, int j) 
 // device lengths (which also records each request's first item and split
 // count for the merge).  Returns false, the same in every thread, when the
 // device lengths disagree with the planned launch.  Every thread calls it.
-__device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w, int item, int *s_scan, int *s_item,
-                                            int &b, int &split, int &nb, int &L) {
+// record_meta: this workgroup records the split metadata of its request when
+// it holds the request's first split (one workgroup per item may).
+__device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w, int item, bool record_meta,
+                                            int *s_scan, int *s_item, int &b, int &split, int &nb, int &L) {
   if (w.n_items > 0) { // planned on the host
     const uint32_t e = w.item[item];
     b = (int)(e >> 16);
@@ -502,12 +504,41 @@ __device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w
   split = __builtin_amdgcn_readfirstlane(s_item[1]);
   nb = __builtin_amdgcn_readfirstlane(s_item[2]);
   if (b < 0) return false;
-  if (p.meta && split == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+  if (p.meta && split == 0 && record_meta && threadIdx.x == 0) {
     p.meta[2 * b] = s_item[3];
     p.meta[2 * b + 1] = nb;
   }
   L = p.kv_len[b];
   return true;
+}
+
+// Order of the multi-row kernels' workgroups.  The launch grid is (items,
+// KV heads x row blocks); the hardware deals workgroups to the XCDs in turn
+// by linear id (x fastest).  Read in launch order, XCD k always gets the
+// items congruent to k.  That keeps one chunk per XCD, and it is balanced
+// when the items hold equal work; in a causal prefill longer than a chunk the
+// early chunks hold far more work than the late ones (a 16384-row prefill in
+// 4 chunks: 1.7x the mean on two XCDs).  There (balanced) the linear id is
+// mapped to (KV head, item, row block), row block fastest: with a multiple
+// of kXcds KV heads each XCD takes whole heads, their items and row blocks in
+// turn (the row blocks of one chunk run together and share it in that XCD's
+// L2); otherwise consecutive row blocks go to consecutive XCDs.  Either way
+// each XCD gets about the same work.
+constexpr int kXcds = 8;
+struct RowsOrder {
+  int kvg, item, rb;
+};
+__device__ __forceinline__ RowsOrder rows_order(int row_blocks, int num_kv_heads, bool balanced) {
+  if (!balanced) return RowsOrder{(int)blockIdx.y / row_blocks, (int)blockIdx.x, (int)blockIdx.y % row_blocks};
+  const int nx = gridDim.x;
+  const int n = blockIdx.x + nx * blockIdx.y;
+  const int total = nx * gridDim.y;
+  const int l = num_kv_heads % kXcds == 0 ? (n % kXcds) * (total / kXcds) + n / kXcds : n;
+  RowsOrder r;
+  r.rb = l % row_blocks;
+  r.item = (l / row_blocks) % nx;
+  r.kvg = l / (row_blocks * nx);
+  return r;
 }
 
 // The bf16 identity operand of lane (c16, q4) for the V transposition by a

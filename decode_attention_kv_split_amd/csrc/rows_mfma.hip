@@ -43,15 +43,16 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int item = blockIdx.x;
   const int row_blocks = (p.col_groups + kGroups - 1) / kGroups; // workgroups per (item, KV head)
-  const int kvg = blockIdx.y / row_blocks;                       // KV head
-  const int cgw = blockIdx.y % row_blocks * kGroups;             // first column group of the workgroup
+  const RowsOrder ord = rows_order(row_blocks, p.num_kv_heads, p.rows_xcd_order != 0);
+  const int item = ord.item;
+  const int kvg = ord.kvg;                                       // KV head
+  const int cgw = ord.rb * kGroups;                              // first column group of the workgroup
   const int g = p.group;
   const int Hk = p.num_kv_heads;
 
   int b, split, nb, L;
-  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  if (!locate_item(p, w, item, kvg == 0 && ord.rb == 0, s_scan, s_item, b, split, nb, L)) return;
   const int nq = req_nq(p, b);
   if (cgw * 16 >= nq * g) return; // no column of this workgroup has a query row (uniform)
   const int lo = request_lo(L, nq, p.window);
@@ -270,15 +271,16 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j32 = lane & 31; // column of the lane (S^T, O^T) / row (K, V^T operands)
   const int h2 = lane >> 5;  // half of the wave
-  const int item = blockIdx.x;
   const int row_blocks = (p.col_groups + kGroups - 1) / kGroups;
-  const int kvg = blockIdx.y / row_blocks;
-  const int cgw = blockIdx.y % row_blocks * kGroups; // first 16-column group of the workgroup
+  const RowsOrder ord = rows_order(row_blocks, p.num_kv_heads, p.rows_xcd_order != 0);
+  const int item = ord.item;
+  const int kvg = ord.kvg;
+  const int cgw = ord.rb * kGroups; // first 16-column group of the workgroup
   const int g = p.group;
   const int Hk = p.num_kv_heads;
 
   int b, split, nb, L;
-  if (!locate_item(p, w, item, s_scan, s_item, b, split, nb, L)) return;
+  if (!locate_item(p, w, item, kvg == 0 && ord.rb == 0, s_scan, s_item, b, split, nb, L)) return;
   const int nq = req_nq(p, b);
   if (cgw * 16 >= nq * g) return; // uniform over the workgroup
   const int lo = request_lo(L, nq, p.window);
