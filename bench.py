@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299481332, "digest": "304ff43e890f6336af6408dc044335cec4868c4d03d7b4aa4086d856131da8b1"},
+        {"bytes": 2299483878, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487912166, "digest": "304ff43e890f6336af6408dc044335cec4868c4d03d7b4aa4086d856131da8b1"},
+        {"bytes": 1487912294, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538235248, "digest": "304ff43e890f6336af6408dc044335cec4868c4d03d7b4aa4086d856131da8b1"},
+        {"bytes": 538235196, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680890566, "digest": "304ff43e890f6336af6408dc044335cec4868c4d03d7b4aa4086d856131da8b1"},
+        {"bytes": 680890723, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
 }
 
 

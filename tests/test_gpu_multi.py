@@ -174,3 +174,16 @@ def test_rows_window_fp8_shared_tile(W):
     spec = dataclasses.replace(small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [40, 700, 1500]),
                                              q_len=("list", [40, 20, 33])), window=W)
     _check(make_inputs(spec, poison=True))
+
+
+@pytest.mark.parametrize("Hq,Hk,kv", [(16, 8, "bf16"), (8, 2, "bf16"), (16, 8, "int4"), (8, 2, "int4")])
+def test_fresh_prefill_longer_than_a_chunk(Hq, Hk, kv):
+    """A fresh 1024-row prefill in 256-key chunks: the rows reach over four
+    chunks, so the multi-row kernels take their XCD-balanced workgroup order
+    (whole KV heads per XCD with 8 KV heads, interleaved row blocks with 2);
+    bf16 runs the 32x32 kernel, INT4 the shared-tile kernel.  Every row
+    against the oracle."""
+    print(f"case multi fresh prefill Hq={Hq} Hk={Hk} kv={kv}", flush=True)
+    spec = DecodeSpec("freshpf", 2, Hq, Hk, 128, 16, kv, "bf16", 128 ** -0.5,
+                      lengths=("list", [1024, 700]), q_len=("list", [1024, 700]), seed=23 + Hk)
+    _check(make_inputs(spec, poison=True), kv_chunk=256)
