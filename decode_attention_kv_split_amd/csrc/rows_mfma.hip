@@ -225,13 +225,15 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
   }
 }
 
-// Several query rows per request, bf16 KV, head_dim 128, from three groups
-// of 16 columns on: 32x32 matrix tiles.  Each wave owns 32 (query row, head)
-// columns of one KV head and the workgroup's four waves share every staged
-// 64-key block (one 16-row part staged by each wave, barriers around it, as
-// in partial_rows_kernel).  Per 32-key tile and wave:
-//   * S^T[key][column] = K . Q^T with v_mfma_f32_32x32x16_bf16 over 8 steps
-//     of 16 dims: lane (i, h) = (l % 32, l / 32) feeds K row i, dims
+// Several query rows per request, bf16 or fp8 KV at head_dim 128 and bf16 at
+// 256, from three groups of 16 columns on: 32x32 matrix tiles.  Each wave
+// owns 32 (query row, head) columns of one KV head (at head_dim 256 a pair of
+// waves shares them, each keeping half of the output dims) and the
+// workgroup's four waves share every staged block of keys (one part staged
+// by each wave, barriers around it, as in partial_rows_kernel).  Per 32-key
+// tile and wave:
+//   * S^T[key][column] = K . Q^T with v_mfma_f32_32x32x16_bf16 over
+//     head_dim / 16 steps of 16 dims: lane (i, h) = (l % 32, l / 32) feeds K row i, dims
 //     16 s + 8 h .. + 7, read from LDS; the result holds, in lane (j, h),
 //     keys 8 (v / 4) + 4 h + v % 4 (register v) of column j.
 //   * online softmax per column over its 32 keys, which sit in lanes j and
@@ -250,16 +252,29 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
 // are exactly the keys of a lane's P^T operand, operand row i of K reads the
 // staged row pi(i), pi swapping bits 3 and 2 of the row within each 16; score
 // row R then belongs to key pi(R).
-template <int KT, int NBUF>
+template <int D, int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params p, const InlineWork w) {
-  static_assert(KT == DT_BF16 || KT == DT_FP8, "bf16 or fp8 KV");
+  static_assert((D == 128 && (KT == DT_BF16 || KT == DT_FP8)) || (D == 256 && KT == DT_BF16),
+                "bf16 or fp8 at head_dim 128, bf16 at 256");
   constexpr bool kFp8 = KT == DT_FP8;
-  constexpr int D = 128;
-  using S = Shape<D, KT>;                         // bf16: 256-byte rows, 16 pieces; fp8: 128, 8
+  using S = Shape<D, KT>;                         // bf16: 16 pieces a row per 128 dims; fp8: 8
   constexpr int kRowBytes = S::kRowBytes;         // one key's K (or V) row of the head
-  constexpr int kBlock = kWaves * kTile;          // 64 keys staged per block
+  // head_dim 256: waves 2 c and 2 c + 1 share column set c; both form the
+  // scores over all dims (the same softmax state), each keeps the O^T dims
+  // 128 w % 2 .. + 127.  Keys are staged 8 rows per wave (32-key blocks) so
+  // that two 32 KB block slots still leave two workgroups per CU.
+  constexpr bool kSplitD = D == 256;
+  constexpr int kColWaves = kSplitD ? kWaves / 2 : kWaves; // 32-column sets per workgroup
+  constexpr int kPart = kSplitD ? 8 : kTile;      // rows each wave stages per block
+  constexpr int kBlock = kWaves * kPart;          // keys staged per block (64 or 32)
+  constexpr int kTiles32 = kBlock / 32;           // 32-key tiles per block
   constexpr int kHalf = kBlock * kRowBytes;       // K (or V) bytes of a block
-  constexpr int kGroups = kWaves * 2;             // 16-column groups per workgroup
+  constexpr int kGroups = kColWaves * 2;          // 16-column groups per workgroup
+  constexpr int kDmaP = kPart * kRowBytes / 1024; // 16-byte DMA loads per wave part (K or V)
+  constexpr int kSteps = D / 16;                  // 32x32x16 products of S^T per tile
+  // blocks of the longest chunk (64 tiles per wave, 4096 keys) per lane of the offset table
+  constexpr int kLaneBlocks = 64 * kWaves * kTile / kBlock / 64;
+  static_assert(kDmaP >= 1 && kLaneBlocks >= 1 && kTiles32 >= 1, "block shape");
   typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
   __shared__ int s_scan[2 * 64];
@@ -297,9 +312,11 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const int k0 = a0 + fb * kBlock;
 
   // ---- this lane's column ----
-  const int col = cgw * 16 + wave * 32 + j32;
+  const int cw = kSplitD ? wave >> 1 : wave; // column set of the wave
+  const int dh = kSplitD ? wave & 1 : 0;     // O^T dims 128 dh .. 128 dh + 127 (head_dim 256)
+  const int col = cgw * 16 + cw * 32 + j32;
   const bool ok = col < nq * g;
-  const bool wave_on = (cgw * 16 + wave * 32) < nq * g; // the same in every lane of the wave
+  const bool wave_on = (cgw * 16 + cw * 32) < nq * g; // the same in every lane of the wave
   const int qi = col / g;
   const int qrow = p.qo_indptr[b] + qi;
   const int qhead = kvg * g + col % g;
@@ -329,11 +346,11 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 
   // Q^T operand of step s: dims 16 s + 8 h2 .. + 7 of the column's query
   // (fp8: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .., the order of its K pieces)
-  bf16x8_t qop[8];
+  bf16x8_t qop[kSteps];
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
       const int d0 = kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2;
       qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
                   : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
@@ -348,20 +365,26 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[sl][v] = 0.0f;
 
-  // ---- staging: this wave's 16-row part of block i, one block per lane ----
+  // ---- staging: this wave's kPart-row part of block i; lane l holds the
+  // offsets of blocks l + 64 q ----
   const size_t row_bytes = (size_t)Hk * kRowBytes;
   const bool paged = p.page_size > 0;
   const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
-  uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
-  if (lane < nblocks) {
-    const int ts = k0 + lane * kBlock + wave * kTile;
-    if (ts < wg_hi && ts + kTile > wg_lo) {
-      const size_t row0 =
-          paged ? (size_t)pages[ts >> p.page_shift] * p.page_size + (ts & (p.page_size - 1)) : (size_t)ts;
-      const size_t off = row0 * row_bytes;
-      voff_lo = (uint32_t)off;
-      voff_hi = (uint32_t)(off >> 32);
-      vbytes = (uint32_t)(min(kTile, wg_hi - ts) * (int)row_bytes);
+  uint32_t voff_lo[kLaneBlocks], voff_hi[kLaneBlocks], vbytes[kLaneBlocks];
+#pragma unroll
+  for (int q = 0; q < kLaneBlocks; ++q) {
+    voff_lo[q] = voff_hi[q] = vbytes[q] = 0;
+    const int bi = lane + 64 * q;
+    if (bi < nblocks) {
+      const int ts = k0 + bi * kBlock + wave * kPart;
+      if (ts < wg_hi && ts + kPart > wg_lo) {
+        const size_t row0 =
+            paged ? (size_t)pages[ts >> p.page_shift] * p.page_size + (ts & (p.page_size - 1)) : (size_t)ts;
+        const size_t off = row0 * row_bytes;
+        voff_lo[q] = (uint32_t)off;
+        voff_hi[q] = (uint32_t)(off >> 32);
+        vbytes[q] = (uint32_t)(min(kPart, wg_hi - ts) * (int)row_bytes);
+      }
     }
   }
   const char *kpool = reinterpret_cast<const char *>(p.k);
@@ -369,35 +392,49 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // lane i of load k: row k * kRowsPerDma + i / kPieces of the part, position
   // i % kPieces, which holds source piece position ^ swizzle(row) (rows of a
   // block keep the swizzle of their position within the part)
-  int dma_voff[S::kDma];
+  int dma_voff[kDmaP];
 #pragma unroll
-  for (int k = 0; k < S::kDma; ++k) {
+  for (int k = 0; k < kDmaP; ++k) {
     const int r = k * S::kRowsPerDma + lane / S::kPieces;
     const int piece = (lane % S::kPieces) ^ stage_swizzle<D, KT>(r);
     dma_voff[k] = r * (int)row_bytes + kvg * kRowBytes + piece * 16;
   }
   auto issue = [&](int i, int slot) {
-    const int li = min(i, 63);
-    const size_t base = ((size_t)__builtin_amdgcn_readlane(voff_hi, li) << 32) | __builtin_amdgcn_readlane(voff_lo, li);
-    const int nbytes = i < nblocks ? (int)__builtin_amdgcn_readlane(vbytes, li) : 0;
+    const int li = i & 63;
+    const int q = min(i >> 6, kLaneBlocks - 1); // uniform
+    uint32_t lo = voff_lo[0], hi = voff_hi[0], nb8 = vbytes[0];
+#pragma unroll
+    for (int c = 1; c < kLaneBlocks; ++c)
+      if (q == c) {
+        lo = voff_lo[c];
+        hi = voff_hi[c];
+        nb8 = vbytes[c];
+      }
+    const size_t base = ((size_t)__builtin_amdgcn_readlane(hi, li) << 32) | __builtin_amdgcn_readlane(lo, li);
+    const int nbytes = i < nblocks ? (int)__builtin_amdgcn_readlane(nb8, li) : 0;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
-    char *kst = smem + slot * 2 * kHalf + wave * kTile * kRowBytes;
+    char *kst = smem + slot * 2 * kHalf + wave * kPart * kRowBytes;
 #pragma unroll
-    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+    for (int k = 0; k < kDmaP; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
 #pragma unroll
-    for (int k = 0; k < S::kDma; ++k) dma16_to_lds(vr, kst + kHalf + 1024 * k, dma_voff[k]);
+    for (int k = 0; k < kDmaP; ++k) dma16_to_lds(vr, kst + kHalf + 1024 * k, dma_voff[k]);
   };
+  // Staged row R of a tile was written with the swizzle of its position in
+  // its wave's part.
+  auto row_swizzle = [](int row) { return stage_swizzle<D, KT>(row % kPart); };
   // K operand: bf16, step s: row j32 of the tile, piece 2 s + h2; fp8: row
-  // pi(j32), piece 2 m + h2 for steps 2 m and 2 m + 1
-  uint32_t k_addr[8];
+  // pi(j32), piece 2 m + h2 for steps 2 m and 2 m + 1.  Eight steps per LDS
+  // read block.
+  uint32_t k_addr[kSteps / 8][8];
   const int krow = kFp8 ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
   {
     const uint32_t base = lds_address(smem) + krow * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) k_addr[s] = base + (((kFp8 ? s & 3 : s) * 2 + h2) ^ stage_swizzle<D, KT>(krow)) * 16;
+    for (int s = 0; s < kSteps; ++s)
+      k_addr[s / 8][s % 8] = base + (((kFp8 ? s & 3 : s) * 2 + h2) ^ row_swizzle(krow)) * 16;
   }
   // fp8 V^T reads (ds_read_b64_tr_b8): lane 16 G + 2 r + c of group G points at
   // staged row 8 (G / 2) + r (+ 16 t), dims 32 sl + 16 (G % 2) + 8 c .. + 7
@@ -412,15 +449,16 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       for (int sl = 0; sl < 4; ++sl) {
         const int row = 16 * t + 8 * (G >> 1) + r;
         const int piece = 2 * sl + (G & 1);
-        vt8_addr[4 * t + sl] =
-            lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row)) * 16) + c * 8;
+        vt8_addr[4 * t + sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ row_swizzle(row)) * 16) + c * 8;
       }
   }
   // V^T operand reads (ds_read_b64_tr_b16): lane l = 16 G + 4 r + c of group G
   // points at key row 8 hh + 4 (G / 2) + r (+ 16 t, an immediate), dims
-  // 32 sl + 16 (G % 2) + 4 c .. + 3, i.e. piece 4 sl + 2 (G % 2) + c / 2, bytes
-  // (c % 2) * 8 of it; lane i of the group then holds keys
-  // 8 hh + 4 (G / 2) + 0..3 of dim 32 sl + 16 (G % 2) + i.
+  // 128 dh + 32 sl + 16 (G % 2) + 4 c .. + 3, i.e. piece
+  // 16 dh + 4 sl + 2 (G % 2) + c / 2, bytes (c % 2) * 8 of it; lane i of the
+  // group then holds keys 8 hh + 4 (G / 2) + 0..3 of dim
+  // 128 dh + 32 sl + 16 (G % 2) + i.  (Rows 16 .. 31 keep the swizzles of
+  // rows 0 .. 15: kPart divides 16.)
   uint32_t vt_addr[8]; // [4 hh + sl]
   if constexpr (!kFp8) {
     const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
@@ -429,8 +467,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         const int row = 8 * hh + 4 * (G >> 1) + r;
-        const int piece = 4 * sl + 2 * (G & 1) + (c >> 1);
-        vt_addr[4 * hh + sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ (row & 15)) * 16) + (c & 1) * 8;
+        const int piece = 16 * dh + 4 * sl + 2 * (G & 1) + (c >> 1);
+        vt_addr[4 * hh + sl] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ row_swizzle(row)) * 16) + (c & 1) * 8;
       }
   }
 
@@ -440,23 +478,27 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
-    bf16x8_t kop[8];
     if constexpr (kFp8) {
+      bf16x8_t kop[8];
       uint4 kr[4];
-      lds_read_x4(kr, k_addr, to);
+      lds_read_x4(kr, k_addr[0], to);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         kop[2 * m] = fp8x8_to_bf16x8(kr[m].x, kr[m].y);
         kop[2 * m + 1] = fp8x8_to_bf16x8(kr[m].z, kr[m].w);
       }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[s], st, 0, 0, 0);
     } else {
-      uint4 kr[8];
-      lds_read_x8(kr, k_addr, to);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kop[s] = __builtin_bit_cast(bf16x8_t, kr[s]);
+      for (int hb = 0; hb < kSteps / 8; ++hb) {
+        uint4 kr[8];
+        lds_read_x8(kr, k_addr[hb], to);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[8 * hb + s], st, 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[s], st, 0, 0, 0);
     // V^T operands, read while the products run: vop[t][sl]
     bf16x8_t vop[2][4];
     if constexpr (kFp8) {
@@ -540,11 +582,11 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
         const int i = it + j;
-        wait_vmem<(NBUF - 1) * 2 * S::kDma>();
+        wait_vmem<(NBUF - 1) * 2 * kDmaP>();
         __syncthreads();
         if (i < nblocks && wave_on) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int u = 0; u < kTiles32; ++u) {
             const int ts = k0 + i * kBlock + u * 2 * kTile;
             if (ts < wv_hi && ts + 2 * kTile > wv_lo) tile32(ts, j * 2 * kHalf + u * 2 * kTile * kRowBytes);
           }
@@ -570,12 +612,12 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int d0 = 32 * sl + 8 * q + 4 * h2;
+        const int d0 = 128 * dh + 32 * sl + 8 * q + 4 * h2;
         *reinterpret_cast<uint2 *>(orow + d0) =
             make_uint2(pack_bf16x2(acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv),
                        pack_bf16x2(acc[sl][4 * q + 2] * inv, acc[sl][4 * q + 3] * inv));
       }
-    if (h2 == 0 && p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
+    if (h2 == 0 && dh == 0 && p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
   } else {
     const int cg = col / 16;
     const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
@@ -584,11 +626,11 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int d0 = 32 * sl + 8 * q + 4 * h2;
+        const int d0 = 128 * dh + 32 * sl + 8 * q + 4 * h2;
         *reinterpret_cast<float4 *>(dst + d0) =
             make_float4(acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv, acc[sl][4 * q + 3] * inv);
       }
-    if (h2 == 0) p.lse_part[slot * p.cols + col % 16] = lse2;
+    if (h2 == 0 && dh == 0) p.lse_part[slot * p.cols + col % 16] = lse2;
   }
 }
 
@@ -624,7 +666,7 @@ constexpr int kRowsMinGroupsQuant = 5;
 // covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
 // all of them.
 int mfma_col_share(int head_dim, int kv_type, int col_groups) {
-  // bf16 and fp8 at head_dim 128 take the 32x32 prefill kernel there
+  // bf16 and fp8 at head_dim 128 (bf16 at 256 too) take the 32x32 prefill kernel there
   const bool tiles32 = head_dim == 128 && (kv_type == DT_BF16 || kv_type == DT_FP8);
   if (col_groups >= (kv_type == DT_BF16 || tiles32 ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
     return kWaves * (head_dim <= 128 ? 2 : 1);
@@ -636,8 +678,8 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
   constexpr int kGroups = kWaves * rows_cg<D>();
   if (p.col_share != kGroups || p.pack != 1) return hipErrorInvalidValue;
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + kGroups - 1) / kGroups));
-  if constexpr (D == 128 && (KT == DT_BF16 || KT == DT_FP8))
-    return launch_kernel(l, partial_prefill_kernel<KT, KT == DT_FP8 ? 4 : 2>, grid, p, w);
+  if constexpr ((D == 128 && (KT == DT_BF16 || KT == DT_FP8)) || (D == 256 && KT == DT_BF16))
+    return launch_kernel(l, partial_prefill_kernel<D, KT, KT == DT_FP8 ? 4 : 2>, grid, p, w);
   return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
 }
 
