@@ -500,10 +500,32 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       }
     }
     // V^T operands, read while the products run: vop[t][sl]
+    // Keys before wv_lo are seen by no column of the wave; their V rows may
+    // hold non-finite values (only visible values are required finite), and
+    // 0 * NaN would reach the accumulator, so their operand elements are
+    // zeroed (a tile starting there is not whole: its scores are masked).
+    const int vt_g = lane >> 4;
     bf16x8_t vop[2][4];
     if constexpr (kFp8) {
       uint2 v8[8];
       lds_read_tr8_x8(v8, vt8_addr, to);
+      if (ts < wv_lo) { // lane holds rows 16 t + 8 (G / 2) + e, byte e (uniform branch)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint32_t lo_keep = 0, hi_keep = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = ts + 16 * t + 8 * (vt_g >> 1) + e;
+            if (key >= wv_lo) lo_keep |= 0xFFu << (8 * e);
+            if (key + 4 >= wv_lo) hi_keep |= 0xFFu << (8 * e);
+          }
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            v8[4 * t + sl].x &= lo_keep;
+            v8[4 * t + sl].y &= hi_keep;
+          }
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -512,6 +534,18 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       s16x4_t vt[2][8]; // [t][4 hh + sl]
 #pragma unroll
       for (int t = 0; t < 2; ++t) lds_read_tr_x8(vt[t], vt_addr, to + t * 16 * kRowBytes);
+      if (ts < wv_lo) { // element e: key 16 t + 8 hh + 4 (G / 2) + e (uniform branch)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ts + 16 * t + 8 * hh + 4 * (vt_g >> 1) + e < wv_lo) {
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) vt[t][4 * hh + sl][e] = 0;
+              }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll

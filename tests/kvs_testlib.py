@@ -237,3 +237,36 @@ def check_append(ai, got):
     assert np.array_equal(raw(k_pool)[mask], raw(np.asarray(c.k))[mask]), "K pool changed outside the new slots"
     assert np.array_equal(raw(v_pool)[mask], raw(np.asarray(c.v))[mask]), "V pool changed outside the new slots"
     return ref
+
+
+# NaN codes of the stored KV formats (INT4 has none)
+_NAN_CODES = {"bf16": 0x7FC0, "fp8": 0x7F}
+
+
+def poison_invisible(inp):
+    """A copy of the workload whose K and V codes before each request's first
+    visible key (the first query row's window start) are NaN: the library
+    may require only the keys some query sees to be finite, so these must
+    not change any result.  Needs a window; bf16 and fp8 KV."""
+    import dataclasses
+
+    s = inp.spec
+    code = _NAN_CODES[s.kv_dtype]
+    k, v = np.array(inp.k, copy=True), np.array(inp.v, copy=True)
+    indptr = None if inp.qo_indptr is None else np.asarray(inp.qo_indptr)
+    touched = 0
+    for b in range(s.batch):
+        L = int(inp.kv_len[b])
+        n = 1 if indptr is None else int(indptr[b + 1] - indptr[b])
+        if n == 0 or s.window <= 0:
+            continue
+        lo = max(0, L - n - s.window + 1)  # first row's window start
+        for t in range(lo):
+            if s.page_size == 0:
+                k[t], v[t] = code, code
+            else:
+                page = int(inp.page_indices[inp.page_indptr[b] + t // s.page_size])
+                k[page, t % s.page_size], v[page, t % s.page_size] = code, code
+        touched += lo
+    assert touched > 0, "no invisible keys to poison"
+    return dataclasses.replace(inp, k=k, v=v)

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from kvs_testlib import compare, run_library
+from kvs_testlib import compare, poison_invisible, run_library
 from workloads import CONFIGS, DecodeSpec, make_inputs, small_variant
 
 pytestmark = pytest.mark.gpu
@@ -187,3 +187,23 @@ def test_fresh_prefill_longer_than_a_chunk(Hq, Hk, kv):
     spec = DecodeSpec("freshpf", 2, Hq, Hk, 128, 16, kv, "bf16", 128 ** -0.5,
                       lengths=("list", [1024, 700]), q_len=("list", [1024, 700]), seed=23 + Hk)
     _check(make_inputs(spec, poison=True), kv_chunk=256)
+
+
+@pytest.mark.parametrize("name,q_len,d,window", [
+    ("c4_paged_bf16_b64", 1, 128, 300),     # decode kernel, one row
+    ("c5_paged_fp8_b128", 1, 128, 300),
+    ("c5_paged_fp8_b128", 3, 128, 200),     # decode kernel, two column groups
+    ("c4_paged_bf16_b64", 40, 128, 250),    # 32x32 kernel, bf16
+    ("c5_paged_fp8_b128", 40, 128, 250),    # 32x32 kernel, fp8
+    ("c4_paged_bf16_b64", 40, 64, 250),     # shared-tile kernel (head_dim 64)
+    ("c4_paged_bf16_b64", 40, 256, 250),    # 32x32 kernel, head_dim 256
+])
+def test_keys_before_the_window_may_be_nan(name, q_len, d, window):
+    """K/V codes of keys no query sees (before the first row's window) are
+    NaN: every kernel must leave them out of the result (a masked weight of
+    0 times a NaN value would poison the output)."""
+    print(f"case multi NaN before window {name} q={q_len} d={d} W={window}", flush=True)
+    spec = dataclasses.replace(small_variant(name, batch=3, lengths=("list", [700, 1500, 333]),
+                                             q_len=("fixed", q_len), window=window),
+                               head_dim=d, sm_scale=d ** -0.5)
+    _check(poison_invisible(make_inputs(spec, poison=True)), kv_chunk=256)
