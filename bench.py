@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299483878, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
+        {"bytes": 2299481620, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487912294, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
+        {"bytes": 1487912271, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538235196, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
+        {"bytes": 538236713, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680890723, "digest": "da3459c6b2ff8e21b96b0202d74c69eb0bcd7a1733dfd7b911dd80452a92da32"},
+        {"bytes": 680891052, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
 }
 
 

@@ -786,43 +786,40 @@ __device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, c
   }
 }
 
+// Whether V^T slices come straight from LDS reads (no matrix product), so
+// that each slice can be formed where its P.V product uses it.
+template <int DE, int KT>
+constexpr bool v_direct() { return vt_from_lds<DE, KT>() || vt_tr8<KT>(); }
+
+// Slice w of a directly read V^T (v_direct): in lane (c16, q4), keys
+// 4 * q4 + r of matrix row c16 of slice w, as bf16 (INT4: 136 + n).
+template <int DE, int KT>
+__device__ __forceinline__ s16x4_t v_slice(const TileRegs<DE, KT> &t, int w) {
+  if constexpr (vt_from_lds<DE, KT>()) {
+    return t.vt[w];
+  } else if constexpr (KT == DT_FP8) { // 32-byte block w / 2, dword w % 2
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    const uint32_t x = (w & 1) ? t.vn[w >> 1].y : t.vn[w >> 1].x;
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    return __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)));
+  } else { // INT4: 64-dim block w / 4, dword (w / 2) % 2, even (w even) or odd nibbles
+    static_assert(KT == DT_INT4, "direct V^T");
+    const uint32_t x = ((w >> 1) & 1) ? t.vn[w >> 2].y : t.vn[w >> 2].x;
+    const uint32_t nib = (w & 1) ? int4_odd(x) : int4_even(x);
+    return __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(nib), offset_bf16_hi(nib)));
+  }
+}
+
 // V^T slices of a staged tile as bf16 operands: va[w] holds, in lane
 // (c16, q4), keys 4 * q4 + r of matrix row c16 of slice w (the 16 dims
 // out_dim describes).
 template <int DE, int KT>
 __device__ __forceinline__ void v_slices(const TileRegs<DE, KT> &t, s16x4_t ident, s16x4_t *va) {
   using S = Shape<DE, KT>;
-  if constexpr (vt_from_lds<DE, KT>()) { // read transposed from LDS already
+  if constexpr (v_direct<DE, KT>()) { // bf16 (16-bit transposing reads), fp8 and INT4 (8-bit ones)
 #pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) va[w] = t.vt[w];
-    return;
-  }
-  if constexpr (KT == DT_FP8) { // 4 keys x 2 dims per read: codes -> bf16, exactly
-    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-#pragma unroll
-    for (int blk = 0; blk < TileRegs<DE, KT>::kTr8Blocks; ++blk) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint32_t x = hf ? t.vn[blk].y : t.vn[blk].x;
-        const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
-        const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
-        va[2 * blk + hf] = __builtin_bit_cast(s16x4_t, make_uint2(__builtin_bit_cast(uint32_t, a),
-                                                                  __builtin_bit_cast(uint32_t, b)));
-      }
-    }
-    return;
-  }
-  if constexpr (KT == DT_INT4) { // 4 keys x 4 dims per read: nibbles -> 136 + n
-#pragma unroll
-    for (int blk = 0; blk < DE / 64; ++blk) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint32_t x = hf ? t.vn[blk].y : t.vn[blk].x;
-        const uint32_t ev = int4_even(x), od = int4_odd(x);
-        va[4 * blk + 2 * hf] = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(ev), offset_bf16_hi(ev)));
-        va[4 * blk + 2 * hf + 1] = __builtin_bit_cast(s16x4_t, make_uint2(offset_bf16_lo(od), offset_bf16_hi(od)));
-      }
-    }
+    for (int w = 0; w < S::kOTiles; ++w) va[w] = v_slice(t, w);
     return;
   }
   // bf16 beyond 128 pack dims: V times an identity, all products first, so
@@ -894,18 +891,22 @@ __device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const Til
     softmax_step<8>(cs, c, sv, pk);
     pt[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   }
-  s16x4_t va[S::kOTiles], vb[S::kOTiles];
-  v_slices(ta, ident, va);
-  v_slices(tb, ident, vb);
+  auto pv = [&](int w, s16x4_t sa, s16x4_t sb) {
+    const uint2 a = __builtin_bit_cast(uint2, sa), bv = __builtin_bit_cast(uint2, sb);
+    const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, bv.x, bv.y));
 #pragma unroll
-  for (int c = 0; c < CG; ++c) {
-    if (c > 0 && !cs.on[c]) continue;
+    for (int c = 0; c < CG; ++c)
+      if (c == 0 || cs.on[c]) cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pt[c], cs.acc[c][w], 0, 0, 0);
+  };
+  if constexpr (v_direct<DE, KT>()) { // each slice formed where its products use it
 #pragma unroll
-    for (int w = 0; w < S::kOTiles; ++w) {
-      const uint2 a = __builtin_bit_cast(uint2, va[w]), bv = __builtin_bit_cast(uint2, vb[w]);
-      const bf16x8_t v8 = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, bv.x, bv.y));
-      cs.acc[c][w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pt[c], cs.acc[c][w], 0, 0, 0);
-    }
+    for (int w = 0; w < S::kOTiles; ++w) pv(w, v_slice(ta, w), v_slice(tb, w));
+  } else {
+    s16x4_t va[S::kOTiles], vb[S::kOTiles];
+    v_slices(ta, ident, va);
+    v_slices(tb, ident, vb);
+#pragma unroll
+    for (int w = 0; w < S::kOTiles; ++w) pv(w, va[w], vb[w]);
   }
 }
 
