@@ -295,9 +295,37 @@ def cold_steps(step, stream, ev: "HipEvents", nbytes: int, steps: int) -> dict:
     return out
 
 
+def graph_steps(a, ws, steps: int) -> float:
+    """Microseconds per step over `steps` replays of one kvs_decode call
+    captured in a HIP graph (host launch cost out of the loop)."""
+    import torch
+
+    import decode_attention_kv_split_amd as kvs
+
+    a.prof_events[0] = a.prof_events[1] = None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call on the side stream before capture
+        st = kvs.kvs_decode(a, ws.data_ptr(), ws.numel(), side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st = kvs.kvs_decode(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    if st != kvs.KVS_OK:
+        raise kvs.KvsError(st)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / steps
+
+
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
-        q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0) -> dict:
+        q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0, graph: bool = False) -> dict:
     import dataclasses
 
     import torch
@@ -424,6 +452,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
                                frac=round(tf / PEAK_BF16_TFLOPS, 4))
     if cold:
         out["cold_cache"] = cold_steps(step, stream, HipEvents(), nbytes, max(20, steps // 2))
+    if graph:  # the same step replayed from a captured HIP graph
+        out["graph_us_per_step"] = round(graph_steps(a, ws, steps), 2)
     if not events:
         out["roofline"].update(achieved=None, frac=None, kernel_us=None, kernel_us_p10_p50_p90=None)
     if with_cpu:
@@ -581,6 +611,8 @@ def main():
                          "shows in the step time of launch-bound workloads); roofline timing fields become null")
     ap.add_argument("--cold", action="store_true",
                     help="also time single event-bracketed steps with and without a 1 GiB read before each (caches flushed)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (graph_us_per_step)")
     ap.add_argument("--probe-copy", type=int, default=0, metavar="BYTES",
                     help="only run kvs_probe_copy of BYTES bytes (hardware byte-counter calibration)")
     args = ap.parse_args()
@@ -599,7 +631,7 @@ def main():
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
-              soft_cap=args.soft_cap, kv_len=args.kv_len)
+              soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph)
     print(json.dumps(res), flush=True)
 
 
