@@ -287,3 +287,30 @@ def test_many_items_device_planned():
         o, lse = run_library(inp, kv_chunk=16, algo=algo)
         o_ref, lse_ref = oracle.decode_reference(inp)
         compare(o, lse, o_ref, lse_ref, "bf16")
+
+
+def test_python_helpers_single_and_paged():
+    """single_decode (one request, contiguous cache, q [Hq, d]) and
+    batch_decode_paged (the paged batch) give the oracle's results."""
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    print("case python helpers", flush=True)
+    spec = small_variant("c3_llama2_7b_32k", lengths=("fixed", 3000))
+    inp = make_inputs(spec)
+    t = to_torch(inp)
+    o, lse = kvs.single_decode(t["q"][0], t["k"], t["v"], sm_scale=spec.sm_scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    compare(o[None].to(torch.float64).cpu().numpy(), lse[None].to(torch.float64).cpu().numpy(), o_ref, lse_ref,
+            spec.kv_dtype)
+
+    spec = small_variant("c5_paged_fp8_b128", batch=4, lengths=("list", [5, 600, 2000, 129]))
+    inp = make_inputs(spec, poison=True)
+    t = to_torch(inp)
+    o, lse = kvs.batch_decode_paged(t["q"], t["k"], t["v"], t["page_indptr"], t["page_indices"], t["kv_len"],
+                                    kv_len_host=inp.kv_len, sm_scale=spec.sm_scale, k_scale=t["k_scale"],
+                                    v_scale=t["v_scale"])
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    compare(o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy(), o_ref, lse_ref, spec.kv_dtype)
