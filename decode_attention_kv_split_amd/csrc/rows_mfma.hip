@@ -555,12 +555,19 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
         }
     }
     // ---- scores: register v holds key ts + 8 (v / 4) + 4 h2 + v % 4 ----
+    // Without a soft cap the scale goes into the exponent: the max of the
+    // raw scores times the (positive) scale is the max of the scaled ones,
+    // and p = exp2(fma(s, scale, -m)) needs no separate multiply.  With a cap
+    // the capped scores are formed first and ks is 1.
+    const bool capped = cap_out > 0.0f; // uniform
+    const float ks = capped ? 1.0f : cscale;
     float sv[16];
+    if (capped) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sv[v] = st[v] * cscale;
-    if (cap_out > 0.0f) {
+      for (int v = 0; v < 16; ++v) sv[v] = tanhf(st[v] * cscale) * cap_out;
+    } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sv[v] = tanhf(sv[v]) * cap_out;
+      for (int v = 0; v < 16; ++v) sv[v] = st[v];
     }
     if (ts < all_lo || ts + 2 * kTile > all_hi) { // some column misses some key (uniform)
 #pragma unroll
@@ -574,6 +581,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = xor32_max(mx);
+    mx = mx == -INFINITY ? -INFINITY : mx * ks; // in scaled units (-inf stays, even for a zero scale)
     // lazy rescale (as in the 16x16 kernels): the reference moves only when a
     // score exceeds it by more than kLazy
     const bool empty = l_run == 0.0f;
@@ -592,8 +600,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     float sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      const float p0 = live ? __builtin_amdgcn_exp2f(sv[v] - m_run) : 0.0f;
-      const float p1 = live ? __builtin_amdgcn_exp2f(sv[v + 1] - m_run) : 0.0f;
+      const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
+      const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
       sum += p0 + p1;
       pk[v / 2] = pack_bf16x2(p0, p1);
     }
