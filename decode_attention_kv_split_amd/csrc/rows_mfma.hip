@@ -558,9 +558,11 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     // Without a soft cap the scale goes into the exponent: the max of the
     // raw scores times the (positive) scale is the max of the scaled ones,
     // and p = exp2(fma(s, scale, -m)) needs no separate multiply.  With a cap
-    // the capped scores are formed first and ks is 1.
+    // the capped scores are formed first and ks is 1.  A zero K scale is
+    // raised to the least normal float, so that a masked -inf stays -inf
+    // (-inf * 0 would be NaN) while visible scores still contribute nothing.
     const bool capped = cap_out > 0.0f; // uniform
-    const float ks = capped ? 1.0f : cscale;
+    const float ks = capped ? 1.0f : fmaxf(cscale, __FLT_MIN__);
     float sv[16];
     if (capped) {
 #pragma unroll
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = xor32_max(mx);
-    mx = mx == -INFINITY ? -INFINITY : mx * ks; // in scaled units (-inf stays, even for a zero scale)
+    mx *= ks; // in scaled units
     // lazy rescale (as in the 16x16 kernels): the reference moves only when a
     // score exceeds it by more than kLazy
     const bool empty = l_run == 0.0f;
@@ -595,13 +597,24 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[sl][v] *= alpha;
     }
+    // No reference yet (m_run = -inf) means every score of the tile is
+    // masked, so any finite offset gives weights of 0 (bf16: one select per
+    // tile).  The fp8 variant keeps a select per weight: the shorter form
+    // pushed its register allocation past 256 (one wave per SIMD).
     const bool live = m_run != -INFINITY;
+    const float neg_m = live ? -m_run : 0.0f;
     uint32_t pk[8];
     float sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
-      const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
+      float p0, p1;
+      if constexpr (kFp8) {
+        p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
+        p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
+      } else {
+        p0 = __builtin_amdgcn_exp2f(fmaf(sv[v], ks, neg_m));
+        p1 = __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, neg_m));
+      }
       sum += p0 + p1;
       pk[v / 2] = pack_bf16x2(p0, p1);
     }
