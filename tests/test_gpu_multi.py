@@ -209,14 +209,15 @@ def test_keys_before_the_window_may_be_nan(name, q_len, d, window):
     _check(poison_invisible(make_inputs(spec, poison=True)), kv_chunk=256)
 
 
-def test_fp8_zero_k_scale_on_the_32x32_kernel():
+@pytest.mark.parametrize("q_len", [("list", [40, 33, 10]), ("list", [1, 1, 1])])
+def test_fp8_zero_k_scale(q_len):
     """A request whose fp8 K scale is 0 (an all-zero K cache quantised with
     scale 0): every visible score is 0, so its rows average V uniformly over
     their visible keys; masked keys must still get weight 0 (-inf times a
-    zero scale must not become NaN)."""
-    print("case multi fp8 zero K scale", flush=True)
-    spec = small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [300, 900, 64]),
-                         q_len=("list", [40, 33, 10]))
+    zero scale must not become NaN).  Several rows (the 32x32 kernel) and
+    one row (the decode kernel)."""
+    print(f"case multi fp8 zero K scale {q_len}", flush=True)
+    spec = small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [300, 900, 64]), q_len=q_len)
     inp = make_inputs(spec, poison=True)
     k_scale = np.array(inp.k_scale, copy=True)
     k_scale[1] = 0.0
