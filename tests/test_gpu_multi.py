@@ -197,6 +197,7 @@ def test_fresh_prefill_longer_than_a_chunk(Hq, Hk, kv):
     ("c5_paged_fp8_b128", 40, 128, 250),    # 32x32 kernel, fp8
     ("c4_paged_bf16_b64", 40, 64, 250),     # shared-tile kernel (head_dim 64)
     ("c4_paged_bf16_b64", 40, 256, 250),    # 32x32 kernel, head_dim 256
+    ("c5_paged_fp8_b128", 40, 256, 250),    # shared-tile kernel, fp8 at head_dim 256
 ])
 def test_keys_before_the_window_may_be_nan(name, q_len, d, window):
     """K/V codes of keys no query sees (before the first row's window) are
@@ -222,3 +223,14 @@ def test_fp8_zero_k_scale(q_len):
     k_scale = np.array(inp.k_scale, copy=True)
     k_scale[1] = 0.0
     _check(dataclasses.replace(inp, k_scale=k_scale), kv_chunk=256)
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_fp8_head_dim_256_rows(chunk):
+    """fp8 KV at head_dim 256 with several rows per request (from 3 column
+    groups the shared-tile kernel, one group per wave), split and unsplit
+    chunks."""
+    print(f"case multi fp8 d256 chunk={chunk}", flush=True)
+    spec = dataclasses.replace(small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [40, 700, 1500]),
+                                             q_len=("list", [40, 9, 33])), head_dim=256, sm_scale=1 / 16)
+    _check(make_inputs(spec, poison=True), kv_chunk=chunk)
