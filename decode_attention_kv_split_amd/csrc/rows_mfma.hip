@@ -711,10 +711,11 @@ constexpr int rows_nbuf() {
 // groups on, but for the compute-heavier fp8 and INT4 tiles only once three
 // of the four waves have work (batch-128 fp8, 8 rows of 8 heads = 4 groups:
 // 656 us with the chunk-splitting kernel, 980 us shared-tile).  At head_dim
-// 256 a workgroup covers 4 groups, one per wave, so fp8 there takes it from
-// 3 groups too (batch-128 fp8 at head_dim 256, 8 rows: 904 us, against
-// 2059 us chunk-splitting and 962 us on the 32x32 kernel, whose wave pairs
-// convert every K code twice).
+// 256 a workgroup covers 4 groups, one per wave, so fp8 and INT4 there take
+// it from 3 groups too (batch-128 fp8 at head_dim 256, 8 rows: 904 us,
+// against 2059 us chunk-splitting and 962 us on the 32x32 kernel, whose wave
+// pairs convert every K code twice; INT4, 6 and 8 rows: 751 and 781 us
+// against 874 and 1128 us chunk-splitting).
 constexpr int kRowsMinGroupsBf16 = 3;
 constexpr int kRowsMinGroupsQuant = 5;
 
@@ -727,8 +728,8 @@ constexpr int kRowsMinGroupsQuant = 5;
 int mfma_col_share(int head_dim, int kv_type, int col_groups) {
   // bf16 and fp8 at head_dim 128 (bf16 at 256 too) take the 32x32 prefill kernel there
   const bool tiles32 = head_dim == 128 && (kv_type == DT_BF16 || kv_type == DT_FP8);
-  const bool fp8_wide = kv_type == DT_FP8 && head_dim == 256;
-  if (col_groups >= (kv_type == DT_BF16 || tiles32 || fp8_wide ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
+  const bool quant_wide = (kv_type == DT_FP8 || kv_type == DT_INT4) && head_dim == 256;
+  if (col_groups >= (kv_type == DT_BF16 || tiles32 || quant_wide ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
     return kWaves * (head_dim <= 128 ? 2 : 1);
   return col_groups >= 2 && head_dim <= 128 ? 2 : 1;
 }

@@ -234,3 +234,12 @@ def test_fp8_head_dim_256_rows(chunk):
     spec = dataclasses.replace(small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [40, 700, 1500]),
                                              q_len=("list", [40, 9, 33])), head_dim=256, sm_scale=1 / 16)
     _check(make_inputs(spec, poison=True), kv_chunk=chunk)
+
+
+def test_int4_head_dim_256_rows_from_three_groups():
+    """INT4 KV at head_dim 256 with 3 to 4 column groups (6 to 8 rows of 8
+    heads): the shared-tile kernel, one group per wave."""
+    print("case multi int4 d256 rows", flush=True)
+    spec = dataclasses.replace(small_variant("c6_paged_int4_b128", batch=3, lengths=("list", [40, 700, 1500]),
+                                             q_len=("list", [6, 8, 3])), head_dim=256, sm_scale=1 / 16)
+    _check(make_inputs(spec, poison=True), kv_chunk=256)
