@@ -689,6 +689,323 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   }
 }
 
+// Two column groups (17 to 32 (query row, head) columns per KV head: a few
+// query rows per request, as in speculative decoding) with fp8 KV at
+// head_dim 128: decode-style work split with 32x32 matrix tiles.  The four
+// waves take the chunk's 32-key tiles in turn (wave w: tiles w, w + 4, ...),
+// each staging its own tiles through a private ring of LDS slots (no
+// workgroup barriers); every wave computes all 32 columns on its tiles with
+// the products, key order and softmax of partial_prefill_kernel, and the
+// waves' states are merged through LDS at the end.  Against the 16x16 decode
+// kernel with two groups, the P.V product runs at the full rate of the
+// 32x32x16 form and each key's max and weights are formed once per column.
+template <int NBUF>
+__global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p, const InlineWork w) {
+  constexpr int KT = DT_FP8;
+  constexpr int D = 128;
+  using S = Shape<D, KT>;                   // 128-byte rows, 8 pieces
+  constexpr int kRowBytes = S::kRowBytes;
+  constexpr int kT = 32;                    // keys per wave tile
+  constexpr int kHalfB = kTile * kRowBytes; // one 16-row half of a K (or V) tile
+  constexpr int kTileB = 2 * kHalfB;        // K (or V) bytes of a tile
+  constexpr int kSlot = 2 * kTileB;         // K, then V
+  constexpr int kDmaH = kHalfB / 1024;      // DMA loads per half
+  constexpr int OSTRIDE = D + 4;
+  constexpr int kStage = kWaves * NBUF * kSlot;
+  constexpr int kEpi = 2 * kWaves * 16 * 4 + kWaves * 16 * OSTRIDE * 4;
+  constexpr int kSmem = kStage > kEpi ? kStage : kEpi;
+  static_assert(kDmaH >= 1, "half-tile loads");
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+  __shared__ int s_scan[2 * 64];
+  __shared__ int s_item[4];
+  // K/V staging during the main loop; per-wave softmax states afterwards
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  float(*sm_m)[16] = reinterpret_cast<float(*)[16]>(smem);
+  float(*sm_l)[16] = reinterpret_cast<float(*)[16]>(smem + kWaves * 16 * 4);
+  float *sm_o = reinterpret_cast<float *>(smem + 2 * kWaves * 16 * 4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j32 = lane & 31; // column of the lane (S^T, O^T) / row (K, V^T operands)
+  const int h2 = lane >> 5;
+  const int item = blockIdx.x;
+  const int col_blocks = (p.col_groups + 1) / 2; // workgroups per (item, KV head)
+  const int kvg = blockIdx.y / col_blocks;
+  const int cg0 = blockIdx.y % col_blocks * 2;   // first of the workgroup's two column groups
+  const int g = p.group;
+  const int Hk = p.num_kv_heads;
+
+  int b, split, nb, L;
+  if (!locate_item(p, w, item, blockIdx.y == 0, s_scan, s_item, b, split, nb, L)) return;
+  const int nq = req_nq(p, b);
+  if (cg0 * 16 >= nq * g) return; // uniform over the workgroup
+  const int lo = request_lo(L, nq, p.window);
+  const int a0 = (lo & ~(kTile - 1)) + split * p.chunk;
+  const int t_begin = max(lo, a0);
+  const int t_end = min(L, a0 + p.chunk);
+
+  // ---- this lane's column and the keys it sees ----
+  const int col = cg0 * 16 + j32;
+  const bool ok = col < nq * g;
+  const int qi = col / g;
+  const int qrow = p.qo_indptr[b] + qi;
+  const int qhead = kvg * g + col % g;
+  const int qpos = L - nq + qi;
+  const int c_lo = max(t_begin, p.window > 0 ? max(0, qpos - p.window + 1) : 0);
+  const int c_hi = min(t_end, qpos + 1);
+  int all_lo = t_begin, all_hi = t_end, w_lo = t_end, w_hi = t_begin;
+  if (ok) {
+    all_lo = c_lo;
+    all_hi = c_hi;
+    if (c_lo < c_hi) {
+      w_lo = c_lo;
+      w_hi = c_hi;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    all_lo = max(all_lo, __shfl_xor(all_lo, o, 64));
+    all_hi = min(all_hi, __shfl_xor(all_hi, o, 64));
+    w_lo = min(w_lo, __shfl_xor(w_lo, o, 64));
+    w_hi = max(w_hi, __shfl_xor(w_hi, o, 64));
+  }
+  all_lo = __builtin_amdgcn_readfirstlane(all_lo);
+  all_hi = __builtin_amdgcn_readfirstlane(all_hi);
+  w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+  w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+  // 32-key tiles from the (16-aligned) chunk start that hold keys some column sees
+  const int ft = w_hi > w_lo ? (w_lo - a0) / kT : 0;
+  const int ntiles = w_hi > w_lo ? (w_hi - a0 + kT - 1) / kT - ft : 0;
+  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+
+  // Q^T operand of step s: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .. + 7 (the order of the K pieces)
+  bf16x8_t qop[8];
+  {
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int d0 = 16 * (2 * (s / 2) + h2) + 8 * (s % 2);
+      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
+                  : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    }
+  }
+  const float cscale = p.score_scale * p.k_scale[b * Hk + kvg];
+  const float cap_out = p.cap_out;
+  const bool capped = cap_out > 0.0f;
+  const float ks = capped ? 1.0f : fmaxf(cscale, __FLT_MIN__); // see partial_prefill_kernel
+  float m_run = p.m_init, l_run = 0.0f;
+  f32x16_t acc[4]; // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[sl][v] = 0.0f;
+
+  // ---- staging: lane i holds where the two 16-row halves of this wave's
+  // tile i start and how many of their bytes hold keys (a wave owns at most
+  // 32 tiles: chunks are capped at 4096 keys) ----
+  const size_t row_bytes = (size_t)Hk * kRowBytes;
+  const bool paged = p.page_size > 0;
+  const int *pages = paged ? p.page_indices + p.page_indptr[b] : nullptr;
+  uint32_t voff_lo[2] = {0, 0}, voff_hi[2] = {0, 0}, vbytes[2] = {0, 0};
+  if (lane < my_tiles) {
+    const int ts = a0 + (ft + wave + lane * kWaves) * kT;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hs = ts + hh * kTile;
+      if (hs < w_hi) {
+        const size_t row0 = paged ? (size_t)pages[hs >> p.page_shift] * p.page_size + (hs & (p.page_size - 1)) : (size_t)hs;
+        const size_t off = row0 * row_bytes;
+        voff_lo[hh] = (uint32_t)off;
+        voff_hi[hh] = (uint32_t)(off >> 32);
+        vbytes[hh] = (uint32_t)(min(kTile, w_hi - hs) * (int)row_bytes);
+      }
+    }
+  }
+  const char *kpool = reinterpret_cast<const char *>(p.k);
+  const char *vpool = reinterpret_cast<const char *>(p.v);
+  int dma_voff[kDmaH];
+#pragma unroll
+  for (int k = 0; k < kDmaH; ++k) {
+    const int r = k * S::kRowsPerDma + lane / S::kPieces;
+    const int piece = (lane % S::kPieces) ^ stage_swizzle<D, KT>(r);
+    dma_voff[k] = r * (int)row_bytes + kvg * kRowBytes + piece * 16;
+  }
+  char *wave_stage = smem + wave * NBUF * kSlot;
+  auto issue = [&](int i, int slot) {
+    const int li = min(i, 63);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const size_t base =
+          ((size_t)__builtin_amdgcn_readlane(voff_hi[hh], li) << 32) | __builtin_amdgcn_readlane(voff_lo[hh], li);
+      const int nbytes = i < my_tiles ? (int)__builtin_amdgcn_readlane(vbytes[hh], li) : 0;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(kpool + base), (short)0, nbytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(vpool + base), (short)0, nbytes, kBufferFlags);
+      char *kst = wave_stage + slot * kSlot + hh * kHalfB;
+#pragma unroll
+      for (int k = 0; k < kDmaH; ++k) dma16_to_lds(kr, kst + 1024 * k, dma_voff[k]);
+#pragma unroll
+      for (int k = 0; k < kDmaH; ++k) dma16_to_lds(vr, kst + kTileB + 1024 * k, dma_voff[k]);
+    }
+  };
+  // Staged row R of a tile carries the swizzle of its position in its half.
+  // K operand: row pi(j32) (bits 3 and 2 swapped within each 16), pieces
+  // 2 m + h2; V^T (8-bit transposing reads): lane 16 G + 2 r + c points at
+  // row 16 t + 8 (G / 2) + r, dims 32 sl + 16 (G % 2) + 8 c .. + 7.
+  const int krow = (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1);
+  uint32_t k_addr[4], vt8_addr[8];
+  {
+    const uint32_t base = lds_address(wave_stage);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      k_addr[m] = base + krow * kRowBytes + (((2 * m + h2) ^ stage_swizzle<D, KT>(krow % kTile)) * 16);
+    const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int row = 16 * t + 8 * (G >> 1) + r;
+        const int piece = 2 * sl + (G & 1);
+        vt8_addr[4 * t + sl] =
+            base + kTileB + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row % kTile)) * 16) + c * 8;
+      }
+  }
+  const int vt_g = lane >> 4;
+
+  // one staged 32-key tile (first key ts) from its raw K pieces and V^T bytes
+  auto tile32 = [&](const uint4 (&kr)[4], uint2 (&v8)[8], int ts) {
+    f32x16_t st;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) st[v] = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].x, kr[m].y), qop[2 * m], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].z, kr[m].w), qop[2 * m + 1], st, 0, 0, 0);
+    }
+    // keys before w_lo are seen by no column (their values need not be
+    // finite): zero their V^T bytes; the tile's scores there are masked
+    if (ts < w_lo) { // lane holds rows 16 t + 8 (G / 2) + e, byte e (uniform branch)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t lo_keep = 0, hi_keep = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = ts + 16 * t + 8 * (vt_g >> 1) + e;
+          if (key >= w_lo) lo_keep |= 0xFFu << (8 * e);
+          if (key + 4 >= w_lo) hi_keep |= 0xFFu << (8 * e);
+        }
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          v8[4 * t + sl].x &= lo_keep;
+          v8[4 * t + sl].y &= hi_keep;
+        }
+      }
+    }
+    // ---- scores: register v holds key ts + pi(8 (v / 4) + 4 h2 + v % 4) ----
+    float sv[16];
+    if (capped) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = tanhf(st[v] * cscale) * cap_out;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sv[v] = st[v];
+    }
+    if (ts < all_lo || ts + kT > all_hi) { // some column misses some key (uniform)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3);
+        const int tok = ts + ((row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1));
+        if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
+      }
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
+    mx = xor32_max(mx) * ks;
+    const bool empty = l_run == 0.0f;
+    const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
+      m_run = grow ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[sl][v] *= alpha;
+    }
+    const bool live = m_run != -INFINITY;
+    uint32_t pk[8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
+      const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
+      sum += p0 + p1;
+      pk[v / 2] = pack_bf16x2(p0, p1);
+    }
+    l_run += sum;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(v8[4 * t + sl].x, v8[4 * t + sl].y), pt,
+                                                          acc[sl], 0, 0, 0);
+    }
+  };
+
+  // ---- ring of NBUF slots per wave, refilled as soon as a tile is in registers ----
+  if (my_tiles > 0) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) issue(j, j);
+    const int n_iter = (my_tiles + NBUF - 1) / NBUF * NBUF;
+    for (int it = 0; it < n_iter; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int i = it + j;
+        wait_vmem<(NBUF - 1) * 4 * kDmaH>(); // tile i has landed; NBUF - 1 newer tiles may fly
+        uint4 kr[4];
+        uint2 v8[8];
+        lds_read_x4(kr, k_addr, j * kSlot);
+        lds_read_tr8_x8(v8, vt8_addr, j * kSlot);
+        issue(i + NBUF, j);
+        if (i < my_tiles) tile32(kr, v8, a0 + (ft + wave + i * kWaves) * kT);
+      }
+    }
+    wait_vmem<0>(); // no DMA may land in the staging area once it is reused
+  }
+  __syncthreads(); // staging area is reused for the per-wave states below
+
+  // ---- per-wave states to LDS, merged over the waves, one column group at a time ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c > 0) {
+      if ((cg0 + 1) * 16 >= nq * g) break; // the same in every lane of the workgroup
+      __syncthreads();                      // the previous group's merge has read the states
+    }
+    if ((j32 >> 4) == c) {
+      const int h = j32 & 15;
+      if (h2 == 0) {
+        sm_m[wave][h] = l_tot > 0.0f ? m_run : -INFINITY; // an empty state keeps no reference
+        sm_l[wave][h] = l_tot;
+      }
+      float *dst = sm_o + (wave * 16 + h) * OSTRIDE;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4 *>(dst + 32 * sl + 8 * q + 4 * h2) =
+              make_float4(acc[sl][4 * q], acc[sl][4 * q + 1], acc[sl][4 * q + 2], acc[sl][4 * q + 3]);
+    }
+    __syncthreads();
+    merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
+  }
+}
+
 // Column groups one wave of the shared-tile kernel computes: two for
 // head_dim <= 128; head_dim 256 keeps one, its accumulators would not fit in
 // registers twice.
@@ -742,6 +1059,11 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
   if constexpr ((D == 128 && (KT == DT_BF16 || KT == DT_FP8)) || (D == 256 && KT == DT_BF16))
     return launch_kernel(l, partial_prefill_kernel<D, KT, KT == DT_FP8 ? 4 : 2>, grid, p, w);
   return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
+}
+
+hipError_t launch_cols32(const Params &p, const InlineWork &w, const Launch &l) {
+  if (p.col_share != 2 || p.pack != 1) return hipErrorInvalidValue;
+  return launch_kernel(l, partial_cols32_kernel<2>, dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
 }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {

@@ -243,3 +243,29 @@ def test_int4_head_dim_256_rows_from_three_groups():
     spec = dataclasses.replace(small_variant("c6_paged_int4_b128", batch=3, lengths=("list", [40, 700, 1500]),
                                              q_len=("list", [6, 8, 3])), head_dim=256, sm_scale=1 / 16)
     _check(make_inputs(spec, poison=True), kv_chunk=256)
+
+
+@pytest.mark.parametrize("chunk,window,extra", [
+    (0, -1, {}), (16, -1, {}), (64, 100, {}), (0, 7, {}),
+    (256, -1, {"unified_max": 40.0}), (0, -1, {"logits_soft_cap": 30.0}),
+])
+def test_fp8_two_groups_cols32(chunk, window, extra):
+    """fp8 KV, head_dim 128, 17 to 32 (query row, head) columns per KV head
+    (3 and 4 rows of 8 heads, and fewer): the 32-column kernel whose waves
+    split the keys, next to empty and one-row requests."""
+    print(f"case multi fp8 cols32 chunk={chunk} window={window} {extra}", flush=True)
+    spec = small_variant("c5_paged_fp8_b128", batch=5, lengths=("list", [3, 700, 2049, 40, 0]),
+                         q_len=("list", [3, 4, 4, 1, 0]), window=window)
+    if "logits_soft_cap" in extra:
+        spec = dataclasses.replace(spec, soft_cap=extra["logits_soft_cap"])
+        extra = {}
+    _check(make_inputs(spec, poison=True), kv_chunk=chunk, **extra)
+
+
+def test_fp8_two_groups_cols32_device_planned():
+    """300 requests with 3 to 4 rows of 8 heads (the device-side work list)
+    on the 32-column fp8 kernel."""
+    print("case multi fp8 cols32 large batch", flush=True)
+    spec = DecodeSpec("cols32rows", 300, 16, 2, 128, 16, "fp8", "bf16", 128 ** -0.5,
+                      lengths=("uniform", 4, 600), q_len=("uniform", 3, 4), seed=77)
+    _check(make_inputs(spec, poison=True))
