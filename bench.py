@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299481620, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
+        {"bytes": 2299484507, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487912271, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
+        {"bytes": 1487912540, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538236713, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
+        {"bytes": 538235216, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680891052, "digest": "b50142be01505d98ee518d18395569eed40ec501a97a3b233c9579ad6db9449c"},
+        {"bytes": 680890781, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
 }
 
 
