@@ -690,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 }
 
 // Two column groups (17 to 32 (query row, head) columns per KV head: a few
-// query rows per request, as in speculative decoding) with fp8 KV at
+// query rows per request, as in speculative decoding) with bf16 or fp8 KV at
 // head_dim 128: decode-style work split with 32x32 matrix tiles.  The four
 // waves take the chunk's 32-key tiles in turn (wave w: tiles w, w + 4, ...),
 // each staging its own tiles through a private ring of LDS slots (no
@@ -699,11 +699,12 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 // waves' states are merged through LDS at the end.  Against the 16x16 decode
 // kernel with two groups, the P.V product runs at the full rate of the
 // 32x32x16 form and each key's max and weights are formed once per column.
-template <int NBUF>
+template <int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p, const InlineWork w) {
-  constexpr int KT = DT_FP8;
+  static_assert(KT == DT_BF16 || KT == DT_FP8, "bf16 or fp8 KV");
+  constexpr bool kFp8 = KT == DT_FP8;
   constexpr int D = 128;
-  using S = Shape<D, KT>;                   // 128-byte rows, 8 pieces
+  using S = Shape<D, KT>;                   // fp8: 128-byte rows, 8 pieces; bf16: 256, 16
   constexpr int kRowBytes = S::kRowBytes;
   constexpr int kT = 32;                    // keys per wave tile
   constexpr int kHalfB = kTile * kRowBytes; // one 16-row half of a K (or V) tile
@@ -780,18 +781,19 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
   const int ntiles = w_hi > w_lo ? (w_hi - a0 + kT - 1) / kT - ft : 0;
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-  // Q^T operand of step s: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .. + 7 (the order of the K pieces)
+  // Q^T operand of step s: bf16 dims 16 s + 8 h2 .. + 7; fp8 dims
+  // 16 (2 (s / 2) + h2) + 8 (s % 2) .. + 7 (the order of its K pieces)
   bf16x8_t qop[8];
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int d0 = 16 * (2 * (s / 2) + h2) + 8 * (s % 2);
+      const int d0 = kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2;
       qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
                   : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     }
   }
-  const float cscale = p.score_scale * p.k_scale[b * Hk + kvg];
+  const float cscale = kFp8 ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
   const float cap_out = p.cap_out;
   const bool capped = cap_out > 0.0f;
   const float ks = capped ? 1.0f : fmaxf(cscale, __FLT_MIN__); // see partial_prefill_kernel
@@ -852,57 +854,78 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     }
   };
   // Staged row R of a tile carries the swizzle of its position in its half.
-  // K operand: row pi(j32) (bits 3 and 2 swapped within each 16), pieces
-  // 2 m + h2; V^T (8-bit transposing reads): lane 16 G + 2 r + c points at
-  // row 16 t + 8 (G / 2) + r, dims 32 sl + 16 (G % 2) + 8 c .. + 7.
-  const int krow = (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1);
-  uint32_t k_addr[4], vt8_addr[8];
+  // The operand layouts are partial_prefill_kernel's.  fp8: K row pi(j32)
+  // (bits 3 and 2 swapped within each 16), pieces 2 m + h2; V^T by 8-bit
+  // transposing reads, lane 16 G + 2 r + c at row 16 t + 8 (G / 2) + r, dims
+  // 32 sl + 16 (G % 2) + 8 c .. + 7.  bf16: K row j32, pieces 2 s + h2; V^T
+  // by 16-bit transposing reads, lane 16 G + 4 r + c at row
+  // 8 hh + 4 (G / 2) + r (+ 16 t), dims 32 sl + 16 (G % 2) + 4 c .. + 3.
+  constexpr int kKReads = kFp8 ? 4 : 8;
+  const int krow = kFp8 ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
+  uint32_t k_addr[kKReads], vt_addr[8];
   {
     const uint32_t base = lds_address(wave_stage);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < kKReads; ++m)
       k_addr[m] = base + krow * kRowBytes + (((2 * m + h2) ^ stage_swizzle<D, KT>(krow % kTile)) * 16);
-    const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
+    const int G = lane >> 4;
+    if constexpr (kFp8) {
+      const int r = (lane >> 1) & 7, c = lane & 1;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int row = 16 * t + 8 * (G >> 1) + r;
-        const int piece = 2 * sl + (G & 1);
-        vt8_addr[4 * t + sl] =
-            base + kTileB + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row % kTile)) * 16) + c * 8;
-      }
+        for (int sl = 0; sl < 4; ++sl) {
+          const int row = 16 * t + 8 * (G >> 1) + r;
+          const int piece = 2 * sl + (G & 1);
+          vt_addr[4 * t + sl] =
+              base + kTileB + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row % kTile)) * 16) + c * 8;
+        }
+    } else {
+      const int r = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int row = 8 * hh + 4 * (G >> 1) + r;
+          const int piece = 4 * sl + 2 * (G & 1) + (c >> 1);
+          vt_addr[4 * hh + sl] =
+              base + kTileB + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row % kTile)) * 16) + (c & 1) * 8;
+        }
+    }
   }
   const int vt_g = lane >> 4;
 
-  // one staged 32-key tile (first key ts) from its raw K pieces and V^T bytes
-  auto tile32 = [&](const uint4 (&kr)[4], uint2 (&v8)[8], int ts) {
+  // one staged 32-key tile (first key ts): its raw K pieces and the V^T
+  // operands vop[t][sl] of key half t, whose element e holds key
+  // 16 t + 8 (G / 2) + e (fp8) or 16 t + 8 (e / 4) + 4 (G / 2) + e % 4 (bf16)
+  auto tile32 = [&](const uint4 (&kr)[kKReads], bf16x8_t (&vop)[2][4], int ts) {
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].x, kr[m].y), qop[2 * m], st, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].z, kr[m].w), qop[2 * m + 1], st, 0, 0, 0);
+      for (int m = 0; m < 4; ++m) {
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].x, kr[m].y), qop[2 * m], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].z, kr[m].w), qop[2 * m + 1], st, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[m]), qop[m], st, 0, 0, 0);
     }
     // keys before w_lo are seen by no column (their values need not be
-    // finite): zero their V^T bytes; the tile's scores there are masked
-    if (ts < w_lo) { // lane holds rows 16 t + 8 (G / 2) + e, byte e (uniform branch)
+    // finite): zero their V^T elements; the tile's scores there are masked
+    if (ts < w_lo) { // uniform branch
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t lo_keep = 0, hi_keep = 0;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = ts + 16 * t + 8 * (vt_g >> 1) + e;
-          if (key >= w_lo) lo_keep |= 0xFFu << (8 * e);
-          if (key + 4 >= w_lo) hi_keep |= 0xFFu << (8 * e);
+        for (int e = 0; e < 8; ++e) {
+          const int key = ts + 16 * t + (kFp8 ? 8 * (vt_g >> 1) + e : 8 * (e >> 2) + 4 * (vt_g >> 1) + (e & 3));
+          if (key < w_lo) {
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) vop[t][sl][e] = (__bf16)0.0f;
+          }
         }
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          v8[4 * t + sl].x &= lo_keep;
-          v8[4 * t + sl].y &= hi_keep;
-        }
-      }
     }
     // ---- scores: register v holds key ts + pi(8 (v / 4) + 4 h2 + v % 4) ----
     float sv[16];
@@ -916,8 +939,8 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     if (ts < all_lo || ts + kT > all_hi) { // some column misses some key (uniform)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3);
-        const int tok = ts + ((row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1));
+        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8: key pi(row)
+        const int tok = ts + (kFp8 ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
         if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
       }
     }
@@ -951,9 +974,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     for (int t = 0; t < 2; ++t) {
       const bf16x8_t pt = __builtin_bit_cast(bf16x8_t, make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]));
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-        acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(v8[4 * t + sl].x, v8[4 * t + sl].y), pt,
-                                                          acc[sl], 0, 0, 0);
+      for (int sl = 0; sl < 4; ++sl) acc[sl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[t][sl], pt, acc[sl], 0, 0, 0);
     }
   };
 
@@ -967,12 +988,32 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
       for (int j = 0; j < NBUF; ++j) {
         const int i = it + j;
         wait_vmem<(NBUF - 1) * 4 * kDmaH>(); // tile i has landed; NBUF - 1 newer tiles may fly
-        uint4 kr[4];
-        uint2 v8[8];
-        lds_read_x4(kr, k_addr, j * kSlot);
-        lds_read_tr8_x8(v8, vt8_addr, j * kSlot);
-        issue(i + NBUF, j);
-        if (i < my_tiles) tile32(kr, v8, a0 + (ft + wave + i * kWaves) * kT);
+        uint4 kr[kKReads];
+        bf16x8_t vop[2][4];
+        if constexpr (kFp8) {
+          uint2 v8[8];
+          lds_read_x4(kr, k_addr, j * kSlot);
+          lds_read_tr8_x8(v8, vt_addr, j * kSlot);
+          issue(i + NBUF, j);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) vop[t][sl] = fp8x8_to_bf16x8(v8[4 * t + sl].x, v8[4 * t + sl].y);
+        } else { // operand (t, sl): two reads of four keys, key halves hh = 0, 1
+          s16x4_t vt0[8], vt1[8];
+          lds_read_x8(kr, k_addr, j * kSlot);
+          lds_read_tr_x8(vt0, vt_addr, j * kSlot);
+          lds_read_tr_x8(vt1, vt_addr, j * kSlot + kTile * kRowBytes);
+          issue(i + NBUF, j);
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            const uint2 a0v = __builtin_bit_cast(uint2, vt0[sl]), c0v = __builtin_bit_cast(uint2, vt0[4 + sl]);
+            const uint2 a1v = __builtin_bit_cast(uint2, vt1[sl]), c1v = __builtin_bit_cast(uint2, vt1[4 + sl]);
+            vop[0][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(a0v.x, a0v.y, c0v.x, c0v.y));
+            vop[1][sl] = __builtin_bit_cast(bf16x8_t, make_uint4(a1v.x, a1v.y, c1v.x, c1v.y));
+          }
+        }
+        if (i < my_tiles) tile32(kr, vop, a0 + (ft + wave + i * kWaves) * kT);
       }
     }
     wait_vmem<0>(); // no DMA may land in the staging area once it is reused
@@ -1061,9 +1102,13 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
   return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
 }
 
-hipError_t launch_cols32(const Params &p, const InlineWork &w, const Launch &l) {
+hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, const Launch &l) {
   if (p.col_share != 2 || p.pack != 1) return hipErrorInvalidValue;
-  return launch_kernel(l, partial_cols32_kernel<2>, dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
+  const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2));
+  // one 16 KB bf16 slot per wave, two 8 KB fp8 ones: 64 KB per workgroup either way
+  if (kv_type == DT_FP8) return launch_kernel(l, partial_cols32_kernel<DT_FP8, 2>, grid, p, w);
+  if (kv_type == DT_BF16) return launch_kernel(l, partial_cols32_kernel<DT_BF16, 1>, grid, p, w);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {

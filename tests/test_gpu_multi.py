@@ -192,7 +192,8 @@ def test_fresh_prefill_longer_than_a_chunk(Hq, Hk, kv):
 @pytest.mark.parametrize("name,q_len,d,window", [
     ("c4_paged_bf16_b64", 1, 128, 300),     # decode kernel, one row
     ("c5_paged_fp8_b128", 1, 128, 300),
-    ("c5_paged_fp8_b128", 3, 128, 200),     # decode kernel, two column groups
+    ("c5_paged_fp8_b128", 3, 128, 200),     # 32-column kernel (two column groups), fp8
+    ("c4_paged_bf16_b64", 6, 128, 200),     # 32-column kernel, bf16
     ("c4_paged_bf16_b64", 40, 128, 250),    # 32x32 kernel, bf16
     ("c5_paged_fp8_b128", 40, 128, 250),    # 32x32 kernel, fp8
     ("c4_paged_bf16_b64", 40, 64, 250),     # shared-tile kernel (head_dim 64)
@@ -245,27 +246,34 @@ def test_int4_head_dim_256_rows_from_three_groups():
     _check(make_inputs(spec, poison=True), kv_chunk=256)
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
 @pytest.mark.parametrize("chunk,window,extra", [
     (0, -1, {}), (16, -1, {}), (64, 100, {}), (0, 7, {}),
     (256, -1, {"unified_max": 40.0}), (0, -1, {"logits_soft_cap": 30.0}),
 ])
-def test_fp8_two_groups_cols32(chunk, window, extra):
-    """fp8 KV, head_dim 128, 17 to 32 (query row, head) columns per KV head
-    (3 and 4 rows of 8 heads, and fewer): the 32-column kernel whose waves
-    split the keys, next to empty and one-row requests."""
-    print(f"case multi fp8 cols32 chunk={chunk} window={window} {extra}", flush=True)
-    spec = small_variant("c5_paged_fp8_b128", batch=5, lengths=("list", [3, 700, 2049, 40, 0]),
-                         q_len=("list", [3, 4, 4, 1, 0]), window=window)
+def test_two_groups_cols32(kv, chunk, window, extra):
+    """bf16 or fp8 KV, head_dim 128, 17 to 32 (query row, head) columns per
+    KV head (fp8: 3 and 4 rows of 8 heads; bf16: 5 to 8 rows of 4 heads; and
+    fewer): the 32-column kernel whose waves split the keys, next to empty
+    and one-row requests."""
+    print(f"case multi {kv} cols32 chunk={chunk} window={window} {extra}", flush=True)
+    if kv == "fp8":
+        spec = small_variant("c5_paged_fp8_b128", batch=5, lengths=("list", [3, 700, 2049, 40, 0]),
+                             q_len=("list", [3, 4, 4, 1, 0]), window=window)
+    else:
+        spec = small_variant("c4_paged_bf16_b64", batch=5, lengths=("list", [5, 700, 2049, 40, 0]),
+                             q_len=("list", [5, 8, 7, 1, 0]), window=window)
     if "logits_soft_cap" in extra:
         spec = dataclasses.replace(spec, soft_cap=extra["logits_soft_cap"])
         extra = {}
     _check(make_inputs(spec, poison=True), kv_chunk=chunk, **extra)
 
 
-def test_fp8_two_groups_cols32_device_planned():
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_two_groups_cols32_device_planned(kv):
     """300 requests with 3 to 4 rows of 8 heads (the device-side work list)
-    on the 32-column fp8 kernel."""
-    print("case multi fp8 cols32 large batch", flush=True)
-    spec = DecodeSpec("cols32rows", 300, 16, 2, 128, 16, "fp8", "bf16", 128 ** -0.5,
+    on the 32-column kernel."""
+    print(f"case multi {kv} cols32 large batch", flush=True)
+    spec = DecodeSpec("cols32rows", 300, 16, 2, 128, 16, kv, "bf16", 128 ** -0.5,
                       lengths=("uniform", 4, 600), q_len=("uniform", 3, 4), seed=77)
     _check(make_inputs(spec, poison=True))
