@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299484507, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
+        {"bytes": 2299481172, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487912540, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
+        {"bytes": 1487912265, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538235216, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
+        {"bytes": 538235136, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680890781, "digest": "0aa259a75c8bc7effab5c9e863987815a704f4529b4ef7ec55a2d0a59ff732c3"},
+        {"bytes": 680890759, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
 }
 
 
