@@ -277,3 +277,12 @@ def test_two_groups_cols32_device_planned(kv):
     spec = DecodeSpec("cols32rows", 300, 16, 2, 128, 16, kv, "bf16", 128 ** -0.5,
                       lengths=("uniform", 4, 600), q_len=("uniform", 3, 4), seed=77)
     _check(make_inputs(spec, poison=True))
+
+
+@pytest.mark.parametrize("rows,window", [(20, -1), (32, -1), (27, 9)])
+def test_two_groups_cols32_contiguous(rows, window):
+    """A contiguous MHA cache (one head per KV head) with 17 to 32 new rows:
+    two column groups on the 32-column kernel over [L, Hk, d] rows."""
+    print(f"case multi cols32 contiguous rows={rows} window={window}", flush=True)
+    spec = small_variant("c3_llama2_7b_32k", lengths=("fixed", 1500), q_len=("fixed", rows), window=window)
+    _check(make_inputs(spec), kv_chunk=256)
