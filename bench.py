@@ -394,7 +394,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     achieved = nbytes / (part_avg * 1e-3) / 1e9
     props = torch.cuda.get_device_properties(0)
     kernel = ("partial_valu_kernel" if plan.algo == kvs.KVS_ALGO_VALU else
-              "partial_cols32_kernel" if plan.col_share == 2 and s.kv_dtype in ("bf16", "fp8") and s.head_dim == 128 else
+              "partial_cols32_kernel" if plan.col_share == 2 and s.head_dim == 128 else
               "partial_mfma_kernel" if plan.col_share < 4 else
               "partial_prefill_kernel" if (s.kv_dtype in ("bf16", "fp8") and s.head_dim == 128)
               or (s.kv_dtype == "bf16" and s.head_dim == 256) else

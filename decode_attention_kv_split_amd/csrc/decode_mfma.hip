@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
 template <int D, int PACK, int KT>
 static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Launch &l) {
   constexpr int NB = Shape<D * PACK, KT>::kNBuf;
-  if constexpr (PACK == 1 && D == 128 && (KT == DT_FP8 || KT == DT_BF16)) {
+  if constexpr (PACK == 1 && D == 128) {
     if (p.col_share == 2) return launch_cols32(p, w, KT, l); // 32x32 tiles, keys split over the waves
   }
   if constexpr (PACK == 1 && D <= 128) {

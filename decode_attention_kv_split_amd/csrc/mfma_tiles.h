@@ -916,7 +916,7 @@ __device__ __forceinline__ void pair_update(ColumnSet<DE, KT, CG> &cs, const Til
 // workgroups cover 4 or 8 column groups (Params::col_share).
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l);
 // Launches the 32-column kernel (rows_mfma.hip) for two column groups of
-// (query row, head) pairs, bf16 or fp8 KV at head_dim 128 (Params::col_share 2).
+// (query row, head) pairs at head_dim 128 (Params::col_share 2).
 hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, const Launch &l);
 
 } // namespace kvs

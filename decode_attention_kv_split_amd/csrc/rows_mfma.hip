@@ -689,9 +689,28 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   }
 }
 
+// Four 8-bit transposing reads (ds_read_b64_tr_b8, layout as for
+// lds_read_tr8_x8) at four lane addresses, one wait.
+__device__ __forceinline__ void lds_read_tr8_x4(uint2 (&v)[4], const uint32_t (&a)[4], uint32_t off) {
+  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b64_tr_b8 %0, %4\n\t"
+                   "ds_read_b64_tr_b8 %1, %5\n\t"
+                   "ds_read_b64_tr_b8 %2, %6\n\t"
+                   "ds_read_b64_tr_b8 %3, %7\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off)
+                   : "memory");
+  v[0] = __builtin_bit_cast(uint2, r0);
+  v[1] = __builtin_bit_cast(uint2, r1);
+  v[2] = __builtin_bit_cast(uint2, r2);
+  v[3] = __builtin_bit_cast(uint2, r3);
+}
+
 // Two column groups (17 to 32 (query row, head) columns per KV head: a few
-// query rows per request, as in speculative decoding) with bf16 or fp8 KV at
-// head_dim 128: decode-style work split with 32x32 matrix tiles.  The four
+// query rows per request, as in speculative decoding) with bf16, fp8 or INT4
+// KV at head_dim 128: decode-style work split with 32x32 matrix tiles.  The four
 // waves take the chunk's 32-key tiles in turn (wave w: tiles w, w + 4, ...),
 // each staging its own tiles through a private ring of LDS slots (no
 // workgroup barriers); every wave computes all 32 columns on its tiles with
@@ -701,10 +720,12 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 // 32x32x16 form and each key's max and weights are formed once per column.
 template <int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p, const InlineWork w) {
-  static_assert(KT == DT_BF16 || KT == DT_FP8, "bf16 or fp8 KV");
+  static_assert(KT == DT_BF16 || KT == DT_FP8 || KT == DT_INT4, "bf16, fp8 or INT4 KV");
   constexpr bool kFp8 = KT == DT_FP8;
+  constexpr bool kInt4 = KT == DT_INT4;
+  constexpr bool kPerm = kFp8 || kInt4;     // V^T by 8-bit transposing reads: K rows pi-permuted
   constexpr int D = 128;
-  using S = Shape<D, KT>;                   // fp8: 128-byte rows, 8 pieces; bf16: 256, 16
+  using S = Shape<D, KT>;                   // fp8: 128-byte rows, 8 pieces; bf16: 256, 16; INT4: 64, 4
   constexpr int kRowBytes = S::kRowBytes;
   constexpr int kT = 32;                    // keys per wave tile
   constexpr int kHalfB = kTile * kRowBytes; // one 16-row half of a K (or V) tile
@@ -782,23 +803,35 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
   const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // Q^T operand of step s: bf16 dims 16 s + 8 h2 .. + 7; fp8 dims
-  // 16 (2 (s / 2) + h2) + 8 (s % 2) .. + 7 (the order of its K pieces)
+  // 16 (2 (s / 2) + h2) + 8 (s % 2) .. + 7 (the order of its K pieces);
+  // INT4 the 8 dims of K dword 8 h2 + s, even ones first (as its nibbles)
   bf16x8_t qop[8];
+  float qoff = 0.0f; // INT4: the scores carry 136 * (sum of the column's q)
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int d0 = kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2;
-      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
-                  : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      const int d0 = kInt4 ? 8 * (8 * h2 + s) : (kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2);
+      bf16x8_t x = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
+                      : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      if constexpr (kInt4) {
+        x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qoff += (float)x[e];
+      }
+      qop[s] = x;
     }
   }
-  const float cscale = kFp8 ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
+  if constexpr (kInt4) qoff = (qoff + __shfl_xor(qoff, 32, 64)) * kInt4Offset;
+  const float cscale = kPerm ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
   const float cap_out = p.cap_out;
   const bool capped = cap_out > 0.0f;
   const float ks = capped ? 1.0f : fmaxf(cscale, __FLT_MIN__); // see partial_prefill_kernel
   float m_run = p.m_init, l_run = 0.0f;
-  f32x16_t acc[4]; // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
+  float lb_run = 0.0f; // INT4: the same sum of the bf16-rounded weights P.V saw
+  // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4;
+  // INT4: dim 64 (sl / 2) + 2 (8 (v / 4) + 4 h2 + v % 4) + sl % 2
+  f32x16_t acc[4];
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -860,16 +893,34 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
   // 32 sl + 16 (G % 2) + 8 c .. + 7.  bf16: K row j32, pieces 2 s + h2; V^T
   // by 16-bit transposing reads, lane 16 G + 4 r + c at row
   // 8 hh + 4 (G / 2) + r (+ 16 t), dims 32 sl + 16 (G % 2) + 4 c .. + 3.
-  constexpr int kKReads = kFp8 ? 4 : 8;
-  const int krow = kFp8 ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
+  // INT4: K pieces 2 h2 and 2 h2 + 1 of row pi(j32) (dwords 8 h2 .. 8 h2 + 7);
+  // V^T by 8-bit transposing reads per key half t and 64-dim block blk,
+  // lane 16 G + 2 r + c at row 16 t + 8 (G / 2) + r, bytes
+  // 32 blk + 16 (G % 2) + 8 c .. + 7, so lane j of a half-wave holds byte j
+  // of the block (dims 2 j, 2 j + 1) for 8 consecutive keys.
+  constexpr int kKReads = kFp8 ? 4 : (kInt4 ? 2 : 8);
+  const int krow = kPerm ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
   uint32_t k_addr[kKReads], vt_addr[8];
   {
     const uint32_t base = lds_address(wave_stage);
 #pragma unroll
-    for (int m = 0; m < kKReads; ++m)
-      k_addr[m] = base + krow * kRowBytes + (((2 * m + h2) ^ stage_swizzle<D, KT>(krow % kTile)) * 16);
+    for (int m = 0; m < kKReads; ++m) {
+      const int piece = kInt4 ? 2 * h2 + m : 2 * m + h2;
+      k_addr[m] = base + krow * kRowBytes + ((piece ^ stage_swizzle<D, KT>(krow % kTile)) * 16);
+    }
     const int G = lane >> 4;
-    if constexpr (kFp8) {
+    if constexpr (kInt4) {
+      const int r = (lane >> 1) & 7, c = lane & 1;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int row = 16 * t + 8 * (G >> 1) + r;
+          const int piece = 2 * blk + (G & 1);
+          vt_addr[2 * t + blk] =
+              base + kTileB + row * kRowBytes + ((piece ^ stage_swizzle<D, KT>(row % kTile)) * 16) + c * 8;
+        }
+    } else if constexpr (kFp8) {
       const int r = (lane >> 1) & 7, c = lane & 1;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -902,7 +953,18 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
-    if constexpr (kFp8) {
+    if constexpr (kInt4) { // dword s of the lane's 32 bytes, as 136 + n (even nibbles, then odd)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t x = dword_of(kr[s >> 2], s & 3);
+        const uint32_t ev = int4_even(x), od = int4_odd(x);
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, make_uint4(offset_bf16_lo(ev), offset_bf16_hi(ev), offset_bf16_lo(od), offset_bf16_hi(od)));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[s], st, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[v] -= qoff;
+    } else if constexpr (kFp8) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_to_bf16x8(kr[m].x, kr[m].y), qop[2 * m], st, 0, 0, 0);
@@ -915,12 +977,13 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     }
     // keys before w_lo are seen by no column (their values need not be
     // finite): zero their V^T elements; the tile's scores there are masked
-    if (ts < w_lo) { // uniform branch
+    // (every INT4 code is finite)
+    if (!kInt4 && ts < w_lo) { // uniform branch
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int key = ts + 16 * t + (kFp8 ? 8 * (vt_g >> 1) + e : 8 * (e >> 2) + 4 * (vt_g >> 1) + (e & 3));
+          const int key = ts + 16 * t + (kPerm ? 8 * (vt_g >> 1) + e : 8 * (e >> 2) + 4 * (vt_g >> 1) + (e & 3));
           if (key < w_lo) {
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) vop[t][sl][e] = (__bf16)0.0f;
@@ -939,8 +1002,8 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     if (ts < all_lo || ts + kT > all_hi) { // some column misses some key (uniform)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8: key pi(row)
-        const int tok = ts + (kFp8 ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
+        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8 / INT4: key pi(row)
+        const int tok = ts + (kPerm ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
         if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
       }
     }
@@ -954,6 +1017,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
       const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = grow ? mx : m_run;
       l_run *= alpha;
+      if constexpr (kInt4) lb_run *= alpha;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -968,6 +1032,8 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
       const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
       sum += p0 + p1;
       pk[v / 2] = pack_bf16x2(p0, p1);
+      if constexpr (kInt4) // the weights as the P.V product sees them
+        lb_run += __uint_as_float(pk[v / 2] << 16) + __uint_as_float(pk[v / 2] & 0xFFFF0000u);
     }
     l_run += sum;
 #pragma unroll
@@ -990,7 +1056,23 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
         wait_vmem<(NBUF - 1) * 4 * kDmaH>(); // tile i has landed; NBUF - 1 newer tiles may fly
         uint4 kr[kKReads];
         bf16x8_t vop[2][4];
-        if constexpr (kFp8) {
+        if constexpr (kInt4) { // operand (t, 2 blk + odd): even or odd nibbles of one read, as 136 + n
+          uint2 vn[4];
+          lds_read_k2(kr[0], kr[1], k_addr[0] + j * kSlot, k_addr[1] + j * kSlot);
+          lds_read_tr8_x4(vn, *reinterpret_cast<const uint32_t(*)[4]>(&vt_addr[0]), j * kSlot);
+          issue(i + NBUF, j);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+              const uint2 x = vn[2 * t + blk];
+              const uint32_t e0 = int4_even(x.x), e1 = int4_even(x.y), o0 = int4_odd(x.x), o1 = int4_odd(x.y);
+              vop[t][2 * blk] = __builtin_bit_cast(
+                  bf16x8_t, make_uint4(offset_bf16_lo(e0), offset_bf16_hi(e0), offset_bf16_lo(e1), offset_bf16_hi(e1)));
+              vop[t][2 * blk + 1] = __builtin_bit_cast(
+                  bf16x8_t, make_uint4(offset_bf16_lo(o0), offset_bf16_hi(o0), offset_bf16_lo(o1), offset_bf16_hi(o1)));
+            }
+        } else if constexpr (kFp8) {
           uint2 v8[8];
           lds_read_x4(kr, k_addr, j * kSlot);
           lds_read_tr8_x8(v8, vt_addr, j * kSlot);
@@ -1022,6 +1104,8 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
 
   // ---- per-wave states to LDS, merged over the waves, one column group at a time ----
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
+  const float voff = kInt4 ? kInt4Offset * (lb_run + __shfl_xor(lb_run, 32, 64)) : 0.0f;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c > 0) {
@@ -1035,12 +1119,20 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
         sm_l[wave][h] = l_tot;
       }
       float *dst = sm_o + (wave * 16 + h) * OSTRIDE;
+      if constexpr (kInt4) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
+        for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4 *>(dst + 32 * sl + 8 * q + 4 * h2) =
-              make_float4(acc[sl][4 * q], acc[sl][4 * q + 1], acc[sl][4 * q + 2], acc[sl][4 * q + 3]);
+          for (int v = 0; v < 16; ++v)
+            dst[64 * (sl >> 1) + 2 * (8 * (v >> 2) + 4 * h2 + (v & 3)) + (sl & 1)] = acc[sl][v] - voff;
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(dst + 32 * sl + 8 * q + 4 * h2) =
+                make_float4(acc[sl][4 * q], acc[sl][4 * q + 1], acc[sl][4 * q + 2], acc[sl][4 * q + 3]);
+      }
     }
     __syncthreads();
     merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
@@ -1105,9 +1197,10 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
 hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, const Launch &l) {
   if (p.col_share != 2 || p.pack != 1) return hipErrorInvalidValue;
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2));
-  // one 16 KB bf16 slot per wave, two 8 KB fp8 ones: 64 KB per workgroup either way
+  // one 16 KB bf16 slot per wave, two 8 KB fp8 ones, four 4 KB INT4 ones: 64 KB per workgroup
   if (kv_type == DT_FP8) return launch_kernel(l, partial_cols32_kernel<DT_FP8, 2>, grid, p, w);
   if (kv_type == DT_BF16) return launch_kernel(l, partial_cols32_kernel<DT_BF16, 1>, grid, p, w);
+  if (kv_type == DT_INT4) return launch_kernel(l, partial_cols32_kernel<DT_INT4, 4>, grid, p, w);
   return hipErrorInvalidValue;
 }
 

@@ -246,19 +246,20 @@ def test_int4_head_dim_256_rows_from_three_groups():
     _check(make_inputs(spec, poison=True), kv_chunk=256)
 
 
-@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("kv", ["fp8", "bf16", "int4"])
 @pytest.mark.parametrize("chunk,window,extra", [
     (0, -1, {}), (16, -1, {}), (64, 100, {}), (0, 7, {}),
     (256, -1, {"unified_max": 40.0}), (0, -1, {"logits_soft_cap": 30.0}),
 ])
 def test_two_groups_cols32(kv, chunk, window, extra):
-    """bf16 or fp8 KV, head_dim 128, 17 to 32 (query row, head) columns per
-    KV head (fp8: 3 and 4 rows of 8 heads; bf16: 5 to 8 rows of 4 heads; and
-    fewer): the 32-column kernel whose waves split the keys, next to empty
-    and one-row requests."""
+    """bf16, fp8 or INT4 KV, head_dim 128, 17 to 32 (query row, head) columns
+    per KV head (fp8 / INT4: 3 and 4 rows of 8 heads; bf16: 5 to 8 rows of 4
+    heads; and fewer): the 32-column kernel whose waves split the keys, next
+    to empty and one-row requests."""
     print(f"case multi {kv} cols32 chunk={chunk} window={window} {extra}", flush=True)
-    if kv == "fp8":
-        spec = small_variant("c5_paged_fp8_b128", batch=5, lengths=("list", [3, 700, 2049, 40, 0]),
+    if kv in ("fp8", "int4"):
+        name = "c5_paged_fp8_b128" if kv == "fp8" else "c6_paged_int4_b128"
+        spec = small_variant(name, batch=5, lengths=("list", [3, 700, 2049, 40, 0]),
                              q_len=("list", [3, 4, 4, 1, 0]), window=window)
     else:
         spec = small_variant("c4_paged_bf16_b64", batch=5, lengths=("list", [5, 700, 2049, 40, 0]),
@@ -269,7 +270,7 @@ def test_two_groups_cols32(kv, chunk, window, extra):
     _check(make_inputs(spec, poison=True), kv_chunk=chunk, **extra)
 
 
-@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+@pytest.mark.parametrize("kv", ["fp8", "bf16", "int4"])
 def test_two_groups_cols32_device_planned(kv):
     """300 requests with 3 to 4 rows of 8 heads (the device-side work list)
     on the 32-column kernel."""
