@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299481172, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
+        {"bytes": 2299472156, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487912265, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
+        {"bytes": 1487906319, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538235136, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
+        {"bytes": 538233116, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680890759, "digest": "947dea4ccfad2abbcde4b4a1df45bbe80760b1a6bf62ba60f7759a0ca1c9fdf1"},
+        {"bytes": 680888097, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
 }
 
 
