@@ -396,7 +396,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     kernel = ("partial_valu_kernel" if plan.algo == kvs.KVS_ALGO_VALU else
               "partial_cols32_kernel" if plan.col_share == 2 and s.head_dim == 128 else
               "partial_mfma_kernel" if plan.col_share < 4 else
-              "partial_prefill_kernel" if (s.kv_dtype in ("bf16", "fp8") and s.head_dim == 128)
+              "partial_prefill_kernel" if (s.kv_dtype in ("bf16", "fp8", "int4") and s.head_dim == 128)
               or (s.kv_dtype == "bf16" and s.head_dim == 256) else
               "partial_rows_kernel")
     flops = attention_flops(inp)

@@ -4,7 +4,7 @@
 // waves of a workgroup own different columns and share every staged K/V
 // block, so the keys are read once for all of them: partial_rows_kernel with
 // the 16x16 operand layouts of mfma_tiles.h, and partial_prefill_kernel with
-// 32x32 tiles for bf16 head_dim 128.
+// 32x32 tiles for bf16, fp8 and INT4 at head_dim 128 and bf16 at 256.
 #include "mfma_tiles.h"
 
 namespace kvs {
@@ -225,8 +225,28 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
   }
 }
 
-// Several query rows per request, bf16 or fp8 KV at head_dim 128 and bf16 at
-// 256, from three groups of 16 columns on: 32x32 matrix tiles.  Each wave
+// Four 8-bit transposing reads (ds_read_b64_tr_b8, layout as for
+// lds_read_tr8_x8) at four lane addresses, one wait.
+__device__ __forceinline__ void lds_read_tr8_x4(uint2 (&v)[4], const uint32_t (&a)[4], uint32_t off) {
+  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v r0, r1, r2, r3;
+  __asm__ volatile("ds_read_b64_tr_b8 %0, %4\n\t"
+                   "ds_read_b64_tr_b8 %1, %5\n\t"
+                   "ds_read_b64_tr_b8 %2, %6\n\t"
+                   "ds_read_b64_tr_b8 %3, %7\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off)
+                   : "memory");
+  v[0] = __builtin_bit_cast(uint2, r0);
+  v[1] = __builtin_bit_cast(uint2, r1);
+  v[2] = __builtin_bit_cast(uint2, r2);
+  v[3] = __builtin_bit_cast(uint2, r3);
+}
+
+// Several query rows per request, bf16, fp8 or INT4 KV at head_dim 128 and
+// bf16 at 256, from three groups of 16 columns on (INT4: five): 32x32
+// matrix tiles.  Each wave
 // owns 32 (query row, head) columns of one KV head (at head_dim 256 a pair of
 // waves shares them, each keeping half of the output dims) and the
 // workgroup's four waves share every staged block of keys (one part staged
@@ -252,11 +272,19 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
 // are exactly the keys of a lane's P^T operand, operand row i of K reads the
 // staged row pi(i), pi swapping bits 3 and 2 of the row within each 16; score
 // row R then belongs to key pi(R).
+// INT4 KV: the same key order; a lane half takes 32 bytes of a K row (64
+// dims, nibbles as 136 + n in bf16, even dims then odd, the query permuted to
+// match), and one 8-bit transposing read per 64-dim block gives the even and
+// odd dims' V^T operands.  The offsets 136 * sum(q) and 136 * sum(p) are taken
+// out of the scores and the output.
+
 template <int D, int KT, int NBUF>
 __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params p, const InlineWork w) {
-  static_assert((D == 128 && (KT == DT_BF16 || KT == DT_FP8)) || (D == 256 && KT == DT_BF16),
-                "bf16 or fp8 at head_dim 128, bf16 at 256");
+  static_assert((D == 128 && (KT == DT_BF16 || KT == DT_FP8 || KT == DT_INT4)) || (D == 256 && KT == DT_BF16),
+                "bf16, fp8 or INT4 at head_dim 128, bf16 at 256");
   constexpr bool kFp8 = KT == DT_FP8;
+  constexpr bool kInt4 = KT == DT_INT4;
+  constexpr bool kPerm = kFp8 || kInt4; // V^T by 8-bit transposing reads: K rows pi-permuted
   using S = Shape<D, KT>;                         // bf16: 16 pieces a row per 128 dims; fp8: 8
   constexpr int kRowBytes = S::kRowBytes;         // one key's K (or V) row of the head
   // head_dim 256: waves 2 c and 2 c + 1 share column set c; both form the
@@ -345,21 +373,33 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   wv_hi = __builtin_amdgcn_readfirstlane(wv_hi);
 
   // Q^T operand of step s: dims 16 s + 8 h2 .. + 7 of the column's query
-  // (fp8: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .., the order of its K pieces)
+  // (fp8: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .., the order of its K pieces;
+  // INT4: the 8 dims of K dword 8 h2 + s, even ones first, as its nibbles)
   bf16x8_t qop[kSteps];
+  float qoff = 0.0f; // INT4: the scores carry 136 * (sum of the column's q)
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int d0 = kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2;
-      qop[s] = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
-                  : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      const int d0 = kInt4 ? 8 * (8 * h2 + s) : (kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2);
+      bf16x8_t x = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
+                      : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      if constexpr (kInt4) {
+        x = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qoff += (float)x[e];
+      }
+      qop[s] = x;
     }
   }
-  const float cscale = kFp8 ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
+  if constexpr (kInt4) qoff = (qoff + __shfl_xor(qoff, 32, 64)) * kInt4Offset;
+  const float cscale = kPerm ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
   const float cap_out = p.cap_out;
   float m_run = p.m_init, l_run = 0.0f;
-  f32x16_t acc[4]; // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
+  float lb_run = 0.0f; // INT4: the same sum of the bf16-rounded weights P.V saw
+  // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
+  // (INT4: dim 64 (sl / 2) + 2 (8 (v / 4) + 4 h2 + v % 4) + sl % 2)
+  f32x16_t acc[4];
 #pragma unroll
   for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -428,19 +468,37 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // K operand: bf16, step s: row j32 of the tile, piece 2 s + h2; fp8: row
   // pi(j32), piece 2 m + h2 for steps 2 m and 2 m + 1.  Eight steps per LDS
   // read block.
+  // INT4: pieces 2 h2 and 2 h2 + 1 of row pi(j32) (dwords 8 h2 .. 8 h2 + 7).
   uint32_t k_addr[kSteps / 8][8];
-  const int krow = kFp8 ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
+  const int krow = kPerm ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
   {
     const uint32_t base = lds_address(smem) + krow * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      k_addr[s / 8][s % 8] = base + (((kFp8 ? s & 3 : s) * 2 + h2) ^ row_swizzle(krow)) * 16;
+    for (int s = 0; s < kSteps; ++s) {
+      const int piece = kInt4 ? 2 * h2 + (s & 1) : (kFp8 ? s & 3 : s) * 2 + h2;
+      k_addr[s / 8][s % 8] = base + (piece ^ row_swizzle(krow)) * 16;
+    }
   }
   // fp8 V^T reads (ds_read_b64_tr_b8): lane 16 G + 2 r + c of group G points at
   // staged row 8 (G / 2) + r (+ 16 t), dims 32 sl + 16 (G % 2) + 8 c .. + 7
   // (piece 2 sl + G % 2, bytes 8 c of it); lane i of the group then holds rows
   // 8 (G / 2) + 0..7 of dim 32 sl + 16 (G % 2) + i.
-  uint32_t vt8_addr[8]; // [4 t + sl]
+  // INT4 V^T: one 8-bit transposing read per key half t and 64-dim block blk,
+  // lane 16 G + 2 r + c at row 16 t + 8 (G / 2) + r, bytes
+  // 32 blk + 16 (G % 2) + 8 c .. + 7: lane j of a half-wave holds byte j of
+  // the block (dims 2 j, 2 j + 1) for 8 consecutive keys.
+  uint32_t vt8_addr[8]; // [4 t + sl]; INT4: [2 t + blk]
+  if constexpr (kInt4) {
+    const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int row = 16 * t + 8 * (G >> 1) + r;
+        const int piece = 2 * blk + (G & 1);
+        vt8_addr[2 * t + blk] = lds_address(smem) + kHalf + row * kRowBytes + ((piece ^ row_swizzle(row)) * 16) + c * 8;
+      }
+  }
   if constexpr (kFp8) {
     const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
 #pragma unroll
@@ -460,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // 128 dh + 32 sl + 16 (G % 2) + i.  (Rows 16 .. 31 keep the swizzles of
   // rows 0 .. 15: kPart divides 16.)
   uint32_t vt_addr[8]; // [4 hh + sl]
-  if constexpr (!kFp8) {
+  if constexpr (!kPerm) {
     const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -478,7 +536,20 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     f32x16_t st;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st[v] = 0.0f;
-    if constexpr (kFp8) {
+    if constexpr (kInt4) { // dword s of the lane's 32 bytes, as 136 + n (even nibbles, then odd)
+      uint4 kr0, kr1;
+      lds_read_k2(kr0, kr1, k_addr[0][0] + to, k_addr[0][1] + to);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t x = dword_of(s < 4 ? kr0 : kr1, s & 3);
+        const uint32_t ev = int4_even(x), od = int4_odd(x);
+        const bf16x8_t kop = __builtin_bit_cast(
+            bf16x8_t, make_uint4(offset_bf16_lo(ev), offset_bf16_hi(ev), offset_bf16_lo(od), offset_bf16_hi(od)));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[s], st, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) st[v] -= qoff;
+    } else if constexpr (kFp8) {
       bf16x8_t kop[8];
       uint4 kr[4];
       lds_read_x4(kr, k_addr[0], to);
@@ -506,7 +577,21 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     // zeroed (a tile starting there is not whole: its scores are masked).
     const int vt_g = lane >> 4;
     bf16x8_t vop[2][4];
-    if constexpr (kFp8) {
+    if constexpr (kInt4) { // operand (t, 2 blk + odd): even or odd nibbles of one read, as 136 + n
+      uint2 vn[4];
+      lds_read_tr8_x4(vn, *reinterpret_cast<const uint32_t(*)[4]>(&vt8_addr[0]), to);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const uint2 x = vn[2 * t + blk];
+          const uint32_t e0 = int4_even(x.x), e1 = int4_even(x.y), o0 = int4_odd(x.x), o1 = int4_odd(x.y);
+          vop[t][2 * blk] = __builtin_bit_cast(
+              bf16x8_t, make_uint4(offset_bf16_lo(e0), offset_bf16_hi(e0), offset_bf16_lo(e1), offset_bf16_hi(e1)));
+          vop[t][2 * blk + 1] = __builtin_bit_cast(
+              bf16x8_t, make_uint4(offset_bf16_lo(o0), offset_bf16_hi(o0), offset_bf16_lo(o1), offset_bf16_hi(o1)));
+        }
+    } else if constexpr (kFp8) {
       uint2 v8[8];
       lds_read_tr8_x8(v8, vt8_addr, to);
       if (ts < wv_lo) { // lane holds rows 16 t + 8 (G / 2) + e, byte e (uniform branch)
@@ -574,8 +659,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     if (ts < all_lo || ts + 2 * kTile > all_hi) { // some column misses some key (uniform)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8: key pi(row)
-        const int tok = ts + (kFp8 ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
+        const int row = 8 * (v >> 2) + 4 * h2 + (v & 3); // score row; fp8, INT4: key pi(row)
+        const int tok = ts + (kPerm ? (row & ~12) | ((row & 8) >> 1) | ((row & 4) << 1) : row);
         if (tok < c_lo || tok >= c_hi) sv[v] = -INFINITY;
       }
     }
@@ -592,6 +677,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
       m_run = grow ? mx : m_run;
       l_run *= alpha;
+      if constexpr (kInt4) lb_run *= alpha;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -599,8 +685,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     }
     // No reference yet (m_run = -inf) means every score of the tile is
     // masked, so any finite offset gives weights of 0 (bf16: one select per
-    // tile).  The fp8 variant keeps a select per weight: the shorter form
-    // pushed its register allocation past 256 (one wave per SIMD).
+    // tile).  The fp8 and INT4 variants keep a select per weight: the shorter
+    // form pushed their register allocation past 256 (one wave per SIMD).
     const bool live = m_run != -INFINITY;
     const float neg_m = live ? -m_run : 0.0f;
     uint32_t pk[8];
@@ -608,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       float p0, p1;
-      if constexpr (kFp8) {
+      if constexpr (kPerm) {
         p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
         p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
       } else {
@@ -617,6 +703,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       }
       sum += p0 + p1;
       pk[v / 2] = pack_bf16x2(p0, p1);
+      if constexpr (kInt4) // the weights as the P.V product sees them
+        lb_run += __uint_as_float(pk[v / 2] << 16) + __uint_as_float(pk[v / 2] & 0xFFFF0000u);
     }
     l_run += sum;
     // ---- O^T += V^T . P^T, k = 16 keys per product ----
@@ -658,9 +746,52 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!ok) return;
   const bool live = l_tot > 0.0f;
-  const float vscale = kFp8 ? p.v_scale[b * Hk + kvg] : 1.0f;
+  const float vscale = kPerm ? p.v_scale[b * Hk + kvg] : 1.0f;
   const float inv = live ? vscale / l_tot : 0.0f;
   const float lse2 = live ? m_run + __log2f(l_tot) : -INFINITY;
+  if constexpr (kInt4) {
+    // V entered the product as 136 + n: remove 136 * (sum of the weights it
+    // saw).  Slices 2 blk and 2 blk + 1 hold the even and odd dims of block
+    // blk, so registers 4 q .. 4 q + 3 of the pair are dims
+    // 64 blk + 16 q + 8 h2 .. + 7, interleaved.
+    const float voff = kInt4Offset * (lb_run + __shfl_xor(lb_run, 32, 64));
+    float *dst = nullptr;
+    uint16_t *orow = nullptr;
+    size_t slot = 0;
+    if (nb == 1) {
+      orow = reinterpret_cast<uint16_t *>(p.o) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
+    } else {
+      slot = ((size_t)kvg * p.col_groups + col / 16) * p.items + item;
+      dst = p.o_part + (slot * p.cols + col % 16) * D;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float o8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o8[2 * e] = (acc[2 * blk][4 * q + e] - voff) * inv;
+          o8[2 * e + 1] = (acc[2 * blk + 1][4 * q + e] - voff) * inv;
+        }
+        const int d0 = 64 * blk + 16 * q + 8 * h2;
+        if (nb == 1) {
+          *reinterpret_cast<uint4 *>(orow + d0) = make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]),
+                                                             pack_bf16x2(o8[4], o8[5]), pack_bf16x2(o8[6], o8[7]));
+        } else {
+          *reinterpret_cast<float4 *>(dst + d0) = make_float4(o8[0], o8[1], o8[2], o8[3]);
+          *reinterpret_cast<float4 *>(dst + d0 + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+        }
+      }
+    if (h2 == 0) {
+      if (nb == 1) {
+        if (p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
+      } else {
+        p.lse_part[slot * p.cols + col % 16] = lse2;
+      }
+    }
+    return;
+  }
   if (nb == 1) {
     uint16_t *orow = reinterpret_cast<uint16_t *>(p.o) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
@@ -687,25 +818,6 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       }
     if (h2 == 0 && dh == 0) p.lse_part[slot * p.cols + col % 16] = lse2;
   }
-}
-
-// Four 8-bit transposing reads (ds_read_b64_tr_b8, layout as for
-// lds_read_tr8_x8) at four lane addresses, one wait.
-__device__ __forceinline__ void lds_read_tr8_x4(uint2 (&v)[4], const uint32_t (&a)[4], uint32_t off) {
-  typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
-  u32x2v r0, r1, r2, r3;
-  __asm__ volatile("ds_read_b64_tr_b8 %0, %4\n\t"
-                   "ds_read_b64_tr_b8 %1, %5\n\t"
-                   "ds_read_b64_tr_b8 %2, %6\n\t"
-                   "ds_read_b64_tr_b8 %3, %7\n\t"
-                   "s_waitcnt lgkmcnt(0)"
-                   : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-                   : "v"(a[0] + off), "v"(a[1] + off), "v"(a[2] + off), "v"(a[3] + off)
-                   : "memory");
-  v[0] = __builtin_bit_cast(uint2, r0);
-  v[1] = __builtin_bit_cast(uint2, r1);
-  v[2] = __builtin_bit_cast(uint2, r2);
-  v[3] = __builtin_bit_cast(uint2, r3);
 }
 
 // Two column groups (17 to 32 (query row, head) columns per KV head: a few
@@ -1165,7 +1277,9 @@ constexpr int rows_nbuf() {
 // it from 3 groups too (batch-128 fp8 at head_dim 256, 8 rows: 904 us,
 // against 2059 us chunk-splitting and 962 us on the 32x32 kernel, whose wave
 // pairs convert every K code twice; INT4, 6 and 8 rows: 751 and 781 us
-// against 874 and 1128 us chunk-splitting).
+// against 874 and 1128 us chunk-splitting).  INT4 at head_dim 128 keeps 5
+// groups on the 32x32 kernel as well (batch-128, 6 and 8 rows: 510 and
+// 537 us on the 32-column kernel, 557 and 559 us on the 32x32 one).
 constexpr int kRowsMinGroupsBf16 = 3;
 constexpr int kRowsMinGroupsQuant = 5;
 
@@ -1176,7 +1290,8 @@ constexpr int kRowsMinGroupsQuant = 5;
 // covers 8 groups (head_dim <= 128) or 4 (256) and reads the keys once for
 // all of them.
 int mfma_col_share(int head_dim, int kv_type, int col_groups) {
-  // bf16 and fp8 at head_dim 128 (bf16 at 256 too) take the 32x32 prefill kernel there
+  // bf16, fp8 and INT4 at head_dim 128 (bf16 at 256 too) take the 32x32
+  // prefill kernel there; bf16 and fp8 at 128 from 3 groups
   const bool tiles32 = head_dim == 128 && (kv_type == DT_BF16 || kv_type == DT_FP8);
   const bool quant_wide = (kv_type == DT_FP8 || kv_type == DT_INT4) && head_dim == 256;
   if (col_groups >= (kv_type == DT_BF16 || tiles32 || quant_wide ? kRowsMinGroupsBf16 : kRowsMinGroupsQuant))
@@ -1189,8 +1304,8 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
   constexpr int kGroups = kWaves * rows_cg<D>();
   if (p.col_share != kGroups || p.pack != 1) return hipErrorInvalidValue;
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + kGroups - 1) / kGroups));
-  if constexpr ((D == 128 && (KT == DT_BF16 || KT == DT_FP8)) || (D == 256 && KT == DT_BF16))
-    return launch_kernel(l, partial_prefill_kernel<D, KT, KT == DT_FP8 ? 4 : 2>, grid, p, w);
+  if constexpr ((D == 128 && (KT == DT_BF16 || KT == DT_FP8 || KT == DT_INT4)) || (D == 256 && KT == DT_BF16))
+    return launch_kernel(l, partial_prefill_kernel<D, KT, KT == DT_INT4 ? 8 : (KT == DT_FP8 ? 4 : 2)>, grid, p, w);
   return launch_kernel(l, partial_rows_kernel<D, KT, rows_nbuf<D, KT>(), rows_cg<D>()>, grid, p, w);
 }
 

@@ -166,12 +166,14 @@ def test_rows_page_sizes(P, rows):
     _check(make_inputs(spec, poison=True))
 
 
+@pytest.mark.parametrize("kv", ["fp8", "int4"])
 @pytest.mark.parametrize("W", [1, 17, 64, 300])
-def test_rows_window_fp8_shared_tile(W):
-    """fp8 with 8 heads per KV head and 20-40 rows (the shared-tile kernel)
-    under a sliding window."""
-    print(f"case multi window fp8 {W}", flush=True)
-    spec = dataclasses.replace(small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [40, 700, 1500]),
+def test_rows_window_quantised_32x32(W, kv):
+    """fp8 and INT4 with 8 heads per KV head and 20-40 rows (the 32x32
+    kernel) under a sliding window."""
+    print(f"case multi window {kv} {W}", flush=True)
+    name = "c5_paged_fp8_b128" if kv == "fp8" else "c6_paged_int4_b128"
+    spec = dataclasses.replace(small_variant(name, batch=3, lengths=("list", [40, 700, 1500]),
                                              q_len=("list", [40, 20, 33])), window=W)
     _check(make_inputs(spec, poison=True))
 
@@ -181,8 +183,7 @@ def test_fresh_prefill_longer_than_a_chunk(Hq, Hk, kv):
     """A fresh 1024-row prefill in 256-key chunks: the rows reach over four
     chunks, so the multi-row kernels take their XCD-balanced workgroup order
     (whole KV heads per XCD with 8 KV heads, interleaved row blocks with 2);
-    bf16 runs the 32x32 kernel, INT4 the shared-tile kernel.  Every row
-    against the oracle."""
+    both KV types run the 32x32 kernel.  Every row against the oracle."""
     print(f"case multi fresh prefill Hq={Hq} Hk={Hk} kv={kv}", flush=True)
     spec = DecodeSpec("freshpf", 2, Hq, Hk, 128, 16, kv, "bf16", 128 ** -0.5,
                       lengths=("list", [1024, 700]), q_len=("list", [1024, 700]), seed=23 + Hk)
