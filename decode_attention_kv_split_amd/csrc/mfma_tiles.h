@@ -566,6 +566,7 @@ struct ColumnSet {
   int lo[CG], hi[CG];         // keys of the chunk the lane's column sees
   float m[CG];                // reference max, log2 domain (the same in the 4 quarters)
   float l[CG];                // partial sum over the lane's tokens
+  bool seen[CG];              // the column has had a visible key (the same in its 4 lanes)
   float lb[CG];               // INT4: the same sum of the bf16-rounded weights P.V saw
   f32x4_t acc[CG][S::kOTiles];
 };
@@ -667,6 +668,7 @@ __device__ __forceinline__ void load_columns(ColumnSet<DE, KT, CG> &cs, const Pa
     }
     cs.m[c] = p.m_init;
     cs.l[c] = 0.0f;
+    cs.seen[c] = false;
     cs.lb[c] = 0.0f;
 #pragma unroll
     for (int w = 0; w < S::kOTiles; ++w) cs.acc[c][w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -753,8 +755,11 @@ __device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, c
   // reference is used.
   // m = -inf: any visible key grows it.  A given starting reference (unified
   // max) far above a still-empty state's first scores is moved down to
-  // them, so no weight underflows.
-  const bool empty = cs.l[c] == 0.0f;
+  // them, so no weight underflows.  Empty means no visible key in the whole
+  // column so far: a lane's own l can be 0 while the column's other lanes
+  // have keys (a window start inside a tile), and its share of the output
+  // dims then already holds their contributions.
+  const bool empty = !cs.seen[c];
   const bool grow = mx > cs.m[c] + kLazy || (empty && mx != -INFINITY && mx < cs.m[c] - kDrop);
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(cs.m[c] - mx)) : 1.0f;
@@ -767,6 +772,7 @@ __device__ __forceinline__ void softmax_step(ColumnSet<DE, KT, CG> &cs, int c, c
       for (int r = 0; r < 4; ++r) cs.acc[c][w][r] *= alpha;
     }
   }
+  cs.seen[c] = cs.seen[c] || mx != -INFINITY;
   // no visible key so far for this column: weights 0, state unchanged
   const bool live = cs.m[c] != -INFINITY;
   float pr[NS];

@@ -396,6 +396,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const float cscale = kPerm ? p.score_scale * p.k_scale[b * Hk + kvg] : p.score_scale;
   const float cap_out = p.cap_out;
   float m_run = p.m_init, l_run = 0.0f;
+  bool seen = false; // the column has had a visible key (the same in its two lanes)
   float lb_run = 0.0f; // INT4: the same sum of the bf16-rounded weights P.V saw
   // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4
   // (INT4: dim 64 (sl / 2) + 2 (8 (v / 4) + 4 h2 + v % 4) + sl % 2)
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     mx *= ks; // in scaled units
     // lazy rescale (as in the 16x16 kernels): the reference moves only when a
     // score exceeds it by more than kLazy
-    const bool empty = l_run == 0.0f;
+    const bool empty = !seen; // not l_run == 0: the column's other lane may hold its keys so far
     const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
@@ -683,6 +684,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[sl][v] *= alpha;
     }
+    seen = seen || mx != -INFINITY;
     // No reference yet (m_run = -inf) means every score of the tile is
     // masked, so any finite offset gives weights of 0 (bf16: one select per
     // tile).  The fp8 and INT4 variants keep a select per weight: the shorter
@@ -940,6 +942,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
   const bool capped = cap_out > 0.0f;
   const float ks = capped ? 1.0f : fmaxf(cscale, __FLT_MIN__); // see partial_prefill_kernel
   float m_run = p.m_init, l_run = 0.0f;
+  bool seen = false; // the column has had a visible key (the same in its two lanes)
   float lb_run = 0.0f; // INT4: the same sum of the bf16-rounded weights P.V saw
   // O^T, 32-dim slice sl: register v holds dim 32 sl + 8 (v / 4) + 4 h2 + v % 4;
   // INT4: dim 64 (sl / 2) + 2 (8 (v / 4) + 4 h2 + v % 4) + sl % 2
@@ -1123,7 +1126,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = xor32_max(mx) * ks;
-    const bool empty = l_run == 0.0f;
+    const bool empty = !seen; // not l_run == 0: the column's other lane may hold its keys so far
     const bool grow = mx > m_run + kLazy || (empty && mx != -INFINITY && mx < m_run - kDrop);
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float alpha = grow ? (empty ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx)) : 1.0f;
@@ -1135,6 +1138,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[sl][v] *= alpha;
     }
+    seen = seen || mx != -INFINITY;
     const bool live = m_run != -INFINITY;
     uint32_t pk[8];
     float sum = 0.0f;

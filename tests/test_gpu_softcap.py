@@ -73,6 +73,19 @@ def test_rows_and_window():
     _check(make_inputs(dataclasses.replace(spec, window=64), poison=True))
 
 
+@pytest.mark.parametrize("umax", [None, 4.0, -3.0])
+@pytest.mark.parametrize("name", ["c4_paged_bf16_b64", "c5_paged_fp8_b128", "c6_paged_int4_b128"])
+def test_rows_32x32_kernel(name, umax):
+    """9-33 rows per request (5 to 17 groups of 16 columns: the 32x32
+    kernel for every KV type at head_dim 128) with a cap, a window and
+    256-key chunks, with and without a unified max."""
+    print(f"case softcap rows 32x32 {name} umax={umax}", flush=True)
+    spec = _capped(small_variant(name, batch=3, lengths=("list", [40, 700, 1500]), q_len=("list", [20, 9, 33])),
+                   4.0)
+    kw = {} if umax is None else {"unified_max": umax}
+    _check(make_inputs(dataclasses.replace(spec, window=300), poison=True), kv_chunk=256, **kw)
+
+
 @pytest.mark.parametrize("umax", [4.0, 1.0, -3.0])
 def test_unified_max(umax):
     """The cap bounds every score by c, so a unified max of c never needs
