@@ -43,13 +43,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299472156, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
+        {"bytes": 2299480990, "digest": "082e81f2c25202d265757d5aed677df69682ece767378546413e408e29eb8f07"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487906319, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
+        {"bytes": 1487914590, "digest": "082e81f2c25202d265757d5aed677df69682ece767378546413e408e29eb8f07"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538233116, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
+        {"bytes": 538234282, "digest": "082e81f2c25202d265757d5aed677df69682ece767378546413e408e29eb8f07"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680888097, "digest": "b93752913345083343dc4d9fc590ffa24f234238b5c9a7e4223ddf6857ce632a"},
+        {"bytes": 680890838, "digest": "082e81f2c25202d265757d5aed677df69682ece767378546413e408e29eb8f07"},
 }
 
 
