@@ -314,3 +314,41 @@ def test_python_helpers_single_and_paged():
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.decode_reference(inp)
     compare(o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy(), o_ref, lse_ref, spec.kv_dtype)
+
+
+@pytest.mark.parametrize("q_len,d", [
+    (None, 128),  # decode kernel
+    (6, 128),     # 32-column kernel
+    (40, 128),    # 32x32 kernel
+    (40, 64),     # shared-tile kernel
+])
+def test_score_spike_after_a_window_start_inside_a_tile(q_len, d):
+    """Default settings, a wide score range: the one-row window starts at
+    key 29 of a 32-key tile (13 of a 16-key one), and every K row from the
+    next tile on is scaled by 8 (exactly, a power of two), so the scores
+    after the first few visible keys lie far above theirs and the softmax
+    reference moves in mid-stream.  (With two tiles per softmax update in
+    the decode kernel this does not leave any lane of a column without keys
+    when the reference moves; the unified-max tests force that case.)"""
+    print(f"case spike after window start q={q_len} d={d}", flush=True)
+    kw = {} if q_len is None else {"q_len": ("fixed", q_len)}
+    spec = dataclasses.replace(small_variant("c4_paged_bf16_b64", batch=3, lengths=("list", [714, 1530, 362]),
+                                             window=301, **kw), head_dim=d, sm_scale=d ** -0.5)
+    inp = make_inputs(spec, poison=True)
+    k = np.array(inp.k, copy=True)
+    P = spec.page_size
+    for b in range(spec.batch):
+        L = int(inp.kv_len[b])
+        n = 1 if inp.qo_indptr is None else int(inp.qo_indptr[b + 1] - inp.qo_indptr[b])
+        lo = (max(0, L - n - spec.window + 1) // 32 + 1) * 32  # the next 32-key (and 16-key) tile
+        for t in range(lo, L):
+            page = int(inp.page_indices[inp.page_indptr[b] + t // P])
+            row = (k[page, t % P].astype(np.uint32) << 16).view(np.float32) * np.float32(8.0)
+            k[page, t % P] = (row.view(np.uint32) >> 16).astype(np.uint16)
+    inp = dataclasses.replace(inp, k=k)
+    if inp.qo_indptr is None:
+        o_ref, lse_ref = oracle.decode_reference(inp)
+    else:
+        o_ref, lse_ref = oracle.attention_reference(inp)
+    o, lse = run_library(inp, kv_chunk=256)
+    compare(o, lse, o_ref, lse_ref, "bf16")

@@ -66,15 +66,15 @@ def test_reference_moves_after_a_window_start_inside_a_tile(name, q_len, d):
     """A column's keys are spread over several lanes.  A window start inside
     a tile leaves some of them with no visible key on that tile while the
     others already hold weights; a unified max of -3 under a cap of 4 then
-    makes the reference move on a later tile.  The state must count as
+    makes the reference move on a later tile (the one-row window start L - 301
+    is key 29 of its 32-key tile, 13 of its 16-key one).  The state must count as
     non-empty in every lane of the column, or the lanes without keys so far
     would drop their share of the output (and could move their reference
     apart from the others)."""
     print(f"case unified max moving reference {name} q={q_len} d={d}", flush=True)
     kw = {} if q_len is None else {"q_len": ("fixed", q_len)}
-    # one-row window starts L - 300 at key 30 of a 32-key tile (14 of a 16-key
-    # one): only the column's last lanes see keys there; with several rows
-    # the starts run through every offset
+    # only the column's last lanes see keys on the first tile; with several
+    # rows the starts run through every offset
     spec = dataclasses.replace(small_variant(name, batch=3, lengths=("list", [714, 1530, 362]), window=301, **kw),
                                head_dim=d, sm_scale=d ** -0.5, soft_cap=4.0)
     inp = make_inputs(spec, poison=True)
