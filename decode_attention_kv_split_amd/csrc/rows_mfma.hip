@@ -548,8 +548,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
             bf16x8_t, make_uint4(offset_bf16_lo(ev), offset_bf16_hi(ev), offset_bf16_lo(od), offset_bf16_hi(od)));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[s], st, 0, 0, 0);
       }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[v] -= qoff;
+      // st still carries qoff: taken out in the max and the exponent below
     } else if constexpr (kFp8) {
       bf16x8_t kop[8];
       uint4 kr[4];
@@ -652,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     float sv[16];
     if (capped) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sv[v] = tanhf(st[v] * cscale) * cap_out;
+      for (int v = 0; v < 16; ++v) sv[v] = tanhf((kInt4 ? st[v] - qoff : st[v]) * cscale) * cap_out;
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sv[v] = st[v];
@@ -669,6 +668,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = xor32_max(mx);
+    if constexpr (kInt4) mx -= capped ? 0.0f : qoff; // uncapped INT4 scores still carry qoff
     mx *= ks; // in scaled units
     // lazy rescale (as in the 16x16 kernels): the reference moves only when a
     // score exceeds it by more than kLazy
@@ -691,14 +691,15 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     // form pushed their register allocation past 256 (one wave per SIMD).
     const bool live = m_run != -INFINITY;
     const float neg_m = live ? -m_run : 0.0f;
+    const float bias = kInt4 && !capped ? -m_run - qoff * ks : -m_run; // fp8, INT4 exponent offset
     uint32_t pk[8];
     float sum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       float p0, p1;
       if constexpr (kPerm) {
-        p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, -m_run)) : 0.0f;
-        p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, -m_run)) : 0.0f;
+        p0 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v], ks, bias)) : 0.0f;
+        p1 = live ? __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, bias)) : 0.0f;
       } else {
         p0 = __builtin_amdgcn_exp2f(fmaf(sv[v], ks, neg_m));
         p1 = __builtin_amdgcn_exp2f(fmaf(sv[v + 1], ks, neg_m));
