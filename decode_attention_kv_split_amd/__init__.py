@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 7
+KVS_ABI_VERSION = 8
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
@@ -257,7 +257,11 @@ _ws_lock = threading.Lock()
 
 
 def _workspace(nbytes: int, device, stream: int):
-    """Per (device, stream) scratch buffer, grown on demand (torch allocation)."""
+    """Per (device, stream) scratch buffer, grown on demand (torch allocation).
+
+    The buffer is allocated on the stream that uses it, so that when a larger
+    one replaces it, torch's caching allocator hands its memory out again
+    only in that stream's order (after the kernels that still use it)."""
     import torch
 
     if nbytes == 0:
@@ -266,7 +270,8 @@ def _workspace(nbytes: int, device, stream: int):
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            with torch.cuda.device(device), torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
+                buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             _ws_cache[key] = buf
     return buf
 
@@ -311,8 +316,8 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     else:
         if k.dim() != 3:
             raise ValueError("contiguous k/v must be [kv_len, num_kv_heads, head_dim]")
-        _, Hk, dk = k.shape
-        P, num_pages = 0, 0
+        capacity, Hk, dk = k.shape
+        P, num_pages = 0, capacity
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("k and v must have the same shape and dtype")
     if kv_dtype == "int4":
@@ -320,22 +325,29 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
             raise ValueError("int4 k/v must be uint8 with head_dim / 2 bytes per row")
     elif dk != d:
         raise ValueError("head_dim of q and k differ")
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len"), (page_indptr, "page_indptr"),
-                 (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale"),
-                 (qo_indptr, "qo_indptr")):
-        _check_dev(t, n, device)
     if kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("kv_len must be int32 [batch]")
     if kv_len_host is None:
         kv_len_host = kv_len.cpu()
     kvh = np.ascontiguousarray(np.asarray(kv_len_host.cpu() if isinstance(kv_len_host, torch.Tensor)
                                           else kv_len_host, dtype=np.int32))
+    if kvh.shape != (B,):
+        raise ValueError("kv_len_host must hold one length per request")
+    if not paged and B and int(kvh.max()) > k.shape[0]:
+        raise ValueError("kv_len exceeds the rows of the contiguous cache")
     if out is None:
         out = torch.empty((rows, Hq, d), dtype=q.dtype, device=device)
+    elif tuple(out.shape) != (rows, Hq, d) or out.dtype != q.dtype:
+        raise ValueError(f"out must be [{rows}, {Hq}, {d}] in q's dtype")
     if lse is None:
         lse = torch.empty((rows, Hq), dtype=torch.float32, device=device)
-    _check_dev(out, "out", device)
-    _check_dev(lse, "lse", device)
+    elif tuple(lse.shape) != (rows, Hq) or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 [{rows}, {Hq}]")
+    # shapes and types first (above), then where the tensors live
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (kv_len, "kv_len"), (page_indptr, "page_indptr"),
+                 (page_indices, "page_indices"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (qo_indptr, "qo_indptr"), (out, "out"), (lse, "lse")):
+        _check_dev(t, n, device)
     a = KvsDecodeArgs()
     a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = B, Hq, Hk, d
     a.q_dtype = _dtype_code(q, "q")

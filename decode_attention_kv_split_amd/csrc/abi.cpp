@@ -56,6 +56,7 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
   if (a->page_size > 0 && a->num_pages < 1) return KVS_ERR_INVALID_ARG;
+  if (a->num_pages < 0) return KVS_ERR_INVALID_ARG;
   if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale)) return KVS_ERR_INVALID_ARG;
   if (a->window < -1 || a->window == 0) return KVS_ERR_INVALID_ARG;
   if (a->kv_chunk < 0) return KVS_ERR_INVALID_ARG;
@@ -67,7 +68,9 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   for (int b = 0; b < a->batch; ++b) {
     const int L = a->kv_len_host[b];
     if (L < 0) return KVS_ERR_INVALID_ARG;
-    if (a->page_size > 0 && (int64_t)L > (int64_t)a->num_pages * a->page_size) return KVS_ERR_INVALID_ARG;
+    // the pool (paged) or the rows of the cache (contiguous) must hold L tokens
+    const int64_t capacity = a->page_size > 0 ? (int64_t)a->num_pages * a->page_size : (int64_t)a->num_pages;
+    if ((int64_t)L > capacity) return KVS_ERR_INVALID_ARG;
   }
   // several queries per request: row offsets start at 0, never decrease, and
   // a request has at most kv_len new tokens

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 7
+#define KVS_ABI_VERSION 8
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -97,8 +97,10 @@ typedef struct {
   int32_t page_size;    /* 0: contiguous K, V [kv_len, Hk, head_dim];
                            > 0: paged pools [num_pages, page_size, Hk, head_dim]
                            (INT4: the last axis is head_dim / 2 bytes) */
-  int32_t num_pages;    /* paged: number of pages in each pool (for validation of
-                           the host-side lengths only; page ids are not checked) */
+  int32_t num_pages;    /* paged: number of pages in each pool; contiguous: the
+                           cache's capacity in tokens (rows of k and v).  Only
+                           the host-side lengths are checked against it
+                           (kv_len_host[b] <= capacity); page ids are not */
 
   /* device inputs (caller-owned, row-major, dense) */
   const void *q;               /* [batch, Hq, head_dim], q_dtype */

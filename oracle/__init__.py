@@ -12,9 +12,9 @@ the codecs) and invariants of the definition; see ``tests/test_oracle.py``,
 ``tests/test_codecs.py`` and ``tests/test_append_oracle.py``.
 """
 from .append import (append_codes, append_reference, apply_append, cache_slot, rms_norm, rope,
-                     rope_angles, transform_head)
+                     rope_angles, token_rows, transform_head)
 from .codecs import (bf16_to_f64, decode_codes, encode_codes, f64_to_bf16_codes, f64_to_fp8_e4m3fn_codes,
-                     fp8_e4m3fn_to_f64, int4_to_f64, round_to_grid)
+                     f64_to_int4_codes, fp8_e4m3fn_to_f64, int4_to_f64, round_to_grid)
 from .multi import attention_reference, query_position, query_range
 from .decode import (attend_chunked, attend_direct, cap_scores, chunk_state, decode_reference,
                      decode_reference_chunked, decode_reference_sampled, kv_head_of,
@@ -22,9 +22,9 @@ from .decode import (attend_chunked, attend_direct, cap_scores, chunk_state, dec
 
 __all__ = [
     "bf16_to_f64", "fp8_e4m3fn_to_f64", "int4_to_f64", "decode_codes", "encode_codes", "f64_to_bf16_codes",
-    "f64_to_fp8_e4m3fn_codes", "round_to_grid",
+    "f64_to_fp8_e4m3fn_codes", "f64_to_int4_codes", "round_to_grid",
     "rms_norm", "rope", "rope_angles", "transform_head", "append_reference", "append_codes",
-    "apply_append", "cache_slot",
+    "apply_append", "cache_slot", "token_rows",
     "attend_direct", "attend_chunked", "cap_scores", "chunk_state", "merge_states", "softmax_from_scores",
     "decode_reference", "decode_reference_chunked", "decode_reference_sampled",
     "kv_head_of", "visible_range", "request_kv",

@@ -12,7 +12,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["bf16_to_f64", "fp8_e4m3fn_to_f64", "int4_to_f64", "decode_codes",
-           "round_to_grid", "f64_to_bf16_codes", "f64_to_fp8_e4m3fn_codes", "encode_codes"]
+           "round_to_grid", "f64_to_bf16_codes", "f64_to_fp8_e4m3fn_codes", "f64_to_int4_codes", "encode_codes"]
 
 
 def bf16_to_f64(codes: np.ndarray) -> np.ndarray:
@@ -135,12 +135,29 @@ def f64_to_fp8_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def f64_to_int4_codes(x: np.ndarray) -> np.ndarray:
+    """Packed signed 4-bit codes of x [..., 2n] (values already divided by
+    their scale): each element becomes the nearest integer, ties to the even
+    one, saturated to [-8, 7] (NaN gives 0); element 2i goes to the low
+    nibble of byte i, element 2i + 1 to the high one, as two's complement.
+    Returns [..., n] uint8."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.shape[-1] % 2:
+        raise ValueError("INT4 rows hold an even number of elements")
+    k = np.clip(np.rint(np.nan_to_num(x, nan=0.0)), -8, 7).astype(np.int64)  # np.rint: half to even
+    nib = k & 0xF
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
 def encode_codes(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 to storage codes ('f32', 'bf16', 'fp8'), nearest-even."""
+    """float64 to storage codes ('f32', 'bf16', 'fp8', 'int4'), nearest-even
+    (int4: the last axis halves)."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32)
     if dtype == "bf16":
         return f64_to_bf16_codes(x)
     if dtype == "fp8":
         return f64_to_fp8_e4m3fn_codes(x)
+    if dtype == "int4":
+        return f64_to_int4_codes(x)
     raise ValueError(f"unknown storage type {dtype!r}")

@@ -11,8 +11,11 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# max |o - o_ref| over all elements, by KV storage type
-O_TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int4": 6e-2}
+# max |o - o_ref| over all elements, by KV storage type.  INT4 takes the
+# bf16 gate: the oracle decodes the same codes, and the kernel's arithmetic
+# on them is the bf16 path's (exact bf16 operands 136 + n, bf16 weights,
+# fp32 accumulation).
+O_TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int4": 2e-2}
 LSE_REL = 1e-3
 
 

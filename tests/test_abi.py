@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 7
-    assert re.search(r"#define KVS_ABI_VERSION 7\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 8
+    assert re.search(r"#define KVS_ABI_VERSION 8\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -115,7 +115,10 @@ BAD = [
     (dict(q=kvs.KVS_F32, kv=kvs.KVS_INT4), kvs.KVS_ERR_UNSUPPORTED),
     (dict(kv=4), kvs.KVS_ERR_INVALID_ARG),
     # 2^26 splits of 16 tokens x 32 KV heads: more workgroups than one launch holds
-    (dict(batch=1, P=0, Hq=32, Hk=32, lens=(1 << 30,), chunk=16), kvs.KVS_ERR_UNSUPPORTED),
+    (dict(batch=1, P=0, Hq=32, Hk=32, lens=(1 << 30,), chunk=16, num_pages=1 << 30), kvs.KVS_ERR_UNSUPPORTED),
+    # a contiguous cache holds num_pages tokens
+    (dict(batch=1, P=0, lens=(1001,), num_pages=1000), kvs.KVS_ERR_INVALID_ARG),
+    (dict(batch=1, P=0, lens=(5,), num_pages=-1), kvs.KVS_ERR_INVALID_ARG),
 ]
 
 
@@ -250,7 +253,7 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
 
 
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):
-    a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(32768,), num_pages=0)
+    a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(32768,), num_pages=32768)
     info = kvs.kvs_decode_plan(a)
     assert info.items_per_kv_head * 32 >= 256  # at least one chunk per CU
     assert info.kv_chunk >= 512
@@ -262,7 +265,7 @@ def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):
 
 
 def test_algo_resolution(lib):
-    a, keep = _args(q=kvs.KVS_F32, kv=kvs.KVS_F32, Hq=8, Hk=8, d=64, batch=1, P=0, lens=(512,), num_pages=0)
+    a, keep = _args(q=kvs.KVS_F32, kv=kvs.KVS_F32, Hq=8, Hk=8, d=64, batch=1, P=0, lens=(512,), num_pages=512)
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_VALU
     a, keep = _args(P=8)
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_VALU
@@ -270,7 +273,7 @@ def test_algo_resolution(lib):
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
     a.algo = kvs.KVS_ALGO_MFMA_PACKED
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA_PACKED
-    a, keep = _args(q=kvs.KVS_F32, kv=kvs.KVS_F32, Hq=8, Hk=8, d=64, batch=1, P=0, lens=(512,), num_pages=0,
+    a, keep = _args(q=kvs.KVS_F32, kv=kvs.KVS_F32, Hq=8, Hk=8, d=64, batch=1, P=0, lens=(512,), num_pages=512,
                     algo=kvs.KVS_ALGO_MFMA_PACKED)
     with pytest.raises(kvs.KvsError):
         kvs.kvs_decode_plan(a)
@@ -341,3 +344,49 @@ def test_int4_packs_two_heads_when_it_can(lib):
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
     a, keep = _args(kv=kvs.KVS_FP8_E4M3, ptrs=False)             # fp8 stays unpacked by default
     assert kvs.kvs_decode_plan(a).algo == kvs.KVS_ALGO_MFMA
+
+
+# ----------------------------------------------------------------------------
+# the Python binding rejects buffers the kernels would overrun, before it
+# looks at where the tensors live (so these checks run on the CPU)
+# ----------------------------------------------------------------------------
+
+def _torch_case(L=40, cap=40, paged=False):
+    import torch
+
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    if paged:
+        k = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16)
+        extra = dict(page_indptr=torch.tensor([0, 3], dtype=torch.int32),
+                     page_indices=torch.tensor([0, 1, 2], dtype=torch.int32))
+    else:
+        k = torch.zeros(cap, 2, 64, dtype=torch.bfloat16)
+        extra = {}
+    return q, k, k.clone(), torch.tensor([L], dtype=torch.int32), extra
+
+
+@pytest.mark.parametrize("bad", ["out_shape", "out_dtype", "lse_shape", "lse_dtype", "kv_len_past_cache"])
+def test_binding_rejects_unsafe_buffers(bad):
+    import torch
+
+    q, k, v, kv_len, extra = _torch_case(L=41 if bad == "kv_len_past_cache" else 40)
+    kw = {}
+    if bad == "out_shape":
+        kw["out"] = torch.empty(1, 8, 32, dtype=torch.bfloat16)
+    elif bad == "out_dtype":
+        kw["out"] = torch.empty(1, 8, 64, dtype=torch.float32)
+    elif bad == "lse_shape":
+        kw["lse"] = torch.empty(1, 4, dtype=torch.float32)
+    elif bad == "lse_dtype":
+        kw["lse"] = torch.empty(1, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out must|lse must|exceeds the rows"):
+        kvs.make_args(q, k, v, kv_len, kv_len_host=[int(kv_len[0])], **kw, **extra)
+
+
+def test_binding_passes_contiguous_capacity():
+    """A well-formed case gets past every shape check (it then stops at the
+    device check, since these tensors are on the CPU)."""
+    q, k, v, kv_len, extra = _torch_case(L=40, cap=64)
+    with pytest.raises(ValueError, match="must be on"):
+        kvs.make_args(q, k, v, kv_len, kv_len_host=[40])
+

@@ -280,3 +280,213 @@ def test_planted_position_error_is_caught(monkeypatch):
     monkeypatch.setattr(A, "transform_head", lambda x, pos, *r: good(x, pos + 1, *r))
     with pytest.raises(AssertionError):
         test_append_position_is_kv_len()
+
+
+# ------------------------------------------------------------------ INT4 encoder
+
+def _int4_by_bits(codes):
+    """Independent INT4 decode: the byte's bits (numpy's unpackbits, least
+    significant first) weighted 1, 2, 4, -8 (two's complement), low nibble
+    first."""
+    bits = np.unpackbits(np.asarray(codes, np.uint8)[..., None], axis=-1, bitorder="little").astype(np.int64)
+    w = np.array([1, 2, 4, -8])
+    return np.stack([bits[..., :4] @ w, bits[..., 4:] @ w], -1).reshape(np.shape(codes)[:-1] + (-1,))
+
+
+def test_int4_encoder_every_code_in_both_nibbles():
+    v = np.arange(-8, 8, dtype=np.float64)
+    pairs = np.stack(np.meshgrid(v, v, indexing="ij"), -1).reshape(256, 2)  # (element 2i, element 2i + 1)
+    codes = C.f64_to_int4_codes(pairs)
+    assert codes.shape == (256, 1)
+    assert sorted(codes[:, 0].tolist()) == list(range(256))  # every byte once
+    np.testing.assert_array_equal(_int4_by_bits(codes), pairs)
+    np.testing.assert_array_equal(C.int4_to_f64(codes), pairs)
+
+
+def test_int4_encoder_ties_and_saturation():
+    k = np.arange(-8, 7)
+    ties = k + 0.5
+    want = np.where(k % 2 == 0, k, k + 1)  # the even neighbour
+    got = C.int4_to_f64(C.f64_to_int4_codes(np.repeat(ties, 2)))[0::2]
+    np.testing.assert_array_equal(got, want)
+    below = C.int4_to_f64(C.f64_to_int4_codes(np.repeat(np.nextafter(ties, -np.inf), 2)))[0::2]
+    above = C.int4_to_f64(C.f64_to_int4_codes(np.repeat(np.nextafter(ties, np.inf), 2)))[0::2]
+    np.testing.assert_array_equal(below, k)
+    np.testing.assert_array_equal(above, k + 1)
+    sat = np.array([7.49, 7.5, 8.0, 100.0, -8.49, -8.5, -9.0, -1e9, np.nan, -0.0])
+    np.testing.assert_array_equal(C.int4_to_f64(C.f64_to_int4_codes(sat)), [7, 7, 7, 7, -8, -8, -8, -8, 0, 0])
+
+
+def test_int4_encoder_is_the_nearest_code():
+    """Brute force over the 16 values: the nearest, ties to the even one."""
+    x = np.random.default_rng(4).uniform(-11, 11, 4000)
+    x[:200] = np.round(x[:200] * 2) / 2  # plenty of exact ties
+    vals = np.arange(-8, 8, dtype=np.float64)
+    dist = np.abs(x[:, None] - vals[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = np.where(dist == best, vals[None, :], np.nan)
+    even = np.where(np.nanmax(np.where(np.abs(cand) % 2 == 0, cand, np.nan), axis=1, initial=-99) > -99,
+                    np.nanmax(np.where(np.abs(cand) % 2 == 0, cand, np.nan), axis=1, initial=-99),
+                    np.nanmax(cand, axis=1))
+    np.testing.assert_array_equal(_int4_by_bits(C.f64_to_int4_codes(x)), even)
+
+
+# ------------------------------------------------------------------ ragged rows (several new tokens per request)
+
+def _unit_queries(ai, d):
+    """Every new q row = e_0 (exactly 1.0 at dimension 0), in q's codes."""
+    q = np.zeros(np.shape(ai.q_new)[:-1] + (d,), np.float32)
+    q[..., 0] = 1.0
+    return torch.from_numpy(q).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_ragged_rows_take_consecutive_positions():
+    """q = e_0 with no norm: the first rotation pair turns by the position
+    itself (theta^0 = 1), so q_out[0] = cos(p) and q_out[d/2] = sin(p) give
+    every row's position in closed form: kv_len[b] + i for row i."""
+    import dataclasses
+
+    spec = small_variant("c4_paged_bf16_b64", batch=4, lengths=("list", [15, 0, 40, 7]))
+    rows = [3, 2, 0, 5]
+    ai = make_append_inputs(spec, seed=12, norm=False, theta=1e4, rows=rows)
+    ai = dataclasses.replace(ai, q_new=_unit_queries(ai, 128))
+    ref = A.append_reference(ai)
+    r = 0
+    for b, n in enumerate(rows):
+        for i in range(n):
+            p = int(ai.cache.kv_len[b]) + i
+            assert ref["q_out"][r, 0, 0] == pytest.approx(math.cos(p), abs=1e-12)
+            assert ref["q_out"][r, 0, 64] == pytest.approx(math.sin(p), abs=1e-12)
+            assert ref["pos"][r] == p and ref["req"][r] == b
+            r += 1
+    assert r == len(ref["pos"])
+
+
+def test_one_row_per_request_equals_the_single_token_step():
+    spec = small_variant("c5_paged_fp8_b128", batch=3, lengths=("list", [5, 300, 17]))
+    one = make_append_inputs(spec, seed=2, theta=1e4)
+    rag = make_append_inputs(spec, seed=2, theta=1e4, rows=[1, 1, 1])
+    a, b = A.append_reference(one), A.append_reference(rag)
+    for key in ("q_out", "k", "v", "pos"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_ragged_append_equals_successive_single_token_steps():
+    """n rows of one request appended at once = n one-token steps, each at
+    the length the previous step left (the one-token reading, pinned above)."""
+    import dataclasses
+
+    spec = small_variant("c4_paged_bf16_b64", batch=1, lengths=("list", [14]))
+    n = 5
+    rag = make_append_inputs(spec, seed=4, theta=1e4, rows=[n])
+    ref = A.append_reference(rag)
+    codes = A.append_codes(ref, "bf16", "bf16")
+    k_all, v_all, kv_all = A.apply_append(rag, codes)
+    assert kv_all[0] == 14 + n
+    cache = rag.cache
+    for i in range(n):
+        step = dataclasses.replace(rag, q_new=rag.q_new[i:i + 1], k_new=rag.k_new[i:i + 1],
+                                   v_new=rag.v_new[i:i + 1], qo_indptr=None, cache=cache)
+        r1 = A.append_reference(step)
+        np.testing.assert_array_equal(r1["q_out"][0], ref["q_out"][i])
+        c1 = A.append_codes(r1, "bf16", "bf16")
+        kp, vp, kl = A.apply_append(step, c1)
+        cache = dataclasses.replace(cache, k=kp, v=vp, kv_len=kl)
+    np.testing.assert_array_equal(cache.k, k_all)
+    np.testing.assert_array_equal(cache.v, v_all)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
+def test_ragged_append_then_attend(kv):
+    """Append a ragged batch, then attend with the same rows as queries:
+    equals causal attention over the old logical K/V followed by the new
+    rows' decoded codes, computed directly; only the new slots change."""
+    name = {"bf16": "c4_paged_bf16_b64", "fp8": "c5_paged_fp8_b128", "int4": "c6_paged_int4_b128"}[kv]
+    spec = small_variant(name, batch=3, lengths=("list", [0, 31, 50]))
+    rows = [4, 0, 17]
+    ai = make_append_inputs(spec, seed=7, theta=1e4, rows=rows, poison=True)
+    ref = A.append_reference(ai)
+    codes = A.append_codes(ref, "bf16", kv)
+    k_pool, v_pool, kv_len = A.apply_append(ai, codes)
+    np.testing.assert_array_equal(kv_len, np.asarray(ai.cache.kv_len) + rows)
+    ci = ai.cache
+    changed = np.argwhere(np.any(k_pool != ci.k, axis=(2, 3)) | np.any(v_pool != ci.v, axis=(2, 3)))
+    want = {A.cache_slot(b, p, 16, ci.page_indptr, ci.page_indices) for _, b, p in A.token_rows(ai)}
+    assert {(int(a), int(c)) for a, c in changed} <= want
+    import dataclasses
+
+    after = dataclasses.replace(ci, q=codes["q_out"], k=k_pool, v=v_pool, kv_len=kv_len, qo_indptr=ai.qo_indptr)
+    o, lse = oracle.attention_reference(after)
+    s = spec
+    g = s.num_qo_heads // s.num_kv_heads
+    f = dict(k=ci.k, v=ci.v, kv_len=ci.kv_len, kv_dtype=kv, page_size=16, page_indptr=ci.page_indptr,
+             page_indices=ci.page_indices, k_scale=ci.k_scale, v_scale=ci.v_scale)
+    Q = C.decode_codes(codes["q_out"], "bf16").reshape(-1, s.num_qo_heads, s.head_dim)
+    for r, b, p in A.token_rows(ai):
+        K, V = oracle.request_kv(b, **f)  # the old tokens
+        first = int(ai.qo_indptr[b])
+        kn = C.decode_codes(codes["k"][first:r + 1], kv)
+        vn = C.decode_codes(codes["v"][first:r + 1], kv)
+        if kv != "bf16":
+            kn, vn = kn * ci.k_scale[b][:, None], vn * ci.v_scale[b][:, None]
+        K, V = np.concatenate([K, kn]), np.concatenate([V, vn])
+        assert K.shape[0] == p + 1
+        for h in range(s.num_qo_heads):
+            o2, l2 = oracle.attend_direct(Q[r, h], K[:, h // g], V[:, h // g], s.sm_scale)
+            assert np.allclose(o[r, h], o2, rtol=0, atol=1e-12) and abs(lse[r, h] - l2) < 1e-12
+
+
+def test_int4_append_quantises_with_the_existing_scale():
+    spec = small_variant("c6_paged_int4_b128", batch=2, lengths=("list", [300, 40]))
+    ai = make_append_inputs(spec, seed=8, theta=1e4, rows=[2, 3])
+    ref = A.append_reference(ai)
+    codes = A.append_codes(ref, "bf16", "int4")
+    for r, b, _ in A.token_rows(ai):
+        x = ref["k"][r] * ai.cache.k_scale[b][:, None]  # undo the division
+        dq = C.int4_to_f64(codes["k"][r]) * ai.cache.k_scale[b][:, None]
+        sat = (x > 7.5 * ai.cache.k_scale[b][:, None]) | (x < -8.5 * ai.cache.k_scale[b][:, None])
+        assert np.all((np.abs(dq - x) <= 0.5 * ai.cache.k_scale[b][:, None] * (1 + 1e-12)) | sat)
+
+
+def test_planted_reversed_rows_are_caught(monkeypatch):
+    good = A.token_rows
+
+    def reversed_rows(ai):
+        out = good(ai)
+        by_req = {}
+        for r, b, p in out:
+            by_req.setdefault(b, []).append(p)
+        return [(r, b, by_req[b][len(by_req[b]) - 1 - [x[0] for x in out if x[1] == b].index(r)]) for r, b, p in out]
+
+    monkeypatch.setattr(A, "token_rows", reversed_rows)
+    with pytest.raises(AssertionError):
+        test_ragged_rows_take_consecutive_positions()
+
+
+def test_planted_row_position_off_by_one_is_caught(monkeypatch):
+    good = A.token_rows
+    monkeypatch.setattr(A, "token_rows", lambda ai: [(r, b, p + 1) for r, b, p in good(ai)])
+    with pytest.raises(AssertionError):
+        test_ragged_rows_take_consecutive_positions()
+
+
+def test_planted_int4_nibble_order_is_caught(monkeypatch):
+    good = C.f64_to_int4_codes
+
+    def swapped(x):
+        c = good(x)
+        return ((c >> 4) | (c << 4)).astype(np.uint8)
+
+    monkeypatch.setattr(C, "f64_to_int4_codes", swapped)
+    with pytest.raises(AssertionError):
+        test_int4_encoder_every_code_in_both_nibbles()
+
+
+def test_planted_int4_half_up_rounding_is_caught(monkeypatch):
+    def half_up(x):
+        k = np.clip(np.floor(np.asarray(x, np.float64) + 0.5), -8, 7).astype(np.int64) & 0xF
+        return (k[..., 0::2] | (k[..., 1::2] << 4)).astype(np.uint8)
+
+    monkeypatch.setattr(C, "f64_to_int4_codes", half_up)
+    with pytest.raises(AssertionError):
+        test_int4_encoder_ties_and_saturation()

@@ -1,9 +1,15 @@
 """INT4 KV cache (packed two's-complement nibbles, per-(request, KV head)
 scale) on the matrix-core kernel against the fp64 oracle on the GPU.
 
-Tolerance: max |o - o_ref| <= 6e-2 as for the other quantised KV type (fp8);
-the oracle decodes the same codes and scales, so the error is the kernel's
-arithmetic alone (bf16 weights and V operands, fp32 accumulation)."""
+Tolerance: max |o - o_ref| <= 2e-2, the bf16 gate.  The oracle decodes the
+same codes and scales, so quantisation error is not part of the comparison;
+what remains is the kernel's arithmetic, which is the bf16 path's: the
+operands 136 + n are exact in bf16 (integers below 256), q is bf16, the
+weights are rounded to bf16 before the P.V product and everything is
+accumulated in fp32; the offsets 136 * sum(q) and 136 * sum(p) are removed
+in fp32 from sums of at most a few thousand terms.  |V| <= 8/7 * amax, the
+range of the bf16 workloads' N(0, 1) values.  The whole batch-128 INT4
+workload is compared in tests/test_gpu_fullsize.py."""
 import dataclasses
 
 import numpy as np
@@ -68,19 +74,3 @@ def test_int4_unified_max(phi):
     print(f"case int4 unified max {phi}", flush=True)
     spec = small_variant("c6_paged_int4_b128", batch=3, lengths=("list", [5, 900, 128]))
     _check(make_inputs(spec, poison=True), unified_max=phi)
-
-
-def test_int4_full_batch_sampled():
-    """The full batch-128 INT4 workload in the launch configuration the
-    benchmark times; 24 (request, head) pairs against the oracle."""
-    print("case int4 full sampled", flush=True)
-    inp = make_inputs(CONFIGS["c6_paged_int4_b128"])
-    o, lse = run_library(inp)
-    rng = np.random.default_rng(0)
-    B, Hq = inp.spec.batch, inp.spec.num_qo_heads
-    L = inp.kv_len
-    picks = [(int(np.argmax(L)), 0), (int(np.argmin(L)), Hq - 1)]
-    picks += [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 22), rng.integers(0, Hq, 22))]
-    ref = oracle.decode_reference_sampled(inp, picks)
-    for (b, h), (o_r, l_r) in zip(picks, ref):
-        compare(o[b, h][None], lse[b, h][None], o_r[None], np.array([l_r]), "int4")

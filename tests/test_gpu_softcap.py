@@ -95,10 +95,11 @@ def test_unified_max(umax):
     _check(make_inputs(spec, poison=True), unified_max=umax)
 
 
-def test_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_full_size():
     print("case softcap full c4", flush=True)
     inp = make_inputs(_capped(CONFIGS["c4_paged_bf16_b64"], 50.0))
     o, lse = run_library(inp)
-    reqs = [0, 7, int(np.argmax(inp.kv_len)), 63]
-    o_ref, lse_ref = oracle.decode_reference(inp, requests=reqs)
-    compare(o[reqs], lse[reqs], o_ref[reqs], lse_ref[reqs], "bf16")
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    err, rel = compare(o, lse, o_ref, lse_ref, "bf16")
+    print(f"PARITY c4 soft cap 50 full: max|o-o_ref|={err:.3e} lse_rel={rel:.3e}", flush=True)

@@ -480,3 +480,66 @@ def test_planted_transposed_operand_is_caught(monkeypatch):
 
     monkeypatch.setattr(od, "softmax_from_scores", wrong)
     assert _fails(test_golden_worked_examples, _golden_cases()[0])
+
+
+# ----------------------------------------------------------------------------
+# decode_reference_sampled: the per-(request, head) helper of the full-size
+# GPU checks, pinned against the whole-batch oracle on interleaved picks
+# ----------------------------------------------------------------------------
+
+def _sampled_agrees(fn, kv):
+    """fn(inp, picks) must reproduce decode_reference bit for bit on a pick
+    list that revisits requests out of order (a stale per-request cache
+    would show) and covers every query head of two KV heads (a wrong head
+    map would show), on a paged GQA cache with a window."""
+    int4 = kv == "int4"
+    spec = DecodeSpec("s", 4, 8, 2, 128 if int4 else 32, 16, kv, "bf16", 0.2, window=50,
+                      lengths=("list", [90, 0, 33, 200]), seed=31)
+    inp = make_inputs(spec, poison=True)
+    o_ref, l_ref = oracle.decode_reference(inp)
+    picks = [(3, 0), (0, 7), (3, 5), (2, 1), (0, 0), (3, 7), (1, 3), (2, 6), (0, 4), (3, 2)]
+    got = fn(inp, picks)
+    assert len(got) == len(picks)
+    for (b, h), (o, lse) in zip(picks, got):
+        np.testing.assert_array_equal(o, o_ref[b, h])
+        assert (lse == l_ref[b, h]) or (math.isinf(lse) and math.isinf(l_ref[b, h]))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int4"])
+def test_sampled_reference_matches_whole_batch(kv):
+    _sampled_agrees(oracle.decode_reference_sampled, kv)
+
+
+def test_planted_stale_request_cache_in_sampled_is_caught():
+    def stale(inp, picks):  # keeps the first request's K/V for every later pick
+        s = inp.spec
+        g = s.num_qo_heads // s.num_kv_heads
+        Q = oracle.decode_codes(inp.q, s.q_dtype).reshape(s.batch, s.num_qo_heads, s.head_dim)
+        f = od._fields(inp)
+        kv_cache = None
+        out = []
+        for b, h in picks:
+            if kv_cache is None:
+                lo, hi = od.visible_range(int(inp.kv_len[b]), s.window)
+                kv_cache = od.request_kv(b, tokens=(lo, hi), **f)
+            K, V = kv_cache
+            out.append(od.attend_direct(Q[b, h], K[:, h // g], V[:, h // g], s.sm_scale, s.soft_cap))
+        return out
+
+    assert _fails(_sampled_agrees, stale, "bf16")
+
+
+def test_planted_head_map_in_sampled_is_caught():
+    def wrong_head(inp, picks):  # KV head h % Hk instead of h // g
+        s = inp.spec
+        Q = oracle.decode_codes(inp.q, s.q_dtype).reshape(s.batch, s.num_qo_heads, s.head_dim)
+        f = od._fields(inp)
+        out = []
+        for b, h in picks:
+            lo, hi = od.visible_range(int(inp.kv_len[b]), s.window)
+            K, V = od.request_kv(b, tokens=(lo, hi), **f)
+            kh = h % s.num_kv_heads
+            out.append(od.attend_direct(Q[b, h], K[:, kh], V[:, kh], s.sm_scale, s.soft_cap))
+        return out
+
+    assert _fails(_sampled_agrees, wrong_head, "bf16")

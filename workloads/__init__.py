@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -355,39 +355,55 @@ def small_variant(name: str, *, batch: Optional[int] = None, lengths: Optional[t
 
 @dataclasses.dataclass
 class AppendInputs:
-    """One decode step's new token for every request, and the cache it joins.
+    """One step's new tokens for every request, and the cache they join.
 
-    ``cache`` is a DecodeInputs whose requests each have room for one more
-    token; the new token goes to position kv_len[b].
+    ``cache`` is a DecodeInputs whose requests each have room for the new
+    tokens.  Without ``qo_indptr`` each request gets one new token, at
+    position kv_len[b]; with it, rows qo_indptr[b] .. qo_indptr[b+1] - 1 are
+    request b's, row i at position kv_len[b] + i.
     """
     cache: DecodeInputs
-    q_new: np.ndarray   # [B, Hq, d] codes of q's type
-    k_new: np.ndarray   # [B, Hk, d] codes of q's type
-    v_new: np.ndarray   # [B, Hk, d] codes of q's type
+    q_new: np.ndarray   # [T, Hq, d] codes of q's type (T = rows; B without qo_indptr)
+    k_new: np.ndarray   # [T, Hk, d] codes of q's type
+    v_new: np.ndarray   # [T, Hk, d] codes of q's type
     q_norm_weight: Optional[np.ndarray]  # float32 [d] or None (no QK-norm)
     k_norm_weight: Optional[np.ndarray]
     eps: float
     theta: float        # 0: no rotary embedding
     interleave: bool
+    qo_indptr: Optional[np.ndarray] = None  # int32 [B + 1]: new token rows of each request
 
 
 def make_append_inputs(spec: DecodeSpec, seed: Optional[int] = None, *, norm: bool = True,
                        theta: float = 10000.0, interleave: bool = False, eps: float = 1e-6,
-                       poison: bool = False, lengths: Optional[np.ndarray] = None) -> AppendInputs:
-    """Draw a cache like make_inputs (with one reserved slot per request) and
-    the new token: q, k, v ~ N(0, 1) in q's storage type; QK-norm weights
-    ~ N(1, 0.25) per dimension when ``norm``."""
+                       poison: bool = False, lengths: Optional[np.ndarray] = None,
+                       rows: Optional[Sequence[int]] = None) -> AppendInputs:
+    """Draw a cache like make_inputs and the new tokens: q, k, v ~ N(0, 1) in
+    q's storage type; QK-norm weights ~ N(1, 0.25) per dimension when
+    ``norm``.  ``rows`` (one count per request, >= 0) asks for that many new
+    tokens per request (a packed ragged batch, qo_indptr); without it every
+    request gets one.  Each request's cache has room for its new tokens (the
+    most rows of any request are reserved after every cache), filled like
+    padding."""
     seed = spec.seed if seed is None else seed
-    cache = make_inputs(spec, seed, poison=poison, lengths=lengths, reserve_tokens=1)
+    B, Hq, Hk, d = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    qo_indptr = None
+    if rows is not None:
+        rows = np.asarray(rows, np.int64)
+        if rows.shape != (B,) or np.any(rows < 0):
+            raise ValueError("rows must hold one count >= 0 per request")
+        qo_indptr = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    T = B if qo_indptr is None else int(qo_indptr[-1])
+    reserve = 1 if rows is None else max(1, int(rows.max(initial=0)))
+    cache = make_inputs(spec, seed, poison=poison, lengths=lengths, reserve_tokens=reserve)
     r_q, r_k, r_v, r_w = [np.random.Generator(np.random.PCG64(s))
                           for s in np.random.SeedSequence([seed, 0xA11]).spawn(4)]
-    B, Hq, Hk, d = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
-    q = r_q.standard_normal((B, Hq, d), dtype=np.float32)
-    k = r_k.standard_normal((B, Hk, d), dtype=np.float32)
-    v = r_v.standard_normal((B, Hk, d), dtype=np.float32)
+    q = r_q.standard_normal((T, Hq, d), dtype=np.float32)
+    k = r_k.standard_normal((T, Hk, d), dtype=np.float32)
+    v = r_v.standard_normal((T, Hk, d), dtype=np.float32)
     wq = wk = None
     if norm:
         wq = (1.0 + 0.25 * r_w.standard_normal(d)).astype(np.float32)
         wk = (1.0 + 0.25 * r_w.standard_normal(d)).astype(np.float32)
     return AppendInputs(cache, _store(q, spec.q_dtype), _store(k, spec.q_dtype), _store(v, spec.q_dtype),
-                        wq, wk, float(eps), float(theta), bool(interleave))
+                        wq, wk, float(eps), float(theta), bool(interleave), qo_indptr)
