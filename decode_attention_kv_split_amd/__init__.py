@@ -15,7 +15,7 @@ High level, on torch tensors already on the GPU:
     decode(...)              any layout, returns (o, lse)
     single_decode(q, k, v)   one request, contiguous cache
     batch_decode_paged(...)  paged cache
-    append(...)              QK-norm, rotary embedding and KV append of the new token
+    append(...)              QK-norm, rotary embedding and KV append of the new tokens
 """
 from __future__ import annotations
 
@@ -37,7 +37,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 8
+KVS_ABI_VERSION = 9
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
@@ -127,6 +127,8 @@ class KvsAppendArgs(ctypes.Structure):
         ("rope_theta", ctypes.c_float),
         ("rope_interleave", ctypes.c_int32),
         ("prof_events", ctypes.c_void_p * 2),
+        ("qo_indptr", ctypes.c_void_p),
+        ("qo_indptr_host", ctypes.c_void_p),
     ]
 
 
@@ -425,44 +427,66 @@ def batch_decode_paged(q, k_pages, v_pages, page_indptr, page_indices, kv_len, *
 def make_append_args(q, k, v, k_cache, v_cache, kv_len, *, page_indptr=None, page_indices=None,
                      k_scale=None, v_scale=None, q_norm_weight=None, k_norm_weight=None,
                      norm_eps: float = 1e-6, rope_theta: float = 10000.0, rope_interleave: bool = False,
-                     q_out=None) -> Tuple[KvsAppendArgs, object]:
+                     q_out=None, qo_indptr=None, qo_indptr_host=None,
+                     kv_dtype: Optional[str] = None) -> Tuple[KvsAppendArgs, object]:
     """Build the C argument block of kvs_append from torch tensors.
 
-    q [batch, Hq, d], k and v [batch, Hk, d] (q's dtype); the cache as for
+    q [rows, Hq, d], k and v [rows, Hk, d] (q's dtype), rows = batch (one new
+    token per request) or qo_indptr[batch] (qo_indptr: int32 [batch + 1] on
+    the device, with a host copy; request b's rows are qo_indptr[b] ..
+    qo_indptr[b+1] - 1, row i at position kv_len[b] + i).  The cache as for
     decode (paged [num_pages, page_size, Hk, d] or contiguous
-    [capacity, Hk, d]); kv_len int32 [batch] on the device (the new token's
-    position).  q_out defaults to a new tensor; it may be q."""
+    [capacity, Hk, d]; kv_dtype='int4' marks uint8 caches of d / 2 packed
+    bytes per row); kv_len int32 [batch] on the device (tokens cached
+    before the call).  q_out defaults to a new tensor; it may be q."""
+    import numpy as np
     import torch
 
     device = q.device
-    B, Hq, d = q.shape
+    rows, Hq, d = q.shape
+    B = int(kv_len.numel())
     Hk = k.shape[1]
-    if k.shape != (B, Hk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k and v must be [batch, num_kv_heads, head_dim] in q's dtype")
+    if k.shape != (rows, Hk, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [rows, num_kv_heads, head_dim] in q's dtype")
+    qoh = None
+    if qo_indptr is not None:
+        src = qo_indptr_host if qo_indptr_host is not None else qo_indptr.cpu()
+        qoh = np.ascontiguousarray(np.asarray(src.cpu() if isinstance(src, torch.Tensor) else src, dtype=np.int32))
+        if qoh.shape != (B + 1,) or int(qoh[-1]) != rows or int(qoh[0]) != 0 or np.any(np.diff(qoh) < 0):
+            raise ValueError("qo_indptr must be [batch + 1], non-decreasing from 0 to q's row count")
+        if qo_indptr.dtype != torch.int32 or qo_indptr.numel() != B + 1:
+            raise ValueError("qo_indptr must be int32 [batch + 1]")
+    elif rows != B:
+        raise ValueError("q must have one row per request without qo_indptr")
     paged = page_indptr is not None
     if paged:
         num_pages, P, Hk2, d2 = k_cache.shape
     else:
         num_pages, Hk2, d2 = k_cache.shape
         P = 0
-    if (Hk2, d2) != (Hk, d) or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("cache shape does not match the new token")
+    int4 = kv_dtype == "int4"
+    if int4 and k_cache.dtype != torch.uint8:
+        raise ValueError("an int4 cache is uint8 with head_dim / 2 bytes per row")
+    if (Hk2, d2) != (Hk, d // 2 if int4 else d) or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("cache shape does not match the new tokens")
     if kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("kv_len must be int32 [batch]")
     if q_out is None:
         q_out = torch.empty_like(q)
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_len, "kv_len"),
-                 (page_indptr, "page_indptr"), (page_indices, "page_indices"), (k_scale, "k_scale"),
-                 (v_scale, "v_scale"), (q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight"),
-                 (q_out, "q_out")):
-        _check_dev(t, n, device)
+    elif q_out.shape != q.shape or q_out.dtype != q.dtype:
+        raise ValueError("q_out must have q's shape and dtype")
     for w, n in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
         if w is not None and (w.dtype != torch.float32 or w.numel() != d):
             raise ValueError(f"{n} must be float32 [head_dim]")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_len, "kv_len"),
+                 (page_indptr, "page_indptr"), (page_indices, "page_indices"), (k_scale, "k_scale"),
+                 (v_scale, "v_scale"), (q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight"),
+                 (q_out, "q_out"), (qo_indptr, "qo_indptr")):
+        _check_dev(t, n, device)
     a = KvsAppendArgs()
     a.batch, a.num_qo_heads, a.num_kv_heads, a.head_dim = B, Hq, Hk, d
     a.q_dtype = _dtype_code(q, "q")
-    a.kv_dtype = _dtype_code(k_cache, "kv")
+    a.kv_dtype = _dtype_code(k_cache, "kv", kv_dtype)
     a.page_size, a.num_pages = P, num_pages
     a.q_in, a.k_in, a.v_in, a.q_out = _ptr(q), _ptr(k), _ptr(v), _ptr(q_out)
     a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
@@ -473,21 +497,26 @@ def make_append_args(q, k, v, k_cache, v_cache, kv_len, *, page_indptr=None, pag
     a.norm_eps = float(norm_eps)
     a.rope_theta = float(rope_theta)
     a.rope_interleave = int(bool(rope_interleave))
-    return a, (q_out,)
+    if qoh is not None:
+        a.qo_indptr, a.qo_indptr_host = _ptr(qo_indptr), qoh.ctypes.data
+    return a, (q_out, qoh)
 
 
 def append(q, k, v, k_cache, v_cache, kv_len, *, page_indptr=None, page_indices=None, k_scale=None,
            v_scale=None, q_norm_weight=None, k_norm_weight=None, norm_eps: float = 1e-6,
-           rope_theta: float = 10000.0, rope_interleave: bool = False, q_out=None, stream=None):
-    """QK-norm and rotary embedding of the new token, and its K/V stored at
-    position kv_len[b] of each request's cache.  Returns q_out.  kv_len is
-    not changed."""
+           rope_theta: float = 10000.0, rope_interleave: bool = False, q_out=None, stream=None,
+           qo_indptr=None, qo_indptr_host=None, kv_dtype: Optional[str] = None):
+    """QK-norm and rotary embedding of the new tokens, and their K/V stored
+    after each request's cached tokens (one per request at kv_len[b], or the
+    rows of qo_indptr at kv_len[b] + i).  Returns q_out.  kv_len is not
+    changed."""
     import torch
 
     a, keep = make_append_args(q, k, v, k_cache, v_cache, kv_len, page_indptr=page_indptr,
                                page_indices=page_indices, k_scale=k_scale, v_scale=v_scale,
                                q_norm_weight=q_norm_weight, k_norm_weight=k_norm_weight, norm_eps=norm_eps,
-                               rope_theta=rope_theta, rope_interleave=rope_interleave, q_out=q_out)
+                               rope_theta=rope_theta, rope_interleave=rope_interleave, q_out=q_out,
+                               qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host, kv_dtype=kv_dtype)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     st = kvs_append(a, s)
     if st != KVS_OK:

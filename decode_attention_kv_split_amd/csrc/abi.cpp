@@ -131,20 +131,33 @@ kvs_status validate_append(const kvs_append_args *a) {
   if (a->q_dtype < 0 || a->q_dtype > 2 || a->kv_dtype < 0 || a->kv_dtype > 3) return KVS_ERR_INVALID_ARG;
   const bool pair_ok = (a->q_dtype == KVS_F32 && a->kv_dtype == KVS_F32) ||
                        (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_BF16) ||
-                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3);
-  if (!pair_ok) return KVS_ERR_UNSUPPORTED; // INT4 caches are not written by this step
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_FP8_E4M3) ||
+                       (a->q_dtype == KVS_BF16 && a->kv_dtype == KVS_INT4);
+  if (!pair_ok) return KVS_ERR_UNSUPPORTED;
+  // INT4 caches exist at the head sizes the decode kernels read
+  if (a->kv_dtype == KVS_INT4 && a->head_dim != 128 && a->head_dim != 256) return KVS_ERR_UNSUPPORTED;
+  const bool scaled = a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4;
   if (a->page_size < 0 || a->num_pages < 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size == 0 && a->batch != 1) return KVS_ERR_INVALID_ARG;
   if (a->page_size > 0 && !is_pow2(a->page_size)) return KVS_ERR_UNSUPPORTED;
   if (!(a->norm_eps >= 0.0f) || !std::isfinite(a->norm_eps)) return KVS_ERR_INVALID_ARG;
   if (!(a->rope_theta >= 0.0f) || !std::isfinite(a->rope_theta)) return KVS_ERR_INVALID_ARG;
   if (a->rope_interleave != 0 && a->rope_interleave != 1) return KVS_ERR_INVALID_ARG;
-  if ((int64_t)a->batch * (a->num_qo_heads + a->num_kv_heads) > ((int64_t)1 << 32) / kvs::kThreads * kvs::kWaves)
+  // token rows: one per request, or a packed ragged batch
+  if ((a->qo_indptr == nullptr) != (a->qo_indptr_host == nullptr)) return KVS_ERR_INVALID_ARG;
+  int64_t rows = a->batch;
+  if (a->qo_indptr_host) {
+    if (a->qo_indptr_host[0] != 0) return KVS_ERR_INVALID_ARG;
+    for (int b = 0; b < a->batch; ++b)
+      if (a->qo_indptr_host[b + 1] < a->qo_indptr_host[b]) return KVS_ERR_INVALID_ARG;
+    rows = a->qo_indptr_host[a->batch];
+  }
+  if (rows * (a->num_qo_heads + a->num_kv_heads) > ((int64_t)1 << 32) / kvs::kThreads * kvs::kWaves)
     return KVS_ERR_UNSUPPORTED; // one launch holds fewer than 2^32 work-items
   if (!a->q_in || !a->k_in || !a->v_in || !a->q_out || !a->k_cache || !a->v_cache || !a->kv_len)
     return KVS_ERR_INVALID_ARG;
   if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
-  if (a->kv_dtype == KVS_FP8_E4M3 && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
+  if (scaled && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
   return KVS_OK;
 }
 

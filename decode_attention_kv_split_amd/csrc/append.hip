@@ -1,6 +1,9 @@
-// The step before decode attention, for the one new token of every request:
+// The step before decode attention, for the new tokens of every request:
 // QK-norm, rotary embedding, and the append of the new key and value to the
-// cache at position p = kv_len[b].
+// cache.  One new token per request goes to position p = kv_len[b]; with a
+// packed ragged batch of token rows (qo_indptr), row i of request b goes to
+// position kv_len[b] + i and is rotated there (the three-kernels section of
+// the FlashInfer-from-JAX page: apply_rope over a packed batch).
 //
 //   QK-norm: an RMSNorm over each head's q and k before their dot product
 //     (FlashInfer-from-JAX tutorial page, Gemma 3 section): x / sqrt(mean(x^2)
@@ -10,14 +13,16 @@
 //     names apply_rope and its Gemma 3 section the per-layer theta, 10,000 for
 //     local and 1,000,000 for global layers).  Pairs (j, j + d/2), or
 //     (2j, 2j + 1) when interleaved.
-//   Append to the growing paged or contiguous cache, fp8 included ("Beyond the
-//     Memory Wall", section "2. FlashInfer"); an fp8 value is stored as the
-//     nearest code of x / scale[b, kv head], saturating at +-448.
+//   Append to the growing paged or contiguous cache, fp8 and INT4 included
+//     ("Beyond the Memory Wall", section "2. FlashInfer"); an fp8 value is
+//     stored as the nearest code of x / scale[b, kv head], saturating at
+//     +-448, an INT4 value as the nearest integer to it (ties to even),
+//     saturating to [-8, 7], two per byte with element 2i in the low nibble.
 //
-// Head rows [0, Hq) of a request are its query heads (written to q_out), rows
+// Head rows [0, Hq) of a token are its query heads (written to q_out), rows
 // [Hq, Hq + Hk) its KV heads (k transformed like q, v copied; both stored).
-// A wave takes two consecutive rows of one request: they share the position,
-// so the rotation is computed once per wave.  Lane l holds E = d / 64 elements: indices l + 64 e (pairs
+// A wave takes two consecutive head rows of one token: they share the
+// position, so the rotation is computed once per wave.  Lane l holds E = d / 64 elements: indices l + 64 e (pairs
 // (j, j + d/2) then sit in one lane for d >= 128 and in lanes l, l ^ 32 for
 // d = 64), or E l + e when interleaved (pairs in one lane, or in lanes l, l ^ 1
 // for d = 64).  The angle is computed in double precision and reduced modulo
@@ -51,8 +56,33 @@ struct AppendParams {
   float rope_theta;
   int interleave;
   int q_f32;   // q_in, k_in, v_in, q_out are fp32 (else bf16)
-  int kv_type; // DT_F32, DT_BF16, DT_FP8
+  int kv_type; // DT_F32, DT_BF16, DT_FP8, DT_INT4
+  int n_tok;   // token rows: batch, or qo_indptr[batch]
+  const int *qo_indptr; // [batch + 1] token rows of each request; null: one each
 };
+
+// The host copy of qo_indptr, passed in the kernel arguments when the batch
+// fits, so that a wave finds its token's request without a dependent read.
+struct AppendRows {
+  int n;                            // entries below (batch + 1); 0: not provided
+  int indptr[kInlineRequests + 1];
+};
+
+// Request of token row r: the last b with indptr[b] <= r (an empty request's
+// indptr[b] equals the next one's, so the search lands on the request that
+// holds r).  r is the same in every lane of the wave.
+template <typename Ind>
+__device__ __forceinline__ int request_of_row(Ind indptr, int batch, int r) {
+  int lo = 0, hi = batch; // indptr[lo] <= r < indptr[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (indptr(mid) <= r)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -184,10 +214,35 @@ __device__ __forceinline__ void store_q(const AppendParams &p, size_t row, int l
   }
 }
 
+// INT4 code of x (already divided by its scale): nearest integer, ties to
+// even, saturated to [-8, 7]; NaN gives 0.  Returned as the low nibble.
+__device__ __forceinline__ uint32_t f32_to_int4_sat(float x) {
+  if (__builtin_isnan(x)) return 0u;
+  const float r = fminf(fmaxf(rintf(x), -8.0f), 7.0f);
+  return (uint32_t)(int)r & 0xFu;
+}
+
 template <int D>
 __device__ __forceinline__ void store_kv(const AppendParams &p, void *cache, size_t off, float scale, int lane,
                                          const float (&x)[D / 64]) {
   constexpr int E = D / 64;
+  if (p.kv_type == DT_INT4) {
+    // byte j of the row holds elements 2j (low nibble) and 2j + 1 (high)
+    uint8_t *row = reinterpret_cast<uint8_t *>(cache) + off / 2;
+    if (p.interleave && E >= 2) { // elements E lane + e: both of a pair in this lane
+#pragma unroll
+      for (int e = 0; e < E; e += 2)
+        row[(E * lane + e) / 2] = (uint8_t)(f32_to_int4_sat(x[e] / scale) | (f32_to_int4_sat(x[e + 1] / scale) << 4));
+    } else { // elements lane + 64 e (or lane for E = 1): the pair's other element is in lane ^ 1
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t c = f32_to_int4_sat(x[e] / scale);
+        const uint32_t other = (uint32_t)__shfl_xor((int)c, 1, 64);
+        if ((lane & 1) == 0) row[(elem_index<D>(lane, e, p.interleave)) / 2] = (uint8_t)(c | (other << 4));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = elem_index<D>(lane, e, p.interleave);
@@ -205,16 +260,26 @@ __device__ __forceinline__ void store_kv(const AppendParams &p, void *cache, siz
 constexpr int kRowsPerWave = 2;
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void append_kernel(const AppendParams p) {
+__global__ __launch_bounds__(kThreads) void append_kernel(const AppendParams p, const AppendRows inl) {
   constexpr int E = D / 64;
   const int lane = threadIdx.x & 63;
-  const int rows_per_req = p.num_qo_heads + p.num_kv_heads;
+  const int rows_per_req = p.num_qo_heads + p.num_kv_heads; // head rows of one token
   const int waves_per_req = (rows_per_req + kRowsPerWave - 1) / kRowsPerWave;
-  const int wid = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (wid >= p.batch * waves_per_req) return; // whole waves exit
-  const int b = wid / waves_per_req;
+  const int wid = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wid >= p.n_tok * waves_per_req) return; // whole waves exit
+  const int tr = wid / waves_per_req;  // token row (q_in / k_in / v_in / q_out row)
   const int h0 = (wid % waves_per_req) * kRowsPerWave;
-  const int pos = p.kv_len[b];
+  int b = tr, i = 0; // request and index of the token within it
+  if (p.qo_indptr) {
+    if (inl.n > 0) {
+      b = request_of_row([&](int x) { return inl.indptr[x]; }, p.batch, tr);
+      i = tr - inl.indptr[b];
+    } else {
+      b = request_of_row([&](int x) { return p.qo_indptr[x]; }, p.batch, tr);
+      i = tr - p.qo_indptr[b];
+    }
+  }
+  const int pos = p.kv_len[b] + i;
 
   // where the new token goes; a slot its page list does not cover is not written
   bool write_kv = true;
@@ -241,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const AppendParams p) 
     const int h = h0 + rr;
     if (h >= rows_per_req) break;
     if (h < p.num_qo_heads) {
-      load_row<D>(p, p.q_in, (size_t)b * p.num_qo_heads + h, lane, x[rr]);
+      load_row<D>(p, p.q_in, (size_t)tr * p.num_qo_heads + h, lane, x[rr]);
     } else {
-      const size_t r = (size_t)b * p.num_kv_heads + (h - p.num_qo_heads);
+      const size_t r = (size_t)tr * p.num_kv_heads + (h - p.num_qo_heads);
       load_row<D>(p, p.k_in, r, lane, x[rr]);
       load_row<D>(p, p.v_in, r, lane, v[rr]);
     }
@@ -258,16 +323,17 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const AppendParams p) 
     if (h < p.num_qo_heads) {
       if (p.q_norm_weight) rms_norm<D>(p, p.q_norm_weight, lane, x[rr]);
       if (p.rope_theta > 0.0f) rope<D>(p, rot, lane, x[rr]);
-      store_q<D>(p, (size_t)b * p.num_qo_heads + h, lane, x[rr]);
+      store_q<D>(p, (size_t)tr * p.num_qo_heads + h, lane, x[rr]);
     } else {
       const int kh = h - p.num_qo_heads;
       if (p.k_norm_weight) rms_norm<D>(p, p.k_norm_weight, lane, x[rr]);
       if (p.rope_theta > 0.0f) rope<D>(p, rot, lane, x[rr]);
       if (write_kv) {
-        const size_t r = (size_t)b * p.num_kv_heads + kh;
-        const size_t off = (tok * p.num_kv_heads + kh) * D;
-        store_kv<D>(p, p.k_cache, off, p.kv_type == DT_FP8 ? p.k_scale[r] : 1.0f, lane, x[rr]);
-        store_kv<D>(p, p.v_cache, off, p.kv_type == DT_FP8 ? p.v_scale[r] : 1.0f, lane, v[rr]);
+        const size_t r = (size_t)b * p.num_kv_heads + kh; // scales are per (request, KV head)
+        const size_t off = (tok * p.num_kv_heads + kh) * D; // in elements
+        const bool scaled = p.kv_type == DT_FP8 || p.kv_type == DT_INT4;
+        store_kv<D>(p, p.k_cache, off, scaled ? p.k_scale[r] : 1.0f, lane, x[rr]);
+        store_kv<D>(p, p.v_cache, off, scaled ? p.v_scale[r] : 1.0f, lane, v[rr]);
       }
     }
   }
@@ -304,13 +370,25 @@ hipError_t launch_append(const kvs_append_args *a, const Launch &l) {
   p.rope_theta = a->rope_theta;
   p.interleave = a->rope_interleave;
   p.q_f32 = a->q_dtype == KVS_F32;
-  p.kv_type = a->kv_dtype == KVS_F32 ? DT_F32 : (a->kv_dtype == KVS_BF16 ? DT_BF16 : DT_FP8);
-  const int64_t waves = (int64_t)a->batch * ((a->num_qo_heads + a->num_kv_heads + kRowsPerWave - 1) / kRowsPerWave);
+  p.kv_type = a->kv_dtype == KVS_F32 ? DT_F32
+              : a->kv_dtype == KVS_BF16 ? DT_BF16
+              : a->kv_dtype == KVS_FP8_E4M3 ? DT_FP8
+                                            : DT_INT4;
+  p.qo_indptr = a->qo_indptr_host ? a->qo_indptr : nullptr;
+  p.n_tok = a->qo_indptr_host ? a->qo_indptr_host[a->batch] : a->batch;
+  AppendRows inl;
+  inl.n = 0;
+  if (a->qo_indptr_host && a->batch <= kInlineRequests) {
+    for (int b = 0; b <= a->batch; ++b) inl.indptr[b] = a->qo_indptr_host[b];
+    inl.n = a->batch + 1;
+  }
+  if (p.n_tok == 0) return hipSuccess; // no new token anywhere
+  const int64_t waves = (int64_t)p.n_tok * ((a->num_qo_heads + a->num_kv_heads + kRowsPerWave - 1) / kRowsPerWave);
   const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
   switch (a->head_dim) {
-  case 64: return launch_kernel(l, append_kernel<64>, grid, p);
-  case 128: return launch_kernel(l, append_kernel<128>, grid, p);
-  case 256: return launch_kernel(l, append_kernel<256>, grid, p);
+  case 64: return launch_kernel(l, append_kernel<64>, grid, p, inl);
+  case 128: return launch_kernel(l, append_kernel<128>, grid, p, inl);
+  case 256: return launch_kernel(l, append_kernel<256>, grid, p, inl);
   default: return hipErrorInvalidValue;
   }
 }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 8
+#define KVS_ABI_VERSION 9
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -215,12 +215,15 @@ kvs_status kvs_decode(const kvs_decode_args *args, void *workspace, size_t works
 
 /* ------------------------------------------------------------------------
  * The step before attention: QK-norm, rotary embedding and KV append for the
- * one new token of every request (one decode step of one layer).
+ * new tokens of every request (one decode step of one layer, or a packed
+ * ragged batch of several new tokens per request).
  *
- * For request b with position p = kv_len[b] (the tokens already cached):
- *   q_out[b,h,:]    = rope(norm(q_in[b,h,:], q_norm_weight), p)     h < Hq
- *   K[b, p, kh, :]  = store(rope(norm(k_in[b,kh,:], k_norm_weight), p))
- *   V[b, p, kh, :]  = store(v_in[b,kh,:])                          kh < Hk
+ * For token row r of request b at position p (one new token per request:
+ * r = b and p = kv_len[b], the tokens already cached; with qo_indptr: rows
+ * r = qo_indptr[b] + i, i < qo_indptr[b+1] - qo_indptr[b], at p = kv_len[b] + i):
+ *   q_out[r,h,:]    = rope(norm(q_in[r,h,:], q_norm_weight), p)     h < Hq
+ *   K[b, p, kh, :]  = store(rope(norm(k_in[r,kh,:], k_norm_weight), p))
+ *   V[b, p, kh, :]  = store(v_in[r,kh,:])                          kh < Hk
  * norm(x, w) = x / sqrt(mean(x^2) + norm_eps) * w over the head dimension,
  *   skipped when the weight is NULL (QK-norm: the FlashInfer-from-JAX
  *   tutorial page, Gemma 3 section);
@@ -231,21 +234,28 @@ kvs_status kvs_decode(const kvs_decode_args *args, void *workspace, size_t works
  *   per-layer theta -- 10,000 local, 1,000,000 global: same page, the
  *   three-kernels and Gemma 3 sections);
  * store: to kv_dtype, nearest even; FP8_E4M3 stores the nearest code of
- *   x / k_scale[b,kh] (v_scale for V), saturating at +-448 ("Beyond the
- *   Memory Wall", section "2. FlashInfer": appending to the growing, paged,
- *   fp8 cache).
+ *   x / k_scale[b,kh] (v_scale for V), saturating at +-448; INT4 the nearest
+ *   integer to x / scale, ties to even, saturated to [-8, 7] (NaN: 0), two
+ *   per byte, element 2i in the low nibble ("Beyond the Memory Wall",
+ *   section "2. FlashInfer": appending to the growing, paged, fp8 or INT4
+ *   cache; the request's existing scale is kept, as the pages give no
+ *   running-scale rule).
+ * Several new tokens per request follow the packed batch that apply_rope
+ * rotates (FlashInfer-from-JAX page, three-kernels section); row i of a
+ * request takes the i-th free position after its cached tokens.
  * Angles are formed in double precision; the rest runs in fp32.
  *
- * Layouts as for kvs_decode: q_in, q_out [batch, Hq, d]; k_in, v_in
- * [batch, Hk, d]; the cache [num_pages, page_size, Hk, d] or, with
- * page_size 0 (batch 1), [num_pages, Hk, d] where num_pages is then the
- * capacity in tokens.  q_out may be q_in (in place).
+ * Layouts as for kvs_decode: q_in, q_out [rows, Hq, d]; k_in, v_in
+ * [rows, Hk, d] (rows = batch, or qo_indptr[batch]); the cache
+ * [num_pages, page_size, Hk, d] (INT4: d / 2 bytes) or, with page_size 0
+ * (batch 1), [num_pages, Hk, d] where num_pages is then the capacity in
+ * tokens.  q_out may be q_in (in place).
  * kv_len is read, not changed: the caller raises kv_len and kv_len_host by
- * one before the decode call that should see the new token.
+ * each request's new rows before the decode call that should see them.
  * Errors: argument checks run on the host before any HIP call, as for
- * kvs_decode.  Not checked (device data): a request whose page list does
- * not cover position p, or whose page id there is >= num_pages (contiguous:
- * p >= capacity), gets q_out but no cache write.
+ * kvs_decode.  Not checked (device data): a token whose position p is not
+ * covered by its request's page list, or whose page id there is >=
+ * num_pages (contiguous: p >= capacity), gets q_out but no cache write.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t batch;
@@ -253,7 +263,7 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;   /* 64, 128 or 256 */
   int32_t q_dtype;    /* q_in, k_in, v_in, q_out: KVS_F32 or KVS_BF16 */
-  int32_t kv_dtype;   /* cache; pairs as for kvs_decode, INT4 not supported */
+  int32_t kv_dtype;   /* cache; pairs as for kvs_decode (INT4: head_dim 128 or 256) */
   int32_t page_size;  /* 0: contiguous; else a power of two */
   int32_t num_pages;  /* paged: pages in each pool; contiguous: capacity (tokens) */
 
@@ -266,7 +276,7 @@ typedef struct {
   const int32_t *page_indptr;  /* paged only, as for kvs_decode */
   const int32_t *page_indices; /* paged only */
   const int32_t *kv_len;       /* device [batch]: position of the new token */
-  const float *k_scale;        /* FP8 cache only, [batch, Hk] */
+  const float *k_scale;        /* FP8 and INT4 caches only, [batch, Hk] */
   const float *v_scale;
   const float *q_norm_weight;  /* device [head_dim] fp32, or NULL: no q norm */
   const float *k_norm_weight;  /* device [head_dim] fp32, or NULL: no k norm */
@@ -277,6 +287,12 @@ typedef struct {
   /* optional profiling: two hipEvent_t stamped by the kernel's own dispatch
    * with its start and end; NULL to skip */
   void *prof_events[2];
+
+  /* optional: several new tokens per request.  NULL (both): one per request.
+   * Otherwise request b's token rows are qo_indptr[b] .. qo_indptr[b+1] - 1
+   * (0 rows allowed) and q_in, k_in, v_in, q_out hold qo_indptr[batch] rows. */
+  const int32_t *qo_indptr;      /* device [batch + 1] */
+  const int32_t *qo_indptr_host; /* host copy (sizes the launch); must equal qo_indptr */
 } kvs_append_args;
 
 /* Run the step asynchronously on `stream`.  Allocates nothing. */

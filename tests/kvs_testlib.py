@@ -136,10 +136,14 @@ def run_append(ai, in_place: bool = False, tensors=None):
     v = _codes_to_torch(ai.v_new, s.q_dtype)
     wq = None if ai.q_norm_weight is None else torch.from_numpy(ai.q_norm_weight).cuda()
     wk = None if ai.k_norm_weight is None else torch.from_numpy(ai.k_norm_weight).cuda()
+    rows = None
+    if ai.qo_indptr is not None:
+        rows = torch.from_numpy(np.asarray(ai.qo_indptr, np.int32)).cuda()
     q_out = kvs.append(q, k, v, t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                        page_indices=t.get("page_indices"), k_scale=t.get("k_scale"), v_scale=t.get("v_scale"),
                        q_norm_weight=wq, k_norm_weight=wk, norm_eps=ai.eps, rope_theta=ai.theta,
-                       rope_interleave=ai.interleave, q_out=q if in_place else None)
+                       rope_interleave=ai.interleave, q_out=q if in_place else None, qo_indptr=rows,
+                       qo_indptr_host=ai.qo_indptr, kv_dtype="int4" if s.kv_dtype == "int4" else None)
     torch.cuda.synchronize()
     got = {"q_out": _to_codes(q_out, s.q_dtype), "k_pool": _to_codes(t["k"], s.kv_dtype),
            "v_pool": _to_codes(t["v"], s.kv_dtype)}
@@ -164,13 +168,28 @@ def check_codes(got, y, dtype, what="", mag=None):
 
     got = np.asarray(got)
     y = np.asarray(y, dtype=np.float64)
-    assert got.shape == y.shape, (what, got.shape, y.shape)
+    packed = dtype == "int4"  # two codes per byte
+    assert got.shape[:-1] + (got.shape[-1] * (2 if packed else 1),) == y.shape, (what, got.shape, y.shape)
     scale = np.abs(y) if mag is None else np.maximum(np.abs(y), np.asarray(mag, np.float64))
     if dtype == "f32":
         err = np.abs(got.astype(np.float64) - y)
         bad = err > TIE_REL * np.maximum(scale, 1.0)
         assert not np.any(bad), f"{what}: fp32 error {float(np.max(err)):.3e}"
         return 0
+    if dtype == "int4":  # packed bytes: compare the unpacked integers
+        gv = oracle.int4_to_f64(got)
+        wv = oracle.int4_to_f64(oracle.encode_codes(y, "int4"))
+        diff = gv != wv
+        if not np.any(diff):
+            return 0
+        mid = (gv[diff] + wv[diff]) / 2
+        near_tie = (np.abs(gv[diff] - wv[diff]) == 1) & \
+            (np.abs(y[diff] - mid) <= TIE_REL * np.maximum(scale[diff], 1.0))
+        assert np.all(near_tie), (f"{what}: {int(np.sum(~near_tie))} INT4 codes differ away from a tie; "
+                                  f"first y={y[diff][~near_tie][:4]} got={gv[diff][~near_tie][:4]}")
+        n = int(np.sum(diff))
+        assert n <= max(1, y.size // 100), f"{what}: {n} of {y.size} codes at ties"
+        return n
     want = oracle.encode_codes(y, dtype)
     diff = got != want
     if not np.any(diff):
@@ -207,32 +226,35 @@ def _term_size(ai, x, weight, norm):
 
 def check_append(ai, got):
     """Every output of kvs_append against the oracle: q_out, the new K/V
-    slots, and the rest of both pools unchanged bit for bit."""
+    slots of every token row, and the rest of both pools unchanged bit for
+    bit."""
     import oracle
 
     c = ai.cache
     s = c.spec
-    B, Hq, Hk, d = s.batch, s.num_qo_heads, s.num_kv_heads, s.head_dim
+    Hq, Hk, d = s.num_qo_heads, s.num_kv_heads, s.head_dim
     ref = oracle.append_reference(ai)
-    Q = oracle.decode_codes(ai.q_new, s.q_dtype).reshape(B, Hq, d)
-    K = oracle.decode_codes(ai.k_new, s.q_dtype).reshape(B, Hk, d)
-    V = oracle.decode_codes(ai.v_new, s.q_dtype).reshape(B, Hk, d)
+    T = ref["q_out"].shape[0]
+    Q = oracle.decode_codes(ai.q_new, s.q_dtype).reshape(T, Hq, d)
+    K = oracle.decode_codes(ai.k_new, s.q_dtype).reshape(T, Hk, d)
+    V = oracle.decode_codes(ai.v_new, s.q_dtype).reshape(T, Hk, d)
     mq = _term_size(ai, Q, ai.q_norm_weight, ai.q_norm_weight is not None)
     mk = _term_size(ai, K, ai.k_norm_weight, ai.k_norm_weight is not None)
     mv = np.abs(V)
-    if s.kv_dtype == "fp8":
-        mk = mk / np.asarray(c.k_scale, np.float64)[:, :, None]
-        mv = mv / np.asarray(c.v_scale, np.float64)[:, :, None]
+    if s.kv_dtype in ("fp8", "int4"):
+        req = ref["req"]
+        mk = mk / np.asarray(c.k_scale, np.float64)[req][:, :, None]
+        mv = mv / np.asarray(c.v_scale, np.float64)[req][:, :, None]
     check_codes(got["q_out"], ref["q_out"], s.q_dtype, "q_out", mag=mq)
     raw = lambda a: a.view(np.uint32) if a.dtype == np.float32 else a
     k_pool, v_pool = got["k_pool"], got["v_pool"]
     mask = np.ones(k_pool.shape[:-2], dtype=bool)  # [rows] or [pages, page_size]
-    for b in range(s.batch):
-        row, slot = oracle.cache_slot(b, int(c.kv_len[b]), s.page_size, c.page_indptr, c.page_indices)
+    for r, b, pos in oracle.token_rows(ai):
+        row, slot = oracle.cache_slot(b, pos, s.page_size, c.page_indptr, c.page_indices)
         kk = k_pool[row] if slot is None else k_pool[row, slot]
         vv = v_pool[row] if slot is None else v_pool[row, slot]
-        check_codes(kk, ref["k"][b], s.kv_dtype, f"k[{b}]", mag=mk[b])
-        check_codes(vv, ref["v"][b], s.kv_dtype, f"v[{b}]", mag=mv[b])
+        check_codes(kk, ref["k"][r], s.kv_dtype, f"k[{r}]", mag=mk[r])
+        check_codes(vv, ref["v"][r], s.kv_dtype, f"v[{r}]", mag=mv[r])
         if slot is None:
             mask[row] = False
         else:

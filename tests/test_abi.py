@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 8
-    assert re.search(r"#define KVS_ABI_VERSION 8\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 9
+    assert re.search(r"#define KVS_ABI_VERSION 9\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -289,7 +289,7 @@ def _append_args(batch=2, Hq=8, Hk=2, d=128, q=kvs.KVS_BF16, kv=kvs.KVS_BF16, P=
     fake = 0x1000
     a.q_in = a.k_in = a.v_in = a.q_out = a.k_cache = a.v_cache = a.kv_len = fake
     a.page_indptr = a.page_indices = fake if P else None
-    a.k_scale = a.v_scale = fake if kv == kvs.KVS_FP8_E4M3 else None
+    a.k_scale = a.v_scale = fake if kv in (kvs.KVS_FP8_E4M3, kvs.KVS_INT4) else None
     a.norm_eps, a.rope_theta, a.rope_interleave = eps, theta, interleave
     return a
 
@@ -300,7 +300,8 @@ BAD_APPEND = [
     (dict(d=96), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=kvs.KVS_F32, kv=kvs.KVS_BF16), kvs.KVS_ERR_UNSUPPORTED),
     (dict(q=5), kvs.KVS_ERR_INVALID_ARG),
-    (dict(kv=kvs.KVS_INT4), kvs.KVS_ERR_UNSUPPORTED),           # the step does not write INT4 caches
+    (dict(kv=kvs.KVS_INT4, d=64), kvs.KVS_ERR_UNSUPPORTED),     # INT4 caches: head_dim 128 or 256
+    (dict(q=kvs.KVS_F32, kv=kvs.KVS_INT4), kvs.KVS_ERR_UNSUPPORTED),
     (dict(P=0), kvs.KVS_ERR_INVALID_ARG),          # contiguous with batch 2
     (dict(P=24), kvs.KVS_ERR_UNSUPPORTED),
     (dict(P=-16), kvs.KVS_ERR_INVALID_ARG),
@@ -317,6 +318,29 @@ BAD_APPEND = [
 @pytest.mark.parametrize("kw,status", BAD_APPEND, ids=[str(b[0]) for b in BAD_APPEND])
 def test_append_validation_before_any_hip_call(lib, kw, status):
     assert kvs.kvs_append(_append_args(**kw), 0) == status
+
+
+def test_append_token_row_checks(lib):
+    """A packed ragged batch: both row arrays or neither, offsets from 0,
+    never decreasing; INT4 caches accepted at head_dim 128 / 256."""
+    def with_rows(rows, dev=True, **kw):
+        a = _append_args(**kw)
+        qo = np.asarray(rows, np.int32)
+        a.qo_indptr, a.qo_indptr_host = (0x2000 if dev else None), qo.ctypes.data
+        return a, qo
+    for rows, dev, want in (([0, 3, 5], True, None), ([0, 0, 0], True, None), ([1, 3, 5], True, kvs.KVS_ERR_INVALID_ARG),
+                            ([0, 4, 2], True, kvs.KVS_ERR_INVALID_ARG), ([0, 3, 5], False, kvs.KVS_ERR_INVALID_ARG)):
+        a, keep = with_rows(rows, dev)
+        if want is not None:
+            assert kvs.kvs_append(a, 0) == want, rows
+    a = _append_args()
+    a.qo_indptr = 0x2000  # device array without its host copy
+    assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_INVALID_ARG
+    a, keep = with_rows([0, 1 << 22, 1 << 23], Hq=32, Hk=8)  # 2^23 token rows x 40 head rows: too many
+    assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_UNSUPPORTED
+    a = _append_args(kv=kvs.KVS_INT4)
+    a.k_scale = None
+    assert kvs.kvs_append(a, 0) == kvs.KVS_ERR_INVALID_ARG
 
 
 def test_append_null_pointers_rejected(lib):
@@ -389,4 +413,3 @@ def test_binding_passes_contiguous_capacity():
     q, k, v, kv_len, extra = _torch_case(L=40, cap=64)
     with pytest.raises(ValueError, match="must be on"):
         kvs.make_args(q, k, v, kv_len, kv_len_host=[40])
-

@@ -490,3 +490,26 @@ def test_planted_int4_half_up_rounding_is_caught(monkeypatch):
     monkeypatch.setattr(C, "f64_to_int4_codes", half_up)
     with pytest.raises(AssertionError):
         test_int4_encoder_ties_and_saturation()
+
+
+# ------------------------------------------------------------------ the GPU tests' checker, on the CPU
+
+@pytest.mark.parametrize("kv,rows", [("bf16", None), ("fp8", [2, 0, 5]), ("int4", [3, 1, 0]), ("int4", None)])
+def test_append_checker_accepts_the_oracle_and_catches_a_slip(kv, rows):
+    """check_append (what the GPU append tests run) passes on the oracle's
+    own codes laid into the pools, and fails when one stored code is off."""
+    from kvs_testlib import check_append
+
+    name = {"bf16": "c4_paged_bf16_b64", "fp8": "c5_paged_fp8_b128", "int4": "c6_paged_int4_b128"}[kv]
+    spec = small_variant(name, batch=3, lengths=("list", [5, 40, 16]))
+    ai = make_append_inputs(spec, seed=1, theta=1e4, rows=rows, poison=True)
+    codes = A.append_codes(A.append_reference(ai), "bf16", kv)
+    k_pool, v_pool, _ = A.apply_append(ai, codes)
+    got = {"q_out": codes["q_out"], "k_pool": k_pool, "v_pool": v_pool}
+    check_append(ai, got)
+    r, b, p = A.token_rows(ai)[-1]
+    page, slot = A.cache_slot(b, p, 16, ai.cache.page_indptr, ai.cache.page_indices)
+    bad = np.array(k_pool, copy=True)
+    bad[page, slot, 0, 0] ^= 0x22 if kv == "int4" else 0x02  # a different code
+    with pytest.raises(AssertionError):
+        check_append(ai, dict(got, k_pool=bad))

@@ -26,21 +26,29 @@ def _lib():
 
 
 def _append_then_decode(ai, **kw):
-    """Run the append, check it, then decode over the appended cache."""
+    """Run the append, check it, then attend over the appended cache with
+    the appended rows as queries (one per request: decode; several: the
+    causal rows of each request) and compare with the oracle's attention
+    over the oracle-appended cache."""
+    import torch
+
     got, t = run_append(ai, **kw)
     ref = check_append(ai, got)
     c = ai.cache
     s = c.spec
     codes = oracle.append_codes(ref, s.q_dtype, s.kv_dtype)
     k_pool, v_pool, kv_len = oracle.apply_append(ai, codes)
-    after = dataclasses.replace(c, q=codes["q_out"], k=k_pool, v=v_pool, kv_len=kv_len)
-    o_ref, lse_ref = oracle.decode_reference(after)
-    # the GPU decode reads the GPU-appended cache and the GPU's q_out
-    t["kv_len"] += 1
+    after = dataclasses.replace(c, q=codes["q_out"], k=k_pool, v=v_pool, kv_len=kv_len, qo_indptr=ai.qo_indptr)
+    o_ref, lse_ref = oracle.attention_reference(after)
+    # the GPU attention reads the GPU-appended cache and the GPU's q_out
+    t["kv_len"] = torch.from_numpy(kv_len.astype(np.int32)).cuda()
     t["q"] = _codes_to_torch(got["q_out"], s.q_dtype)
-    gpu_after = dataclasses.replace(c, kv_len=kv_len)
+    if ai.qo_indptr is not None:
+        t["qo_indptr"] = torch.from_numpy(np.asarray(ai.qo_indptr, np.int32)).cuda()
+    gpu_after = dataclasses.replace(c, kv_len=kv_len, qo_indptr=ai.qo_indptr)
     o, lse = run_library(gpu_after, tensors=t)
-    compare(o, lse, o_ref, lse_ref, s.kv_dtype)
+    err, rel = compare(o, lse, o_ref, lse_ref, s.kv_dtype)
+    print(f"  attention after append: max|o-o_ref|={err:.2e} lse_rel={rel:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("name,lens,theta", [
@@ -133,5 +141,66 @@ def test_append_full_size(name):
     oracle, the pools otherwise unchanged."""
     print(f"case append full {name}", flush=True)
     ai = make_append_inputs(CONFIGS[name], theta=1e4)
+    got, _ = run_append(ai)
+    check_append(ai, got)
+
+
+# ------------------------------------------------------------------ INT4 caches, ragged token rows
+
+@pytest.mark.parametrize("interleave", [False, True])
+@pytest.mark.parametrize("d", [128, 256])
+def test_int4_append_then_decode(d, interleave):
+    """New tokens stored into an INT4 cache with each request's existing
+    scale (nearest even, saturated to [-8, 7]), then decode over it."""
+    print(f"case append int4 d={d} interleave={interleave}", flush=True)
+    spec = dataclasses.replace(small_variant("c6_paged_int4_b128", batch=4, lengths=("list", [0, 15, 16, 700])),
+                               head_dim=d, sm_scale=d ** -0.5)
+    _append_then_decode(make_append_inputs(spec, seed=19 + d, theta=1e4, interleave=interleave, poison=True))
+
+
+def test_int4_append_saturates():
+    """Scales far below the new values: every new code saturates at -8 or 7."""
+    print("case append int4 saturation", flush=True)
+    spec = small_variant("c6_paged_int4_b128", batch=2, lengths=("list", [30, 3]))
+    ai = make_append_inputs(spec, seed=2, theta=1e4, norm=False)
+    small = dataclasses.replace(ai.cache, k_scale=np.full_like(ai.cache.k_scale, 1e-3),
+                                v_scale=np.full_like(ai.cache.v_scale, 1e-3))
+    ai = dataclasses.replace(ai, cache=small)
+    got, _ = run_append(ai)
+    check_append(ai, got)
+
+
+@pytest.mark.parametrize("name,rows", [
+    ("c4_paged_bf16_b64", [3, 0, 17, 1, 40]),
+    ("c5_paged_fp8_b128", [5, 12, 0, 33, 2]),
+    ("c6_paged_int4_b128", [8, 1, 21, 0, 64]),
+    ("c3_llama2_7b_32k", [100]),
+])
+def test_ragged_append_then_attend(name, rows):
+    """A packed ragged batch of new tokens (0 to 100 per request, paged and
+    contiguous, bf16 / fp8 / INT4 caches): every row normed, rotated at its
+    own position and stored there, then attention with the appended rows as
+    the causal queries of each request."""
+    print(f"case append ragged {name} rows={rows}", flush=True)
+    lens = [40, 0, 333, 16, 1000][:len(rows)] if len(rows) > 1 else [600]
+    spec = small_variant(name, batch=len(rows), lengths=("list", lens))
+    _append_then_decode(make_append_inputs(spec, seed=23, theta=1e4, rows=rows, poison=True))
+
+
+def test_ragged_append_many_requests():
+    """300 requests: the request of each token row comes from qo_indptr on
+    the device (a binary search) instead of the kernel arguments."""
+    print("case append ragged 300 requests", flush=True)
+    spec = DecodeSpec("ragged300", 300, 8, 2, 128, 16, "bf16", "bf16", 128 ** -0.5, lengths=("uniform", 0, 300),
+                      seed=44)
+    rows = np.random.default_rng(1).integers(0, 6, 300)
+    _append_then_decode(make_append_inputs(spec, theta=1e4, rows=rows, poison=True))
+
+
+def test_ragged_append_full_size():
+    """The batch-64 paged workload with 4 new tokens per request, every
+    output against the oracle."""
+    print("case append ragged full c4 x 4", flush=True)
+    ai = make_append_inputs(CONFIGS["c4_paged_bf16_b64"], theta=1e4, rows=[4] * 64)
     got, _ = run_append(ai)
     check_append(ai, got)
