@@ -6,6 +6,7 @@ not built, every call raises.
 
 Low level (same names as the C ABI in ``include/kvsplit.h``):
     kvs_decode(args, workspace_ptr, workspace_bytes, stream) -> status
+    kvs_decode_noalloc(args, stream) -> status
     kvs_decode_plan(args) -> KvsPlanInfo
     kvs_decode_workspace_bytes(args) -> int
     kvs_append(args, stream) -> status
@@ -27,6 +28,7 @@ from typing import Optional, Tuple
 
 __all__ = [
     "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
+    "KVS_ERR_TOO_LARGE", "KVS_NOALLOC_SCRATCH_BYTES", "kvs_decode_noalloc",
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_INT4", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
     "KVS_ALGO_MFMA_PACKED",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
@@ -40,6 +42,8 @@ __all__ = [
 KVS_ABI_VERSION = 9
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
+KVS_ERR_TOO_LARGE = -5
+KVS_NOALLOC_SCRATCH_BYTES = 32 << 20
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
 KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
 _ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
@@ -155,6 +159,8 @@ def load_library():
             lib.kvs_decode.restype = ctypes.c_int
             lib.kvs_decode.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
+            lib.kvs_decode_noalloc.restype = ctypes.c_int
+            lib.kvs_decode_noalloc.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.c_void_p]
             lib.kvs_decode_plan.restype = ctypes.c_int
             lib.kvs_decode_plan.argtypes = [ctypes.POINTER(KvsDecodeArgs), ctypes.POINTER(KvsPlanInfo)]
             lib.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -181,6 +187,10 @@ def load_library():
 def kvs_decode(args: KvsDecodeArgs, workspace: int, workspace_bytes: int, stream: int) -> int:
     return int(load_library().kvs_decode(ctypes.byref(args), ctypes.c_void_p(workspace or None),
                                          ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream or None)))
+
+
+def kvs_decode_noalloc(args: KvsDecodeArgs, stream: int) -> int:
+    return int(load_library().kvs_decode_noalloc(ctypes.byref(args), ctypes.c_void_p(stream or None)))
 
 
 def kvs_decode_plan(args: KvsDecodeArgs) -> KvsPlanInfo:

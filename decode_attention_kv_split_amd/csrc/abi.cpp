@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "kvsplit.h"
@@ -222,6 +223,41 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   return KVS_OK;
 }
 
+// Device memory of kvs_decode_noalloc: one file-scope array that every GPU
+// the library runs on holds, at its own address, until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the address each device gives for it (hipGetSymbolAddress, with that device
+// current) is what kernels receive.
+static __device__ __align__(256) char scratch[KVS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device; null on a HIP error.
+void *scratch_address(kvs_status *st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *st = KVS_ERR_HIP;
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    *st = KVS_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *st = KVS_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 } // namespace
 
 extern "C" {
@@ -340,6 +376,24 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   return KVS_OK;
 }
 
+kvs_status kvs_decode_noalloc(const kvs_decode_args *a, hipStream_t stream) {
+  kvs::Plan pl;
+  int algo = 0, cus = 0;
+  kvs_status st = plan_call(a, true, &pl, &algo, &cus);
+  if (st != KVS_OK) return st;
+  if (pl.workspace_bytes > KVS_NOALLOC_SCRATCH_BYTES) return KVS_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  if (pl.workspace_bytes > 0) {
+    st = KVS_OK;
+    ws = scratch_address(&st);
+    if (!ws) return st;
+  }
+  // the partial and merge kernels of kvs_decode, with the fixed array as their
+  // workspace (which needs no clearing: every byte the merge reads, the
+  // partial kernel of the same call wrote)
+  return kvs_decode(a, ws, KVS_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 kvs_status kvs_append(const kvs_append_args *args, hipStream_t stream) {
   const kvs_status st = validate_append(args);
   if (st != KVS_OK) return st;
@@ -355,6 +409,8 @@ const char *kvs_status_string(int s) {
   case KVS_ERR_UNSUPPORTED: return "unsupported shape or type";
   case KVS_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
   case KVS_ERR_HIP: return "HIP runtime or launch error";
+  case KVS_ERR_TOO_LARGE: return "call needs more scratch than kvs_decode_noalloc's fixed device array "
+                                 "(KVS_NOALLOC_SCRATCH_BYTES); use kvs_decode with a workspace";
   default: return "unknown status";
   }
 }

@@ -61,7 +61,9 @@ typedef enum {
   KVS_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shapes */
   KVS_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
   KVS_ERR_WORKSPACE = -3,   /* workspace null, too small or misaligned */
-  KVS_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+  KVS_ERR_HIP = -4,         /* a HIP runtime call or launch failed */
+  KVS_ERR_TOO_LARGE = -5    /* kvs_decode_noalloc: the call needs more scratch than
+                               KVS_NOALLOC_SCRATCH_BYTES */
 } kvs_status;
 
 /* Element types.  q and o share q_dtype; K and V share kv_dtype.
@@ -212,6 +214,21 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
  * visible K/V values are finite. */
 kvs_status kvs_decode(const kvs_decode_args *args, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): kvs_decode
+ * with no workspace argument.  The split partials live in one device array
+ * of KVS_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its address on the current device is looked up
+ * once, on the first call there.  The caller still passes every input and
+ * output.  The call allocates nothing and runs the kernels of kvs_decode.
+ * Returns KVS_ERR_TOO_LARGE (before any HIP call) when
+ * kvs_decode_workspace_bytes(args) exceeds KVS_NOALLOC_SCRATCH_BYTES: use
+ * kvs_decode with a workspace then.  All calls on one GPU share the array,
+ * so calls that may overlap on one GPU (different streams, or host threads
+ * racing on one stream) race on it and give wrong results; serialise them. */
+#define KVS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kvs_status kvs_decode_noalloc(const kvs_decode_args *args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * The step before attention: QK-norm, rotary embedding and KV append for the

@@ -413,3 +413,16 @@ def test_binding_passes_contiguous_capacity():
     q, k, v, kv_len, extra = _torch_case(L=40, cap=64)
     with pytest.raises(ValueError, match="must be on"):
         kvs.make_args(q, k, v, kv_len, kv_len_host=[40])
+
+
+def test_noalloc_rejects_oversized_calls_before_any_hip_call(lib):
+    """kvs_decode_noalloc validates like kvs_decode, then refuses a call whose
+    split partials would not fit its fixed device array."""
+    a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(1 << 20,), chunk=16, num_pages=1 << 20)
+    assert kvs.kvs_decode_workspace_bytes(a) > kvs.KVS_NOALLOC_SCRATCH_BYTES
+    assert kvs.kvs_decode_noalloc(a, 0) == kvs.KVS_ERR_TOO_LARGE
+    assert "KVS_NOALLOC_SCRATCH_BYTES" in kvs.kvs_status_string(kvs.KVS_ERR_TOO_LARGE)
+    a, keep = _args(window=0)
+    assert kvs.kvs_decode_noalloc(a, 0) == kvs.KVS_ERR_INVALID_ARG
+    assert re.search(r"#define KVS_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", open(HEADER).read())
+    assert kvs.KVS_NOALLOC_SCRATCH_BYTES == 32 << 20
