@@ -351,7 +351,8 @@ def graph_steps(a, ws, steps: int) -> float:
 
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
-        q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0, graph: bool = False, probe: bool = True) -> dict:
+        q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0, graph: bool = False, probe: bool = True,
+        merge_mode: str = "auto") -> dict:
     import dataclasses
 
     import torch
@@ -381,9 +382,9 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
                             window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max,
                             kv_dtype="int4" if s.kv_dtype == "int4" else None,
                             qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr,
-                            logits_soft_cap=spec.soft_cap)
+                            logits_soft_cap=spec.soft_cap, merge_mode=merge_mode)
     plan = kvs.kvs_decode_plan(a)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")  # merge counters start at zero
     stream = torch.cuda.current_stream().cuda_stream
     def step(e0=None, e1=None):
         a.prof_events[0] = e0
@@ -451,7 +452,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "head_dim": s.head_dim, "page_size": s.page_size, "window": s.window, "kv_dtype": s.kv_dtype,
             "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
-            "max_splits": plan.max_splits, "parallelism": "single GPU",
+            "max_splits": plan.max_splits, "merge_in_partial": plan.merge_in_partial, "parallelism": "single GPU",
             "unified_max": unified_max, "q_len": q_len, "soft_cap": spec.soft_cap,
             "kv_len_override": kv_len or None,
         },
@@ -558,7 +559,7 @@ def run_append_op(config_name: str, steps: int, warmup: int, with_decode: bool, 
                                page_indices=t.get("page_indices"), kv_len_host=host1,
                                k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=spec.sm_scale,
                                window=spec.window, algo=algo)
-    ws = torch.empty(max(kvs.kvs_decode_workspace_bytes(da), 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(kvs.kvs_decode_workspace_bytes(da), 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     def step(e0=None, e1=None):
         aa.prof_events[0], aa.prof_events[1] = e0, e1
@@ -642,6 +643,9 @@ def main():
                          "embedding + KV append of the new token; step: append then decode")
     ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "mfma_packed", "valu"])
     ap.add_argument("--kv-chunk", type=int, default=0)
+    ap.add_argument("--merge", default="auto", choices=["auto", "in_partial", "kernel"],
+                    help="where split partials are merged: chosen by the planner, inside the partial kernel, "
+                         "or by a second kernel")
     ap.add_argument("--unified-max", type=float, default=None,
                     help="start every chunk's softmax from this reference max (scaled-score units)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -680,8 +684,8 @@ def main():
         return
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
-              soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph)
-    plain = (args.algo == "auto" and args.kv_chunk == 0 and args.unified_max is None and args.q_len == 1
+              soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph, merge_mode=args.merge)
+    plain = (args.merge == "auto" and args.algo == "auto" and args.kv_chunk == 0 and args.unified_max is None and args.q_len == 1
              and not args.soft_cap and not args.kv_len and not args.cold and not args.graph)
     if name == DEFAULT and plain and not args.single:
         # the other two long-context / batched paged workloads of the 70%-of-peak

@@ -28,9 +28,9 @@ from typing import Optional, Tuple
 
 __all__ = [
     "KVS_OK", "KVS_ERR_INVALID_ARG", "KVS_ERR_UNSUPPORTED", "KVS_ERR_WORKSPACE", "KVS_ERR_HIP",
-    "KVS_ERR_TOO_LARGE", "KVS_NOALLOC_SCRATCH_BYTES", "kvs_decode_noalloc",
+    "KVS_ERR_TOO_LARGE", "KVS_NOALLOC_SCRATCH_BYTES", "kvs_decode_noalloc", "KVS_WORKSPACE_COUNTER_BYTES",
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_INT4", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
-    "KVS_ALGO_MFMA_PACKED",
+    "KVS_ALGO_MFMA_PACKED", "KVS_MERGE_AUTO", "KVS_MERGE_IN_PARTIAL", "KVS_MERGE_KERNEL",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
     "library_path", "load_library",
     "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_append", "kvs_status_string",
@@ -39,13 +39,16 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 9
+KVS_ABI_VERSION = 10
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_ERR_TOO_LARGE = -5
 KVS_NOALLOC_SCRATCH_BYTES = 32 << 20
+KVS_WORKSPACE_COUNTER_BYTES = 65536
 KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
 KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
+KVS_MERGE_AUTO, KVS_MERGE_IN_PARTIAL, KVS_MERGE_KERNEL = 0, 1, 2
+_MERGE_MODES = {"auto": KVS_MERGE_AUTO, "in_partial": KVS_MERGE_IN_PARTIAL, "kernel": KVS_MERGE_KERNEL}
 _ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +90,7 @@ class KvsDecodeArgs(ctypes.Structure):
         ("qo_indptr", ctypes.c_void_p),
         ("qo_indptr_host", ctypes.c_void_p),
         ("logits_soft_cap", ctypes.c_float),
+        ("merge_mode", ctypes.c_int32),
     ]
 
 
@@ -101,6 +105,7 @@ class KvsPlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("col_groups", ctypes.c_int32),
         ("col_share", ctypes.c_int32),
+        ("merge_in_partial", ctypes.c_int32),
     ]
 
 
@@ -282,8 +287,10 @@ def _workspace(nbytes: int, device, stream: int):
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
+            # zeroed: the first KVS_WORKSPACE_COUNTER_BYTES are merge counters
+            # that must start at zero (every call leaves them zero)
             with torch.cuda.device(device), torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
-                buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+                buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             _ws_cache[key] = buf
     return buf
 
@@ -292,7 +299,8 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
               k_scale=None, v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0,
               algo="auto", out=None, lse=None, num_cus: int = 0,
               unified_max: Optional[float] = None, kv_dtype: Optional[str] = None, qo_indptr=None,
-              qo_indptr_host=None, logits_soft_cap: float = 0.0) -> Tuple[KvsDecodeArgs, object]:
+              qo_indptr_host=None, logits_soft_cap: float = 0.0,
+              merge_mode="auto") -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
@@ -381,6 +389,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     if qoh is not None:
         a.qo_indptr, a.qo_indptr_host = _ptr(qo_indptr), qoh.ctypes.data
     a.logits_soft_cap = float(logits_soft_cap)
+    a.merge_mode = _MERGE_MODES[merge_mode] if isinstance(merge_mode, str) else int(merge_mode)
     keep = (kvh, out, lse, qoh)
     return a, keep
 
@@ -388,7 +397,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
            workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None,
-           qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0):
+           qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0, merge_mode="auto"):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
@@ -397,7 +406,7 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
                         window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
                         kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host,
-                        logits_soft_cap=logits_soft_cap)
+                        logits_soft_cap=logits_soft_cap, merge_mode=merge_mode)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

@@ -22,8 +22,16 @@ int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow
 bool mfma_packable(int head_dim, int group, int num_kv_heads, int kv_type);
 int mfma_col_share(int head_dim, int kv_type, int col_groups);
 bool mfma_head_dim_ok(int head_dim, int kv_type);
+bool rows_merge_in_kernel(int head_dim, int kv_type);
 hipError_t launch_append(const kvs_append_args *a, const Launch &l);
 } // namespace kvs
+
+static_assert(kvs::kPlanInlineRequests == kvs::kInlineRequests && kvs::kPlanInlineItems == kvs::kInlineItems &&
+                  kvs::kPlanInlineSplits == kvs::kInlineSplits,
+              "planner and kernels agree on the inline work-list sizes");
+static_assert(sizeof(kvs::Params) + sizeof(kvs::InlineWork) <= 4096, "kernel arguments fit 4 KB");
+static_assert(kvs::kPlanCounterBytes == kvs::kCounterBytes && kvs::kCounterBytes == KVS_WORKSPACE_COUNTER_BYTES,
+              "planner, kernels and header agree on the counter area");
 
 namespace {
 
@@ -66,6 +74,7 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (a->use_unified_max != 0 && a->use_unified_max != 1) return KVS_ERR_INVALID_ARG;
   if (a->use_unified_max && !std::isfinite(a->unified_max)) return KVS_ERR_INVALID_ARG;
   if (!(a->logits_soft_cap >= 0.0f) || !std::isfinite(a->logits_soft_cap)) return KVS_ERR_INVALID_ARG;
+  if (a->merge_mode < KVS_MERGE_AUTO || a->merge_mode > KVS_MERGE_KERNEL) return KVS_ERR_INVALID_ARG;
   for (int b = 0; b < a->batch; ++b) {
     const int L = a->kv_len_host[b];
     if (L < 0) return KVS_ERR_INVALID_ARG;
@@ -206,6 +215,22 @@ Columns columns_of(const kvs_decode_args *a) {
   return c;
 }
 
+// KV heads per partial workgroup for the resolved kernel family.
+int kv_pack(const kvs_decode_args *a, int algo) {
+  if (algo == KVS_ALGO_VALU) return 1;
+  return kvs::mfma_pack(a->head_dim, a->num_qo_heads / a->num_kv_heads, a->num_kv_heads, a->kv_dtype,
+                        algo == KVS_ALGO_MFMA_PACKED);
+}
+
+// Whether the partial kernel merges the splits itself: the plan allows it
+// (host work list, counters fit) and the kernel that runs has the merge
+// compiled in (the shared-tile kernel for INT4 at head_dim 256 does not).
+bool merges_in_partial(const kvs::Plan &pl, const kvs_decode_args *a, const Columns &c) {
+  if (!pl.fused || a->merge_mode == KVS_MERGE_KERNEL) return false;
+  if (c.col_share >= 4 && !kvs::rows_merge_in_kernel(a->head_dim, a->kv_dtype)) return false;
+  return a->merge_mode == KVS_MERGE_IN_PARTIAL || pl.fused_pays;
+}
+
 kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, int *algo, int *cus,
                      Columns *cols_out = nullptr) {
   kvs_status st = validate(a, need_ptrs, algo);
@@ -213,8 +238,9 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   st = resolve_cus(a, cus);
   if (st != KVS_OK) return st;
   Columns c = columns_of(a);
+  const int pack = kv_pack(a, *algo);
   if (!kvs::make_plan(a->kv_len_host, c.nq.empty() ? nullptr : c.nq.data(), a->batch, a->window,
-                      a->num_kv_heads, c.cols, c.col_blocks, a->head_dim, a->kv_chunk, *cus, pl))
+                      a->num_kv_heads, c.cols, c.col_blocks, pack, a->head_dim, a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
   // (the merge runs one workgroup per column group)
@@ -233,6 +259,12 @@ static __device__ __align__(256) char scratch[KVS_NOALLOC_SCRATCH_BYTES];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_clear[kMaxDevices] = {}; // its counter area has been zeroed on the device
+
+// Zeroes n 32-bit words (the merge counters at the start of `scratch`).
+__global__ void zero_words(unsigned *w, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) w[i] = 0u;
+}
 
 // Device address of `scratch` on the current device, looked up once per
 // device; null on a HIP error.
@@ -258,6 +290,25 @@ void *scratch_address(kvs_status *st) {
   return g_scratch_ptr[dev];
 }
 
+// Before the first call on a device: zero the counter area of `scratch` with a
+// kernel on the caller's stream (ahead of that call's own kernels).  A call
+// under graph capture records the zeroing into the graph and leaves the
+// device unmarked, so the next eager call zeroes again; calls leave the
+// counters zero, so later calls need nothing.
+kvs_status clear_scratch_counters(void *ptr, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_clear[dev]) return KVS_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return KVS_ERR_HIP;
+  const int words = (int)(KVS_WORKSPACE_COUNTER_BYTES / sizeof(unsigned));
+  hipLaunchKernelGGL(zero_words, dim3(words / 256), dim3(256), 0, stream, reinterpret_cast<unsigned *>(ptr), words);
+  if (hipGetLastError() != hipSuccess) return KVS_ERR_HIP;
+  if (cap == hipStreamCaptureStatusNone) g_scratch_clear[dev] = true;
+  return KVS_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -278,6 +329,7 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   const Columns c = columns_of(args);
   out->col_groups = c.col_groups;
   out->col_share = c.col_share;
+  out->merge_in_partial = merges_in_partial(pl, args, c) ? 1 : 0;
   return KVS_OK;
 }
 
@@ -310,20 +362,18 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.v_scale = scaled ? a->v_scale : nullptr;
   p.o = a->o;
   p.lse = a->lse;
-  p.o_part = pl.workspace_bytes ? reinterpret_cast<float *>(workspace) : nullptr;
-  p.lse_part = pl.workspace_bytes
-                   ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + pl.o_part_bytes)
-                   : nullptr;
-  p.meta = pl.workspace_bytes ? reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) + pl.o_part_bytes +
-                                                        pl.lse_part_bytes)
-                              : nullptr;
+  char *ws = reinterpret_cast<char *>(workspace);
+  p.counters = nullptr;
+  p.o_part = pl.workspace_bytes ? reinterpret_cast<float *>(ws + pl.counter_bytes) : nullptr;
+  p.lse_part = pl.workspace_bytes ? reinterpret_cast<float *>(ws + pl.counter_bytes + pl.o_part_bytes) : nullptr;
+  p.meta = pl.workspace_bytes
+               ? reinterpret_cast<int *>(ws + pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes)
+               : nullptr;
   p.batch = a->batch;
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;
   p.group = a->num_qo_heads / a->num_kv_heads;
-  p.pack = algo == KVS_ALGO_VALU ? 1
-                                 : kvs::mfma_pack(a->head_dim, p.group, a->num_kv_heads, a->kv_dtype,
-                                                  algo == KVS_ALGO_MFMA_PACKED);
+  p.pack = kv_pack(a, algo);
   p.qo_indptr = a->qo_indptr_host ? a->qo_indptr : nullptr;
   p.col_groups = cols.col_groups;
   p.col_share = cols.col_share;
@@ -350,7 +400,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   w.n_items = 0;
   kvs::InlineMerge ml;
   ml.n = -1;
-  if (a->batch <= kvs::kInlineRequests && pl.items <= kvs::kInlineItems) {
+  if (kvs::plan_inline(a->batch, pl.items, pl.max_splits)) {
     int n_merges = 0; // at most one entry per request, so it fits too
     kvs::list_work(a->kv_len_host, cols.nq.empty() ? nullptr : cols.nq.data(), a->batch, a->window, pl.chunk,
                    w.item, ml.req, ml.first, &n_merges);
@@ -359,6 +409,9 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
     ml.n = n_merges;
     p.meta = nullptr; // the merge kernel reads its list from the arguments
   }
+  // the partial kernel merges the splits itself when its work list is the
+  // host's (every planned split then arrives) and the counters fit
+  if (w.n_items > 0 && merges_in_partial(pl, a, cols)) p.counters = reinterpret_cast<unsigned *>(ws);
 
   // the partial kernel's dispatch stamps the profiling events itself
   const kvs::Launch lp{stream, reinterpret_cast<hipEvent_t>(a->prof_events[0]),
@@ -369,7 +422,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   else
     e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, lp);
   if (e != hipSuccess) return KVS_ERR_HIP;
-  if (pl.needs_merge) {
+  if (pl.needs_merge && !p.counters) {
     e = kvs::launch_merge(p, ml, a->head_dim, stream);
     if (e != hipSuccess) return KVS_ERR_HIP;
   }
@@ -387,10 +440,11 @@ kvs_status kvs_decode_noalloc(const kvs_decode_args *a, hipStream_t stream) {
     st = KVS_OK;
     ws = scratch_address(&st);
     if (!ws) return st;
+    st = clear_scratch_counters(ws, stream);
+    if (st != KVS_OK) return st;
   }
-  // the partial and merge kernels of kvs_decode, with the fixed array as their
-  // workspace (which needs no clearing: every byte the merge reads, the
-  // partial kernel of the same call wrote)
+  // the kernels of kvs_decode, with the fixed array as their workspace: its
+  // counter area is zero (above), and every call leaves it zero
   return kvs_decode(a, ws, KVS_NOALLOC_SCRATCH_BYTES, stream);
 }
 

@@ -251,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     __syncthreads();
     merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
+  finish_split<D>(p, blockIdx.y, b, kvg, cg0, CG, item, split, nb, smem);
 }
 
 } // namespace

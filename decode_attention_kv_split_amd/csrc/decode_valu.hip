@@ -88,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
   int b, split, nb, L;
   if (w.n_items > 0) { // planned on the host
     const uint32_t e = w.item[item];
-    b = (int)(e >> 16);
-    split = (int)(e & 0xFFFF);
+    b = (int)(e >> 8);
+    split = (int)(e & 0xFF);
     L = w.req_len[b];
     nb = num_splits(L, 1, p.window, p.chunk);
   } else {
@@ -231,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(const Params p, 
   }
   __syncthreads();
   merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvh, 0, item, nb);
+  finish_split<D>(p, blockIdx.y, b, kvh, 0, 1, item, split, nb, sm_o);
 }
 
 template <int D, int KVT>

@@ -90,20 +90,60 @@ struct Params {
   int out_bf16;   // o (and q) stored as bf16
   float score_scale; // sm_scale * log2(e); with a soft cap c: sm_scale / c
   float cap_out;     // soft cap: scores become tanh(score_scale * qk) * cap_out, cap_out = c * log2(e); 0: no cap
+  // Merge in the partial kernel (null: a second kernel merges): one arrival
+  // counter per (partial-launch slot grid.y, request), zero between calls.
+  unsigned *counters;
 };
+
+// Counters of the merge done inside the partial kernel sit at the start of
+// the workspace: at most this many bytes, one uint32 per (grid.y slot,
+// request).  They must be zero when a call starts; every call that uses
+// them leaves them zero.
+constexpr size_t kCounterBytes = 65536;
+
+// Split partials (o_part, lse_part) are written and, by the merge inside the
+// partial kernel, read back with device-scope relaxed atomic accesses: on
+// gfx950 these are the sc1 forms of the plain loads and stores, which write
+// through and read at the point where the XCDs' L2 caches are coherent.  So a
+// partial written on one XCD is visible to the merging workgroup on another
+// once its store has completed, and no workgroup needs a device-scope fence
+// (a write-back and invalidate of its whole L2, which made every split
+// workgroup pay for the others' traffic).
+__device__ __forceinline__ void store_partial(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_partial4(float *p, float a, float b, float c, float d) {
+  store_partial(p, a);
+  store_partial(p + 1, b);
+  store_partial(p + 2, c);
+  store_partial(p + 3, d);
+}
+__device__ __forceinline__ float load_partial(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every memory access this thread issued has completed (vmcnt 0;
+// on gfx9 stores count there too), and keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void wait_all_vmem() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); // vmcnt(0), expcnt and lgkmcnt untouched
+  __asm__ volatile("" ::: "memory");
+}
 
 // Work lists planned on the host from kv_len_host and passed in the kernel
 // arguments when they fit, which saves each workgroup a dependent memory read
 // before its first K/V load; larger batches derive the same lists from kv_len
 // on the device (scan_requests, meta).
+// An item is 16 bits, request and split 8 bits each, so the list holds up to
+// 1344 items of at most 256 requests with at most 256 splits each.
 constexpr int kInlineRequests = 256;
-constexpr int kInlineItems = 448;
+constexpr int kInlineSplits = 256;
+constexpr int kInlineItems = 1344;
 constexpr int kInlineMerges = 384;
 
 struct InlineWork {
   int n_items;                   // items per KV head listed below; 0: not provided
   int req_len[kInlineRequests];  // kv_len of each request (the host copy)
-  uint32_t item[kInlineItems];   // work item x: (request << 16) | split
+  uint16_t item[kInlineItems];   // work item x: (request << 8) | split
 };
 
 struct InlineMerge {
@@ -250,10 +290,180 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, const flo
       if (d == 0 && p.lse) p.lse[(size_t)row * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
       const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-      p.o_part[(slot * p.cols + h) * D + d] = val;
-      if (d == 0) p.lse_part[slot * p.cols + h] = lse2;
+      store_partial(p.o_part + (slot * p.cols + h) * D + d, val);
+      if (d == 0) store_partial(p.lse_part + slot * p.cols + h, lse2);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of split partials.  For an output with splits c holding a
+// normalised partial o_c and a log2-domain log-sum-exp l_c:
+//   M = max_c l_c,  w_c = 2^(l_c - M),  o = sum_c w_c o_c / sum_c w_c,
+//   lse = (M + log2 sum_c w_c) * ln 2,  all l_c = -inf -> o = 0, lse = -inf.
+// This is the online-softmax rescale ("Forcing Flash Attention onto TPU",
+// section "Flash Attention in JAX": multiply the old accumulator and sum by
+// exp(old max - new max)) applied across chunks; the FlashDecoding++
+// explainer's asynchronous-softmax section describes this synchronised update
+// of per-tile partial softmax results with the previous max and sum.
+
+// Splits whose loads are in flight together per thread: 16 in the merge
+// kernel; fewer where the merge runs at the end of a partial kernel, whose
+// register budget it shares.
+constexpr int kMergeBatch = 16;
+constexpr int kFusedMergeBatch = 8;
+
+struct MergeState {
+  float m;    // running max of the split LSEs (log2 domain)
+  float w;    // sum of 2^(lse_c - m)
+  float4 acc; // sum of 2^(lse_c - m) * o_c
+};
+
+__device__ __forceinline__ void merge_fold(MergeState &st, float lc, const float4 &o) {
+  // lc = -inf (a split that saw no key) contributes nothing
+  if (lc == -INFINITY) return;
+  if (lc > st.m) {
+    const float r = st.m == -INFINITY ? 0.0f : exp2f(st.m - lc);
+    st.w *= r;
+    st.acc.x *= r;
+    st.acc.y *= r;
+    st.acc.z *= r;
+    st.acc.w *= r;
+    st.m = lc;
+  }
+  const float e = exp2f(lc - st.m);
+  st.w += e;
+  st.acc.x += e * o.x;
+  st.acc.y += e * o.y;
+  st.acc.z += e * o.z;
+  st.acc.w += e * o.w;
+}
+
+__device__ __forceinline__ void merge_combine(MergeState &a, const MergeState &b) {
+  if (b.m == -INFINITY) return;
+  const float M = fmaxf(a.m, b.m);
+  const float ra = a.m == -INFINITY ? 0.0f : exp2f(a.m - M);
+  const float rb = exp2f(b.m - M);
+  a.w = a.w * ra + b.w * rb;
+  a.acc.x = a.acc.x * ra + b.acc.x * rb;
+  a.acc.y = a.acc.y * ra + b.acc.y * rb;
+  a.acc.z = a.acc.z * ra + b.acc.z * rb;
+  a.acc.w = a.acc.w * ra + b.acc.w * rb;
+  a.m = M;
+}
+
+// Fold splits tg, tg + step, ... (< nb) of one float4 of outputs: their LSEs
+// at lp[c * lstride] and partials at op[c * ostride], NB loads of each in
+// flight at a time.
+// COHERENT: read with load_partial (the merge inside the partial kernel, which
+// may read partials other XCDs wrote in the same launch); otherwise plain
+// loads (the merge kernel, after the partial kernel has ended).
+template <int NB, bool COHERENT>
+__device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *lp, size_t lstride,
+                                                  const float4 *op, size_t ostride, int tg, int step, int nb) {
+  for (int c0 = tg; c0 < nb; c0 += step * NB) {
+    float lc[NB];
+    float4 v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int c = c0 + u * step;
+      if (c < nb) {
+        if constexpr (COHERENT) {
+          const float *o = reinterpret_cast<const float *>(op + (size_t)c * ostride);
+          lc[u] = load_partial(lp + (size_t)c * lstride);
+          v[u] = make_float4(load_partial(o), load_partial(o + 1), load_partial(o + 2), load_partial(o + 3));
+        } else {
+          lc[u] = lp[(size_t)c * lstride];
+          v[u] = op[(size_t)c * ostride];
+        }
+      } else {
+        lc[u] = -INFINITY;
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) merge_fold(st, lc[u], v[u]);
+  }
+}
+
+// Final output of one merged float4 (dims d .. d + 3 of query row / head
+// (row, hq)), and its lse from the thread that holds dim 0.
+__device__ __forceinline__ void merge_store(const Params &p, const MergeState &st, int row, int hq, int D, int d) {
+  const float inv = st.w > 0.0f ? 1.0f / st.w : 0.0f;
+  const float4 o = make_float4(st.acc.x * inv, st.acc.y * inv, st.acc.z * inv, st.acc.w * inv);
+  const size_t off = ((size_t)row * p.num_qo_heads + hq) * D + d;
+  if (p.out_bf16) {
+    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
+        make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+  } else {
+    *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + off) = o;
+  }
+  if (d == 0 && p.lse)
+    p.lse[(size_t)row * p.num_qo_heads + hq] = st.m == -INFINITY ? -INFINITY : (st.m + __log2f(st.w)) * kLn2;
+}
+
+// Merge every split of request b for column groups cg_first .. cg_first +
+// ncg - 1 of KV-head pack kvg (its splits are work items first .. first + nb
+// - 1) and write the final outputs.  The whole workgroup calls it; s_st holds
+// kThreads states of LDS.  When the outputs are fewer than the threads,
+// thread groups share the splits of each output and combine through LDS.
+template <int D, int NB>
+__device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int ncg, int first, int nb,
+                             MergeState *s_st) {
+  constexpr int D4 = D / 4;
+  const int tid = threadIdx.x;
+  const int cols = p.cols;
+  const int ncg_live = min(ncg, p.col_groups - cg_first);
+  const int F = ncg_live * cols * D4;                // float4 outputs
+  const int SG = F >= kThreads ? 1 : kThreads / F;  // thread groups over the splits
+  const size_t ostride = (size_t)cols * D4;         // float4 between consecutive splits of one slot
+  for (int f0 = 0; f0 < F; f0 += kThreads) {
+    const int t = f0 + (SG > 1 ? tid % F : tid);
+    const int tg = SG > 1 ? tid / F : 0;
+    const int cgi = t / (cols * D4);
+    const int h = (t / D4) % cols;
+    const int d = 4 * (t % D4);
+    int row = 0, hq = 0;
+    const bool has = t < F && tg < SG && column_target(p, b, kvg, cg_first + cgi, h, row, hq);
+    MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (has) {
+      const size_t slot0 = ((size_t)kvg * p.col_groups + cg_first + cgi) * p.items + first;
+      const float4 *op = reinterpret_cast<const float4 *>(p.o_part) + (slot0 * cols + h) * D4 + d / 4;
+      merge_fold_splits<NB, true>(st, p.lse_part + slot0 * cols + h, cols, op, ostride, tg, SG, nb);
+    }
+    if (SG > 1) { // one pass only (F < kThreads): the barriers are uniform
+      s_st[tid] = st;
+      __syncthreads();
+      if (tid < F)
+        for (int j = 1; j < SG; ++j) merge_combine(st, s_st[tid + j * F]);
+    }
+    if (has && tg == 0) merge_store(p, st, row, hq, D, d);
+  }
+}
+
+// End of a partial workgroup whose request has several splits: count its
+// arrival for (grid.y slot `yslot`, request b); the workgroup that brings the
+// last split merges them all (merge_splits) and resets the counter, so no
+// second kernel runs and no workgroup ever waits for another.  Every thread's
+// partial stores (store_partial: written through to the device-coherent
+// level) have completed before the count, and the merging workgroup reads
+// them back with load_partial after it.
+// Call with the whole workgroup, after the partial stores; `lds` (at least
+// kThreads MergeStates) may be any LDS no thread still reads.  NB: loads in
+// flight per thread during the merge (fewer where registers are tight).
+template <int D, int NB = kFusedMergeBatch>
+__device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, int kvg, int cg_first, int ncg,
+                                             int item, int split, int nb, void *lds) {
+  __shared__ int s_last;
+  if (nb <= 1 || !p.counters) return; // the same in every thread
+  wait_all_vmem(); // this thread's partial stores have completed
+  __syncthreads();
+  unsigned *ctr = p.counters + (size_t)yslot * p.batch + b;
+  if (threadIdx.x == 0) s_last = atomicAdd(ctr, 1u) == (unsigned)(nb - 1);
+  __syncthreads();
+  if (!s_last) return;
+  merge_splits<D, NB>(p, b, kvg, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
+  if (threadIdx.x == 0) atomicExch(ctr, 0u); // every split of this call has arrived: ready for the next call
 }
 
 } // namespace kvs

@@ -484,8 +484,8 @@ __device__ __forceinline__ bool locate_item(const Params &p, const InlineWork &w
                                             int *s_scan, int *s_item, int &b, int &split, int &nb, int &L) {
   if (w.n_items > 0) { // planned on the host
     const uint32_t e = w.item[item];
-    b = (int)(e >> 16);
-    split = (int)(e & 0xFFFF);
+    b = (int)(e >> 8);
+    split = (int)(e & 0xFF);
     L = w.req_len[b];
     nb = num_splits(L, req_nq(p, b), p.window, p.chunk);
     return true;

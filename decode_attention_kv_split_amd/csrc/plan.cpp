@@ -10,7 +10,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(0, L - nq + 1 - window) : 0; }
 
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int head_dim, int forced_chunk, int num_cus, Plan *out) {
+               int col_blocks, int pack, int head_dim, int forced_chunk, int num_cus, Plan *out) {
   Plan pl;
   // span of request b: from its first 16-aligned visible tile to its last key
   int64_t total = 0;
@@ -47,16 +47,33 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
   pl.needs_merge = max_splits > 1;
   if (pl.needs_merge) {
     const size_t slots = (size_t)items * num_kv_heads * cols;
+    // the counter area is always reserved, so a workspace shared by fused and
+    // two-kernel calls keeps its counters zero
+    pl.counter_bytes = kPlanCounterBytes;
     pl.o_part_bytes = align256(slots * head_dim * sizeof(float));
     pl.lse_part_bytes = align256(slots * sizeof(float));
     pl.meta_bytes = align256((size_t)batch * 2 * sizeof(int));
+    // one counter per (KV head, column block, request) at most (packing two
+    // KV heads per workgroup halves it)
+    const int64_t counters = (int64_t)num_kv_heads * col_blocks * batch;
+    pl.fused = plan_inline(batch, (int)items, max_splits) &&
+               counters * (int64_t)sizeof(unsigned) <= (int64_t)kPlanCounterBytes;
+    // The merge inside the partial kernel costs every split workgroup a wait
+    // for its partial stores and a counter round trip before it exits, and
+    // one workgroup folds all splits of a request.  Measured on MI355X it
+    // pays only where a second launch is the larger cost: launches of at most
+    // one workgroup per CU whose requests have few splits (a 512-key fp32 MHA
+    // decode: 9.1 against 10.5 us per step; a 32k-key MHA decode, 2048
+    // workgroups: 95 against 88 us; 128 splits of one request: 43 against 17 us).
+    const int64_t wgs = items * (int64_t)(num_kv_heads / std::max(1, pack)) * col_blocks;
+    pl.fused_pays = pl.fused && wgs <= std::max(1, num_cus) && max_splits <= 8;
   }
-  pl.workspace_bytes = pl.o_part_bytes + pl.lse_part_bytes + pl.meta_bytes;
+  pl.workspace_bytes = pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes + pl.meta_bytes;
   *out = pl;
   return true;
 }
 
-void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint32_t *items,
+void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint16_t *items,
                uint32_t *merge_req, uint32_t *merge_first, int *n_merges) {
   int x = 0, m = 0;
   for (int b = 0; b < batch; ++b) {
@@ -69,7 +86,7 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
       merge_first[m] = (uint32_t)x;
       ++m;
     }
-    for (int s = 0; s < n; ++s) items[x++] = ((uint32_t)b << 16) | (uint32_t)s;
+    for (int s = 0; s < n; ++s) items[x++] = (uint16_t)((b << 8) | s);
   }
   if (n_merges) *n_merges = m;
 }

@@ -7,11 +7,25 @@
 
 namespace kvs {
 
+// Work lists travel in the kernel arguments up to these sizes (kvs_device.h
+// InlineWork); merge counters fill at most kPlanCounterBytes at the start of
+// the workspace (kvs_device.h kCounterBytes).
+constexpr int kPlanInlineRequests = 256;
+constexpr int kPlanInlineSplits = 256;
+constexpr int kPlanInlineItems = 1344;
+constexpr size_t kPlanCounterBytes = 65536;
+
 struct Plan {
   int chunk = 0;        // tokens per split (multiple of 16)
   int items = 0;        // work items per KV head (sum of splits)
   int max_splits = 0;
   bool needs_merge = false;
+  // The partial kernel merges the splits itself (the workgroup that writes a
+  // request's last split merges them): the work list is planned on the host
+  // and the arrival counters fit their area.  Otherwise a second kernel merges.
+  bool fused = false;
+  bool fused_pays = false;  // auto mode takes the in-kernel merge (see make_plan)
+  size_t counter_bytes = 0; // arrival counters at the start of the workspace (zero between calls)
   size_t o_part_bytes = 0;
   size_t lse_part_bytes = 0;
   size_t meta_bytes = 0;
@@ -32,21 +46,28 @@ constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
 // its tiles in one register, one per lane).
 constexpr int kMaxChunk = 4096;
 
+// Whether a plan's work list travels in the kernel arguments (InlineWork).
+inline bool plan_inline(int batch, int items, int max_splits) {
+  return batch <= kPlanInlineRequests && items <= kPlanInlineItems && max_splits <= kPlanInlineSplits;
+}
+
 // Host copies of the device work lists for a plan (see InlineWork /
-// InlineMerge): items[x] = (request << 16) | split for the items of one KV
-// head in device order; merges = (request << 16) | splits and the request's
-// first item, for requests with more than one split.
+// InlineMerge): items[x] = (request << 8) | split for the items of one KV
+// head in device order (the plan must be inline); merges = (request << 16) |
+// splits and the request's first item, for requests with more than one split.
 // nq: query rows per request (null: one each); a request's keys start at the
 // first key its first query sees.
-void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint32_t *items,
+void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, int chunk, uint16_t *items,
                uint32_t *merge_req, uint32_t *merge_first, int *n_merges);
 
 // kv_len: host lengths [batch]; nq: query rows per request or null (one
 // each); cols: partial-result columns per KV head over all column groups
 // (the group size with one query per request, col_groups * 16 with
-// several); col_blocks: partial workgroups per (item, KV head).  Returns
-// false if a length is negative.
+// several); col_blocks: partial workgroups per (item, KV head); pack: KV
+// heads per workgroup.  Returns
+// false if a length is negative.  Workspace layout when a request has several
+// splits: [counters][o_part][lse_part][meta].
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int head_dim, int forced_chunk, int num_cus, Plan *out);
+               int col_blocks, int pack, int head_dim, int forced_chunk, int num_cus, Plan *out);
 
 } // namespace kvs

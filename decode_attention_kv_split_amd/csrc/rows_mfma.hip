@@ -21,6 +21,9 @@ using namespace tiles;
 // through its column groups, and a second barrier frees the slot for the
 // block NBUF further on.  A wave's columns are its own, so it writes its
 // results with no merge across waves.
+// Whether the shared-tile kernel merges a request's splits itself.
+constexpr bool rows_merges_in_kernel(int D, int KT) { return !(D == 256 && KT == DT_INT4); }
+
 template <int D, int KT, int NBUF, int CG>
 __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, const InlineWork w) {
   using S = Shape<D, KT>;
@@ -218,11 +221,15 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
       for (int wt = 0; wt < S::kOTiles; ++wt) {
         const int od = out_dim<D, KT>(wt, q4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[od + r * S::kOutStride] = (cs.acc[c][wt][r] - voff) * inv;
+        for (int r = 0; r < 4; ++r) store_partial(dst + od + r * S::kOutStride, (cs.acc[c][wt][r] - voff) * inv);
       }
-      if (q4 == 0) p.lse_part[slot * p.cols + c16] = lse2;
+      if (q4 == 0) store_partial(p.lse_part + slot * p.cols + c16, lse2);
     }
   }
+  // INT4 at head_dim 256 sits at the register limit, and the merge code would
+  // cost it half its occupancy: the host leaves its merge to the merge kernel
+  if constexpr (rows_merges_in_kernel(D, KT))
+    finish_split<D>(p, kvg * row_blocks + ord.rb, b, kvg, cgw, kGroups, item, split, nb, smem);
 }
 
 // Four 8-bit transposing reads (ds_read_b64_tr_b8, layout as for
@@ -745,6 +752,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   }
 
   // ---- this lane's column: final output, or the split's partial ----
+  [&] {
   if (!wave_on) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!ok) return;
@@ -782,15 +790,15 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
           *reinterpret_cast<uint4 *>(orow + d0) = make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]),
                                                              pack_bf16x2(o8[4], o8[5]), pack_bf16x2(o8[6], o8[7]));
         } else {
-          *reinterpret_cast<float4 *>(dst + d0) = make_float4(o8[0], o8[1], o8[2], o8[3]);
-          *reinterpret_cast<float4 *>(dst + d0 + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
+          store_partial4(dst + d0, o8[0], o8[1], o8[2], o8[3]);
+          store_partial4(dst + d0 + 4, o8[4], o8[5], o8[6], o8[7]);
         }
       }
     if (h2 == 0) {
       if (nb == 1) {
         if (p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
       } else {
-        p.lse_part[slot * p.cols + col % 16] = lse2;
+        store_partial(p.lse_part + slot * p.cols + col % 16, lse2);
       }
     }
     return;
@@ -816,11 +824,13 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d0 = 128 * dh + 32 * sl + 8 * q + 4 * h2;
-        *reinterpret_cast<float4 *>(dst + d0) =
-            make_float4(acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv, acc[sl][4 * q + 3] * inv);
+        store_partial4(dst + d0, acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv,
+                       acc[sl][4 * q + 3] * inv);
       }
-    if (h2 == 0 && dh == 0) p.lse_part[slot * p.cols + col % 16] = lse2;
+    if (h2 == 0 && dh == 0) store_partial(p.lse_part + slot * p.cols + col % 16, lse2);
   }
+  }();
+  finish_split<D>(p, kvg * row_blocks + ord.rb, b, kvg, cgw, kGroups, item, split, nb, smem);
 }
 
 // Two column groups (17 to 32 (query row, head) columns per KV head: a few
@@ -1254,6 +1264,7 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
     __syncthreads();
     merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
+  finish_split<D>(p, blockIdx.y, b, kvg, cg0, 2, item, split, nb, smem);
 }
 
 // Column groups one wave of the shared-tile kernel computes: two for
@@ -1323,6 +1334,8 @@ hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, cons
   if (kv_type == DT_INT4) return launch_kernel(l, partial_cols32_kernel<DT_INT4, 4>, grid, p, w);
   return hipErrorInvalidValue;
 }
+
+bool rows_merge_in_kernel(int head_dim, int kv_type) { return rows_merges_in_kernel(head_dim, kv_type); }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
   if (kv_type == DT_INT4) {

@@ -31,9 +31,10 @@
  * Computation: the visible keys of each (request, KV head) are cut into
  * chunks of kv_chunk tokens; one workgroup computes the partial softmax of a
  * chunk (fp32 running max / sum / accumulator) for all query heads of the
- * group; a second kernel merges the chunks of each request by log-sum-exp.
- * A request whose keys fit in one chunk is written directly by the first
- * kernel.
+ * group; the chunks of each request are merged by log-sum-exp, by the
+ * workgroup that finishes the request's last chunk (or, for work lists
+ * derived on the device, by a second kernel).  A request whose keys fit in
+ * one chunk is written directly by its workgroup.
  *
  * Threading / streams: every call is asynchronous on the given stream and
  * never synchronises.  The library keeps no pointer after returning and
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 9
+#define KVS_ABI_VERSION 10
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -174,7 +175,16 @@ typedef struct {
    * kernels; combines with windows, several query rows and the unified max
    * (give unified_max in capped units, at most c). */
   float logits_soft_cap;
+
+  /* where the splits of a request are merged: KVS_MERGE_AUTO chooses; KVS_MERGE_IN_PARTIAL
+   * asks for the merge inside the partial kernel (the workgroup that finishes a
+   * request's last split merges them; used when the work list is planned on the
+   * host and the counters fit, else the merge kernel runs); KVS_MERGE_KERNEL
+   * asks for the second kernel. */
+  int32_t merge_mode;
 } kvs_decode_args;
+
+enum { KVS_MERGE_AUTO = 0, KVS_MERGE_IN_PARTIAL = 1, KVS_MERGE_KERNEL = 2 };
 
 /* What a call will launch, computed on the host from kv_len_host. */
 typedef struct {
@@ -191,6 +201,8 @@ typedef struct {
   int32_t col_share;         /* column groups one partial workgroup computes: 1 (one query per
                                 request), 2, or 4 / 8 (several rows per request on the
                                 shared-tile kernel, partial_rows_kernel) */
+  int32_t merge_in_partial;  /* 1: the partial kernel merges the splits itself (one launch);
+                                0: a second kernel merges them (or nothing needs merging) */
 } kvs_plan_info;
 
 /* Plan a call without launching anything.  Makes no HIP call when
@@ -204,10 +216,20 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out);
  * arguments).  Same HIP-call rule as kvs_decode_plan. */
 size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
 
+/* Bytes at the start of every workspace that hold merge counters. */
+#define KVS_WORKSPACE_COUNTER_BYTES ((size_t)65536)
+
 /* Run one decode-attention step asynchronously on `stream`.
  * workspace: device memory, 256-byte aligned, at least
- * kvs_decode_workspace_bytes(args) bytes; holds the per-split partial
- * outputs (fp32) and their log-sum-exp values.  It needs no initialisation.
+ * kvs_decode_workspace_bytes(args) bytes (0 when no request needs more than
+ * one split).  Its first KVS_WORKSPACE_COUNTER_BYTES hold arrival counters:
+ * they must be zero before the first call that uses the workspace (allocate
+ * it zeroed), and every call leaves them zero.  With the work list planned
+ * on the host (batch <= 256, at most 448 splits per KV head) the workgroup
+ * that writes a request's last split merges all of its splits (one launch;
+ * no workgroup waits for another); otherwise a second kernel merges.  The
+ * rest of the workspace holds the per-split partial outputs (fp32) and their
+ * log-sum-exp values, rewritten by every call.
  * Preconditions that are not checked (they would need a device sync):
  * kv_len equals kv_len_host, page_indptr[b+1] - page_indptr[b] >=
  * ceil(kv_len[b] / page_size), every page id is < num_pages, and all

@@ -32,6 +32,7 @@ class SweepCase:
     algo: str
     unified_max: object  # None or float
     poison_invisible: bool
+    merge_mode: str = "auto"
 
     @property
     def multi(self) -> bool:
@@ -55,6 +56,8 @@ class SweepCase:
             parts.append(self.algo)
         if self.poison_invisible:
             parts.append("nan")
+        if self.merge_mode != "auto":
+            parts.append(f"merge-{self.merge_mode}")
         return "-".join(parts)
 
 
@@ -133,7 +136,9 @@ def draw_case(rng, index: int) -> SweepCase:
     spec = DecodeSpec(f"sweep{index}", batch, g * hk, hk, d, P, kv, "f32" if kv == "f32" else "bf16", sm,
                       window=window, lengths=("list", [int(x) for x in lens]), qk_rmsnorm=qk_norm,
                       seed=SWEEP_SEED + index, q_len=q_len, soft_cap=cap)
-    return SweepCase(index, spec, int(chunk), algo, unified, poison_inv)
+    # where the splits merge, from a stream of its own (the other draws stay as they were)
+    merge = ["auto", "in_partial", "kernel"][int(np.random.default_rng([SWEEP_SEED, index]).integers(0, 3))]
+    return SweepCase(index, spec, int(chunk), algo, unified, poison_inv, merge)
 
 
 def sweep_cases(n: int = SWEEP_CASES, seed: int = SWEEP_SEED) -> List[SweepCase]:

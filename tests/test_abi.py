@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 9
-    assert re.search(r"#define KVS_ABI_VERSION 9\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 10
+    assert re.search(r"#define KVS_ABI_VERSION 10\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -247,7 +247,7 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
     if info.needs_merge:
         slots = info.items_per_kv_head * 2 * g
         want = (-(-slots * 128 * 4 // 256) * 256) + (-(-slots * 4 // 256) * 256) + (-(-len(lens) * 8 // 256) * 256)
-        assert info.workspace_bytes == want
+        assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want  # counters, then the partials
     else:
         assert info.workspace_bytes == 0
 
@@ -426,3 +426,61 @@ def test_noalloc_rejects_oversized_calls_before_any_hip_call(lib):
     assert kvs.kvs_decode_noalloc(a, 0) == kvs.KVS_ERR_INVALID_ARG
     assert re.search(r"#define KVS_NOALLOC_SCRATCH_BYTES \(\(size_t\)32 << 20\)", open(HEADER).read())
     assert kvs.KVS_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_merge_runs_in_the_partial_kernel_when_the_plan_allows(lib):
+    """Asked for (merge_mode IN_PARTIAL), the partial kernel merges for
+    host-planned work lists whose counters fit; a second merge kernel runs
+    otherwise."""
+    real = globals()["_args"]
+
+    def _args(**kw):  # noqa: F811 (this test asks for the in-kernel merge)
+        a, keep = real(**kw)
+        a.merge_mode = kvs.KVS_MERGE_IN_PARTIAL
+        return a, keep
+
+    a, keep = _args(ptrs=False)                                    # 2 requests, split
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge and info.merge_in_partial == 1
+    assert info.workspace_bytes >= kvs.KVS_WORKSPACE_COUNTER_BYTES
+    a, keep = _args(ptrs=False, lens=(10, 20))                     # nothing to merge: no workspace
+    info = kvs.kvs_decode_plan(a)
+    assert not info.needs_merge and info.merge_in_partial == 0 and info.workspace_bytes == 0
+    a, keep = _args(ptrs=False, batch=300, lens=(700,) * 300, num_pages=20000, chunk=64)  # device work list
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 0
+    a, keep = _args(ptrs=False, batch=1, lens=(8192,), chunk=16, num_pages=600)  # 512 splits > 256
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 0
+    a, keep = _args(ptrs=False, batch=200, lens=(650,) * 200, chunk=128, num_pages=9000)  # 1200 items: inline
+    assert kvs.kvs_decode_plan(a).items_per_kv_head == 1200 and kvs.kvs_decode_plan(a).merge_in_partial == 1
+    a, keep = _args(ptrs=False, batch=250, lens=(1000,) * 250, chunk=128, num_pages=16000)  # 2000 items > 1344
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 0
+    # 200 requests x 128 KV heads = 25,600 counters > 16,384
+    a, keep = _args(ptrs=False, batch=200, Hq=128, Hk=128, d=64, lens=(32,) * 200, chunk=16, num_pages=1000)
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge and info.merge_in_partial == 0
+    # the INT4 head_dim-256 shared-tile kernel leaves its merge to the merge kernel
+    a, keep = _args(ptrs=False, kv=kvs.KVS_INT4, d=256, lens=(700, 1500), chunk=256)
+    rows = np.array([0, 40, 80], np.int32)
+    a.qo_indptr_host = rows.ctypes.data
+    info = kvs.kvs_decode_plan(a)
+    assert info.col_share >= 4 and info.needs_merge and info.merge_in_partial == 0
+    a.kv_dtype = kvs.KVS_BF16                                      # the bf16 one merges itself
+    info = kvs.kvs_decode_plan(a)
+    assert info.col_share >= 4 and info.merge_in_partial == 1
+
+
+def test_merge_mode_auto_and_kernel(lib):
+    """AUTO merges inside the partial kernel only for launches of at most one
+    workgroup per CU (there a second launch costs more than the merge);
+    KERNEL always takes the merge kernel; other values are rejected."""
+    a, keep = _args(ptrs=False, batch=1, P=0, Hq=8, Hk=8, d=64, q=kvs.KVS_F32, kv=kvs.KVS_F32,
+                    lens=(512,), num_pages=512)                    # 8 chunks x 8 heads = 64 workgroups
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 1
+    a.merge_mode = kvs.KVS_MERGE_KERNEL
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 0
+    a, keep = _args(ptrs=False, batch=1, P=0, Hq=32, Hk=32, lens=(32768,), num_pages=32768)  # 2048 workgroups
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 0
+    a.merge_mode = kvs.KVS_MERGE_IN_PARTIAL
+    assert kvs.kvs_decode_plan(a).merge_in_partial == 1
+    a.merge_mode = 3
+    assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG

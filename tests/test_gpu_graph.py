@@ -53,7 +53,7 @@ def test_graph_replays_match_eager(name, q_len):
                              page_indices=t.get("page_indices"), kv_len_host=inp.kv_len,
                              k_scale=t.get("k_scale"), v_scale=t.get("v_scale"), sm_scale=spec.sm_scale,
                              window=spec.window, qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr)
-    ws = torch.empty(max(1, kvs.kvs_decode_workspace_bytes(a)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(1, kvs.kvs_decode_workspace_bytes(a)), dtype=torch.uint8, device=dev)  # counters start at zero
     shape_o = (rows, spec.num_qo_heads, spec.head_dim)
     o_e = torch.empty(shape_o, dtype=o_dtype, device=dev)
     lse_e = torch.empty((rows, spec.num_qo_heads), dtype=torch.float32, device=dev)

@@ -149,8 +149,8 @@ def test_rows_large_batch_device_planned(q_len):
 
 
 def test_rows_many_items_device_planned():
-    """More than 448 work items per KV head (16-token chunks of an 8192-key
-    request) with 40 and 3 new rows."""
+    """More than 256 splits of one request (16-token chunks of an 8192-key
+    request: the device-side work list) with 40 and 3 new rows."""
     print("case multi many items", flush=True)
     spec = DecodeSpec("itemsrows", 2, 8, 2, 128, 16, "bf16", "bf16", 0.1, lengths=("list", [8192, 300]),
                       q_len=("list", [40, 3]), seed=42)

@@ -225,7 +225,7 @@ def test_lse_output_optional_and_stream():
                             page_indices=t["page_indices"], kv_len_host=inp.kv_len, sm_scale=spec.sm_scale)
     a.lse = None
     s = torch.cuda.Stream()
-    ws = torch.empty(max(kvs.kvs_decode_workspace_bytes(a), 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(kvs.kvs_decode_workspace_bytes(a), 256), dtype=torch.uint8, device="cuda")  # counters start at zero
     assert kvs.kvs_decode(a, ws.data_ptr(), ws.numel(), s.cuda_stream) == kvs.KVS_OK
     s.synchronize()
     o_ref, lse_ref = oracle.decode_reference(inp)
@@ -279,7 +279,8 @@ def test_large_batch_device_planned(kv):
 
 
 def test_many_items_device_planned():
-    """More than 448 work items per KV head (small forced chunks)."""
+    """More than 256 splits of one request (16-key chunks of an 8192-key
+    request): the work list comes from kv_len on the device."""
     print("case many items", flush=True)
     spec = DecodeSpec("items", 2, 8, 2, 128, 16, "bf16", "bf16", 0.1, lengths=("list", [8192, 300]), seed=32)
     inp = make_inputs(spec, poison=True)

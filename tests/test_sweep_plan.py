@@ -24,6 +24,7 @@ def test_sweep_is_seeded_and_varied():
     assert sum(c.spec.window > 0 for c in a) > 30 and sum(c.spec.soft_cap > 0 for c in a) > 20
     assert sum(c.unified_max is not None for c in a) > 10 and sum(c.kv_chunk > 0 for c in a) > 50
     assert {c.algo for c in a} == {"auto", "valu", "mfma_packed"}
+    assert {c.merge_mode for c in a} == {"auto", "in_partial", "kernel"}
 
 
 @pytest.mark.parametrize("case", sweep_cases(), ids=lambda c: c.label())
@@ -54,5 +55,6 @@ def test_sweep_case_plans(lib, case):
     if case.unified_max is not None:
         a.use_unified_max, a.unified_max = 1, case.unified_max
     a.logits_soft_cap = s.soft_cap
+    a.merge_mode = {"auto": 0, "in_partial": 1, "kernel": 2}[case.merge_mode]
     info = kvs.kvs_decode_plan(a)  # raises on any status but KVS_OK
     assert info.items_per_kv_head >= s.batch

@@ -27,7 +27,7 @@ def _both(inp, kv_chunk):
     assert plan.needs_merge and 0 < plan.workspace_bytes <= kvs.KVS_NOALLOC_SCRATCH_BYTES
     assert kvs.kvs_decode_noalloc(a1, stream) == kvs.KVS_OK
     a2, keep2 = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], **common)
-    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")  # counters start at zero
     assert kvs.kvs_decode(a2, ws.data_ptr(), ws.numel(), stream) == kvs.KVS_OK
     torch.cuda.synchronize()
     (o1, l1), (o2, l2) = keep1[1:3], keep2[1:3]
