@@ -49,12 +49,24 @@ constexpr float kLazy = 8.0f;
 // tile max is moved down to it.
 constexpr float kDrop = 64.0f;
 
-// XOR swizzle of the 16-byte pieces of staged row r: the 16 rows a matrix
-// operand reads at the same logical piece land in distinct LDS banks.
+// XOR swizzle of the 16-byte pieces of staged row r.  gfx950's LDS has 64
+// banks of 4 bytes: rows of 256 bytes or more all start in bank 0, rows of
+// 128 bytes alternate between the two bank halves, so rows with the same
+// u = r / kRowsPerBankPeriod collide.  u -> u ^ ((u & 3) << s) permutes the
+// piece index bits, so
+//   * the 16 rows a K operand read takes at one logical piece land on 16
+//     distinct pieces (conflict-free 16-byte reads), and
+//   * four consecutive u, which a transposing V^T read takes at one aligned
+//     group of 2^s pieces (four 16-bit rows x four pieces, s = 2; four 8-bit
+//     row pairs x two pieces, s = 1), land in four different groups.
+// With the plain swizzle u ^ piece the four rows stayed inside one group:
+// every 16-bit transposing read of a 256-byte row was a four-way conflict.
 template <int DE, int KT>
 __device__ __forceinline__ int stage_swizzle(int r) {
   using S = Shape<DE, KT>;
-  return (r / S::kRowsPerBankPeriod) & (S::kPieces - 1);
+  constexpr int kShift = S::kRowsPerBankPeriod == 1 ? 2 : 1;
+  const int u = r / S::kRowsPerBankPeriod;
+  return (u ^ ((u & 3) << kShift)) & (S::kPieces - 1);
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
