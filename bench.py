@@ -352,7 +352,7 @@ def graph_steps(a, ws, steps: int) -> float:
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
         q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0, graph: bool = False, probe: bool = True,
-        merge_mode: str = "auto") -> dict:
+        merge_mode: str = "auto", wave_split: str = "auto", pool_offset: int = 0) -> dict:
     import dataclasses
 
     import torch
@@ -374,6 +374,16 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
     t_gen = time.perf_counter()
     inp = make_inputs(spec)
     t = to_torch(inp)
+    if pool_offset:
+        # the K and V pools placed pool_offset bytes past the start of their allocations
+        for name in ("k", "v"):
+            x = t[name]
+            nb = x.numel() * x.element_size()
+            buf = torch.empty(nb + pool_offset, dtype=torch.uint8, device=x.device)
+            y = buf[pool_offset:pool_offset + nb].view(x.dtype).view(x.shape)
+            y.copy_(x)
+            t[name] = y
+            t[name + "_buf"] = buf
     t_gen = time.perf_counter() - t_gen
     s = spec
     a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
@@ -382,7 +392,7 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
                             window=s.window, kv_chunk=kv_chunk, algo=algo, unified_max=unified_max,
                             kv_dtype="int4" if s.kv_dtype == "int4" else None,
                             qo_indptr=t.get("qo_indptr"), qo_indptr_host=inp.qo_indptr,
-                            logits_soft_cap=spec.soft_cap, merge_mode=merge_mode)
+                            logits_soft_cap=spec.soft_cap, merge_mode=merge_mode, wave_split=wave_split)
     plan = kvs.kvs_decode_plan(a)
     ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")  # merge counters start at zero
     stream = torch.cuda.current_stream().cuda_stream
@@ -452,9 +462,14 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             "head_dim": s.head_dim, "page_size": s.page_size, "window": s.window, "kv_dtype": s.kv_dtype,
             "sum_kv_len": int(inp.kv_len.sum()), "seed": s.seed,
             "kv_chunk": plan.kv_chunk, "items_per_kv_head": plan.items_per_kv_head,
-            "max_splits": plan.max_splits, "merge_in_partial": plan.merge_in_partial, "parallelism": "single GPU",
+            "max_splits": plan.max_splits, "merge_in_partial": plan.merge_in_partial,
+            "kv_head_packs_per_workgroup": plan.wave_packs, "parallelism": "single GPU",
             "unified_max": unified_max, "q_len": q_len, "soft_cap": spec.soft_cap,
             "kv_len_override": kv_len or None,
+            # where the pools sit (a 2 MiB page holds the start of each)
+            "kv_pools": {"k_addr": hex(t["k"].data_ptr()), "v_addr": hex(t["v"].data_ptr()),
+                         "k_mod_2MiB": t["k"].data_ptr() % (2 << 20), "v_mod_2MiB": t["v"].data_ptr() % (2 << 20),
+                         "offset": pool_offset},
         },
         "roofline": {
             "bound": "hbm",
@@ -466,7 +481,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
             # the counters were taken in the default configuration of each workload
             "traffic": (measured_traffic(config_name, kernel)
                         if q_len == 1 and not soft_cap and not kv_len and not kv_chunk and algo == "auto"
-                        and merge_mode == "auto" and unified_max is None else None),
+                        and merge_mode == "auto" and wave_split == "auto" and unified_max is None and not pool_offset
+                        else None),
             "kernel_us": round(part_avg * 1e3, 2),
             "kernel_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
             "kernel_launches_timed": n_samples,
@@ -504,7 +520,8 @@ def summary(rec: dict) -> dict:
             "pct_of_peak": rec["pct_of_peak"], "dtype": rec["dtype"],
             "config": {k: c[k] for k in ("batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size",
                                          "kv_dtype", "sum_kv_len", "seed", "kv_chunk", "items_per_kv_head",
-                                         "max_splits")},
+                                         "max_splits", "merge_in_partial", "kv_head_packs_per_workgroup",
+                                         "kv_pools")},
             "roofline": {k: r[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac", "traffic",
                                            "kernel_us", "kernel_us_p10_p50_p90", "algorithmic_bytes")}}
 
@@ -649,6 +666,11 @@ def main():
     ap.add_argument("--merge", default="auto", choices=["auto", "in_partial", "kernel"],
                     help="where split partials are merged: chosen by the planner, inside the partial kernel, "
                          "or by a second kernel")
+    ap.add_argument("--waves", default="auto", choices=["auto", "heads", "tiles"],
+                    help="how a matrix-core decode workgroup's four waves share work: one KV-head pack each "
+                         "over the whole chunk, or one pack's tiles")
+    ap.add_argument("--pool-offset", type=int, default=0, metavar="BYTES",
+                    help="place the K and V pools BYTES past the start of their allocations (multiple of 256)")
     ap.add_argument("--unified-max", type=float, default=None,
                     help="start every chunk's softmax from this reference max (scaled-score units)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -685,11 +707,15 @@ def main():
                             algo=args.algo)
         print(json.dumps(res), flush=True)
         return
+    if args.pool_offset % 256 or args.pool_offset < 0:
+        sys.exit("--pool-offset must be a non-negative multiple of 256")
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
-              soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph, merge_mode=args.merge)
-    plain = (args.merge == "auto" and args.algo == "auto" and args.kv_chunk == 0 and args.unified_max is None and args.q_len == 1
-             and not args.soft_cap and not args.kv_len and not args.cold and not args.graph)
+              soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph, merge_mode=args.merge,
+              wave_split=args.waves, pool_offset=args.pool_offset)
+    plain = (args.merge == "auto" and args.waves == "auto" and args.algo == "auto" and args.kv_chunk == 0
+             and args.unified_max is None and args.q_len == 1 and not args.soft_cap and not args.kv_len
+             and not args.cold and not args.graph and not args.pool_offset)
     if name == DEFAULT and plain and not args.single:
         # the other two long-context / batched paged workloads of the 70%-of-peak
         # target, measured the same way in the same process

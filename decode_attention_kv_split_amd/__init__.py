@@ -31,6 +31,7 @@ __all__ = [
     "KVS_ERR_TOO_LARGE", "KVS_NOALLOC_SCRATCH_BYTES", "kvs_decode_noalloc", "KVS_WORKSPACE_COUNTER_BYTES",
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_INT4", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
     "KVS_ALGO_MFMA_PACKED", "KVS_MERGE_AUTO", "KVS_MERGE_IN_PARTIAL", "KVS_MERGE_KERNEL",
+    "KVS_WAVES_AUTO", "KVS_WAVES_HEADS", "KVS_WAVES_TILES",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
     "library_path", "load_library",
     "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_append", "kvs_status_string",
@@ -39,7 +40,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 10
+KVS_ABI_VERSION = 11
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_ERR_TOO_LARGE = -5
@@ -49,6 +50,8 @@ KVS_F32, KVS_BF16, KVS_FP8_E4M3, KVS_INT4 = 0, 1, 2, 3
 KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
 KVS_MERGE_AUTO, KVS_MERGE_IN_PARTIAL, KVS_MERGE_KERNEL = 0, 1, 2
 _MERGE_MODES = {"auto": KVS_MERGE_AUTO, "in_partial": KVS_MERGE_IN_PARTIAL, "kernel": KVS_MERGE_KERNEL}
+KVS_WAVES_AUTO, KVS_WAVES_HEADS, KVS_WAVES_TILES = 0, 1, 2
+_WAVE_SPLITS = {"auto": KVS_WAVES_AUTO, "heads": KVS_WAVES_HEADS, "tiles": KVS_WAVES_TILES}
 _ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +94,7 @@ class KvsDecodeArgs(ctypes.Structure):
         ("qo_indptr_host", ctypes.c_void_p),
         ("logits_soft_cap", ctypes.c_float),
         ("merge_mode", ctypes.c_int32),
+        ("wave_split", ctypes.c_int32),
     ]
 
 
@@ -106,6 +110,7 @@ class KvsPlanInfo(ctypes.Structure):
         ("col_groups", ctypes.c_int32),
         ("col_share", ctypes.c_int32),
         ("merge_in_partial", ctypes.c_int32),
+        ("wave_packs", ctypes.c_int32),
     ]
 
 
@@ -300,7 +305,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
               algo="auto", out=None, lse=None, num_cus: int = 0,
               unified_max: Optional[float] = None, kv_dtype: Optional[str] = None, qo_indptr=None,
               qo_indptr_host=None, logits_soft_cap: float = 0.0,
-              merge_mode="auto") -> Tuple[KvsDecodeArgs, object]:
+              merge_mode="auto", wave_split="auto") -> Tuple[KvsDecodeArgs, object]:
     """Build the C argument block from torch tensors.
 
     q: [batch, Hq, d]; k, v: contiguous [kv_len, Hk, d] (batch 1) or paged
@@ -309,6 +314,8 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
     packed nibbles.  qo_indptr (int32 [batch + 1] on the device, with a host
     copy) gives several query rows per request: q is then [total_q, Hq, d].
     logits_soft_cap c > 0 caps the scaled scores to c * tanh(s / c).
+    merge_mode: "auto" | "in_partial" | "kernel"; wave_split: "auto" |
+    "heads" | "tiles" (how a matrix-core workgroup's waves share its work).
     Returns (args, keepalive)."""
     import numpy as np
     import torch
@@ -390,6 +397,7 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
         a.qo_indptr, a.qo_indptr_host = _ptr(qo_indptr), qoh.ctypes.data
     a.logits_soft_cap = float(logits_soft_cap)
     a.merge_mode = _MERGE_MODES[merge_mode] if isinstance(merge_mode, str) else int(merge_mode)
+    a.wave_split = _WAVE_SPLITS[wave_split] if isinstance(wave_split, str) else int(wave_split)
     keep = (kvh, out, lse, qoh)
     return a, keep
 
@@ -397,7 +405,8 @@ def make_args(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_ho
 def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=None, k_scale=None,
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
            workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None,
-           qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0, merge_mode="auto"):
+           qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0, merge_mode="auto",
+           wave_split="auto"):
     """One decode-attention step on the current (or given) HIP stream.
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
@@ -406,7 +415,7 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
                         window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
                         kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host,
-                        logits_soft_cap=logits_soft_cap, merge_mode=merge_mode)
+                        logits_soft_cap=logits_soft_cap, merge_mode=merge_mode, wave_split=wave_split)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

@@ -75,6 +75,7 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   if (a->use_unified_max && !std::isfinite(a->unified_max)) return KVS_ERR_INVALID_ARG;
   if (!(a->logits_soft_cap >= 0.0f) || !std::isfinite(a->logits_soft_cap)) return KVS_ERR_INVALID_ARG;
   if (a->merge_mode < KVS_MERGE_AUTO || a->merge_mode > KVS_MERGE_KERNEL) return KVS_ERR_INVALID_ARG;
+  if (a->wave_split < KVS_WAVES_AUTO || a->wave_split > KVS_WAVES_TILES) return KVS_ERR_INVALID_ARG;
   for (int b = 0; b < a->batch; ++b) {
     const int L = a->kv_len_host[b];
     if (L < 0) return KVS_ERR_INVALID_ARG;
@@ -95,6 +96,8 @@ kvs_status validate(const kvs_decode_args *a, bool need_ptrs, int *algo) {
   }
   if (need_ptrs) {
     if (!a->q || !a->k || !a->v || !a->kv_len || !a->o) return KVS_ERR_INVALID_ARG;
+    // rows of q and o move in 16-byte pieces
+    if ((reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->o)) & 15) return KVS_ERR_INVALID_ARG;
     if (a->page_size > 0 && (!a->page_indptr || !a->page_indices)) return KVS_ERR_INVALID_ARG;
     if (scaled && (!a->k_scale || !a->v_scale)) return KVS_ERR_INVALID_ARG;
     if (multi && !a->qo_indptr) return KVS_ERR_INVALID_ARG;
@@ -222,6 +225,21 @@ int kv_pack(const kvs_decode_args *a, int algo) {
                         algo == KVS_ALGO_MFMA_PACKED);
 }
 
+// KV-head packs per matrix-core decode workgroup: 4 (one per wave, each over
+// the whole chunk) when asked for (KVS_WAVES_HEADS) and every request has one
+// query row and the packs come in fours; else 1 (the waves split one pack's
+// tiles), which is also the automatic choice: at the workgroup counts the
+// chunk heuristic aims for, the heads split needs chunks four times shorter,
+// and the extra split partials it writes cost more than its row-wise reads
+// gain (batch-64 bf16 378 against 365 us, batch-128 fp8 271 against 253 us).
+// -1: KVS_WAVES_HEADS asked for where it does not apply.
+int wave_packs_of(const kvs_decode_args *a, int algo, const Columns &c) {
+  if (a->wave_split != KVS_WAVES_HEADS) return 1;
+  const bool fits = algo != KVS_ALGO_VALU && !a->qo_indptr_host && c.col_groups == 1 &&
+                    (a->num_kv_heads / kv_pack(a, algo)) % kvs::kWaves == 0;
+  return fits ? kvs::kWaves : -1;
+}
+
 // Whether the partial kernel merges the splits itself: the plan allows it
 // (host work list, counters fit) and the kernel that runs has the merge
 // compiled in (the shared-tile kernel for INT4 at head_dim 256 does not).
@@ -239,8 +257,11 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   if (st != KVS_OK) return st;
   Columns c = columns_of(a);
   const int pack = kv_pack(a, *algo);
+  const int wave_packs = wave_packs_of(a, *algo, c);
+  if (wave_packs < 0) return KVS_ERR_UNSUPPORTED;
   if (!kvs::make_plan(a->kv_len_host, c.nq.empty() ? nullptr : c.nq.data(), a->batch, a->window,
-                      a->num_kv_heads, c.cols, c.col_blocks, pack, a->head_dim, a->kv_chunk, *cus, pl))
+                      a->num_kv_heads, c.cols, c.col_blocks, pack, wave_packs, a->head_dim, a->kv_chunk, *cus,
+                      pl))
     return KVS_ERR_INVALID_ARG;
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
   // (the merge runs one workgroup per column group)
@@ -330,6 +351,7 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   out->col_groups = c.col_groups;
   out->col_share = c.col_share;
   out->merge_in_partial = merges_in_partial(pl, args, c) ? 1 : 0;
+  out->wave_packs = wave_packs_of(args, algo, c);
   return KVS_OK;
 }
 
@@ -378,6 +400,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.col_groups = cols.col_groups;
   p.col_share = cols.col_share;
   p.cols = a->qo_indptr_host ? 16 : p.group * p.pack;
+  p.wave_packs = wave_packs_of(a, algo, cols);
   // The chunks of a request differ in work only when its query rows reach
   // over more than one chunk (the early rows stop before the late chunks);
   // only then do the multi-row kernels deal their workgroups to the XCDs by

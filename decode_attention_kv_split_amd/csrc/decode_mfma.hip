@@ -56,9 +56,17 @@ using namespace tiles;
 // more than one only with several query rows per request and one KV head per
 // workgroup.  The groups share the K operand and the V^T products, so K/V
 // are read once for all of them.
-template <int D, int PACK, int KT, int NBUF, int CG>
+// HEADS: each wave takes its own KV-head pack (packs 4 y .. 4 y + 3 for
+// blockIdx.y = y) over all tiles of the chunk, instead of a quarter of one
+// pack's tiles.  The four waves then stream four adjacent head slices of the
+// same token rows at the same time, so each 16-token page of the pool is read
+// as longer contiguous runs; on MI355X that streamed 6-13% faster (batch-64
+// bf16, batch-128 fp8 and INT4, 32k MHA), and each wave's state is already
+// its pack's whole chunk, so no cross-wave merge is needed.
+template <int D, int PACK, int KT, int NBUF, int CG, bool HEADS>
 __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, const InlineWork w) {
   static_assert(CG == 1 || PACK == 1, "column groups of (query row, head) pairs take one KV head");
+  static_assert(!HEADS || CG == 1, "one pack per wave: one column group");
   constexpr int DE = D * PACK;
   using S = Shape<DE, KT>;
   constexpr int OSTRIDE = D + 4;
@@ -84,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // that run all heads of an item together (on one XCD or spread over XCDs).
   const int item = blockIdx.x;
   const int col_blocks = (p.col_groups + CG - 1) / CG; // workgroups per (item, KV head pack)
-  const int kvg = blockIdx.y / col_blocks;             // KV heads kvg*PACK .. kvg*PACK+PACK-1
+  // KV heads kvg*PACK .. kvg*PACK+PACK-1
+  const int kvg = HEADS ? blockIdx.y * kWaves + wave : blockIdx.y / col_blocks;
   const int cg0 = blockIdx.y % col_blocks * CG;        // first column group (several queries per request)
   const int g = p.group;
   const int gp = g * PACK;    // query heads of the pack (<= 16)
@@ -114,7 +123,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // chunk does.  With one query per request this is the whole chunk.
   const int ft = w_hi > w_lo ? (w_lo - a0) / kTile : 0; // first tile, counted from the chunk start
   const int ntiles = w_hi > w_lo ? (w_hi - a0 + kTile - 1) / kTile - ft : 0;
-  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  // this wave's tiles: all of them (HEADS; chunks of at most 64 tiles) or
+  // every fourth, from the wave's index
+  const int my_tiles = HEADS ? min(ntiles, 64) : (ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0);
+  const int t_first = HEADS ? ft : ft + wave;    // tile i of the wave: t_first + i * t_step
+  const int t_step = HEADS ? 1 : kWaves;
   load_columns<D>(cs, p, q4, my_kv);
 
   float cscale = p.score_scale;
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   // them with v_readlane and never waits on memory for an address.
   uint32_t voff_lo = 0, voff_hi = 0, vbytes = 0;
   if (lane < my_tiles) {
-    const int ts = a0 + (ft + wave + lane * kWaves) * kTile;
+    const int ts = a0 + (t_first + lane * t_step) * kTile;
     const size_t row0 = paged ? (size_t)pages[ts >> pshift] * p.page_size + (ts & pmask) : (size_t)ts;
     const size_t off = row0 * row_bytes;
     voff_lo = (uint32_t)off;
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   auto read_stage = [&](TileRegs<DE, KT> &t, int slot) { stage.read(t, slot * 2 * S::kTileBytes); };
 
   auto compute = [&](TileRegs<DE, KT> t, int i) {
-    const int ts = a0 + (ft + wave + i * kWaves) * kTile;
+    const int ts = a0 + (t_first + i * t_step) * kTile;
     zero_v_before(t, ts, w_lo, c16, q4); // rows before the first key any column sees
     tile_update(cs, t, ts, all_lo, all_hi, cscale, cap_out, ident, q4);
   };
@@ -208,6 +221,92 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       }
     }
     wait_vmem<0>(); // no DMA may land in the staging area once it is reused
+  }
+  if constexpr (HEADS) {
+    // ---- one pack per wave: the wave's state is its pack's whole chunk.
+    // Each lane normalises its own dims into the wave's staging slots (free
+    // once its last DMA has landed; no other wave touches them), and the
+    // wave then stores whole output rows from there: written straight from
+    // the registers, every store instruction covered 16 rows in 64-byte
+    // pieces, and that cost batch-64 bf16 about 12% of its time ----
+    // dims in NP passes of DP when 16 padded rows of D floats exceed the slots
+    constexpr int kStage = NBUF * 2 * S::kTileBytes;
+    constexpr int NP = 16 * (D + 4) * 4 <= kStage ? 1 : 2;
+    constexpr int DP = D / NP;
+    constexpr int WS = DP + 4; // LDS row stride (floats) of a column
+    static_assert(16 * WS * 4 <= kStage, "a wave's output fits its staging slots");
+    float *wo = reinterpret_cast<float *>(wave_stage);
+    float l_tot = cs.l[0] + __shfl_xor(cs.l[0], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    float voff = 0.0f; // INT4: V entered the product as 136 + n (136 * the weights' sum)
+    if constexpr (KT == DT_INT4) {
+      float lb_tot = cs.lb[0] + __shfl_xor(cs.lb[0], 16, 64);
+      lb_tot += __shfl_xor(lb_tot, 32, 64);
+      voff = kInt4Offset * lb_tot;
+    }
+    const size_t slot = (size_t)kvg * p.items + item; // one column group
+    const bool live = l_tot > 0.0f;                   // else no visible key: o = 0, lse = -inf
+    float inv = 0.0f;
+    if (cs.ok[0]) {
+      const int hq = cs.head[0];
+      const float vscale = p.v_scale ? p.v_scale[b * Hk + hq / g] : 1.0f;
+      inv = live ? vscale / l_tot : 0.0f;
+      if (q4 == 0) {
+        const float lse2 = live ? cs.m[0] + __log2f(l_tot) : -INFINITY;
+        if (nb == 1) {
+          if (p.lse) p.lse[(size_t)cs.row[0] * p.num_qo_heads + hq] = lse2 * kLn2;
+        } else {
+          store_partial(p, p.lse_part + slot * p.cols + c16, lse2);
+        }
+      }
+    }
+    const int gp_live = min(gp, 16);
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+      if (ps > 0) { // the previous pass's reads are issued before these writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      if (cs.ok[0]) {
+#pragma unroll
+        for (int w = 0; w < S::kOTiles; ++w) {
+          const int od = out_dim<DE, KT>(w, q4);
+          const int d = od % D - ps * DP; // a slice's dims lie in one pass
+          if (od / D != my_kv || d < 0 || d >= DP) continue; // the pack's other KV head, or another pass
+          float *dst = wo + c16 * WS + d;
+          if constexpr (S::kOutStride == 1) {
+            *reinterpret_cast<float4 *>(dst) =
+                make_float4((cs.acc[0][w][0] - voff) * inv, (cs.acc[0][w][1] - voff) * inv,
+                            (cs.acc[0][w][2] - voff) * inv, (cs.acc[0][w][3] - voff) * inv);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[r * S::kOutStride] = (cs.acc[0][w][r] - voff) * inv;
+          }
+        }
+      }
+      // the reads below follow this wave's LDS writes (one wave's LDS
+      // accesses complete in order; the fences keep the compiler from
+      // moving them)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int f = lane; f < gp_live * (DP / 4); f += 64) { // float4 f: column f / (DP / 4)
+        const int h = f / (DP / 4);
+        const int dl = 4 * (f - h * (DP / 4));
+        const int d = ps * DP + dl;
+        const float4 v = *reinterpret_cast<const float4 *>(wo + h * WS + dl);
+        if (nb == 1) {
+          const size_t off = ((size_t)b * p.num_qo_heads + kvg * gp + h) * D + d; // bf16 q and o (matrix-core path)
+          *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        } else {
+          store_partial4(p, p.o_part + (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+        }
+      }
+    }
+    finish_split<D>(p, blockIdx.y, b, blockIdx.y * kWaves, 0, 1, item, split, nb, smem, kWaves);
+    return;
   }
   __syncthreads(); // staging area is reused for the per-wave states below
 
@@ -264,11 +363,18 @@ static hipError_t launch_mfma_d(const Params &p, const InlineWork &w, const Laun
   }
   if constexpr (PACK == 1 && D <= 128) {
     if (p.col_share == 2)
-      return launch_kernel(l, partial_mfma_kernel<D, 1, KT, NB, 2>,
+      return launch_kernel(l, partial_mfma_kernel<D, 1, KT, NB, 2, false>,
                            dim3(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2)), p, w);
   }
   if (p.col_share != 1) return hipErrorInvalidValue;
-  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB, 1>,
+  if (p.wave_packs == kWaves) { // one pack per wave (one query row per request)
+    if (p.qo_indptr || p.col_groups != 1 || p.num_kv_heads / PACK % kWaves != 0 || p.chunk > 64 * kTile)
+      return hipErrorInvalidValue;
+    return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB, 1, true>,
+                         dim3(p.items, p.num_kv_heads / PACK / kWaves), p, w);
+  }
+  if (p.wave_packs != 1) return hipErrorInvalidValue;
+  return launch_kernel(l, partial_mfma_kernel<D, PACK, KT, NB, 1, false>,
                        dim3(p.items, p.num_kv_heads / PACK * p.col_groups), p, w);
 }
 

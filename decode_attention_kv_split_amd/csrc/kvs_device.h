@@ -85,6 +85,8 @@ struct Params {
   int col_groups; // groups of 16 (query, head) columns per KV head (1 for one query)
   int col_share;  // column groups one partial workgroup computes together (1 or 2)
   int cols;       // columns per partial slot: group * pack (one query) or 16
+  int wave_packs; // KV-head packs per partial workgroup: 4 (one per wave, each over the
+                  // whole chunk) or 1 (the four waves split one pack's tiles)
   int rows_xcd_order; // multi-row kernels: workgroups in the XCD-balanced order (rows_order)
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
@@ -101,22 +103,35 @@ struct Params {
 // them leaves them zero.
 constexpr size_t kCounterBytes = 65536;
 
-// Split partials (o_part, lse_part) are written and, by the merge inside the
-// partial kernel, read back with device-scope relaxed atomic accesses: on
-// gfx950 these are the sc1 forms of the plain loads and stores, which write
-// through and read at the point where the XCDs' L2 caches are coherent.  So a
-// partial written on one XCD is visible to the merging workgroup on another
-// once its store has completed, and no workgroup needs a device-scope fence
-// (a write-back and invalidate of its whole L2, which made every split
-// workgroup pay for the others' traffic).
-__device__ __forceinline__ void store_partial(float *p, float v) {
+// Split partials (o_part, lse_part) that the merge inside the partial kernel
+// reads back (Params::counters set) are written and read with device-scope
+// relaxed atomic accesses: on gfx950 these are the sc1 forms of the plain
+// loads and stores, which write through and read at the point where the
+// XCDs' L2 caches are coherent.  So a partial written on one XCD is visible
+// to the merging workgroup on another once its store has completed, and no
+// workgroup needs a device-scope fence (a write-back and invalidate of its
+// whole L2, which made every split workgroup pay for the others' traffic).
+// Partials for the merge kernel are ordinary (cached, 16-byte) stores: the
+// kernel boundary makes them visible.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_partial4(float *p, float a, float b, float c, float d) {
-  store_partial(p, a);
-  store_partial(p + 1, b);
-  store_partial(p + 2, c);
-  store_partial(p + 3, d);
+__device__ __forceinline__ void store_partial(const Params &prm, float *p, float v) {
+  if (prm.counters)
+    store_coherent(p, v);
+  else
+    *p = v;
+}
+// four consecutive floats at p (16-byte aligned)
+__device__ __forceinline__ void store_partial4(const Params &prm, float *p, float a, float b, float c, float d) {
+  if (prm.counters) {
+    store_coherent(p, a);
+    store_coherent(p + 1, b);
+    store_coherent(p + 2, c);
+    store_coherent(p + 3, d);
+  } else {
+    *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+  }
 }
 __device__ __forceinline__ float load_partial(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -252,46 +267,68 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
 // output (request with one split) or the split's partial.
 //   sm_m[w][h], sm_l[w][h]: running max (log2 domain) and sum of wave w;
 //   sm_o[w][h][d]: unnormalised accumulator of wave w (fp32).
+// One thread per column first turns the waves' states into weights
+// 2^(m_w - M) * v_scale / L (over sm_m) and the column's lse (into
+// sm_l[0]); then every thread combines four dims of one column with them.
+// The whole workgroup calls it (one barrier inside); sm_m and sm_l are
+// overwritten.
 template <int D, int OSTRIDE>
-__device__ __forceinline__ void merge_waves_and_store(const Params &p, const float (*sm_m)[16],
-                                                      const float (*sm_l)[16], const float *sm_o,
-                                                      int b, int kvg, int cg, int item, int nb) {
-  const int g = p.group;
-  for (int idx = threadIdx.x; idx < p.cols * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
+__device__ __forceinline__ void merge_waves_and_store(const Params &p, float (*sm_m)[16], float (*sm_l)[16],
+                                                      const float *sm_o, int b, int kvg, int cg, int item, int nb) {
+  static_assert(D % 4 == 0 && OSTRIDE % 4 == 0, "float4 rows");
+  const int tid = threadIdx.x;
+  if (tid < p.cols) { // at most 16 columns
+    const int h = tid;
     int row, hq;
-    if (!column_target(p, b, kvg, cg, h, row, hq)) continue; // padding column
-    const float vscale = p.v_scale ? p.v_scale[b * p.num_kv_heads + hq / g] : 1.0f;
+    const bool has = column_target(p, b, kvg, cg, h, row, hq);
+    const float vscale = has && p.v_scale ? p.v_scale[b * p.num_kv_heads + hq / p.group] : 1.0f;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float val = 0.0f, lse2 = -INFINITY;
-    if (M != -INFINITY) {
-      float L = 0.0f, acc = 0.0f;
+    float a[kWaves];
+    float L = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_m[w][h];
-        const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-        L += a * sm_l[w][h];
-        acc += a * sm_o[(w * 16 + h) * OSTRIDE + d];
-      }
-      if (L > 0.0f) { // a finite reference with no visible key leaves L = 0: empty
-        val = acc / L * vscale;
-        lse2 = M + __log2f(L);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_m[w][h];
+      a[w] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      L += a[w] * sm_l[w][h];
     }
+    // no visible key (M = -inf), or a finite reference with none (L = 0): empty
+    const bool live = M != -INFINITY && L > 0.0f;
+    const float inv = live ? vscale / L : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sm_m[w][h] = a[w] * inv;
+    sm_l[0][h] = live ? M + __log2f(L) : -INFINITY;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < p.cols * (D / 4); idx += kThreads) {
+    const int h = idx / (D / 4);
+    const int d = 4 * (idx - h * (D / 4));
+    int row, hq;
+    if (!column_target(p, b, kvg, cg, h, row, hq)) continue; // padding column
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = sm_m[w][h];
+      const float4 x = *reinterpret_cast<const float4 *>(sm_o + (w * 16 + h) * OSTRIDE + d);
+      v.x += c * x.x;
+      v.y += c * x.y;
+      v.z += c * x.z;
+      v.w += c * x.w;
+    }
+    const float lse2 = sm_l[0][h];
     if (nb == 1) {
       const size_t off = ((size_t)row * p.num_qo_heads + hq) * D + d;
       if (p.out_bf16)
-        reinterpret_cast<uint16_t *>(p.o)[off] = f32_to_bf16_bits(val);
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
+            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       else
-        reinterpret_cast<float *>(p.o)[off] = val;
+        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.o) + off) = v;
       if (d == 0 && p.lse) p.lse[(size_t)row * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
       const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-      store_partial(p.o_part + (slot * p.cols + h) * D + d, val);
-      if (d == 0) store_partial(p.lse_part + slot * p.cols + h, lse2);
+      store_partial4(p, p.o_part + (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+      if (d == 0) store_partial(p, p.lse_part + slot * p.cols + h, lse2);
     }
   }
 }
@@ -443,9 +480,10 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
 
 // End of a partial workgroup whose request has several splits: count its
 // arrival for (grid.y slot `yslot`, request b); the workgroup that brings the
-// last split merges them all (merge_splits) and resets the counter, so no
+// last split merges them all (merge_splits, for each of its npack KV-head
+// packs kvg .. kvg + npack - 1) and resets the counter, so no
 // second kernel runs and no workgroup ever waits for another.  Every thread's
-// partial stores (store_partial: written through to the device-coherent
+// partial stores (store_partial with counters: written through to the device-coherent
 // level) have completed before the count, and the merging workgroup reads
 // them back with load_partial after it.
 // Call with the whole workgroup, after the partial stores; `lds` (at least
@@ -453,7 +491,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
 // flight per thread during the merge (fewer where registers are tight).
 template <int D, int NB = kFusedMergeBatch>
 __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, int kvg, int cg_first, int ncg,
-                                             int item, int split, int nb, void *lds) {
+                                             int item, int split, int nb, void *lds, int npack = 1) {
   __shared__ int s_last;
   if (nb <= 1 || !p.counters) return; // the same in every thread
   wait_all_vmem(); // this thread's partial stores have completed
@@ -462,7 +500,10 @@ __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, 
   if (threadIdx.x == 0) s_last = atomicAdd(ctr, 1u) == (unsigned)(nb - 1);
   __syncthreads();
   if (!s_last) return;
-  merge_splits<D, NB>(p, b, kvg, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
+  for (int k = 0; k < npack; ++k) { // KV-head packs kvg .. kvg + npack - 1 (the same in every thread)
+    if (k > 0) __syncthreads();     // the previous pack's merge has read its LDS states
+    merge_splits<D, NB>(p, b, kvg + k, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
+  }
   if (threadIdx.x == 0) atomicExch(ctr, 0u); // every split of this call has arrived: ready for the next call
 }
 

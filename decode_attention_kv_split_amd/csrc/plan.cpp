@@ -10,26 +10,35 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(0, L - nq + 1 - window) : 0; }
 
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int pack, int head_dim, int forced_chunk, int num_cus, Plan *out) {
+               int col_blocks, int pack, int wave_packs, int head_dim, int forced_chunk, int num_cus, Plan *out) {
   Plan pl;
+  wave_packs = std::max(1, wave_packs);
+  const bool per_wave = wave_packs > 1;
   // span of request b: from its first 16-aligned visible tile to its last key
-  int64_t total = 0;
+  int64_t total = 0, longest = 0;
   for (int b = 0; b < batch; ++b) {
     const int L = kv_len[b];
     if (L < 0) return false;
     const int lo = request_lo(L, nq ? nq[b] : 1, window);
     total += L - (lo & ~15);
+    longest = std::max<int64_t>(longest, L - (lo & ~15));
   }
   int64_t chunk;
   if (forced_chunk > 0) {
     chunk = ((int64_t)forced_chunk + 15) / 16 * 16;
   } else {
-    const int64_t target = (int64_t)kItemsPerCu * std::max(1, num_cus);
+    // the same work per workgroup whichever way the waves share it: a
+    // workgroup holding wave_packs packs takes chunks wave_packs times shorter
+    const int64_t target = (int64_t)kItemsPerCu * std::max(1, num_cus) * wave_packs;
+    const int64_t quantum = per_wave ? kWaveChunkQuantum : kChunkQuantum;
     chunk = (total * num_kv_heads * col_blocks + target - 1) / target;
-    chunk = (chunk + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
-    chunk = std::max<int64_t>(chunk, kMinChunk);
+    // at most kPlanInlineSplits splits per request, so that the work list
+    // can still travel in the kernel arguments
+    chunk = std::max<int64_t>(chunk, (longest + kPlanInlineSplits - 1) / kPlanInlineSplits);
+    chunk = (chunk + quantum - 1) / quantum * quantum;
+    chunk = std::max<int64_t>(chunk, per_wave ? kWaveChunkQuantum : kMinChunk);
   }
-  chunk = std::min<int64_t>(chunk, kMaxChunk);
+  chunk = std::min<int64_t>(chunk, per_wave ? kMaxWaveChunk : kMaxChunk);
   pl.chunk = (int)chunk;
   int64_t items = 0;
   int max_splits = 0;
@@ -65,7 +74,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
     // one workgroup per CU whose requests have few splits (a 512-key fp32 MHA
     // decode: 9.1 against 10.5 us per step; a 32k-key MHA decode, 2048
     // workgroups: 95 against 88 us; 128 splits of one request: 43 against 17 us).
-    const int64_t wgs = items * (int64_t)(num_kv_heads / std::max(1, pack)) * col_blocks;
+    const int64_t wgs = items * (int64_t)(num_kv_heads / std::max(1, pack)) * col_blocks / wave_packs;
     pl.fused_pays = pl.fused && wgs <= std::max(1, num_cus) && max_splits <= 8;
   }
   pl.workspace_bytes = pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes + pl.meta_bytes;

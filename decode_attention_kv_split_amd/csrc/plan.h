@@ -45,6 +45,10 @@ constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
 // Largest chunk: 64 tiles of 16 tokens per wave (a wave keeps the page ids of
 // its tiles in one register, one per lane).
 constexpr int kMaxChunk = 4096;
+// With one KV-head pack per wave (wave_packs = 4) every wave streams the whole
+// chunk: chunks are whole tiles, at most 64 of them.
+constexpr int kWaveChunkQuantum = 16;
+constexpr int kMaxWaveChunk = 1024;
 
 // Whether a plan's work list travels in the kernel arguments (InlineWork).
 inline bool plan_inline(int batch, int items, int max_splits) {
@@ -64,10 +68,11 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
 // each); cols: partial-result columns per KV head over all column groups
 // (the group size with one query per request, col_groups * 16 with
 // several); col_blocks: partial workgroups per (item, KV head); pack: KV
-// heads per workgroup.  Returns
+// heads per workgroup; wave_packs: KV-head packs per workgroup (4: one per
+// wave over the whole chunk; 1: the waves split one pack's tiles).  Returns
 // false if a length is negative.  Workspace layout when a request has several
 // splits: [counters][o_part][lse_part][meta].
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int pack, int head_dim, int forced_chunk, int num_cus, Plan *out);
+               int col_blocks, int pack, int wave_packs, int head_dim, int forced_chunk, int num_cus, Plan *out);
 
 } // namespace kvs

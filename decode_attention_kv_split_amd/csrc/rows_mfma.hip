@@ -221,9 +221,9 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
       for (int wt = 0; wt < S::kOTiles; ++wt) {
         const int od = out_dim<D, KT>(wt, q4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) store_partial(dst + od + r * S::kOutStride, (cs.acc[c][wt][r] - voff) * inv);
+        for (int r = 0; r < 4; ++r) store_partial(p, dst + od + r * S::kOutStride, (cs.acc[c][wt][r] - voff) * inv);
       }
-      if (q4 == 0) store_partial(p.lse_part + slot * p.cols + c16, lse2);
+      if (q4 == 0) store_partial(p, p.lse_part + slot * p.cols + c16, lse2);
     }
   }
   // INT4 at head_dim 256 sits at the register limit, and the merge code would
@@ -790,15 +790,15 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
           *reinterpret_cast<uint4 *>(orow + d0) = make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]),
                                                              pack_bf16x2(o8[4], o8[5]), pack_bf16x2(o8[6], o8[7]));
         } else {
-          store_partial4(dst + d0, o8[0], o8[1], o8[2], o8[3]);
-          store_partial4(dst + d0 + 4, o8[4], o8[5], o8[6], o8[7]);
+          store_partial4(p, dst + d0, o8[0], o8[1], o8[2], o8[3]);
+          store_partial4(p, dst + d0 + 4, o8[4], o8[5], o8[6], o8[7]);
         }
       }
     if (h2 == 0) {
       if (nb == 1) {
         if (p.lse) p.lse[(size_t)qrow * p.num_qo_heads + qhead] = lse2 * kLn2;
       } else {
-        store_partial(p.lse_part + slot * p.cols + col % 16, lse2);
+        store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);
       }
     }
     return;
@@ -824,10 +824,10 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d0 = 128 * dh + 32 * sl + 8 * q + 4 * h2;
-        store_partial4(dst + d0, acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv,
+        store_partial4(p, dst + d0, acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv,
                        acc[sl][4 * q + 3] * inv);
       }
-    if (h2 == 0 && dh == 0) store_partial(p.lse_part + slot * p.cols + col % 16, lse2);
+    if (h2 == 0 && dh == 0) store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);
   }
   }();
   finish_split<D>(p, kvg * row_blocks + ord.rb, b, kvg, cgw, kGroups, item, split, nb, smem);

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 10
+#define KVS_ABI_VERSION 11
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -124,12 +124,14 @@ typedef struct {
   float sm_scale;     /* > 0 and finite, multiplies <q, k> */
   int32_t window;     /* -1: no window; W > 0: attend to the last W keys */
   int32_t kv_chunk;   /* 0: heuristic; > 0: tokens per split, rounded up to a
-                         multiple of 16 and capped at 4096 */
+                         multiple of 16 and capped at 4096 (1024 with
+                         KVS_WAVES_HEADS: 64 tiles per wave) */
   int32_t algo;       /* kvs_algo */
   int32_t num_cus;    /* 0: ask the current device; > 0: plan for this many CUs */
 
   /* device outputs (caller-owned) */
-  void *o;    /* [batch, Hq, head_dim], q_dtype, round to nearest even */
+  void *o;    /* [batch, Hq, head_dim], q_dtype, round to nearest even; q and o
+                 16-byte aligned (KVS_ERR_INVALID_ARG otherwise) */
   float *lse; /* [batch, Hq] natural-log LSE of the scaled scores, or NULL */
 
   /* optional profiling: two hipEvent_t (created by the caller) that the
@@ -182,15 +184,28 @@ typedef struct {
    * host and the counters fit, else the merge kernel runs); KVS_MERGE_KERNEL
    * asks for the second kernel. */
   int32_t merge_mode;
+
+  /* How the four waves of a matrix-core decode workgroup share its work
+   * (one query row per request only; other calls always split tiles).
+   * KVS_WAVES_HEADS: each wave takes one KV-head pack (pack = 1 or 2 adjacent
+   * KV heads) over the whole chunk, so a workgroup holds four packs and reads
+   * four adjacent head slices of every token row together; needs
+   * (num_kv_heads / pack) % 4 == 0, else KVS_ERR_UNSUPPORTED.  KVS_WAVES_TILES:
+   * the waves split the chunk's 16-token tiles of one pack.  KVS_WAVES_AUTO:
+   * TILES (at equal workgroup counts HEADS needs chunks four times shorter,
+   * and the extra split partials cost more than its reads gain). */
+  int32_t wave_split;
 } kvs_decode_args;
 
 enum { KVS_MERGE_AUTO = 0, KVS_MERGE_IN_PARTIAL = 1, KVS_MERGE_KERNEL = 2 };
+enum { KVS_WAVES_AUTO = 0, KVS_WAVES_HEADS = 1, KVS_WAVES_TILES = 2 };
 
 /* What a call will launch, computed on the host from kv_len_host. */
 typedef struct {
   int32_t kv_chunk;          /* tokens per split */
   int32_t items_per_kv_head; /* sum over requests of splits; the partial kernel runs
-                                items_per_kv_head * num_kv_heads / pack workgroups */
+                                items_per_kv_head * num_kv_heads / (pack * wave_packs)
+                                workgroups (one query row per request) */
   int32_t max_splits;        /* largest number of splits of one request */
   int32_t needs_merge;       /* 1 if some request has more than one split */
   int32_t algo;              /* resolved kvs_algo (VALU, MFMA or MFMA_PACKED) */
@@ -203,6 +218,8 @@ typedef struct {
                                 shared-tile kernel, partial_rows_kernel) */
   int32_t merge_in_partial;  /* 1: the partial kernel merges the splits itself (one launch);
                                 0: a second kernel merges them (or nothing needs merging) */
+  int32_t wave_packs;        /* KV-head packs per partial workgroup: 4 (one per wave,
+                                KVS_WAVES_HEADS) or 1 */
 } kvs_plan_info;
 
 /* Plan a call without launching anything.  Makes no HIP call when

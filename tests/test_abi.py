@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 10
-    assert re.search(r"#define KVS_ABI_VERSION 10\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 11
+    assert re.search(r"#define KVS_ABI_VERSION 11\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -254,14 +254,21 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
 
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):
     a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(32768,), num_pages=32768)
-    info = kvs.kvs_decode_plan(a)
-    assert info.items_per_kv_head * 32 >= 256  # at least one chunk per CU
-    assert info.kv_chunk >= 512
-    assert info.algo == kvs.KVS_ALGO_MFMA
-    a.num_cus = 64
-    assert kvs.kvs_decode_plan(a).kv_chunk >= info.kv_chunk
-    # deterministic
-    assert kvs.kvs_decode_plan(a).kv_chunk == kvs.kvs_decode_plan(a).kv_chunk
+    cus = a.num_cus
+    for split, packs in (("tiles", 1), ("heads", 4), ("auto", 1)):
+        a.wave_split = {"auto": 0, "heads": 1, "tiles": 2}[split]
+        a.num_cus = cus
+        info = kvs.kvs_decode_plan(a)
+        assert info.wave_packs == packs
+        # at least one workgroup per CU, each with the same work either way
+        assert info.items_per_kv_head * 32 // packs >= 256
+        assert info.kv_chunk * packs >= 512
+        assert info.kv_chunk % 16 == 0 and info.kv_chunk <= (1024 if packs == 4 else 4096)
+        assert info.algo == kvs.KVS_ALGO_MFMA
+        a.num_cus = 64
+        assert kvs.kvs_decode_plan(a).kv_chunk >= info.kv_chunk
+        # deterministic
+        assert kvs.kvs_decode_plan(a).kv_chunk == kvs.kvs_decode_plan(a).kv_chunk
 
 
 def test_algo_resolution(lib):
@@ -484,3 +491,64 @@ def test_merge_mode_auto_and_kernel(lib):
     assert kvs.kvs_decode_plan(a).merge_in_partial == 1
     a.merge_mode = 3
     assert kvs.kvs_decode(a, 0, 0, 0) == kvs.KVS_ERR_INVALID_ARG
+
+
+def _plan_status(a):
+    try:
+        kvs.kvs_decode_plan(a)
+    except kvs.KvsError as e:
+        return e.status
+    return kvs.KVS_OK
+
+
+def test_wave_split_choice_and_validation(lib):
+    """One KV-head pack per wave when asked for (HEADS) where the packs come
+    in fours with one query row per request; the tiles split otherwise and
+    by default; HEADS asked for where it does not apply is unsupported,
+    unknown values are invalid."""
+    # GQA paged decode, 8 KV heads: two workgroups of four packs per chunk
+    a, keep = _args(ptrs=False, batch=3, Hq=32, Hk=8, lens=(100, 2000, 9000))
+    assert kvs.kvs_decode_plan(a).wave_packs == 1
+    a.wave_split = kvs.KVS_WAVES_HEADS
+    info = kvs.kvs_decode_plan(a)
+    assert info.wave_packs == 4 and info.kv_chunk % 16 == 0 and info.kv_chunk <= 1024
+    a.kv_chunk = 4096                                      # capped at 64 tiles per wave
+    assert kvs.kvs_decode_plan(a).kv_chunk == 1024
+    a.wave_split = kvs.KVS_WAVES_TILES
+    info = kvs.kvs_decode_plan(a)
+    assert info.wave_packs == 1 and info.kv_chunk == 4096
+    a.wave_split = 3
+    assert _plan_status(a) == kvs.KVS_ERR_INVALID_ARG
+    # INT4 head_dim 128: two heads per pack, 8 heads -> 4 packs, one workgroup
+    a, keep = _args(ptrs=False, batch=2, Hq=64, Hk=8, kv=kvs.KVS_INT4, lens=(500, 3000))
+    a.wave_split = kvs.KVS_WAVES_HEADS
+    info = kvs.kvs_decode_plan(a)
+    assert info.algo == kvs.KVS_ALGO_MFMA_PACKED and info.wave_packs == 4
+    # not in fours: one KV head; 6 KV heads
+    for Hk in (1, 2, 6):
+        a, keep = _args(ptrs=False, batch=2, Hq=6 * Hk, Hk=Hk, lens=(500, 3000))
+        assert kvs.kvs_decode_plan(a).wave_packs == 1
+        a.wave_split = kvs.KVS_WAVES_HEADS
+        assert _plan_status(a) == kvs.KVS_ERR_UNSUPPORTED
+    # several query rows per request, and the vector kernel: tiles only
+    a, keep = _args(ptrs=False, batch=2, Hq=32, Hk=8, lens=(500, 3000))
+    rows = np.array([0, 2, 5], np.int32)
+    a.qo_indptr_host = rows.ctypes.data
+    assert kvs.kvs_decode_plan(a).wave_packs == 1
+    a.wave_split = kvs.KVS_WAVES_HEADS
+    assert _plan_status(a) == kvs.KVS_ERR_UNSUPPORTED
+    a, keep = _args(ptrs=False, batch=2, Hq=32, Hk=8, q=kvs.KVS_F32, kv=kvs.KVS_F32, lens=(500, 3000))
+    info = kvs.kvs_decode_plan(a)
+    assert info.algo == kvs.KVS_ALGO_VALU and info.wave_packs == 1
+    a.wave_split = kvs.KVS_WAVES_HEADS
+    assert _plan_status(a) == kvs.KVS_ERR_UNSUPPORTED
+
+
+def test_q_and_o_must_be_16_byte_aligned(lib):
+    """Rows of q and o move in 16-byte pieces: a misaligned pointer is an
+    invalid argument, reported before any launch."""
+    for field in ("q", "o"):
+        a, keep = _args()
+        setattr(a, field, 0x1008)
+        ws = (ctypes.c_uint8 * 256)()
+        assert kvs.kvs_decode(a, ctypes.addressof(ws), 0, None) == kvs.KVS_ERR_INVALID_ARG

@@ -102,7 +102,7 @@ def test_one_workspace_for_calls_of_any_shape():
 # several column blocks, each with its own counter
 FAMILIES = [
     ("c1_mha_f32", None, 64, "vector"),
-    ("c3_llama2_7b_32k", None, 0, "decode, one request, 64 splits per head"),
+    ("c3_llama2_7b_32k", None, 0, "decode, one request, 256 splits per head"),
     ("c4_paged_bf16_b64", None, 128, "decode"),
     ("c6_paged_int4_b128", None, 64, "decode, two INT4 heads per workgroup"),
     ("c4_paged_bf16_b64", ("list", [5, 7, 8]), 128, "32-column"),
