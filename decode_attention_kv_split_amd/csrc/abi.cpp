@@ -225,19 +225,11 @@ int kv_pack(const kvs_decode_args *a, int algo) {
                         algo == KVS_ALGO_MFMA_PACKED);
 }
 
-// KV-head packs per matrix-core decode workgroup: 4 (one per wave, each over
-// the whole chunk) when asked for (KVS_WAVES_HEADS) and every request has one
-// query row and the packs come in fours; else 1 (the waves split one pack's
-// tiles), which is also the automatic choice: at the workgroup counts the
-// chunk heuristic aims for, the heads split needs chunks four times shorter,
-// and the extra split partials it writes cost more than its row-wise reads
-// gain (batch-64 bf16 378 against 365 us, batch-128 fp8 271 against 253 us).
-// -1: KVS_WAVES_HEADS asked for where it does not apply.
-int wave_packs_of(const kvs_decode_args *a, int algo, const Columns &c) {
-  if (a->wave_split != KVS_WAVES_HEADS) return 1;
-  const bool fits = algo != KVS_ALGO_VALU && !a->qo_indptr_host && c.col_groups == 1 &&
-                    (a->num_kv_heads / kv_pack(a, algo)) % kvs::kWaves == 0;
-  return fits ? kvs::kWaves : -1;
+// Whether one KV-head pack per wave (KVS_WAVES_HEADS) applies: every
+// request has one query row and the matrix-core packs come in fours.
+bool heads_fit(const kvs_decode_args *a, int algo, const Columns &c) {
+  return algo != KVS_ALGO_VALU && !a->qo_indptr_host && c.col_groups == 1 &&
+         (a->num_kv_heads / kv_pack(a, algo)) % kvs::kWaves == 0;
 }
 
 // Whether the partial kernel merges the splits itself: the plan allows it
@@ -257,12 +249,25 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   if (st != KVS_OK) return st;
   Columns c = columns_of(a);
   const int pack = kv_pack(a, *algo);
-  const int wave_packs = wave_packs_of(a, *algo, c);
-  if (wave_packs < 0) return KVS_ERR_UNSUPPORTED;
-  if (!kvs::make_plan(a->kv_len_host, c.nq.empty() ? nullptr : c.nq.data(), a->batch, a->window,
-                      a->num_kv_heads, c.cols, c.col_blocks, pack, wave_packs, a->head_dim, a->kv_chunk, *cus,
-                      pl))
+  const bool heads = heads_fit(a, *algo, c);
+  if (a->wave_split == KVS_WAVES_HEADS && !heads) return KVS_ERR_UNSUPPORTED;
+  const int32_t *nq = c.nq.empty() ? nullptr : c.nq.data();
+  if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
+                      a->wave_split == KVS_WAVES_HEADS ? kvs::kWaves : 1, a->head_dim, a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
+  // Automatic wave split: the tiles split, unless the heads split can keep
+  // the tiles plan's chunks (at most 64 tiles per wave) and still give every
+  // CU a workgroup.  With the same chunks both write the same split
+  // partials, and the heads split then reads whole runs of adjacent head rows
+  // (32k-token MHA decode: 81.7 against 84.1 us).  With shorter chunks its
+  // extra partials cost more than that (batch-64 bf16: 374 against 365 us).
+  const int64_t head_wgs = (int64_t)pl->items * (a->num_kv_heads / pack) / kvs::kWaves;
+  if (a->wave_split == KVS_WAVES_AUTO && heads && pl->chunk <= kvs::kMaxWaveChunk &&
+      head_wgs >= std::max(1, *cus)) {
+    if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
+                        kvs::kWaves, a->head_dim, pl->chunk, *cus, pl))
+      return KVS_ERR_INVALID_ARG;
+  }
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
   // (the merge runs one workgroup per column group)
   if ((int64_t)pl->items * a->num_kv_heads * c.col_groups > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
@@ -351,7 +356,7 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   out->col_groups = c.col_groups;
   out->col_share = c.col_share;
   out->merge_in_partial = merges_in_partial(pl, args, c) ? 1 : 0;
-  out->wave_packs = wave_packs_of(args, algo, c);
+  out->wave_packs = pl.wave_packs;
   return KVS_OK;
 }
 
@@ -400,7 +405,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.col_groups = cols.col_groups;
   p.col_share = cols.col_share;
   p.cols = a->qo_indptr_host ? 16 : p.group * p.pack;
-  p.wave_packs = wave_packs_of(a, algo, cols);
+  p.wave_packs = pl.wave_packs;
   // The chunks of a request differ in work only when its query rows reach
   // over more than one chunk (the early rows stop before the late chunks);
   // only then do the multi-row kernels deal their workgroups to the XCDs by

@@ -14,6 +14,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
   Plan pl;
   wave_packs = std::max(1, wave_packs);
   const bool per_wave = wave_packs > 1;
+  pl.wave_packs = wave_packs;
   // span of request b: from its first 16-aligned visible tile to its last key
   int64_t total = 0, longest = 0;
   for (int b = 0; b < batch; ++b) {

@@ -19,6 +19,7 @@ struct Plan {
   int chunk = 0;        // tokens per split (multiple of 16)
   int items = 0;        // work items per KV head (sum of splits)
   int max_splits = 0;
+  int wave_packs = 1;   // KV-head packs per workgroup (4: one per wave)
   bool needs_merge = false;
   // The partial kernel merges the splits itself (the workgroup that writes a
   // request's last split merges them): the work list is planned on the host

@@ -192,8 +192,10 @@ typedef struct {
    * four adjacent head slices of every token row together; needs
    * (num_kv_heads / pack) % 4 == 0, else KVS_ERR_UNSUPPORTED.  KVS_WAVES_TILES:
    * the waves split the chunk's 16-token tiles of one pack.  KVS_WAVES_AUTO:
-   * TILES (at equal workgroup counts HEADS needs chunks four times shorter,
-   * and the extra split partials cost more than its reads gain). */
+   * HEADS where it applies and can keep the chunks TILES would use (at most
+   * 1024 tokens) with at least one workgroup per CU, else TILES (shorter
+   * chunks would mean more split partials, which cost more than HEADS'
+   * reads gain). */
   int32_t wave_split;
 } kvs_decode_args;
 

@@ -33,6 +33,7 @@ class SweepCase:
     unified_max: object  # None or float
     poison_invisible: bool
     merge_mode: str = "auto"
+    wave_split: str = "auto"
 
     @property
     def multi(self) -> bool:
@@ -58,6 +59,8 @@ class SweepCase:
             parts.append("nan")
         if self.merge_mode != "auto":
             parts.append(f"merge-{self.merge_mode}")
+        if self.wave_split != "auto":
+            parts.append(f"waves-{self.wave_split}")
         return "-".join(parts)
 
 
@@ -136,9 +139,17 @@ def draw_case(rng, index: int) -> SweepCase:
     spec = DecodeSpec(f"sweep{index}", batch, g * hk, hk, d, P, kv, "f32" if kv == "f32" else "bf16", sm,
                       window=window, lengths=("list", [int(x) for x in lens]), qk_rmsnorm=qk_norm,
                       seed=SWEEP_SEED + index, q_len=q_len, soft_cap=cap)
-    # where the splits merge, from a stream of its own (the other draws stay as they were)
+    # where the splits merge and how a workgroup's waves share its work, from
+    # streams of their own (the other draws stay as they were); one KV-head
+    # pack per wave needs one query row and the packs in fours
     merge = ["auto", "in_partial", "kernel"][int(np.random.default_rng([SWEEP_SEED, index]).integers(0, 3))]
-    return SweepCase(index, spec, int(chunk), algo, unified, poison_inv, merge)
+    waves = "auto"
+    bytes_per = {"bf16": 2, "fp8": 1, "int4": 0.5}.get(kv, 4)
+    packable = (d == 128 if kv == "int4" else d * bytes_per < 256) and 2 * g <= 16 and hk % 2 == 0
+    pack = 2 if packable and (algo == "mfma_packed" or (kv == "int4" and algo == "auto")) else 1
+    if matrix and not multi and (hk // pack) % 4 == 0 and np.random.default_rng([SWEEP_SEED, index, 1]).random() < 0.6:
+        waves = "heads"
+    return SweepCase(index, spec, int(chunk), algo, unified, poison_inv, merge, waves)
 
 
 def sweep_cases(n: int = SWEEP_CASES, seed: int = SWEEP_SEED) -> List[SweepCase]:

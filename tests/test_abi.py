@@ -255,7 +255,7 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):
     a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(32768,), num_pages=32768)
     cus = a.num_cus
-    for split, packs in (("tiles", 1), ("heads", 4), ("auto", 1)):
+    for split, packs in (("tiles", 1), ("heads", 4), ("auto", 4)):
         a.wave_split = {"auto": 0, "heads": 1, "tiles": 2}[split]
         a.num_cus = cus
         info = kvs.kvs_decode_plan(a)
@@ -503,12 +503,26 @@ def _plan_status(a):
 
 def test_wave_split_choice_and_validation(lib):
     """One KV-head pack per wave when asked for (HEADS) where the packs come
-    in fours with one query row per request; the tiles split otherwise and
-    by default; HEADS asked for where it does not apply is unsupported,
-    unknown values are invalid."""
+    in fours with one query row per request, and automatically where it can
+    keep the tiles split's chunks (at most 1024 keys) with a workgroup per
+    CU; the tiles split otherwise.  HEADS asked for where it does not apply
+    is unsupported, unknown values are invalid."""
     # GQA paged decode, 8 KV heads: two workgroups of four packs per chunk
     a, keep = _args(ptrs=False, batch=3, Hq=32, Hk=8, lens=(100, 2000, 9000))
+    a.wave_split = kvs.KVS_WAVES_TILES
+    tiles = kvs.kvs_decode_plan(a)
+    assert tiles.wave_packs == 1 and tiles.kv_chunk <= 1024
+    a.wave_split = kvs.KVS_WAVES_AUTO                      # same chunks, 350 workgroups: heads
+    info = kvs.kvs_decode_plan(a)
+    assert info.wave_packs == 4 and info.kv_chunk == tiles.kv_chunk
+    assert info.items_per_kv_head == tiles.items_per_kv_head and info.workspace_bytes == tiles.workspace_bytes
+    a.num_cus = 1024                                       # fewer workgroups than CUs: tiles
     assert kvs.kvs_decode_plan(a).wave_packs == 1
+    a.num_cus = 256
+    # a batch whose tiles chunks exceed 1024 keys keeps the tiles split
+    big, keep2 = _args(ptrs=False, batch=64, Hq=32, Hk=8, lens=tuple(range(512, 16384, 248))[:64], num_pages=70000)
+    info = kvs.kvs_decode_plan(big)
+    assert info.kv_chunk > 1024 and info.wave_packs == 1
     a.wave_split = kvs.KVS_WAVES_HEADS
     info = kvs.kvs_decode_plan(a)
     assert info.wave_packs == 4 and info.kv_chunk % 16 == 0 and info.kv_chunk <= 1024

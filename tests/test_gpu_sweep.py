@@ -1,7 +1,7 @@
 """Randomized parity sweep: 150 seeded configurations drawn over KV type x
 head_dim x group x KV heads x page size (or a contiguous cache) x ragged
 lengths x window x query rows per request x forced chunk size x unified
-max x soft cap x kernel family x merge place (tests/sweep_configs.py), each compared
+max x soft cap x kernel family x merge place x wave split (tests/sweep_configs.py), each compared
 element by element with the fp64 oracle at the KV type's tolerance.  Run
 with -x: the first failing case stops the run and is named by its index."""
 import numpy as np
@@ -37,7 +37,7 @@ def test_sweep(case):
     if case.poison_invisible and _has_invisible_keys(inp):
         inp = poison_invisible(inp)
     o, lse = run_library(inp, kv_chunk=case.kv_chunk, algo=case.algo, unified_max=case.unified_max,
-                         merge_mode=case.merge_mode)
+                         merge_mode=case.merge_mode, wave_split=case.wave_split)
     o_ref, lse_ref = oracle.attention_reference(inp)
     err, rel = compare(o, lse, o_ref, lse_ref, case.spec.kv_dtype)
     print(f"  max|o-o_ref|={err:.2e} lse_rel={rel:.2e}", flush=True)

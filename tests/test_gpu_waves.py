@@ -100,9 +100,9 @@ def test_heads_and_tiles_match_the_oracle(cid, spec, chunk, merge, umax):
         outs[split] = (o, err, plan)
         print(f"  {split}: chunk {plan.kv_chunk} items {plan.items_per_kv_head} "
               f"merge_in_partial {plan.merge_in_partial} max err {err:.2e}", flush=True)
-    # the automatic choice splits the tiles
+    # the automatic choice (either split, by the planner's rule)
     o, lse, plan = _run(inp, ws, "auto", kv_chunk=chunk, merge_mode=merge, unified_max=umax)
-    assert plan.wave_packs == 1
+    compare(o, lse, o_ref, lse_ref, spec.kv_dtype)
 
 
 def test_heads_rejected_where_it_does_not_apply():

@@ -56,5 +56,7 @@ def test_sweep_case_plans(lib, case):
         a.use_unified_max, a.unified_max = 1, case.unified_max
     a.logits_soft_cap = s.soft_cap
     a.merge_mode = {"auto": 0, "in_partial": 1, "kernel": 2}[case.merge_mode]
+    a.wave_split = {"auto": 0, "heads": 1, "tiles": 2}[case.wave_split]
     info = kvs.kvs_decode_plan(a)  # raises on any status but KVS_OK
+    assert info.wave_packs in ((4,) if case.wave_split == "heads" else (1, 4))
     assert info.items_per_kv_head >= s.batch
