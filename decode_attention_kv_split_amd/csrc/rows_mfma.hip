@@ -307,6 +307,9 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   constexpr int kGroups = kColWaves * 2;          // 16-column groups per workgroup
   constexpr int kDmaP = kPart * kRowBytes / 1024; // 16-byte DMA loads per wave part (K or V)
   constexpr int kSteps = D / 16;                  // 32x32x16 products of S^T per tile
+  // head_dim 256: each wave of a pair forms the score product over its own
+  // 128 dims and the pair adds the two halves through LDS
+  constexpr int kStepsW = kSplitD ? kSteps / 2 : kSteps; // products per wave
   // blocks of the longest chunk (64 tiles per wave, 4096 keys) per lane of the offset table
   constexpr int kLaneBlocks = 64 * kWaves * kTile / kBlock / 64;
   static_assert(kDmaP >= 1 && kLaneBlocks >= 1 && kTiles32 >= 1, "block shape");
@@ -382,13 +385,14 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // Q^T operand of step s: dims 16 s + 8 h2 .. + 7 of the column's query
   // (fp8: dims 16 (2 (s / 2) + h2) + 8 (s % 2) .., the order of its K pieces;
   // INT4: the 8 dims of K dword 8 h2 + s, even ones first, as its nibbles)
-  bf16x8_t qop[kSteps];
+  bf16x8_t qop[kStepsW];
   float qoff = 0.0f; // INT4: the scores carry 136 * (sum of the column's q)
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(p.q) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int d0 = kInt4 ? 8 * (8 * h2 + s) : (kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 16 * s + 8 * h2);
+    for (int s = 0; s < kStepsW; ++s) {
+      const int d0 = kInt4 ? 8 * (8 * h2 + s)
+                           : (kFp8 ? 16 * (2 * (s / 2) + h2) + 8 * (s % 2) : 128 * dh + 16 * s + 8 * h2);
       bf16x8_t x = ok ? __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qb + d0))
                       : __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
       if constexpr (kInt4) {
@@ -477,13 +481,13 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // pi(j32), piece 2 m + h2 for steps 2 m and 2 m + 1.  Eight steps per LDS
   // read block.
   // INT4: pieces 2 h2 and 2 h2 + 1 of row pi(j32) (dwords 8 h2 .. 8 h2 + 7).
-  uint32_t k_addr[kSteps / 8][8];
+  uint32_t k_addr[kStepsW / 8][8];
   const int krow = kPerm ? (j32 & ~12) | ((j32 & 8) >> 1) | ((j32 & 4) << 1) : j32;
   {
     const uint32_t base = lds_address(smem) + krow * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int piece = kInt4 ? 2 * h2 + (s & 1) : (kFp8 ? s & 3 : s) * 2 + h2;
+    for (int s = 0; s < kStepsW; ++s) {
+      const int piece = kInt4 ? 2 * h2 + (s & 1) : (kFp8 ? s & 3 : (kSplitD ? 8 * dh + s : s)) * 2 + h2;
       k_addr[s / 8][s % 8] = base + (piece ^ row_swizzle(krow)) * 16;
     }
   }
@@ -538,8 +542,9 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       }
   }
 
-  // one 32-key tile (first key ts) at byte offset `to` of the staged block
-  auto tile32 = [&](int ts, uint32_t to) {
+  // one 32-key tile (first key ts) at byte offset `to` of the staged block:
+  // the score product (of the wave's dims), then the rest
+  auto scores32 = [&](uint32_t to) {
     // ---- S^T = K . Q^T ----
     f32x16_t st;
 #pragma unroll
@@ -569,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
       for (int s = 0; s < 8; ++s) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[s], st, 0, 0, 0);
     } else {
 #pragma unroll
-      for (int hb = 0; hb < kSteps / 8; ++hb) {
+      for (int hb = 0; hb < kStepsW / 8; ++hb) {
         uint4 kr[8];
         lds_read_x8(kr, k_addr[hb], to);
 #pragma unroll
@@ -577,6 +582,9 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
           st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[s]), qop[8 * hb + s], st, 0, 0, 0);
       }
     }
+    return st;
+  };
+  auto finish32 = [&](int ts, uint32_t to, const f32x16_t &st) {
     // V^T operands, read while the products run: vop[t][sl]
     // Keys before wv_lo are seen by no column of the wave; their V rows may
     // hold non-finite values (only visible values are required finite), and
@@ -737,11 +745,35 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
         const int i = it + j;
         wait_vmem<(NBUF - 1) * 2 * kDmaP>();
         __syncthreads();
-        if (i < nblocks && wave_on) {
+        if constexpr (kSplitD) {
+          // one 32-key tile per block; the pair's two score halves meet in
+          // the block's K rows, which no wave reads once its products are
+          // formed (the barriers are taken by every wave, whether or not it
+          // has keys in this tile)
+          static_assert(!kSplitD || kTiles32 == 1, "one tile per block");
+          const int ts = k0 + i * kBlock;
+          const uint32_t to = j * 2 * kHalf;
+          const bool vis = i < nblocks && wave_on && ts < wv_hi && ts + 2 * kTile > wv_lo; // the same in a pair
+          f32x16_t st;
+          if (vis) st = scores32(to);
+          __syncthreads(); // every wave's K reads of this block are done
+          float *xs = reinterpret_cast<float *>(smem + to);
+          if (vis) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) xs[(wave * 16 + v) * 64 + lane] = st[v];
+          }
+          __syncthreads();
+          if (vis) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st[v] += xs[((wave ^ 1) * 16 + v) * 64 + lane];
+            finish32(ts, to, st);
+          }
+        } else if (i < nblocks && wave_on) {
 #pragma unroll
           for (int u = 0; u < kTiles32; ++u) {
             const int ts = k0 + i * kBlock + u * 2 * kTile;
-            if (ts < wv_hi && ts + 2 * kTile > wv_lo) tile32(ts, j * 2 * kHalf + u * 2 * kTile * kRowBytes);
+            const uint32_t to = j * 2 * kHalf + u * 2 * kTile * kRowBytes;
+            if (ts < wv_hi && ts + 2 * kTile > wv_lo) finish32(ts, to, scores32(to));
           }
         }
         __syncthreads();
