@@ -16,7 +16,7 @@
 namespace kvs {
 hipError_t launch_partial_mfma(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l);
 hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, const Launch &l);
-hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream);
+hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, int max_splits, hipStream_t stream);
 int valu_max_group(int kv_dtype);
 int mfma_pack(int head_dim, int group, int num_kv_heads, int kv_type, bool allow_pack);
 bool mfma_packable(int head_dim, int group, int num_kv_heads, int kv_type);
@@ -451,7 +451,7 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
     e = kvs::launch_partial_valu(p, w, a->head_dim, a->kv_dtype, lp);
   if (e != hipSuccess) return KVS_ERR_HIP;
   if (pl.needs_merge && !p.counters) {
-    e = kvs::launch_merge(p, ml, a->head_dim, stream);
+    e = kvs::launch_merge(p, ml, a->head_dim, pl.max_splits, stream);
     if (e != hipSuccess) return KVS_ERR_HIP;
   }
   return KVS_OK;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
 
 } // namespace
 
-hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hipStream_t stream) {
+hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, int max_splits, hipStream_t stream) {
   const int rows = ml.n >= 0 ? ml.n : p.batch;
   if (rows == 0) return hipSuccess;
   // enough workgroups to spread a small batch: cut the head dimension into up
@@ -73,6 +73,15 @@ hipError_t launch_merge(const Params &p, const InlineMerge &ml, int head_dim, hi
   int slices = 1;
   const int packs = p.num_kv_heads / p.pack * p.col_groups;
   while (slices * 64 < head_dim && (int64_t)rows * packs * slices < 256) slices *= 2;
+  // then, down to 16-dim slices, until no thread folds more than one batch of
+  // splits: each batch is a dependent round trip to memory, and a long request
+  // in a small grid would otherwise chain several
+  auto folds = [&](int s) { // splits folded one after another by a thread
+    const int F = p.cols * (head_dim / s) / 4;
+    const int SG = F >= kThreads ? 1 : kThreads / F;
+    return ((F + kThreads - 1) / kThreads) * ((max_splits + SG - 1) / SG);
+  };
+  while (slices * 16 < head_dim && folds(slices) > kMergeBatch) slices *= 2;
   dim3 grid(rows, packs, slices);
   return launch_kernel(Launch{stream}, merge_kernel, grid, p, ml, head_dim, slices);
 }
