@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     float inv = 0.0f;
     if (cs.ok[0]) {
       const int hq = cs.head[0];
-      const float vscale = p.v_scale ? p.v_scale[b * Hk + hq / g] : 1.0f;
+      const float vscale = p.v_scale && writer_scales_v(p, nb) ? p.v_scale[b * Hk + hq / g] : 1.0f;
       inv = live ? vscale / l_tot : 0.0f;
       if (q4 == 0) {
         const float lse2 = live ? cs.m[0] + __log2f(l_tot) : -INFINITY;
@@ -301,11 +301,11 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
           *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
               make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
         } else {
-          store_partial4(p, p.o_part + (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+          store_part4(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
         }
       }
     }
-    finish_split<D>(p, blockIdx.y, b, blockIdx.y * kWaves, 0, 1, item, split, nb, smem, kWaves);
+    finish_split<D, PACK>(p, blockIdx.y, b, blockIdx.y * kWaves, 0, 1, item, split, nb, smem, kWaves);
     return;
   }
   __syncthreads(); // staging area is reused for the per-wave states below
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     __syncthreads();
     merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
-  finish_split<D>(p, blockIdx.y, b, kvg, cg0, CG, item, split, nb, smem);
+  finish_split<D, PACK>(p, blockIdx.y, b, kvg, cg0, CG, item, split, nb, smem);
 }
 
 } // namespace

@@ -22,9 +22,14 @@
 // one KV head (column c = row * g + head), in column group cg.  Partial
 // results of split x of slot (pack kvg, column group cg) live in the
 // workspace: o_part[((S * I + x) * cols + h) * D + d] with S = kvg *
-// col_groups + cg (fp32, already divided by the chunk's sum and multiplied by
-// the V scale) and lse_part[(S * I + x) * cols + h] (log2 domain: chunk max +
-// log2(chunk sum), -inf when the chunk saw no key), I = items per KV head.
+// col_groups + cg (already divided by the chunk's sum) and
+// lse_part[(S * I + x) * cols + h] (fp32, log2 domain: chunk max + log2(chunk
+// sum), -inf when the chunk saw no key), I = items per KV head.  o_part is
+// fp32 and includes the V scale for bf16 and fp32 caches.  For fp8 and INT4
+// caches (part_f16) it is fp16 and leaves the V scale to the merge: it then
+// holds a weighted average of the decoded codes, which lies inside their range
+// (|x| <= 448 for e4m3, <= 8 for INT4), where fp16 keeps 11 significant bits;
+// half the bytes of fp32.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -90,6 +95,7 @@ struct Params {
   int rows_xcd_order; // multi-row kernels: workgroups in the XCD-balanced order (rows_order)
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
+  int part_f16;   // split partials o_part hold fp16 averages of the stored V codes (fp8, INT4 caches)
   float score_scale; // sm_scale * log2(e); with a soft cap c: sm_scale / c
   float cap_out;     // soft cap: scores become tanh(score_scale * qk) * cap_out, cap_out = c * log2(e); 0: no cap
   // Merge in the partial kernel (null: a second kernel merges): one arrival
@@ -135,6 +141,86 @@ __device__ __forceinline__ void store_partial4(const Params &prm, float *p, floa
 }
 __device__ __forceinline__ float load_partial(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// fp16 partials (Params::part_f16): two values per dword, round to nearest even
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const half2_t h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float2 unpack_f16x2(uint32_t u) {
+  const half2_t h = __builtin_bit_cast(half2_t, u);
+  return make_float2((float)h.x, (float)h.y);
+}
+// Split partial dims e .. e + 3 of o_part (e: element index, a multiple of 4),
+// in the partials' type (F16: Params::part_f16); written through to the
+// coherent level when the partial kernel merges (Params::counters).
+template <bool F16>
+__device__ __forceinline__ void store_part4(const Params &prm, size_t e, float a, float b, float c, float d) {
+  if constexpr (F16) {
+    uint32_t *q = reinterpret_cast<uint32_t *>(prm.o_part) + e / 2;
+    const uint32_t lo = pack_f16x2(a, b), hi = pack_f16x2(c, d);
+    if (prm.counters) {
+      __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *reinterpret_cast<uint2 *>(q) = make_uint2(lo, hi);
+    }
+  } else {
+    store_partial4(prm, prm.o_part + e, a, b, c, d);
+  }
+}
+__device__ __forceinline__ void store_part4(const Params &prm, size_t e, float a, float b, float c, float d) {
+  if (prm.part_f16)
+    store_part4<true>(prm, e, a, b, c, d);
+  else
+    store_part4<false>(prm, e, a, b, c, d);
+}
+// One element e of o_part (store_part4 where four consecutive dims are at hand).
+template <bool F16> __device__ __forceinline__ void store_part1(const Params &prm, size_t e, float v) {
+  if constexpr (F16) {
+    uint16_t *q = reinterpret_cast<uint16_t *>(prm.o_part) + e;
+    const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)v);
+    if (prm.counters)
+      __hip_atomic_store(q, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *q = h;
+  } else {
+    store_partial(prm, prm.o_part + e, v);
+  }
+}
+// Kernels that know their KV type at compile time: the host sets
+// Params::part_f16 by the same rule.
+template <int KT> constexpr bool part_f16_of() { return KT == DT_FP8 || KT == DT_INT4; }
+// Dims 4 i .. 4 i + 3 of o_part (i: index in units of four elements).
+template <bool F16, bool COHERENT>
+__device__ __forceinline__ float4 load_part4(const float *o_part, size_t i) {
+  if constexpr (F16) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(o_part) + 2 * i;
+    uint32_t lo, hi;
+    if constexpr (COHERENT) {
+      lo = __hip_atomic_load(const_cast<uint32_t *>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hi = __hip_atomic_load(const_cast<uint32_t *>(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2 *>(q);
+      lo = u.x;
+      hi = u.y;
+    }
+    const float2 a = unpack_f16x2(lo), b = unpack_f16x2(hi);
+    return make_float4(a.x, a.y, b.x, b.y);
+  } else if constexpr (COHERENT) {
+    const float *o = o_part + 4 * i;
+    return make_float4(load_partial(o), load_partial(o + 1), load_partial(o + 2), load_partial(o + 3));
+  } else {
+    return reinterpret_cast<const float4 *>(o_part)[i];
+  }
+}
+// The V scale a partial's writer applies to o: none where the merge applies it.
+__device__ __forceinline__ bool writer_scales_v(const Params &p, int nb) { return nb == 1 || !p.part_f16; }
+// The V scale the merge applies to the merged o of KV head kvh of request b.
+__device__ __forceinline__ float merge_vscale(const Params &p, int b, int kvh) {
+  return p.part_f16 && p.v_scale ? p.v_scale[b * p.num_kv_heads + kvh] : 1.0f;
 }
 // Waits until every memory access this thread issued has completed (vmcnt 0;
 // on gfx9 stores count there too), and keeps the compiler from moving memory
@@ -268,7 +354,8 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
 //   sm_m[w][h], sm_l[w][h]: running max (log2 domain) and sum of wave w;
 //   sm_o[w][h][d]: unnormalised accumulator of wave w (fp32).
 // One thread per column first turns the waves' states into weights
-// 2^(m_w - M) * v_scale / L (over sm_m) and the column's lse (into
+// 2^(m_w - M) * v_scale / L (over sm_m; without v_scale for fp16 partials)
+// and the column's lse (into
 // sm_l[0]); then every thread combines four dims of one column with them.
 // The whole workgroup calls it (one barrier inside); sm_m and sm_l are
 // overwritten.
@@ -281,7 +368,8 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, float (*s
     const int h = tid;
     int row, hq;
     const bool has = column_target(p, b, kvg, cg, h, row, hq);
-    const float vscale = has && p.v_scale ? p.v_scale[b * p.num_kv_heads + hq / p.group] : 1.0f;
+    const float vscale =
+        has && p.v_scale && writer_scales_v(p, nb) ? p.v_scale[b * p.num_kv_heads + hq / p.group] : 1.0f;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -327,7 +415,7 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, float (*s
       if (d == 0 && p.lse) p.lse[(size_t)row * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
       const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-      store_partial4(p, p.o_part + (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+      store_part4(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
       if (d == 0) store_partial(p, p.lse_part + slot * p.cols + h, lse2);
     }
   }
@@ -389,15 +477,17 @@ __device__ __forceinline__ void merge_combine(MergeState &a, const MergeState &b
   a.m = M;
 }
 
-// Fold splits tg, tg + step, ... (< nb) of one float4 of outputs: their LSEs
-// at lp[c * lstride] and partials at op[c * ostride], NB loads of each in
-// flight at a time.
-// COHERENT: read with load_partial (the merge inside the partial kernel, which
-// may read partials other XCDs wrote in the same launch); otherwise plain
-// loads (the merge kernel, after the partial kernel has ended).
-template <int NB, bool COHERENT>
+// Fold splits tg, tg + step, ... (< nb) of four outputs: their LSEs at
+// lp[c * lstride] and partials at four-element index o4 + c * ostride of
+// o_part (load_part4; F16: fp16 partials), NB loads of each in flight at a
+// time.
+// COHERENT: read at the coherent level (the merge inside the partial kernel,
+// which may read partials other XCDs wrote in the same launch); otherwise
+// plain loads (the merge kernel, after the partial kernel has ended).
+template <int NB, bool COHERENT, bool F16>
 __device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *lp, size_t lstride,
-                                                  const float4 *op, size_t ostride, int tg, int step, int nb) {
+                                                  const float *o_part, size_t o4, size_t ostride, int tg, int step,
+                                                  int nb) {
   for (int c0 = tg; c0 < nb; c0 += step * NB) {
     float lc[NB];
     float4 v[NB];
@@ -405,14 +495,8 @@ __device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *l
     for (int u = 0; u < NB; ++u) {
       const int c = c0 + u * step;
       if (c < nb) {
-        if constexpr (COHERENT) {
-          const float *o = reinterpret_cast<const float *>(op + (size_t)c * ostride);
-          lc[u] = load_partial(lp + (size_t)c * lstride);
-          v[u] = make_float4(load_partial(o), load_partial(o + 1), load_partial(o + 2), load_partial(o + 3));
-        } else {
-          lc[u] = lp[(size_t)c * lstride];
-          v[u] = op[(size_t)c * ostride];
-        }
+        lc[u] = COHERENT ? load_partial(lp + (size_t)c * lstride) : lp[(size_t)c * lstride];
+        v[u] = load_part4<F16, COHERENT>(o_part, o4 + (size_t)c * ostride);
       } else {
         lc[u] = -INFINITY;
         v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -424,9 +508,11 @@ __device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *l
 }
 
 // Final output of one merged float4 (dims d .. d + 3 of query row / head
-// (row, hq)), and its lse from the thread that holds dim 0.
-__device__ __forceinline__ void merge_store(const Params &p, const MergeState &st, int row, int hq, int D, int d) {
-  const float inv = st.w > 0.0f ? 1.0f / st.w : 0.0f;
+// (row, hq)), times vs (merge_vscale), and its lse from the thread that holds
+// dim 0.
+__device__ __forceinline__ void merge_store(const Params &p, const MergeState &st, int row, int hq, int D, int d,
+                                            float vs) {
+  const float inv = st.w > 0.0f ? vs / st.w : 0.0f;
   const float4 o = make_float4(st.acc.x * inv, st.acc.y * inv, st.acc.z * inv, st.acc.w * inv);
   const size_t off = ((size_t)row * p.num_qo_heads + hq) * D + d;
   if (p.out_bf16) {
@@ -444,7 +530,8 @@ __device__ __forceinline__ void merge_store(const Params &p, const MergeState &s
 // - 1) and write the final outputs.  The whole workgroup calls it; s_st holds
 // kThreads states of LDS.  When the outputs are fewer than the threads,
 // thread groups share the splits of each output and combine through LDS.
-template <int D, int NB>
+// PACK: KV heads per pack (1 with several query rows per request).
+template <int D, int PACK, int NB>
 __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int ncg, int first, int nb,
                              MergeState *s_st) {
   constexpr int D4 = D / 4;
@@ -453,7 +540,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
   const int ncg_live = min(ncg, p.col_groups - cg_first);
   const int F = ncg_live * cols * D4;                // float4 outputs
   const int SG = F >= kThreads ? 1 : kThreads / F;  // thread groups over the splits
-  const size_t ostride = (size_t)cols * D4;         // float4 between consecutive splits of one slot
+  const size_t ostride = (size_t)cols * D4;         // four-element units between consecutive splits of one slot
   for (int f0 = 0; f0 < F; f0 += kThreads) {
     const int t = f0 + (SG > 1 ? tid % F : tid);
     const int tg = SG > 1 ? tid / F : 0;
@@ -463,10 +550,16 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
     int row = 0, hq = 0;
     const bool has = t < F && tg < SG && column_target(p, b, kvg, cg_first + cgi, h, row, hq);
     MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    // the column's KV head: uniform in the workgroup with one KV head per pack
+    const float vs = merge_vscale(p, b, PACK == 1 ? kvg : kvg * PACK + h / p.group);
     if (has) {
       const size_t slot0 = ((size_t)kvg * p.col_groups + cg_first + cgi) * p.items + first;
-      const float4 *op = reinterpret_cast<const float4 *>(p.o_part) + (slot0 * cols + h) * D4 + d / 4;
-      merge_fold_splits<NB, true>(st, p.lse_part + slot0 * cols + h, cols, op, ostride, tg, SG, nb);
+      const size_t o4 = (slot0 * cols + h) * D4 + d / 4;
+      if (p.part_f16)
+        merge_fold_splits<NB, true, true>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg, SG, nb);
+      else
+        merge_fold_splits<NB, true, false>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg, SG,
+                                           nb);
     }
     if (SG > 1) { // one pass only (F < kThreads): the barriers are uniform
       s_st[tid] = st;
@@ -474,7 +567,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
       if (tid < F)
         for (int j = 1; j < SG; ++j) merge_combine(st, s_st[tid + j * F]);
     }
-    if (has && tg == 0) merge_store(p, st, row, hq, D, d);
+    if (has && tg == 0) merge_store(p, st, row, hq, D, d, vs);
   }
 }
 
@@ -489,7 +582,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
 // Call with the whole workgroup, after the partial stores; `lds` (at least
 // kThreads MergeStates) may be any LDS no thread still reads.  NB: loads in
 // flight per thread during the merge (fewer where registers are tight).
-template <int D, int NB = kFusedMergeBatch>
+template <int D, int PACK = 1, int NB = kFusedMergeBatch>
 __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, int kvg, int cg_first, int ncg,
                                              int item, int split, int nb, void *lds, int npack = 1) {
   __shared__ int s_last;
@@ -502,7 +595,7 @@ __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, 
   if (!s_last) return;
   for (int k = 0; k < npack; ++k) { // KV-head packs kvg .. kvg + npack - 1 (the same in every thread)
     if (k > 0) __syncthreads();     // the previous pack's merge has read its LDS states
-    merge_splits<D, NB>(p, b, kvg + k, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
+    merge_splits<D, PACK, NB>(p, b, kvg + k, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
   }
   if (threadIdx.x == 0) atomicExch(ctr, 0u); // every split of this call has arrived: ready for the next call
 }

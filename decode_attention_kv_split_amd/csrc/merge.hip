@@ -40,8 +40,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
   const int d0 = slice * Ds;
   const int F = g * Ds / 4;                        // float4 outputs of this workgroup
   const int SG = F >= kThreads ? 1 : kThreads / F; // thread groups splitting the splits
-  const size_t cstride = (size_t)g * D / 4;        // float4 between consecutive splits
-  const float4 *op = reinterpret_cast<const float4 *>(p.o_part) + slot0 * cstride;
+  const size_t cstride = (size_t)g * D / 4;        // four-element units between consecutive splits
   const float *lp = p.lse_part + slot0 * g;
   for (int f0 = 0; f0 < F; f0 += kThreads) {
     const int t = f0 + (SG > 1 ? tid % F : tid);
@@ -50,7 +49,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
     const int h = t / (Ds / 4);
     const int d = d0 + 4 * (t % (Ds / 4));
     MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    if (active) merge_fold_splits<kMergeBatch, false>(st, lp + h, g, op + ((size_t)h * D + d) / 4, cstride, tg, SG, nb);
+    const size_t o4 = slot0 * cstride + ((size_t)h * D + d) / 4;
+    if (active) {
+      if (p.part_f16)
+        merge_fold_splits<kMergeBatch, false, true>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb);
+      else
+        merge_fold_splits<kMergeBatch, false, false>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb);
+    }
     if (SG > 1) {
       s_st[tid] = st;
       __syncthreads();
@@ -58,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
         for (int j = 1; j < SG; ++j) merge_combine(st, s_st[tid + j * F]);
     }
     int row, hq;
-    if (active && tg == 0 && column_target(p, b, kvg, cg, h, row, hq)) merge_store(p, st, row, hq, D, d);
+    if (active && tg == 0 && column_target(p, b, kvg, cg, h, row, hq))
+      merge_store(p, st, row, hq, D, d, merge_vscale(p, b, hq / p.group));
   }
 }
 

@@ -70,10 +70,12 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
 // (the group size with one query per request, col_groups * 16 with
 // several); col_blocks: partial workgroups per (item, KV head); pack: KV
 // heads per workgroup; wave_packs: KV-head packs per workgroup (4: one per
-// wave over the whole chunk; 1: the waves split one pack's tiles).  Returns
-// false if a length is negative.  Workspace layout when a request has several
+// wave over the whole chunk; 1: the waves split one pack's tiles);
+// part_bytes: bytes per element of the split partials o_part (4: fp32, 2:
+// fp16).  Returns false if a length is negative.  Workspace layout when a request has several
 // splits: [counters][o_part][lse_part][meta].
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int pack, int wave_packs, int head_dim, int forced_chunk, int num_cus, Plan *out);
+               int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, int forced_chunk, int num_cus,
+               Plan *out);
 
 } // namespace kvs

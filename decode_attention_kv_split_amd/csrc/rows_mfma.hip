@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
     }
     if (!cs.ok[c]) continue;
     const bool live = l_tot > 0.0f; // a finite reference with no visible key leaves l = 0: empty
-    const float vscale = p.v_scale ? p.v_scale[b * Hk + kvg] : 1.0f;
+    const float vscale = p.v_scale && (nb == 1 || !part_f16_of<KT>()) ? p.v_scale[b * Hk + kvg] : 1.0f;
     const float inv = live ? vscale / l_tot : 0.0f;
     const float lse2 = live ? cs.m[c] + __log2f(l_tot) : -INFINITY;
     // INT4: V entered the product as 136 + n; remove 136 * (sum of the weights it saw)
@@ -216,12 +216,13 @@ __global__ __launch_bounds__(kThreads) void partial_rows_kernel(const Params p, 
     } else {
       const int cg = cgw + wave * CG + c;
       const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-      float *dst = p.o_part + (slot * p.cols + c16) * D;
+      const size_t dst = (slot * p.cols + c16) * D;
 #pragma unroll
       for (int wt = 0; wt < S::kOTiles; ++wt) {
         const int od = out_dim<D, KT>(wt, q4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) store_partial(p, dst + od + r * S::kOutStride, (cs.acc[c][wt][r] - voff) * inv);
+        for (int r = 0; r < 4; ++r)
+          store_part1<part_f16_of<KT>()>(p, dst + od + r * S::kOutStride, (cs.acc[c][wt][r] - voff) * inv);
       }
       if (q4 == 0) store_partial(p, p.lse_part + slot * p.cols + c16, lse2);
     }
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!ok) return;
   const bool live = l_tot > 0.0f;
-  const float vscale = kPerm ? p.v_scale[b * Hk + kvg] : 1.0f;
+  const float vscale = kPerm && writer_scales_v(p, nb) ? p.v_scale[b * Hk + kvg] : 1.0f;
   const float inv = live ? vscale / l_tot : 0.0f;
   const float lse2 = live ? m_run + __log2f(l_tot) : -INFINITY;
   if constexpr (kInt4) {
@@ -798,14 +799,14 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     // blk, so registers 4 q .. 4 q + 3 of the pair are dims
     // 64 blk + 16 q + 8 h2 .. + 7, interleaved.
     const float voff = kInt4Offset * (lb_run + __shfl_xor(lb_run, 32, 64));
-    float *dst = nullptr;
+    size_t dst = 0;
     uint16_t *orow = nullptr;
     size_t slot = 0;
     if (nb == 1) {
       orow = reinterpret_cast<uint16_t *>(p.o) + ((size_t)qrow * p.num_qo_heads + qhead) * D;
     } else {
       slot = ((size_t)kvg * p.col_groups + col / 16) * p.items + item;
-      dst = p.o_part + (slot * p.cols + col % 16) * D;
+      dst = (slot * p.cols + col % 16) * D;
     }
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -822,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
           *reinterpret_cast<uint4 *>(orow + d0) = make_uint4(pack_bf16x2(o8[0], o8[1]), pack_bf16x2(o8[2], o8[3]),
                                                              pack_bf16x2(o8[4], o8[5]), pack_bf16x2(o8[6], o8[7]));
         } else {
-          store_partial4(p, dst + d0, o8[0], o8[1], o8[2], o8[3]);
-          store_partial4(p, dst + d0 + 4, o8[4], o8[5], o8[6], o8[7]);
+          store_part4(p, dst + d0, o8[0], o8[1], o8[2], o8[3]);
+          store_part4(p, dst + d0 + 4, o8[4], o8[5], o8[6], o8[7]);
         }
       }
     if (h2 == 0) {
@@ -850,13 +851,13 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   } else {
     const int cg = col / 16;
     const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-    float *dst = p.o_part + (slot * p.cols + col % 16) * D;
+    const size_t dst = (slot * p.cols + col % 16) * D;
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d0 = 128 * dh + 32 * sl + 8 * q + 4 * h2;
-        store_partial4(p, dst + d0, acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv,
+        store_part4(p, dst + d0, acc[sl][4 * q] * inv, acc[sl][4 * q + 1] * inv, acc[sl][4 * q + 2] * inv,
                        acc[sl][4 * q + 3] * inv);
       }
     if (h2 == 0 && dh == 0) store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);

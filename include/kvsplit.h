@@ -244,11 +244,15 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
  * one split).  Its first KVS_WORKSPACE_COUNTER_BYTES hold arrival counters:
  * they must be zero before the first call that uses the workspace (allocate
  * it zeroed), and every call leaves them zero.  With the work list planned
- * on the host (batch <= 256, at most 448 splits per KV head) the workgroup
- * that writes a request's last split merges all of its splits (one launch;
- * no workgroup waits for another); otherwise a second kernel merges.  The
- * rest of the workspace holds the per-split partial outputs (fp32) and their
- * log-sum-exp values, rewritten by every call.
+ * on the host (batch <= 256, at most 1344 splits per KV head and 256 per
+ * request) the workgroup that writes a request's last split merges all of
+ * its splits when that pays (merge_mode; one launch, no workgroup waits for
+ * another); otherwise a second kernel merges.  The rest of the workspace
+ * holds the per-split partial outputs and their log-sum-exp values (fp32),
+ * rewritten by every call.  The partial outputs are fp32 for bf16 and fp32
+ * caches; for fp8 and INT4 caches they are fp16 weighted averages of the
+ * stored codes, which lie inside the codes' range (the merge applies the V
+ * scale), so fp16 keeps 11 significant bits at half the bytes.
  * Preconditions that are not checked (they would need a device sync):
  * kv_len equals kv_len_host, page_indptr[b+1] - page_indptr[b] >=
  * ceil(kv_len[b] / page_size), every page id is < num_pages, and all

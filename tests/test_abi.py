@@ -252,6 +252,21 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
         assert info.workspace_bytes == 0
 
 
+@pytest.mark.parametrize("kv,part_bytes", [(kvs.KVS_BF16, 4), (kvs.KVS_FP8_E4M3, 2), (kvs.KVS_INT4, 2)])
+def test_split_partials_size_by_kv_type(lib, kv, part_bytes):
+    """The split partial outputs are fp32 for bf16 caches and fp16 (code
+    averages, V scale applied by the merge) for fp8 and INT4 caches; their
+    LSEs are fp32 either way."""
+    a, keep = _args(kv=kv, lens=(100, 3000, 5000), batch=3, chunk=256, algo=kvs.KVS_ALGO_MFMA)
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge
+    g = 4
+    slots = info.items_per_kv_head * 2 * g
+    r256 = lambda n: -(-n // 256) * 256
+    want = r256(slots * 128 * part_bytes) + r256(slots * 4) + r256(3 * 8)
+    assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+
+
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):
     a, keep = _args(batch=1, Hq=32, Hk=32, P=0, lens=(32768,), num_pages=32768)
     cus = a.num_cus
