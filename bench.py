@@ -46,13 +46,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538246011, "digest": "9f22d5a896db0291511caec78ca24a33c6fd007c3cc06d260cd4243c41ea4fd3"},
+        {"bytes": 538243695, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299475331, "digest": "9f22d5a896db0291511caec78ca24a33c6fd007c3cc06d260cd4243c41ea4fd3"},
+        {"bytes": 2299497163, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1487913707, "digest": "9f22d5a896db0291511caec78ca24a33c6fd007c3cc06d260cd4243c41ea4fd3"},
+        {"bytes": 1483203372, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 680888463, "digest": "9f22d5a896db0291511caec78ca24a33c6fd007c3cc06d260cd4243c41ea4fd3"},
+        {"bytes": 676094612, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
 }
 
 
