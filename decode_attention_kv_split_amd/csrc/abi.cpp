@@ -218,10 +218,17 @@ Columns columns_of(const kvs_decode_args *a) {
   return c;
 }
 
-// KV heads per partial workgroup for the resolved kernel family.
 // Split partials of fp8 and INT4 caches are fp16 averages of the stored codes
-// (the merge applies the V scale); those of bf16 and fp32 caches are fp32.
-bool part_f16(const kvs_decode_args *a) { return a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4; }
+// (the merge applies the V scale); those of fp32 caches are fp32.  Those of
+// bf16 caches are fp16 rows scaled by a power of two (the multiplier beside
+// each row's LSE) where the decode kernel writes them, one column group per
+// workgroup; the other kernels write them in fp32.
+bool part_codes_f16(const kvs_decode_args *a) { return a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4; }
+bool part_row_scaled(const kvs_decode_args *a, int algo, const Columns &c) {
+  return a->kv_dtype == KVS_BF16 && algo != KVS_ALGO_VALU && c.col_share == 1;
+}
+
+// KV heads per partial workgroup for the resolved kernel family.
 
 int kv_pack(const kvs_decode_args *a, int algo) {
   if (algo == KVS_ALGO_VALU) return 1;
@@ -256,10 +263,11 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   const bool heads = heads_fit(a, *algo, c);
   if (a->wave_split == KVS_WAVES_HEADS && !heads) return KVS_ERR_UNSUPPORTED;
   const int32_t *nq = c.nq.empty() ? nullptr : c.nq.data();
-  const int part_bytes = part_f16(a) ? 2 : 4;
+  const bool row_scaled = part_row_scaled(a, *algo, c);
+  const int part_bytes = part_codes_f16(a) || row_scaled ? 2 : 4;
   if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
-                      a->wave_split == KVS_WAVES_HEADS ? kvs::kWaves : 1, a->head_dim, part_bytes, a->kv_chunk, *cus,
-                      pl))
+                      a->wave_split == KVS_WAVES_HEADS ? kvs::kWaves : 1, a->head_dim, part_bytes, row_scaled,
+                      a->kv_chunk, *cus, pl))
     return KVS_ERR_INVALID_ARG;
   // Automatic wave split: the tiles split, unless the heads split can keep
   // the tiles plan's chunks (at most 64 tiles per wave) and still give every
@@ -271,7 +279,7 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   if (a->wave_split == KVS_WAVES_AUTO && heads && pl->chunk <= kvs::kMaxWaveChunk &&
       head_wgs >= std::max(1, *cus)) {
     if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
-                        kvs::kWaves, a->head_dim, part_bytes, pl->chunk, *cus, pl))
+                        kvs::kWaves, a->head_dim, part_bytes, row_scaled, pl->chunk, *cus, pl))
       return KVS_ERR_INVALID_ARG;
   }
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
@@ -399,9 +407,12 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.counters = nullptr;
   p.o_part = pl.workspace_bytes ? reinterpret_cast<float *>(ws + pl.counter_bytes) : nullptr;
   p.lse_part = pl.workspace_bytes ? reinterpret_cast<float *>(ws + pl.counter_bytes + pl.o_part_bytes) : nullptr;
-  p.meta = pl.workspace_bytes
-               ? reinterpret_cast<int *>(ws + pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes)
-               : nullptr;
+  p.sc_part = pl.sc_part_bytes ? reinterpret_cast<float *>(ws + pl.counter_bytes + pl.o_part_bytes +
+                                                           pl.lse_part_bytes)
+                               : nullptr;
+  p.meta = pl.workspace_bytes ? reinterpret_cast<int *>(ws + pl.counter_bytes + pl.o_part_bytes +
+                                                        pl.lse_part_bytes + pl.sc_part_bytes)
+                              : nullptr;
   p.batch = a->batch;
   p.num_qo_heads = a->num_qo_heads;
   p.num_kv_heads = a->num_kv_heads;
@@ -423,7 +434,8 @@ kvs_status kvs_decode(const kvs_decode_args *a, void *workspace, size_t workspac
   p.chunk = pl.chunk;
   p.items = pl.items;
   p.out_bf16 = a->q_dtype == KVS_BF16 ? 1 : 0;
-  p.part_f16 = part_f16(a) ? 1 : 0;
+  p.part_row_scale = pl.sc_part_bytes ? 1 : 0;
+  p.part_f16 = part_codes_f16(a) || p.part_row_scale ? 1 : 0;
   // with a soft cap c the kernels form tanh(sm_scale / c * qk) * c * log2(e)
   const bool capped = a->logits_soft_cap > 0.0f;
   p.score_scale = capped ? a->sm_scale / a->logits_soft_cap : a->sm_scale * kvs::kLog2e;

@@ -70,6 +70,8 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
   constexpr int DE = D * PACK;
   using S = Shape<DE, KT>;
   constexpr int OSTRIDE = D + 4;
+  // bf16 caches: split partials stored as row-scaled fp16 when the host asks
+  constexpr bool ROWSC = KT == DT_BF16;
   constexpr int kStageBytes = kWaves * NBUF * 2 * S::kTileBytes;
   constexpr int kEpiBytes = 2 * kWaves * 16 * 4 + kWaves * 16 * OSTRIDE * 4;
   constexpr int kSmem = kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes;
@@ -246,17 +248,36 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
     }
     const size_t slot = (size_t)kvg * p.items + item; // one column group
     const bool live = l_tot > 0.0f;                   // else no visible key: o = 0, lse = -inf
+    const bool row_scaled = ROWSC && p.part_row_scale && nb > 1;
+    // row-scaled partials: the largest |acc| of the lane's column over the
+    // pack's dims it holds, then over the column's four lane quarters
+    float amax = 0.0f;
+    if (row_scaled) {
+#pragma unroll
+      for (int w = 0; w < S::kOTiles; ++w)
+        if (out_dim<DE, KT>(w, q4) / D == my_kv)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(cs.acc[0][w][r]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    }
     float inv = 0.0f;
     if (cs.ok[0]) {
       const int hq = cs.head[0];
       const float vscale = p.v_scale && writer_scales_v(p, nb) ? p.v_scale[b * Hk + hq / g] : 1.0f;
       inv = live ? vscale / l_tot : 0.0f;
+      int k = 0;
+      if (row_scaled) { // the column's partial row is stored times 2^k
+        k = row_scale_exp(amax * inv);
+        inv = ldexpf(inv, k);
+      }
       if (q4 == 0) {
         const float lse2 = live ? cs.m[0] + __log2f(l_tot) : -INFINITY;
         if (nb == 1) {
           if (p.lse) p.lse[(size_t)cs.row[0] * p.num_qo_heads + hq] = lse2 * kLn2;
         } else {
           store_partial(p, p.lse_part + slot * p.cols + c16, lse2);
+          if (row_scaled) store_partial(p, p.sc_part + slot * p.cols + c16, ldexpf(1.0f, -k));
         }
       }
     }
@@ -300,12 +321,15 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
           const size_t off = ((size_t)b * p.num_qo_heads + kvg * gp + h) * D + d; // bf16 q and o (matrix-core path)
           *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.o) + off) =
               make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        } else if (row_scaled) {
+          store_part4<true>(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
         } else {
           store_part4(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
         }
       }
     }
-    finish_split<D, PACK>(p, blockIdx.y, b, blockIdx.y * kWaves, 0, 1, item, split, nb, smem, kWaves);
+    finish_split<D, PACK, kFusedMergeBatch, ROWSC>(p, blockIdx.y, b, blockIdx.y * kWaves, 0, 1, item, split, nb,
+                                                   smem, kWaves);
     return;
   }
   __syncthreads(); // staging area is reused for the per-wave states below
@@ -348,9 +372,9 @@ __global__ __launch_bounds__(kThreads) void partial_mfma_kernel(const Params p, 
       }
     }
     __syncthreads();
-    merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
+    merge_waves_and_store<D, OSTRIDE, ROWSC>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
-  finish_split<D, PACK>(p, blockIdx.y, b, kvg, cg0, CG, item, split, nb, smem);
+  finish_split<D, PACK, kFusedMergeBatch, ROWSC>(p, blockIdx.y, b, kvg, cg0, CG, item, split, nb, smem);
 }
 
 } // namespace

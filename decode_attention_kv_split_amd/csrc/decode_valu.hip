@@ -252,6 +252,7 @@ hipError_t launch_valu_dk(const Params &p, const InlineWork &w, const Launch &l)
 int valu_max_group(int kv_dtype) { return kv_dtype == DT_FP8 ? 8 : 16; }
 
 hipError_t launch_partial_valu(const Params &p, const InlineWork &w, int head_dim, int kv_dtype, const Launch &l) {
+  if (p.part_row_scale) return hipErrorInvalidValue; // this kernel writes fp32 or code partials
   switch (kv_dtype) {
   case DT_F32:
     switch (head_dim) {

@@ -25,11 +25,15 @@
 // col_groups + cg (already divided by the chunk's sum) and
 // lse_part[(S * I + x) * cols + h] (fp32, log2 domain: chunk max + log2(chunk
 // sum), -inf when the chunk saw no key), I = items per KV head.  o_part is
-// fp32 and includes the V scale for bf16 and fp32 caches.  For fp8 and INT4
-// caches (part_f16) it is fp16 and leaves the V scale to the merge: it then
-// holds a weighted average of the decoded codes, which lies inside their range
-// (|x| <= 448 for e4m3, <= 8 for INT4), where fp16 keeps 11 significant bits;
-// half the bytes of fp32.
+// fp32 and includes the V scale for fp32 caches and for bf16 caches outside
+// the decode kernel.  For fp8 and INT4 caches (part_f16) it is fp16 and
+// leaves the V scale to the merge: it then holds a weighted average of the
+// decoded codes, which lies inside their range (|x| <= 448 for e4m3, <= 8 for
+// INT4), where fp16 keeps 11 significant bits; half the bytes of fp32.  A
+// bf16 cache's averages have no such bound, so the decode kernel stores each
+// partial row scaled by a power of two that puts its largest magnitude in
+// [2^14, 2^15) and leaves the inverse in sc_part[(S * I + x) * cols + h]
+// (part_row_scale); the merge multiplies it back (exact).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -95,7 +99,10 @@ struct Params {
   int rows_xcd_order; // multi-row kernels: workgroups in the XCD-balanced order (rows_order)
   float m_init;   // reference max each chunk starts from (log2 units; -inf: none)
   int out_bf16;   // o (and q) stored as bf16
-  int part_f16;   // split partials o_part hold fp16 averages of the stored V codes (fp8, INT4 caches)
+  int part_f16;   // split partials o_part are fp16: averages of the stored V codes (fp8, INT4 caches)
+                  // or, with part_row_scale, row-scaled averages of bf16 V
+  int part_row_scale; // each fp16 partial row is scaled; sc_part holds the multiplier that restores it
+  float *sc_part;     // [slots][cols] multipliers (powers of two) of the partial rows (part_row_scale)
   float score_scale; // sm_scale * log2(e); with a soft cap c: sm_scale / c
   float cap_out;     // soft cap: scores become tanh(score_scale * qk) * cap_out, cap_out = c * log2(e); 0: no cap
   // Merge in the partial kernel (null: a second kernel merges): one arrival
@@ -189,6 +196,16 @@ template <bool F16> __device__ __forceinline__ void store_part1(const Params &pr
   } else {
     store_partial(prm, prm.o_part + e, v);
   }
+}
+// Row-scaled fp16 partials (Params::part_row_scale): a partial row whose
+// largest magnitude is mx is stored times 2^k, which puts mx in [2^14, 2^15)
+// (11 significant bits there, no fp16 overflow); the merge multiplies by 2^-k
+// (both exact).  k is kept within [-85, 115] so that both factors stay normal
+// fp32 numbers.
+__device__ __forceinline__ int row_scale_exp(float mx) {
+  int ex = 0;
+  (void)frexpf(mx, &ex); // mx = f * 2^ex, f in [0.5, 1); 0 gives ex = 0
+  return 15 - min(max(ex, -100), 100);
 }
 // Kernels that know their KV type at compile time: the host sets
 // Params::part_f16 by the same rule.
@@ -359,7 +376,9 @@ __device__ __forceinline__ void scan_requests(const Params &p, int *scratch, F &
 // sm_l[0]); then every thread combines four dims of one column with them.
 // The whole workgroup calls it (one barrier inside); sm_m and sm_l are
 // overwritten.
-template <int D, int OSTRIDE>
+// ROWSC: a split's partial rows are stored row-scaled (part_row_scale) when
+// the host asks for it.
+template <int D, int OSTRIDE, bool ROWSC = false>
 __device__ __forceinline__ void merge_waves_and_store(const Params &p, float (*sm_m)[16], float (*sm_l)[16],
                                                       const float *sm_o, int b, int kvg, int cg, int item, int nb) {
   static_assert(D % 4 == 0 && OSTRIDE % 4 == 0, "float4 rows");
@@ -415,7 +434,20 @@ __device__ __forceinline__ void merge_waves_and_store(const Params &p, float (*s
       if (d == 0 && p.lse) p.lse[(size_t)row * p.num_qo_heads + hq] = lse2 * kLn2;
     } else {
       const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
-      store_part4(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+      if (ROWSC && p.part_row_scale) {
+        // the row's largest magnitude over the D / 4 threads of its column
+        // (aligned lanes of one wave, all active: a column is padding or not
+        // as a whole)
+        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+        for (int off = 1; off < D / 4; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const int k = row_scale_exp(mx);
+        const float sc = ldexpf(1.0f, k);
+        store_part4<true>(p, (slot * p.cols + h) * D + d, v.x * sc, v.y * sc, v.z * sc, v.w * sc);
+        if (d == 0) store_partial(p, p.sc_part + slot * p.cols + h, ldexpf(1.0f, -k));
+      } else {
+        store_part4(p, (slot * p.cols + h) * D + d, v.x, v.y, v.z, v.w);
+      }
       if (d == 0) store_partial(p, p.lse_part + slot * p.cols + h, lse2);
     }
   }
@@ -484,26 +516,32 @@ __device__ __forceinline__ void merge_combine(MergeState &a, const MergeState &b
 // COHERENT: read at the coherent level (the merge inside the partial kernel,
 // which may read partials other XCDs wrote in the same launch); otherwise
 // plain loads (the merge kernel, after the partial kernel has ended).
-template <int NB, bool COHERENT, bool F16>
+// SC: partial rows carry multipliers at sp[c * lstride] (part_row_scale).
+template <int NB, bool COHERENT, bool F16, bool SC = false>
 __device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *lp, size_t lstride,
                                                   const float *o_part, size_t o4, size_t ostride, int tg, int step,
-                                                  int nb) {
+                                                  int nb, const float *sp = nullptr) {
   for (int c0 = tg; c0 < nb; c0 += step * NB) {
-    float lc[NB];
+    float lc[NB], sc[NB];
     float4 v[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int c = c0 + u * step;
+      sc[u] = 1.0f;
       if (c < nb) {
         lc[u] = COHERENT ? load_partial(lp + (size_t)c * lstride) : lp[(size_t)c * lstride];
         v[u] = load_part4<F16, COHERENT>(o_part, o4 + (size_t)c * ostride);
+        if constexpr (SC) sc[u] = COHERENT ? load_partial(sp + (size_t)c * lstride) : sp[(size_t)c * lstride];
       } else {
         lc[u] = -INFINITY;
         v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
 #pragma unroll
-    for (int u = 0; u < NB; ++u) merge_fold(st, lc[u], v[u]);
+    for (int u = 0; u < NB; ++u) {
+      if constexpr (SC) v[u] = make_float4(v[u].x * sc[u], v[u].y * sc[u], v[u].z * sc[u], v[u].w * sc[u]);
+      merge_fold(st, lc[u], v[u]);
+    }
   }
 }
 
@@ -530,8 +568,9 @@ __device__ __forceinline__ void merge_store(const Params &p, const MergeState &s
 // - 1) and write the final outputs.  The whole workgroup calls it; s_st holds
 // kThreads states of LDS.  When the outputs are fewer than the threads,
 // thread groups share the splits of each output and combine through LDS.
-// PACK: KV heads per pack (1 with several query rows per request).
-template <int D, int PACK, int NB>
+// PACK: KV heads per pack (1 with several query rows per request).  ROWSC:
+// the kernel may write row-scaled fp16 partials (part_row_scale).
+template <int D, int PACK, int NB, bool ROWSC>
 __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int ncg, int first, int nb,
                              MergeState *s_st) {
   constexpr int D4 = D / 4;
@@ -555,7 +594,10 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
     if (has) {
       const size_t slot0 = ((size_t)kvg * p.col_groups + cg_first + cgi) * p.items + first;
       const size_t o4 = (slot0 * cols + h) * D4 + d / 4;
-      if (p.part_f16)
+      if (ROWSC && p.part_row_scale)
+        merge_fold_splits<NB, true, true, ROWSC>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg,
+                                                SG, nb, p.sc_part + slot0 * cols + h);
+      else if (p.part_f16)
         merge_fold_splits<NB, true, true>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg, SG, nb);
       else
         merge_fold_splits<NB, true, false>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg, SG,
@@ -582,7 +624,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
 // Call with the whole workgroup, after the partial stores; `lds` (at least
 // kThreads MergeStates) may be any LDS no thread still reads.  NB: loads in
 // flight per thread during the merge (fewer where registers are tight).
-template <int D, int PACK = 1, int NB = kFusedMergeBatch>
+template <int D, int PACK = 1, int NB = kFusedMergeBatch, bool ROWSC = false>
 __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, int kvg, int cg_first, int ncg,
                                              int item, int split, int nb, void *lds, int npack = 1) {
   __shared__ int s_last;
@@ -595,7 +637,7 @@ __device__ __forceinline__ void finish_split(const Params &p, int yslot, int b, 
   if (!s_last) return;
   for (int k = 0; k < npack; ++k) { // KV-head packs kvg .. kvg + npack - 1 (the same in every thread)
     if (k > 0) __syncthreads();     // the previous pack's merge has read its LDS states
-    merge_splits<D, PACK, NB>(p, b, kvg + k, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
+    merge_splits<D, PACK, NB, ROWSC>(p, b, kvg + k, cg_first, ncg, item - split, nb, reinterpret_cast<MergeState *>(lds));
   }
   if (threadIdx.x == 0) atomicExch(ctr, 0u); // every split of this call has arrived: ready for the next call
 }

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
     MergeState st = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
     const size_t o4 = slot0 * cstride + ((size_t)h * D + d) / 4;
     if (active) {
-      if (p.part_f16)
+      if (p.part_row_scale)
+        merge_fold_splits<kMergeBatch, false, true, true>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb,
+                                                           p.sc_part + slot0 * g + h);
+      else if (p.part_f16)
         merge_fold_splits<kMergeBatch, false, true>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb);
       else
         merge_fold_splits<kMergeBatch, false, false>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb);

@@ -10,8 +10,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(0, L - nq + 1 - window) : 0; }
 
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, int forced_chunk, int num_cus,
-               Plan *out) {
+               int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, bool row_scales,
+               int forced_chunk, int num_cus, Plan *out) {
   Plan pl;
   wave_packs = std::max(1, wave_packs);
   const bool per_wave = wave_packs > 1;
@@ -63,6 +63,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
     pl.counter_bytes = kPlanCounterBytes;
     pl.o_part_bytes = align256(slots * head_dim * part_bytes);
     pl.lse_part_bytes = align256(slots * sizeof(float));
+    pl.sc_part_bytes = row_scales ? align256(slots * sizeof(float)) : 0;
     pl.meta_bytes = align256((size_t)batch * 2 * sizeof(int));
     // one counter per (KV head, column block, request) at most (packing two
     // KV heads per workgroup halves it)
@@ -79,7 +80,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
     const int64_t wgs = items * (int64_t)(num_kv_heads / std::max(1, pack)) * col_blocks / wave_packs;
     pl.fused_pays = pl.fused && wgs <= std::max(1, num_cus) && max_splits <= 8;
   }
-  pl.workspace_bytes = pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes + pl.meta_bytes;
+  pl.workspace_bytes = pl.counter_bytes + pl.o_part_bytes + pl.lse_part_bytes + pl.sc_part_bytes + pl.meta_bytes;
   *out = pl;
   return true;
 }

@@ -29,6 +29,7 @@ struct Plan {
   size_t counter_bytes = 0; // arrival counters at the start of the workspace (zero between calls)
   size_t o_part_bytes = 0;
   size_t lse_part_bytes = 0;
+  size_t sc_part_bytes = 0; // multipliers of row-scaled fp16 partials (0: none)
   size_t meta_bytes = 0;
   size_t workspace_bytes = 0;
 };
@@ -72,10 +73,12 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
 // heads per workgroup; wave_packs: KV-head packs per workgroup (4: one per
 // wave over the whole chunk; 1: the waves split one pack's tiles);
 // part_bytes: bytes per element of the split partials o_part (4: fp32, 2:
-// fp16).  Returns false if a length is negative.  Workspace layout when a request has several
-// splits: [counters][o_part][lse_part][meta].
+// fp16); row_scales: each partial row has an fp32 multiplier (sc_part, laid
+// out like lse_part).  Returns false if a length is negative.  Workspace
+// layout when a request has several splits:
+// [counters][o_part][lse_part][sc_part][meta].
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
-               int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, int forced_chunk, int num_cus,
-               Plan *out);
+               int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, bool row_scales,
+               int forced_chunk, int num_cus, Plan *out);
 
 } // namespace kvs

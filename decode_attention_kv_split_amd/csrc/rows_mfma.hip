@@ -1359,7 +1359,7 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
 }
 
 hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, const Launch &l) {
-  if (p.col_share != 2 || p.pack != 1) return hipErrorInvalidValue;
+  if (p.col_share != 2 || p.pack != 1 || p.part_row_scale) return hipErrorInvalidValue; // fp32 or code partials
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2));
   // one 16 KB bf16 slot per wave, two 8 KB fp8 ones, four 4 KB INT4 ones: 64 KB per workgroup
   if (kv_type == DT_FP8) return launch_kernel(l, partial_cols32_kernel<DT_FP8, 2>, grid, p, w);
@@ -1371,6 +1371,7 @@ hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, cons
 bool rows_merge_in_kernel(int head_dim, int kv_type) { return rows_merges_in_kernel(head_dim, kv_type); }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
+  if (p.part_row_scale) return hipErrorInvalidValue; // these kernels write fp32 or code partials
   if (kv_type == DT_INT4) {
     if (head_dim == 128) return launch_rows_d<128, DT_INT4>(p, w, l);
     if (head_dim == 256) return launch_rows_d<256, DT_INT4>(p, w, l);

@@ -245,25 +245,49 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
         assert covered == list(range(lo, L))
     g = 4
     if info.needs_merge:
+        # bf16 decode-kernel partials: fp16 rows, then their LSEs and multipliers
         slots = info.items_per_kv_head * 2 * g
-        want = (-(-slots * 128 * 4 // 256) * 256) + (-(-slots * 4 // 256) * 256) + (-(-len(lens) * 8 // 256) * 256)
+        r256 = lambda n: -(-n // 256) * 256
+        want = r256(slots * 128 * 2) + 2 * r256(slots * 4) + r256(len(lens) * 8)
         assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want  # counters, then the partials
     else:
         assert info.workspace_bytes == 0
 
 
-@pytest.mark.parametrize("kv,part_bytes", [(kvs.KVS_BF16, 4), (kvs.KVS_FP8_E4M3, 2), (kvs.KVS_INT4, 2)])
-def test_split_partials_size_by_kv_type(lib, kv, part_bytes):
-    """The split partial outputs are fp32 for bf16 caches and fp16 (code
-    averages, V scale applied by the merge) for fp8 and INT4 caches; their
-    LSEs are fp32 either way."""
-    a, keep = _args(kv=kv, lens=(100, 3000, 5000), batch=3, chunk=256, algo=kvs.KVS_ALGO_MFMA)
+@pytest.mark.parametrize("kv,algo,part_bytes,row_scales", [
+    (kvs.KVS_BF16, kvs.KVS_ALGO_MFMA, 2, True),    # decode kernel: row-scaled fp16
+    (kvs.KVS_BF16, kvs.KVS_ALGO_VALU, 4, False),   # vector kernel: fp32
+    (kvs.KVS_FP8_E4M3, kvs.KVS_ALGO_MFMA, 2, False),
+    (kvs.KVS_INT4, kvs.KVS_ALGO_MFMA, 2, False),
+])
+def test_split_partials_size_by_kv_type(lib, kv, algo, part_bytes, row_scales):
+    """The split partial outputs are fp16 code averages (V scale applied by
+    the merge) for fp8 and INT4 caches; for bf16 caches, fp16 rows with an fp32
+    multiplier each from the decode kernel, fp32 from the others.  Their LSEs
+    are fp32 either way."""
+    a, keep = _args(kv=kv, lens=(100, 3000, 5000), batch=3, chunk=256, algo=algo)
     info = kvs.kvs_decode_plan(a)
     assert info.needs_merge
     g = 4
     slots = info.items_per_kv_head * 2 * g
     r256 = lambda n: -(-n // 256) * 256
-    want = r256(slots * 128 * part_bytes) + r256(slots * 4) + r256(3 * 8)
+    want = r256(slots * 128 * part_bytes) + r256(slots * 4) * (2 if row_scales else 1) + r256(3 * 8)
+    assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+
+
+def test_bf16_partials_of_the_multi_row_kernels_stay_fp32(lib):
+    """bf16 caches with enough query rows per request for the shared-tile
+    kernel (col_share >= 4): fp32 partials, no multipliers."""
+    qo = np.array([0, 40, 80, 120], np.int32)
+    a, keep = _args(lens=(1000, 3000, 5000), batch=3, chunk=256)
+    a.qo_indptr = 0x1000
+    a.qo_indptr_host = qo.ctypes.data
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge and info.col_share >= 4
+    cols = 16 * -(-40 * 4 // 16)  # (query row, head) columns per KV head: 10 groups of 16
+    slots = info.items_per_kv_head * 2 * cols
+    r256 = lambda n: -(-n // 256) * 256
+    want = r256(slots * 128 * 4) + r256(slots * 4) + r256(3 * 8)
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
 
 

@@ -1,0 +1,97 @@
+"""Row-scaled fp16 split partials of bf16 caches (the decode kernel stores
+each split's partial row in fp16 times a power of two, and the merge
+multiplies it back).  V is bf16 N(0, 1) scaled by exact powers of two, far
+above fp16's largest value (2^18) and far below its smallest normal (2^-20),
+and in a mix whose splits differ by 2^32 in scale; the output scales by the
+same power of two, so o / 2^k must match the oracle's o / 2^k to the bf16
+gate.  Forced short chunks make every request split; both wave splits and
+both merge places."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from kvs_testlib import O_TOL, LSE_REL, run_library
+from workloads import make_inputs, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import decode_attention_kv_split_amd as kvs
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kvs.load_library()
+
+
+def _scaled_v(inp, exps):
+    """bf16 V codes times 2^exps[token] (exact: the exponent moves, the
+    mantissa stays).  Paged pools: exps is indexed by the pool's token slot."""
+    v = inp.v.astype(np.uint32) << 16
+    f = v.view(np.float32).astype(np.float64)
+    if inp.spec.page_size:
+        e = np.asarray(exps, np.float64).reshape(f.shape[0], f.shape[1], 1, 1)
+    else:
+        e = np.asarray(exps, np.float64).reshape(f.shape[0], 1, 1)
+    g = (f * np.exp2(e)).astype(np.float32)
+    assert np.array_equal(g.astype(np.float64) / np.exp2(e), f), "scaling must be exact"
+    return (g.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _check(inp, k_out, **kw):
+    o, lse = run_library(inp, **kw)
+    o_ref, lse_ref = oracle.decode_reference(inp)
+    assert np.all(np.isfinite(o)), "non-finite output"
+    err = float(np.max(np.abs((o - o_ref) * 2.0 ** -k_out)))
+    print(f"  max |o - o_ref| / 2^{k_out} = {err:.3e}", flush=True)
+    assert err <= O_TOL["bf16"], f"max |o - o_ref| / 2^{k_out} = {err:.3e}"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
+    rel = np.abs(lse[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+    assert float(rel.max()) <= LSE_REL
+
+
+def _paged(d=128, Hq=32, Hk=8):
+    spec = small_variant("c4_paged_bf16_b64", batch=5, lengths=("list", [700, 1500, 64, 3000, 17]))
+    return dataclasses.replace(spec, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=d)
+
+
+@pytest.mark.parametrize("scale", ["big", "tiny", "mixed"])
+@pytest.mark.parametrize("waves", ["tiles", "heads"])
+@pytest.mark.parametrize("merge", ["kernel", "in_partial"])
+def test_row_scaled_partials_paged(scale, waves, merge):
+    print(f"case partials {scale} {waves} {merge}", flush=True)
+    inp = make_inputs(_paged(), seed=77)
+    n_pages, P = inp.v.shape[0], inp.v.shape[1]
+    if scale == "big":
+        exps, k_out = np.full((n_pages, P), 18.0), 18
+    elif scale == "tiny":
+        exps, k_out = np.full((n_pages, P), -20.0), -20
+    else:  # pages alternate between 2^16 and 2^-16; one page per split, so splits differ by 2^32
+        exps, k_out = np.where(np.arange(n_pages)[:, None] % 2 == 0, 16.0, -16.0) * np.ones((1, P)), 16
+    inp = dataclasses.replace(inp, v=_scaled_v(inp, exps))
+    chunk = 16 if scale == "mixed" else (64 if waves == "heads" else 256)
+    _check(inp, k_out, kv_chunk=chunk, wave_split=waves, merge_mode=merge)
+
+
+@pytest.mark.parametrize("d,Hq,Hk", [(64, 16, 4), (256, 8, 2)])
+@pytest.mark.parametrize("scale", ["big", "tiny"])
+def test_row_scaled_partials_head_dims(d, Hq, Hk, scale):
+    print(f"case partials d={d} {scale}", flush=True)
+    inp = make_inputs(_paged(d, Hq, Hk), seed=78)
+    k_out = 18 if scale == "big" else -20
+    inp = dataclasses.replace(inp, v=_scaled_v(inp, np.full(inp.v.shape[:2], float(k_out))))
+    _check(inp, k_out, kv_chunk=128)
+
+
+def test_row_scaled_partials_contiguous_mha():
+    """The 32k-token MHA decode's shape (contiguous cache, one head per KV
+    head), shortened; V at 2^18."""
+    print("case partials contiguous MHA", flush=True)
+    spec = small_variant("c3_llama2_7b_32k", lengths=("fixed", 5000))
+    inp = make_inputs(spec, seed=79)
+    inp = dataclasses.replace(inp, v=_scaled_v(inp, np.full(inp.v.shape[0], 18.0)))
+    _check(inp, 18, kv_chunk=512)

@@ -53,8 +53,8 @@ def test_noalloc_rejects_a_call_larger_than_its_array():
     import decode_attention_kv_split_amd as kvs
     import torch
 
-    # 16-key chunks of 9000 keys x 64 query heads x 256 dims of fp32 partials: about 37 MB
-    spec = DecodeSpec("noalloc_big", 1, 64, 4, 256, 0, "bf16", "bf16", 0.1, lengths=("fixed", 9000), seed=3)
+    # 16-key chunks of 18000 keys x 64 query heads x 256 dims of fp16 partials: about 37 MB
+    spec = DecodeSpec("noalloc_big", 1, 64, 4, 256, 0, "bf16", "bf16", 0.1, lengths=("fixed", 18000), seed=3)
     inp = make_inputs(spec)
     t = to_torch(inp)
     a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], kv_len_host=inp.kv_len, kv_chunk=16)
