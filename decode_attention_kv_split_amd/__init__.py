@@ -32,6 +32,7 @@ __all__ = [
     "KVS_F32", "KVS_BF16", "KVS_FP8_E4M3", "KVS_INT4", "KVS_ALGO_AUTO", "KVS_ALGO_VALU", "KVS_ALGO_MFMA",
     "KVS_ALGO_MFMA_PACKED", "KVS_MERGE_AUTO", "KVS_MERGE_IN_PARTIAL", "KVS_MERGE_KERNEL",
     "KVS_WAVES_AUTO", "KVS_WAVES_HEADS", "KVS_WAVES_TILES",
+    "KVS_PART_F32", "KVS_PART_F16_CODES", "KVS_PART_F16_ROWS",
     "KvsDecodeArgs", "KvsPlanInfo", "KvsAppendArgs", "KvsError",
     "library_path", "load_library",
     "kvs_decode", "kvs_decode_plan", "kvs_decode_workspace_bytes", "kvs_append", "kvs_status_string",
@@ -40,7 +41,7 @@ __all__ = [
     "decode", "single_decode", "batch_decode_paged", "append", "make_append_args",
 ]
 
-KVS_ABI_VERSION = 11
+KVS_ABI_VERSION = 12
 
 KVS_OK, KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = 0, -1, -2, -3, -4
 KVS_ERR_TOO_LARGE = -5
@@ -51,6 +52,7 @@ KVS_ALGO_AUTO, KVS_ALGO_VALU, KVS_ALGO_MFMA, KVS_ALGO_MFMA_PACKED = 0, 1, 2, 3
 KVS_MERGE_AUTO, KVS_MERGE_IN_PARTIAL, KVS_MERGE_KERNEL = 0, 1, 2
 _MERGE_MODES = {"auto": KVS_MERGE_AUTO, "in_partial": KVS_MERGE_IN_PARTIAL, "kernel": KVS_MERGE_KERNEL}
 KVS_WAVES_AUTO, KVS_WAVES_HEADS, KVS_WAVES_TILES = 0, 1, 2
+KVS_PART_F32, KVS_PART_F16_CODES, KVS_PART_F16_ROWS = 0, 1, 2
 _WAVE_SPLITS = {"auto": KVS_WAVES_AUTO, "heads": KVS_WAVES_HEADS, "tiles": KVS_WAVES_TILES}
 _ALGOS = {"auto": KVS_ALGO_AUTO, "valu": KVS_ALGO_VALU, "mfma": KVS_ALGO_MFMA, "mfma_packed": KVS_ALGO_MFMA_PACKED}
 
@@ -111,6 +113,7 @@ class KvsPlanInfo(ctypes.Structure):
         ("col_share", ctypes.c_int32),
         ("merge_in_partial", ctypes.c_int32),
         ("wave_packs", ctypes.c_int32),
+        ("part_format", ctypes.c_int32),
     ]
 
 

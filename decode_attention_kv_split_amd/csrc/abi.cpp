@@ -282,6 +282,16 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
                         kvs::kWaves, a->head_dim, part_bytes, row_scaled, pl->chunk, *cus, pl))
       return KVS_ERR_INVALID_ARG;
   }
+  // Row-scaled partials only for launches of more workgroups than CUs: a
+  // smaller launch is bound by latency, not by its partials' bytes, and the
+  // row reduction in its epilogue costs more than the halved bytes save
+  // (Gemma-shaped single decode, 128 splits: 14.4 against 14.05 us per step).
+  const int64_t wgs = (int64_t)pl->items * (a->num_kv_heads / pack) * c.col_blocks / pl->wave_packs;
+  if (row_scaled && wgs <= std::max(1, *cus)) {
+    if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
+                        pl->wave_packs, a->head_dim, 4, false, pl->chunk, *cus, pl))
+      return KVS_ERR_INVALID_ARG;
+  }
   // grid.x (items) x grid.y of kThreads work-items must stay below 2^32 work-items
   // (the merge runs one workgroup per column group)
   if ((int64_t)pl->items * a->num_kv_heads * c.col_groups > kvs::kMaxWorkgroups) return KVS_ERR_UNSUPPORTED;
@@ -371,6 +381,7 @@ kvs_status kvs_decode_plan(const kvs_decode_args *args, kvs_plan_info *out) {
   out->col_share = c.col_share;
   out->merge_in_partial = merges_in_partial(pl, args, c) ? 1 : 0;
   out->wave_packs = pl.wave_packs;
+  out->part_format = pl.sc_part_bytes ? KVS_PART_F16_ROWS : part_codes_f16(args) ? KVS_PART_F16_CODES : KVS_PART_F32;
   return KVS_OK;
 }
 

@@ -211,26 +211,39 @@ __device__ __forceinline__ int row_scale_exp(float mx) {
 // Params::part_f16 by the same rule.
 template <int KT> constexpr bool part_f16_of() { return KT == DT_FP8 || KT == DT_INT4; }
 // Dims 4 i .. 4 i + 3 of o_part (i: index in units of four elements).
+// The stored bits of dims 4 i .. 4 i + 3 of o_part (i: index in units of four
+// elements): two dwords of fp16 pairs (F16; z, w unused) or four fp32.  The
+// merge keeps the raw bits until every load of a batch is issued, and
+// converts them afterwards (part_bits_to_float4): converted inside the
+// guarded load, the compiler waited for each split's load before issuing
+// the next one.
 template <bool F16, bool COHERENT>
-__device__ __forceinline__ float4 load_part4(const float *o_part, size_t i) {
+__device__ __forceinline__ uint4 load_part_bits(const float *o_part, size_t i) {
   if constexpr (F16) {
     const uint32_t *q = reinterpret_cast<const uint32_t *>(o_part) + 2 * i;
-    uint32_t lo, hi;
     if constexpr (COHERENT) {
-      lo = __hip_atomic_load(const_cast<uint32_t *>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      hi = __hip_atomic_load(const_cast<uint32_t *>(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return make_uint4(__hip_atomic_load(const_cast<uint32_t *>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                        __hip_atomic_load(const_cast<uint32_t *>(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                        0u, 0u);
     } else {
       const uint2 u = *reinterpret_cast<const uint2 *>(q);
-      lo = u.x;
-      hi = u.y;
+      return make_uint4(u.x, u.y, 0u, 0u);
     }
-    const float2 a = unpack_f16x2(lo), b = unpack_f16x2(hi);
-    return make_float4(a.x, a.y, b.x, b.y);
   } else if constexpr (COHERENT) {
     const float *o = o_part + 4 * i;
-    return make_float4(load_partial(o), load_partial(o + 1), load_partial(o + 2), load_partial(o + 3));
+    return make_uint4(__float_as_uint(load_partial(o)), __float_as_uint(load_partial(o + 1)),
+                      __float_as_uint(load_partial(o + 2)), __float_as_uint(load_partial(o + 3)));
   } else {
-    return reinterpret_cast<const float4 *>(o_part)[i];
+    return reinterpret_cast<const uint4 *>(o_part)[i];
+  }
+}
+// The four values of load_part_bits (all-zero bits are 0 in both forms).
+template <bool F16> __device__ __forceinline__ float4 part_bits_to_float4(const uint4 &u) {
+  if constexpr (F16) {
+    const float2 a = unpack_f16x2(u.x), b = unpack_f16x2(u.y);
+    return make_float4(a.x, a.y, b.x, b.y);
+  } else {
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
   }
 }
 // The V scale a partial's writer applies to o: none where the merge applies it.
@@ -511,7 +524,7 @@ __device__ __forceinline__ void merge_combine(MergeState &a, const MergeState &b
 
 // Fold splits tg, tg + step, ... (< nb) of four outputs: their LSEs at
 // lp[c * lstride] and partials at four-element index o4 + c * ostride of
-// o_part (load_part4; F16: fp16 partials), NB loads of each in flight at a
+// o_part (load_part_bits; F16: fp16 partials), NB loads of each in flight at a
 // time.
 // COHERENT: read at the coherent level (the merge inside the partial kernel,
 // which may read partials other XCDs wrote in the same launch); otherwise
@@ -523,24 +536,25 @@ __device__ __forceinline__ void merge_fold_splits(MergeState &st, const float *l
                                                   int nb, const float *sp = nullptr) {
   for (int c0 = tg; c0 < nb; c0 += step * NB) {
     float lc[NB], sc[NB];
-    float4 v[NB];
+    uint4 raw[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int c = c0 + u * step;
       sc[u] = 1.0f;
       if (c < nb) {
         lc[u] = COHERENT ? load_partial(lp + (size_t)c * lstride) : lp[(size_t)c * lstride];
-        v[u] = load_part4<F16, COHERENT>(o_part, o4 + (size_t)c * ostride);
+        raw[u] = load_part_bits<F16, COHERENT>(o_part, o4 + (size_t)c * ostride);
         if constexpr (SC) sc[u] = COHERENT ? load_partial(sp + (size_t)c * lstride) : sp[(size_t)c * lstride];
       } else {
         lc[u] = -INFINITY;
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        raw[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if constexpr (SC) v[u] = make_float4(v[u].x * sc[u], v[u].y * sc[u], v[u].z * sc[u], v[u].w * sc[u]);
-      merge_fold(st, lc[u], v[u]);
+      float4 v = part_bits_to_float4<F16>(raw[u]);
+      if constexpr (SC) v = make_float4(v.x * sc[u], v.y * sc[u], v.z * sc[u], v.w * sc[u]);
+      merge_fold(st, lc[u], v);
     }
   }
 }

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 11
+#define KVS_ABI_VERSION 12
 
 /* Status codes.  Every check of KVS_ERR_INVALID_ARG, KVS_ERR_UNSUPPORTED and
  * KVS_ERR_WORKSPACE runs on the host before any HIP call. */
@@ -222,7 +222,15 @@ typedef struct {
                                 0: a second kernel merges them (or nothing needs merging) */
   int32_t wave_packs;        /* KV-head packs per partial workgroup: 4 (one per wave,
                                 KVS_WAVES_HEADS) or 1 */
+  int32_t part_format;       /* kvs_part_format of the split partials in the workspace */
 } kvs_plan_info;
+
+/* How the split partial outputs are stored in the workspace (kvs_decode). */
+enum {
+  KVS_PART_F32 = 0,      /* fp32 */
+  KVS_PART_F16_CODES = 1, /* fp16 averages of the stored fp8 / INT4 codes; the merge applies the V scale */
+  KVS_PART_F16_ROWS = 2   /* fp16 rows of a bf16 cache, each times a power of two (multiplier stored) */
+};
 
 /* Plan a call without launching anything.  Makes no HIP call when
  * args->num_cus > 0.  Validates the arguments like kvs_decode (except that

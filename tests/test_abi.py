@@ -41,8 +41,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 11
-    assert re.search(r"#define KVS_ABI_VERSION 11\b", open(HEADER).read())
+    assert kvs.kvs_abi_version() == kvs.KVS_ABI_VERSION == 12
+    assert re.search(r"#define KVS_ABI_VERSION 12\b", open(HEADER).read())
     assert kvs.kvs_status_string(kvs.KVS_ERR_WORKSPACE).startswith("workspace")
 
 
@@ -245,10 +245,12 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
         assert covered == list(range(lo, L))
     g = 4
     if info.needs_merge:
-        # bf16 decode-kernel partials: fp16 rows, then their LSEs and multipliers
+        # bf16 decode-kernel partials: fp16 rows, then their LSEs and
+        # multipliers, when the launch has more workgroups than CUs; else fp32
         slots = info.items_per_kv_head * 2 * g
         r256 = lambda n: -(-n // 256) * 256
-        want = r256(slots * 128 * 2) + 2 * r256(slots * 4) + r256(len(lens) * 8)
+        big = info.items_per_kv_head * 2 > 256
+        want = r256(slots * 128 * (2 if big else 4)) + (2 if big else 1) * r256(slots * 4) + r256(len(lens) * 8)
         assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want  # counters, then the partials
     else:
         assert info.workspace_bytes == 0
@@ -263,9 +265,11 @@ def test_plan_tiles_each_request_exactly_once(lib, window, chunk):
 def test_split_partials_size_by_kv_type(lib, kv, algo, part_bytes, row_scales):
     """The split partial outputs are fp16 code averages (V scale applied by
     the merge) for fp8 and INT4 caches; for bf16 caches, fp16 rows with an fp32
-    multiplier each from the decode kernel, fp32 from the others.  Their LSEs
-    are fp32 either way."""
+    multiplier each from the decode kernel (in launches of more workgroups
+    than CUs: 66 here, on 16 CUs), fp32 from the others.  Their LSEs are fp32
+    either way."""
     a, keep = _args(kv=kv, lens=(100, 3000, 5000), batch=3, chunk=256, algo=algo)
+    a.num_cus = 16
     info = kvs.kvs_decode_plan(a)
     assert info.needs_merge
     g = 4
@@ -273,6 +277,23 @@ def test_split_partials_size_by_kv_type(lib, kv, algo, part_bytes, row_scales):
     r256 = lambda n: -(-n // 256) * 256
     want = r256(slots * 128 * part_bytes) + r256(slots * 4) * (2 if row_scales else 1) + r256(3 * 8)
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+    fmt = kvs.KVS_PART_F16_ROWS if row_scales else kvs.KVS_PART_F32 if part_bytes == 4 else kvs.KVS_PART_F16_CODES
+    assert info.part_format == fmt
+
+
+@pytest.mark.parametrize("cus,row_scales", [(65, True), (66, False), (256, False)])
+def test_bf16_row_scaled_partials_only_past_one_workgroup_per_cu(lib, cus, row_scales):
+    """66 decode workgroups (33 items x 2 KV heads): row-scaled fp16 partials
+    on fewer CUs, fp32 ones on as many or more."""
+    a, keep = _args(lens=(100, 3000, 5000), batch=3, chunk=256)
+    a.num_cus = cus
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge and info.items_per_kv_head == 33
+    slots = 33 * 2 * 4
+    r256 = lambda n: -(-n // 256) * 256
+    want = r256(slots * 128 * (2 if row_scales else 4)) + r256(slots * 4) * (2 if row_scales else 1) + r256(3 * 8)
+    assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+    assert info.part_format == (kvs.KVS_PART_F16_ROWS if row_scales else kvs.KVS_PART_F32)
 
 
 def test_bf16_partials_of_the_multi_row_kernels_stay_fp32(lib):
@@ -289,6 +310,7 @@ def test_bf16_partials_of_the_multi_row_kernels_stay_fp32(lib):
     r256 = lambda n: -(-n // 256) * 256
     want = r256(slots * 128 * 4) + r256(slots * 4) + r256(3 * 8)
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+    assert info.part_format == kvs.KVS_PART_F32
 
 
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):

@@ -4,8 +4,9 @@ multiplies it back).  V is bf16 N(0, 1) scaled by exact powers of two, far
 above fp16's largest value (2^18) and far below its smallest normal (2^-20),
 and in a mix whose splits differ by 2^32 in scale; the output scales by the
 same power of two, so o / 2^k must match the oracle's o / 2^k to the bf16
-gate.  Forced short chunks make every request split; both wave splits and
-both merge places."""
+gate.  Forced short chunks make every request split and the launch larger
+than one workgroup per CU (smaller launches keep fp32 partials); both wave
+splits and both merge places."""
 import dataclasses
 
 import numpy as np
@@ -41,7 +42,22 @@ def _scaled_v(inp, exps):
     return (g.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _plan_format(inp, **kw):
+    import decode_attention_kv_split_amd as kvs
+    from kvs_testlib import to_torch
+
+    s = inp.spec
+    t = to_torch(inp)
+    a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
+                            page_indices=t.get("page_indices"), kv_len_host=inp.kv_len, sm_scale=s.sm_scale,
+                            window=s.window, **kw)
+    return kvs.kvs_decode_plan(a).part_format
+
+
 def _check(inp, k_out, **kw):
+    import decode_attention_kv_split_amd as kvs
+
+    assert _plan_format(inp, **kw) == kvs.KVS_PART_F16_ROWS, "the case must run the row-scaled format"
     o, lse = run_library(inp, **kw)
     o_ref, lse_ref = oracle.decode_reference(inp)
     assert np.all(np.isfinite(o)), "non-finite output"
@@ -73,7 +89,8 @@ def test_row_scaled_partials_paged(scale, waves, merge):
     else:  # pages alternate between 2^16 and 2^-16; one page per split, so splits differ by 2^32
         exps, k_out = np.where(np.arange(n_pages)[:, None] % 2 == 0, 16.0, -16.0) * np.ones((1, P)), 16
     inp = dataclasses.replace(inp, v=_scaled_v(inp, exps))
-    chunk = 16 if scale == "mixed" else (64 if waves == "heads" else 256)
+    # short enough for more workgroups than CUs (the launches that store row-scaled partials)
+    chunk = 16 if scale == "mixed" else 32
     _check(inp, k_out, kv_chunk=chunk, wave_split=waves, merge_mode=merge)
 
 
@@ -84,7 +101,7 @@ def test_row_scaled_partials_head_dims(d, Hq, Hk, scale):
     inp = make_inputs(_paged(d, Hq, Hk), seed=78)
     k_out = 18 if scale == "big" else -20
     inp = dataclasses.replace(inp, v=_scaled_v(inp, np.full(inp.v.shape[:2], float(k_out))))
-    _check(inp, k_out, kv_chunk=128)
+    _check(inp, k_out, kv_chunk=32)
 
 
 def test_row_scaled_partials_contiguous_mha():
@@ -94,4 +111,4 @@ def test_row_scaled_partials_contiguous_mha():
     spec = small_variant("c3_llama2_7b_32k", lengths=("fixed", 5000))
     inp = make_inputs(spec, seed=79)
     inp = dataclasses.replace(inp, v=_scaled_v(inp, np.full(inp.v.shape[0], 18.0)))
-    _check(inp, 18, kv_chunk=512)
+    _check(inp, 18, kv_chunk=64)
