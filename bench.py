@@ -45,14 +45,14 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # that decide the partial kernel's memory traffic hash to the digest it was
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 538243695, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2299497163, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
+        {"bytes": 2297306413, "digest": "f67c1f927763c932348059165e3b2d9c8b7bb5b4120d0f1ff80d8dbc6aae96a3"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1483203372, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
+        {"bytes": 1483200475, "digest": "f67c1f927763c932348059165e3b2d9c8b7bb5b4120d0f1ff80d8dbc6aae96a3"},
+    ("c3_llama2_7b_32k", "partial_mfma_kernel"):
+        {"bytes": 537790376, "digest": "f67c1f927763c932348059165e3b2d9c8b7bb5b4120d0f1ff80d8dbc6aae96a3"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 676094612, "digest": "f701e489fe66e6d3c5ecee7c22dcf58cb79f3cb099cdca073376ccfbaab7b962"},
+        {"bytes": 676094399, "digest": "f67c1f927763c932348059165e3b2d9c8b7bb5b4120d0f1ff80d8dbc6aae96a3"},
 }
 
 
@@ -352,7 +352,7 @@ def graph_steps(a, ws, steps: int) -> float:
 def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk: int = 0,
         with_cpu: bool = True, events: bool = True, cold: bool = False, unified_max=None,
         q_len: int = 1, soft_cap: float = 0.0, kv_len: int = 0, graph: bool = False, probe: bool = True,
-        merge_mode: str = "auto", wave_split: str = "auto", pool_offset: int = 0) -> dict:
+        merge_mode: str = "auto", wave_split: str = "auto", pool_offset: int = 0, seed=None) -> dict:
     import dataclasses
 
     import torch
@@ -371,6 +371,8 @@ def run(config_name: str, steps: int, warmup: int, algo: str = "auto", kv_chunk:
         spec = dataclasses.replace(spec, soft_cap=soft_cap)
     if kv_len:
         spec = dataclasses.replace(spec, lengths=("fixed", kv_len))
+    if seed is not None:
+        spec = dataclasses.replace(spec, seed=seed)
     t_gen = time.perf_counter()
     inp = make_inputs(spec)
     t = to_torch(inp)
@@ -680,6 +682,8 @@ def main():
                     help="give every request this cache length (0: the workload's own lengths)")
     ap.add_argument("--soft-cap", type=float, default=0.0,
                     help="logit soft-cap c: scores become c * tanh(s / c) (0: none)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="draw the workload from this seed instead of its own (other lengths and values)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--single", action="store_true",
                     help="measure the named workload only (the default run adds records of "
@@ -712,8 +716,8 @@ def main():
     res = run(name, args.steps, args.warmup, args.algo, args.kv_chunk, with_cpu=not args.no_cpu,
               events=not args.no_events, cold=args.cold, unified_max=args.unified_max, q_len=args.q_len,
               soft_cap=args.soft_cap, kv_len=args.kv_len, graph=args.graph, merge_mode=args.merge,
-              wave_split=args.waves, pool_offset=args.pool_offset)
-    plain = (args.merge == "auto" and args.waves == "auto" and args.algo == "auto" and args.kv_chunk == 0
+              wave_split=args.waves, pool_offset=args.pool_offset, seed=args.seed)
+    plain = (args.seed is None and args.merge == "auto" and args.waves == "auto" and args.algo == "auto" and args.kv_chunk == 0
              and args.unified_max is None and args.q_len == 1 and not args.soft_cap and not args.kv_len
              and not args.cold and not args.graph and not args.pool_offset)
     if name == DEFAULT and plain and not args.single:
