@@ -409,8 +409,9 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
            v_scale=None, sm_scale=None, window: int = -1, kv_chunk: int = 0, algo="auto", out=None, lse=None,
            workspace=None, stream=None, unified_max: Optional[float] = None, kv_dtype: Optional[str] = None,
            qo_indptr=None, qo_indptr_host=None, logits_soft_cap: float = 0.0, merge_mode="auto",
-           wave_split="auto"):
+           wave_split="auto", num_cus: int = 0):
     """One decode-attention step on the current (or given) HIP stream.
+    num_cus: CU count to plan for (0: the device's).
     Returns (o [batch, Hq, d] in q's dtype, lse [batch, Hq] fp32, natural log)."""
     import torch
 
@@ -418,7 +419,8 @@ def decode(q, k, v, kv_len, *, page_indptr=None, page_indices=None, kv_len_host=
                         kv_len_host=kv_len_host, k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale,
                         window=window, kv_chunk=kv_chunk, algo=algo, out=out, lse=lse, unified_max=unified_max,
                         kv_dtype=kv_dtype, qo_indptr=qo_indptr, qo_indptr_host=qo_indptr_host,
-                        logits_soft_cap=logits_soft_cap, merge_mode=merge_mode, wave_split=wave_split)
+                        logits_soft_cap=logits_soft_cap, merge_mode=merge_mode, wave_split=wave_split,
+                        num_cus=num_cus)
     s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
     need = kvs_decode_workspace_bytes(a)
     if workspace is None:

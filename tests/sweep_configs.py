@@ -34,6 +34,7 @@ class SweepCase:
     poison_invisible: bool
     merge_mode: str = "auto"
     wave_split: str = "auto"
+    num_cus: int = 0  # CU count the call is planned for (0: the device's)
 
     @property
     def multi(self) -> bool:
@@ -61,6 +62,8 @@ class SweepCase:
             parts.append(f"merge-{self.merge_mode}")
         if self.wave_split != "auto":
             parts.append(f"waves-{self.wave_split}")
+        if self.num_cus:
+            parts.append(f"cus{self.num_cus}")
         return "-".join(parts)
 
 
@@ -155,3 +158,49 @@ def draw_case(rng, index: int) -> SweepCase:
 def sweep_cases(n: int = SWEEP_CASES, seed: int = SWEEP_SEED) -> List[SweepCase]:
     rng = np.random.default_rng(seed)
     return [draw_case(rng, i) for i in range(n)]
+
+
+ROW_SCALE_SEED = 20261204
+ROW_SCALE_CASES = 30
+
+
+def draw_row_scaled_case(rng, index: int) -> SweepCase:
+    """A bf16 decode on the matrix-core decode kernel (one query row, pages of
+    16 or more or a contiguous cache) with a forced chunk, planned for one CU:
+    every launch of two or more workgroups then stores its split partials as
+    row-scaled fp16 rows."""
+    d = _pick(rng, [64, 128, 256])
+    g = _pick(rng, [1, 2, 4, 8, 16])
+    hk = _pick(rng, [1, 2, 4, 8])
+    if g * hk > 64:
+        hk = max(1, 64 // g)
+    contiguous = rng.random() < 0.2
+    batch = 1 if contiguous else int(rng.integers(1, 6))
+    P = 0 if contiguous else _pick(rng, [16, 32, 64])
+    lmax = _pick(rng, [300, 2500, 9000], p=[0.3, 0.5, 0.2])
+    lens = rng.integers(1, lmax + 1, size=batch)
+    for i in range(batch):
+        if rng.random() < 0.15:
+            lens[i] = _pick(rng, [1, 15, 16, 17, 63, 64, 65])
+    window = -1 if rng.random() < 0.5 else _pick(rng, [1, 7, 16, 31, 100, 513, 2000])
+    while _oracle_macs(lens, ("fixed", 1), window, g * hk, d) > _ORACLE_MACS:
+        lens = np.maximum(lens // 2, 1)
+    chunk = _pick(rng, [16, 32, 48, 64, 96, 256])
+    algo = "mfma_packed" if rng.random() < 0.3 else "auto"
+    unified = float(_pick(rng, [-20.0, 0.0, 3.0, 30.0])) if rng.random() < 0.2 else None
+    cap = 0.0 if rng.random() < 0.7 else float(_pick(rng, [0.5, 4.0, 30.0]))
+    sm = d ** -0.5 * (4.0 if rng.random() < 0.2 else 1.0)
+    poison_inv = window > 0 and rng.random() < 0.5
+    merge = _pick(rng, ["auto", "in_partial", "kernel"])
+    packable = d * 2 < 256 and 2 * g <= 16 and hk % 2 == 0
+    pack = 2 if packable and algo == "mfma_packed" else 1
+    waves = "heads" if (hk // pack) % 4 == 0 and hk >= 4 and rng.random() < 0.5 else "auto"
+    spec = DecodeSpec(f"rowscale{index}", batch, g * hk, hk, d, P, "bf16", "bf16", sm, window=window,
+                      lengths=("list", [int(x) for x in lens]), qk_rmsnorm=rng.random() < 0.2,
+                      seed=ROW_SCALE_SEED + index, soft_cap=cap)
+    return SweepCase(index, spec, int(chunk), algo, unified, poison_inv, merge, waves, num_cus=1)
+
+
+def row_scaled_cases(n: int = ROW_SCALE_CASES, seed: int = ROW_SCALE_SEED) -> List[SweepCase]:
+    rng = np.random.default_rng(seed)
+    return [draw_row_scaled_case(rng, i) for i in range(n)]

@@ -5,7 +5,7 @@ import pytest
 
 import decode_attention_kv_split_amd as kvs
 from kvs_testlib import ensure_built
-from sweep_configs import sweep_cases
+from sweep_configs import row_scaled_cases, sweep_cases
 from workloads import make_inputs
 
 _DT = {"f32": kvs.KVS_F32, "bf16": kvs.KVS_BF16, "fp8": kvs.KVS_FP8_E4M3, "int4": kvs.KVS_INT4}
@@ -27,8 +27,8 @@ def test_sweep_is_seeded_and_varied():
     assert {c.merge_mode for c in a} == {"auto", "in_partial", "kernel"}
 
 
-@pytest.mark.parametrize("case", sweep_cases(), ids=lambda c: c.label())
-def test_sweep_case_plans(lib, case):
+def _plan(case):
+    """kvs_decode_plan of a sweep case (host only; fake device pointers)."""
     s = case.spec
     inp = make_inputs(s)
     a = kvs.KvsDecodeArgs()
@@ -51,12 +51,42 @@ def test_sweep_case_plans(lib, case):
     a.window = s.window
     a.kv_chunk = case.kv_chunk
     a.algo = {"auto": 0, "valu": 1, "mfma": 2, "mfma_packed": 3}[case.algo]
-    a.num_cus = 256
+    a.num_cus = case.num_cus or 256
     if case.unified_max is not None:
         a.use_unified_max, a.unified_max = 1, case.unified_max
     a.logits_soft_cap = s.soft_cap
     a.merge_mode = {"auto": 0, "in_partial": 1, "kernel": 2}[case.merge_mode]
     a.wave_split = {"auto": 0, "heads": 1, "tiles": 2}[case.wave_split]
-    info = kvs.kvs_decode_plan(a)  # raises on any status but KVS_OK
+    return kvs.kvs_decode_plan(a)  # raises on any status but KVS_OK
+
+
+@pytest.mark.parametrize("case", sweep_cases(), ids=lambda c: c.label())
+def test_sweep_case_plans(lib, case):
+    info = _plan(case)
     assert info.wave_packs in ((4,) if case.wave_split == "heads" else (1, 4))
-    assert info.items_per_kv_head >= s.batch
+    assert info.items_per_kv_head >= case.spec.batch
+
+
+def test_sweep_covers_every_partial_format(lib):
+    """Cases whose requests split: bf16 ones with fp32 partials (vector kernel,
+    several rows, small launches), fp8 / INT4 ones with fp16 code averages,
+    fp32 ones in fp32; the row-scaled set with row-scaled fp16 partials."""
+    seen = {}
+    for case in sweep_cases():
+        info = _plan(case)
+        if info.needs_merge:
+            key = (case.spec.kv_dtype, info.part_format)
+            seen[key] = seen.get(key, 0) + 1
+    assert seen.get(("bf16", kvs.KVS_PART_F32), 0) >= 5, seen
+    assert seen.get(("fp8", kvs.KVS_PART_F16_CODES), 0) >= 10, seen
+    assert seen.get(("int4", kvs.KVS_PART_F16_CODES), 0) >= 10, seen
+    assert seen.get(("f32", kvs.KVS_PART_F32), 0) >= 3, seen
+    rows = [_plan(c) for c in row_scaled_cases()]
+    split = [i for i in rows if i.needs_merge]
+    assert len(split) >= 20 and all(i.part_format == kvs.KVS_PART_F16_ROWS for i in split)
+
+
+@pytest.mark.parametrize("case", row_scaled_cases(), ids=lambda c: c.label())
+def test_row_scaled_case_plans(lib, case):
+    info = _plan(case)
+    assert info.part_format == (kvs.KVS_PART_F16_ROWS if info.needs_merge else kvs.KVS_PART_F32)
