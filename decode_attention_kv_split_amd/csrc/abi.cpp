@@ -265,9 +265,10 @@ kvs_status plan_call(const kvs_decode_args *a, bool need_ptrs, kvs::Plan *pl, in
   const int32_t *nq = c.nq.empty() ? nullptr : c.nq.data();
   const bool row_scaled = part_row_scaled(a, *algo, c);
   const int part_bytes = part_codes_f16(a) || row_scaled ? 2 : 4;
+  const int min_chunk = *algo != KVS_ALGO_VALU && c.col_share == 1 ? kvs::kMinMatrixChunk : kvs::kMinChunk;
   if (!kvs::make_plan(a->kv_len_host, nq, a->batch, a->window, a->num_kv_heads, c.cols, c.col_blocks, pack,
                       a->wave_split == KVS_WAVES_HEADS ? kvs::kWaves : 1, a->head_dim, part_bytes, row_scaled,
-                      a->kv_chunk, *cus, pl))
+                      a->kv_chunk, *cus, pl, min_chunk))
     return KVS_ERR_INVALID_ARG;
   // Automatic wave split: the tiles split, unless the heads split can keep
   // the tiles plan's chunks (at most 64 tiles per wave) and still give every

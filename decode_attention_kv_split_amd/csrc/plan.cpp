@@ -11,7 +11,7 @@ static int request_lo(int L, int nq, int window) { return window > 0 ? std::max(
 
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
                int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, bool row_scales,
-               int forced_chunk, int num_cus, Plan *out) {
+               int forced_chunk, int num_cus, Plan *out, int min_chunk) {
   Plan pl;
   wave_packs = std::max(1, wave_packs);
   const bool per_wave = wave_packs > 1;
@@ -38,7 +38,7 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
     // can still travel in the kernel arguments
     chunk = std::max<int64_t>(chunk, (longest + kPlanInlineSplits - 1) / kPlanInlineSplits);
     chunk = (chunk + quantum - 1) / quantum * quantum;
-    chunk = std::max<int64_t>(chunk, per_wave ? kWaveChunkQuantum : kMinChunk);
+    chunk = std::max<int64_t>(chunk, per_wave ? kWaveChunkQuantum : min_chunk);
   }
   chunk = std::min<int64_t>(chunk, per_wave ? kMaxWaveChunk : kMaxChunk);
   pl.chunk = (int)chunk;

@@ -43,6 +43,13 @@ struct Plan {
 // tokens (one tile per wave) so that they still spread over many CUs.
 constexpr int kItemsPerCu = 8;
 constexpr int kMinChunk = 64;
+// The matrix-core decode kernel (one column group per workgroup) takes at
+// least two tiles per wave: its second tile's loads overlap the first one's
+// products, and half the splits halve the merge's work.  Gemma-shaped single
+// decode (8192 keys, head_dim 256): 13.4 against 13.9 us per step, with a
+// 512-key window 10.6 against 11.6 us; the vector kernel stays at 64 (a
+// 512-key fp32 MHA decode: 9.3 against 10.1 us).
+constexpr int kMinMatrixChunk = 128;
 constexpr int kChunkQuantum = 64; // 4 waves x 16-token tiles
 // Largest chunk: 64 tiles of 16 tokens per wave (a wave keeps the page ids of
 // its tiles in one register, one per lane).
@@ -77,8 +84,10 @@ void list_work(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
 // out like lse_part).  Returns false if a length is negative.  Workspace
 // layout when a request has several splits:
 // [counters][o_part][lse_part][sc_part][meta].
+// min_chunk: the smallest chunk the heuristic picks with the tiles split
+// (kMinChunk or kMinMatrixChunk; the heads split takes kWaveChunkQuantum).
 bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, int num_kv_heads, int cols,
                int col_blocks, int pack, int wave_packs, int head_dim, int part_bytes, bool row_scales,
-               int forced_chunk, int num_cus, Plan *out);
+               int forced_chunk, int num_cus, Plan *out, int min_chunk = kMinChunk);
 
 } // namespace kvs

@@ -569,11 +569,11 @@ def test_wave_split_choice_and_validation(lib):
     CU; the tiles split otherwise.  HEADS asked for where it does not apply
     is unsupported, unknown values are invalid."""
     # GQA paged decode, 8 KV heads: two workgroups of four packs per chunk
-    a, keep = _args(ptrs=False, batch=3, Hq=32, Hk=8, lens=(100, 2000, 9000))
+    a, keep = _args(ptrs=False, batch=3, Hq=32, Hk=8, lens=(100, 4000, 18000), num_pages=2000)
     a.wave_split = kvs.KVS_WAVES_TILES
     tiles = kvs.kvs_decode_plan(a)
     assert tiles.wave_packs == 1 and tiles.kv_chunk <= 1024
-    a.wave_split = kvs.KVS_WAVES_AUTO                      # same chunks, 350 workgroups: heads
+    a.wave_split = kvs.KVS_WAVES_AUTO                      # same chunks, 348 workgroups: heads
     info = kvs.kvs_decode_plan(a)
     assert info.wave_packs == 4 and info.kv_chunk == tiles.kv_chunk
     assert info.items_per_kv_head == tiles.items_per_kv_head and info.workspace_bytes == tiles.workspace_bytes
