@@ -46,13 +46,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2297305631, "digest": "352cbc0dc16c833a49dcf91d949ce8c9e5e3b9df651f24832365535e4d2588c9"},
+        {"bytes": 2297309404, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1483200255, "digest": "352cbc0dc16c833a49dcf91d949ce8c9e5e3b9df651f24832365535e4d2588c9"},
+        {"bytes": 1483200233, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 537790305, "digest": "352cbc0dc16c833a49dcf91d949ce8c9e5e3b9df651f24832365535e4d2588c9"},
+        {"bytes": 537790321, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 676094407, "digest": "352cbc0dc16c833a49dcf91d949ce8c9e5e3b9df651f24832365535e4d2588c9"},
+        {"bytes": 677633135, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
 }
 
 

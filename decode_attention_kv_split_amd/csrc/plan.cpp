@@ -31,7 +31,8 @@ bool make_plan(const int32_t *kv_len, const int32_t *nq, int batch, int window, 
   } else {
     // the same work per workgroup whichever way the waves share it: a
     // workgroup holding wave_packs packs takes chunks wave_packs times shorter
-    const int64_t target = (int64_t)kItemsPerCu * std::max(1, num_cus) * wave_packs;
+    const int64_t per_cu = pack > 1 ? kPackedItemsPerCu : kItemsPerCu;
+    const int64_t target = per_cu * std::max(1, num_cus) * wave_packs;
     const int64_t quantum = per_wave ? kWaveChunkQuantum : kChunkQuantum;
     chunk = (total * num_kv_heads * col_blocks + target - 1) / target;
     // at most kPlanInlineSplits splits per request, so that the work list

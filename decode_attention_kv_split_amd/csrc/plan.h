@@ -42,6 +42,14 @@ struct Plan {
 // several chunks to stream; small problems get chunks down to kMinChunk
 // tokens (one tile per wave) so that they still spread over many CUs.
 constexpr int kItemsPerCu = 8;
+// Workgroups that hold two KV heads (pack 2: INT4 at head_dim 128) take
+// chunks sized for 10 (item, KV head) pairs per CU, i.e. 5 workgroups per CU
+// rather than 4.  Batch-128 INT4 decode, three draws of its lengths, step
+// us at the resulting 2048-key chunks against the 2560 of 8 pairs: 138.2 /
+// 151.2 / 151.0 against 141.1 / 153.0 / 151.6.  Counting workgroups instead
+// (8 per CU, 1280-key chunks) sped the partial kernel but slowed the step
+// through the larger merge.
+constexpr int kPackedItemsPerCu = 10;
 constexpr int kMinChunk = 64;
 // The matrix-core decode kernel (one column group per workgroup) takes at
 // least two tiles per wave: its second tile's loads overlap the first one's
