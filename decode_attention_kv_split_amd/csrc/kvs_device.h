@@ -522,6 +522,27 @@ __device__ __forceinline__ void merge_combine(MergeState &a, const MergeState &b
   a.m = M;
 }
 
+// Combine the states of SG thread groups into group 0: group tg = tid / F
+// holds a share of the splits of output tid % F.  Pairwise, in about
+// log2(SG) rounds through LDS (one combine after another took SG - 1
+// dependent LDS round trips).  In round s the groups tg = 0 mod 2s take in
+// group tg + s, which writes nothing that round.  The whole workgroup calls
+// it with the same F and SG (its barriers are uniform); s_st holds kThreads
+// states.
+__device__ __forceinline__ void merge_groups(MergeState &st, MergeState *s_st, int F, int SG) {
+  const int tid = threadIdx.x;
+  const int tg = tid / F;
+  s_st[tid] = st;
+  __syncthreads();
+  for (int s = 1; s < SG; s <<= 1) {
+    if (tg % (2 * s) == 0 && tg + s < SG) {
+      merge_combine(st, s_st[tid + s * F]);
+      s_st[tid] = st;
+    }
+    __syncthreads();
+  }
+}
+
 // Fold splits tg, tg + step, ... (< nb) of four outputs: their LSEs at
 // lp[c * lstride] and partials at four-element index o4 + c * ostride of
 // o_part (load_part_bits; F16: fp16 partials), NB loads of each in flight at a
@@ -617,12 +638,7 @@ __device__ void merge_splits(const Params &p, int b, int kvg, int cg_first, int 
         merge_fold_splits<NB, true, false>(st, p.lse_part + slot0 * cols + h, cols, p.o_part, o4, ostride, tg, SG,
                                            nb);
     }
-    if (SG > 1) { // one pass only (F < kThreads): the barriers are uniform
-      s_st[tid] = st;
-      __syncthreads();
-      if (tid < F)
-        for (int j = 1; j < SG; ++j) merge_combine(st, s_st[tid + j * F]);
-    }
+    if (SG > 1) merge_groups(st, s_st, F, SG); // one pass only (F < kThreads): uniform
     if (has && tg == 0) merge_store(p, st, row, hq, D, d, vs);
   }
 }

@@ -11,7 +11,7 @@
 // of up to 16 splits at once and folds them with the running-max rescale, so
 // a request's merge costs about one memory round trip after its metadata;
 // the thread groups that share an output then combine their (max, weight,
-// accumulator) states in LDS.
+// accumulator) states pairwise in LDS.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -59,12 +59,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const Params p, const I
       else
         merge_fold_splits<kMergeBatch, false, false>(st, lp + h, g, p.o_part, o4, cstride, tg, SG, nb);
     }
-    if (SG > 1) {
-      s_st[tid] = st;
-      __syncthreads();
-      if (tid < F)
-        for (int j = 1; j < SG; ++j) merge_combine(st, s_st[tid + j * F]);
-    }
+    if (SG > 1) merge_groups(st, s_st, F, SG); // one pass (F < kThreads): uniform
     int row, hq;
     if (active && tg == 0 && column_target(p, b, kvg, cg, h, row, hq))
       merge_store(p, st, row, hq, D, d, merge_vscale(p, b, hq / p.group));
