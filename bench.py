@@ -46,13 +46,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2297309404, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
+        {"bytes": 2297289327, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1483200233, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
+        {"bytes": 1483218783, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 537790321, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
+        {"bytes": 537777958, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 677633135, "digest": "6c68803c83e32694e6eee0fdee357b81ba294ab8858598a92fa323e592d462f5"},
+        {"bytes": 677645382, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
 }
 
 
