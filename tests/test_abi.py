@@ -69,6 +69,23 @@ def test_struct_layout_matches_header(tmp_path):
     assert vals == want
 
 
+def test_constants_match_header(tmp_path):
+    """Every KVS_ constant the header defines (enums and macros) has the same
+    value in the binding, and the binding defines no other."""
+    names = sorted(set(re.findall(r"\bKVS_[A-Z0-9_]+\b", open(HEADER).read())))
+    ours = sorted(n for n in dir(kvs) if n.startswith("KVS_"))
+    assert names == ours
+    prog = ["#include <stdio.h>", f'#include "{HEADER}"', "int main(void){"]
+    prog += [f'printf("%lld\\n", (long long)({n}));' for n in names]
+    prog.append("return 0;}")
+    c = tmp_path / "consts.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "consts"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", str(c), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals == [int(getattr(kvs, n)) for n in names]
+
+
 def _args(batch=2, Hq=8, Hk=2, d=128, q=kvs.KVS_BF16, kv=kvs.KVS_BF16, P=16, lens=(100, 3000), window=-1,
           chunk=0, num_pages=1000, algo=0, ptrs=True):
     a = kvs.KvsDecodeArgs()
