@@ -221,11 +221,12 @@ Columns columns_of(const kvs_decode_args *a) {
 // Split partials of fp8 and INT4 caches are fp16 averages of the stored codes
 // (the merge applies the V scale); those of fp32 caches are fp32.  Those of
 // bf16 caches are fp16 rows scaled by a power of two (the multiplier beside
-// each row's LSE) where the decode kernel writes them, one column group per
-// workgroup; the other kernels write them in fp32.
+// each row's LSE) where the decode kernel or the 32-column kernel writes
+// them (one or two column groups per workgroup); the shared-tile and 32x32
+// prefill kernels write them in fp32.
 bool part_codes_f16(const kvs_decode_args *a) { return a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4; }
 bool part_row_scaled(const kvs_decode_args *a, int algo, const Columns &c) {
-  return a->kv_dtype == KVS_BF16 && algo != KVS_ALGO_VALU && c.col_share == 1;
+  return a->kv_dtype == KVS_BF16 && algo != KVS_ALGO_VALU && c.col_share <= 2;
 }
 
 // KV heads per partial workgroup for the resolved kernel family.

@@ -1295,9 +1295,10 @@ __global__ __launch_bounds__(kThreads) void partial_cols32_kernel(const Params p
       }
     }
     __syncthreads();
-    merge_waves_and_store<D, OSTRIDE>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
+    // bf16 caches: split partials stored as row-scaled fp16 when the host asks
+    merge_waves_and_store<D, OSTRIDE, KT == DT_BF16>(p, sm_m, sm_l, sm_o, b, kvg, cg0 + c, item, nb);
   }
-  finish_split<D>(p, blockIdx.y, b, kvg, cg0, 2, item, split, nb, smem);
+  finish_split<D, 1, kFusedMergeBatch, KT == DT_BF16>(p, blockIdx.y, b, kvg, cg0, 2, item, split, nb, smem);
 }
 
 // Column groups one wave of the shared-tile kernel computes: two for
@@ -1359,7 +1360,7 @@ static hipError_t launch_rows_d(const Params &p, const InlineWork &w, const Laun
 }
 
 hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, const Launch &l) {
-  if (p.col_share != 2 || p.pack != 1 || p.part_row_scale) return hipErrorInvalidValue; // fp32 or code partials
+  if (p.col_share != 2 || p.pack != 1 || (p.part_row_scale && kv_type != DT_BF16)) return hipErrorInvalidValue;
   const dim3 grid(p.items, p.num_kv_heads * ((p.col_groups + 1) / 2));
   // one 16 KB bf16 slot per wave, two 8 KB fp8 ones, four 4 KB INT4 ones: 64 KB per workgroup
   if (kv_type == DT_FP8) return launch_kernel(l, partial_cols32_kernel<DT_FP8, 2>, grid, p, w);

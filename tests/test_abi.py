@@ -313,9 +313,27 @@ def test_bf16_row_scaled_partials_only_past_one_workgroup_per_cu(lib, cus, row_s
     assert info.part_format == (kvs.KVS_PART_F16_ROWS if row_scales else kvs.KVS_PART_F32)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_two_column_groups_store_row_scaled_partials(lib, d):
+    """5 to 8 query rows per request at 4 heads per KV head (two groups of 16
+    columns, one workgroup: the 32-column kernel at 128, the decode kernel at
+    64): row-scaled fp16 partials in a launch past one workgroup per CU."""
+    qo = np.array([0, 8, 13, 19], np.int32)
+    a, keep = _args(d=d, lens=(1000, 3000, 5000), batch=3, chunk=64)
+    a.qo_indptr = 0x1000
+    a.qo_indptr_host = qo.ctypes.data
+    info = kvs.kvs_decode_plan(a)
+    assert info.needs_merge and info.col_groups == 2 and info.col_share == 2
+    assert info.part_format == kvs.KVS_PART_F16_ROWS
+    slots = info.items_per_kv_head * 2 * 32
+    r256 = lambda n: -(-n // 256) * 256
+    want = r256(slots * d * 2) + 2 * r256(slots * 4) + r256(3 * 8)
+    assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
+
+
 def test_bf16_partials_of_the_multi_row_kernels_stay_fp32(lib):
-    """bf16 caches with enough query rows per request for the shared-tile
-    kernel (col_share >= 4): fp32 partials, no multipliers."""
+    """bf16 caches with enough query rows per request for the shared-tile or
+    32x32 kernels (col_share >= 4): fp32 partials, no multipliers."""
     qo = np.array([0, 40, 80, 120], np.int32)
     a, keep = _args(lens=(1000, 3000, 5000), batch=3, chunk=256)
     a.qo_indptr = 0x1000

@@ -50,7 +50,8 @@ def _plan_format(inp, **kw):
     t = to_torch(inp)
     a, keep = kvs.make_args(t["q"], t["k"], t["v"], t["kv_len"], page_indptr=t.get("page_indptr"),
                             page_indices=t.get("page_indices"), kv_len_host=inp.kv_len, sm_scale=s.sm_scale,
-                            window=s.window, **kw)
+                            window=s.window, qo_indptr=t.get("qo_indptr"),
+                            qo_indptr_host=getattr(inp, "qo_indptr", None), **kw)
     return kvs.kvs_decode_plan(a).part_format
 
 
@@ -59,7 +60,7 @@ def _check(inp, k_out, **kw):
 
     assert _plan_format(inp, **kw) == kvs.KVS_PART_F16_ROWS, "the case must run the row-scaled format"
     o, lse = run_library(inp, **kw)
-    o_ref, lse_ref = oracle.decode_reference(inp)
+    o_ref, lse_ref = oracle.attention_reference(inp)
     assert np.all(np.isfinite(o)), "non-finite output"
     err = float(np.max(np.abs((o - o_ref) * 2.0 ** -k_out)))
     print(f"  max |o - o_ref| / 2^{k_out} = {err:.3e}", flush=True)
@@ -112,3 +113,22 @@ def test_row_scaled_partials_contiguous_mha():
     inp = make_inputs(spec, seed=79)
     inp = dataclasses.replace(inp, v=_scaled_v(inp, np.full(inp.v.shape[0], 18.0)))
     _check(inp, 18, kv_chunk=64)
+
+
+@pytest.mark.parametrize("d,Hq,Hk", [(128, 32, 8), (64, 16, 4)])
+@pytest.mark.parametrize("scale", ["big", "tiny", "mixed"])
+def test_row_scaled_partials_two_column_groups(d, Hq, Hk, scale):
+    """5 to 8 query rows per request with 4 query heads per KV head: two
+    groups of 16 (query row, head) columns, on the 32-column kernel (head_dim
+    128) or the decode kernel's two-group form (64)."""
+    print(f"case partials two groups d={d} {scale}", flush=True)
+    spec = dataclasses.replace(_paged(d, Hq, Hk), q_len=("list", [8, 5, 6, 8, 1]))
+    inp = make_inputs(spec, seed=80)
+    n_pages, P = inp.v.shape[0], inp.v.shape[1]
+    if scale == "mixed":
+        exps, k_out, chunk = np.where(np.arange(n_pages)[:, None] % 2 == 0, 16.0, -16.0) * np.ones((1, P)), 16, 16
+    else:
+        k_out = 18 if scale == "big" else -20
+        exps, chunk = np.full((n_pages, P), float(k_out)), 32
+    inp = dataclasses.replace(inp, v=_scaled_v(inp, exps))
+    _check(inp, k_out, kv_chunk=chunk)
