@@ -46,13 +46,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2297289327, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
+        {"bytes": 2297288149, "digest": "df00d06953ea7881cb3c9e36e05b7d7b195e5a74607f29db211b6209b9ceead3"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1483218783, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
+        {"bytes": 1483218871, "digest": "df00d06953ea7881cb3c9e36e05b7d7b195e5a74607f29db211b6209b9ceead3"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 537777958, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
+        {"bytes": 537778041, "digest": "df00d06953ea7881cb3c9e36e05b7d7b195e5a74607f29db211b6209b9ceead3"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 677645382, "digest": "aa9b2ab0eb5dd031fe67773bf4fd5d626dc19f5f520d446901e12c6672f3f2a7"},
+        {"bytes": 677645370, "digest": "df00d06953ea7881cb3c9e36e05b7d7b195e5a74607f29db211b6209b9ceead3"},
 }
 
 
