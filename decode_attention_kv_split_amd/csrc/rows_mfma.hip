@@ -300,6 +300,9 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // 128 w % 2 .. + 127.  Keys are staged 8 rows per wave (32-key blocks) so
   // that two 32 KB block slots still leave two workgroups per CU.
   constexpr bool kSplitD = D == 256;
+  // bf16 at head_dim 128: split partials stored as row-scaled fp16 when the
+  // host asks (a row is one wave's, in two lane halves)
+  constexpr bool kRowScaled = KT == DT_BF16 && !kSplitD;
   constexpr int kColWaves = kSplitD ? kWaves / 2 : kWaves; // 32-column sets per workgroup
   constexpr int kPart = kSplitD ? 8 : kTile;      // rows each wave stages per block
   constexpr int kBlock = kWaves * kPart;          // keys staged per block (64 or 32)
@@ -852,6 +855,29 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     const int cg = col / 16;
     const size_t slot = ((size_t)kvg * p.col_groups + cg) * p.items + item;
     const size_t dst = (slot * p.cols + col % 16) * D;
+    if constexpr (kRowScaled) {
+      if (p.part_row_scale) { // the row is the lane's 64 dims and its other half's (lane ^ 32)
+        float amax = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[sl][v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int k = row_scale_exp(amax * inv);
+        const float sc = ldexpf(inv, k);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            store_part4<true>(p, dst + 32 * sl + 8 * q + 4 * h2, acc[sl][4 * q] * sc, acc[sl][4 * q + 1] * sc,
+                              acc[sl][4 * q + 2] * sc, acc[sl][4 * q + 3] * sc);
+        if (h2 == 0) {
+          store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);
+          store_partial(p, p.sc_part + slot * p.cols + col % 16, ldexpf(1.0f, -k));
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
@@ -863,7 +889,8 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     if (h2 == 0 && dh == 0) store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);
   }
   }();
-  finish_split<D>(p, kvg * row_blocks + ord.rb, b, kvg, cgw, kGroups, item, split, nb, smem);
+  finish_split<D, 1, kFusedMergeBatch, kRowScaled>(p, kvg * row_blocks + ord.rb, b, kvg, cgw, kGroups, item, split,
+                                                    nb, smem);
 }
 
 // Two column groups (17 to 32 (query row, head) columns per KV head: a few
@@ -1372,7 +1399,8 @@ hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, cons
 bool rows_merge_in_kernel(int head_dim, int kv_type) { return rows_merges_in_kernel(head_dim, kv_type); }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
-  if (p.part_row_scale) return hipErrorInvalidValue; // these kernels write fp32 or code partials
+  // row-scaled partials: only the 32x32 prefill kernel for bf16 at head_dim 128 writes them
+  if (p.part_row_scale && !(kv_type == DT_BF16 && head_dim == 128)) return hipErrorInvalidValue;
   if (kv_type == DT_INT4) {
     if (head_dim == 128) return launch_rows_d<128, DT_INT4>(p, w, l);
     if (head_dim == 256) return launch_rows_d<256, DT_INT4>(p, w, l);

@@ -331,21 +331,26 @@ def test_bf16_two_column_groups_store_row_scaled_partials(lib, d):
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
 
 
-def test_bf16_partials_of_the_multi_row_kernels_stay_fp32(lib):
+@pytest.mark.parametrize("d,row_scales", [(64, False), (128, True), (256, False)])
+def test_bf16_partials_of_the_multi_row_kernels(lib, d, row_scales):
     """bf16 caches with enough query rows per request for the shared-tile or
-    32x32 kernels (col_share >= 4): fp32 partials, no multipliers."""
+    32x32 kernels (col_share >= 4): row-scaled fp16 partials from the 32x32
+    prefill kernel at head_dim 128 (a row is one wave's); fp32 ones from the
+    shared-tile kernel (64) and the head_dim-256 prefill (rows over a wave
+    pair)."""
     qo = np.array([0, 40, 80, 120], np.int32)
-    a, keep = _args(lens=(1000, 3000, 5000), batch=3, chunk=256)
+    a, keep = _args(d=d, lens=(1000, 3000, 5000), batch=3, chunk=256)
     a.qo_indptr = 0x1000
     a.qo_indptr_host = qo.ctypes.data
+    a.num_cus = 16  # 144 workgroups: past one per CU
     info = kvs.kvs_decode_plan(a)
     assert info.needs_merge and info.col_share >= 4
     cols = 16 * -(-40 * 4 // 16)  # (query row, head) columns per KV head: 10 groups of 16
     slots = info.items_per_kv_head * 2 * cols
     r256 = lambda n: -(-n // 256) * 256
-    want = r256(slots * 128 * 4) + r256(slots * 4) + r256(3 * 8)
+    want = r256(slots * d * (2 if row_scales else 4)) + r256(slots * 4) * (2 if row_scales else 1) + r256(3 * 8)
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
-    assert info.part_format == kvs.KVS_PART_F32
+    assert info.part_format == (kvs.KVS_PART_F16_ROWS if row_scales else kvs.KVS_PART_F32)
 
 
 def test_plan_heuristic_fills_the_gpu_at_batch_one(lib):

@@ -132,3 +132,22 @@ def test_row_scaled_partials_two_column_groups(d, Hq, Hk, scale):
         exps, chunk = np.full((n_pages, P), float(k_out)), 32
     inp = dataclasses.replace(inp, v=_scaled_v(inp, exps))
     _check(inp, k_out, kv_chunk=chunk)
+
+
+@pytest.mark.parametrize("scale", ["big", "tiny", "mixed"])
+def test_row_scaled_partials_prefill_kernel(scale):
+    """40 query rows per request at 4 query heads per KV head (ten groups of
+    16 columns): the 32x32 prefill kernel at head_dim 128, planned for 16 CUs
+    so that the launch stores row-scaled partials."""
+    print(f"case partials prefill {scale}", flush=True)
+    spec = small_variant("c4_paged_bf16_b64", batch=5, lengths=("list", [300, 700, 64, 1200, 40]))
+    spec = dataclasses.replace(spec, num_qo_heads=16, num_kv_heads=4, q_len=("list", [40, 40, 40, 40, 40]))
+    inp = make_inputs(spec, seed=81)
+    n_pages, P = inp.v.shape[0], inp.v.shape[1]
+    if scale == "mixed":
+        exps, k_out = np.where(np.arange(n_pages)[:, None] % 2 == 0, 16.0, -16.0) * np.ones((1, P)), 16
+    else:
+        k_out = 18 if scale == "big" else -20
+        exps = np.full((n_pages, P), float(k_out))
+    inp = dataclasses.replace(inp, v=_scaled_v(inp, exps))
+    _check(inp, k_out, kv_chunk=64, num_cus=16)
