@@ -25,15 +25,16 @@
 // col_groups + cg (already divided by the chunk's sum) and
 // lse_part[(S * I + x) * cols + h] (fp32, log2 domain: chunk max + log2(chunk
 // sum), -inf when the chunk saw no key), I = items per KV head.  o_part is
-// fp32 and includes the V scale for fp32 caches and for bf16 caches outside
-// the decode kernel.  For fp8 and INT4 caches (part_f16) it is fp16 and
-// leaves the V scale to the merge: it then holds a weighted average of the
-// decoded codes, which lies inside their range (|x| <= 448 for e4m3, <= 8 for
-// INT4), where fp16 keeps 11 significant bits; half the bytes of fp32.  A
-// bf16 cache's averages have no such bound, so the decode kernel stores each
-// partial row scaled by a power of two that puts its largest magnitude in
-// [2^14, 2^15) and leaves the inverse in sc_part[(S * I + x) * cols + h]
-// (part_row_scale); the merge multiplies it back (exact).
+// fp32 for fp32 caches and for the bf16 launches the host keeps in fp32.
+// For fp8 and INT4 caches (part_f16) it is fp16 and leaves the V scale to
+// the merge: it then holds a weighted average of the decoded codes, which
+// lies inside their range (|x| <= 448 for e4m3, <= 8 for INT4), where fp16
+// keeps 11 significant bits; half the bytes of fp32.  A bf16 cache's averages
+// have no such bound, so the decode, 32-column and head_dim-128 prefill
+// kernels store each partial row scaled by a power of two that puts its
+// largest magnitude in [2^14, 2^15) and leave the inverse in
+// sc_part[(S * I + x) * cols + h] (part_row_scale); the merge multiplies it
+// back (exact).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -210,7 +211,6 @@ __device__ __forceinline__ int row_scale_exp(float mx) {
 // Kernels that know their KV type at compile time: the host sets
 // Params::part_f16 by the same rule.
 template <int KT> constexpr bool part_f16_of() { return KT == DT_FP8 || KT == DT_INT4; }
-// Dims 4 i .. 4 i + 3 of o_part (i: index in units of four elements).
 // The stored bits of dims 4 i .. 4 i + 3 of o_part (i: index in units of four
 // elements): two dwords of fp16 pairs (F16; z, w unused) or four fp32.  The
 // merge keeps the raw bits until every load of a batch is issued, and

@@ -260,11 +260,13 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
  * rewritten by every call.  The partial outputs are fp32 for fp32 caches;
  * for fp8 and INT4 caches they are fp16 weighted averages of the stored
  * codes, which lie inside the codes' range (the merge applies the V scale),
- * so fp16 keeps 11 significant bits at half the bytes.  For bf16 caches with
- * one column group per partial workgroup (col_share 1) each partial row is
- * stored in fp16 times a power of two that puts its largest magnitude in
+ * so fp16 keeps 11 significant bits at half the bytes.  For bf16 caches in
+ * launches of more workgroups than CUs, on the decode and 32-column kernels
+ * (col_share 1 or 2) and the prefill kernel at head_dim 128, each partial row
+ * is stored in fp16 times a power of two that puts its largest magnitude in
  * [2^14, 2^15), with the inverse multiplier (fp32) beside its log-sum-exp;
- * the other bf16 kernels write fp32 partials.
+ * other bf16 launches write fp32 partials.  kvs_plan_info.part_format names
+ * the format of a call.
  * Preconditions that are not checked (they would need a device sync):
  * kv_len equals kv_len_host, page_indptr[b+1] - page_indptr[b] >=
  * ceil(kv_len[b] / page_size), every page id is < num_pages, and all
