@@ -222,12 +222,12 @@ Columns columns_of(const kvs_decode_args *a) {
 // (the merge applies the V scale); those of fp32 caches are fp32.  Those of
 // bf16 caches are fp16 rows scaled by a power of two (the multiplier beside
 // each row's LSE) where the decode kernel, the 32-column kernel (one or two
-// column groups per workgroup) or the 32x32 prefill kernel at head_dim 128
-// (four or more) writes them; the shared-tile kernel (head_dim 64) and the
-// head_dim-256 prefill, whose rows span a wave pair, write them in fp32.
+// column groups per workgroup) or the 32x32 prefill kernel (four or more, at
+// head_dim 128 or 256) writes them; the shared-tile kernel (several rows at
+// head_dim 64) writes them in fp32.
 bool part_codes_f16(const kvs_decode_args *a) { return a->kv_dtype == KVS_FP8_E4M3 || a->kv_dtype == KVS_INT4; }
 bool part_row_scaled(const kvs_decode_args *a, int algo, const Columns &c) {
-  return a->kv_dtype == KVS_BF16 && algo != KVS_ALGO_VALU && (c.col_share <= 2 || a->head_dim == 128);
+  return a->kv_dtype == KVS_BF16 && algo != KVS_ALGO_VALU && (c.col_share <= 2 || a->head_dim >= 128);
 }
 
 // KV heads per partial workgroup for the resolved kernel family.

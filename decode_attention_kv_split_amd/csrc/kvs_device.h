@@ -30,8 +30,8 @@
 // the merge: it then holds a weighted average of the decoded codes, which
 // lies inside their range (|x| <= 448 for e4m3, <= 8 for INT4), where fp16
 // keeps 11 significant bits; half the bytes of fp32.  A bf16 cache's averages
-// have no such bound, so the decode, 32-column and head_dim-128 prefill
-// kernels store each partial row scaled by a power of two that puts its
+// have no such bound, so the decode, 32-column and 32x32 prefill kernels
+// store each partial row scaled by a power of two that puts its
 // largest magnitude in [2^14, 2^15) and leave the inverse in
 // sc_part[(S * I + x) * cols + h] (part_row_scale); the merge multiplies it
 // back (exact).

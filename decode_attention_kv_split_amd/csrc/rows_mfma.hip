@@ -300,9 +300,9 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
   // 128 w % 2 .. + 127.  Keys are staged 8 rows per wave (32-key blocks) so
   // that two 32 KB block slots still leave two workgroups per CU.
   constexpr bool kSplitD = D == 256;
-  // bf16 at head_dim 128: split partials stored as row-scaled fp16 when the
-  // host asks (a row is one wave's, in two lane halves)
-  constexpr bool kRowScaled = KT == DT_BF16 && !kSplitD;
+  // bf16: split partials stored as row-scaled fp16 when the host asks (a
+  // row is one wave's, in two lane halves; at head_dim 256 a wave pair's)
+  constexpr bool kRowScaled = KT == DT_BF16;
   constexpr int kColWaves = kSplitD ? kWaves / 2 : kWaves; // 32-column sets per workgroup
   constexpr int kPart = kSplitD ? 8 : kTile;      // rows each wave stages per block
   constexpr int kBlock = kWaves * kPart;          // keys staged per block (64 or 32)
@@ -787,6 +787,25 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     wait_vmem<0>();
   }
 
+  // head_dim 256, row-scaled partials: the largest magnitude of each row
+  // over both waves of its pair (each holds 128 of its dims), exchanged
+  // through LDS; every wave takes the barrier (part_row_scale is uniform)
+  float pair_amax = 0.0f;
+  if constexpr (kRowScaled && kSplitD) {
+    __shared__ float s_amax[kWaves][32];
+    if (p.part_row_scale) {
+      float a = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) a = fmaxf(a, fabsf(acc[sl][v]));
+      a = fmaxf(a, __shfl_xor(a, 32, 64));
+      if (h2 == 0) s_amax[wave][j32] = a;
+      __syncthreads();
+      pair_amax = fmaxf(a, s_amax[wave ^ 1][j32]);
+    }
+  }
+
   // ---- this lane's column: final output, or the split's partial ----
   [&] {
   if (!wave_on) return;
@@ -857,21 +876,23 @@ __global__ __launch_bounds__(kThreads) void partial_prefill_kernel(const Params 
     const size_t dst = (slot * p.cols + col % 16) * D;
     if constexpr (kRowScaled) {
       if (p.part_row_scale) { // the row is the lane's 64 dims and its other half's (lane ^ 32)
-        float amax = 0.0f;
+        float amax = pair_amax;  // head_dim 256: both waves of the pair (above)
+        if constexpr (!kSplitD) {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
+          for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[sl][v]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(acc[sl][v]));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        }
         const int k = row_scale_exp(amax * inv);
         const float sc = ldexpf(inv, k);
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            store_part4<true>(p, dst + 32 * sl + 8 * q + 4 * h2, acc[sl][4 * q] * sc, acc[sl][4 * q + 1] * sc,
-                              acc[sl][4 * q + 2] * sc, acc[sl][4 * q + 3] * sc);
-        if (h2 == 0) {
+            store_part4<true>(p, dst + 128 * dh + 32 * sl + 8 * q + 4 * h2, acc[sl][4 * q] * sc,
+                              acc[sl][4 * q + 1] * sc, acc[sl][4 * q + 2] * sc, acc[sl][4 * q + 3] * sc);
+        if (h2 == 0 && dh == 0) {
           store_partial(p, p.lse_part + slot * p.cols + col % 16, lse2);
           store_partial(p, p.sc_part + slot * p.cols + col % 16, ldexpf(1.0f, -k));
         }
@@ -1399,8 +1420,8 @@ hipError_t launch_cols32(const Params &p, const InlineWork &w, int kv_type, cons
 bool rows_merge_in_kernel(int head_dim, int kv_type) { return rows_merges_in_kernel(head_dim, kv_type); }
 
 hipError_t launch_partial_rows(const Params &p, const InlineWork &w, int head_dim, int kv_type, const Launch &l) {
-  // row-scaled partials: only the 32x32 prefill kernel for bf16 at head_dim 128 writes them
-  if (p.part_row_scale && !(kv_type == DT_BF16 && head_dim == 128)) return hipErrorInvalidValue;
+  // row-scaled partials: only the 32x32 prefill kernel (bf16 at head_dim 128 and 256) writes them
+  if (p.part_row_scale && !(kv_type == DT_BF16 && head_dim >= 128)) return hipErrorInvalidValue;
   if (kv_type == DT_INT4) {
     if (head_dim == 128) return launch_rows_d<128, DT_INT4>(p, w, l);
     if (head_dim == 256) return launch_rows_d<256, DT_INT4>(p, w, l);

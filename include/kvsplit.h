@@ -262,7 +262,7 @@ size_t kvs_decode_workspace_bytes(const kvs_decode_args *args);
  * codes, which lie inside the codes' range (the merge applies the V scale),
  * so fp16 keeps 11 significant bits at half the bytes.  For bf16 caches in
  * launches of more workgroups than CUs, on the decode and 32-column kernels
- * (col_share 1 or 2) and the prefill kernel at head_dim 128, each partial row
+ * (col_share 1 or 2) and the prefill kernel (head_dim 128 or 256), each partial row
  * is stored in fp16 times a power of two that puts its largest magnitude in
  * [2^14, 2^15), with the inverse multiplier (fp32) beside its log-sum-exp;
  * other bf16 launches write fp32 partials.  kvs_plan_info.part_format names

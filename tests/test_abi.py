@@ -331,13 +331,12 @@ def test_bf16_two_column_groups_store_row_scaled_partials(lib, d):
     assert info.workspace_bytes == kvs.KVS_WORKSPACE_COUNTER_BYTES + want
 
 
-@pytest.mark.parametrize("d,row_scales", [(64, False), (128, True), (256, False)])
+@pytest.mark.parametrize("d,row_scales", [(64, False), (128, True), (256, True)])
 def test_bf16_partials_of_the_multi_row_kernels(lib, d, row_scales):
     """bf16 caches with enough query rows per request for the shared-tile or
     32x32 kernels (col_share >= 4): row-scaled fp16 partials from the 32x32
-    prefill kernel at head_dim 128 (a row is one wave's); fp32 ones from the
-    shared-tile kernel (64) and the head_dim-256 prefill (rows over a wave
-    pair)."""
+    prefill kernel (head_dim 128: a row is one wave's; 256: a wave pair's);
+    fp32 ones from the shared-tile kernel (head_dim 64)."""
     qo = np.array([0, 40, 80, 120], np.int32)
     a, keep = _args(d=d, lens=(1000, 3000, 5000), batch=3, chunk=256)
     a.qo_indptr = 0x1000

@@ -134,14 +134,16 @@ def test_row_scaled_partials_two_column_groups(d, Hq, Hk, scale):
     _check(inp, k_out, kv_chunk=chunk)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("scale", ["big", "tiny", "mixed"])
-def test_row_scaled_partials_prefill_kernel(scale):
+def test_row_scaled_partials_prefill_kernel(d, scale):
     """40 query rows per request at 4 query heads per KV head (ten groups of
-    16 columns): the 32x32 prefill kernel at head_dim 128, planned for 16 CUs
-    so that the launch stores row-scaled partials."""
-    print(f"case partials prefill {scale}", flush=True)
+    16 columns): the 32x32 prefill kernel (head_dim 256: a row over a wave
+    pair), planned for 16 CUs so that the launch stores row-scaled partials."""
+    print(f"case partials prefill d={d} {scale}", flush=True)
     spec = small_variant("c4_paged_bf16_b64", batch=5, lengths=("list", [300, 700, 64, 1200, 40]))
-    spec = dataclasses.replace(spec, num_qo_heads=16, num_kv_heads=4, q_len=("list", [40, 40, 40, 40, 40]))
+    spec = dataclasses.replace(spec, num_qo_heads=16 if d == 128 else 8, num_kv_heads=4 if d == 128 else 2,
+                               head_dim=d, sm_scale=d ** -0.5, q_len=("list", [40, 40, 40, 40, 40]))
     inp = make_inputs(spec, seed=81)
     n_pages, P = inp.v.shape[0], inp.v.shape[1]
     if scale == "mixed":
