@@ -46,13 +46,13 @@ _BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}
 # measured with (partial_kernel_digest); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     ("c4_paged_bf16_b64", "partial_mfma_kernel"):
-        {"bytes": 2297288598, "digest": "c0a947335c99d46453139500dc4afa92182c623f555dab3a840ceaa9e6bd94a5"},
+        {"bytes": 2297291927, "digest": "d53822c022b9899e8f7debb5a0c8b52bc0e22ff7b9ad916aca1c9fefd5213595"},
     ("c5_paged_fp8_b128", "partial_mfma_kernel"):
-        {"bytes": 1483218935, "digest": "c0a947335c99d46453139500dc4afa92182c623f555dab3a840ceaa9e6bd94a5"},
+        {"bytes": 1483218586, "digest": "d53822c022b9899e8f7debb5a0c8b52bc0e22ff7b9ad916aca1c9fefd5213595"},
     ("c3_llama2_7b_32k", "partial_mfma_kernel"):
-        {"bytes": 537778613, "digest": "c0a947335c99d46453139500dc4afa92182c623f555dab3a840ceaa9e6bd94a5"},
+        {"bytes": 537777903, "digest": "d53822c022b9899e8f7debb5a0c8b52bc0e22ff7b9ad916aca1c9fefd5213595"},
     ("c6_paged_int4_b128", "partial_mfma_kernel"):
-        {"bytes": 677645553, "digest": "c0a947335c99d46453139500dc4afa92182c623f555dab3a840ceaa9e6bd94a5"},
+        {"bytes": 677645231, "digest": "d53822c022b9899e8f7debb5a0c8b52bc0e22ff7b9ad916aca1c9fefd5213595"},
 }
 
 
